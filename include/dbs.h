@@ -1,0 +1,235 @@
+/*
+ * dbs.h — dual-view blocked sparse matrix x sparse vector multiplication
+ * (DB-SpMSpV) with BFS and sparse-decode drivers, for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The method is the one of "DB-SpMSpV: Dual-View Blocked Sparse Matrix-Sparse
+ * Vector Multiplication for Dynamic GPU Workloads" (arXiv 2608.16308):
+ *   section 2.1      the product y = A x with push (column-driven) and pull
+ *                    (row-driven) formulations, Algorithm 1;
+ *   section 3.2      the dual-view blocked format: 16x16 tiles, block-level
+ *                    CSR and CSC index views over one shared tile payload,
+ *                    five tile formats, 16-element vector blocks with masks;
+ *   section 3.3      the two-level adaptive engine: push/pull selection from
+ *                    the nonzero-block ratio, per-tile microkernels, load
+ *                    balancing and hierarchical writeback;
+ *   section 4.1      on-GPU construction of the vector-block metadata;
+ *   section 4.2      DB-BFS (frontier = sparse x, visited mask);
+ *   section 4.3      DB-Decoding (dense activation -> activation masks).
+ *
+ * Conventions for every entry point
+ *   - Matrix and vector pointers are DEVICE pointers (memory from hipMalloc or
+ *     any allocator of the current device), unless stated otherwise.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls are stream-ordered and asynchronous unless stated otherwise.
+ *   - The caller owns all input and output buffers.  The handle owns the
+ *     blocked format and the transient scratch it uses.  Inputs are never
+ *     written.  Outputs are overwritten completely on every call.
+ *   - Errors are reported by the return code only; nothing is thrown across
+ *     the ABI.  On an error return no output has been written, except where
+ *     a device-side check is documented.
+ *   - A handle may be used by one stream at a time: calls on one handle that
+ *     overlap in time race on its scratch.
+ */
+#ifndef DBS_H
+#define DBS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct dbs_matrix *dbs_handle; /* opaque */
+
+typedef enum {
+  DBS_OK = 0,
+  DBS_ERR_INVALID_ARG = 1,   /* null pointer, bad size, bad enum, dtype/semiring mismatch */
+  DBS_ERR_BAD_CSR = 2,       /* row_ptr not monotone / not starting at 0 / not ending at nnz,
+                                column out of range, columns not strictly increasing in a row */
+  DBS_ERR_OUT_OF_MEMORY = 3, /* a device allocation failed; nothing is leaked */
+  DBS_ERR_DEVICE = 4,        /* a HIP runtime call failed */
+  DBS_ERR_UNSUPPORTED = 5,   /* valid request this library does not implement */
+  DBS_ERR_BAD_VECTOR = 6     /* check mode found x_idx not strictly increasing */
+} dbs_status;
+
+/* value type of the matrix (and of x for DBS_PLUS_TIMES) */
+typedef enum { DBS_F32 = 0, DBS_BF16 = 1, DBS_PATTERN = 2 } dbs_dtype;
+
+/* PLUS_TIMES: y_i = sum_j a_ij x_j over active j, fp32 output, fp32 accumulation.
+ * OR_AND:     y_i = 1 iff row i has a stored entry in an active column (values
+ *             ignored, explicitly stored zeros count), uint8 0/1 output. */
+typedef enum { DBS_PLUS_TIMES = 0, DBS_OR_AND = 1 } dbs_semiring;
+
+/* Tile formats of section 3.2.1 (Figure 5(b)). */
+typedef enum {
+  DBS_TILE_COO = 0,       /* nnz < th0: packed (row<<4 | col) bytes + values */
+  DBS_TILE_DENSE = 1,     /* nnz > th1: 256 values, row-major */
+  DBS_TILE_FORCE_CSR = 2, /* column skew > th2 x row skew: row masks + row pointers */
+  DBS_TILE_FORCE_CSC = 3, /* row skew > th2 x column skew: column masks + column pointers */
+  DBS_TILE_CSR = 4        /* otherwise: patched CSR (row view + col_ptr + row_idx_csc2csr) */
+} dbs_tile_format;
+
+/* ------------------------------------------------------------------------
+ * Build-time options (section 3.2.1 thresholds, section 3.3.2 segment weights).
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int32_t th0;            /* COO below this nnz (default 32) */
+  int32_t th1;            /* Dense above this nnz (default 128) */
+  int32_t th2_num;        /* skew ratio threshold th2 = th2_num / th2_den (default 2/1) */
+  int32_t th2_den;
+  int32_t force_format;   /* -1 = adaptive (default); a dbs_tile_format value stores every
+                             tile in that format (the format ablation of Figure 10) */
+  int32_t seg_w_dense;    /* pull segment weights: Dense (default 4) */
+  int32_t seg_w_csr;      /*   ForceCSR / ForceCSC / CSR (default 2) */
+  int32_t seg_w_coo;      /*   COO (default 1) */
+  int32_t seg_cap;        /* a segment closes at the tile bringing its weight to >= cap.
+                             Default 64: one 64-lane wave works on a segment, one COO tile
+                             per lane (the pages' 32-lane warps use 16). */
+} dbs_build_options;
+
+/* Fills `opt` with the defaults above.  Never fails for a non-NULL pointer. */
+dbs_status dbs_build_options_default(dbs_build_options *opt);
+
+/*
+ * dbs_build — convert a CSR matrix into the dual-view blocked format
+ * (section 3.2.1, Figure 5(b)); the conversion runs on the GPU.
+ *
+ *   m, n      rows and columns, 1 <= m, n < 2^31
+ *   nnz       stored entries, 0 <= nnz < 2^31
+ *   row_ptr   device int32[m+1], row_ptr[0] = 0, non-decreasing, row_ptr[m] = nnz
+ *   col_idx   device int32[nnz], strictly increasing within each row, in [0, n)
+ *   val       device values: float[nnz] (DBS_F32), bf16 bit patterns uint16[nnz]
+ *             (DBS_BF16) or NULL (DBS_PATTERN: structure only)
+ *   opt       build options, or NULL for the defaults
+ *   stream    hipStream_t; the call is SYNCHRONOUS on it (it reads sizes back)
+ *   out       receives the new handle; untouched on error
+ *
+ * The CSR arrays may be freed once the call returns.  Returns DBS_ERR_BAD_CSR
+ * for an invalid CSR (checked on the device before any other work).
+ */
+dbs_status dbs_build(int32_t m, int32_t n, int64_t nnz, const int32_t *row_ptr,
+                     const int32_t *col_idx, const void *val, dbs_dtype dtype,
+                     const dbs_build_options *opt, void *stream, dbs_handle *out);
+
+/*
+ * dbs_spmspv — y = A x for a sparse x (sections 3.3, 4.1).
+ *
+ *   nnz_x     number of listed entries, 0 <= nnz_x <= n
+ *   x_idx     device int32[nnz_x], strictly increasing.  Listed positions form
+ *             the active set; an index outside [0, n) contributes nothing.
+ *   x_val     device values of the matrix dtype (float or bf16 bits), required
+ *             for DBS_PLUS_TIMES, ignored (may be NULL) for DBS_OR_AND.
+ *   sr        DBS_PLUS_TIMES (not allowed on a DBS_PATTERN matrix) or DBS_OR_AND
+ *   y         device float[m] (PLUS_TIMES) or uint8[m] holding 0/1 (OR_AND)
+ *
+ * One call launches the vector-metadata kernel and the SpMSpV kernel; the
+ * push/pull choice (push iff N_nzblk / N_blk < th3) is taken on the device.
+ * In check mode (DBS_OPT_CHECK) a non-increasing x_idx is flagged on the
+ * device and reported by the next dbs_get_stats as DBS_ERR_BAD_VECTOR;
+ * without check mode such input gives unspecified (but memory-safe) y.
+ */
+dbs_status dbs_spmspv(dbs_handle A, int32_t nnz_x, const int32_t *x_idx, const void *x_val,
+                      dbs_semiring sr, void *y, void *stream);
+
+/*
+ * dbs_spmspv_dense — y = A x for a dense x whose zeros are inactive, the
+ * single-token decode case (section 4.3).  The activation masks are built on
+ * the GPU from x (section 4.1): x_j is active iff x_j != 0 (+0 and -0 are
+ * inactive).
+ *
+ *   x   device float[n] (DBS_F32) or bf16 bits uint16[n] (DBS_BF16); for
+ *       DBS_OR_AND on a DBS_PATTERN matrix, float[n]
+ *   y   as for dbs_spmspv
+ */
+dbs_status dbs_spmspv_dense(dbs_handle A, const void *x, dbs_semiring sr, void *y,
+                            void *stream);
+
+/*
+ * dbs_bfs — single-source BFS levels (section 4.2, Algorithm 5).  Each level
+ * is one masked OR_AND SpMSpV y = A f with the frontier f as the sparse
+ * vector; push or pull is chosen per level from the frontier's nonzero-block
+ * ratio with the same rule as dbs_spmspv.  Vertex i is reached from j when
+ * A_ij is stored (for a symmetric A this is the usual undirected BFS).
+ *
+ *   A        square (m == n) matrix of any dtype (values are ignored)
+ *   src      source vertex, 0 <= src < m
+ *   levels   device int32[m]: hop distance from src, -1 if unreachable
+ *
+ * Synchronizes the stream once per level to read the frontier size.
+ */
+dbs_status dbs_bfs(dbs_handle A, int32_t src, int32_t *levels, void *stream);
+
+/* Per-handle run-time options (dbs_set_option / dbs_get_option). */
+enum {
+  DBS_OPT_PATH = 0,              /* 0 auto (default), 1 force push, 2 force pull */
+  DBS_OPT_TH3_NUM = 1,           /* th3 = num / den (default 1 / 100): push iff */
+  DBS_OPT_TH3_DEN = 2,           /*   N_nzblk * den < N_blk * num              */
+  DBS_OPT_LOCAL_PUSH_CUTOFF = 3, /* patched-CSR tiles use the column (push) microkernel
+                                    when popcount(blk_x_mask) < cutoff (default 8) */
+  DBS_OPT_TIMING = 4,            /* 1: time the kernels of each call with HIP events */
+  DBS_OPT_CHECK = 5              /* 1: validate x_idx ordering on the device */
+};
+dbs_status dbs_set_option(dbs_handle A, int32_t option, int64_t value);
+dbs_status dbs_get_option(dbs_handle A, int32_t option, int64_t *value);
+
+typedef struct {
+  /* format (fixed at build time) */
+  int32_t m, n, mb, nb;            /* rows, columns, row blocks, column blocks */
+  int64_t nnz, tiles;
+  int64_t tiles_by_format[5];      /* indexed by dbs_tile_format */
+  int64_t nnz_by_format[5];
+  int64_t segments;                /* pull segments */
+  int64_t payload_bytes;           /* tile payload arena */
+  int64_t index_bytes;             /* block-CSR + block-CSC views and tile metadata */
+  int64_t format_bytes;            /* payload + index + segment descriptors */
+  int64_t build_peak_bytes;        /* peak device memory held during dbs_build */
+  /* last dbs_spmspv / dbs_spmspv_dense call (reading them synchronizes its stream) */
+  int32_t last_path;               /* 0 push, 1 pull, -1 no call yet */
+  int32_t last_n_nzblk;            /* nonzero vector blocks */
+  int64_t last_push_chunks;        /* 64-tile work chunks listed for push */
+  float last_meta_ms;              /* metadata kernel time (DBS_OPT_TIMING), else -1 */
+  float last_compute_ms;           /* SpMSpV kernel time (DBS_OPT_TIMING), else -1 */
+  /* last dbs_bfs call */
+  int32_t bfs_levels;              /* levels run (including the empty last one) */
+  int32_t bfs_push_levels;         /* of which push */
+  int64_t bfs_reached;             /* vertices with a level >= 0 */
+  float bfs_ms;                    /* whole BFS (DBS_OPT_TIMING), else -1 */
+  float bfs_kernel_ms;             /* sum of the level kernels (DBS_OPT_TIMING), else -1 */
+} dbs_stats;
+
+/* Fills `out`; synchronizes the stream of the last call.  Returns
+ * DBS_ERR_BAD_VECTOR (and still fills `out`) if check mode flagged the last call. */
+dbs_status dbs_get_stats(dbs_handle A, dbs_stats *out);
+
+/* Internal arrays of the format, copied to HOST memory for inspection and
+ * tests.  `bytes_out` (may be NULL) receives the array's size; `dst` may be
+ * NULL to query the size only; otherwise `capacity` must be at least that
+ * size.  Synchronous.  Layouts are described in the library's design notes. */
+enum {
+  DBS_ARR_RB_PTR = 0,      /* uint32[mb+1]   global_block_csr_row_ptr */
+  DBS_ARR_T_CB = 1,        /* uint32[T]      global_block_csr_col_idx */
+  DBS_ARR_T_META = 2,      /* uint64[T]      payload offset | (nnz-1)<<40 | format<<48 */
+  DBS_ARR_CB_PTR = 3,      /* uint32[nb+1]   global_block_csc_col_ptr */
+  DBS_ARR_CSC_RB = 4,      /* uint32[T]      global_block_csc_row_idx */
+  DBS_ARR_CSC2CSR = 5,     /* uint32[T]      global_block_csc2csr */
+  DBS_ARR_PAYLOAD = 6,     /* uint8[]        tile payload arena */
+  DBS_ARR_SEGMENTS = 7,    /* uint32[4*S]    {row block | split<<31, t0, t1, 0} */
+  DBS_ARR_XMASK = 8,       /* uint16[nb]     blk_x_mask of the last call */
+  DBS_ARR_ACTIVE = 9       /* uint32[N_nzblk] nonzero vector blocks of the last call (any order) */
+};
+dbs_status dbs_copy_array(dbs_handle A, int32_t which, void *dst, int64_t capacity,
+                          int64_t *bytes_out);
+
+/* Releases the handle and everything it owns (synchronizes its last stream).
+ * NULL is accepted. */
+dbs_status dbs_free(dbs_handle A);
+
+/* Static description of a status code. */
+const char *dbs_status_string(dbs_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DBS_H */

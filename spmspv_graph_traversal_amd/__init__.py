@@ -1,0 +1,20 @@
+"""DB-SpMSpV for AMD Instinct MI355X (gfx950).
+
+The computation lives in the HIP library ``libdbs.so`` (C ABI in
+``include/dbs.h``); :mod:`spmspv_graph_traversal_amd.binding` marshals torch
+tensors into it.  Attribute access on this package loads the binding and
+fails with ``ImportError`` when the library has not been built.
+"""
+import importlib
+
+__all__ = ["binding"]
+
+
+def __getattr__(name):
+    binding = importlib.import_module(".binding", __name__)
+    if name == "binding":
+        return binding
+    try:
+        return getattr(binding, name)
+    except AttributeError:
+        raise AttributeError(f"module {__name__!r} has no attribute {name!r}") from None

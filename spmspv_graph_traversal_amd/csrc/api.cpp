@@ -1,0 +1,329 @@
+// C-ABI entry points of the library (declared in include/dbs.h): argument
+// validation, handle lifetime, options, statistics and array export.  All
+// compute is in the HIP kernels of build.hip, spmspv.hip and bfs.hip.
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+
+#include "common.h"
+
+hipError_t dbs_note(hipError_t e, const char *file, int line) {
+  static const int verbose = getenv("DBS_VERBOSE") != nullptr;
+  if (e != hipSuccess && verbose) fprintf(stderr, "[dbs] %s:%d: %s\n", file, line, hipGetErrorString(e));
+  return e;
+}
+
+hipError_t dbs_dev_alloc(dbs_matrix *A, void **p, size_t bytes) {
+  hipError_t e = hipMalloc(p, bytes);
+  if (e != hipSuccess) {
+    *p = nullptr;
+    (void)hipGetLastError();  // clear the sticky error of a failed allocation
+    return e;
+  }
+  A->mem_now += (int64_t)bytes;
+  if (A->mem_now > A->mem_peak) A->mem_peak = A->mem_now;
+  return hipSuccess;
+}
+
+void dbs_dev_free(dbs_matrix *A, void *p, size_t bytes) {
+  if (!p) return;
+  (void)hipFree(p);
+  A->mem_now -= (int64_t)bytes;
+}
+
+namespace {
+
+void free_all(dbs_matrix *A) {
+  void *bufs[] = {A->rb_ptr, A->t_cb,     A->t_meta,   A->cb_ptr,     A->csc_rb,  A->csc2csr,
+                  A->payload, A->segs,    A->xmask,    A->xd,         A->act_list, A->chunks,
+                  A->ctr,    A->bfs_bm,   A->bfs_vis,  A->bfs_list,   A->bfs_chunks, A->bfs_ctr};
+  for (void *b : bufs)
+    if (b) (void)hipFree(b);
+  if (A->bfs_host) (void)hipHostFree(A->bfs_host);
+  for (int i = 0; i < 6; ++i)
+    if (A->ev[i]) (void)hipEventDestroy(A->ev[i]);
+}
+
+dbs_status map_err(hipError_t e) {
+  if (e == hipSuccess) return DBS_OK;
+  if (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation) return DBS_ERR_OUT_OF_MEMORY;
+  return DBS_ERR_DEVICE;
+}
+
+#define API_TRY(expr)                       \
+  do {                                      \
+    dbs_status st_ = map_err(DBS_NOTE(expr));         \
+    if (st_ != DBS_OK) return st_;          \
+  } while (0)
+
+bool valid_options(const dbs_build_options &o) {
+  if (o.th0 < 0 || o.th1 < 0 || o.th2_num <= 0 || o.th2_den <= 0) return false;
+  if (o.force_format < -1 || o.force_format > DBS_TILE_CSR) return false;
+  if (o.seg_w_dense < 1 || o.seg_w_csr < 1 || o.seg_w_coo < 1 || o.seg_cap < 1) return false;
+  return true;
+}
+
+dbs_status alloc_call_scratch(dbs_matrix *A) {
+  const int vs = A->vk == VK_F32 ? 4 : 2;  // a dense f32 x on a pattern matrix needs no staging
+  API_TRY(dbs_dev_alloc(A, (void **)&A->xmask, (size_t)A->nb * 4));
+  API_TRY(hipMemset(A->xmask, 0, (size_t)A->nb * 4));
+  API_TRY(dbs_dev_alloc(A, &A->xd, (size_t)A->nb * 16 * vs));
+  API_TRY(dbs_dev_alloc(A, (void **)&A->act_list, (size_t)A->nb * 4));
+  A->max_chunks = A->T / 64 + A->nb + 1;
+  API_TRY(dbs_dev_alloc(A, (void **)&A->chunks, (size_t)A->max_chunks * 8));
+  API_TRY(dbs_dev_alloc(A, (void **)&A->ctr, 16 * 4));
+  API_TRY(hipMemset(A->ctr, 0, 16 * 4));
+  return DBS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dbs_status dbs_build_options_default(dbs_build_options *o) {
+  if (!o) return DBS_ERR_INVALID_ARG;
+  o->th0 = 32;
+  o->th1 = 128;
+  o->th2_num = 2;
+  o->th2_den = 1;
+  o->force_format = -1;
+  o->seg_w_dense = 4;
+  o->seg_w_csr = 2;
+  o->seg_w_coo = 1;
+  o->seg_cap = 64;
+  return DBS_OK;
+}
+
+dbs_status dbs_build(int32_t m, int32_t n, int64_t nnz, const int32_t *row_ptr, const int32_t *col_idx,
+                     const void *val, dbs_dtype dtype, const dbs_build_options *opt, void *stream,
+                     dbs_handle *out) {
+  if (!out || !row_ptr || m < 1 || n < 1 || nnz < 0 || nnz >= (int64_t)1 << 31) return DBS_ERR_INVALID_ARG;
+  if (dtype != DBS_F32 && dtype != DBS_BF16 && dtype != DBS_PATTERN) return DBS_ERR_INVALID_ARG;
+  if (nnz > 0 && !col_idx) return DBS_ERR_INVALID_ARG;
+  if (dtype != DBS_PATTERN && nnz > 0 && !val) return DBS_ERR_INVALID_ARG;
+  dbs_build_options o;
+  if (opt) o = *opt;
+  else dbs_build_options_default(&o);
+  if (!valid_options(o)) return DBS_ERR_INVALID_ARG;
+
+  dbs_matrix *A = new (std::nothrow) dbs_matrix;
+  if (!A) return DBS_ERR_OUT_OF_MEMORY;
+  memset((void *)A, 0, sizeof(*A));
+  hipStream_t s = (hipStream_t)stream;
+  if (DBS_NOTE(hipGetDevice(&A->device)) != hipSuccess) {
+    delete A;
+    return DBS_ERR_DEVICE;
+  }
+  A->m = m;
+  A->n = n;
+  A->mb = (m + 15) / 16;
+  A->nb = (n + 15) / 16;
+  A->nnz = nnz;
+  A->dtype = dtype;
+  A->vk = dtype == DBS_F32 ? VK_F32 : dtype == DBS_BF16 ? VK_BF16 : VK_PAT;
+  A->bopt = o;
+  A->opt[DBS_OPT_PATH] = 0;
+  A->opt[DBS_OPT_TH3_NUM] = 1;
+  A->opt[DBS_OPT_TH3_DEN] = 100;
+  A->opt[DBS_OPT_LOCAL_PUSH_CUTOFF] = 8;
+  A->opt[DBS_OPT_TIMING] = 0;
+  A->opt[DBS_OPT_CHECK] = 0;
+  A->st.last_path = -1;
+  A->st.last_meta_ms = -1.0f;
+  A->st.last_compute_ms = -1.0f;
+  A->st.bfs_ms = -1.0f;
+  A->st.bfs_kernel_ms = -1.0f;
+  A->last_stream = s;
+
+  dbs_status st = dbs_build_impl(A, row_ptr, col_idx, val, s);
+  if (st != DBS_OK && getenv("DBS_VERBOSE")) fprintf(stderr, "[dbs] build stage failed: %d\n", (int)st);
+  if (st == DBS_OK) {
+    A->st.build_peak_bytes = A->mem_peak;
+    st = alloc_call_scratch(A);
+  }
+  for (int i = 0; st == DBS_OK && i < 6; ++i) st = map_err(DBS_NOTE(hipEventCreate(&A->ev[i])));
+  if (st == DBS_OK) st = map_err(DBS_NOTE(hipStreamSynchronize(s)));
+  if (st != DBS_OK) {
+    (void)hipStreamSynchronize(s);
+    free_all(A);
+    delete A;
+    return st;
+  }
+  A->st.m = m;
+  A->st.n = n;
+  A->st.mb = A->mb;
+  A->st.nb = A->nb;
+  A->st.nnz = nnz;
+  A->st.tiles = A->T;
+  A->st.segments = A->nseg;
+  A->st.payload_bytes = A->payload_bytes;
+  A->st.index_bytes = (int64_t)(A->mb + 1) * 4 + A->T * (4 + 8 + 4 + 4) + (int64_t)(A->nb + 1) * 4;
+  A->st.format_bytes = A->st.payload_bytes + A->st.index_bytes + A->nseg * 16;
+  *out = A;
+  return DBS_OK;
+}
+
+static dbs_status check_semiring(const dbs_matrix *A, dbs_semiring sr) {
+  if (sr != DBS_PLUS_TIMES && sr != DBS_OR_AND) return DBS_ERR_INVALID_ARG;
+  if (sr == DBS_PLUS_TIMES && A->dtype == DBS_PATTERN) return DBS_ERR_INVALID_ARG;
+  return DBS_OK;
+}
+
+dbs_status dbs_spmspv(dbs_handle A, int32_t nnz_x, const int32_t *x_idx, const void *x_val, dbs_semiring sr,
+                      void *y, void *stream) {
+  if (!A || !y || nnz_x < 0 || nnz_x > A->n) return DBS_ERR_INVALID_ARG;
+  if (nnz_x > 0 && !x_idx) return DBS_ERR_INVALID_ARG;
+  dbs_status st = check_semiring(A, sr);
+  if (st != DBS_OK) return st;
+  if (sr == DBS_PLUS_TIMES && nnz_x > 0 && !x_val) return DBS_ERR_INVALID_ARG;
+  return dbs_spmspv_impl(A, nnz_x, x_idx, x_val, nullptr, sr, y, (hipStream_t)stream);
+}
+
+dbs_status dbs_spmspv_dense(dbs_handle A, const void *x, dbs_semiring sr, void *y, void *stream) {
+  if (!A || !x || !y) return DBS_ERR_INVALID_ARG;
+  dbs_status st = check_semiring(A, sr);
+  if (st != DBS_OK) return st;
+  return dbs_spmspv_impl(A, 0, nullptr, nullptr, x, sr, y, (hipStream_t)stream);
+}
+
+dbs_status dbs_bfs(dbs_handle A, int32_t src, int32_t *levels, void *stream) {
+  if (!A || !levels || A->m != A->n || src < 0 || src >= A->m) return DBS_ERR_INVALID_ARG;
+  return dbs_bfs_impl(A, src, levels, (hipStream_t)stream);
+}
+
+dbs_status dbs_set_option(dbs_handle A, int32_t option, int64_t value) {
+  if (!A) return DBS_ERR_INVALID_ARG;
+  switch (option) {
+    case DBS_OPT_PATH:
+      if (value < 0 || value > 2) return DBS_ERR_INVALID_ARG;
+      break;
+    case DBS_OPT_TH3_NUM:
+      if (value < 0 || value > ((int64_t)1 << 31)) return DBS_ERR_INVALID_ARG;
+      break;
+    case DBS_OPT_TH3_DEN:
+      if (value < 1 || value > ((int64_t)1 << 31)) return DBS_ERR_INVALID_ARG;
+      break;
+    case DBS_OPT_LOCAL_PUSH_CUTOFF:
+      if (value < 0 || value > 17) return DBS_ERR_INVALID_ARG;
+      break;
+    case DBS_OPT_TIMING:
+    case DBS_OPT_CHECK:
+      if (value != 0 && value != 1) return DBS_ERR_INVALID_ARG;
+      break;
+    default:
+      return DBS_ERR_INVALID_ARG;
+  }
+  A->opt[option] = value;
+  return DBS_OK;
+}
+
+dbs_status dbs_get_option(dbs_handle A, int32_t option, int64_t *value) {
+  if (!A || !value || option < 0 || option > DBS_OPT_CHECK) return DBS_ERR_INVALID_ARG;
+  *value = A->opt[option];
+  return DBS_OK;
+}
+
+dbs_status dbs_get_stats(dbs_handle A, dbs_stats *out) {
+  if (!A || !out) return DBS_ERR_INVALID_ARG;
+  dbs_status ret = DBS_OK;
+  if (A->st.last_path == -2) {
+    // counters of the last call live in the buffer before the current one
+    const uint32_t *c = A->ctr + 8 * (1 - A->cbuf);
+    uint32_t h[8];
+    API_TRY(hipMemcpyAsync(h, c, sizeof h, hipMemcpyDeviceToHost, A->last_stream));
+    API_TRY(hipStreamSynchronize(A->last_stream));
+    A->st.last_n_nzblk = (int32_t)h[0];
+    A->st.last_push_chunks = h[1];
+    const int64_t fp = A->opt[DBS_OPT_PATH];
+    const bool push = fp == 1 || (fp == 0 && (int64_t)h[0] * A->opt[DBS_OPT_TH3_DEN] <
+                                                 (int64_t)A->nb * A->opt[DBS_OPT_TH3_NUM]);
+    A->st.last_path = push ? 0 : 1;
+    A->st.last_meta_ms = -1.0f;
+    A->st.last_compute_ms = -1.0f;
+    if (A->timing_pending) {
+      float a = 0.0f, b = 0.0f;
+      API_TRY(hipEventSynchronize(A->ev[2]));
+      API_TRY(hipEventElapsedTime(&a, A->ev[0], A->ev[1]));
+      API_TRY(hipEventElapsedTime(&b, A->ev[1], A->ev[2]));
+      A->st.last_meta_ms = a;
+      A->st.last_compute_ms = b;
+    }
+    if (h[2]) ret = DBS_ERR_BAD_VECTOR;
+    A->timing_pending = 0;
+  } else {
+    API_TRY(hipStreamSynchronize(A->last_stream));
+  }
+  *out = A->st;
+  return ret;
+}
+
+dbs_status dbs_copy_array(dbs_handle A, int32_t which, void *dst, int64_t capacity, int64_t *bytes_out) {
+  if (!A) return DBS_ERR_INVALID_ARG;
+  const void *src = nullptr;
+  int64_t bytes = 0;
+  switch (which) {
+    case DBS_ARR_RB_PTR: src = A->rb_ptr; bytes = (int64_t)(A->mb + 1) * 4; break;
+    case DBS_ARR_T_CB: src = A->t_cb; bytes = A->T * 4; break;
+    case DBS_ARR_T_META: src = A->t_meta; bytes = A->T * 8; break;
+    case DBS_ARR_CB_PTR: src = A->cb_ptr; bytes = (int64_t)(A->nb + 1) * 4; break;
+    case DBS_ARR_CSC_RB: src = A->csc_rb; bytes = A->T * 4; break;
+    case DBS_ARR_CSC2CSR: src = A->csc2csr; bytes = A->T * 4; break;
+    case DBS_ARR_PAYLOAD: src = A->payload; bytes = A->payload_bytes; break;
+    case DBS_ARR_SEGMENTS: src = A->segs; bytes = A->nseg * 16; break;
+    case DBS_ARR_XMASK: src = A->xmask; bytes = (int64_t)A->nb * 2; break;
+    case DBS_ARR_ACTIVE: {
+      dbs_stats tmp;
+      dbs_status s2 = dbs_get_stats(A, &tmp);
+      if (s2 != DBS_OK && s2 != DBS_ERR_BAD_VECTOR) return s2;
+      src = A->act_list;
+      bytes = A->st.last_path >= 0 ? (int64_t)A->st.last_n_nzblk * 4 : 0;
+      break;
+    }
+    default: return DBS_ERR_INVALID_ARG;
+  }
+  if (bytes_out) *bytes_out = bytes;
+  if (!dst) return DBS_OK;
+  if (capacity < bytes) return DBS_ERR_INVALID_ARG;
+  API_TRY(hipStreamSynchronize(A->last_stream));
+  if (which == DBS_ARR_XMASK) {
+    // untag: entries of an older epoch are zero masks
+    uint32_t *tmp = (uint32_t *)malloc((size_t)A->nb * 4 + 4);
+    if (!tmp) return DBS_ERR_OUT_OF_MEMORY;
+    hipError_t e = hipMemcpy(tmp, A->xmask, (size_t)A->nb * 4, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) {
+      free(tmp);
+      return map_err(e);
+    }
+    uint16_t *d = (uint16_t *)dst;
+    for (int32_t b = 0; b < A->nb; ++b) d[b] = (tmp[b] >> 16) == A->epoch ? (uint16_t)(tmp[b] & 0xFFFFu) : 0;
+    free(tmp);
+    return DBS_OK;
+  }
+  if (bytes > 0) API_TRY(hipMemcpy(dst, src, (size_t)bytes, hipMemcpyDeviceToHost));
+  return DBS_OK;
+}
+
+dbs_status dbs_free(dbs_handle A) {
+  if (!A) return DBS_OK;
+  (void)hipStreamSynchronize(A->last_stream);
+  free_all(A);
+  delete A;
+  return DBS_OK;
+}
+
+const char *dbs_status_string(dbs_status s) {
+  switch (s) {
+    case DBS_OK: return "ok";
+    case DBS_ERR_INVALID_ARG: return "invalid argument";
+    case DBS_ERR_BAD_CSR: return "invalid CSR input";
+    case DBS_ERR_OUT_OF_MEMORY: return "device out of memory";
+    case DBS_ERR_DEVICE: return "HIP runtime error";
+    case DBS_ERR_UNSUPPORTED: return "unsupported";
+    case DBS_ERR_BAD_VECTOR: return "x_idx not strictly increasing";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

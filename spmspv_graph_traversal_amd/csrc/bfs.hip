@@ -1,0 +1,319 @@
+// DB-BFS (section 4.2 and Algorithm 5 of "DB-SpMSpV: Dual-View Blocked Sparse
+// Matrix-Sparse Vector Multiplication for Dynamic GPU Workloads").
+//
+// The frontier is kept as a bitmap, 16 bits per vertex block, which is
+// directly the blk_x_mask array of the SpMSpV (section 4.1: "the frontier can
+// be represented directly as a set of masks").  Per level:
+//   k_bfs_level  masked Boolean SpMSpV next = A f & ~visited, push or pull
+//                chosen on the device from the frontier's nonzero-block count;
+//                newly found vertices are claimed with an atomic OR on the
+//                next bitmap (the winner writes their level and marks them
+//                visited);
+//   k_bfs_meta   counts the nonzero blocks of the next bitmap, lists them and
+//                reserves their push chunks (one atomic per workgroup), and
+//                clears the bitmap two levels back.
+// Three bitmaps rotate: current frontier, next frontier, and one being
+// cleared.  The host reads one counter per level to stop.
+#include "tile_kernels.h"
+
+namespace {
+
+constexpr int KT = 256;
+
+struct BfsParams {
+  const uint32_t *t_cb;
+  const uint64_t *t_meta;
+  const uint32_t *cb_ptr;
+  const uint32_t *csc_rb;
+  const uint32_t *csc2csr;
+  const uint8_t *payload;
+  uint64_t dense_mask_off;
+  const uint32_t *segs;
+  int64_t nseg;
+  int32_t m, nb;
+  const uint32_t *cur_bm;   // frontier of this level
+  uint32_t *next_bm;        // frontier of the next level (cleared)
+  uint32_t *vis;            // visited bitmap
+  const uint32_t *cur_ctr;  // [0] nonzero blocks, [1] push chunks
+  const uint64_t *cur_chunks;
+  int32_t *levels;
+  int32_t level;            // level of the current frontier
+  int32_t force_path;
+  int64_t th3_num, th3_den;
+};
+
+DBS_DEV uint32_t bm_get(const uint32_t *bm, uint32_t b) { return (bm[b >> 1] >> ((b & 1u) * 16u)) & 0xFFFFu; }
+
+DBS_DEV uint32_t rows_valid(int32_t m, uint32_t rb) {
+  const int64_t left = (int64_t)m - (int64_t)rb * 16;
+  return left >= 16 ? 0xFFFFu : (left <= 0 ? 0u : ((1u << left) - 1u));
+}
+
+// claim the vertices `f` of row block rb for the next level
+DBS_DEV void discover(const BfsParams &P, uint32_t rb, uint32_t f) {
+  const uint32_t sh = (rb & 1u) * 16u;
+  f &= ~bm_get(P.vis, rb) & rows_valid(P.m, rb);
+  if (!f) return;
+  const uint32_t old = atomicOr(&P.next_bm[rb >> 1], f << sh);
+  const uint32_t fresh = f & ~(old >> sh);
+  if (!fresh) return;
+  atomicOr(&P.vis[rb >> 1], fresh << sh);
+  for (uint32_t b = fresh; b; b &= b - 1u) P.levels[rb * 16u + (uint32_t)(__ffs(b) - 1)] = P.level + 1;
+}
+
+template <int VK>
+DBS_DEV const uint8_t *dmask(const BfsParams &P, uint64_t vp) {
+  constexpr uint64_t TS = VK == VK_F32 ? 1024 : 512;
+  return P.payload + P.dense_mask_off + 32 * (vp / TS);
+}
+
+template <int VK>
+DBS_DEV void bfs_push_chunk(const BfsParams &P, uint64_t own, int lane) {
+  const uint32_t b = (uint32_t)own, j = (uint32_t)(own >> 32);
+  const uint32_t m = bm_get(P.cur_bm, b);
+  const uint32_t k = P.cb_ptr[b] + j * 64u + (uint32_t)lane;
+  const bool act = k < P.cb_ptr[b + 1];
+  uint32_t rb = 0;
+  uint64_t meta = 0;
+  if (act) {
+    rb = P.csc_rb[k];
+    meta = P.t_meta[P.csc2csr[k]];
+  }
+  const uint32_t type = meta_type(meta);
+  if (act && type == DBS_TILE_COO) discover(P, rb, coo_or(P.payload + meta_vp(meta), meta_nnz(meta), m));
+  uint64_t todo = __ballot(act && type != DBS_TILE_COO);
+  while (todo) {
+    const int src = __ffsll((unsigned long long)todo) - 1;
+    todo &= todo - 1;
+    const uint32_t trb = (uint32_t)__shfl((int)rb, src);
+    const uint64_t tm = __shfl(meta, src);
+    const uint32_t f = tile_or<VK>(P.payload + meta_vp(tm), dmask<VK>(P, meta_vp(tm)), meta_type(tm), m, lane);
+    if (lane == 0) discover(P, trb, f);
+  }
+}
+
+template <int VK>
+DBS_DEV void bfs_pull_segment(const BfsParams &P, int64_t s, int lane) {
+  const uint4 seg = ((const uint4 *)P.segs)[s];
+  const uint32_t rb = seg.x & ~SEG_SPLIT;
+  // rows still to be found in this row block; a fully visited row block is
+  // skipped without reading its tiles
+  const uint32_t need = ~bm_get(P.vis, rb) & rows_valid(P.m, rb);
+  if (!need) return;
+  const uint32_t t = seg.y + (uint32_t)lane;
+  bool act = t < seg.z;
+  uint32_t m = 0;
+  uint64_t meta = 0;
+  if (act) {
+    m = bm_get(P.cur_bm, P.t_cb[t]);
+    act = m != 0u;
+    if (act) meta = P.t_meta[t];
+  }
+  const uint32_t type = meta_type(meta);
+  uint32_t f = 0;
+  if (act && type == DBS_TILE_COO) f = coo_or(P.payload + meta_vp(meta), meta_nnz(meta), m);
+  f = group_or_u32<64>(f);
+  uint64_t todo = __ballot(act && type != DBS_TILE_COO);
+  while (todo && (f & need) != need) {
+    const int src = __ffsll((unsigned long long)todo) - 1;
+    todo &= todo - 1;
+    const uint64_t tm = __shfl(meta, src);
+    const uint32_t tmask = (uint32_t)__shfl((int)m, src);
+    f |= tile_or<VK>(P.payload + meta_vp(tm), dmask<VK>(P, meta_vp(tm)), meta_type(tm), tmask, lane);
+  }
+  if (lane == 0 && (f & need)) discover(P, rb, f & need);
+}
+
+template <int VK>
+__global__ __launch_bounds__(KT) void k_bfs_level(BfsParams P) {
+  const int lane = __lane_id(), w = threadIdx.x / DBS_WAVE;
+  const uint32_t nz = P.cur_ctr[0];
+  const bool push = P.force_path == 1 ||
+                    (P.force_path == 0 && (int64_t)nz * P.th3_den < (int64_t)P.nb * P.th3_num);
+  const int64_t gw = (int64_t)blockIdx.x * (KT / DBS_WAVE) + w;
+  const int64_t nw = (int64_t)gridDim.x * (KT / DBS_WAVE);
+  if (push) {
+    const int64_t nch = P.cur_ctr[1];
+    for (int64_t c = gw; c < nch; c += nw) bfs_push_chunk<VK>(P, P.cur_chunks[c], lane);
+  } else {
+    for (int64_t s = gw; s < P.nseg; s += nw) bfs_pull_segment<VK>(P, s, lane);
+  }
+}
+
+// Frontier metadata: nonzero blocks of `bm`, their list and push chunks;
+// clears `clr_bm` / `clr_ctr` (the buffers two levels back) when given.
+__global__ __launch_bounds__(KT) void k_bfs_meta(const uint32_t *bm, int32_t nb, const uint32_t *cb_ptr,
+                                                 uint32_t *ctr, uint32_t *list, uint64_t *chunks,
+                                                 uint32_t *clr_bm, uint32_t *clr_ctr, int64_t nwords,
+                                                 int32_t *levels_done_flag) {
+  __shared__ uint32_t s_cnt[KT / DBS_WAVE], s_ch[KT / DBS_WAVE];
+  __shared__ uint32_t s_base_cnt, s_base_ch;
+  const int lane = __lane_id(), w = threadIdx.x / DBS_WAVE;
+  const int64_t gs = (int64_t)gridDim.x * KT;
+  if (clr_bm) {
+    for (int64_t k = (int64_t)blockIdx.x * KT + threadIdx.x; k < nwords; k += gs) clr_bm[k] = 0;
+    if (blockIdx.x == 0 && threadIdx.x < 8) clr_ctr[threadIdx.x] = 0;
+  }
+  (void)levels_done_flag;
+  for (int64_t base = (int64_t)blockIdx.x * KT; base < nb; base += gs) {
+    const int64_t b = base + threadIdx.x;
+    const bool leader = b < nb && bm_get(bm, (uint32_t)b) != 0u;
+    uint32_t nch = 0;
+    if (leader) nch = (cb_ptr[b + 1] - cb_ptr[b] + 63u) >> 6;
+    const uint64_t bal = __ballot(leader);
+    const uint32_t rank = (uint32_t)__popcll(bal & __lanemask_lt());
+    const uint32_t chinc = group_incl_scan_u32<64>(nch);
+    if (lane == 63) {
+      s_cnt[w] = (uint32_t)__popcll(bal);
+      s_ch[w] = chinc;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t tc = 0, th = 0;
+      for (int i = 0; i < KT / DBS_WAVE; ++i) {
+        tc += s_cnt[i];
+        th += s_ch[i];
+      }
+      s_base_cnt = tc ? atomicAdd(&ctr[0], tc) : 0u;
+      s_base_ch = th ? atomicAdd(&ctr[1], th) : 0u;
+    }
+    __syncthreads();
+    if (leader) {
+      uint32_t pc = s_base_cnt, ph = s_base_ch;
+      for (int i = 0; i < w; ++i) {
+        pc += s_cnt[i];
+        ph += s_ch[i];
+      }
+      list[pc + rank] = (uint32_t)b;
+      const uint32_t first = ph + chinc - nch;
+      for (uint32_t k = 0; k < nch; ++k) chunks[first + k] = (uint64_t)b | ((uint64_t)k << 32);
+    }
+    __syncthreads();
+  }
+}
+
+__global__ void k_bfs_init(int32_t *levels, int32_t m, uint32_t *bm3, int64_t bm_words3, uint32_t *vis,
+                           int64_t nwords, uint32_t *ctr3, int32_t src) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t gs = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t k = i; k < m; k += gs) levels[k] = k == src ? 0 : -1;
+  for (int64_t k = i; k < bm_words3; k += gs) bm3[k] = 0;
+  for (int64_t k = i; k < nwords; k += gs) vis[k] = 0;
+  if (i < 24) ctr3[i] = 0;
+}
+
+__global__ void k_bfs_seed(uint32_t *bm0, uint32_t *vis, int32_t src) {
+  const uint32_t b = (uint32_t)src >> 4, bit = 1u << ((uint32_t)src & 15u);
+  const uint32_t sh = (b & 1u) * 16u;
+  bm0[b >> 1] = bit << sh;
+  vis[b >> 1] = bit << sh;
+}
+
+}  // namespace
+
+#define BFS_TRY(expr)                                                                            \
+  do {                                                                                           \
+    hipError_t e_ = DBS_NOTE(expr);                                                                      \
+    if (e_ != hipSuccess)                                                                        \
+      return (e_ == hipErrorOutOfMemory || e_ == hipErrorMemoryAllocation) ? DBS_ERR_OUT_OF_MEMORY \
+                                                                       : DBS_ERR_DEVICE;        \
+  } while (0)
+
+dbs_status dbs_bfs_impl(dbs_matrix *A, int32_t src, int32_t *levels, hipStream_t s) {
+  const int64_t nwords = ((int64_t)A->nb + 1) / 2;
+  const int64_t chunk_cap = A->max_chunks;
+  if (!A->bfs_bm) {
+    BFS_TRY(dbs_dev_alloc(A, (void **)&A->bfs_bm, (size_t)(3 * nwords + 1) * 4));
+    BFS_TRY(dbs_dev_alloc(A, (void **)&A->bfs_vis, (size_t)(nwords + 1) * 4));
+    BFS_TRY(dbs_dev_alloc(A, (void **)&A->bfs_list, (size_t)(3 * (int64_t)A->nb + 1) * 4));
+    BFS_TRY(dbs_dev_alloc(A, (void **)&A->bfs_chunks, (size_t)(3 * chunk_cap + 1) * 8));
+    BFS_TRY(dbs_dev_alloc(A, (void **)&A->bfs_ctr, 24 * 4));
+    BFS_TRY(hipHostMalloc((void **)&A->bfs_host, 64, hipHostMallocDefault));
+  }
+  const bool timing = A->opt[DBS_OPT_TIMING] != 0;
+  if (timing) BFS_TRY(hipEventRecord(A->ev[3], s));
+  hipLaunchKernelGGL(k_bfs_init, dim3(1024), dim3(256), 0, s, levels, A->m, A->bfs_bm, 3 * nwords,
+                     A->bfs_vis, nwords, A->bfs_ctr, src);
+  hipLaunchKernelGGL(k_bfs_seed, dim3(1), dim3(1), 0, s, A->bfs_bm, A->bfs_vis, src);
+  BFS_TRY(hipGetLastError());
+  const unsigned mgrid = (unsigned)(((int64_t)A->nb + KT - 1) / KT < 1024 ? ((int64_t)A->nb + KT - 1) / KT : 1024);
+  hipLaunchKernelGGL(k_bfs_meta, dim3(mgrid ? mgrid : 1), dim3(KT), 0, s, (const uint32_t *)A->bfs_bm, A->nb,
+                     (const uint32_t *)A->cb_ptr, A->bfs_ctr, A->bfs_list, A->bfs_chunks, (uint32_t *)nullptr,
+                     (uint32_t *)nullptr, (int64_t)0, (int32_t *)nullptr);
+  BFS_TRY(hipGetLastError());
+
+  BfsParams P;
+  P.t_cb = A->t_cb;
+  P.t_meta = A->t_meta;
+  P.cb_ptr = A->cb_ptr;
+  P.csc_rb = A->csc_rb;
+  P.csc2csr = A->csc2csr;
+  P.payload = A->payload;
+  P.dense_mask_off = A->dense_mask_off;
+  P.segs = A->segs;
+  P.nseg = A->nseg;
+  P.m = A->m;
+  P.nb = A->nb;
+  P.vis = A->bfs_vis;
+  P.levels = levels;
+  P.force_path = (int32_t)A->opt[DBS_OPT_PATH];
+  P.th3_num = A->opt[DBS_OPT_TH3_NUM];
+  P.th3_den = A->opt[DBS_OPT_TH3_DEN];
+  int64_t waves = A->nseg > chunk_cap ? A->nseg : chunk_cap;
+  int64_t g = (waves + 3) / 4;
+  const unsigned grid = (unsigned)(g < 1 ? 1 : (g > 2048 ? 2048 : g));
+
+  int32_t L = 0, push_levels = 0;
+  float kms = 0.0f;
+  while (true) {
+    const int cur = L % 3, nxt = (L + 1) % 3, clr = (L + 2) % 3;
+    P.cur_bm = A->bfs_bm + cur * nwords;
+    P.next_bm = A->bfs_bm + nxt * nwords;
+    P.cur_ctr = A->bfs_ctr + 8 * cur;
+    P.cur_chunks = A->bfs_chunks + cur * chunk_cap;
+    P.level = L;
+    if (timing) BFS_TRY(hipEventRecord(A->ev[4], s));
+    if (A->vk == VK_F32) hipLaunchKernelGGL(k_bfs_level<VK_F32>, dim3(grid), dim3(KT), 0, s, P);
+    else if (A->vk == VK_BF16) hipLaunchKernelGGL(k_bfs_level<VK_BF16>, dim3(grid), dim3(KT), 0, s, P);
+    else hipLaunchKernelGGL(k_bfs_level<VK_PAT>, dim3(grid), dim3(KT), 0, s, P);
+    BFS_TRY(hipGetLastError());
+    if (timing) BFS_TRY(hipEventRecord(A->ev[5], s));
+    hipLaunchKernelGGL(k_bfs_meta, dim3(mgrid ? mgrid : 1), dim3(KT), 0, s, (const uint32_t *)P.next_bm, A->nb,
+                       (const uint32_t *)A->cb_ptr, A->bfs_ctr + 8 * nxt, A->bfs_list + (int64_t)nxt * A->nb,
+                       A->bfs_chunks + nxt * chunk_cap, A->bfs_bm + clr * nwords, A->bfs_ctr + 8 * clr, nwords,
+                       (int32_t *)nullptr);
+    BFS_TRY(hipGetLastError());
+    BFS_TRY(hipMemcpyAsync(A->bfs_host, A->bfs_ctr + 8 * cur, 8, hipMemcpyDeviceToHost, s));
+    BFS_TRY(hipMemcpyAsync(A->bfs_host + 2, A->bfs_ctr + 8 * nxt, 4, hipMemcpyDeviceToHost, s));
+    BFS_TRY(hipStreamSynchronize(s));
+    if (timing) {
+      float ms = 0.0f;
+      BFS_TRY(hipEventElapsedTime(&ms, A->ev[4], A->ev[5]));
+      kms += ms;
+    }
+    const uint32_t nz_cur = A->bfs_host[0];
+    const bool was_push = A->opt[DBS_OPT_PATH] == 1 ||
+                          (A->opt[DBS_OPT_PATH] == 0 &&
+                           (int64_t)nz_cur * A->opt[DBS_OPT_TH3_DEN] < (int64_t)A->nb * A->opt[DBS_OPT_TH3_NUM]);
+    push_levels += was_push ? 1 : 0;
+    ++L;
+    if (A->bfs_host[2] == 0u) break;
+    if (L > A->m + 1) return DBS_ERR_DEVICE;  // cannot happen: every level adds a vertex
+  }
+  if (timing) {
+    BFS_TRY(hipEventRecord(A->ev[4], s));
+    BFS_TRY(hipEventSynchronize(A->ev[4]));
+    float ms = 0.0f;
+    BFS_TRY(hipEventElapsedTime(&ms, A->ev[3], A->ev[4]));
+    A->st.bfs_ms = ms;
+    A->st.bfs_kernel_ms = kms;
+  } else {
+    A->st.bfs_ms = -1.0f;
+    A->st.bfs_kernel_ms = -1.0f;
+  }
+  A->st.bfs_levels = L;
+  A->st.bfs_push_levels = push_levels;
+  A->st.bfs_reached = -1;
+  A->last_stream = s;
+  return DBS_OK;
+}

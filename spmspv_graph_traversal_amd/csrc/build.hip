@@ -1,0 +1,510 @@
+// Format builder: CSR -> dual-view blocked format (section 3.2.1 and Figure
+// 5(b) of "DB-SpMSpV: Dual-View Blocked Sparse Matrix-Sparse Vector
+// Multiplication for Dynamic GPU Workloads"), entirely on the GPU.
+//
+// Tiles are found by a 16-way merge: one aligned group of 16 lanes (a DPP
+// row of the wave) owns one row block, one lane per row; each step takes the
+// smallest column block over the 16 row cursors, which yields the tiles of
+// the row block in ascending column-block order (the primary block-CSR order)
+// together with each row's slice of the tile.  The merge runs three times
+// (count, classify, fill) so that nothing per-nonzero has to be stored.
+#include <stdlib.h>
+#include <string.h>
+
+#include "common.h"
+
+namespace {
+
+constexpr int BT = 256;               // threads per block
+constexpr int RB_PER_BLOCK = BT / 16;  // row blocks per block (4 per wave)
+
+// flags of the CSR validation
+enum { BAD_FIRST = 1, BAD_LAST = 2, BAD_PTR = 4, BAD_COL = 8, BAD_ORDER = 16 };
+
+__global__ __launch_bounds__(BT) void k_validate(int32_t m, int32_t n, int64_t nnz,
+                                                 const int32_t *row_ptr, const int32_t *col_idx,
+                                                 uint32_t *flag) {
+  const int64_t i = (int64_t)blockIdx.x * BT + threadIdx.x;
+  if (i >= m) return;
+  const int64_t a = row_ptr[i], b = row_ptr[i + 1];
+  uint32_t f = 0;
+  if (i == 0 && a != 0) f |= BAD_FIRST;
+  if (i == m - 1 && b != nnz) f |= BAD_LAST;
+  if (a < 0 || b < a || b > nnz) {
+    atomicOr(flag, f | BAD_PTR);
+    return;
+  }
+  int64_t prev = -1;
+  for (int64_t k = a; k < b; ++k) {
+    const int64_t c = col_idx[k];
+    if (c < 0 || c >= n) f |= BAD_COL;
+    if (c <= prev) f |= BAD_ORDER;
+    prev = c;
+  }
+  if (f) atomicOr(flag, f);
+}
+
+// Per-lane row cursor of the merge.
+struct RowCursor {
+  int64_t p, e;
+};
+
+DBS_DEV RowCursor row_cursor(int32_t m, int32_t mb, const int32_t *row_ptr, int32_t rb, int r) {
+  RowCursor c{0, 0};
+  const int64_t row = (int64_t)rb * DBS_TILE + r;
+  if (rb < mb && row < m) {
+    c.p = row_ptr[row];
+    c.e = row_ptr[row + 1];
+  }
+  return c;
+}
+
+DBS_DEV uint32_t cursor_cb(const RowCursor &c, const int32_t *col_idx) {
+  return c.p < c.e ? ((uint32_t)col_idx[c.p] >> 4) : 0xFFFFFFFFu;
+}
+
+// advance the cursor over the entries of column block `cb`; returns the row's
+// 16-bit mask of local columns in this tile
+DBS_DEV uint32_t cursor_take(RowCursor &c, const int32_t *col_idx, uint32_t cb) {
+  uint32_t rm = 0;
+  while (c.p < c.e) {
+    const uint32_t col = (uint32_t)col_idx[c.p];
+    if ((col >> 4) != cb) break;
+    rm |= 1u << (col & 15u);
+    ++c.p;
+  }
+  return rm;
+}
+
+// column masks of the tile: lane r (of the 16-lane group) returns the mask of
+// local rows holding an entry in local column r
+DBS_DEV uint32_t transpose_masks16(uint32_t rm, int r) {
+  uint32_t cm = 0;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const uint32_t v = (uint32_t)__shfl((int)rm, k, 16);
+    cm |= ((v >> r) & 1u) << k;
+  }
+  return cm;
+}
+
+// Tile format from nnz and the largest row / column counts (section 3.2.1).
+// skew_r / skew_c = max_row / max_col because both skews divide by
+// nnz / 16 + eps, so the th2 tests are exact integer comparisons.
+DBS_DEV uint32_t classify_tile(uint32_t nnz, uint32_t maxr, uint32_t maxc,
+                               const dbs_build_options &o) {
+  if (o.force_format >= 0) return (uint32_t)o.force_format;
+  if ((int)nnz < o.th0) return DBS_TILE_COO;
+  if ((int)nnz > o.th1) return DBS_TILE_DENSE;
+  if ((uint64_t)maxr * (uint64_t)o.th2_den > (uint64_t)maxc * (uint64_t)o.th2_num)
+    return DBS_TILE_FORCE_CSC;
+  if ((uint64_t)maxc * (uint64_t)o.th2_den > (uint64_t)maxr * (uint64_t)o.th2_num)
+    return DBS_TILE_FORCE_CSR;
+  return DBS_TILE_CSR;
+}
+
+// pass 1: tiles per row block
+__global__ __launch_bounds__(BT) void k_tile_count(int32_t m, int32_t mb, const int32_t *row_ptr,
+                                                   const int32_t *col_idx, uint32_t *rb_cnt) {
+  const int r = threadIdx.x & 15;
+  const int32_t rb = (int32_t)blockIdx.x * RB_PER_BLOCK + (int32_t)(threadIdx.x >> 4);
+  RowCursor c = row_cursor(m, mb, row_ptr, rb, r);
+  uint32_t cnt = 0;
+  while (true) {
+    const uint32_t cb = group_min_u32<16>(cursor_cb(c, col_idx));
+    if (cb == 0xFFFFFFFFu) break;
+    ++cnt;
+    (void)cursor_take(c, col_idx, cb);
+  }
+  if (r == 0 && rb < mb) rb_cnt[rb] = cnt;
+}
+
+// pass 2: per tile column block, row block, nnz, format and payload size
+__global__ __launch_bounds__(BT) void k_tile_classify(int32_t m, int32_t mb, const int32_t *row_ptr,
+                                                      const int32_t *col_idx, const uint32_t *rb_ptr,
+                                                      dbs_build_options o, int vk, int64_t T,
+                                                      uint32_t *t_cb, uint32_t *t_rb, uint32_t *t_nt,
+                                                      uint64_t *sizes) {
+  const int r = threadIdx.x & 15;
+  const int32_t rb = (int32_t)blockIdx.x * RB_PER_BLOCK + (int32_t)(threadIdx.x >> 4);
+  RowCursor c = row_cursor(m, mb, row_ptr, rb, r);
+  int64_t t = rb < mb ? (int64_t)rb_ptr[rb] : 0;
+  while (true) {
+    const uint32_t cb = group_min_u32<16>(cursor_cb(c, col_idx));
+    if (cb == 0xFFFFFFFFu) break;
+    const uint32_t rm = cursor_take(c, col_idx, cb);
+    const uint32_t cm = transpose_masks16(rm, r);
+    const uint32_t nnz = group_sum_u32<16>((uint32_t)__popc(rm));
+    const uint32_t maxr = group_max_u32<16>((uint32_t)__popc(rm));
+    const uint32_t maxc = group_max_u32<16>((uint32_t)__popc(cm));
+    const uint32_t type = classify_tile(nnz, maxr, maxc, o);
+    if (r == 0) {
+      t_cb[t] = cb;
+      t_rb[t] = (uint32_t)rb;
+      t_nt[t] = (nnz - 1) | (type << 16);
+      const int sec = tile_section((int)type, vk);
+      const uint64_t bytes = tile_payload_bytes((int)type, nnz, vk);
+      sizes[t] = sec == 0 ? bytes : 0;
+      sizes[T + t] = sec == 1 ? bytes : 0;
+      sizes[2 * T + t] = sec == 2 ? bytes : 0;
+    }
+    ++t;
+  }
+}
+
+__global__ void k_pack_meta(int64_t T, int vk, const uint32_t *t_nt, const uint64_t *off,
+                            uint64_t *t_meta) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T) return;
+  const uint32_t nt = t_nt[t];
+  const uint32_t nnz = (nt & 0xFFFFu) + 1, type = nt >> 16;
+  const int sec = tile_section((int)type, vk);
+  t_meta[t] = meta_pack(off[(int64_t)sec * T + t], nnz, type);
+}
+
+template <int VK>
+DBS_DEV void store_val(uint8_t *dst, const void *val, int64_t k) {
+  if (VK == VK_F32) {
+    *(float *)dst = ((const float *)val)[k];
+  } else if (VK == VK_BF16) {
+    *(uint16_t *)dst = ((const uint16_t *)val)[k];
+  }
+}
+template <int VK>
+DBS_DEV void store_zero(uint8_t *dst) {
+  if (VK == VK_F32) *(float *)dst = 0.0f;
+  else if (VK == VK_BF16) *(uint16_t *)dst = 0;
+}
+
+// pass 3: write every tile's payload in its format
+template <int VK>
+__global__ __launch_bounds__(BT) void k_tile_fill(int32_t m, int32_t mb, const int32_t *row_ptr,
+                                                  const int32_t *col_idx, const void *val,
+                                                  const uint32_t *rb_ptr, const uint64_t *t_meta,
+                                                  uint8_t *payload, uint64_t dense_mask_off) {
+  constexpr int VS = VK == VK_F32 ? 4 : VK == VK_BF16 ? 2 : 0;
+  const int r = threadIdx.x & 15;
+  const int32_t rb = (int32_t)blockIdx.x * RB_PER_BLOCK + (int32_t)(threadIdx.x >> 4);
+  RowCursor c = row_cursor(m, mb, row_ptr, rb, r);
+  int64_t t = rb < mb ? (int64_t)rb_ptr[rb] : 0;
+  while (true) {
+    const uint32_t cb = group_min_u32<16>(cursor_cb(c, col_idx));
+    if (cb == 0xFFFFFFFFu) break;
+    const int64_t p0 = c.p;
+    const uint32_t rm = cursor_take(c, col_idx, cb);
+    const uint32_t cnt = (uint32_t)__popc(rm);
+    const uint32_t rp = group_incl_scan_u32<16>(cnt) - cnt;  // row start inside the tile
+    const uint32_t cm = transpose_masks16(rm, r);            // lane r: column r
+    const uint32_t ccnt = (uint32_t)__popc(cm);
+    const uint32_t cp = group_incl_scan_u32<16>(ccnt) - ccnt;  // column start
+    const uint64_t meta = t_meta[t];
+    const uint32_t type = meta_type(meta), nnz = meta_nnz(meta);
+    uint8_t *base = payload + meta_vp(meta);
+    if (type == DBS_TILE_COO) {
+      for (uint32_t j = 0; j < cnt; ++j) {
+        const uint32_t col = (uint32_t)col_idx[p0 + j] & 15u;
+        base[rp + j] = (uint8_t)((r << 4) | col);
+        if (VS) store_val<VK>(base + coo_val_off(nnz) + (rp + j) * VS, val, p0 + j);
+      }
+    } else if (VK == VK_PAT) {
+      ((uint16_t *)(base + PL_MASK))[r] = (uint16_t)rm;
+      ((uint16_t *)(base + PL_PAT_COLMASK))[r] = (uint16_t)cm;
+    } else if (type == DBS_TILE_DENSE) {
+      ((uint16_t *)(payload + dense_mask_off + 32 * (meta_vp(meta) / (256 * VS))))[r] = (uint16_t)rm;
+      uint32_t j = 0;
+      for (int cc = 0; cc < 16; ++cc) {
+        uint8_t *dst = base + (r * 16 + cc) * VS;
+        if ((rm >> cc) & 1u) store_val<VK>(dst, val, p0 + (j++));
+        else store_zero<VK>(dst);
+      }
+    } else if (type == DBS_TILE_FORCE_CSR) {
+      ((uint16_t *)(base + PL_MASK))[r] = (uint16_t)rm;
+      base[PL_PTR + r] = (uint8_t)rp;
+      for (uint32_t j = 0; j < cnt; ++j) store_val<VK>(base + PL_FORCE_VAL + (rp + j) * VS, val, p0 + j);
+    } else {
+      // ForceCSC and patched CSR need every column's mask and start
+      if (type == DBS_TILE_FORCE_CSC) {
+        ((uint16_t *)(base + PL_MASK))[r] = (uint16_t)cm;
+        base[PL_PTR + r] = (uint8_t)cp;
+      } else {
+        ((uint16_t *)(base + PL_MASK))[r] = (uint16_t)rm;
+        base[PL_PTR + r] = (uint8_t)rp;
+        base[PL_CSR_COLPTR + r] = (uint8_t)cp;
+      }
+      uint32_t j = 0;
+#pragma unroll 1
+      for (int cc = 0; cc < 16; ++cc) {
+        const uint32_t cmc = (uint32_t)__shfl((int)cm, cc, 16);
+        const uint32_t cpc = (uint32_t)__shfl((int)cp, cc, 16);
+        if ((rm >> cc) & 1u) {
+          const uint32_t pos = cpc + (uint32_t)__popc(cmc & below_mask((uint32_t)r));
+          if (type == DBS_TILE_FORCE_CSC) {
+            store_val<VK>(base + PL_FORCE_VAL + pos * VS, val, p0 + j);
+          } else {
+            base[PL_CSR_RC + pos] = (uint8_t)((r << 4) | j);
+            store_val<VK>(base + csr_val_off(nnz) + (rp + j) * VS, val, p0 + j);
+          }
+          ++j;
+        }
+      }
+    }
+    ++t;
+  }
+}
+
+__global__ void k_iota(uint32_t *v, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) v[i] = (uint32_t)i;
+}
+
+__global__ void k_hist_cb(const uint32_t *t_cb, int64_t T, uint32_t *cnt) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < T) atomicAdd(&cnt[t_cb[i]], 1u);
+}
+
+__global__ void k_gather_rb(const uint32_t *csc2csr, const uint32_t *t_rb, int64_t T,
+                            uint32_t *csc_rb) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < T) csc_rb[i] = t_rb[csc2csr[i]];
+}
+
+DBS_DEV uint32_t seg_weight(uint32_t type, const dbs_build_options &o) {
+  return type == DBS_TILE_DENSE ? (uint32_t)o.seg_w_dense
+                                : type == DBS_TILE_COO ? (uint32_t)o.seg_w_coo : (uint32_t)o.seg_w_csr;
+}
+
+// Pull load balance (section 3.3.2): greedy weighted segments inside each row
+// block.  mode 0 counts, mode 1 writes.
+__global__ void k_segments(int32_t mb, const uint32_t *rb_ptr, const uint32_t *t_nt,
+                           dbs_build_options o, uint32_t *seg_cnt, const uint32_t *seg_off,
+                           uint32_t *segs, int mode) {
+  const int32_t rb = (int32_t)(blockIdx.x * blockDim.x + threadIdx.x);
+  if (rb >= mb) return;
+  const uint32_t t0 = rb_ptr[rb], t1 = rb_ptr[rb + 1];
+  uint32_t nseg = 0, acc = 0, start = t0;
+  uint32_t out = mode ? seg_off[rb] : 0;
+  const uint32_t split = (mode && seg_cnt[rb] > 1) ? SEG_SPLIT : 0u;
+  for (uint32_t t = t0; t < t1; ++t) {
+    acc += seg_weight(t_nt[t] >> 16, o);
+    if (acc >= (uint32_t)o.seg_cap) {
+      if (mode) {
+        uint32_t *s = segs + 4 * (uint64_t)(out + nseg);
+        s[0] = (uint32_t)rb | split;
+        s[1] = start;
+        s[2] = t + 1;
+        s[3] = 0;
+      }
+      ++nseg;
+      start = t + 1;
+      acc = 0;
+    }
+  }
+  if (start < t1) {
+    if (mode) {
+      uint32_t *s = segs + 4 * (uint64_t)(out + nseg);
+      s[0] = (uint32_t)rb | split;
+      s[1] = start;
+      s[2] = t1;
+      s[3] = 0;
+    }
+    ++nseg;
+  }
+  if (!mode) seg_cnt[rb] = nseg;
+}
+
+__global__ void k_type_stats(const uint32_t *t_nt, int64_t T, unsigned long long *st) {
+  __shared__ unsigned long long s[10];
+  if (threadIdx.x < 10) s[threadIdx.x] = 0;
+  __syncthreads();
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < T;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const uint32_t nt = t_nt[i];
+    atomicAdd(&s[nt >> 16], 1ull);
+    atomicAdd(&s[5 + (nt >> 16)], (unsigned long long)((nt & 0xFFFFu) + 1));
+  }
+  __syncthreads();
+  if (threadIdx.x < 10) atomicAdd(&st[threadIdx.x], s[threadIdx.x]);
+}
+
+inline unsigned nblocks(int64_t n, int b) { return (unsigned)((n + b - 1) / b); }
+
+int bits_for(uint32_t maxval) {
+  int b = 0;
+  while (b < 32 && (maxval >> b) != 0) ++b;
+  return b;
+}
+
+}  // namespace
+
+// temporaries of the build, freed on every exit path
+struct BuildTmp {
+  static constexpr int kMax = 32;
+  dbs_matrix *A;
+  void *p[kMax] = {nullptr};
+  size_t sz[kMax] = {0};
+  int k = 0;
+  explicit BuildTmp(dbs_matrix *a) : A(a) {}
+  hipError_t get(void **out, size_t bytes) {
+    if (k >= kMax) return hipErrorInvalidValue;
+    void *q = nullptr;
+    hipError_t e = dbs_dev_alloc(A, &q, bytes ? bytes : 1);
+    if (e != hipSuccess) return e;
+    p[k] = q;
+    sz[k] = bytes ? bytes : 1;
+    ++k;
+    *out = q;
+    return hipSuccess;
+  }
+  ~BuildTmp() {
+    for (int i = 0; i < k; ++i) dbs_dev_free(A, p[i], sz[i]);
+  }
+};
+
+#define BUILD_TRY(expr)                                                                     \
+  do {                                                                                      \
+    hipError_t e_ = DBS_NOTE(expr);                                                                 \
+    if (e_ != hipSuccess)                                                                   \
+      return (e_ == hipErrorOutOfMemory || e_ == hipErrorMemoryAllocation) ? DBS_ERR_OUT_OF_MEMORY \
+                                                                        : DBS_ERR_DEVICE;  \
+  } while (0)
+
+dbs_status dbs_build_impl(dbs_matrix *A, const int32_t *row_ptr, const int32_t *col_idx,
+                          const void *val, hipStream_t s) {
+  BuildTmp tmp(A);
+  const int32_t m = A->m, mb = A->mb, nb = A->nb;
+  const int64_t nnz = A->nnz;
+  const int vk = A->vk;
+
+  // --- validate the CSR on the device
+  uint32_t *flag;
+  BUILD_TRY(tmp.get((void **)&flag, 4));
+  BUILD_TRY(hipMemsetAsync(flag, 0, 4, s));
+  hipLaunchKernelGGL(k_validate, dim3(nblocks(m, BT)), dim3(BT), 0, s, m, A->n, nnz, row_ptr,
+                     col_idx, flag);
+  BUILD_TRY(hipGetLastError());
+  uint32_t hflag = 0;
+  BUILD_TRY(hipMemcpyAsync(&hflag, flag, 4, hipMemcpyDeviceToHost, s));
+  BUILD_TRY(hipStreamSynchronize(s));
+  if (hflag) return DBS_ERR_BAD_CSR;
+
+  // --- pass 1: tiles per row block, block-CSR row pointer
+  uint32_t *rb_cnt;
+  BUILD_TRY(tmp.get((void **)&rb_cnt, (size_t)mb * 4));
+  BUILD_TRY(dbs_dev_alloc(A, (void **)&A->rb_ptr, (size_t)(mb + 1) * 4));
+  void *stmp;
+  BUILD_TRY(tmp.get(&stmp, dbs_scan_tmp_bytes((int64_t)mb + 1)));
+  const unsigned gblocks = nblocks(mb, RB_PER_BLOCK);
+  hipLaunchKernelGGL(k_tile_count, dim3(gblocks), dim3(BT), 0, s, m, mb, row_ptr, col_idx, rb_cnt);
+  BUILD_TRY(hipGetLastError());
+  BUILD_TRY(dbs_scan_u32(rb_cnt, A->rb_ptr, mb, stmp, s));
+  uint32_t hT = 0;
+  BUILD_TRY(hipMemcpyAsync(&hT, A->rb_ptr + mb, 4, hipMemcpyDeviceToHost, s));
+  BUILD_TRY(hipStreamSynchronize(s));
+  const int64_t T = hT;
+  A->T = T;
+
+  // --- pass 2: classify tiles, payload sizes per section
+  uint32_t *t_rb, *t_nt;
+  uint64_t *sizes, *offs;
+  BUILD_TRY(dbs_dev_alloc(A, (void **)&A->t_cb, (size_t)T * 4 + 4));
+  BUILD_TRY(dbs_dev_alloc(A, (void **)&A->t_meta, (size_t)T * 8 + 8));
+  BUILD_TRY(tmp.get((void **)&t_rb, (size_t)T * 4 + 4));
+  BUILD_TRY(tmp.get((void **)&t_nt, (size_t)T * 4 + 4));
+  BUILD_TRY(tmp.get((void **)&sizes, (size_t)3 * T * 8 + 8));
+  BUILD_TRY(tmp.get((void **)&offs, (size_t)(3 * T + 1) * 8));
+  void *stmp3;
+  BUILD_TRY(tmp.get(&stmp3, dbs_scan_tmp_bytes(3 * T + 1)));
+  hipLaunchKernelGGL(k_tile_classify, dim3(gblocks), dim3(BT), 0, s, m, mb, row_ptr, col_idx,
+                     (const uint32_t *)A->rb_ptr, A->bopt, vk, T, A->t_cb, t_rb, t_nt, sizes);
+  BUILD_TRY(hipGetLastError());
+  BUILD_TRY(dbs_scan_u64(sizes, offs, 3 * T, stmp3, s));
+  uint64_t total = 0, dense_bytes = 0;
+  BUILD_TRY(hipMemcpyAsync(&total, offs + 3 * T, 8, hipMemcpyDeviceToHost, s));
+  BUILD_TRY(hipMemcpyAsync(&dense_bytes, offs + T, 8, hipMemcpyDeviceToHost, s));
+  BUILD_TRY(hipStreamSynchronize(s));
+  // Dense row masks after the three value sections (value matrices only)
+  A->dense_mask_off = (total + 127) & ~127ull;
+  if (vk != VK_PAT) total = A->dense_mask_off + 32ull * (dense_bytes / (256ull * (uint64_t)vk_size(vk)));
+  if (total >= (1ull << 40)) return DBS_ERR_UNSUPPORTED;
+  A->payload_bytes = (int64_t)total;
+  BUILD_TRY(dbs_dev_alloc(A, (void **)&A->payload, (size_t)total + 256));
+  if (T > 0) {
+    hipLaunchKernelGGL(k_pack_meta, dim3(nblocks(T, BT)), dim3(BT), 0, s, T, vk, t_nt, offs, A->t_meta);
+    BUILD_TRY(hipGetLastError());
+  }
+
+  // --- pass 3: payloads
+  if (vk == VK_F32)
+    hipLaunchKernelGGL(k_tile_fill<VK_F32>, dim3(gblocks), dim3(BT), 0, s, m, mb, row_ptr, col_idx, val,
+                       (const uint32_t *)A->rb_ptr, (const uint64_t *)A->t_meta, A->payload, A->dense_mask_off);
+  else if (vk == VK_BF16)
+    hipLaunchKernelGGL(k_tile_fill<VK_BF16>, dim3(gblocks), dim3(BT), 0, s, m, mb, row_ptr, col_idx, val,
+                       (const uint32_t *)A->rb_ptr, (const uint64_t *)A->t_meta, A->payload, A->dense_mask_off);
+  else
+    hipLaunchKernelGGL(k_tile_fill<VK_PAT>, dim3(gblocks), dim3(BT), 0, s, m, mb, row_ptr, col_idx, val,
+                       (const uint32_t *)A->rb_ptr, (const uint64_t *)A->t_meta, A->payload, A->dense_mask_off);
+  BUILD_TRY(hipGetLastError());
+
+  // --- block-level CSC view: stable sort of the tiles by column block
+  BUILD_TRY(dbs_dev_alloc(A, (void **)&A->cb_ptr, (size_t)(nb + 1) * 4));
+  BUILD_TRY(dbs_dev_alloc(A, (void **)&A->csc_rb, (size_t)T * 4 + 4));
+  BUILD_TRY(dbs_dev_alloc(A, (void **)&A->csc2csr, (size_t)T * 4 + 4));
+  uint32_t *keys, *keys_tmp, *vals_tmp, *cb_cnt;
+  void *rtmp;
+  BUILD_TRY(tmp.get((void **)&keys, (size_t)T * 4 + 4));
+  BUILD_TRY(tmp.get((void **)&keys_tmp, (size_t)T * 4 + 4));
+  BUILD_TRY(tmp.get((void **)&vals_tmp, (size_t)T * 4 + 4));
+  BUILD_TRY(tmp.get((void **)&cb_cnt, (size_t)nb * 4));
+  BUILD_TRY(tmp.get(&rtmp, dbs_radix_tmp_bytes(T)));
+  void *stmpn;
+  BUILD_TRY(tmp.get(&stmpn, dbs_scan_tmp_bytes((int64_t)nb + 1)));
+  BUILD_TRY(hipMemsetAsync(cb_cnt, 0, (size_t)nb * 4, s));
+  if (T > 0) {
+    BUILD_TRY(hipMemcpyAsync(keys, A->t_cb, (size_t)T * 4, hipMemcpyDeviceToDevice, s));
+    hipLaunchKernelGGL(k_iota, dim3(nblocks(T, BT)), dim3(BT), 0, s, A->csc2csr, T);
+    hipLaunchKernelGGL(k_hist_cb, dim3(nblocks(T, BT)), dim3(BT), 0, s, (const uint32_t *)A->t_cb, T, cb_cnt);
+    BUILD_TRY(hipGetLastError());
+    BUILD_TRY(dbs_radix_sort_pairs(keys, A->csc2csr, keys_tmp, vals_tmp, T, bits_for((uint32_t)(nb - 1)),
+                                   rtmp, s));
+    hipLaunchKernelGGL(k_gather_rb, dim3(nblocks(T, BT)), dim3(BT), 0, s, (const uint32_t *)A->csc2csr,
+                       (const uint32_t *)t_rb, T, A->csc_rb);
+    BUILD_TRY(hipGetLastError());
+  }
+  BUILD_TRY(dbs_scan_u32(cb_cnt, A->cb_ptr, nb, stmpn, s));
+
+  // --- pull segments
+  uint32_t *seg_cnt, *seg_off;
+  BUILD_TRY(tmp.get((void **)&seg_cnt, (size_t)mb * 4));
+  BUILD_TRY(tmp.get((void **)&seg_off, (size_t)(mb + 1) * 4));
+  hipLaunchKernelGGL(k_segments, dim3(nblocks(mb, BT)), dim3(BT), 0, s, mb, (const uint32_t *)A->rb_ptr,
+                     (const uint32_t *)t_nt, A->bopt, seg_cnt, (const uint32_t *)nullptr,
+                     (uint32_t *)nullptr, 0);
+  BUILD_TRY(hipGetLastError());
+  BUILD_TRY(dbs_scan_u32(seg_cnt, seg_off, mb, stmp, s));
+  uint32_t hS = 0;
+  BUILD_TRY(hipMemcpyAsync(&hS, seg_off + mb, 4, hipMemcpyDeviceToHost, s));
+  BUILD_TRY(hipStreamSynchronize(s));
+  A->nseg = hS;
+  BUILD_TRY(dbs_dev_alloc(A, (void **)&A->segs, (size_t)hS * 16 + 16));
+  hipLaunchKernelGGL(k_segments, dim3(nblocks(mb, BT)), dim3(BT), 0, s, mb, (const uint32_t *)A->rb_ptr,
+                     (const uint32_t *)t_nt, A->bopt, seg_cnt, (const uint32_t *)seg_off, A->segs, 1);
+  BUILD_TRY(hipGetLastError());
+
+  // --- statistics per format
+  unsigned long long *st;
+  BUILD_TRY(tmp.get((void **)&st, 10 * 8));
+  BUILD_TRY(hipMemsetAsync(st, 0, 80, s));
+  if (T > 0) {
+    hipLaunchKernelGGL(k_type_stats, dim3(nblocks(T, BT) < 1024u ? nblocks(T, BT) : 1024u), dim3(BT), 0, s,
+                       (const uint32_t *)t_nt, T, st);
+    BUILD_TRY(hipGetLastError());
+  }
+  unsigned long long hst[10];
+  BUILD_TRY(hipMemcpyAsync(hst, st, 80, hipMemcpyDeviceToHost, s));
+  BUILD_TRY(hipStreamSynchronize(s));
+  for (int i = 0; i < 5; ++i) {
+    A->st.tiles_by_format[i] = (int64_t)hst[i];
+    A->st.nnz_by_format[i] = (int64_t)hst[5 + i];
+  }
+  return DBS_OK;
+}

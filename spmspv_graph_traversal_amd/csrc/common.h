@@ -1,0 +1,218 @@
+// Shared definitions of the HIP library: the handle, the tile-payload layout
+// and wave64 helpers.  Citations refer to "DB-SpMSpV: Dual-View Blocked Sparse
+// Matrix-Sparse Vector Multiplication for Dynamic GPU Workloads" (arXiv
+// 2608.16308) by section / algorithm / figure.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/dbs.h"
+
+// ---------------------------------------------------------------------------
+// Geometry: 16x16 tiles and 16-element vector blocks (sections 3.2.1, 3.2.2).
+// ---------------------------------------------------------------------------
+#define DBS_TILE 16
+#define DBS_WAVE 64
+
+// value kinds of the payload
+enum { VK_F32 = 0, VK_BF16 = 1, VK_PAT = 2 };
+
+__host__ __device__ inline int vk_size(int vk) { return vk == VK_F32 ? 4 : vk == VK_BF16 ? 2 : 0; }
+__host__ __device__ inline uint32_t align_up(uint32_t x, uint32_t a) { return (x + a - 1) & ~(a - 1); }
+
+// ---------------------------------------------------------------------------
+// Tile payload layout (one arena, three sections: Dense | mask-based | COO).
+// Offsets are bytes from the tile's payload start `vp`.
+//
+//   COO (values):    coord u8[nnz] (row<<4 | col, row-major) @0,
+//                    values @align4(nnz)
+//   COO (pattern):   coord u8[nnz] @0
+//   Dense:           values[256] row-major @0 (tile start is 512/1024-B aligned)
+//   ForceCSR:        row_mask u16[16] @0, row_ptr u8[16] @32, values @48
+//                    (row-major, ascending column within a row)
+//   ForceCSC:        col_mask u16[16] @0, col_ptr u8[16] @32, values @48
+//                    (column-major, ascending row within a column)
+//   patched CSR:     row_mask u16[16] @0, row_ptr u8[16] @32, col_ptr u8[16] @48,
+//                    row_idx_csc2csr u8[nnz] @64 (column-major; byte = row<<4 |
+//                    index of the entry inside its row), values
+//                    @64+align16(nnz) row-major
+//   any non-COO tile of a pattern matrix:
+//                    row_mask u16[16] @0, col_mask u16[16] @32
+// Dense tiles store absent entries as zeros, so their structure (needed by
+// the OR-AND semiring, where stored zeros count) lives in a fourth section
+// after the COO one: row_mask u16[16] per Dense tile, at
+// dense_mask_off + 32 * (vp / (256 * value size)).
+// Bit k of a row mask is local column k; bit k of a column mask is local row k
+// (Figure 5 caption: a row mask of 10 = 0b1010 holds columns 1 and 3).
+// ---------------------------------------------------------------------------
+#define PL_MASK 0
+#define PL_PTR 32
+#define PL_FORCE_VAL 48
+#define PL_CSR_COLPTR 48
+#define PL_CSR_RC 64
+#define PL_PAT_COLMASK 32
+
+__host__ __device__ inline uint32_t coo_val_off(uint32_t nnz) { return align_up(nnz, 4); }
+__host__ __device__ inline uint32_t csr_val_off(uint32_t nnz) { return PL_CSR_RC + align_up(nnz, 16); }
+
+// section of a tile in the arena: 0 Dense, 1 mask-based, 2 COO
+__host__ __device__ inline int tile_section(int type, int vk) {
+  if (type == DBS_TILE_COO) return 2;
+  if (type == DBS_TILE_DENSE && vk != VK_PAT) return 0;
+  return 1;
+}
+
+__host__ __device__ inline uint32_t tile_payload_bytes(int type, uint32_t nnz, int vk) {
+  const uint32_t vs = (uint32_t)vk_size(vk);
+  if (type == DBS_TILE_COO) return vk == VK_PAT ? nnz : coo_val_off(nnz) + align_up(nnz * vs, 4);
+  if (vk == VK_PAT) return 64;
+  if (type == DBS_TILE_DENSE) return 256 * vs;
+  if (type == DBS_TILE_CSR) return align_up(csr_val_off(nnz) + nnz * vs, 16);
+  return align_up(PL_FORCE_VAL + nnz * vs, 16);  // ForceCSR / ForceCSC
+}
+
+// Tile metadata word: payload offset (40 bits) | (nnz-1) << 40 | format << 48.
+__host__ __device__ inline uint64_t meta_pack(uint64_t vp, uint32_t nnz, uint32_t type) {
+  return vp | ((uint64_t)(nnz - 1) << 40) | ((uint64_t)type << 48);
+}
+__host__ __device__ inline uint64_t meta_vp(uint64_t m) { return m & ((1ull << 40) - 1); }
+__host__ __device__ inline uint32_t meta_nnz(uint64_t m) { return (uint32_t)((m >> 40) & 0xFF) + 1; }
+__host__ __device__ inline uint32_t meta_type(uint64_t m) { return (uint32_t)((m >> 48) & 0x7); }
+
+// Pull segment descriptor: {row block | split << 31, first tile, end tile, 0}.
+#define SEG_SPLIT 0x80000000u
+
+// ---------------------------------------------------------------------------
+// The handle.
+// ---------------------------------------------------------------------------
+struct dbs_matrix {
+  int device;
+  int32_t m, n, mb, nb;
+  int64_t nnz, T, nseg;
+  dbs_dtype dtype;
+  int vk;
+  dbs_build_options bopt;
+
+  // dual-view blocked format (device)
+  uint32_t *rb_ptr;     // [mb+1] block-CSR row pointer
+  uint32_t *t_cb;       // [T]    block-CSR column block of each tile (primary order)
+  uint64_t *t_meta;     // [T]    payload offset | nnz | format
+  uint32_t *cb_ptr;     // [nb+1] block-CSC column pointer
+  uint32_t *csc_rb;     // [T]    block-CSC row block
+  uint32_t *csc2csr;    // [T]    primary tile id of each CSC position
+  uint8_t *payload;     // arena
+  uint64_t dense_mask_off;  // start of the Dense row-mask section in the arena
+  uint32_t *segs;       // [4*nseg] pull segments
+  int64_t payload_bytes;
+
+  // per-call scratch (device)
+  uint32_t *xmask;       // [nb] (epoch << 16) | blk_x_mask
+  void *xd;              // [n] staged x values (only active positions are meaningful)
+  uint32_t *act_list;    // [nb] compacted nonzero vector blocks
+  uint64_t *chunks;      // [max_chunks] push work: column block | chunk index << 32
+  int64_t max_chunks;
+  uint32_t *ctr;         // [2][8] double-buffered per-call counters
+  uint32_t epoch;
+  int cbuf;
+
+  // BFS scratch (allocated on first use)
+  uint32_t *bfs_bm;      // 3 frontier bitmaps of nb/2 words (16 bits per vertex block)
+  uint32_t *bfs_vis;     // visited bitmap
+  uint32_t *bfs_list;    // 3 lists of nb vertex blocks
+  uint64_t *bfs_chunks;  // 3 chunk lists
+  uint32_t *bfs_ctr;     // 3 x 8 counters
+  uint32_t *bfs_host;    // pinned host mirror of a counter
+
+  // options and statistics
+  int64_t opt[8];
+  dbs_stats st;
+  hipStream_t last_stream;
+  hipEvent_t ev[6];
+  int timing_pending;    // which events hold a measurement
+  int64_t mem_now, mem_peak;
+};
+
+// ---------------------------------------------------------------------------
+// Host-side helpers implemented in the .hip files.
+// ---------------------------------------------------------------------------
+hipError_t dbs_dev_alloc(dbs_matrix *A, void **p, size_t bytes);
+void dbs_dev_free(dbs_matrix *A, void *p, size_t bytes);
+
+// exclusive scans writing n+1 values (out[n] = total)
+hipError_t dbs_scan_u32(const uint32_t *in, uint32_t *out, int64_t n, void *tmp, hipStream_t s);
+hipError_t dbs_scan_u64(const uint64_t *in, uint64_t *out, int64_t n, void *tmp, hipStream_t s);
+size_t dbs_scan_tmp_bytes(int64_t n);
+// stable LSD radix sort of (key, value) pairs by key < 2^bits
+hipError_t dbs_radix_sort_pairs(uint32_t *keys, uint32_t *vals, uint32_t *keys_tmp,
+                                uint32_t *vals_tmp, int64_t n, int bits, void *tmp,
+                                hipStream_t s);
+size_t dbs_radix_tmp_bytes(int64_t n);
+
+dbs_status dbs_build_impl(dbs_matrix *A, const int32_t *row_ptr, const int32_t *col_idx,
+                          const void *val, hipStream_t s);
+dbs_status dbs_spmspv_impl(dbs_matrix *A, int32_t nnz_x, const int32_t *x_idx,
+                           const void *x_val, const void *x_dense, dbs_semiring sr, void *y,
+                           hipStream_t s);
+dbs_status dbs_bfs_impl(dbs_matrix *A, int32_t src, int32_t *levels, hipStream_t s);
+
+// Returns e; with DBS_VERBOSE=1 in the environment a failing call is printed
+// to stderr with its source location.
+hipError_t dbs_note(hipError_t e, const char *file, int line);
+#define DBS_NOTE(expr) dbs_note((expr), __FILE__, __LINE__)
+
+#define DBS_HIP_TRY(expr)                                \
+  do {                                                   \
+    hipError_t e_ = DBS_NOTE(expr);                      \
+    if (e_ != hipSuccess) return e_;                     \
+  } while (0)
+
+// ---------------------------------------------------------------------------
+// Device helpers (wave64).
+// ---------------------------------------------------------------------------
+#ifdef __HIP_DEVICE_COMPILE__
+#define DBS_DEV __device__ __forceinline__
+#else
+#define DBS_DEV __device__ inline
+#endif
+
+DBS_DEV uint32_t below_mask(uint32_t k) { return (1u << k) - 1u; }
+
+// reductions inside aligned groups of `W` lanes
+template <int W>
+DBS_DEV uint32_t group_min_u32(uint32_t v) {
+#pragma unroll
+  for (int o = W / 2; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, W));
+  return v;
+}
+template <int W>
+DBS_DEV uint32_t group_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = W / 2; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, W));
+  return v;
+}
+template <int W>
+DBS_DEV uint32_t group_sum_u32(uint32_t v) {
+#pragma unroll
+  for (int o = W / 2; o > 0; o >>= 1) v += (uint32_t)__shfl_xor((int)v, o, W);
+  return v;
+}
+template <int W>
+DBS_DEV uint32_t group_or_u32(uint32_t v) {
+#pragma unroll
+  for (int o = W / 2; o > 0; o >>= 1) v |= (uint32_t)__shfl_xor((int)v, o, W);
+  return v;
+}
+// inclusive prefix sum inside aligned groups of W lanes
+template <int W>
+DBS_DEV uint32_t group_incl_scan_u32(uint32_t v) {
+  const int l = __lane_id() & (W - 1);
+#pragma unroll
+  for (int o = 1; o < W; o <<= 1) {
+    uint32_t t = (uint32_t)__shfl_up((int)v, o, W);
+    if (l >= o) v += t;
+  }
+  return v;
+}
+
+DBS_DEV float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }

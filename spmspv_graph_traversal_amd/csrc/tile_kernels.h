@@ -1,0 +1,255 @@
+// Per-tile wave64 microkernels (section 3.3.3 of "DB-SpMSpV: Dual-View Blocked
+// Sparse Matrix-Sparse Vector Multiplication for Dynamic GPU Workloads";
+// Algorithms 2-5) and the COO lane-per-tile path.
+//
+// A 64-lane wave covers a whole 16x16 tile at once: lane L = q*16 + r works
+// on row r and quarter q (q = L >> 4).  Where the pages split a 32-lane warp
+// in two halves or pairs, the wave splits in four; row partials are merged
+// across the quarters with xor-16 and xor-32 exchanges, after which lanes
+// 0..15 hold the 16 row results of the tile.
+//
+// x values of the tile's vector block are staged in LDS (one 16-entry slot
+// per wave) so that lanes with different amounts of work can read them.
+#pragma once
+
+#include "common.h"
+
+template <int VK>
+DBS_DEV float load_a(const uint8_t *p) {
+  if (VK == VK_F32) return *(const float *)p;
+  if (VK == VK_BF16) return bf16_to_f32(*(const uint16_t *)p);
+  return 1.0f;
+}
+
+template <int VK>
+DBS_DEV float load_x(const void *xd, int64_t j) {
+  if (VK == VK_F32) return ((const float *)xd)[j];
+  if (VK == VK_BF16) return bf16_to_f32(((const uint16_t *)xd)[j]);
+  return 1.0f;
+}
+
+DBS_DEV float quarter_merge(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+// remove the lowest k set bits
+DBS_DEV uint32_t drop_low_bits(uint32_t v, int k) {
+  for (int i = 0; i < k; ++i) v &= v - 1u;
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// PLUS_TIMES microkernels.  `m` is the tile's blk_x_mask, sx the staged x
+// values (inactive entries hold 0).  Return: row r's partial in every lane
+// with that r (use lanes 0..15).
+// ---------------------------------------------------------------------------
+
+// Dense, row-major (Algorithm 4): lane (q, r) loads row r, columns 4q..4q+3
+// with one 16-B (fp32) or 8-B (bf16) load; the wave reads the tile with a
+// single fully coalesced access.  The same kernel serves push, where the
+// pages transpose through shared memory to reach columns contiguously: here
+// every lane already holds its slice of each row.
+template <int VK>
+DBS_DEV float mk_dense(const uint8_t *base, uint32_t m, const float *sx, int q, int r) {
+  float a[4];
+  if (VK == VK_F32) {
+    const float4 v = *(const float4 *)(base + (r * 16 + 4 * q) * 4);
+    a[0] = v.x; a[1] = v.y; a[2] = v.z; a[3] = v.w;
+  } else {
+    const uint2 v = *(const uint2 *)(base + (r * 16 + 4 * q) * 2);
+    a[0] = __uint_as_float(v.x << 16);
+    a[1] = __uint_as_float(v.x & 0xFFFF0000u);
+    a[2] = __uint_as_float(v.y << 16);
+    a[3] = __uint_as_float(v.y & 0xFFFF0000u);
+  }
+  float part = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int c = 4 * q + k;
+    if ((m >> c) & 1u) part += a[k] * sx[c];
+  }
+  return quarter_merge(part);
+}
+
+// ForceCSR pull (Algorithm 2): four interleaved lanes per row; lane q takes
+// the active columns of rank q, q+4, ... ; value position = row_ptr[r] +
+// popcount of the row mask below the column.
+template <int VK>
+DBS_DEV float mk_force_csr(const uint8_t *base, uint32_t val_off, uint32_t m, const float *sx,
+                           int q, int r) {
+  constexpr int VS = VK == VK_F32 ? 4 : 2;
+  const uint32_t rmk = ((const uint16_t *)(base + PL_MASK))[r];
+  const uint32_t rp = base[PL_PTR + r];
+  uint32_t act = drop_low_bits(rmk & m, q);
+  float part = 0.0f;
+  while (act) {
+    const uint32_t c = (uint32_t)__ffs(act) - 1u;
+    const uint32_t off = rp + (uint32_t)__popc(rmk & below_mask(c));
+    part += load_a<VK>(base + val_off + off * VS) * sx[c];
+    act = drop_low_bits(act, 4);
+  }
+  return quarter_merge(part);
+}
+
+// ForceCSC push (Algorithm 3): lane (q, r) scans the active columns of
+// quarter q (columns 4q..4q+3) and tests bit r of each column mask; value
+// position = col_ptr[c] + popcount of the column mask below the row.
+template <int VK>
+DBS_DEV float mk_force_csc(const uint8_t *base, uint32_t m, const float *sx, int q, int r) {
+  constexpr int VS = VK == VK_F32 ? 4 : 2;
+  uint32_t act = m & (0xFu << (4 * q));
+  float part = 0.0f;
+  while (act) {
+    const uint32_t c = (uint32_t)__ffs(act) - 1u;
+    const uint32_t cm = ((const uint16_t *)(base + PL_MASK))[c];
+    if ((cm >> r) & 1u) {
+      const uint32_t off = base[PL_PTR + c] + (uint32_t)__popc(cm & below_mask((uint32_t)r));
+      part += load_a<VK>(base + PL_FORCE_VAL + off * VS) * sx[c];
+    }
+    act &= act - 1u;
+  }
+  return quarter_merge(part);
+}
+
+// Patched CSR, column (push) variant: for each active column c the entries
+// col_ptr[c] .. col_ptr[c+1] of row_idx_csc2csr give (row, index in row);
+// the value sits at row_ptr[row] + index, so the row-major value array serves
+// both directions.  Quarter q takes the active columns of rank q, q+4, ...;
+// lane (q, e) takes entry e of that column.  Rows inside one column are
+// distinct, so the per-quarter LDS partials never see two lanes on one
+// address.
+template <int VK>
+DBS_DEV float mk_csr_push(const uint8_t *base, uint32_t nnz, uint32_t m, const float *sx,
+                          float *spart /* [4][16] of this wave */, int q, int r) {
+  constexpr int VS = VK == VK_F32 ? 4 : 2;
+  const uint32_t voff = csr_val_off(nnz);
+  spart[q * 16 + r] = 0.0f;
+  __syncwarp();
+  uint32_t act = drop_low_bits(m, q);
+  // every lane runs the same number of rounds: that of quarter 0 (the most)
+  uint32_t rounds = ((uint32_t)__popc(m) + 3u) >> 2;
+  for (uint32_t it = 0; it < rounds; ++it) {
+    if (act) {
+      const uint32_t c = (uint32_t)__ffs(act) - 1u;
+      const uint32_t start = base[PL_CSR_COLPTR + c];
+      const uint32_t end = c < 15 ? base[PL_CSR_COLPTR + c + 1] : nnz;
+      if (start + (uint32_t)r < end) {
+        const uint32_t rc = base[PL_CSR_RC + start + r];
+        const uint32_t row = rc >> 4, j = rc & 15u;
+        const uint32_t off = base[PL_PTR + row] + j;
+        spart[q * 16 + row] += load_a<VK>(base + voff + off * VS) * sx[c];
+      }
+      act = drop_low_bits(act, 4);
+    }
+    __syncwarp();
+  }
+  return quarter_merge(spart[q * 16 + r]);
+}
+
+// ---------------------------------------------------------------------------
+// OR_AND microkernels: 16-bit mask of rows with a stored entry in an active
+// column (wave-uniform result).
+// ---------------------------------------------------------------------------
+DBS_DEV uint32_t mk_bool_rows(const uint16_t *row_mask, uint32_t m, int lane) {
+  uint32_t f = 0;
+  if (lane < 16) f = (((uint32_t)row_mask[lane] & m) != 0u) ? (1u << lane) : 0u;
+  return group_or_u32<64>(f);
+}
+
+// Algorithm 5 (Boolean ForceCSC push): OR of the masks of the active columns
+DBS_DEV uint32_t mk_bool_cols(const uint16_t *col_mask, uint32_t m, int lane) {
+  uint32_t f = 0;
+  if (lane < 16 && ((m >> lane) & 1u)) f = col_mask[lane];
+  return group_or_u32<64>(f);
+}
+
+// ---------------------------------------------------------------------------
+// Tile dispatch.  `dense_mask` points at the Dense tile's row masks (value
+// matrices, OR_AND only).
+// ---------------------------------------------------------------------------
+template <int VK>
+DBS_DEV float tile_plus(const uint8_t *base, uint32_t type, uint32_t nnz, uint32_t m,
+                        const float *sx, float *spart, int local_cutoff, int lane) {
+  const int q = lane >> 4, r = lane & 15;
+  if (type == DBS_TILE_DENSE) return mk_dense<VK>(base, m, sx, q, r);
+  if (type == DBS_TILE_FORCE_CSR) return mk_force_csr<VK>(base, PL_FORCE_VAL, m, sx, q, r);
+  if (type == DBS_TILE_FORCE_CSC) return mk_force_csc<VK>(base, m, sx, q, r);
+  // patched CSR: local choice from the number of active x entries (section 3.3.3)
+  if (__popc(m) >= local_cutoff) return mk_force_csr<VK>(base, csr_val_off(nnz), m, sx, q, r);
+  return mk_csr_push<VK>(base, nnz, m, sx, spart, q, r);
+}
+
+template <int VK>
+DBS_DEV uint32_t tile_or(const uint8_t *base, const uint8_t *dense_mask, uint32_t type, uint32_t m,
+                         int lane) {
+  if (VK == VK_PAT) {
+    if (type == DBS_TILE_FORCE_CSC) return mk_bool_cols((const uint16_t *)(base + PL_PAT_COLMASK), m, lane);
+    return mk_bool_rows((const uint16_t *)(base + PL_MASK), m, lane);
+  }
+  if (type == DBS_TILE_DENSE) return mk_bool_rows((const uint16_t *)dense_mask, m, lane);
+  if (type == DBS_TILE_FORCE_CSC) return mk_bool_cols((const uint16_t *)(base + PL_MASK), m, lane);
+  return mk_bool_rows((const uint16_t *)(base + PL_MASK), m, lane);  // ForceCSR, CSR
+}
+
+// ---------------------------------------------------------------------------
+// COO (section 3.3.3: scan the packed coordinates), one tile per lane.
+// ---------------------------------------------------------------------------
+// PLUS_TIMES, accumulated into the lane's 16 row registers
+template <int VK>
+DBS_DEV void coo_plus(const uint8_t *base, uint32_t nnz, uint32_t m, const void *xd, int64_t xbase,
+                      float (&acc)[16]) {
+  constexpr int VS = VK == VK_F32 ? 4 : 2;
+  const uint8_t *vals = base + coo_val_off(nnz);
+  for (uint32_t e = 0; e < nnz; ++e) {
+    const uint32_t rc = base[e];
+    const uint32_t c = rc & 15u;
+    if ((m >> c) & 1u) {
+      const uint32_t rr = rc >> 4;
+      const float t = load_a<VK>(vals + e * VS) * load_x<VK>(xd, xbase + c);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) acc[k] += (rr == (uint32_t)k) ? t : 0.0f;
+    }
+  }
+}
+
+DBS_DEV uint32_t coo_or(const uint8_t *base, uint32_t nnz, uint32_t m) {
+  uint32_t f = 0;
+  for (uint32_t e = 0; e < nnz; ++e) {
+    const uint32_t rc = base[e];
+    if ((m >> (rc & 15u)) & 1u) f |= 1u << (rc >> 4);
+  }
+  return f;
+}
+
+// Sum of the 16 per-lane row registers over the wave; row k's total ends in
+// lane k (lanes 0..15).  Recursive halving: each of the first four exchange
+// rounds keeps half of the rows, then two rounds finish the sum.
+DBS_DEV float wave_rows_reduce(float (&acc)[16], int lane) {
+  float v8[8], v4[4], v2[2];
+  const bool h5 = lane & 32, h4 = lane & 16, h3 = lane & 8, h2 = lane & 4;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float keep = h5 ? acc[8 + i] : acc[i];
+    const float send = h5 ? acc[i] : acc[8 + i];
+    v8[i] = keep + __shfl_xor(send, 32);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float keep = h4 ? v8[4 + i] : v8[i];
+    const float send = h4 ? v8[i] : v8[4 + i];
+    v4[i] = keep + __shfl_xor(send, 16);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const float keep = h3 ? v4[2 + i] : v4[i];
+    const float send = h3 ? v4[i] : v4[2 + i];
+    v2[i] = keep + __shfl_xor(send, 8);
+  }
+  float v = (h2 ? v2[1] : v2[0]) + __shfl_xor(h2 ? v2[0] : v2[1], 4);
+  v += __shfl_xor(v, 2);
+  v += __shfl_xor(v, 1);
+  // lanes 4k..4k+3 hold row k
+  return __shfl(v, (lane & 15) * 4);
+}

@@ -1,0 +1,156 @@
+"""GPU format builder vs the oracle's tile view (bit-exact indices) and a full
+round trip of the payload back to the input CSR."""
+import numpy as np
+import pytest
+
+import oracle as orc
+from gpu_helpers import bf16_csr_of, build, csr_of, mixed_tile_dense, options
+from synth import csr_from_dense, decode_weight_csr, rmat_csr, rng_for, uniform_csr
+from format_decode import decode
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dbs():
+    import spmspv_graph_traversal_amd as d
+
+    return d
+
+
+def _arrays(dbs, A):
+    return {
+        "rb_ptr": dbs.dbs_copy_array(A, dbs.DBS_ARR_RB_PTR),
+        "t_cb": dbs.dbs_copy_array(A, dbs.DBS_ARR_T_CB),
+        "t_meta": dbs.dbs_copy_array(A, dbs.DBS_ARR_T_META),
+        "cb_ptr": dbs.dbs_copy_array(A, dbs.DBS_ARR_CB_PTR),
+        "csc_rb": dbs.dbs_copy_array(A, dbs.DBS_ARR_CSC_RB),
+        "csc2csr": dbs.dbs_copy_array(A, dbs.DBS_ARR_CSC2CSR),
+        "payload": dbs.dbs_copy_array(A, dbs.DBS_ARR_PAYLOAD),
+        "segs": dbs.dbs_copy_array(A, dbs.DBS_ARR_SEGMENTS).reshape(-1, 4),
+    }
+
+
+def check_format(dbs, m, n, rp, ci, vbits, dtype, vk, opt=None, th=(32, 128, 2.0), force=-1, cap=64):
+    A = build(dbs, m, n, rp, ci, vbits, dtype, options=opt)
+    ar = _arrays(dbs, A)
+    tv = orc.tile_view(m, n, rp, ci, th[0], th[1], th[2])
+    np.testing.assert_array_equal(ar["rb_ptr"], tv["rb_ptr"])
+    np.testing.assert_array_equal(ar["t_cb"], tv["t_cb"])
+    np.testing.assert_array_equal(ar["cb_ptr"], tv["cb_ptr"])
+    np.testing.assert_array_equal(ar["csc_rb"], tv["csc_rb"])
+    np.testing.assert_array_equal(ar["csc2csr"], tv["csc2csr"])
+    st = dbs.dbs_get_stats(A)
+    exp_types = tv["t_type"] if force < 0 else np.full(tv["T"], force)
+    n_dense = int(np.count_nonzero(exp_types == orc.DENSE))
+    rows, cols, vals, typ, nnz = decode(ar, vk, n_dense)
+    np.testing.assert_array_equal(typ, exp_types)
+    np.testing.assert_array_equal(nnz, tv["t_nnz"])
+    # round trip: same entries, same value bits
+    order = np.lexsort((cols, rows))
+    ref_rows = np.repeat(np.arange(m), np.diff(rp))
+    np.testing.assert_array_equal(rows[order], ref_rows)
+    np.testing.assert_array_equal(cols[order], ci)
+    if vals is not None:
+        ref = np.asarray(vbits).view(np.uint32 if vk == 0 else np.uint16)
+        np.testing.assert_array_equal(vals[order], ref)
+    # pull segments follow the weighted rule of the oracle
+    srb, s0, s1 = orc.segments(tv["rb_ptr"], exp_types, cap=cap)
+    segs = ar["segs"]
+    np.testing.assert_array_equal(segs[:, 0] & 0x7FFFFFFF, srb)
+    np.testing.assert_array_equal(segs[:, 1], s0)
+    np.testing.assert_array_equal(segs[:, 2], s1)
+    per_rb = np.bincount(srb, minlength=(m + 15) // 16)
+    np.testing.assert_array_equal(segs[:, 0] >> 31, (per_rb[srb] > 1).astype(np.uint32))
+    for f in range(5):
+        assert st["tiles_by_format"][f] == int(np.count_nonzero(exp_types == f))
+        assert st["nnz_by_format"][f] == int(tv["t_nnz"][exp_types == f].sum())
+    assert st["tiles"] == tv["T"] and st["segments"] == srb.shape[0]
+    return A, tv
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_mixed_formats_f32(dbs, seed):
+    a = mixed_tile_dense(seed)
+    rp, ci, v = csr_of(a)
+    _, tv = check_format(dbs, a.shape[0], a.shape[1], rp, ci, v, dbs.DBS_F32, 0)
+    assert set(np.unique(tv["t_type"])) == {0, 1, 2, 3, 4}
+
+
+def test_mixed_formats_bf16_and_pattern(dbs):
+    a = mixed_tile_dense(7)
+    rp, ci, bits = bf16_csr_of(a)
+    check_format(dbs, a.shape[0], a.shape[1], rp, ci, bits, dbs.DBS_BF16, 1)
+    check_format(dbs, a.shape[0], a.shape[1], rp, ci, None, dbs.DBS_PATTERN, 2)
+
+
+def test_figure5_views(dbs, golden_dir):
+    import os
+
+    a = np.zeros((48, 48), np.float32)
+    with open(os.path.join(golden_dir, "fig5_block_views.txt")) as f:
+        cells = [ln.split("=", 1)[1].split() for ln in f if ln.startswith("tiles_rb_cb")][0]
+    for cell in cells:
+        rb, cb = map(int, cell.split(","))
+        a[rb * 16 + 3, cb * 16 + 5] = 1.0
+    rp, ci, v = csr_of(a)
+    A, _ = check_format(dbs, 48, 48, rp, ci, v, dbs.DBS_F32, 0)
+    np.testing.assert_array_equal(dbs.dbs_copy_array(A, dbs.DBS_ARR_CB_PTR), [0, 2, 5, 7])
+    np.testing.assert_array_equal(dbs.dbs_copy_array(A, dbs.DBS_ARR_CSC2CSR), [0, 4, 1, 2, 5, 3, 6])
+
+
+def test_uniform_tiny_config(dbs):
+    rp, ci, v = uniform_csr(4096, 4096, 16, rng_for("tiny"))
+    _, tv = check_format(dbs, 4096, 4096, rp, ci, v, dbs.DBS_F32, 0)
+    assert np.all(tv["t_type"] == orc.COO)
+
+
+def test_rmat_pattern(dbs):
+    rp, ci = rmat_csr(11, 16, rng_for("test", 600))
+    check_format(dbs, 2048, 2048, rp, ci, None, dbs.DBS_PATTERN, 2)
+
+
+def test_decode_weight_bf16(dbs):
+    rp, ci, bits = decode_weight_csr(200, 330, 0.5, rng_for("test", 601))
+    _, tv = check_format(dbs, 200, 330, rp, ci, bits, dbs.DBS_BF16, 1)
+    assert set(np.unique(tv["t_type"])) >= {orc.DENSE, orc.CSR}
+
+
+@pytest.mark.parametrize("force", [0, 1, 2, 3, 4])
+def test_forced_formats(dbs, force):
+    a = mixed_tile_dense(3)
+    rp, ci, v = csr_of(a)
+    opt = options(dbs, force_format=force)
+    check_format(dbs, a.shape[0], a.shape[1], rp, ci, v, dbs.DBS_F32, 0, opt=opt, force=force)
+
+
+def test_thresholds_and_cap_options(dbs):
+    a = mixed_tile_dense(4)
+    rp, ci, v = csr_of(a)
+    opt = options(dbs, th0=20, th1=100, th2_num=3, th2_den=2, seg_cap=7)
+    check_format(dbs, a.shape[0], a.shape[1], rp, ci, v, dbs.DBS_F32, 0, opt=opt, th=(20, 100, 1.5), cap=7)
+
+
+def test_empty_rows_cols_and_empty_matrix(dbs):
+    a = np.zeros((70, 90), np.float32)
+    a[5, 80] = 1.0
+    a[69, 0] = -2.0
+    rp, ci, v = csr_of(a)
+    check_format(dbs, 70, 90, rp, ci, v, dbs.DBS_F32, 0)
+    rp0 = np.zeros(34, np.int32)
+    A = build(dbs, 33, 17, rp0, np.zeros(0, np.int32), np.zeros(0, np.float32), dbs.DBS_F32)
+    st = dbs.dbs_get_stats(A)
+    assert st["tiles"] == 0 and st["segments"] == 0
+
+
+def test_bad_csr_is_rejected(dbs):
+    rp = np.array([0, 2, 1, 3], np.int32)  # not monotone
+    ci = np.array([0, 1, 2], np.int32)
+    with pytest.raises(dbs.DBSError) as e:
+        build(dbs, 3, 4, rp, ci, np.ones(3, np.float32), dbs.DBS_F32)
+    assert e.value.status == dbs.DBS_ERR_BAD_CSR
+    rp = np.array([0, 2, 3], np.int32)
+    for bad in ([1, 1, 0], [0, 5, 1], [-1, 0, 1]):  # duplicate, out of range, negative
+        with pytest.raises(dbs.DBSError) as e:
+            build(dbs, 2, 4, rp, np.array(bad, np.int32), np.ones(3, np.float32), dbs.DBS_F32)
+        assert e.value.status == dbs.DBS_ERR_BAD_CSR
