@@ -1,0 +1,429 @@
+#!/usr/bin/env python3
+"""Benchmark of the DB-SpMSpV hot path on one MI355X.
+
+Headline step: the R-MAT scale-20 workload (2^20 vertices, edge factor 16,
+a=0.57 b=0.19 c=0.19, symmetrized, no self-loops or duplicates) under the
+OR-AND semiring, one SpMSpV call for each x density of the sweep 0.01%, 0.1%,
+1%, 10%, 50% (positions uniform, seeded).  `value` is the step's effective
+bandwidth: algorithmic bytes of all its kernels (byte model below) over the
+step's wall time, inputs resident in HBM.
+
+Also reported (nested under "extra"): per-density numbers, BFS on R-MAT
+scale 22 from 64 seeded sources of the largest component (GTEPS), and the
+single-token decode layers 11008x4096 / 4096x11008 (µs per call, warm and
+with rotating copies to defeat the on-package cache).
+
+Byte model (bytes a kernel must move for the path it takes; per call):
+  pull     16*segments + 4*T (column block of every tile) + 4*N_blk (masks)
+           + sum over tiles with an active column block of (8 + payload)
+           + |y|
+  push     8*chunks + 8*active blocks + sum over tiles of active column
+           blocks of (4 + 4 + 8 + payload)
+  metadata 4*nnz_x (+ 2*value size*nnz_x for plus-times) + 8*active blocks
+           + 8*chunks + |y| (the output is cleared there)
+payload = stored bytes of the tile (pattern tiles other than COO: the 32 B
+of masks one direction reads).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "SpMSpV effective GB/s (% of HBM peak) vs x density; BFS GTEPS; decode-layer µs"
+HBM_PEAK_GBS = 8000.0
+DENSITIES = [0.0001, 0.001, 0.01, 0.1, 0.5]
+KERNEL_SRC = ["spmspv.hip", "tile_kernels.h", "common.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------- byte model
+def _align(x, a):
+    return (x + a - 1) // a * a
+
+
+def payload_read_bytes(types, nnz, vk):
+    """Bytes of each tile's payload one microkernel reads (see module doc)."""
+    vs = {0: 4, 1: 2, 2: 0}[vk]
+    types = types.astype(np.int64)
+    nnz = nnz.astype(np.int64)
+    if vk == 2:
+        return np.where(types == 0, nnz, 32)
+    coo = _align(nnz, 4) + _align(nnz * vs, 4)
+    dense = np.full_like(nnz, 256 * vs)
+    force = _align(48 + nnz * vs, 16)
+    csr = _align(64 + _align(nnz, 16) + nnz * vs, 16)
+    return np.select([types == 0, types == 1, types == 4], [coo, dense, csr], force)
+
+
+class Format:
+    """Host copy of the index views needed by the byte model."""
+
+    def __init__(self, dbs, A, vk):
+        st = dbs.dbs_get_stats(A)
+        self.T = st["tiles"]
+        self.nseg = st["segments"]
+        self.nb = st["nb"]
+        self.m = st["m"]
+        meta = dbs.dbs_copy_array(A, dbs.DBS_ARR_T_META)
+        self.t_cb = dbs.dbs_copy_array(A, dbs.DBS_ARR_T_CB).astype(np.int64)
+        self.cb_ptr = dbs.dbs_copy_array(A, dbs.DBS_ARR_CB_PTR).astype(np.int64)
+        csc2csr = dbs.dbs_copy_array(A, dbs.DBS_ARR_CSC2CSR).astype(np.int64)
+        types = ((meta >> np.uint64(48)) & np.uint64(7)).astype(np.int64)
+        nnz = ((meta >> np.uint64(40)) & np.uint64(0xFF)).astype(np.int64) + 1
+        self.pay = payload_read_bytes(types, nnz, vk)
+        # per column block: tiles and payload bytes (push), via the CSC view
+        pay_csc = self.pay[csc2csr]
+        cum = np.concatenate([[0], np.cumsum(pay_csc)])
+        self.cb_tiles = np.diff(self.cb_ptr)
+        self.cb_pay = cum[self.cb_ptr[1:]] - cum[self.cb_ptr[:-1]]
+        self.cb_chunks = (self.cb_tiles + 63) // 64
+
+    def call_bytes(self, act_blocks, nnz_x, ybytes, push, vsize=0):
+        """(metadata bytes, compute bytes) of one call."""
+        nact = act_blocks.shape[0]
+        nch = int(self.cb_chunks[act_blocks].sum())
+        meta_b = 4 * nnz_x + 2 * vsize * nnz_x + 8 * nact + 8 * nch + ybytes
+        if push:
+            comp = 8 * nch + 8 * nact + 16 * int(self.cb_tiles[act_blocks].sum()) + int(self.cb_pay[act_blocks].sum())
+        else:
+            active = np.zeros(self.nb, bool)
+            active[act_blocks] = True
+            at = active[self.t_cb]
+            comp = 16 * self.nseg + 4 * self.T + 4 * self.nb + 8 * int(at.sum()) + int(self.pay[at].sum()) + ybytes
+        return meta_b, comp
+
+
+def kernel_src_sha():
+    h = hashlib.sha256()
+    for f in KERNEL_SRC:
+        with open(os.path.join(ROOT, "spmspv_graph_traversal_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload):
+    """HBM traffic per launch measured with rocprofv3 counters (profiles/), if
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_k_spmspv_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_src_sha") != kernel_src_sha():
+        return None
+    return d.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------- workloads
+def bench_rmat20(dbs, torch, args):
+    from synth import rmat_csr, rng_for, sparse_x
+
+    t0 = time.time()
+    rp, ci = rmat_csr(20, 16, rng_for("rmat20"))
+    n = 1 << 20
+    log(f"[bench] rmat20 generated: nnz={int(rp[-1])} in {time.time() - t0:.1f}s")
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    A = dbs.dbs_build(n, n, torch.from_numpy(rp).to(dev), torch.from_numpy(ci).to(dev), None, dbs.DBS_PATTERN)
+    torch.cuda.synchronize()
+    build_s = time.time() - t0
+    st = dbs.dbs_get_stats(A)
+    log(f"[bench] rmat20 built in {build_s:.2f}s: tiles={st['tiles']} segments={st['segments']} "
+        f"format={st['format_bytes'] / 1e6:.1f} MB")
+    fmt = Format(dbs, A, 2)
+    xs = []
+    for k, d in enumerate(DENSITIES):
+        xi, _ = sparse_x(n, d, rng_for("rmat20", 1, k), with_values=False)
+        act = np.unique(xi // 16)
+        push = 100 * act.shape[0] < fmt.nb
+        mb, cb = fmt.call_bytes(act, xi.shape[0], n, push)
+        xs.append(dict(density=d, xi=xi, x=torch.from_numpy(xi).to(dev), nact=act.shape[0], push=push,
+                       meta_bytes=mb, comp_bytes=cb))
+    y = torch.empty(n, dtype=torch.uint8, device=dev)
+
+    def step():
+        for x in xs:
+            dbs.dbs_spmspv(A, x["x"], None, dbs.DBS_OR_AND, y)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    dbs.dbs_set_option(A, dbs.DBS_OPT_TIMING, 1)  # clears the kernel-time sums
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    total_ms = ev0.elapsed_time(ev1)
+    st = dbs.dbs_get_stats(A)
+    assert st["timed_calls"] == args.steps * len(xs)
+    ms_per_step = total_ms / args.steps
+    step_bytes = sum(x["meta_bytes"] + x["comp_bytes"] for x in xs)
+    comp_bytes = sum(x["comp_bytes"] for x in xs)
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    kernel_ms = st["sum_compute_ms"] / st["timed_calls"]
+    achieved = comp_bytes / len(xs) / (kernel_ms * 1e-3) / 1e9
+
+    # per-density breakdown (separate loops, same kernels)
+    per = []
+    for x in ([] if args.headline_only else xs):
+        dbs.dbs_set_option(A, dbs.DBS_OPT_TIMING, 1)
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(args.steps):
+            dbs.dbs_spmspv(A, x["x"], None, dbs.DBS_OR_AND, y)
+        ev1.record()
+        torch.cuda.synchronize()
+        call_ms = ev0.elapsed_time(ev1) / args.steps
+        s2 = dbs.dbs_get_stats(A)
+        kms = s2["sum_compute_ms"] / s2["timed_calls"]
+        mms = s2["sum_meta_ms"] / s2["timed_calls"]
+        per.append({
+            "density": x["density"], "nnz_x": int(x["xi"].shape[0]), "n_nzblk": s2["last_n_nzblk"],
+            "xb_ratio": round(s2["last_n_nzblk"] / fmt.nb, 5), "path": "push" if s2["last_path"] == 0 else "pull",
+            "call_us": round(call_ms * 1e3, 2), "compute_kernel_us": round(kms * 1e3, 2),
+            "meta_kernel_us": round(mms * 1e3, 2),
+            "bytes": int(x["meta_bytes"] + x["comp_bytes"]),
+            "call_GBps": round((x["meta_bytes"] + x["comp_bytes"]) / (call_ms * 1e-3) / 1e9, 1),
+            "compute_kernel_GBps": round(x["comp_bytes"] / (kms * 1e-3) / 1e9, 1),
+            "compute_kernel_frac_of_hbm": round(x["comp_bytes"] / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        })
+    # forced push at the low densities (ablation of the global selector)
+    forced = []
+    dbs.dbs_set_option(A, dbs.DBS_OPT_PATH, 1)
+    for x in ([] if args.headline_only else xs[:3]):
+        dbs.dbs_set_option(A, dbs.DBS_OPT_TIMING, 1)
+        for _ in range(args.steps):
+            dbs.dbs_spmspv(A, x["x"], None, dbs.DBS_OR_AND, y)
+        s2 = dbs.dbs_get_stats(A)
+        forced.append({"density": x["density"], "path": "push (forced)",
+                       "compute_kernel_us": round(s2["sum_compute_ms"] / s2["timed_calls"] * 1e3, 2)})
+    dbs.dbs_set_option(A, dbs.DBS_OPT_PATH, 0)
+    dbs.dbs_set_option(A, dbs.DBS_OPT_TIMING, 0)
+    res = {
+        "ms_per_step": ms_per_step, "value": value, "step_bytes": step_bytes,
+        "kernel_avg_us": kernel_ms * 1e3, "achieved": achieved, "comp_bytes_per_launch": comp_bytes / len(xs),
+        "per_density": per, "forced_push": forced, "build_s": build_s,
+        "format": {"tiles": st["tiles"], "segments": st["segments"], "format_MB": round(st["format_bytes"] / 1e6, 1),
+                   "tiles_by_format": st["tiles_by_format"]},
+        "graph": (rp, ci, n), "xs": xs,
+    }
+    return res
+
+
+def cpu_baseline_rmat20(res, seconds):
+    import oracle as orc
+
+    rp, ci, n = res["graph"]
+    t0 = time.time()
+    steps = 0
+    while True:
+        for x in res["xs"]:
+            orc.or_and_pull(n, n, rp, ci, x["xi"])
+        steps += 1
+        el = time.time() - t0
+        if el >= seconds or steps >= 50:
+            break
+    per_step = el / steps
+    return {"value": round(res["step_bytes"] / per_step / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "ms_per_step": round(per_step * 1e3, 1),
+            "sample": f"{steps} full sweep steps (5 OR-AND calls each, CSR pull) on one host thread"}
+
+
+def bench_bfs22(dbs, torch, args):
+    from synth import largest_component_vertices, rmat_csr, rng_for
+    import oracle as orc
+
+    t0 = time.time()
+    rp, ci = rmat_csr(22, 16, rng_for("rmat22"))
+    n = 1 << 22
+    log(f"[bench] rmat22 generated: nnz={int(rp[-1])} in {time.time() - t0:.1f}s")
+    lcc = largest_component_vertices(rp, ci, n)
+    deg = np.diff(rp.astype(np.int64))
+    edges = int(deg[lcc].sum()) // 2
+    srcs = rng_for("rmat22", 1).choice(lcc, args.bfs_sources, replace=False)
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    A = dbs.dbs_build(n, n, torch.from_numpy(rp).to(dev), torch.from_numpy(ci).to(dev), None, dbs.DBS_PATTERN)
+    torch.cuda.synchronize()
+    build_s = time.time() - t0
+    lv = torch.empty(n, dtype=torch.int32, device=dev)
+    for s in srcs[:2]:
+        dbs.dbs_bfs(A, int(s), lv)
+    # parity spot check of the first source against the oracle
+    t0 = time.time()
+    ref = orc.bfs(n, rp, ci, int(srcs[0]))
+    cpu_bfs_s = time.time() - t0
+    dbs.dbs_bfs(A, int(srcs[0]), lv)
+    ok = bool(np.array_equal(lv.cpu().numpy(), ref))
+    dbs.dbs_set_option(A, dbs.DBS_OPT_TIMING, 1)
+    times, ktimes, levels, pushl = [], [], [], []
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for s in srcs:
+        ev0.record()
+        dbs.dbs_bfs(A, int(s), lv)
+        ev1.record()
+        torch.cuda.synchronize()
+        times.append(ev0.elapsed_time(ev1))
+        st = dbs.dbs_get_stats(A)
+        ktimes.append(st["bfs_kernel_ms"])
+        levels.append(st["bfs_levels"])
+        pushl.append(st["bfs_push_levels"])
+    dbs.dbs_set_option(A, dbs.DBS_OPT_TIMING, 0)
+    times = np.array(times)
+    gteps = edges / (times * 1e-3) / 1e9
+    return {"workload": "R-MAT scale 22, edge factor 16, symmetrized; 64 sources in the largest component",
+            "vertices_in_component": int(lcc.shape[0]), "undirected_edges_in_component": edges,
+            "gteps_harmonic_mean": round(float(len(gteps) / np.sum(1.0 / gteps)), 2),
+            "gteps_median": round(float(np.median(gteps)), 2),
+            "ms_median": round(float(np.median(times)), 3), "ms_mean": round(float(times.mean()), 3),
+            "level_kernels_ms_median": round(float(np.median(ktimes)), 3),
+            "levels_median": int(np.median(levels)), "push_levels_median": int(np.median(pushl)),
+            "first_source_matches_oracle": ok, "oracle_bfs_s_first_source": round(cpu_bfs_s, 2),
+            "oracle_gteps_first_source": round(edges / cpu_bfs_s / 1e9, 4), "build_s": round(build_s, 2)}
+
+
+def bench_decode(dbs, torch, args):
+    from synth import decode_activation, decode_weight_csr, rng_for
+
+    dev = torch.device("cuda:0")
+    out = []
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for rows, cols in [(11008, 4096), (4096, 11008)]:
+        for sp in (0.5, 0.7):
+            rp, ci, bits = decode_weight_csr(rows, cols, sp, rng_for("decode", rows, int(sp * 10)))
+            rp_d, ci_d = torch.from_numpy(rp).to(dev), torch.from_numpy(ci).to(dev)
+            v_d = torch.from_numpy(bits.view(np.int16)).to(dev)
+            copies = [dbs.dbs_build(rows, cols, rp_d, ci_d, v_d, dbs.DBS_BF16) for _ in range(args.decode_copies)]
+            fmt = Format(dbs, copies[0], 1)
+            st = dbs.dbs_get_stats(copies[0])
+            y = torch.empty(rows, dtype=torch.float32, device=dev)
+            for z in (0.1, 0.5, 0.9):
+                x = decode_activation(cols, z, rng_for("decode", rows, int(sp * 10), int(z * 10)))
+                xd = torch.from_numpy(x.view(np.int16)).to(dev)
+                act = np.unique(np.nonzero(x)[0] // 16)
+                mb, cb = fmt.call_bytes(act, 0, 4 * rows, False)
+                mb += 2 * cols
+                A = copies[0]
+                for _ in range(args.warmup):
+                    dbs.dbs_spmspv_dense(A, xd, dbs.DBS_PLUS_TIMES, y)
+                dbs.dbs_set_option(A, dbs.DBS_OPT_TIMING, 1)
+                torch.cuda.synchronize()
+                ev0.record()
+                for _ in range(args.steps):
+                    dbs.dbs_spmspv_dense(A, xd, dbs.DBS_PLUS_TIMES, y)
+                ev1.record()
+                torch.cuda.synchronize()
+                warm_us = ev0.elapsed_time(ev1) / args.steps * 1e3
+                s2 = dbs.dbs_get_stats(A)
+                kus = s2["sum_compute_ms"] / s2["timed_calls"] * 1e3
+                dbs.dbs_set_option(A, dbs.DBS_OPT_TIMING, 0)
+                # rotating copies: each call reads a different copy of the weights
+                for c in copies:
+                    dbs.dbs_spmspv_dense(c, xd, dbs.DBS_PLUS_TIMES, y)
+                torch.cuda.synchronize()
+                ev0.record()
+                reps = max(args.steps, len(copies))
+                for r in range(reps):
+                    dbs.dbs_spmspv_dense(copies[r % len(copies)], xd, dbs.DBS_PLUS_TIMES, y)
+                ev1.record()
+                torch.cuda.synchronize()
+                cold_us = ev0.elapsed_time(ev1) / reps * 1e3
+                out.append({"shape": [rows, cols], "weight_sparsity": sp, "activation_zeros": z,
+                            "path": "push" if s2["last_path"] == 0 else "pull",
+                            "xb_ratio": round(s2["last_n_nzblk"] / fmt.nb, 4),
+                            "us_warm": round(warm_us, 2), "compute_kernel_us_warm": round(kus, 2),
+                            "us_rotating_copies": round(cold_us, 2),
+                            "bytes": int(mb + cb),
+                            "GBps_warm": round((mb + cb) / (warm_us * 1e-6) / 1e9, 1),
+                            "GBps_rotating": round((mb + cb) / (cold_us * 1e-6) / 1e9, 1),
+                            "tiles_by_format": st["tiles_by_format"]})
+                log(f"[bench] decode {rows}x{cols} s={sp} z={z}: warm {warm_us:.2f} us, rotating {cold_us:.2f} us")
+            del copies
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-bfs", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="only the timed sweep (for profiling: every SpMSpV launch is one of the timed mix)")
+    ap.add_argument("--bfs-sources", type=int, default=64)
+    ap.add_argument("--decode-copies", type=int, default=10)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the method has no multi-GPU path here (--gpus {args.gpus} "
+              "requested); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import spmspv_graph_traversal_amd as dbs
+
+    torch.cuda.set_device(0)
+    res = bench_rmat20(dbs, torch, args)
+    log(f"[bench] rmat20 sweep: {res['ms_per_step']:.3f} ms/step, {res['value']:.1f} GB/s")
+    extra = {"rmat20_per_density": res["per_density"], "rmat20_forced_push": res["forced_push"],
+             "rmat20_format": res["format"], "rmat20_build_s": round(res["build_s"], 2)}
+    cpu = None
+    if args.headline_only:
+        args.no_cpu = args.no_bfs = args.no_decode = True
+    if not args.no_cpu:
+        cpu = cpu_baseline_rmat20(res, args.cpu_seconds)
+        log(f"[bench] cpu baseline: {cpu}")
+    del res["graph"], res["xs"]
+    if not args.no_bfs:
+        extra["bfs_rmat22"] = bench_bfs22(dbs, torch, args)
+        log(f"[bench] bfs: {extra['bfs_rmat22']}")
+    if not args.no_decode:
+        extra["decode"] = bench_decode(dbs, torch, args)
+    traffic = load_traffic("rmat20_sweep")
+    line = {
+        "metric": METRIC,
+        "value": round(res["value"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u8",
+        "data": "synthetic",
+        "config": {"workload": "rmat20_or_and_density_sweep", "vertices": 1 << 20, "edge_factor": 16,
+                   "rmat_abc": [0.57, 0.19, 0.19], "semiring": "or-and", "x_densities": DENSITIES,
+                   "calls_per_step": len(DENSITIES), "tile": 16},
+        "roofline": {"bound": "hbm", "achieved": round(res["achieved"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(res["achieved"] / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "k_spmspv<pattern, or-and>", "kernel_avg_us": round(res["kernel_avg_us"], 2),
+                     "algorithmic_bytes_per_launch": int(res["comp_bytes_per_launch"])},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
