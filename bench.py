@@ -22,7 +22,8 @@ Byte model (bytes a kernel must move for the path it takes; per call):
   metadata 4*nnz_x (+ 2*value size*nnz_x for plus-times) + 8*active blocks
            + 8*chunks + |y| (the output is cleared there)
 payload = stored bytes of the tile (pattern tiles other than COO: the 32 B
-of masks one direction reads).
+of masks one direction reads; pattern COO tiles of up to 4 entries: none, their
+coordinates are in the 8-byte metadata word).
 """
 from __future__ import annotations
 
@@ -59,8 +60,8 @@ def payload_read_bytes(types, nnz, vk):
     vs = {0: 4, 1: 2, 2: 0}[vk]
     types = types.astype(np.int64)
     nnz = nnz.astype(np.int64)
-    if vk == 2:
-        return np.where(types == 0, nnz, 32)
+    if vk == 2:  # COO tiles of up to 4 entries live in the metadata word
+        return np.where(types == 0, np.where(nnz <= 4, 0, _align(nnz, 4)), 32)
     coo = _align(nnz, 4) + _align(nnz * vs, 4)
     dense = np.full_like(nnz, 256 * vs)
     force = _align(48 + nnz * vs, 16)

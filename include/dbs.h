@@ -167,7 +167,8 @@ enum {
   DBS_OPT_TH3_DEN = 2,           /*   N_nzblk * den < N_blk * num              */
   DBS_OPT_LOCAL_PUSH_CUTOFF = 3, /* patched-CSR tiles use the column (push) microkernel
                                     when popcount(blk_x_mask) < cutoff (default 8) */
-  DBS_OPT_TIMING = 4,            /* 1: time the kernels of each call with HIP events */
+  DBS_OPT_TIMING = 4,            /* 1: time the kernels of each call with HIP events (setting
+                                    it, to 0 or 1, also clears the sums in dbs_stats) */
   DBS_OPT_CHECK = 5              /* 1: validate x_idx ordering on the device */
 };
 dbs_status dbs_set_option(dbs_handle A, int32_t option, int64_t value);
@@ -190,6 +191,11 @@ typedef struct {
   int64_t last_push_chunks;        /* 64-tile work chunks listed for push */
   float last_meta_ms;              /* metadata kernel time (DBS_OPT_TIMING), else -1 */
   float last_compute_ms;           /* SpMSpV kernel time (DBS_OPT_TIMING), else -1 */
+  /* sums over the SpMSpV calls made since DBS_OPT_TIMING was last set to 1 (HIP
+     events recorded on each call's stream around each of its two kernels) */
+  int64_t timed_calls;
+  double sum_meta_ms;
+  double sum_compute_ms;
   /* last dbs_bfs call */
   int32_t bfs_levels;              /* levels run (including the empty last one) */
   int32_t bfs_push_levels;         /* of which push */

@@ -35,6 +35,33 @@ void dbs_dev_free(dbs_matrix *A, void *p, size_t bytes) {
 
 namespace {
 
+// fold the timing slot `i` into the sums (waits for its last event)
+hipError_t fold_slot(dbs_matrix *A, int i) {
+  float a = 0.0f, b = 0.0f;
+  hipError_t e = hipEventSynchronize(A->tev[i][2]);
+  if (e == hipSuccess) e = hipEventElapsedTime(&a, A->tev[i][0], A->tev[i][1]);
+  if (e == hipSuccess) e = hipEventElapsedTime(&b, A->tev[i][1], A->tev[i][2]);
+  if (e != hipSuccess) return e;
+  A->st.timed_calls += 1;
+  A->st.sum_meta_ms += a;
+  A->st.sum_compute_ms += b;
+  A->st.last_meta_ms = a;
+  A->st.last_compute_ms = b;
+  return hipSuccess;
+}
+
+// fold every recorded slot, oldest first
+hipError_t fold_all(dbs_matrix *A) {
+  const int R = dbs_matrix::kTimingRing;
+  while (A->tev_used > 0) {
+    const int i = (A->tev_head - A->tev_used + R) % R;
+    hipError_t e = fold_slot(A, i);
+    if (e != hipSuccess) return e;
+    A->tev_used -= 1;
+  }
+  return hipSuccess;
+}
+
 void free_all(dbs_matrix *A) {
   void *bufs[] = {A->rb_ptr, A->t_cb,     A->t_meta,   A->cb_ptr,     A->csc_rb,  A->csc2csr,
                   A->payload, A->segs,    A->xmask,    A->xd,         A->act_list, A->chunks,
@@ -44,6 +71,9 @@ void free_all(dbs_matrix *A) {
   if (A->bfs_host) (void)hipHostFree(A->bfs_host);
   for (int i = 0; i < 6; ++i)
     if (A->ev[i]) (void)hipEventDestroy(A->ev[i]);
+  if (A->tev_ready)
+    for (int i = 0; i < dbs_matrix::kTimingRing; ++i)
+      for (int j = 0; j < 3; ++j) (void)hipEventDestroy(A->tev[i][j]);
 }
 
 dbs_status map_err(hipError_t e) {
@@ -79,6 +109,25 @@ dbs_status alloc_call_scratch(dbs_matrix *A) {
 }
 
 }  // namespace
+
+hipEvent_t *dbs_timing_slot(dbs_matrix *A) {
+  const int R = dbs_matrix::kTimingRing;
+  if (!A->tev_ready) {
+    for (int i = 0; i < R; ++i)
+      for (int j = 0; j < 3; ++j)
+        if (DBS_NOTE(hipEventCreate(&A->tev[i][j])) != hipSuccess) return nullptr;
+    A->tev_ready = 1;
+  }
+  if (A->tev_used == R) {  // ring full: fold the oldest (long finished) call
+    const int i = (A->tev_head - A->tev_used + R) % R;
+    if (DBS_NOTE(fold_slot(A, i)) != hipSuccess) return nullptr;
+    A->tev_used -= 1;
+  }
+  hipEvent_t *slot = A->tev[A->tev_head];
+  A->tev_head = (A->tev_head + 1) % R;
+  A->tev_used += 1;
+  return slot;
+}
 
 extern "C" {
 
@@ -209,6 +258,12 @@ dbs_status dbs_set_option(dbs_handle A, int32_t option, int64_t value) {
       if (value < 0 || value > 17) return DBS_ERR_INVALID_ARG;
       break;
     case DBS_OPT_TIMING:
+      if (value != 0 && value != 1) return DBS_ERR_INVALID_ARG;
+      API_TRY(fold_all(A));
+      A->st.timed_calls = 0;
+      A->st.sum_meta_ms = 0.0;
+      A->st.sum_compute_ms = 0.0;
+      break;
     case DBS_OPT_CHECK:
       if (value != 0 && value != 1) return DBS_ERR_INVALID_ARG;
       break;
@@ -240,21 +295,11 @@ dbs_status dbs_get_stats(dbs_handle A, dbs_stats *out) {
     const bool push = fp == 1 || (fp == 0 && (int64_t)h[0] * A->opt[DBS_OPT_TH3_DEN] <
                                                  (int64_t)A->nb * A->opt[DBS_OPT_TH3_NUM]);
     A->st.last_path = push ? 0 : 1;
-    A->st.last_meta_ms = -1.0f;
-    A->st.last_compute_ms = -1.0f;
-    if (A->timing_pending) {
-      float a = 0.0f, b = 0.0f;
-      API_TRY(hipEventSynchronize(A->ev[2]));
-      API_TRY(hipEventElapsedTime(&a, A->ev[0], A->ev[1]));
-      API_TRY(hipEventElapsedTime(&b, A->ev[1], A->ev[2]));
-      A->st.last_meta_ms = a;
-      A->st.last_compute_ms = b;
-    }
     if (h[2]) ret = DBS_ERR_BAD_VECTOR;
-    A->timing_pending = 0;
   } else {
     API_TRY(hipStreamSynchronize(A->last_stream));
   }
+  API_TRY(fold_all(A));
   *out = A->st;
   return ret;
 }

@@ -14,6 +14,7 @@
 //                clears the bitmap two levels back.
 // Three bitmaps rotate: current frontier, next frontier, and one being
 // cleared.  The host reads one counter per level to stop.
+#include "meta.h"
 #include "tile_kernels.h"
 
 namespace {
@@ -29,7 +30,7 @@ struct BfsParams {
   const uint8_t *payload;
   uint64_t dense_mask_off;
   const uint32_t *segs;
-  int64_t nseg;
+  int64_t nseg, T, payload_bytes;
   int32_t m, nb;
   const uint32_t *cur_bm;   // frontier of this level
   uint32_t *next_bm;        // frontier of the next level (cleared)
@@ -80,7 +81,7 @@ DBS_DEV void bfs_push_chunk(const BfsParams &P, uint64_t own, int lane) {
     meta = P.t_meta[P.csc2csr[k]];
   }
   const uint32_t type = meta_type(meta);
-  if (act && type == DBS_TILE_COO) discover(P, rb, coo_or(P.payload + meta_vp(meta), meta_nnz(meta), m));
+  if (act && type == DBS_TILE_COO) discover(P, rb, coo_or_meta(P.payload, meta, m));
   uint64_t todo = __ballot(act && type != DBS_TILE_COO);
   while (todo) {
     const int src = __ffsll((unsigned long long)todo) - 1;
@@ -92,41 +93,78 @@ DBS_DEV void bfs_push_chunk(const BfsParams &P, uint64_t own, int lane) {
   }
 }
 
-template <int VK>
-DBS_DEV void bfs_pull_segment(const BfsParams &P, int64_t s, int lane) {
-  const uint4 seg = ((const uint4 *)P.segs)[s];
-  const uint32_t rb = seg.x & ~SEG_SPLIT;
-  // rows still to be found in this row block; a fully visited row block is
+// Pull: a wave takes U consecutive segments and issues each load phase for
+// all of them before using any result, with buffer loads (idle lanes pass an
+// out-of-range offset instead of branching), guard-free COO decoding and a
+// DPP wave OR, as in the OR-AND SpMSpV pull.
+struct BfsRes {
+  brsrc_t tcb, tmeta, pay, bm;
+};
+
+template <int VK, int U>
+DBS_DEV void bfs_pull_group(const BfsParams &P, const BfsRes &R, int64_t s0, bool eager, int lane) {
+  uint4 seg[U];
+  uint32_t need[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t si = s0 + u < P.nseg ? s0 + u : P.nseg - 1;
+    seg[u] = ((const uint4 *)P.segs)[si];
+  }
+  // rows still to be found in each row block; a fully visited row block is
   // skipped without reading its tiles
-  const uint32_t need = ~bm_get(P.vis, rb) & rows_valid(P.m, rb);
-  if (!need) return;
-  const uint32_t t = seg.y + (uint32_t)lane;
-  bool act = t < seg.z;
-  uint32_t m = 0;
-  uint64_t meta = 0;
-  if (act) {
-    m = bm_get(P.cur_bm, P.t_cb[t]);
-    act = m != 0u;
-    if (act) meta = P.t_meta[t];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint32_t rb = seg[u].x & ~SEG_SPLIT;
+    need[u] = s0 + u < P.nseg ? (~bm_get(P.vis, rb) & rows_valid(P.m, rb)) : 0u;
   }
-  const uint32_t type = meta_type(meta);
-  uint32_t f = 0;
-  if (act && type == DBS_TILE_COO) f = coo_or(P.payload + meta_vp(meta), meta_nnz(meta), m);
-  f = group_or_u32<64>(f);
-  uint64_t todo = __ballot(act && type != DBS_TILE_COO);
-  while (todo && (f & need) != need) {
-    const int src = __ffsll((unsigned long long)todo) - 1;
-    todo &= todo - 1;
-    const uint64_t tm = __shfl(meta, src);
-    const uint32_t tmask = (uint32_t)__shfl((int)m, src);
-    f |= tile_or<VK>(P.payload + meta_vp(tm), dmask<VK>(P, meta_vp(tm)), meta_type(tm), tmask, lane);
+  uint32_t cb[U], m[U], pw0[U], pw1[U];
+  uint64_t meta[U];
+  bool act[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint32_t t = seg[u].y + (uint32_t)lane;
+    act[u] = need[u] != 0u && t < seg[u].z;
+    cb[u] = bld32(R.tcb, act[u] ? t * 4u : OOB_OFF);
+    meta[u] = eager ? bld64(R.tmeta, act[u] ? t * 8u : OOB_OFF) : 0ull;
   }
-  if (lane == 0 && (f & need)) discover(P, rb, f & need);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint32_t w = bld32(R.bm, act[u] ? (cb[u] >> 1) * 4u : OOB_OFF);
+    m[u] = (w >> ((cb[u] & 1u) * 16u)) & 0xFFFFu;
+    act[u] = m[u] != 0u;
+  }
+  if (!eager) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) meta[u] = bld64(R.tmeta, act[u] ? (seg[u].y + (uint32_t)lane) * 8u : OOB_OFF);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const bool pre = act[u] && meta_type(meta[u]) == DBS_TILE_COO && !meta_inline(meta[u]);
+    const uint32_t off = pre ? (uint32_t)meta_vp(meta[u]) : OOB_OFF;
+    pw0[u] = bld32(R.pay, off);
+    pw1[u] = bld32(R.pay, pre && meta_nnz(meta[u]) > 4 ? off + 4u : OOB_OFF);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (!need[u]) continue;
+    uint32_t f = lane_coo_or(P.payload, meta[u], m[u], act[u], pw0[u], pw1[u]);
+    f = wave_or(f);
+    uint64_t todo = __ballot(act[u] && meta_type(meta[u]) != DBS_TILE_COO);
+    while (todo && (f & need[u]) != need[u]) {
+      const int src = __ffsll((unsigned long long)todo) - 1;
+      todo &= todo - 1;
+      const uint64_t tm = __shfl(meta[u], src);
+      const uint32_t tmask = (uint32_t)__shfl((int)m[u], src);
+      f |= tile_or<VK>(P.payload + meta_vp(tm), dmask<VK>(P, meta_vp(tm)), meta_type(tm), tmask, lane);
+    }
+    if (lane == 0 && (f & need[u])) discover(P, seg[u].x & ~SEG_SPLIT, f & need[u]);
+  }
 }
 
 template <int VK>
 __global__ __launch_bounds__(KT) void k_bfs_level(BfsParams P) {
-  const int lane = __lane_id(), w = threadIdx.x / DBS_WAVE;
+  const int lane = __lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / DBS_WAVE);
   const uint32_t nz = P.cur_ctr[0];
   const bool push = P.force_path == 1 ||
                     (P.force_path == 0 && (int64_t)nz * P.th3_den < (int64_t)P.nb * P.th3_num);
@@ -136,60 +174,30 @@ __global__ __launch_bounds__(KT) void k_bfs_level(BfsParams P) {
     const int64_t nch = P.cur_ctr[1];
     for (int64_t c = gw; c < nch; c += nw) bfs_push_chunk<VK>(P, P.cur_chunks[c], lane);
   } else {
-    for (int64_t s = gw; s < P.nseg; s += nw) bfs_pull_segment<VK>(P, s, lane);
+    constexpr int U = 8;
+    const bool eager = (int64_t)nz * 4 > (int64_t)P.nb;
+    BfsRes R;
+    R.tcb = make_rsrc(P.t_cb, (uint64_t)P.T * 4);
+    R.tmeta = make_rsrc(P.t_meta, (uint64_t)P.T * 8);
+    R.pay = make_rsrc(P.payload, (uint64_t)P.payload_bytes);
+    R.bm = make_rsrc(P.cur_bm, (uint64_t)((P.nb + 1) / 2) * 4);
+    for (int64_t s = gw * U; s < P.nseg; s += nw * U) bfs_pull_group<VK, U>(P, R, s, eager, lane);
   }
 }
 
 // Frontier metadata: nonzero blocks of `bm`, their list and push chunks;
 // clears `clr_bm` / `clr_ctr` (the buffers two levels back) when given.
-__global__ __launch_bounds__(KT) void k_bfs_meta(const uint32_t *bm, int32_t nb, const uint32_t *cb_ptr,
-                                                 uint32_t *ctr, uint32_t *list, uint64_t *chunks,
-                                                 uint32_t *clr_bm, uint32_t *clr_ctr, int64_t nwords,
-                                                 int32_t *levels_done_flag) {
-  __shared__ uint32_t s_cnt[KT / DBS_WAVE], s_ch[KT / DBS_WAVE];
-  __shared__ uint32_t s_base_cnt, s_base_ch;
-  const int lane = __lane_id(), w = threadIdx.x / DBS_WAVE;
+__global__ __launch_bounds__(KT) void k_bfs_meta(const uint32_t *bm, int32_t nb, dbs_meta::Reg reg,
+                                                 uint32_t *clr_bm, uint32_t *clr_ctr, int64_t nwords) {
   const int64_t gs = (int64_t)gridDim.x * KT;
   if (clr_bm) {
     for (int64_t k = (int64_t)blockIdx.x * KT + threadIdx.x; k < nwords; k += gs) clr_bm[k] = 0;
     if (blockIdx.x == 0 && threadIdx.x < 8) clr_ctr[threadIdx.x] = 0;
   }
-  (void)levels_done_flag;
-  for (int64_t base = (int64_t)blockIdx.x * KT; base < nb; base += gs) {
-    const int64_t b = base + threadIdx.x;
-    const bool leader = b < nb && bm_get(bm, (uint32_t)b) != 0u;
-    uint32_t nch = 0;
-    if (leader) nch = (cb_ptr[b + 1] - cb_ptr[b] + 63u) >> 6;
-    const uint64_t bal = __ballot(leader);
-    const uint32_t rank = (uint32_t)__popcll(bal & __lanemask_lt());
-    const uint32_t chinc = group_incl_scan_u32<64>(nch);
-    if (lane == 63) {
-      s_cnt[w] = (uint32_t)__popcll(bal);
-      s_ch[w] = chinc;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      uint32_t tc = 0, th = 0;
-      for (int i = 0; i < KT / DBS_WAVE; ++i) {
-        tc += s_cnt[i];
-        th += s_ch[i];
-      }
-      s_base_cnt = tc ? atomicAdd(&ctr[0], tc) : 0u;
-      s_base_ch = th ? atomicAdd(&ctr[1], th) : 0u;
-    }
-    __syncthreads();
-    if (leader) {
-      uint32_t pc = s_base_cnt, ph = s_base_ch;
-      for (int i = 0; i < w; ++i) {
-        pc += s_cnt[i];
-        ph += s_ch[i];
-      }
-      list[pc + rank] = (uint32_t)b;
-      const uint32_t first = ph + chinc - nch;
-      for (uint32_t k = 0; k < nch; ++k) chunks[first + k] = (uint64_t)b | ((uint64_t)k << 32);
-    }
-    __syncthreads();
-  }
+  dbs_meta::register_blocks(reg, nb, [&](int64_t b, int, bool &leader, uint32_t &bo) {
+    leader = b < nb && bm_get(bm, (uint32_t)b) != 0u;
+    bo = (uint32_t)b;
+  });
 }
 
 __global__ void k_bfs_init(int32_t *levels, int32_t m, uint32_t *bm3, int64_t bm_words3, uint32_t *vis,
@@ -236,10 +244,19 @@ dbs_status dbs_bfs_impl(dbs_matrix *A, int32_t src, int32_t *levels, hipStream_t
                      A->bfs_vis, nwords, A->bfs_ctr, src);
   hipLaunchKernelGGL(k_bfs_seed, dim3(1), dim3(1), 0, s, A->bfs_bm, A->bfs_vis, src);
   BFS_TRY(hipGetLastError());
-  const unsigned mgrid = (unsigned)(((int64_t)A->nb + KT - 1) / KT < 1024 ? ((int64_t)A->nb + KT - 1) / KT : 1024);
-  hipLaunchKernelGGL(k_bfs_meta, dim3(mgrid ? mgrid : 1), dim3(KT), 0, s, (const uint32_t *)A->bfs_bm, A->nb,
-                     (const uint32_t *)A->cb_ptr, A->bfs_ctr, A->bfs_list, A->bfs_chunks, (uint32_t *)nullptr,
-                     (uint32_t *)nullptr, (int64_t)0, (int32_t *)nullptr);
+  const unsigned mgrid = dbs_meta::groups_for(A->nb, nwords);
+  auto reg_for = [&](int buf) {
+    dbs_meta::Reg r;
+    r.ctr = A->bfs_ctr + 8 * buf;
+    r.list = A->bfs_list + (int64_t)buf * A->nb;
+    r.chunks = A->bfs_chunks + buf * chunk_cap;
+    r.list_cap = A->nb;
+    r.chunk_cap = chunk_cap;
+    r.cb_ptr = A->cb_ptr;
+    return r;
+  };
+  hipLaunchKernelGGL(k_bfs_meta, dim3(mgrid), dim3(KT), 0, s, (const uint32_t *)A->bfs_bm, A->nb, reg_for(0),
+                     (uint32_t *)nullptr, (uint32_t *)nullptr, (int64_t)0);
   BFS_TRY(hipGetLastError());
 
   BfsParams P;
@@ -252,6 +269,8 @@ dbs_status dbs_bfs_impl(dbs_matrix *A, int32_t src, int32_t *levels, hipStream_t
   P.dense_mask_off = A->dense_mask_off;
   P.segs = A->segs;
   P.nseg = A->nseg;
+  P.T = A->T;
+  P.payload_bytes = A->payload_bytes;
   P.m = A->m;
   P.nb = A->nb;
   P.vis = A->bfs_vis;
@@ -259,9 +278,13 @@ dbs_status dbs_bfs_impl(dbs_matrix *A, int32_t src, int32_t *levels, hipStream_t
   P.force_path = (int32_t)A->opt[DBS_OPT_PATH];
   P.th3_num = A->opt[DBS_OPT_TH3_NUM];
   P.th3_den = A->opt[DBS_OPT_TH3_DEN];
-  int64_t waves = A->nseg > chunk_cap ? A->nseg : chunk_cap;
+  int64_t waves = (A->nseg + 7) / 8 > chunk_cap ? (A->nseg + 7) / 8 : chunk_cap;
   int64_t g = (waves + 3) / 4;
-  const unsigned grid = (unsigned)(g < 1 ? 1 : (g > 2048 ? 2048 : g));
+  static const unsigned res_f32 = dbs_resident_groups(k_bfs_level<VK_F32>, KT);
+  static const unsigned res_bf16 = dbs_resident_groups(k_bfs_level<VK_BF16>, KT);
+  static const unsigned res_pat = dbs_resident_groups(k_bfs_level<VK_PAT>, KT);
+  const unsigned cap = A->vk == VK_F32 ? res_f32 : A->vk == VK_BF16 ? res_bf16 : res_pat;
+  const unsigned grid = (unsigned)(g < 1 ? 1 : (g > cap ? cap : g));
 
   int32_t L = 0, push_levels = 0;
   float kms = 0.0f;
@@ -278,10 +301,8 @@ dbs_status dbs_bfs_impl(dbs_matrix *A, int32_t src, int32_t *levels, hipStream_t
     else hipLaunchKernelGGL(k_bfs_level<VK_PAT>, dim3(grid), dim3(KT), 0, s, P);
     BFS_TRY(hipGetLastError());
     if (timing) BFS_TRY(hipEventRecord(A->ev[5], s));
-    hipLaunchKernelGGL(k_bfs_meta, dim3(mgrid ? mgrid : 1), dim3(KT), 0, s, (const uint32_t *)P.next_bm, A->nb,
-                       (const uint32_t *)A->cb_ptr, A->bfs_ctr + 8 * nxt, A->bfs_list + (int64_t)nxt * A->nb,
-                       A->bfs_chunks + nxt * chunk_cap, A->bfs_bm + clr * nwords, A->bfs_ctr + 8 * clr, nwords,
-                       (int32_t *)nullptr);
+    hipLaunchKernelGGL(k_bfs_meta, dim3(mgrid), dim3(KT), 0, s, (const uint32_t *)P.next_bm, A->nb, reg_for(nxt),
+                       A->bfs_bm + clr * nwords, A->bfs_ctr + 8 * clr, nwords);
     BFS_TRY(hipGetLastError());
     BFS_TRY(hipMemcpyAsync(A->bfs_host, A->bfs_ctr + 8 * cur, 8, hipMemcpyDeviceToHost, s));
     BFS_TRY(hipMemcpyAsync(A->bfs_host + 2, A->bfs_ctr + 8 * nxt, 4, hipMemcpyDeviceToHost, s));

@@ -181,7 +181,8 @@ template <int VK>
 __global__ __launch_bounds__(BT) void k_tile_fill(int32_t m, int32_t mb, const int32_t *row_ptr,
                                                   const int32_t *col_idx, const void *val,
                                                   const uint32_t *rb_ptr, const uint64_t *t_meta,
-                                                  uint8_t *payload, uint64_t dense_mask_off) {
+                                                  uint64_t *t_meta_w, uint8_t *payload,
+                                                  uint64_t dense_mask_off) {
   constexpr int VS = VK == VK_F32 ? 4 : VK == VK_BF16 ? 2 : 0;
   const int r = threadIdx.x & 15;
   const int32_t rb = (int32_t)blockIdx.x * RB_PER_BLOCK + (int32_t)(threadIdx.x >> 4);
@@ -200,11 +201,28 @@ __global__ __launch_bounds__(BT) void k_tile_fill(int32_t m, int32_t mb, const i
     const uint64_t meta = t_meta[t];
     const uint32_t type = meta_type(meta), nnz = meta_nnz(meta);
     uint8_t *base = payload + meta_vp(meta);
-    if (type == DBS_TILE_COO) {
+    if (type == DBS_TILE_COO && coo_is_inline(VK, nnz)) {
+      // coordinate bytes in row-major order; the unused bytes repeat the last
+      // entry, so OR-AND readers may decode all four without a count check
+      uint32_t word = 0;
+      for (uint32_t j = 0; j < cnt; ++j)
+        word |= ((r << 4) | ((uint32_t)col_idx[p0 + j] & 15u)) << (8 * (rp + j));
+      if (cnt > 0 && rp + cnt == nnz) {
+        const uint32_t last = (r << 4) | ((uint32_t)col_idx[p0 + cnt - 1] & 15u);
+        for (uint32_t e = nnz; e < 4; ++e) word |= last << (8 * e);
+      }
+      word = group_or_u32<16>(word);
+      if (r == 0) ((uint64_t *)t_meta_w)[t] = meta_pack(0, nnz, type) | META_INLINE | word;
+    } else if (type == DBS_TILE_COO) {
       for (uint32_t j = 0; j < cnt; ++j) {
         const uint32_t col = (uint32_t)col_idx[p0 + j] & 15u;
         base[rp + j] = (uint8_t)((r << 4) | col);
         if (VS) store_val<VK>(base + coo_val_off(nnz) + (rp + j) * VS, val, p0 + j);
+      }
+      // padding to the 4-B boundary repeats the last entry (see above)
+      if (cnt > 0 && rp + cnt == nnz) {
+        const uint8_t last = (uint8_t)((r << 4) | ((uint32_t)col_idx[p0 + cnt - 1] & 15u));
+        for (uint32_t e = nnz; e < align_up(nnz, 4); ++e) base[e] = last;
       }
     } else if (VK == VK_PAT) {
       ((uint16_t *)(base + PL_MASK))[r] = (uint16_t)rm;
@@ -436,13 +454,13 @@ dbs_status dbs_build_impl(dbs_matrix *A, const int32_t *row_ptr, const int32_t *
   // --- pass 3: payloads
   if (vk == VK_F32)
     hipLaunchKernelGGL(k_tile_fill<VK_F32>, dim3(gblocks), dim3(BT), 0, s, m, mb, row_ptr, col_idx, val,
-                       (const uint32_t *)A->rb_ptr, (const uint64_t *)A->t_meta, A->payload, A->dense_mask_off);
+                       (const uint32_t *)A->rb_ptr, (const uint64_t *)A->t_meta, A->t_meta, A->payload, A->dense_mask_off);
   else if (vk == VK_BF16)
     hipLaunchKernelGGL(k_tile_fill<VK_BF16>, dim3(gblocks), dim3(BT), 0, s, m, mb, row_ptr, col_idx, val,
-                       (const uint32_t *)A->rb_ptr, (const uint64_t *)A->t_meta, A->payload, A->dense_mask_off);
+                       (const uint32_t *)A->rb_ptr, (const uint64_t *)A->t_meta, A->t_meta, A->payload, A->dense_mask_off);
   else
     hipLaunchKernelGGL(k_tile_fill<VK_PAT>, dim3(gblocks), dim3(BT), 0, s, m, mb, row_ptr, col_idx, val,
-                       (const uint32_t *)A->rb_ptr, (const uint64_t *)A->t_meta, A->payload, A->dense_mask_off);
+                       (const uint32_t *)A->rb_ptr, (const uint64_t *)A->t_meta, A->t_meta, A->payload, A->dense_mask_off);
   BUILD_TRY(hipGetLastError());
 
   // --- block-level CSC view: stable sort of the tiles by column block

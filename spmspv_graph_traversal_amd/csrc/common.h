@@ -25,9 +25,12 @@ __host__ __device__ inline uint32_t align_up(uint32_t x, uint32_t a) { return (x
 // Tile payload layout (one arena, three sections: Dense | mask-based | COO).
 // Offsets are bytes from the tile's payload start `vp`.
 //
-//   COO (values):    coord u8[nnz] (row<<4 | col, row-major) @0,
-//                    values @align4(nnz)
-//   COO (pattern):   coord u8[nnz] @0
+//   COO (values):    coord u8[nnz] (row<<4 | col, row-major) @0, padded to
+//                    4 B by repeating the last coordinate, values @align4(nnz)
+//   COO (pattern):   coord u8[nnz] @0 (padded to 4 B by repeating the last
+//                    coordinate); up to COO_INLINE entries: no payload, the
+//                    coordinate bytes (padded the same way) sit in the
+//                    metadata word
 //   Dense:           values[256] row-major @0 (tile start is 512/1024-B aligned)
 //   ForceCSR:        row_mask u16[16] @0, row_ptr u8[16] @32, values @48
 //                    (row-major, ascending column within a row)
@@ -56,6 +59,21 @@ __host__ __device__ inline uint32_t align_up(uint32_t x, uint32_t a) { return (x
 __host__ __device__ inline uint32_t coo_val_off(uint32_t nnz) { return align_up(nnz, 4); }
 __host__ __device__ inline uint32_t csr_val_off(uint32_t nnz) { return PL_CSR_RC + align_up(nnz, 16); }
 
+// Tile metadata word: payload offset (40 bits) | (nnz-1) << 40 | format << 48.
+// COO tiles of a pattern matrix with at most COO_INLINE entries keep their
+// coordinate bytes in bits 0..31 instead of an offset (bit 51 set) and have
+// no payload: the metadata load brings the whole tile.
+#define COO_INLINE 4
+#define META_INLINE (1ull << 51)
+__host__ __device__ inline uint64_t meta_pack(uint64_t vp, uint32_t nnz, uint32_t type) {
+  return vp | ((uint64_t)(nnz - 1) << 40) | ((uint64_t)type << 48);
+}
+__host__ __device__ inline bool meta_inline(uint64_t m) { return (m & META_INLINE) != 0; }
+__host__ __device__ inline bool coo_is_inline(int vk, uint32_t nnz) { return vk == VK_PAT && nnz <= COO_INLINE; }
+__host__ __device__ inline uint64_t meta_vp(uint64_t m) { return m & ((1ull << 40) - 1); }
+__host__ __device__ inline uint32_t meta_nnz(uint64_t m) { return (uint32_t)((m >> 40) & 0xFF) + 1; }
+__host__ __device__ inline uint32_t meta_type(uint64_t m) { return (uint32_t)((m >> 48) & 0x7); }
+
 // section of a tile in the arena: 0 Dense, 1 mask-based, 2 COO
 __host__ __device__ inline int tile_section(int type, int vk) {
   if (type == DBS_TILE_COO) return 2;
@@ -65,20 +83,15 @@ __host__ __device__ inline int tile_section(int type, int vk) {
 
 __host__ __device__ inline uint32_t tile_payload_bytes(int type, uint32_t nnz, int vk) {
   const uint32_t vs = (uint32_t)vk_size(vk);
-  if (type == DBS_TILE_COO) return vk == VK_PAT ? nnz : coo_val_off(nnz) + align_up(nnz * vs, 4);
+  if (type == DBS_TILE_COO) {
+    if (coo_is_inline(vk, nnz)) return 0;
+    return vk == VK_PAT ? align_up(nnz, 4) : coo_val_off(nnz) + align_up(nnz * vs, 4);
+  }
   if (vk == VK_PAT) return 64;
   if (type == DBS_TILE_DENSE) return 256 * vs;
   if (type == DBS_TILE_CSR) return align_up(csr_val_off(nnz) + nnz * vs, 16);
   return align_up(PL_FORCE_VAL + nnz * vs, 16);  // ForceCSR / ForceCSC
 }
-
-// Tile metadata word: payload offset (40 bits) | (nnz-1) << 40 | format << 48.
-__host__ __device__ inline uint64_t meta_pack(uint64_t vp, uint32_t nnz, uint32_t type) {
-  return vp | ((uint64_t)(nnz - 1) << 40) | ((uint64_t)type << 48);
-}
-__host__ __device__ inline uint64_t meta_vp(uint64_t m) { return m & ((1ull << 40) - 1); }
-__host__ __device__ inline uint32_t meta_nnz(uint64_t m) { return (uint32_t)((m >> 40) & 0xFF) + 1; }
-__host__ __device__ inline uint32_t meta_type(uint64_t m) { return (uint32_t)((m >> 48) & 0x7); }
 
 // Pull segment descriptor: {row block | split << 31, first tile, end tile, 0}.
 #define SEG_SPLIT 0x80000000u
@@ -128,8 +141,11 @@ struct dbs_matrix {
   int64_t opt[8];
   dbs_stats st;
   hipStream_t last_stream;
-  hipEvent_t ev[6];
-  int timing_pending;    // which events hold a measurement
+  hipEvent_t ev[6];      // BFS timing
+  // ring of per-call event triples (before meta, after meta, after compute)
+  static constexpr int kTimingRing = 64;
+  hipEvent_t tev[kTimingRing][3];
+  int tev_head, tev_used, tev_ready;
   int64_t mem_now, mem_peak;
 };
 
@@ -155,11 +171,26 @@ dbs_status dbs_spmspv_impl(dbs_matrix *A, int32_t nnz_x, const int32_t *x_idx,
                            const void *x_val, const void *x_dense, dbs_semiring sr, void *y,
                            hipStream_t s);
 dbs_status dbs_bfs_impl(dbs_matrix *A, int32_t src, int32_t *levels, hipStream_t s);
+// next free event triple of the timing ring (folds the oldest into the sums
+// when the ring is full); nullptr on a HIP error
+hipEvent_t *dbs_timing_slot(dbs_matrix *A);
 
 // Returns e; with DBS_VERBOSE=1 in the environment a failing call is printed
 // to stderr with its source location.
 hipError_t dbs_note(hipError_t e, const char *file, int line);
 #define DBS_NOTE(expr) dbs_note((expr), __FILE__, __LINE__)
+
+// Workgroups of `kernel` (blockDim `threads`) that fit on the device at once
+// (occupancy x compute units), at least 1; cached by the caller.
+template <class K>
+inline unsigned dbs_resident_groups(K kernel, int threads) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 1024;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 1024;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess) return 1024;
+  const long g = (long)cus * (per_cu > 0 ? per_cu : 1);
+  return (unsigned)(g > 0 ? g : 1);
+}
 
 #define DBS_HIP_TRY(expr)                                \
   do {                                                   \

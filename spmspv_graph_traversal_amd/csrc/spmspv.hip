@@ -11,6 +11,7 @@
 //   k_spmspv    reads N_nzblk, picks push or pull on the device, and walks
 //               either the push chunks or the static pull segments, one wave
 //               per chunk / segment, grid-stride.
+#include "meta.h"
 #include "tile_kernels.h"
 
 namespace {
@@ -20,63 +21,13 @@ constexpr int KT = 256;  // threads per workgroup (4 waves)
 struct MetaOut {
   uint32_t *xmask;
   uint32_t epoch;
-  uint32_t *act_list;
-  uint64_t *chunks;
-  uint32_t *ctr;        // this call's counters: [0] N_nzblk, [1] push chunks, [2] error flags
+  dbs_meta::Reg reg;    // this call's counters ([0] N_nzblk, [1] push chunks, [2] error flags) and lists
   uint32_t *ctr_next;   // next call's counters, cleared here
-  const uint32_t *cb_ptr;
   int32_t n, nb;
-  int64_t max_chunks;   // capacity of `chunks`; act_list holds nb entries
   // y clearing: head bytes, 16-B body, tail bytes
   uint8_t *y;
   int64_t y_head, y_body, y_tail;
 };
-
-// Registers the leaders (first lane of each nonzero vector block) of one
-// 256-thread round: compacted list + push chunk reservation, one global
-// atomic per workgroup for each.
-DBS_DEV void register_blocks(const MetaOut &o, bool leader, uint32_t b) {
-  __shared__ uint32_t s_cnt[KT / DBS_WAVE], s_ch[KT / DBS_WAVE];
-  __shared__ uint32_t s_base_cnt, s_base_ch;
-  const int lane = __lane_id(), w = threadIdx.x / DBS_WAVE;
-  uint32_t nch = 0;
-  if (leader) {
-    const uint32_t cnt = o.cb_ptr[b + 1] - o.cb_ptr[b];
-    nch = (cnt + 63u) >> 6;
-  }
-  const uint64_t bal = __ballot(leader);
-  const uint32_t rank = (uint32_t)__popcll(bal & __lanemask_lt());
-  const uint32_t chinc = group_incl_scan_u32<64>(nch);
-  if (lane == 63) {
-    s_cnt[w] = (uint32_t)__popcll(bal);
-    s_ch[w] = chinc;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t tc = 0, th = 0;
-    for (int i = 0; i < KT / DBS_WAVE; ++i) {
-      tc += s_cnt[i];
-      th += s_ch[i];
-    }
-    s_base_cnt = tc ? atomicAdd(&o.ctr[0], tc) : 0u;
-    s_base_ch = th ? atomicAdd(&o.ctr[1], th) : 0u;
-  }
-  __syncthreads();
-  if (leader) {
-    uint32_t pc = s_base_cnt, ph = s_base_ch;
-    for (int i = 0; i < w; ++i) {
-      pc += s_cnt[i];
-      ph += s_ch[i];
-    }
-    // an unsorted x_idx (invalid input) can name a block more than once:
-    // never write past the lists
-    if (pc + rank < (uint32_t)o.nb) o.act_list[pc + rank] = b;
-    const uint32_t first = ph + chinc - nch;
-    for (uint32_t k = 0; k < nch && (int64_t)first + k < o.max_chunks; ++k)
-      o.chunks[first + k] = (uint64_t)b | ((uint64_t)k << 32);
-  }
-  __syncthreads();
-}
 
 DBS_DEV void clear_y(const MetaOut &o) {
   const int64_t gt = (int64_t)blockIdx.x * KT + threadIdx.x, gs = (int64_t)gridDim.x * KT;
@@ -87,39 +38,42 @@ DBS_DEV void clear_y(const MetaOut &o) {
 }
 
 // Sparse x: sorted x_idx.  The first entry of each vector block (the leader)
-// gathers the block's mask from the following entries.
+// builds the block's mask from the following entries.
 template <int VK>
 __global__ __launch_bounds__(KT) void k_xmeta_sparse(MetaOut o, int32_t nnz_x, const int32_t *x_idx,
                                                      const void *x_val, void *xd, int check) {
   if (blockIdx.x == 0 && threadIdx.x < 8) o.ctr_next[threadIdx.x] = 0;
   clear_y(o);
-  const int64_t gs = (int64_t)gridDim.x * KT;
-  for (int64_t base = (int64_t)blockIdx.x * KT; base < nnz_x; base += gs) {
-    const int64_t i = base + threadIdx.x;
+  dbs_meta::register_blocks(o.reg, nnz_x, [&](int64_t i, int pass, bool &leader, uint32_t &bo) {
     const bool valid = i < nnz_x;
-    const int32_t idx = valid ? x_idx[i] : -1;
+    const int64_t ic = valid ? i : 0;  // clamped index (nnz_x > 0 whenever a round runs)
+    const int32_t idx0 = x_idx[ic], prev0 = x_idx[ic > 0 ? ic - 1 : 0];
+    const int32_t idx = valid ? idx0 : -1;
     const bool inb = valid && idx >= 0 && idx < o.n;
     const int32_t b = idx >> 4;
+    const int32_t prev = (valid && i > 0) ? prev0 : -1;
+    leader = inb && (i == 0 || (prev >> 4) != b);
+    bo = (uint32_t)b;
+    if (pass != 0) return;
     if (inb && VK != VK_PAT && x_val) {
       if (VK == VK_F32) ((float *)xd)[idx] = ((const float *)x_val)[i];
       else ((uint16_t *)xd)[idx] = ((const uint16_t *)x_val)[i];
     }
-    const int32_t prev = (valid && i > 0) ? x_idx[i - 1] : -1;
-    if (check && valid && i > 0 && idx <= prev) atomicOr(&o.ctr[2], 1u);
-    const bool leader = inb && (i == 0 || (prev >> 4) != b);
+    if (check && valid && i > 0 && idx <= prev) atomicOr(&o.reg.ctr[2], 1u);
     if (leader) {
-      uint32_t mk = 0;
-      int64_t j = i;
-      for (; j < nnz_x && j < i + 16; ++j) {
+      // a strictly increasing x_idx holds at most 16 entries of block b, all
+      // right after the leader: 15 independent look-ahead loads (no chain)
+      uint32_t mk = 1u << (idx & 15);
+#pragma unroll
+      for (int k = 1; k < 16; ++k) {
+        const int64_t j = i + k < nnz_x ? i + k : i;  // clamped: no branch around the load
         const int32_t v = x_idx[j];
-        if ((v >> 4) != b || v >= o.n) break;
-        mk |= 1u << (v & 15);
+        if (i + k < nnz_x && (v >> 4) == b && v < o.n) mk |= 1u << (v & 15);
       }
-      if (check && j == i + 16 && j < nnz_x && (x_idx[j] >> 4) == b) atomicOr(&o.ctr[2], 1u);
+      if (check && i + 16 < nnz_x && (x_idx[i + 16] >> 4) == b) atomicOr(&o.reg.ctr[2], 1u);
       o.xmask[b] = (o.epoch << 16) | mk;
     }
-    register_blocks(o, leader, (uint32_t)b);
-  }
+  });
 }
 
 // Dense x (decode, section 4.1): one ballot per wave gives the nonzero
@@ -129,10 +83,8 @@ __global__ __launch_bounds__(KT) void k_xmeta_dense(MetaOut o, const void *x) {
   if (blockIdx.x == 0 && threadIdx.x < 8) o.ctr_next[threadIdx.x] = 0;
   clear_y(o);
   const int lane = __lane_id();
-  const int64_t gs = (int64_t)gridDim.x * KT;
   const int64_t npad = (int64_t)o.nb * 16;
-  for (int64_t base = (int64_t)blockIdx.x * KT; base < npad; base += gs) {
-    const int64_t j = base + threadIdx.x;
+  dbs_meta::register_blocks(o.reg, npad, [&](int64_t j, int pass, bool &leader, uint32_t &b) {
     bool nz = false;
     if (j < o.n) {
       if (VK == VK_BF16) nz = (((const uint16_t *)x)[j] & 0x7FFFu) != 0u;
@@ -141,10 +93,10 @@ __global__ __launch_bounds__(KT) void k_xmeta_dense(MetaOut o, const void *x) {
     const uint64_t bal = __ballot(nz);
     const uint32_t mk = (uint32_t)(bal >> (lane & 48)) & 0xFFFFu;
     const bool head = (lane & 15) == 0 && j < npad;
-    const uint32_t b = (uint32_t)(j >> 4);
-    if (head) o.xmask[b] = (o.epoch << 16) | mk;
-    register_blocks(o, head && mk != 0u, b);
-  }
+    b = (uint32_t)(j >> 4);
+    leader = head && mk != 0u;
+    if (pass == 0 && head) o.xmask[b] = (o.epoch << 16) | mk;
+  });
 }
 
 __global__ void k_fill_u32(uint32_t *p, int64_t n, uint32_t v) {
@@ -161,7 +113,7 @@ struct SpmvParams {
   const uint8_t *payload;
   uint64_t dense_mask_off;
   const uint32_t *segs;
-  int64_t nseg;
+  int64_t nseg, T, payload_bytes;
   int32_t m, nb;
   const uint32_t *xmask;
   uint32_t epoch;
@@ -213,7 +165,7 @@ DBS_DEV void push_chunk(const SpmvParams &P, uint64_t own, float *sx, float *spa
     const uint8_t *base = P.payload + meta_vp(meta);
     const uint32_t nnz = meta_nnz(meta);
     if (SR == DBS_OR_AND) {
-      const uint32_t f = coo_or(base, nnz, m);
+      const uint32_t f = coo_or_meta(P.payload, meta, m);
       for (uint32_t ff = f; ff; ff &= ff - 1u) {
         const uint32_t row = rb * 16u + (uint32_t)(__ffs(ff) - 1);
         ((uint8_t *)P.y)[row] = 1;
@@ -221,11 +173,19 @@ DBS_DEV void push_chunk(const SpmvParams &P, uint64_t own, float *sx, float *spa
     } else {
       constexpr int VS = VK == VK_F32 ? 4 : 2;
       const uint8_t *vals = base + coo_val_off(nnz);
-      for (uint32_t e = 0; e < nnz; ++e) {
-        const uint32_t rc = base[e];
-        const uint32_t c = rc & 15u;
-        if ((m >> c) & 1u)
-          unsafeAtomicAdd((float *)P.y + rb * 16u + (rc >> 4), load_a<VK>(vals + e * VS) * sx[c]);
+      for (uint32_t e0 = 0; e0 < nnz; e0 += 8) {  // 8 entries per round of independent loads
+        const uint32_t w0 = ((const uint32_t *)base)[e0 >> 2];
+        const uint32_t w1 = e0 + 4 < nnz ? ((const uint32_t *)base)[(e0 >> 2) + 1] : 0u;
+        float a[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) a[k] = e0 + k < nnz ? load_a<VK>(vals + (e0 + k) * VS) : 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const uint32_t rc = ((k < 4 ? w0 : w1) >> (8 * (k & 3))) & 0xFFu;
+          const uint32_t c = rc & 15u;
+          if (e0 + k < nnz && ((m >> c) & 1u))
+            unsafeAtomicAdd((float *)P.y + rb * 16u + (rc >> 4), a[k] * sx[c]);
+        }
       }
     }
   }
@@ -256,27 +216,18 @@ DBS_DEV void push_chunk(const SpmvParams &P, uint64_t own, float *sx, float *spa
 // once: a plain store when the row block is one segment, an atomic add when
 // several segments share it.
 // ---------------------------------------------------------------------------
+// Finish one segment whose tiles are loaded: COO tiles one per lane, larger
+// tiles by the whole wave, merge in registers, write the row block.
 template <int VK, int SR>
-DBS_DEV void pull_segment(const SpmvParams &P, int64_t s, float *sx, float *spart, int lane) {
-  const uint4 seg = ((const uint4 *)P.segs)[s];
+DBS_DEV void pull_finish(const SpmvParams &P, uint4 seg, uint32_t cb, uint32_t m, uint64_t meta, bool act,
+                         uint32_t pw0, uint32_t pw1, float *sx, float *spart, int lane) {
   const uint32_t rb = seg.x & ~SEG_SPLIT;
   const bool split = (seg.x & SEG_SPLIT) != 0u;
-  const uint32_t t = seg.y + (uint32_t)lane;
-  bool act = t < seg.z;
-  uint32_t cb = 0, m = 0;
-  uint64_t meta = 0;
-  if (act) {
-    cb = P.t_cb[t];
-    const uint32_t w = P.xmask[cb];
-    m = (w >> 16) == P.epoch ? (w & 0xFFFFu) : 0u;
-    act = m != 0u;
-    if (act) meta = P.t_meta[t];
-  }
   const uint32_t type = meta_type(meta);
   const int64_t row0 = (int64_t)rb * 16;
   if (SR == DBS_OR_AND) {
     uint32_t f = 0;
-    if (act && type == DBS_TILE_COO) f = coo_or(P.payload + meta_vp(meta), meta_nnz(meta), m);
+    if (act && type == DBS_TILE_COO) f = coo_or_pre(P.payload, meta, m, pw0, pw1);
     f = group_or_u32<64>(f);
     uint64_t todo = __ballot(act && type != DBS_TILE_COO);
     while (todo) {
@@ -318,11 +269,133 @@ DBS_DEV void pull_segment(const SpmvParams &P, int64_t s, float *sx, float *spar
   }
 }
 
+// ---------------------------------------------------------------------------
+// Pull: static segments of one row block each (section 3.3.2).  A wave takes
+// U consecutive segments and issues each load phase for all of them before
+// using any result (descriptors; column blocks and, when most vector blocks
+// are active, metadata; masks; remaining metadata), so U independent
+// dependency chains overlap in every wave.  The row block's partial is merged
+// in registers and written once: a plain store when the row block is one
+// segment, an atomic add when several segments share it.
+// ---------------------------------------------------------------------------
+template <int VK, int SR, int U>
+DBS_DEV void pull_group(const SpmvParams &P, int64_t s0, bool eager, float *sx, float *spart, int lane) {
+  // Loads are issued without branches (inactive lanes read a valid dummy
+  // address and discard the value): a branch around a load makes the
+  // compiler wait for every outstanding load at the branch.
+  uint4 seg[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t si = s0 + u < P.nseg ? s0 + u : P.nseg - 1;  // wave-uniform: scalar loads
+    seg[u] = ((const uint4 *)P.segs)[si];
+  }
+  uint32_t cb[U], m[U];
+  uint64_t meta[U];
+  bool act[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint32_t t = seg[u].y + (uint32_t)lane;
+    act[u] = s0 + u < P.nseg && t < seg[u].z;
+    const uint32_t tc = act[u] ? t : seg[u].y;
+    cb[u] = P.t_cb[tc];
+    meta[u] = eager ? P.t_meta[tc] : 0ull;
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint32_t w = P.xmask[cb[u]];
+    m[u] = act[u] && (w >> 16) == P.epoch ? (w & 0xFFFFu) : 0u;
+    act[u] = m[u] != 0u;
+  }
+  if (!eager) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) meta[u] = P.t_meta[act[u] ? seg[u].y + (uint32_t)lane : seg[u].y];
+  }
+  uint32_t pw0[U], pw1[U];
+  if (SR == DBS_OR_AND) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) coo_preload(P.payload, meta[u], act[u], pw0[u], pw1[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (s0 + u < P.nseg)
+      pull_finish<VK, SR>(P, seg[u], cb[u], m[u], meta[u], act[u], SR == DBS_OR_AND ? pw0[u] : 0u,
+                          SR == DBS_OR_AND ? pw1[u] : 0u, sx, spart, lane);
+}
+
+// OR-AND pull (the Boolean semiring of graph traversal): as pull_group, with
+// buffer loads, out-of-range offsets for idle lanes, guard-free COO decoding
+// and a DPP wave OR, which keeps the per-tile instruction count small enough
+// for the hypersparse tiles of power-law graphs (mostly 1-4 entries).
+// buffer descriptors of the arrays the pull reads per tile (built in the kernel)
+struct PullRes {
+  brsrc_t tcb, tmeta, pay, xmask;
+};
+
+template <int VK, int U>
+DBS_DEV void pull_or_group(const SpmvParams &P, const PullRes &R, int64_t s0, bool eager, int lane) {
+  uint4 seg[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t si = s0 + u < P.nseg ? s0 + u : P.nseg - 1;
+    seg[u] = ((const uint4 *)P.segs)[si];
+  }
+  uint32_t cb[U], m[U], pw0[U], pw1[U];
+  uint64_t meta[U];
+  bool act[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint32_t t = seg[u].y + (uint32_t)lane;
+    act[u] = s0 + u < P.nseg && t < seg[u].z;
+    cb[u] = bld32(R.tcb, act[u] ? t * 4u : OOB_OFF);
+    meta[u] = eager ? bld64(R.tmeta, act[u] ? t * 8u : OOB_OFF) : 0ull;
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint32_t w = bld32(R.xmask, act[u] ? cb[u] * 4u : OOB_OFF);
+    m[u] = act[u] && (w >> 16) == P.epoch ? (w & 0xFFFFu) : 0u;
+    act[u] = m[u] != 0u;
+  }
+  if (!eager) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) meta[u] = bld64(R.tmeta, act[u] ? (seg[u].y + (uint32_t)lane) * 8u : OOB_OFF);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const bool pre = act[u] && meta_type(meta[u]) == DBS_TILE_COO && !meta_inline(meta[u]);
+    const uint32_t off = pre ? (uint32_t)meta_vp(meta[u]) : OOB_OFF;
+    pw0[u] = bld32(R.pay, off);
+    pw1[u] = bld32(R.pay, pre && meta_nnz(meta[u]) > 4 ? off + 4u : OOB_OFF);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (s0 + u >= P.nseg) break;
+    uint32_t f = lane_coo_or(P.payload, meta[u], m[u], act[u], pw0[u], pw1[u]);
+    uint64_t todo = __ballot(act[u] && meta_type(meta[u]) != DBS_TILE_COO);
+    while (todo) {
+      const int src = __ffsll((unsigned long long)todo) - 1;
+      todo &= todo - 1;
+      const uint64_t tm = __shfl(meta[u], src);
+      const uint32_t tmask = (uint32_t)__shfl((int)m[u], src);
+      f |= tile_or<VK>(P.payload + meta_vp(tm), dense_mask_ptr<VK>(P, meta_vp(tm)), meta_type(tm), tmask,
+                       lane);
+    }
+    f = wave_or(f);
+    const uint32_t rb = seg[u].x & ~SEG_SPLIT;
+    const int64_t row = (int64_t)rb * 16 + lane;
+    if (lane < 16 && row < P.m) {
+      const uint8_t bit = (uint8_t)((f >> lane) & 1u);
+      if (!(seg[u].x & SEG_SPLIT)) ((uint8_t *)P.y)[row] = bit;
+      else if (bit) ((uint8_t *)P.y)[row] = 1;
+    }
+  }
+}
+
 template <int VK, int SR>
 __global__ __launch_bounds__(KT) void k_spmspv(SpmvParams P) {
   __shared__ float s_x[KT / DBS_WAVE][16];
   __shared__ float s_part[KT / DBS_WAVE][64];
-  const int lane = __lane_id(), w = threadIdx.x / DBS_WAVE;
+  const int lane = __lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / DBS_WAVE);
   const uint32_t nz = P.ctr[0];
   const bool push = P.force_path == 1 ||
                     (P.force_path == 0 && (int64_t)nz * P.th3_den < (int64_t)P.nb * P.th3_num);
@@ -332,7 +405,20 @@ __global__ __launch_bounds__(KT) void k_spmspv(SpmvParams P) {
     const int64_t nch = (int64_t)P.ctr[1] < P.max_chunks ? (int64_t)P.ctr[1] : P.max_chunks;
     for (int64_t c = gw; c < nch; c += nw) push_chunk<VK, SR>(P, P.chunks[c], s_x[w], s_part[w], lane);
   } else {
-    for (int64_t s = gw; s < P.nseg; s += nw) pull_segment<VK, SR>(P, s, s_x[w], s_part[w], lane);
+    // metadata of every tile is loaded up front once most vector blocks are active
+    const bool eager = (int64_t)nz * 4 > (int64_t)P.nb;
+    if (SR == DBS_OR_AND) {
+      constexpr int U = 8;
+      PullRes R;
+      R.tcb = make_rsrc(P.t_cb, (uint64_t)P.T * 4);
+      R.tmeta = make_rsrc(P.t_meta, (uint64_t)P.T * 8);
+      R.pay = make_rsrc(P.payload, (uint64_t)P.payload_bytes);
+      R.xmask = make_rsrc(P.xmask, (uint64_t)P.nb * 4);
+      for (int64_t s = gw * U; s < P.nseg; s += nw * U) pull_or_group<VK, U>(P, R, s, eager, lane);
+    } else {
+      constexpr int U = 4;
+      for (int64_t s = gw * U; s < P.nseg; s += nw * U) pull_group<VK, SR, U>(P, s, eager, s_x[w], s_part[w], lane);
+    }
   }
 }
 
@@ -343,8 +429,9 @@ inline unsigned grid_for(int64_t waves, unsigned cap) {
 }
 
 template <int VK, int SR>
-void launch_spmspv(const SpmvParams &P, unsigned grid, hipStream_t s) {
-  hipLaunchKernelGGL((k_spmspv<VK, SR>), dim3(grid), dim3(KT), 0, s, P);
+void launch_spmspv(const SpmvParams &P, int64_t waves, hipStream_t s) {
+  static const unsigned resident = dbs_resident_groups(k_spmspv<VK, SR>, KT);
+  hipLaunchKernelGGL((k_spmspv<VK, SR>), dim3(grid_for(waves, resident)), dim3(KT), 0, s, P);
 }
 
 }  // namespace
@@ -368,14 +455,15 @@ dbs_status dbs_spmspv_impl(dbs_matrix *A, int32_t nnz_x, const int32_t *x_idx, c
   MetaOut o;
   o.xmask = A->xmask;
   o.epoch = A->epoch;
-  o.act_list = A->act_list;
-  o.chunks = A->chunks;
-  o.ctr = A->ctr + 8 * A->cbuf;
+  o.reg.ctr = A->ctr + 8 * A->cbuf;
+  o.reg.list = A->act_list;
+  o.reg.chunks = A->chunks;
+  o.reg.list_cap = A->nb;
+  o.reg.chunk_cap = A->max_chunks;
+  o.reg.cb_ptr = A->cb_ptr;
   o.ctr_next = A->ctr + 8 * (1 - A->cbuf);
-  o.cb_ptr = A->cb_ptr;
   o.n = A->n;
   o.nb = A->nb;
-  o.max_chunks = A->max_chunks;
   const int64_t ybytes = (int64_t)A->m * (sr == DBS_OR_AND ? 1 : 4);
   o.y = (uint8_t *)y;
   int64_t head = (int64_t)((16 - ((uintptr_t)y & 15)) & 15);
@@ -386,17 +474,19 @@ dbs_status dbs_spmspv_impl(dbs_matrix *A, int32_t nnz_x, const int32_t *x_idx, c
 
   const bool dense = x_dense != nullptr;
   const int64_t xwork = dense ? (int64_t)A->nb * 16 : (int64_t)nnz_x;
-  int64_t mwork = xwork > o.y_body ? xwork : o.y_body;
-  unsigned mgrid = (unsigned)((mwork + KT - 1) / KT);
-  if (mgrid < 1) mgrid = 1;
-  if (mgrid > 2048) mgrid = 2048;
+  const unsigned mgrid = dbs_meta::groups_for(xwork, o.y_body);
 
   // metadata uses the value kind of x: the matrix kind, or f32 for a
   // dense x on a pattern matrix
   int xk = A->vk;
   if (xk == VK_PAT) xk = dense ? VK_F32 : VK_PAT;
 
-  if (timing) SPMV_TRY(hipEventRecord(A->ev[0], s));
+  hipEvent_t *tev = nullptr;
+  if (timing) {
+    tev = dbs_timing_slot(A);
+    if (!tev) return DBS_ERR_DEVICE;
+    SPMV_TRY(hipEventRecord(tev[0], s));
+  }
   if (dense) {
     if (xk == VK_BF16) hipLaunchKernelGGL(k_xmeta_dense<VK_BF16>, dim3(mgrid), dim3(KT), 0, s, o, x_dense);
     else hipLaunchKernelGGL(k_xmeta_dense<VK_F32>, dim3(mgrid), dim3(KT), 0, s, o, x_dense);
@@ -411,9 +501,11 @@ dbs_status dbs_spmspv_impl(dbs_matrix *A, int32_t nnz_x, const int32_t *x_idx, c
       hipLaunchKernelGGL(k_xmeta_sparse<VK_PAT>, dim3(mgrid), dim3(KT), 0, s, o, nnz_x, x_idx, xv, A->xd, check);
   }
   SPMV_TRY(hipGetLastError());
-  if (timing) SPMV_TRY(hipEventRecord(A->ev[1], s));
+  if (timing) SPMV_TRY(hipEventRecord(tev[1], s));
 
   SpmvParams P;
+  P.T = A->T;
+  P.payload_bytes = A->payload_bytes;
   P.t_cb = A->t_cb;
   P.t_meta = A->t_meta;
   P.cb_ptr = A->cb_ptr;
@@ -430,26 +522,24 @@ dbs_status dbs_spmspv_impl(dbs_matrix *A, int32_t nnz_x, const int32_t *x_idx, c
   P.xd = dense ? x_dense : A->xd;
   P.chunks = A->chunks;
   P.max_chunks = A->max_chunks;
-  P.ctr = o.ctr;
+  P.ctr = o.reg.ctr;
   P.force_path = (int32_t)A->opt[DBS_OPT_PATH];
   P.th3_num = A->opt[DBS_OPT_TH3_NUM];
   P.th3_den = A->opt[DBS_OPT_TH3_DEN];
   P.local_cutoff = (int32_t)A->opt[DBS_OPT_LOCAL_PUSH_CUTOFF];
   P.y = y;
-  const int64_t waves = A->nseg > A->max_chunks ? A->nseg : A->max_chunks;
-  const unsigned grid = grid_for(waves, 2048);
+  const int64_t waves = (A->nseg + 3) / 4 > A->max_chunks ? (A->nseg + 3) / 4 : A->max_chunks;
   const int vk = A->vk;
   if (sr == DBS_OR_AND) {
-    if (vk == VK_F32) launch_spmspv<VK_F32, DBS_OR_AND>(P, grid, s);
-    else if (vk == VK_BF16) launch_spmspv<VK_BF16, DBS_OR_AND>(P, grid, s);
-    else launch_spmspv<VK_PAT, DBS_OR_AND>(P, grid, s);
+    if (vk == VK_F32) launch_spmspv<VK_F32, DBS_OR_AND>(P, waves, s);
+    else if (vk == VK_BF16) launch_spmspv<VK_BF16, DBS_OR_AND>(P, waves, s);
+    else launch_spmspv<VK_PAT, DBS_OR_AND>(P, waves, s);
   } else {
-    if (vk == VK_F32) launch_spmspv<VK_F32, DBS_PLUS_TIMES>(P, grid, s);
-    else launch_spmspv<VK_BF16, DBS_PLUS_TIMES>(P, grid, s);
+    if (vk == VK_F32) launch_spmspv<VK_F32, DBS_PLUS_TIMES>(P, waves, s);
+    else launch_spmspv<VK_BF16, DBS_PLUS_TIMES>(P, waves, s);
   }
   SPMV_TRY(hipGetLastError());
-  if (timing) SPMV_TRY(hipEventRecord(A->ev[2], s));
-  A->timing_pending = timing ? 1 : 0;
+  if (timing) SPMV_TRY(hipEventRecord(tev[2], s));
   A->cbuf ^= 1;
   A->last_stream = s;
   A->st.last_path = -2;  // resolved from the device counters by dbs_get_stats

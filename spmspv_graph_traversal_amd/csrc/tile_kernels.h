@@ -14,6 +14,44 @@
 
 #include "common.h"
 
+// ---------------------------------------------------------------------------
+// Raw buffer loads: a 128-bit descriptor (base, size) in SGPRs and a 32-bit
+// byte offset per lane.  Reads past the size return 0 without touching
+// memory, so an idle lane passes OOB_OFF instead of branching around the
+// load (a branch around a load makes the compiler wait for every load in
+// flight), and no 64-bit address arithmetic is spent per lane.
+// ---------------------------------------------------------------------------
+#define OOB_OFF 0xFFFFFFF0u
+typedef __amdgpu_buffer_rsrc_t brsrc_t;
+
+DBS_DEV brsrc_t make_rsrc(const void *p, uint64_t bytes) {
+  const uint32_t n = bytes >= 0xFFFFFFF0ull ? 0xFFFFFFF0u : (uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc((void *)p, (short)0, (int)n, 0x00020000);
+}
+DBS_DEV uint32_t bld32(brsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0); }
+DBS_DEV uint64_t bld64(brsrc_t r, uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+  return (uint64_t)v[0] | ((uint64_t)v[1] << 32);
+}
+
+extern "C" __device__ uint32_t __ockl_wfred_or_u32(uint32_t);
+// OR over the 64 lanes of the wave (DPP row shifts + row mirror); uniform result
+DBS_DEV uint32_t wave_or(uint32_t v) { return __ockl_wfred_or_u32(v); }
+
+// OR-AND contribution of four coordinate bytes (row << 4 | col) under the
+// x-block mask m.  Unused bytes of a tile repeat its last entry, so all four
+// are decoded unconditionally (OR is idempotent).
+DBS_DEV uint32_t coo_or4(uint32_t w, uint32_t m) {
+  uint32_t f = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t c = (w >> (8 * k)) & 15u;
+    const uint32_t r = (w >> (8 * k + 4)) & 15u;
+    f |= ((m >> c) & 1u) << r;
+  }
+  return f;
+}
+
 template <int VK>
 DBS_DEV float load_a(const uint8_t *p) {
   if (VK == VK_F32) return *(const float *)p;
@@ -196,31 +234,107 @@ DBS_DEV uint32_t tile_or(const uint8_t *base, const uint8_t *dense_mask, uint32_
 // ---------------------------------------------------------------------------
 // COO (section 3.3.3: scan the packed coordinates), one tile per lane.
 // ---------------------------------------------------------------------------
-// PLUS_TIMES, accumulated into the lane's 16 row registers
+// PLUS_TIMES, accumulated into the lane's 16 row registers.  Coordinates and
+// values are read 8 entries at a time with independent loads (the COO
+// payload is 4-B aligned), then the x values of those entries, so a tile
+// costs two memory round trips per 8 entries instead of one per entry.
 template <int VK>
 DBS_DEV void coo_plus(const uint8_t *base, uint32_t nnz, uint32_t m, const void *xd, int64_t xbase,
                       float (&acc)[16]) {
   constexpr int VS = VK == VK_F32 ? 4 : 2;
   const uint8_t *vals = base + coo_val_off(nnz);
-  for (uint32_t e = 0; e < nnz; ++e) {
-    const uint32_t rc = base[e];
-    const uint32_t c = rc & 15u;
-    if ((m >> c) & 1u) {
-      const uint32_t rr = rc >> 4;
-      const float t = load_a<VK>(vals + e * VS) * load_x<VK>(xd, xbase + c);
+  const uint32_t lastw = (nnz - 1) >> 2;
+  for (uint32_t e0 = 0; e0 < nnz; e0 += 8) {
+    // clamped indices everywhere: no branch around a load
+    const uint32_t w0 = ((const uint32_t *)base)[e0 >> 2];
+    const uint32_t w1 = ((const uint32_t *)base)[((e0 >> 2) + 1) < lastw ? (e0 >> 2) + 1 : lastw];
+    float a[8], xv[8];
+    uint32_t rc[8];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) acc[k] += (rr == (uint32_t)k) ? t : 0.0f;
+    for (int k = 0; k < 8; ++k) {
+      rc[k] = ((k < 4 ? w0 : w1) >> (8 * (k & 3))) & 0xFFu;
+      const uint32_t e = e0 + k < nnz ? e0 + k : nnz - 1;
+      a[k] = load_a<VK>(vals + e * VS);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t c = rc[k] & 15u;
+      const bool on = e0 + k < nnz && ((m >> c) & 1u);
+      const float v = load_x<VK>(xd, xbase + (on ? c : 0u));
+      xv[k] = on ? v : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t c = rc[k] & 15u, rr = rc[k] >> 4;
+      if (e0 + k < nnz && ((m >> c) & 1u)) {
+        const float t = a[k] * xv[k];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[q] += (rr == (uint32_t)q) ? t : 0.0f;
+      }
     }
   }
 }
 
+// OR-AND of a COO tile from its (4-B aligned) coordinate bytes, 32 entries
+// per round of independent loads
 DBS_DEV uint32_t coo_or(const uint8_t *base, uint32_t nnz, uint32_t m) {
   uint32_t f = 0;
-  for (uint32_t e = 0; e < nnz; ++e) {
-    const uint32_t rc = base[e];
-    if ((m >> (rc & 15u)) & 1u) f |= 1u << (rc >> 4);
+  const uint32_t *w = (const uint32_t *)base;
+  const uint32_t last = (nnz - 1) >> 2;  // last word of the tile
+  for (uint32_t e0 = 0; e0 < nnz; e0 += 32) {
+    uint32_t v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {  // clamped word index: no branch around the loads
+      const uint32_t wi = (e0 >> 2) + k;
+      v[k] = w[wi < last ? wi : last];
+    }
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      const uint32_t rc = (v[k >> 2] >> (8 * (k & 3))) & 0xFFu;
+      if (e0 + k < nnz && ((m >> (rc & 15u)) & 1u)) f |= 1u << (rc >> 4);
+    }
   }
   return f;
+}
+
+// OR-AND of a COO tile whose first 8 coordinate bytes were loaded ahead
+// (pw0, pw1); entries beyond the eighth are read here.
+DBS_DEV uint32_t coo_or_pre(const uint8_t *payload, uint64_t meta, uint32_t m, uint32_t pw0, uint32_t pw1) {
+  const uint32_t nnz = meta_nnz(meta);
+  if (meta_inline(meta)) pw0 = (uint32_t)meta;
+  uint32_t f = 0;
+#pragma unroll
+  for (uint32_t e = 0; e < 8; ++e) {
+    const uint32_t rc = ((e < 4 ? pw0 : pw1) >> (8 * (e & 3))) & 0xFFu;
+    if (e < nnz && ((m >> (rc & 15u)) & 1u)) f |= 1u << (rc >> 4);
+  }
+  if (nnz > 8) f |= coo_or(payload + meta_vp(meta) + 8, nnz - 8, m);
+  return f;
+}
+
+// first two payload words of a COO tile that is not inline (else of the
+// arena start, a valid dummy), loaded without a branch
+DBS_DEV void coo_preload(const uint8_t *payload, uint64_t meta, bool act, uint32_t &pw0, uint32_t &pw1) {
+  const bool pre = act && meta_type(meta) == DBS_TILE_COO && !meta_inline(meta);
+  const uint32_t *w = (const uint32_t *)(payload + (pre ? meta_vp(meta) : 0));
+  pw0 = w[0];
+  pw1 = w[1];
+}
+
+// OR-AND of a COO tile given its metadata word (coordinates inline or in the payload)
+DBS_DEV uint32_t coo_or_meta(const uint8_t *payload, uint64_t meta, uint32_t m) {
+  const uint32_t nnz = meta_nnz(meta);
+  if (meta_inline(meta)) {
+    const uint32_t w = (uint32_t)meta;
+    uint32_t f = 0;
+#pragma unroll
+    for (uint32_t e = 0; e < COO_INLINE; ++e) {
+      const uint32_t rc = (w >> (8 * e)) & 0xFFu;
+      if (e < nnz && ((m >> (rc & 15u)) & 1u)) f |= 1u << (rc >> 4);
+    }
+    return f;
+  }
+  return coo_or(payload + meta_vp(meta), nnz, m);
 }
 
 // Sum of the 16 per-lane row registers over the wave; row k's total ends in
@@ -252,4 +366,30 @@ DBS_DEV float wave_rows_reduce(float (&acc)[16], int lane) {
   v += __shfl_xor(v, 1);
   // lanes 4k..4k+3 hold row k
   return __shfl(v, (lane & 15) * 4);
+}
+
+// ---------------------------------------------------------------------------
+// OR-AND contribution of the COO tile held by this lane (pull and push),
+// given the metadata word and the first two payload words loaded ahead (pw0,
+// pw1; only meaningful for COO tiles that are not inline).  Called by every
+// lane of the wave.
+// ---------------------------------------------------------------------------
+DBS_DEV uint32_t lane_coo_or(const uint8_t *payload, uint64_t meta, uint32_t m, bool act, uint32_t pw0,
+                             uint32_t pw1) {
+  const bool coo = act && meta_type(meta) == DBS_TILE_COO;
+  const bool inl = meta_inline(meta);
+  const uint32_t w0 = inl ? (uint32_t)meta : pw0;
+  uint32_t f = coo ? coo_or4(w0, m) : 0u;
+  const uint32_t nnz = meta_nnz(meta);
+  const bool big = coo && !inl && nnz > 4;  // second word: entries 4..7 (values follow a
+                                            // 4-entry COO tile of a value matrix)
+  if (__ballot(big) != 0ull) {
+    f |= big ? coo_or4(pw1, m) : 0u;
+    if (__ballot(big && nnz > 8) != 0ull && big && nnz > 8) {
+      const uint32_t *w = (const uint32_t *)(payload + meta_vp(meta));
+      const uint32_t lastw = (nnz - 1) >> 2;
+      for (uint32_t k = 2; k <= lastw; ++k) f |= coo_or4(w[k], m);
+    }
+  }
+  return f;
 }

@@ -43,7 +43,15 @@ def decode(arrs, vk, n_dense):
     for t in range(T):
         p, k, ty = int(vp[t]), int(nnz[t]), int(typ[t])
         r0, c0 = int(rb_of[t]) * 16, int(arrs["t_cb"][t]) * 16
-        if ty == COO:
+        if ty == COO and (int(meta[t]) >> 51) & 1:
+            # up to four coordinate bytes stored in the metadata word (pattern matrices)
+            assert vk == 2 and k <= 4, f"inline COO tile {t} on a value matrix or with {k} entries"
+            co = np.array([(int(meta[t]) >> (8 * e)) & 0xFF for e in range(k)], np.int64)
+            rr, cc = co >> 4, co & 15
+            assert np.all(np.diff(rr * 16 + cc) > 0), f"COO coords not row-major at tile {t}"
+            vv = None
+        elif ty == COO:
+            assert not (vk == 2 and k <= 4), f"small pattern COO tile {t} not inline"
             co = pay[p:p + k].astype(np.int64)
             rr, cc = co >> 4, co & 15
             assert np.all(np.diff(rr * 16 + cc) > 0), f"COO coords not row-major at tile {t}"
