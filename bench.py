@@ -372,7 +372,19 @@ def main():
     ap.add_argument("--bfs-sources", type=int, default=64)
     ap.add_argument("--decode-copies", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only a plain 256 MiB device copy (x3), the reference for scaling HBM byte counters")
     args = ap.parse_args()
+    if args.copy_probe:
+        import torch
+
+        a = torch.ones(64 * 1024 * 1024, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_per_copy": 4 * a.numel(), "copies": 3}))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the method has no multi-GPU path here (--gpus {args.gpus} "
               "requested); run with --gpus 1.", file=sys.stderr)
