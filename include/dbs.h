@@ -85,7 +85,9 @@ typedef struct {
   int32_t seg_w_coo;      /*   COO (default 1) */
   int32_t seg_cap;        /* a segment closes at the tile bringing its weight to >= cap.
                              Default 64: one 64-lane wave works on a segment, one COO tile
-                             per lane (the pages' 32-lane warps use 16). */
+                             per lane (the pages' 32-lane warps use 16).  Range 1..64 (a
+                             segment holds at most seg_cap tiles, one per lane); other
+                             values give DBS_ERR_INVALID_ARG. */
 } dbs_build_options;
 
 /* Fills `opt` with the defaults above.  Never fails for a non-NULL pointer. */
@@ -166,7 +168,8 @@ enum {
   DBS_OPT_TH3_NUM = 1,           /* th3 = num / den (default 1 / 100): push iff */
   DBS_OPT_TH3_DEN = 2,           /*   N_nzblk * den < N_blk * num              */
   DBS_OPT_LOCAL_PUSH_CUTOFF = 3, /* patched-CSR tiles use the column (push) microkernel
-                                    when popcount(blk_x_mask) < cutoff (default 8) */
+                                    when popcount(blk_x_mask) < cutoff (default 0: always
+                                    the row microkernel, the faster one on this GPU) */
   DBS_OPT_TIMING = 4,            /* 1: time the kernels of each call with HIP events (setting
                                     it, to 0 or 1, also clears the sums in dbs_stats) */
   DBS_OPT_CHECK = 5              /* 1: validate x_idx ordering on the device */

@@ -53,6 +53,7 @@ class dbs_stats(C.Structure):
         ("format_bytes", C.c_int64), ("build_peak_bytes", C.c_int64),
         ("last_path", C.c_int32), ("last_n_nzblk", C.c_int32), ("last_push_chunks", C.c_int64),
         ("last_meta_ms", C.c_float), ("last_compute_ms", C.c_float),
+        ("timed_calls", C.c_int64), ("sum_meta_ms", C.c_double), ("sum_compute_ms", C.c_double),
         ("bfs_levels", C.c_int32), ("bfs_push_levels", C.c_int32), ("bfs_reached", C.c_int64),
         ("bfs_ms", C.c_float), ("bfs_kernel_ms", C.c_float),
     ]

@@ -92,6 +92,7 @@ bool valid_options(const dbs_build_options &o) {
   if (o.th0 < 0 || o.th1 < 0 || o.th2_num <= 0 || o.th2_den <= 0) return false;
   if (o.force_format < -1 || o.force_format > DBS_TILE_CSR) return false;
   if (o.seg_w_dense < 1 || o.seg_w_csr < 1 || o.seg_w_coo < 1 || o.seg_cap < 1) return false;
+  if (o.seg_cap > DBS_WAVE) return false;  // at most one tile per lane in a pull segment
   return true;
 }
 
@@ -176,7 +177,7 @@ dbs_status dbs_build(int32_t m, int32_t n, int64_t nnz, const int32_t *row_ptr, 
   A->opt[DBS_OPT_PATH] = 0;
   A->opt[DBS_OPT_TH3_NUM] = 1;
   A->opt[DBS_OPT_TH3_DEN] = 100;
-  A->opt[DBS_OPT_LOCAL_PUSH_CUTOFF] = 8;
+  A->opt[DBS_OPT_LOCAL_PUSH_CUTOFF] = 0;
   A->opt[DBS_OPT_TIMING] = 0;
   A->opt[DBS_OPT_CHECK] = 0;
   A->st.last_path = -1;

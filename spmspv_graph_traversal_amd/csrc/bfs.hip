@@ -187,11 +187,11 @@ __global__ __launch_bounds__(KT) void k_bfs_level(BfsParams P) {
 
 // Frontier metadata: nonzero blocks of `bm`, their list and push chunks;
 // clears `clr_bm` / `clr_ctr` (the buffers two levels back) when given.
-__global__ __launch_bounds__(KT) void k_bfs_meta(const uint32_t *bm, int32_t nb, dbs_meta::Reg reg,
+__global__ __launch_bounds__(dbs_meta::MT) void k_bfs_meta(const uint32_t *bm, int32_t nb, dbs_meta::Reg reg,
                                                  uint32_t *clr_bm, uint32_t *clr_ctr, int64_t nwords) {
-  const int64_t gs = (int64_t)gridDim.x * KT;
+  const int64_t gs = (int64_t)gridDim.x * dbs_meta::MT;
   if (clr_bm) {
-    for (int64_t k = (int64_t)blockIdx.x * KT + threadIdx.x; k < nwords; k += gs) clr_bm[k] = 0;
+    for (int64_t k = (int64_t)blockIdx.x * dbs_meta::MT + threadIdx.x; k < nwords; k += gs) clr_bm[k] = 0;
     if (blockIdx.x == 0 && threadIdx.x < 8) clr_ctr[threadIdx.x] = 0;
   }
   dbs_meta::register_blocks(reg, nb, [&](int64_t b, int, bool &leader, uint32_t &bo) {
@@ -255,7 +255,7 @@ dbs_status dbs_bfs_impl(dbs_matrix *A, int32_t src, int32_t *levels, hipStream_t
     r.cb_ptr = A->cb_ptr;
     return r;
   };
-  hipLaunchKernelGGL(k_bfs_meta, dim3(mgrid), dim3(KT), 0, s, (const uint32_t *)A->bfs_bm, A->nb, reg_for(0),
+  hipLaunchKernelGGL(k_bfs_meta, dim3(mgrid), dim3(dbs_meta::MT), 0, s, (const uint32_t *)A->bfs_bm, A->nb, reg_for(0),
                      (uint32_t *)nullptr, (uint32_t *)nullptr, (int64_t)0);
   BFS_TRY(hipGetLastError());
 
@@ -301,7 +301,7 @@ dbs_status dbs_bfs_impl(dbs_matrix *A, int32_t src, int32_t *levels, hipStream_t
     else hipLaunchKernelGGL(k_bfs_level<VK_PAT>, dim3(grid), dim3(KT), 0, s, P);
     BFS_TRY(hipGetLastError());
     if (timing) BFS_TRY(hipEventRecord(A->ev[5], s));
-    hipLaunchKernelGGL(k_bfs_meta, dim3(mgrid), dim3(KT), 0, s, (const uint32_t *)P.next_bm, A->nb, reg_for(nxt),
+    hipLaunchKernelGGL(k_bfs_meta, dim3(mgrid), dim3(dbs_meta::MT), 0, s, (const uint32_t *)P.next_bm, A->nb, reg_for(nxt),
                        A->bfs_bm + clr * nwords, A->bfs_ctr + 8 * clr, nwords);
     BFS_TRY(hipGetLastError());
     BFS_TRY(hipMemcpyAsync(A->bfs_host, A->bfs_ctr + 8 * cur, 8, hipMemcpyDeviceToHost, s));

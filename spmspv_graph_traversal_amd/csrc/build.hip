@@ -445,7 +445,8 @@ dbs_status dbs_build_impl(dbs_matrix *A, const int32_t *row_ptr, const int32_t *
   if (vk != VK_PAT) total = A->dense_mask_off + 32ull * (dense_bytes / (256ull * (uint64_t)vk_size(vk)));
   if (total >= (1ull << 40)) return DBS_ERR_UNSUPPORTED;
   A->payload_bytes = (int64_t)total;
-  BUILD_TRY(dbs_dev_alloc(A, (void **)&A->payload, (size_t)total + 256));
+  BUILD_TRY(dbs_dev_alloc(A, (void **)&A->payload, (size_t)total + DBS_PAYLOAD_SLACK));
+  BUILD_TRY(hipMemsetAsync(A->payload + total, 0, DBS_PAYLOAD_SLACK, s));
   if (T > 0) {
     hipLaunchKernelGGL(k_pack_meta, dim3(nblocks(T, BT)), dim3(BT), 0, s, T, vk, t_nt, offs, A->t_meta);
     BUILD_TRY(hipGetLastError());

@@ -95,6 +95,9 @@ __host__ __device__ inline uint32_t tile_payload_bytes(int type, uint32_t nnz, i
 
 // Pull segment descriptor: {row block | split << 31, first tile, end tile, 0}.
 #define SEG_SPLIT 0x80000000u
+// zeroed bytes allocated after the payload: wide row loads that start inside
+// the last tile stay inside the allocation
+#define DBS_PAYLOAD_SLACK 256u
 
 // ---------------------------------------------------------------------------
 // The handle.

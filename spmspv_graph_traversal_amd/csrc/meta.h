@@ -15,8 +15,8 @@
 
 namespace dbs_meta {
 
-constexpr int MT = 256;          // threads per workgroup
-constexpr int MAX_GROUPS = 256;  // workgroups of a registration kernel
+constexpr int MT = 1024;         // threads per workgroup (16 waves: one round covers 1024 items)
+constexpr int MAX_GROUPS = 512;  // workgroups of a registration kernel (<= 512 atomics)
 
 struct Reg {
   uint32_t *ctr;  // [0] blocks (low word), [1] chunks (high word), 8-B aligned

@@ -30,7 +30,7 @@ struct MetaOut {
 };
 
 DBS_DEV void clear_y(const MetaOut &o) {
-  const int64_t gt = (int64_t)blockIdx.x * KT + threadIdx.x, gs = (int64_t)gridDim.x * KT;
+  const int64_t gt = (int64_t)blockIdx.x * blockDim.x + threadIdx.x, gs = (int64_t)gridDim.x * blockDim.x;
   if (gt < o.y_head) o.y[gt] = 0;
   uint4 *body = (uint4 *)(o.y + o.y_head);
   for (int64_t k = gt; k < o.y_body; k += gs) body[k] = make_uint4(0, 0, 0, 0);
@@ -40,7 +40,7 @@ DBS_DEV void clear_y(const MetaOut &o) {
 // Sparse x: sorted x_idx.  The first entry of each vector block (the leader)
 // builds the block's mask from the following entries.
 template <int VK>
-__global__ __launch_bounds__(KT) void k_xmeta_sparse(MetaOut o, int32_t nnz_x, const int32_t *x_idx,
+__global__ __launch_bounds__(dbs_meta::MT) void k_xmeta_sparse(MetaOut o, int32_t nnz_x, const int32_t *x_idx,
                                                      const void *x_val, void *xd, int check) {
   if (blockIdx.x == 0 && threadIdx.x < 8) o.ctr_next[threadIdx.x] = 0;
   clear_y(o);
@@ -79,7 +79,7 @@ __global__ __launch_bounds__(KT) void k_xmeta_sparse(MetaOut o, int32_t nnz_x, c
 // Dense x (decode, section 4.1): one ballot per wave gives the nonzero
 // pattern of 64 consecutive entries, i.e. the masks of four vector blocks.
 template <int VK>
-__global__ __launch_bounds__(KT) void k_xmeta_dense(MetaOut o, const void *x) {
+__global__ __launch_bounds__(dbs_meta::MT) void k_xmeta_dense(MetaOut o, const void *x, void *xd) {
   if (blockIdx.x == 0 && threadIdx.x < 8) o.ctr_next[threadIdx.x] = 0;
   clear_y(o);
   const int lane = __lane_id();
@@ -96,6 +96,12 @@ __global__ __launch_bounds__(KT) void k_xmeta_dense(MetaOut o, const void *x) {
     b = (uint32_t)(j >> 4);
     leader = head && mk != 0u;
     if (pass == 0 && head) o.xmask[b] = (o.epoch << 16) | mk;
+    // PLUS_TIMES: copy x into the block-padded staging vector (zero tail),
+    // so the multiply reads whole column quarters of every vector block
+    if (pass == 0 && xd && j < npad) {
+      if (VK == VK_BF16) ((uint16_t *)xd)[j] = j < o.n ? ((const uint16_t *)x)[j] : (uint16_t)0;
+      else ((float *)xd)[j] = j < o.n ? ((const float *)x)[j] : 0.0f;
+    }
   });
 }
 
@@ -218,6 +224,9 @@ DBS_DEV void push_chunk(const SpmvParams &P, uint64_t own, float *sx, float *spa
 // ---------------------------------------------------------------------------
 // Finish one segment whose tiles are loaded: COO tiles one per lane, larger
 // tiles by the whole wave, merge in registers, write the row block.
+constexpr int PULL_U_PLUS = 1;  // segments per wave step, PLUS_TIMES pull
+constexpr int PULL_U_OR = 8;    // segments per wave step, OR_AND pull
+
 template <int VK, int SR>
 DBS_DEV void pull_finish(const SpmvParams &P, uint4 seg, uint32_t cb, uint32_t m, uint64_t meta, bool act,
                          uint32_t pw0, uint32_t pw1, float *sx, float *spart, int lane) {
@@ -244,13 +253,27 @@ DBS_DEV void pull_finish(const SpmvParams &P, uint4 seg, uint32_t cb, uint32_t m
       else if (bit) ((uint8_t *)P.y)[row0 + lane] = 1;
     }
   } else {
-    float acc[16];
+    constexpr uint64_t VS = VK == VK_F32 ? 4 : 2;
+    float rowsum = 0.0f;
+    const bool coo = act && type == DBS_TILE_COO;
+    if (__ballot(coo) != 0ull) {
+      float acc[16];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) acc[k] = 0.0f;
-    if (act && type == DBS_TILE_COO)
-      coo_plus<VK>(P.payload + meta_vp(meta), meta_nnz(meta), m, P.xd, (int64_t)cb * 16, acc);
-    float rowsum = wave_rows_reduce(acc, lane);
-    uint64_t todo = __ballot(act && type != DBS_TILE_COO);
+      for (int k = 0; k < 16; ++k) acc[k] = 0.0f;
+      if (coo) coo_plus<VK>(P.payload + meta_vp(meta), meta_nnz(meta), m, P.xd, (int64_t)cb * 16, acc);
+      rowsum = wave_rows_reduce(acc, lane);
+    }
+    // patched CSR tiles with few active columns take the column variant
+    // (section 3.3.3); the other row-major tiles go four at a time through
+    // the row-per-lane path; ForceCSC tiles one at a time
+    const uint64_t colv = __ballot(act && type == DBS_TILE_CSR && __popc(m) < P.local_cutoff);
+    const uint64_t rowt = __ballot(act && type != DBS_TILE_COO && type != DBS_TILE_FORCE_CSC) & ~colv;
+    if (rowt) {
+      const brsrc_t pay = make_rsrc(P.payload, (uint64_t)P.payload_bytes + DBS_PAYLOAD_SLACK);
+      const brsrc_t xr = make_rsrc(P.xd, (uint64_t)P.nb * 16 * VS);
+      rowsum += quarter_merge(rows_plus<VK>(pay, xr, rowt, meta, m, cb, lane));
+    }
+    uint64_t todo = __ballot(act && type == DBS_TILE_FORCE_CSC) | colv;
     while (todo) {
       const int src = __ffsll((unsigned long long)todo) - 1;
       todo &= todo - 1;
@@ -408,7 +431,7 @@ __global__ __launch_bounds__(KT) void k_spmspv(SpmvParams P) {
     // metadata of every tile is loaded up front once most vector blocks are active
     const bool eager = (int64_t)nz * 4 > (int64_t)P.nb;
     if (SR == DBS_OR_AND) {
-      constexpr int U = 8;
+      constexpr int U = PULL_U_OR;
       PullRes R;
       R.tcb = make_rsrc(P.t_cb, (uint64_t)P.T * 4);
       R.tmeta = make_rsrc(P.t_meta, (uint64_t)P.T * 8);
@@ -416,7 +439,7 @@ __global__ __launch_bounds__(KT) void k_spmspv(SpmvParams P) {
       R.xmask = make_rsrc(P.xmask, (uint64_t)P.nb * 4);
       for (int64_t s = gw * U; s < P.nseg; s += nw * U) pull_or_group<VK, U>(P, R, s, eager, lane);
     } else {
-      constexpr int U = 4;
+      constexpr int U = PULL_U_PLUS;
       for (int64_t s = gw * U; s < P.nseg; s += nw * U) pull_group<VK, SR, U>(P, s, eager, s_x[w], s_part[w], lane);
     }
   }
@@ -488,17 +511,18 @@ dbs_status dbs_spmspv_impl(dbs_matrix *A, int32_t nnz_x, const int32_t *x_idx, c
     SPMV_TRY(hipEventRecord(tev[0], s));
   }
   if (dense) {
-    if (xk == VK_BF16) hipLaunchKernelGGL(k_xmeta_dense<VK_BF16>, dim3(mgrid), dim3(KT), 0, s, o, x_dense);
-    else hipLaunchKernelGGL(k_xmeta_dense<VK_F32>, dim3(mgrid), dim3(KT), 0, s, o, x_dense);
+    void *xd = sr == DBS_PLUS_TIMES ? A->xd : nullptr;
+    if (xk == VK_BF16) hipLaunchKernelGGL(k_xmeta_dense<VK_BF16>, dim3(mgrid), dim3(dbs_meta::MT), 0, s, o, x_dense, xd);
+    else hipLaunchKernelGGL(k_xmeta_dense<VK_F32>, dim3(mgrid), dim3(dbs_meta::MT), 0, s, o, x_dense, xd);
   } else {
     const int check = (int)A->opt[DBS_OPT_CHECK];
     const void *xv = sr == DBS_PLUS_TIMES ? x_val : nullptr;
     if (xk == VK_F32)
-      hipLaunchKernelGGL(k_xmeta_sparse<VK_F32>, dim3(mgrid), dim3(KT), 0, s, o, nnz_x, x_idx, xv, A->xd, check);
+      hipLaunchKernelGGL(k_xmeta_sparse<VK_F32>, dim3(mgrid), dim3(dbs_meta::MT), 0, s, o, nnz_x, x_idx, xv, A->xd, check);
     else if (xk == VK_BF16)
-      hipLaunchKernelGGL(k_xmeta_sparse<VK_BF16>, dim3(mgrid), dim3(KT), 0, s, o, nnz_x, x_idx, xv, A->xd, check);
+      hipLaunchKernelGGL(k_xmeta_sparse<VK_BF16>, dim3(mgrid), dim3(dbs_meta::MT), 0, s, o, nnz_x, x_idx, xv, A->xd, check);
     else
-      hipLaunchKernelGGL(k_xmeta_sparse<VK_PAT>, dim3(mgrid), dim3(KT), 0, s, o, nnz_x, x_idx, xv, A->xd, check);
+      hipLaunchKernelGGL(k_xmeta_sparse<VK_PAT>, dim3(mgrid), dim3(dbs_meta::MT), 0, s, o, nnz_x, x_idx, xv, A->xd, check);
   }
   SPMV_TRY(hipGetLastError());
   if (timing) SPMV_TRY(hipEventRecord(tev[1], s));
@@ -519,7 +543,7 @@ dbs_status dbs_spmspv_impl(dbs_matrix *A, int32_t nnz_x, const int32_t *x_idx, c
   P.nb = A->nb;
   P.xmask = A->xmask;
   P.epoch = A->epoch;
-  P.xd = dense ? x_dense : A->xd;
+  P.xd = A->xd;  // PLUS_TIMES only: the staged x (OR_AND reads the masks alone)
   P.chunks = A->chunks;
   P.max_chunks = A->max_chunks;
   P.ctr = o.reg.ctr;
@@ -528,7 +552,10 @@ dbs_status dbs_spmspv_impl(dbs_matrix *A, int32_t nnz_x, const int32_t *x_idx, c
   P.th3_den = A->opt[DBS_OPT_TH3_DEN];
   P.local_cutoff = (int32_t)A->opt[DBS_OPT_LOCAL_PUSH_CUTOFF];
   P.y = y;
-  const int64_t waves = (A->nseg + 3) / 4 > A->max_chunks ? (A->nseg + 3) / 4 : A->max_chunks;
+  // one wave per group of pull segments (PULL_U_OR or PULL_U_PLUS of them), capped at the resident grid
+  const int64_t pull_waves = sr == DBS_OR_AND ? (A->nseg + PULL_U_OR - 1) / PULL_U_OR
+                                              : (A->nseg + PULL_U_PLUS - 1) / PULL_U_PLUS;
+  const int64_t waves = pull_waves > A->max_chunks ? pull_waves : A->max_chunks;
   const int vk = A->vk;
   if (sr == DBS_OR_AND) {
     if (vk == VK_F32) launch_spmspv<VK_F32, DBS_OR_AND>(P, waves, s);

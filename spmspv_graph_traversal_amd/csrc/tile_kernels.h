@@ -37,6 +37,18 @@ DBS_DEV uint64_t bld64(brsrc_t r, uint32_t off) {
 extern "C" __device__ uint32_t __ockl_wfred_or_u32(uint32_t);
 // OR over the 64 lanes of the wave (DPP row shifts + row mirror); uniform result
 DBS_DEV uint32_t wave_or(uint32_t v) { return __ockl_wfred_or_u32(v); }
+extern "C" __device__ uint32_t __ockl_wfred_max_u32(uint32_t);
+DBS_DEV uint32_t wave_max(uint32_t v) { return __ockl_wfred_max_u32(v); }
+
+// inclusive prefix sum over the 16 lanes of each quarter (DPP row shifts;
+// lanes shifted in from outside the quarter read 0)
+DBS_DEV uint32_t quarter_incl_scan(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true);  // row_shr:8
+  return v;
+}
 
 // OR-AND contribution of four coordinate bytes (row << 4 | col) under the
 // x-block mask m.  Unused bytes of a tile repeat its last entry, so all four
@@ -392,4 +404,98 @@ DBS_DEV uint32_t lane_coo_or(const uint8_t *payload, uint64_t meta, uint32_t m, 
     }
   }
   return f;
+}
+
+// ---------------------------------------------------------------------------
+// PLUS_TIMES over the row-major larger tiles of one pull segment (Dense,
+// ForceCSR, patched CSR), four tiles per step: quarter q of the wave takes one
+// tile, lane (q, r) its row r.  A lane reads its row mask (Dense: all 16),
+// the x entry of column r of its tile's column block (masked by blk_x_mask),
+// derives row_ptr[r] as the quarter's prefix sum of the row counts, then
+// reads the row's values (contiguous, at most 16) with dword-aligned wide
+// loads.  Products walk the row's stored columns in order; the x value of a
+// column comes from the lane of the quarter that holds it.  Four tiles cost
+// five vector memory instructions (bf16), against about ten per tile when the
+// whole wave works on one tile.  `pay` must extend at least 64 bytes past
+// the last value; `xr` covers the block-padded x.  Returns lane (q, r)'s
+// partial for row r, to be summed over the quarters.
+// ---------------------------------------------------------------------------
+template <int VK>
+DBS_DEV float rows_plus(brsrc_t pay, brsrc_t xr, uint64_t todo, uint64_t meta, uint32_t m, uint32_t cb, int lane) {
+  constexpr uint32_t VS = VK == VK_F32 ? 4u : 2u;
+  const uint32_t q = (uint32_t)lane >> 4, r = (uint32_t)lane & 15u;
+  float part = 0.0f;
+  while (todo) {
+    // lanes holding the next four tiles (wave-uniform), then the one of this quarter
+    int l[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      l[k] = todo ? __ffsll((unsigned long long)todo) - 1 : -1;
+      todo &= todo - 1;
+    }
+    const int src = q == 0 ? l[0] : q == 1 ? l[1] : q == 2 ? l[2] : l[3];
+    const bool valid = src >= 0;
+    const int sl = valid ? src : 0;
+    const uint64_t mt = (uint64_t)(uint32_t)__shfl((int)(uint32_t)meta, sl) |
+                        ((uint64_t)(uint32_t)__shfl((int)(uint32_t)(meta >> 32), sl) << 32);
+    // every lane takes part in each shuffle (a lane outside EXEC reads as 0
+    // to the others), the mask is applied afterwards
+    const uint32_t mall = (uint32_t)__shfl((int)m, sl);
+    const uint32_t mk = valid ? mall : 0u;
+    const uint32_t c = (uint32_t)__shfl((int)cb, sl);
+    const uint32_t ty = meta_type(mt), vp = (uint32_t)meta_vp(mt);
+    const bool dn = ty == DBS_TILE_DENSE;
+    // phase 1: row mask and x
+    uint32_t rmk = __builtin_amdgcn_raw_buffer_load_b16(pay, valid && !dn ? vp + 2u * r : OOB_OFF, 0, 0);
+    rmk = valid && dn ? 0xFFFFu : rmk;
+    float xt;
+    if (VK == VK_F32) {
+      xt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(xr, valid ? (c * 16u + r) * 4u : OOB_OFF, 0, 0));
+    } else {
+      xt = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(xr, valid ? (c * 16u + r) * 2u : OOB_OFF, 0, 0)
+                           << 16);
+    }
+    xt = ((mk >> r) & 1u) ? xt : 0.0f;
+    // phase 2: the row's values
+    const uint32_t cnt = (uint32_t)__popc(rmk);
+    const uint32_t rp = quarter_incl_scan(cnt) - cnt;
+    const uint32_t vbase = ty == DBS_TILE_CSR ? csr_val_off(meta_nnz(mt)) : (uint32_t)PL_FORCE_VAL;
+    const uint32_t voff = dn ? vp + r * 16u * VS : vp + vbase + rp * VS;
+    const uint32_t lo = cnt ? (voff & ~3u) : OOB_OFF;
+    float v[16];
+    if (VK == VK_F32) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const auto w = __builtin_amdgcn_raw_buffer_load_b128(pay, cnt ? lo + 16u * j : OOB_OFF, 0, 0);
+        v[4 * j] = __uint_as_float(w[0]);
+        v[4 * j + 1] = __uint_as_float(w[1]);
+        v[4 * j + 2] = __uint_as_float(w[2]);
+        v[4 * j + 3] = __uint_as_float(w[3]);
+      }
+    } else {
+      const auto wa = __builtin_amdgcn_raw_buffer_load_b128(pay, lo, 0, 0);
+      const auto wb = __builtin_amdgcn_raw_buffer_load_b128(pay, cnt ? lo + 16u : OOB_OFF, 0, 0);
+      const uint32_t wc = __builtin_amdgcn_raw_buffer_load_b32(pay, cnt ? lo + 32u : OOB_OFF, 0, 0);
+      const uint32_t w[9] = {wa[0], wa[1], wa[2], wa[3], wb[0], wb[1], wb[2], wb[3], wc};
+      const bool odd = (voff & 2u) != 0u;  // the row starts in the upper half of a dword
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t u = odd ? __builtin_amdgcn_alignbit(w[j + 1], w[j], 16) : w[j];
+        v[2 * j] = __uint_as_float(u << 16);
+        v[2 * j + 1] = __uint_as_float(u & 0xFFFF0000u);
+      }
+    }
+    // products over the row's stored columns, in order
+    const uint32_t kmax = wave_max(cnt);
+    uint32_t rest = rmk;
+#pragma unroll
+    for (uint32_t k = 0; k < 16; ++k) {
+      if (k >= kmax) break;  // uniform
+      const uint32_t col = (uint32_t)(__ffs(rest) - 1) & 15u;
+      rest &= rest - 1u;
+      const float xv = __shfl(xt, (int)((q << 4) | col));
+      if (k < cnt) part += v[k] * xv;
+    }
+  }
+  return part;
 }

@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 import oracle as orc
-from gpu_helpers import bf16_csr_of, build, csr_of, mixed_tile_dense, up
+from gpu_helpers import bf16_csr_of, build, csr_of, mixed_tile_dense, options, up
 from synth import (bf16_bits_to_f32, f32_to_bf16_bits, rmat_csr, rng_for, sparse_x,
                    uniform_csr)
 
@@ -56,7 +56,7 @@ def test_plus_times_mixed_formats_all_paths(dbs, seed, density):
     xi, xv = sparse_x(n, density, rng_for("test", 700, seed, int(density * 1000)))
     yr, s = orc.spmspv_pull(m, n, rp, ci, v, orc.F32, xi, xv, orc.F32)
     for path in PATHS:
-        for cutoff in (0, 8, 17):  # patched-CSR: always column kernel / default / always row kernel
+        for cutoff in (0, 8, 17):  # patched-CSR: always row kernel (default) / mixed / always column kernel
             dbs.dbs_set_option(A, dbs.DBS_OPT_PATH, path)
             dbs.dbs_set_option(A, dbs.DBS_OPT_LOCAL_PUSH_CUTOFF, cutoff)
             y = run_plus(dbs, A, m, xi, xv)
@@ -77,6 +77,31 @@ def test_plus_times_bf16(dbs, density):
     for path in PATHS:
         dbs.dbs_set_option(A, dbs.DBS_OPT_PATH, path)
         assert_close(run_plus(dbs, A, m, xi, xb, bf16=True), yr, s, f"bf16 path {path}")
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+@pytest.mark.parametrize("cap", [64, 45, 13])
+def test_plus_times_long_row_blocks(dbs, seed, cap):
+    """Row blocks of 75 tiles split into pull segments of up to `cap` weight: the
+    larger tiles go through the four-tiles-per-step path with partial last steps
+    whose tiles sit in lanes of any quarter.  f32 and bf16, sparse and dense x."""
+    a = mixed_tile_dense(seed, mb=3, nb=75)
+    m, n = a.shape
+    opt = options(dbs, seg_cap=cap)
+    rp, ci, v = csr_of(a)
+    A = build(dbs, m, n, rp, ci, v, dbs.DBS_F32, opt)
+    _, _, bits = bf16_csr_of(a)
+    B = build(dbs, m, n, rp, ci, bits, dbs.DBS_BF16, opt)
+    for density in (0.05, 0.6, 1.0):
+        xi, xv = sparse_x(n, density, rng_for("test", 720, seed, cap, int(density * 100)))
+        xb = f32_to_bf16_bits(xv)
+        yr, s = orc.spmspv_pull(m, n, rp, ci, v, orc.F32, xi, xv, orc.F32)
+        yb, sb = orc.spmspv_pull(m, n, rp, ci, bits, orc.BF16, xi, xb, orc.BF16)
+        for path in PATHS:
+            dbs.dbs_set_option(A, dbs.DBS_OPT_PATH, path)
+            dbs.dbs_set_option(B, dbs.DBS_OPT_PATH, path)
+            assert_close(run_plus(dbs, A, m, xi, xv), yr, s, f"f32 path {path} density {density}")
+            assert_close(run_plus(dbs, B, m, xi, xb, bf16=True), yb, sb, f"bf16 path {path} density {density}")
 
 
 def test_tiny_config_full_size(dbs):
@@ -213,6 +238,11 @@ def test_argument_errors(dbs):
     assert lib.dbs_bfs(A.handle, 64, lv.data_ptr(), None) == dbs.DBS_ERR_INVALID_ARG
     assert lib.dbs_set_option(A.handle, 99, 0) == dbs.DBS_ERR_INVALID_ARG
     assert lib.dbs_set_option(A.handle, dbs.DBS_OPT_PATH, 3) == dbs.DBS_ERR_INVALID_ARG
+    # a pull segment holds at most one tile per lane
+    for cap in (0, 65):
+        with pytest.raises(dbs.DBSError) as e:
+            build(dbs, 64, 64, rp, ci, v, dbs.DBS_F32, options(dbs, seg_cap=cap))
+        assert e.value.status == dbs.DBS_ERR_INVALID_ARG
 
 
 def test_rmat20_or_and_sweep_full_size(dbs):
