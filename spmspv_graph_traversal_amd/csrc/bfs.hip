@@ -9,9 +9,9 @@
 //                newly found vertices are claimed with an atomic OR on the
 //                next bitmap (the winner writes their level and marks them
 //                visited);
-//   k_bfs_meta   counts the nonzero blocks of the next bitmap, lists them and
-//                reserves their push chunks (one atomic per workgroup), and
-//                clears the bitmap two levels back.
+//   k_bfs_meta   counts the nonzero blocks of the next bitmap, lists them
+//                (one atomic per workgroup), cuts them into push chunks when
+//                the next level pushes, and clears the bitmap two levels back.
 // Three bitmaps rotate: current frontier, next frontier, and one being
 // cleared.  The host reads one counter per level to stop.
 #include "meta.h"
@@ -253,6 +253,10 @@ dbs_status dbs_bfs_impl(dbs_matrix *A, int32_t src, int32_t *levels, hipStream_t
     r.list_cap = A->nb;
     r.chunk_cap = chunk_cap;
     r.cb_ptr = A->cb_ptr;
+    r.nb = A->nb;
+    r.force_path = (int32_t)A->opt[DBS_OPT_PATH];
+    r.th3_num = A->opt[DBS_OPT_TH3_NUM];
+    r.th3_den = A->opt[DBS_OPT_TH3_DEN];
     return r;
   };
   hipLaunchKernelGGL(k_bfs_meta, dim3(mgrid), dim3(dbs_meta::MT), 0, s, (const uint32_t *)A->bfs_bm, A->nb, reg_for(0),

@@ -21,7 +21,7 @@ constexpr int KT = 256;  // threads per workgroup (4 waves)
 struct MetaOut {
   uint32_t *xmask;
   uint32_t epoch;
-  dbs_meta::Reg reg;    // this call's counters ([0] N_nzblk, [1] push chunks, [2] error flags) and lists
+  dbs_meta::Reg reg;    // this call's counters ([0] N_nzblk, [1] push chunks, [2] error flags, [3] done) and lists
   uint32_t *ctr_next;   // next call's counters, cleared here
   int32_t n, nb;
   // y clearing: head bytes, 16-B body, tail bytes
@@ -354,6 +354,69 @@ struct PullRes {
   brsrc_t tcb, tmeta, pay, xmask;
 };
 
+// write the found rows of one segment's row block (lanes 0..15)
+DBS_DEV void pull_or_store(const SpmvParams &P, uint4 seg, uint32_t f, int lane) {
+  const uint32_t rb = seg.x & ~SEG_SPLIT;
+  const int64_t row = (int64_t)rb * 16 + lane;
+  if (lane < 16 && row < P.m) {
+    const uint8_t bit = (uint8_t)((f >> lane) & 1u);
+    if (!(seg.x & SEG_SPLIT)) ((uint8_t *)P.y)[row] = bit;
+    else if (bit) ((uint8_t *)P.y)[row] = 1;
+  }
+}
+
+// Pattern matrices: every tile, whatever its format, is handled by the lane
+// that holds it.  One 32-byte window at the tile's payload holds the
+// coordinates of a COO tile of up to 32 entries, or the 16 row masks of a
+// larger tile (found row r: row_mask[r] & blk_x_mask != 0, the Boolean row
+// kernel of section 3.3.3 with a whole tile per lane).  So a segment costs the
+// same few vector loads whatever its format mix, and no lane waits for the
+// wave to walk the larger tiles one by one.
+template <int U>
+DBS_DEV void pull_or_pattern(const SpmvParams &P, const PullRes &R, const uint4 (&seg)[U],
+                             const uint64_t (&meta)[U], const uint32_t (&m)[U], const bool (&act)[U],
+                             int64_t s0, int lane) {
+  uint32_t w[U][8];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const bool coo = meta_type(meta[u]) == DBS_TILE_COO;
+    const bool pre = act[u] && !meta_inline(meta[u]);
+    const uint32_t vp = (uint32_t)meta_vp(meta[u]);
+    const auto a = __builtin_amdgcn_raw_buffer_load_b128(R.pay, pre ? vp : OOB_OFF, 0, 0);
+    const bool two = pre && (!coo || meta_nnz(meta[u]) > 16);
+    const auto b = __builtin_amdgcn_raw_buffer_load_b128(R.pay, two ? vp + 16u : OOB_OFF, 0, 0);
+    w[u][0] = a[0]; w[u][1] = a[1]; w[u][2] = a[2]; w[u][3] = a[3];
+    w[u][4] = b[0]; w[u][5] = b[1]; w[u][6] = b[2]; w[u][7] = b[3];
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (s0 + u >= P.nseg) break;
+    const uint32_t type = meta_type(meta[u]), nnz = meta_nnz(meta[u]);
+    const bool coo = act[u] && type == DBS_TILE_COO;
+    // COO: words of 4 coordinates; padding repeats the last coordinate up to
+    // the word boundary, words past the tile belong to the next one
+    const uint32_t nw = coo ? (nnz + 3u) >> 2 : 0u;
+    uint32_t f = coo ? coo_or4(meta_inline(meta[u]) ? (uint32_t)meta[u] : w[u][0], m[u]) : 0u;
+    if (__ballot(nw > 1u) != 0ull) {
+#pragma unroll
+      for (uint32_t k = 1; k < 8; ++k) f |= k < nw ? coo_or4(w[u][k], m[u]) : 0u;
+      if (__ballot(nw > 8u) != 0ull && nw > 8u) {  // more than 32 entries: the rest from memory
+        const uint32_t vp = (uint32_t)meta_vp(meta[u]);
+        for (uint32_t k = 8; k < nw; ++k) f |= coo_or4(bld32(R.pay, vp + 4u * k), m[u]);
+      }
+    }
+    // larger tiles: the row masks
+    const bool big = act[u] && type != DBS_TILE_COO;
+    if (__ballot(big) != 0ull) {
+      uint32_t g = 0;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) g |= (((w[u][r >> 1] >> (16 * (r & 1))) & m[u]) != 0u) ? (1u << r) : 0u;
+      f |= big ? g : 0u;
+    }
+    pull_or_store(P, seg[u], wave_or(f), lane);
+  }
+}
+
 template <int VK, int U>
 DBS_DEV void pull_or_group(const SpmvParams &P, const PullRes &R, int64_t s0, bool eager, int lane) {
   uint4 seg[U];
@@ -382,6 +445,10 @@ DBS_DEV void pull_or_group(const SpmvParams &P, const PullRes &R, int64_t s0, bo
 #pragma unroll
     for (int u = 0; u < U; ++u) meta[u] = bld64(R.tmeta, act[u] ? (seg[u].y + (uint32_t)lane) * 8u : OOB_OFF);
   }
+  if constexpr (VK == VK_PAT) {
+    pull_or_pattern<U>(P, R, seg, meta, m, act, s0, lane);
+    return;
+  }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const bool pre = act[u] && meta_type(meta[u]) == DBS_TILE_COO && !meta_inline(meta[u]);
@@ -402,14 +469,7 @@ DBS_DEV void pull_or_group(const SpmvParams &P, const PullRes &R, int64_t s0, bo
       f |= tile_or<VK>(P.payload + meta_vp(tm), dense_mask_ptr<VK>(P, meta_vp(tm)), meta_type(tm), tmask,
                        lane);
     }
-    f = wave_or(f);
-    const uint32_t rb = seg[u].x & ~SEG_SPLIT;
-    const int64_t row = (int64_t)rb * 16 + lane;
-    if (lane < 16 && row < P.m) {
-      const uint8_t bit = (uint8_t)((f >> lane) & 1u);
-      if (!(seg[u].x & SEG_SPLIT)) ((uint8_t *)P.y)[row] = bit;
-      else if (bit) ((uint8_t *)P.y)[row] = 1;
-    }
+    pull_or_store(P, seg[u], wave_or(f), lane);
   }
 }
 
@@ -435,7 +495,7 @@ __global__ __launch_bounds__(KT) void k_spmspv(SpmvParams P) {
       PullRes R;
       R.tcb = make_rsrc(P.t_cb, (uint64_t)P.T * 4);
       R.tmeta = make_rsrc(P.t_meta, (uint64_t)P.T * 8);
-      R.pay = make_rsrc(P.payload, (uint64_t)P.payload_bytes);
+      R.pay = make_rsrc(P.payload, (uint64_t)P.payload_bytes + DBS_PAYLOAD_SLACK);
       R.xmask = make_rsrc(P.xmask, (uint64_t)P.nb * 4);
       for (int64_t s = gw * U; s < P.nseg; s += nw * U) pull_or_group<VK, U>(P, R, s, eager, lane);
     } else {
@@ -484,6 +544,10 @@ dbs_status dbs_spmspv_impl(dbs_matrix *A, int32_t nnz_x, const int32_t *x_idx, c
   o.reg.list_cap = A->nb;
   o.reg.chunk_cap = A->max_chunks;
   o.reg.cb_ptr = A->cb_ptr;
+  o.reg.nb = A->nb;
+  o.reg.force_path = (int32_t)A->opt[DBS_OPT_PATH];
+  o.reg.th3_num = A->opt[DBS_OPT_TH3_NUM];
+  o.reg.th3_den = A->opt[DBS_OPT_TH3_DEN];
   o.ctr_next = A->ctr + 8 * (1 - A->cbuf);
   o.n = A->n;
   o.nb = A->nb;
