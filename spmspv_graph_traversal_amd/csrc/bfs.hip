@@ -123,7 +123,7 @@ DBS_DEV void bfs_pull_group(const BfsParams &P, const BfsRes &R, int64_t s0, boo
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const uint32_t t = seg[u].y + (uint32_t)lane;
-    act[u] = need[u] != 0u && t < seg[u].z;
+    act[u] = (need[u] != 0u) & (t < seg[u].z);
     cb[u] = bld32(R.tcb, act[u] ? t * 4u : OOB_OFF);
     meta[u] = eager ? bld64(R.tmeta, act[u] ? t * 8u : OOB_OFF) : 0ull;
   }
@@ -139,17 +139,17 @@ DBS_DEV void bfs_pull_group(const BfsParams &P, const BfsRes &R, int64_t s0, boo
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const bool pre = act[u] && meta_type(meta[u]) == DBS_TILE_COO && !meta_inline(meta[u]);
+    const bool pre = act[u] & (meta_type(meta[u]) == DBS_TILE_COO) & !meta_inline(meta[u]);
     const uint32_t off = pre ? (uint32_t)meta_vp(meta[u]) : OOB_OFF;
     pw0[u] = bld32(R.pay, off);
-    pw1[u] = bld32(R.pay, pre && meta_nnz(meta[u]) > 4 ? off + 4u : OOB_OFF);
+    pw1[u] = bld32(R.pay, (pre & (meta_nnz(meta[u]) > 4)) ? off + 4u : OOB_OFF);
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     if (!need[u]) continue;
     uint32_t f = lane_coo_or(P.payload, meta[u], m[u], act[u], pw0[u], pw1[u]);
     f = wave_or(f);
-    uint64_t todo = __ballot(act[u] && meta_type(meta[u]) != DBS_TILE_COO);
+    uint64_t todo = __ballot(act[u] & (meta_type(meta[u]) != DBS_TILE_COO));
     while (todo && (f & need[u]) != need[u]) {
       const int src = __ffsll((unsigned long long)todo) - 1;
       todo &= todo - 1;

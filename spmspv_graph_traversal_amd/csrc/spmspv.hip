@@ -255,7 +255,7 @@ DBS_DEV void pull_finish(const SpmvParams &P, uint4 seg, uint32_t cb, uint32_t m
   } else {
     constexpr uint64_t VS = VK == VK_F32 ? 4 : 2;
     float rowsum = 0.0f;
-    const bool coo = act && type == DBS_TILE_COO;
+    const bool coo = act & (type == DBS_TILE_COO);
     if (__ballot(coo) != 0ull) {
       float acc[16];
 #pragma unroll
@@ -266,14 +266,14 @@ DBS_DEV void pull_finish(const SpmvParams &P, uint4 seg, uint32_t cb, uint32_t m
     // patched CSR tiles with few active columns take the column variant
     // (section 3.3.3); the other row-major tiles go four at a time through
     // the row-per-lane path; ForceCSC tiles one at a time
-    const uint64_t colv = __ballot(act && type == DBS_TILE_CSR && __popc(m) < P.local_cutoff);
-    const uint64_t rowt = __ballot(act && type != DBS_TILE_COO && type != DBS_TILE_FORCE_CSC) & ~colv;
+    const uint64_t colv = __ballot(act & (type == DBS_TILE_CSR) & (__popc(m) < P.local_cutoff));
+    const uint64_t rowt = __ballot(act & (type != DBS_TILE_COO) & (type != DBS_TILE_FORCE_CSC)) & ~colv;
     if (rowt) {
       const brsrc_t pay = make_rsrc(P.payload, (uint64_t)P.payload_bytes + DBS_PAYLOAD_SLACK);
       const brsrc_t xr = make_rsrc(P.xd, (uint64_t)P.nb * 16 * VS);
       rowsum += quarter_merge(rows_plus<VK>(pay, xr, rowt, meta, m, cb, lane));
     }
-    uint64_t todo = __ballot(act && type == DBS_TILE_FORCE_CSC) | colv;
+    uint64_t todo = __ballot(act & (type == DBS_TILE_FORCE_CSC)) | colv;
     while (todo) {
       const int src = __ffsll((unsigned long long)todo) - 1;
       todo &= todo - 1;
@@ -326,7 +326,7 @@ DBS_DEV void pull_group(const SpmvParams &P, int64_t s0, bool eager, float *sx, 
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const uint32_t w = P.xmask[cb[u]];
-    m[u] = act[u] && (w >> 16) == P.epoch ? (w & 0xFFFFu) : 0u;
+    m[u] = (act[u] & ((w >> 16) == P.epoch)) ? (w & 0xFFFFu) : 0u;
     act[u] = m[u] != 0u;
   }
   if (!eager) {
@@ -365,55 +365,124 @@ DBS_DEV void pull_or_store(const SpmvParams &P, uint4 seg, uint32_t f, int lane)
   }
 }
 
-// Pattern matrices: every tile, whatever its format, is handled by the lane
-// that holds it.  One 32-byte window at the tile's payload holds the
-// coordinates of a COO tile of up to 32 entries, or the 16 row masks of a
-// larger tile (found row r: row_mask[r] & blk_x_mask != 0, the Boolean row
-// kernel of section 3.3.3 with a whole tile per lane).  So a segment costs the
-// same few vector loads whatever its format mix, and no lane waits for the
-// wave to walk the larger tiles one by one.
+// Pattern matrices (the graph workloads), pull.  Per step a wave takes U
+// segments and issues each load phase for all of them: segment descriptors
+// (scalar loads), column blocks (and, when most vector blocks are active,
+// metadata) through a buffer range cut to the segment, so lanes past its end
+// read 0 without any address arithmetic; the blk_x_mask gather; metadata of
+// the active tiles; then the coordinate words of the active COO tiles that do
+// not fit in their metadata word.  Those tiles' payloads are consecutive in the
+// COO section, so the segment reads them as one run of words spread over the
+// lanes (word j by lane j), each lane finding the tile of its word by a wave
+// max-scan of the tiles' first-word marks.  A segment thus costs two to five
+// vector memory instructions whatever its size mix, and each instruction
+// covers up to 64 tiles or words.  Larger tiles (Dense, ForceCSR, ForceCSC,
+// patched CSR: all keep the 16 row masks for pattern matrices) are rare and
+// take a separate step.  y is cleared by the metadata kernel, so only found
+// rows are written.
+typedef __attribute__((address_space(4))) const uint32_t cu32_t;  // read-only: scalar loads
+
 template <int U>
-DBS_DEV void pull_or_pattern(const SpmvParams &P, const PullRes &R, const uint4 (&seg)[U],
-                             const uint64_t (&meta)[U], const uint32_t (&m)[U], const bool (&act)[U],
-                             int64_t s0, int lane) {
-  uint32_t w[U][8];
+DBS_DEV void pull_or_pattern_group(const SpmvParams &P, const PullRes &R, int64_t s0, bool eager, int lane,
+                                   uint32_t *s_mark) {
+  const uint32_t l4 = (uint32_t)lane * 4u, l8 = (uint32_t)lane * 8u;
+  uint4 seg[U];
+  uint32_t n[U], cb[U], m[U];
+  uint64_t meta[U];
+  brsrc_t rmeta[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const bool coo = meta_type(meta[u]) == DBS_TILE_COO;
-    const bool pre = act[u] && !meta_inline(meta[u]);
-    const uint32_t vp = (uint32_t)meta_vp(meta[u]);
-    const auto a = __builtin_amdgcn_raw_buffer_load_b128(R.pay, pre ? vp : OOB_OFF, 0, 0);
-    const bool two = pre && (!coo || meta_nnz(meta[u]) > 16);
-    const auto b = __builtin_amdgcn_raw_buffer_load_b128(R.pay, two ? vp + 16u : OOB_OFF, 0, 0);
-    w[u][0] = a[0]; w[u][1] = a[1]; w[u][2] = a[2]; w[u][3] = a[3];
-    w[u][4] = b[0]; w[u][5] = b[1]; w[u][6] = b[2]; w[u][7] = b[3];
+    const int64_t si = s0 + u < P.nseg ? s0 + u : P.nseg - 1;
+    const cu32_t *q = (const cu32_t *)P.segs + 4 * si;
+    seg[u] = make_uint4(q[0], q[1], q[2], 0u);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    n[u] = s0 + u < P.nseg ? seg[u].z - seg[u].y : 0u;
+    const brsrc_t rcb = make_rsrc(P.t_cb + seg[u].y, (uint64_t)n[u] * 4u);
+    rmeta[u] = make_rsrc(P.t_meta + seg[u].y, (uint64_t)n[u] * 8u);
+    cb[u] = __builtin_amdgcn_raw_buffer_load_b32(rcb, l4, 0, 0);
+    meta[u] = eager ? bld64(rmeta[u], l8) : 0ull;
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint32_t w = bld32(R.xmask, (uint32_t)lane < n[u] ? cb[u] * 4u : OOB_OFF);
+    m[u] = ((w >> 16) == P.epoch) ? (w & 0xFFFFu) : 0u;  // an idle lane reads 0: no epoch
+  }
+  if (!eager) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (__ballot(m[u] != 0u) != 0ull) meta[u] = bld64(rmeta[u], m[u] != 0u ? l8 : OOB_OFF);
+  }
+  // coordinate words of the active non-inline COO tiles: [base, base + 4 * nwords)
+  uint32_t word[U], base[U], nwords[U];
+  uint64_t nicb[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const bool nic = (m[u] != 0u) & (meta_type(meta[u]) == DBS_TILE_COO) & !meta_inline(meta[u]);
+    nicb[u] = __ballot(nic);
+    word[u] = 0u;
+    base[u] = 0u;
+    nwords[u] = 0u;
+    if (nicb[u] != 0ull) {
+      const int first = __ffsll((unsigned long long)nicb[u]) - 1;
+      const int last = 63 - __clzll((long long)nicb[u]);
+      const uint32_t vp = (uint32_t)meta_vp(meta[u]);
+      const uint32_t vend = vp + coo_val_off(meta_nnz(meta[u]));
+      base[u] = (uint32_t)__builtin_amdgcn_readlane((int)vp, first);
+      nwords[u] = ((uint32_t)__builtin_amdgcn_readlane((int)vend, last) - base[u]) >> 2;
+      word[u] = bld32(R.pay, (uint32_t)lane < nwords[u] ? base[u] + l4 : OOB_OFF);
+    }
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     if (s0 + u >= P.nseg) break;
-    const uint32_t type = meta_type(meta[u]), nnz = meta_nnz(meta[u]);
-    const bool coo = act[u] && type == DBS_TILE_COO;
-    // COO: words of 4 coordinates; padding repeats the last coordinate up to
-    // the word boundary, words past the tile belong to the next one
-    const uint32_t nw = coo ? (nnz + 3u) >> 2 : 0u;
-    uint32_t f = coo ? coo_or4(meta_inline(meta[u]) ? (uint32_t)meta[u] : w[u][0], m[u]) : 0u;
-    if (__ballot(nw > 1u) != 0ull) {
-#pragma unroll
-      for (uint32_t k = 1; k < 8; ++k) f |= k < nw ? coo_or4(w[u][k], m[u]) : 0u;
-      if (__ballot(nw > 8u) != 0ull && nw > 8u) {  // more than 32 entries: the rest from memory
-        const uint32_t vp = (uint32_t)meta_vp(meta[u]);
-        for (uint32_t k = 8; k < nw; ++k) f |= coo_or4(bld32(R.pay, vp + 4u * k), m[u]);
+    const uint32_t type = meta_type(meta[u]);
+    // COO tiles with at most four entries: the coordinates are in the metadata word
+    uint32_t f = ((m[u] != 0u) & (type == DBS_TILE_COO) & meta_inline(meta[u])) ? coo_or4((uint32_t)meta[u], m[u])
+                                                                                  : 0u;
+    if (nicb[u] != 0ull) {
+      const bool nic = (nicb[u] >> lane) & 1ull;
+      // words [slot, send) of this lane's tile; words between two active tiles
+      // may belong to inactive ones, which the end test leaves out
+      const uint32_t slot = ((uint32_t)meta_vp(meta[u]) - base[u]) >> 2;
+      const uint32_t send = slot + (coo_val_off(meta_nnz(meta[u])) >> 2);
+      uint32_t carry = 0u;
+      for (uint32_t j0 = 0; j0 < nwords[u]; j0 += 64u) {
+        // lanes talk through LDS: each step is fenced at wave scope, or the
+        // compiler may hand a lane back its own earlier store
+        __syncwarp();
+        s_mark[lane] = 0u;
+        __syncwarp();
+        if (nic & (slot >= j0) & (slot < j0 + 64u)) s_mark[slot - j0] = (uint32_t)lane + 1u;
+        __syncwarp();
+        uint32_t own = wave_incl_max(s_mark[lane]);
+        own = own > carry ? own : carry;
+        carry = (uint32_t)__builtin_amdgcn_readlane((int)own, 63);  // owner of the next chunk's first word
+        const uint32_t mw = (uint32_t)__shfl((int)m[u], (int)own - 1);
+        const uint32_t oend = (uint32_t)__shfl((int)send, (int)own - 1);
+        const uint32_t j = j0 + (uint32_t)lane;
+        const uint32_t wd = j0 == 0u ? word[u] : bld32(R.pay, j < nwords[u] ? base[u] + 4u * j : OOB_OFF);
+        f |= ((j < nwords[u]) & (j < oend)) ? coo_or4(wd, mw) : 0u;
       }
     }
-    // larger tiles: the row masks
-    const bool big = act[u] && type != DBS_TILE_COO;
+    // larger tiles: 16 row masks each
+    const bool big = (m[u] != 0u) & (type != DBS_TILE_COO);
     if (__ballot(big) != 0ull) {
+      const uint32_t vp = big ? (uint32_t)meta_vp(meta[u]) : OOB_OFF;
+      const auto a = __builtin_amdgcn_raw_buffer_load_b128(R.pay, vp, 0, 0);
+      const auto b = __builtin_amdgcn_raw_buffer_load_b128(R.pay, big ? vp + 16u : OOB_OFF, 0, 0);
+      const uint32_t rm[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
       uint32_t g = 0;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) g |= (((w[u][r >> 1] >> (16 * (r & 1))) & m[u]) != 0u) ? (1u << r) : 0u;
-      f |= big ? g : 0u;
+      for (int r = 0; r < 16; ++r) g |= (((rm[r >> 1] >> (16 * (r & 1))) & m[u]) != 0u) ? (1u << r) : 0u;
+      f |= g;
     }
-    pull_or_store(P, seg[u], wave_or(f), lane);
+    f = wave_or(f);
+    if (f != 0u) {  // uniform
+      const int64_t row = (int64_t)(seg[u].x & ~SEG_SPLIT) * 16 + lane;
+      if ((lane < 16) & ((f >> lane) & 1u) & (row < P.m)) ((uint8_t *)P.y)[row] = 1;
+    }
   }
 }
 
@@ -437,30 +506,28 @@ DBS_DEV void pull_or_group(const SpmvParams &P, const PullRes &R, int64_t s0, bo
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
+    // an idle lane reads 0, which no epoch (>= 1) matches: the mask needs no
+    // second test of act, so nothing makes the load conditional
     const uint32_t w = bld32(R.xmask, act[u] ? cb[u] * 4u : OOB_OFF);
-    m[u] = act[u] && (w >> 16) == P.epoch ? (w & 0xFFFFu) : 0u;
+    m[u] = ((w >> 16) == P.epoch) ? (w & 0xFFFFu) : 0u;
     act[u] = m[u] != 0u;
   }
   if (!eager) {
 #pragma unroll
     for (int u = 0; u < U; ++u) meta[u] = bld64(R.tmeta, act[u] ? (seg[u].y + (uint32_t)lane) * 8u : OOB_OFF);
   }
-  if constexpr (VK == VK_PAT) {
-    pull_or_pattern<U>(P, R, seg, meta, m, act, s0, lane);
-    return;
-  }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const bool pre = act[u] && meta_type(meta[u]) == DBS_TILE_COO && !meta_inline(meta[u]);
+    const bool pre = act[u] & (meta_type(meta[u]) == DBS_TILE_COO) & !meta_inline(meta[u]);
     const uint32_t off = pre ? (uint32_t)meta_vp(meta[u]) : OOB_OFF;
     pw0[u] = bld32(R.pay, off);
-    pw1[u] = bld32(R.pay, pre && meta_nnz(meta[u]) > 4 ? off + 4u : OOB_OFF);
+    pw1[u] = bld32(R.pay, (pre & (meta_nnz(meta[u]) > 4)) ? off + 4u : OOB_OFF);
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     if (s0 + u >= P.nseg) break;
     uint32_t f = lane_coo_or(P.payload, meta[u], m[u], act[u], pw0[u], pw1[u]);
-    uint64_t todo = __ballot(act[u] && meta_type(meta[u]) != DBS_TILE_COO);
+    uint64_t todo = __ballot(act[u] & (meta_type(meta[u]) != DBS_TILE_COO));
     while (todo) {
       const int src = __ffsll((unsigned long long)todo) - 1;
       todo &= todo - 1;
@@ -477,6 +544,7 @@ template <int VK, int SR>
 __global__ __launch_bounds__(KT) void k_spmspv(SpmvParams P) {
   __shared__ float s_x[KT / DBS_WAVE][16];
   __shared__ float s_part[KT / DBS_WAVE][64];
+  __shared__ uint32_t s_mark[KT / DBS_WAVE][64];
   const int lane = __lane_id();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / DBS_WAVE);
   const uint32_t nz = P.ctr[0];
@@ -497,7 +565,11 @@ __global__ __launch_bounds__(KT) void k_spmspv(SpmvParams P) {
       R.tmeta = make_rsrc(P.t_meta, (uint64_t)P.T * 8);
       R.pay = make_rsrc(P.payload, (uint64_t)P.payload_bytes + DBS_PAYLOAD_SLACK);
       R.xmask = make_rsrc(P.xmask, (uint64_t)P.nb * 4);
-      for (int64_t s = gw * U; s < P.nseg; s += nw * U) pull_or_group<VK, U>(P, R, s, eager, lane);
+      if constexpr (VK == VK_PAT) {
+        for (int64_t s = gw * U; s < P.nseg; s += nw * U) pull_or_pattern_group<U>(P, R, s, eager, lane, s_mark[w]);
+      } else {
+        for (int64_t s = gw * U; s < P.nseg; s += nw * U) pull_or_group<VK, U>(P, R, s, eager, lane);
+      }
     } else {
       constexpr int U = PULL_U_PLUS;
       for (int64_t s = gw * U; s < P.nseg; s += nw * U) pull_group<VK, SR, U>(P, s, eager, s_x[w], s_part[w], lane);

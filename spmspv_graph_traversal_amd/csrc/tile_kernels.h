@@ -40,6 +40,19 @@ DBS_DEV uint32_t wave_or(uint32_t v) { return __ockl_wfred_or_u32(v); }
 extern "C" __device__ uint32_t __ockl_wfred_max_u32(uint32_t);
 DBS_DEV uint32_t wave_max(uint32_t v) { return __ockl_wfred_max_u32(v); }
 
+// inclusive maximum over lanes 0..lane (row shifts within each 16-lane row,
+// then the row broadcasts carry rows 0..2 forward; lanes a DPP step does not
+// write keep 0, the identity)
+DBS_DEV uint32_t wave_incl_max(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true));  // row_shr:1
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true));  // row_shr:2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true));  // row_shr:4
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true));  // row_shr:8
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));  // row_bcast:15
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));  // row_bcast:31
+  return v;
+}
+
 // inclusive prefix sum over the 16 lanes of each quarter (DPP row shifts;
 // lanes shifted in from outside the quarter read 0)
 DBS_DEV uint32_t quarter_incl_scan(uint32_t v) {
@@ -327,7 +340,7 @@ DBS_DEV uint32_t coo_or_pre(const uint8_t *payload, uint64_t meta, uint32_t m, u
 // first two payload words of a COO tile that is not inline (else of the
 // arena start, a valid dummy), loaded without a branch
 DBS_DEV void coo_preload(const uint8_t *payload, uint64_t meta, bool act, uint32_t &pw0, uint32_t &pw1) {
-  const bool pre = act && meta_type(meta) == DBS_TILE_COO && !meta_inline(meta);
+  const bool pre = act & (meta_type(meta) == DBS_TILE_COO) & !meta_inline(meta);
   const uint32_t *w = (const uint32_t *)(payload + (pre ? meta_vp(meta) : 0));
   pw0 = w[0];
   pw1 = w[1];
@@ -388,7 +401,7 @@ DBS_DEV float wave_rows_reduce(float (&acc)[16], int lane) {
 // ---------------------------------------------------------------------------
 DBS_DEV uint32_t lane_coo_or(const uint8_t *payload, uint64_t meta, uint32_t m, bool act, uint32_t pw0,
                              uint32_t pw1) {
-  const bool coo = act && meta_type(meta) == DBS_TILE_COO;
+  const bool coo = act & (meta_type(meta) == DBS_TILE_COO);
   const bool inl = meta_inline(meta);
   const uint32_t w0 = inl ? (uint32_t)meta : pw0;
   uint32_t f = coo ? coo_or4(w0, m) : 0u;
@@ -446,8 +459,8 @@ DBS_DEV float rows_plus(brsrc_t pay, brsrc_t xr, uint64_t todo, uint64_t meta, u
     const uint32_t ty = meta_type(mt), vp = (uint32_t)meta_vp(mt);
     const bool dn = ty == DBS_TILE_DENSE;
     // phase 1: row mask and x
-    uint32_t rmk = __builtin_amdgcn_raw_buffer_load_b16(pay, valid && !dn ? vp + 2u * r : OOB_OFF, 0, 0);
-    rmk = valid && dn ? 0xFFFFu : rmk;
+    uint32_t rmk = __builtin_amdgcn_raw_buffer_load_b16(pay, (valid & !dn) ? vp + 2u * r : OOB_OFF, 0, 0);
+    rmk = (valid & dn) ? 0xFFFFu : rmk;
     float xt;
     if (VK == VK_F32) {
       xt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(xr, valid ? (c * 16u + r) * 4u : OOB_OFF, 0, 0));
