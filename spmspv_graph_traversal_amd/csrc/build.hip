@@ -504,7 +504,9 @@ dbs_status dbs_build_impl(dbs_matrix *A, const int32_t *row_ptr, const int32_t *
   BUILD_TRY(hipMemcpyAsync(&hS, seg_off + mb, 4, hipMemcpyDeviceToHost, s));
   BUILD_TRY(hipStreamSynchronize(s));
   A->nseg = hS;
-  BUILD_TRY(dbs_dev_alloc(A, (void **)&A->segs, (size_t)hS * 16 + 16));
+  // padded with zeroed descriptors: the pull reads them in groups of up to 16
+  BUILD_TRY(dbs_dev_alloc(A, (void **)&A->segs, ((size_t)hS + 16) * 16));
+  BUILD_TRY(hipMemsetAsync(A->segs + 4 * (size_t)hS, 0, 16 * 16, s));
   hipLaunchKernelGGL(k_segments, dim3(nblocks(mb, BT)), dim3(BT), 0, s, mb, (const uint32_t *)A->rb_ptr,
                      (const uint32_t *)t_nt, A->bopt, seg_cnt, (const uint32_t *)seg_off, A->segs, 1);
   BUILD_TRY(hipGetLastError());
