@@ -15,6 +15,7 @@
 // Three bitmaps rotate: current frontier, next frontier, and one being
 // cleared.  The host reads one counter per level to stop.
 #include "meta.h"
+#include "pattern_pull.h"
 #include "tile_kernels.h"
 
 namespace {
@@ -161,8 +162,31 @@ DBS_DEV void bfs_pull_group(const BfsParams &P, const BfsRes &R, int64_t s0, boo
   }
 }
 
+// BFS pull on a pattern matrix: rows of a row block not yet visited are
+// wanted (a hint read through the scalar cache: a stale word only costs
+// work, discover() checks again), masks come from the frontier bitmap, found
+// rows are claimed for the next level.
+struct BfsPol {
+  const BfsParams *P;
+  brsrc_t bm;
+  DBS_DEV uint32_t need(uint32_t rb) const {
+    const cu32_t *v = (const cu32_t *)P->vis;
+    return ~(v[rb >> 1] >> ((rb & 1u) * 16u)) & rows_valid(P->m, rb);
+  }
+  DBS_DEV uint32_t mask(uint32_t cb, bool in) const {
+    const uint32_t w = bld32(bm, in ? (cb >> 1) * 4u : OOB_OFF);
+    return (w >> ((cb & 1u) * 16u)) & 0xFFFFu;
+  }
+  DBS_DEV void found(uint32_t rb, uint32_t f, int lane) const {
+    if (lane == 0) discover(*P, rb, f);
+  }
+};
+
+constexpr int BFS_U_PAT = 4;  // segments per wave step, pattern pull
+
 template <int VK>
 __global__ __launch_bounds__(KT) void k_bfs_level(BfsParams P) {
+  __shared__ uint32_t s_mark[KT / DBS_WAVE][64];
   const int lane = __lane_id();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / DBS_WAVE);
   const uint32_t nz = P.cur_ctr[0];
@@ -181,7 +205,14 @@ __global__ __launch_bounds__(KT) void k_bfs_level(BfsParams P) {
     R.tmeta = make_rsrc(P.t_meta, (uint64_t)P.T * 8);
     R.pay = make_rsrc(P.payload, (uint64_t)P.payload_bytes);
     R.bm = make_rsrc(P.cur_bm, (uint64_t)((P.nb + 1) / 2) * 4);
-    for (int64_t s = gw * U; s < P.nseg; s += nw * U) bfs_pull_group<VK, U>(P, R, s, eager, lane);
+    if constexpr (VK == VK_PAT) {
+      const PatSrc S{P.t_cb, P.t_meta, P.segs, P.nseg,
+                     make_rsrc(P.payload, (uint64_t)P.payload_bytes + DBS_PAYLOAD_SLACK)};
+      const BfsPol pol{&P, R.bm};
+      pattern_pull<BFS_U_PAT>(S, pol, gw * BFS_U_PAT, nw * BFS_U_PAT, eager, lane, s_mark[w]);
+    } else {
+      for (int64_t s = gw * U; s < P.nseg; s += nw * U) bfs_pull_group<VK, U>(P, R, s, eager, lane);
+    }
   }
 }
 
@@ -282,7 +313,8 @@ dbs_status dbs_bfs_impl(dbs_matrix *A, int32_t src, int32_t *levels, hipStream_t
   P.force_path = (int32_t)A->opt[DBS_OPT_PATH];
   P.th3_num = A->opt[DBS_OPT_TH3_NUM];
   P.th3_den = A->opt[DBS_OPT_TH3_DEN];
-  int64_t waves = (A->nseg + 7) / 8 > chunk_cap ? (A->nseg + 7) / 8 : chunk_cap;
+  const int pu = A->vk == VK_PAT ? BFS_U_PAT : 8;
+  int64_t waves = (A->nseg + pu - 1) / pu > chunk_cap ? (A->nseg + pu - 1) / pu : chunk_cap;
   int64_t g = (waves + 3) / 4;
   static const unsigned res_f32 = dbs_resident_groups(k_bfs_level<VK_F32>, KT);
   static const unsigned res_bf16 = dbs_resident_groups(k_bfs_level<VK_BF16>, KT);
