@@ -359,6 +359,69 @@ def bench_decode(dbs, torch, args):
     return out
 
 
+ZIPF_DENSITIES = [1e-5, 1e-4, 1e-3, 1e-2, 5e-2, 0.2]
+
+
+def bench_zipf(dbs, torch, args):
+    """Load-imbalance stress matrix (8,388,608^2, Zipf row lengths, band + 10%
+    uniform), fp32 PLUS_TIMES at each x density; one line per density."""
+    from synth import rng_for, sparse_x_with_dense_blocks, zipf_band_csr
+
+    n = 1 << 23
+    t0 = time.time()
+    rp, ci, v = zipf_band_csr(n, rng_for("zipf"))
+    gen_s = time.time() - t0
+    lens = np.diff(rp.astype(np.int64))
+    log(f"[bench] zipf generated: nnz={ci.shape[0]} max_row={int(lens.max())} in {gen_s:.1f}s")
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    A = dbs.dbs_build(n, n, torch.from_numpy(rp).to(dev), torch.from_numpy(ci).to(dev),
+                      torch.from_numpy(v).to(dev), dbs.DBS_F32)
+    torch.cuda.synchronize()
+    build_s = time.time() - t0
+    del rp, ci, v
+    st = dbs.dbs_get_stats(A)
+    fmt = Format(dbs, A, 0)
+    y = torch.empty(n, dtype=torch.float32, device=dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    per = []
+    for k, d in enumerate(ZIPF_DENSITIES):
+        xi, xv = sparse_x_with_dense_blocks(n, d, rng_for("zipf", 1, k))
+        act = np.unique(xi // 16)
+        push = 100 * act.shape[0] < fmt.nb
+        mb, cb = fmt.call_bytes(act, xi.shape[0], 4 * n, push, vsize=4)
+        xi_d, xv_d = torch.from_numpy(xi).to(dev), torch.from_numpy(xv).to(dev)
+        for _ in range(args.warmup):
+            dbs.dbs_spmspv(A, xi_d, xv_d, dbs.DBS_PLUS_TIMES, y)
+        dbs.dbs_set_option(A, dbs.DBS_OPT_TIMING, 1)
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(args.steps):
+            dbs.dbs_spmspv(A, xi_d, xv_d, dbs.DBS_PLUS_TIMES, y)
+        ev1.record()
+        torch.cuda.synchronize()
+        call_ms = ev0.elapsed_time(ev1) / args.steps
+        s2 = dbs.dbs_get_stats(A)
+        kms = s2["sum_compute_ms"] / s2["timed_calls"]
+        per.append({
+            "density": d, "nnz_x": int(xi.shape[0]), "xb_ratio": round(s2["last_n_nzblk"] / fmt.nb, 5),
+            "path": "push" if s2["last_path"] == 0 else "pull", "call_us": round(call_ms * 1e3, 2),
+            "compute_kernel_us": round(kms * 1e3, 2),
+            "meta_kernel_us": round(s2["sum_meta_ms"] / s2["timed_calls"] * 1e3, 2),
+            "bytes": int(mb + cb), "call_GBps": round((mb + cb) / (call_ms * 1e-3) / 1e9, 1),
+            "compute_kernel_GBps": round(cb / (kms * 1e-3) / 1e9, 1),
+            "compute_kernel_frac_of_hbm": round(cb / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        })
+        log(f"[bench] zipf d={d}: {per[-1]}")
+    dbs.dbs_set_option(A, dbs.DBS_OPT_TIMING, 0)
+    hist = np.bincount(np.floor(np.log2(np.maximum(lens, 1))).astype(np.int64))
+    return {"workload": "zipf(1.8) row lengths capped at 2^20, 90% band + 10% uniform, 8388608^2, fp32",
+            "nnz": int(lens.sum()), "max_row": int(lens.max()),
+            "row_length_log2_histogram": hist.tolist(), "generate_s": round(gen_s, 1), "build_s": round(build_s, 2),
+            "tiles": st["tiles"], "tiles_by_format": st["tiles_by_format"], "segments": st["segments"],
+            "format_MB": round(st["format_bytes"] / 1e6, 1), "per_density": per}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -366,6 +429,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-bfs", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-zipf", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--headline-only", action="store_true",
                     help="only the timed sweep (for profiling: every SpMSpV launch is one of the timed mix)")
@@ -401,7 +465,7 @@ def main():
              "rmat20_format": res["format"], "rmat20_build_s": round(res["build_s"], 2)}
     cpu = None
     if args.headline_only:
-        args.no_cpu = args.no_bfs = args.no_decode = True
+        args.no_cpu = args.no_bfs = args.no_decode = args.no_zipf = True
     if not args.no_cpu:
         cpu = cpu_baseline_rmat20(res, args.cpu_seconds)
         log(f"[bench] cpu baseline: {cpu}")
@@ -411,6 +475,8 @@ def main():
         log(f"[bench] bfs: {extra['bfs_rmat22']}")
     if not args.no_decode:
         extra["decode"] = bench_decode(dbs, torch, args)
+    if not args.no_zipf:
+        extra["zipf_band"] = bench_zipf(dbs, torch, args)
     traffic = load_traffic("rmat20_sweep")
     line = {
         "metric": METRIC,

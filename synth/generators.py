@@ -183,20 +183,23 @@ def decode_activation(k: int, zero_frac: float, rng: np.random.Generator) -> np.
 def zipf_lengths(n: int, rng: np.random.Generator, alpha: float = 1.8,
                  cap: int = 1 << 20, target_nnz: int = 128 * 1000 * 1000) -> np.ndarray:
     """Row lengths min(cap, max(1, round(c*L_i))), L_i ~ Zipf(alpha), c by bisection
-    so that the total is close to ``target_nnz``."""
-    raw = rng.zipf(alpha, size=n).astype(np.float64)
+    so that the total is close to ``target_nnz``.  The bisection runs over the
+    distinct values of L with their counts."""
+    raw = rng.zipf(alpha, size=n)
+    vals, inv, cnt = np.unique(raw, return_inverse=True, return_counts=True)
+    vals = vals.astype(np.float64)
 
-    def total(scale: float) -> int:
-        return int(np.minimum(cap, np.maximum(1.0, np.rint(scale * raw))).sum())
+    def lengths(scale: float) -> np.ndarray:
+        return np.minimum(cap, np.maximum(1.0, np.rint(scale * vals))).astype(np.int64)
 
     lo, hi = 1e-6, 1e3
     for _ in range(80):
         mid = 0.5 * (lo + hi)
-        if total(mid) < target_nnz:
+        if int((lengths(mid) * cnt).sum()) < target_nnz:
             lo = mid
         else:
             hi = mid
-    return np.minimum(cap, np.maximum(1.0, np.rint(lo * raw))).astype(np.int64)
+    return lengths(lo)[inv.reshape(-1)]
 
 
 def zipf_band_csr(n: int, rng: np.random.Generator, alpha: float = 1.8,
@@ -204,34 +207,37 @@ def zipf_band_csr(n: int, rng: np.random.Generator, alpha: float = 1.8,
                   band_frac: float = 0.9):
     """n x n float32 U[-1, 1] matrix with Zipf row lengths.
 
-    Per row i of length L, round(band_frac*L) columns are uniform in the band
-    [i - h, i + h], h = max(64, L) (mirrored at the matrix edges), the rest are
-    uniform over [0, n).  Duplicate columns within a row are merged, so the
-    realized row length can be below L.
+    Row i of length L gets round(band_frac*L) columns in a band of width
+    2h+1, h = max(64, L), centred at i (shifted inward at the matrix edges),
+    one column drawn uniformly in each of that many equal strata of the band,
+    so they are distinct; the other columns are uniform over [0, n).  The few
+    duplicates a far column can make are merged.
     """
     lens = zipf_lengths(n, rng, alpha, cap, target_nnz)
-    total = int(lens.sum())
-    rows = np.repeat(np.arange(n, dtype=np.int64), lens)
-    n_band = np.rint(band_frac * lens).astype(np.int64)
-    # position of each entry within its row
-    starts = np.zeros(n + 1, dtype=np.int64)
-    np.cumsum(lens, out=starts[1:])
-    pos = np.arange(total, dtype=np.int64) - np.repeat(starts[:-1], lens)
-    in_band = pos < np.repeat(n_band, lens)
-    del pos
-    half = np.repeat(np.maximum(64, lens), lens)
-    off = (rng.random(total) * (2 * half + 1)).astype(np.int64) - half
-    del half
-    col = rows + off
-    del off
-    col = np.where(col < 0, -col, col)
-    col = np.where(col >= n, 2 * (n - 1) - col, col)
-    far = rng.integers(0, n, size=total, dtype=np.int64)
-    col = np.where(in_band, col, far)
-    del far, in_band
-    keys = rows * n + col
+    nbnd = np.rint(band_frac * lens).astype(np.int64)
+    nfar = lens - nbnd
+    h = np.maximum(64, lens)
+    w = 2 * h + 1
+    start = np.clip(np.arange(n, dtype=np.int64) - h, 0, n - w)
+    # band columns: entry k of row i lies in stratum k of width w_i / nbnd_i
+    rows = np.repeat(np.arange(n, dtype=np.int64), nbnd)
+    k = np.arange(rows.shape[0], dtype=np.int64) - np.repeat(np.cumsum(nbnd) - nbnd, nbnd)
+    width = (w / np.maximum(nbnd, 1))[rows]
+    col = start[rows] + np.floor((k + rng.random(rows.shape[0])) * width).astype(np.int64)
+    del k, width
+    keys_b = rows * n + col
     del rows, col
-    keys = np.unique(keys)
+    rows = np.repeat(np.arange(n, dtype=np.int64), nfar)
+    keys_f = rows * n + rng.integers(0, n, size=rows.shape[0], dtype=np.int64)
+    del rows
+    keys = np.concatenate([keys_b, keys_f])
+    del keys_b, keys_f
+    keys.sort()
+    keep = np.empty(keys.shape[0], dtype=bool)
+    keep[0] = True
+    np.not_equal(keys[1:], keys[:-1], out=keep[1:])
+    keys = keys[keep]
+    del keep
     row_ptr, col_idx = _csr_from_sorted_keys(keys, n, n)
     del keys
     vals = rng.uniform(-1.0, 1.0, size=col_idx.shape[0]).astype(np.float32)
