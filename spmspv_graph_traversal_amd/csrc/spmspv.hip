@@ -131,6 +131,7 @@ struct SpmvParams {
   int32_t force_path;
   int64_t th3_num, th3_den;
   int32_t local_cutoff;
+  int32_t plus_u;  // segments per wave step of the PLUS_TIMES pull (1 or PULL_U_PLUS_WIDE)
   void *y;
 };
 
@@ -222,129 +223,185 @@ DBS_DEV void push_chunk(const SpmvParams &P, uint64_t own, float *sx, float *spa
 // whole wave.  The row block's partial is merged in registers and written
 // once: a plain store when the row block is one segment, an atomic add when
 // several segments share it.
-// ---------------------------------------------------------------------------
-// Finish one segment whose tiles are loaded: COO tiles one per lane, larger
-// tiles by the whole wave, merge in registers, write the row block.
-constexpr int PULL_U_PLUS = 1;  // segments per wave step, PLUS_TIMES pull
+constexpr int PULL_U_PLUS_WIDE = 4;  // segments per wave step, PLUS_TIMES pull with many segments
 constexpr int PULL_U_OR = 8;    // segments per wave step, OR_AND pull (value matrices)
 constexpr int PULL_U_PAT = 4;   // segments per wave step, OR_AND pull of pattern matrices
 
-template <int VK, int SR>
+// ---------------------------------------------------------------------------
+// PLUS_TIMES over the COO tiles of one pull segment, entries spread over the
+// lanes: the COO tiles' payloads (coordinates, then values) follow one
+// another in tile order, so entry j of the segment is entry j - start_t of
+// the tile t whose first entry start_t (a wave prefix sum of the tiles' entry
+// counts) is the last one at or below j, found by a wave max-scan of the
+// tiles' marks.  Lane j reads its entry's coordinate, value and x value and
+// adds the product to its row in LDS (s_y, 16 floats of this wave).  Each
+// vector memory instruction thus covers 64 entries, whatever the tiles'
+// sizes, instead of one tile per lane looping over the largest tile's
+// entries.  The row totals are left in s_y.
+// ---------------------------------------------------------------------------
+template <int VK>
+DBS_DEV void coo_entries_plus(const brsrc_t pay, const brsrc_t xr, bool coo, uint64_t meta, uint32_t m, uint32_t cb,
+                              uint32_t *s_mark, float *s_y, int lane) {
+  constexpr uint32_t VS = VK == VK_F32 ? 4u : 2u;
+  constexpr int B = 4;  // chunks of 64 entries whose loads are issued together
+  const uint32_t cnt = coo ? meta_nnz(meta) : 0u;
+  const uint32_t start = wave_incl_add(cnt) - cnt;
+  const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)(start + cnt), 63);
+  const uint32_t vp = (uint32_t)meta_vp(meta);
+  uint32_t carry = 0u;
+  for (uint32_t j00 = 0; j00 < total; j00 += 64u * B) {
+    // owner tile of each entry of the B chunks (lanes talk through LDS, each
+    // step fenced at wave scope)
+    int own[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const uint32_t j0 = j00 + 64u * b;
+      own[b] = 0;
+      if (j0 >= total) continue;  // uniform
+      __syncwarp();
+      s_mark[lane] = 0u;
+      __syncwarp();
+      if ((cnt != 0u) & (start >= j0) & (start < j0 + 64u)) s_mark[start - j0] = (uint32_t)lane + 1u;
+      __syncwarp();
+      uint32_t o = wave_incl_max(s_mark[lane]);
+      o = o > carry ? o : carry;
+      carry = (uint32_t)__builtin_amdgcn_readlane((int)o, 63);
+      own[b] = (int)o - 1;
+    }
+    // coordinates and values, then x values, of all B chunks
+    uint32_t rc[B], ocb[B], om[B];
+    float a[B], x[B];
+    bool live[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const uint32_t j = j00 + 64u * b + (uint32_t)lane;
+      live[b] = j < total;
+      const uint32_t ovp = (uint32_t)__shfl((int)vp, own[b]), ost = (uint32_t)__shfl((int)start, own[b]);
+      const uint32_t ocnt = (uint32_t)__shfl((int)cnt, own[b]);
+      ocb[b] = (uint32_t)__shfl((int)cb, own[b]);
+      om[b] = (uint32_t)__shfl((int)m, own[b]);
+      const uint32_t e = j - ost;
+      rc[b] = __builtin_amdgcn_raw_buffer_load_b8(pay, live[b] ? ovp + e : OOB_OFF, 0, 0);
+      const uint32_t aoff = live[b] ? ovp + coo_val_off(ocnt) + e * VS : OOB_OFF;
+      if (VK == VK_F32) a[b] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(pay, aoff, 0, 0));
+      else a[b] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(pay, aoff, 0, 0) << 16);
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const uint32_t c = rc[b] & 15u;
+      live[b] = live[b] & ((om[b] >> c) & 1u);
+      const uint32_t xoff = live[b] ? (ocb[b] * 16u + c) * VS : OOB_OFF;
+      if (VK == VK_F32) x[b] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(xr, xoff, 0, 0));
+      else x[b] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(xr, xoff, 0, 0) << 16);
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b)
+      if (live[b]) atomicAdd(&s_y[rc[b] >> 4], a[b] * x[b]);
+  }
+  __syncwarp();
+}
+
+// ---------------------------------------------------------------------------
+// Finish one PLUS_TIMES pull segment whose tiles are loaded: COO entries over
+// the lanes, Dense and CSR-family tiles four at a time (row per lane),
+// ForceCSC and few-column patched CSR tiles one at a time; then write the row
+// block: a plain store when it is one segment, an atomic add when several
+// segments share it.
+// ---------------------------------------------------------------------------
+template <int VK>
 DBS_DEV void pull_finish(const SpmvParams &P, uint4 seg, uint32_t cb, uint32_t m, uint64_t meta, bool act,
-                         uint32_t pw0, uint32_t pw1, float *sx, float *spart, int lane) {
+                         float *sx, float *spart, uint32_t *s_mark, int lane) {
+  constexpr uint64_t VS = VK == VK_F32 ? 4 : 2;
   const uint32_t rb = seg.x & ~SEG_SPLIT;
   const bool split = (seg.x & SEG_SPLIT) != 0u;
   const uint32_t type = meta_type(meta);
   const int64_t row0 = (int64_t)rb * 16;
-  if (SR == DBS_OR_AND) {
-    uint32_t f = 0;
-    if (act && type == DBS_TILE_COO) f = coo_or_pre(P.payload, meta, m, pw0, pw1);
-    f = group_or_u32<64>(f);
-    uint64_t todo = __ballot(act && type != DBS_TILE_COO);
-    while (todo) {
-      const int src = __ffsll((unsigned long long)todo) - 1;
-      todo &= todo - 1;
-      const uint64_t tm = __shfl(meta, src);
-      const uint32_t tmask = (uint32_t)__shfl((int)m, src);
-      f |= tile_or<VK>(P.payload + meta_vp(tm), dense_mask_ptr<VK>(P, meta_vp(tm)), meta_type(tm), tmask,
-                       lane);
-    }
-    if (lane < 16 && row0 + lane < P.m) {
-      const uint8_t bit = (uint8_t)((f >> lane) & 1u);
-      if (!split) ((uint8_t *)P.y)[row0 + lane] = bit;
-      else if (bit) ((uint8_t *)P.y)[row0 + lane] = 1;
-    }
-  } else {
-    constexpr uint64_t VS = VK == VK_F32 ? 4 : 2;
-    float rowsum = 0.0f;
-    const bool coo = act & (type == DBS_TILE_COO);
-    if (__ballot(coo) != 0ull) {
-      float acc[16];
-#pragma unroll
-      for (int k = 0; k < 16; ++k) acc[k] = 0.0f;
-      if (coo) coo_plus<VK>(P.payload + meta_vp(meta), meta_nnz(meta), m, P.xd, (int64_t)cb * 16, acc);
-      rowsum = wave_rows_reduce(acc, lane);
-    }
-    // patched CSR tiles with few active columns take the column variant
-    // (section 3.3.3); the other row-major tiles go four at a time through
-    // the row-per-lane path; ForceCSC tiles one at a time
-    const uint64_t colv = __ballot(act & (type == DBS_TILE_CSR) & (__popc(m) < P.local_cutoff));
-    const uint64_t rowt = __ballot(act & (type != DBS_TILE_COO) & (type != DBS_TILE_FORCE_CSC)) & ~colv;
-    if (rowt) {
-      const brsrc_t pay = make_rsrc(P.payload, (uint64_t)P.payload_bytes + DBS_PAYLOAD_SLACK);
-      const brsrc_t xr = make_rsrc(P.xd, (uint64_t)P.nb * 16 * VS);
-      rowsum += quarter_merge(rows_plus<VK>(pay, xr, rowt, meta, m, cb, lane));
-    }
-    uint64_t todo = __ballot(act & (type == DBS_TILE_FORCE_CSC)) | colv;
-    while (todo) {
-      const int src = __ffsll((unsigned long long)todo) - 1;
-      todo &= todo - 1;
-      const uint64_t tm = __shfl(meta, src);
-      const uint32_t tmask = (uint32_t)__shfl((int)m, src);
-      const uint32_t tcb = (uint32_t)__shfl((int)cb, src);
-      stage_x<VK>(sx, P.xd, tcb, tmask, lane);
-      rowsum += tile_plus<VK>(P.payload + meta_vp(tm), meta_type(tm), meta_nnz(tm), tmask, sx, spart,
-                              P.local_cutoff, lane);
-      __syncwarp();
-    }
-    if (lane < 16 && row0 + lane < P.m) {
-      if (!split) ((float *)P.y)[row0 + lane] = rowsum;
-      else if (rowsum != 0.0f) unsafeAtomicAdd((float *)P.y + row0 + lane, rowsum);
-    }
+  const brsrc_t pay = make_rsrc(P.payload, (uint64_t)P.payload_bytes + DBS_PAYLOAD_SLACK);
+  const brsrc_t xr = make_rsrc(P.xd, (uint64_t)P.nb * 16 * VS);
+  float rowsum = 0.0f;
+  const bool coo = act & (type == DBS_TILE_COO);
+  if (__ballot(coo) != 0ull) {
+    float *s_y = spart;
+    if (lane < 16) s_y[lane] = 0.0f;
+    coo_entries_plus<VK>(pay, xr, coo, meta, m, cb, s_mark, s_y, lane);
+    rowsum = s_y[lane & 15];
+    __syncwarp();
+  }
+  // patched CSR tiles with few active columns take the column variant
+  // (section 3.3.3); the other row-major tiles go four at a time through
+  // the row-per-lane path; ForceCSC tiles one at a time
+  const uint64_t colv = __ballot(act & (type == DBS_TILE_CSR) & (__popc(m) < P.local_cutoff));
+  const uint64_t rowt = __ballot(act & (type != DBS_TILE_COO) & (type != DBS_TILE_FORCE_CSC)) & ~colv;
+  if (rowt) rowsum += quarter_merge(rows_plus<VK>(pay, xr, rowt, meta, m, cb, lane));
+  uint64_t todo = __ballot(act & (type == DBS_TILE_FORCE_CSC)) | colv;
+  while (todo) {
+    const int src = __ffsll((unsigned long long)todo) - 1;
+    todo &= todo - 1;
+    const uint64_t tm = __shfl(meta, src);
+    const uint32_t tmask = (uint32_t)__shfl((int)m, src);
+    const uint32_t tcb = (uint32_t)__shfl((int)cb, src);
+    stage_x<VK>(sx, P.xd, tcb, tmask, lane);
+    rowsum += tile_plus<VK>(P.payload + meta_vp(tm), meta_type(tm), meta_nnz(tm), tmask, sx, spart,
+                            P.local_cutoff, lane);
+    __syncwarp();
+  }
+  if (lane < 16 && row0 + lane < P.m) {
+    if (!split) ((float *)P.y)[row0 + lane] = rowsum;
+    else if (rowsum != 0.0f) unsafeAtomicAdd((float *)P.y + row0 + lane, rowsum);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Pull: static segments of one row block each (section 3.3.2).  A wave takes
-// U consecutive segments and issues each load phase for all of them before
-// using any result (descriptors; column blocks and, when most vector blocks
-// are active, metadata; masks; remaining metadata), so U independent
-// dependency chains overlap in every wave.  The row block's partial is merged
-// in registers and written once: a plain store when the row block is one
-// segment, an atomic add when several segments share it.
+// PLUS_TIMES pull: static segments of one row block each (section 3.3.2),
+// U per wave step, software-pipelined like the Boolean pull: descriptors,
+// column blocks and metadata of step i+1 are in flight while step i works.
+// U = 1 when there are too few segments to give every resident wave several
+// (the decode layers), PULL_U_PLUS_WIDE otherwise.
 // ---------------------------------------------------------------------------
-template <int VK, int SR, int U>
-DBS_DEV void pull_group(const SpmvParams &P, int64_t s0, bool eager, float *sx, float *spart, int lane) {
-  // Loads are issued without branches (inactive lanes read a valid dummy
-  // address and discard the value): a branch around a load makes the
-  // compiler wait for every outstanding load at the branch.
-  uint4 seg[U];
+struct AllRows {
+  DBS_DEV uint32_t need(uint32_t) const { return 0xFFFFu; }
+};
+
+template <int VK, int U, bool EAGER>
+DBS_DEV void plus_pull_wave(const SpmvParams &P, const PatSrc &S, const brsrc_t xm, int64_t s0, int64_t stride,
+                            float *sx, float *spart, uint32_t *s_mark, int lane) {
+  if (s0 >= S.nseg) return;
+  const uint32_t l4 = (uint32_t)lane * 4u, l8 = (uint32_t)lane * 8u;
+  const AllRows pol;
+  PatRound<U> cur, nxt;
+  pat_issue<U, EAGER>(S, pol, s0, true, l4, l8, cur);
+  while (true) {
+    uint32_t m[U];
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int64_t si = s0 + u < P.nseg ? s0 + u : P.nseg - 1;  // wave-uniform: scalar loads
-    seg[u] = ((const uint4 *)P.segs)[si];
+    for (int u = 0; u < U; ++u) {
+      const uint32_t w = bld32(xm, (uint32_t)lane < cur.n[u] ? cur.cb[u] * 4u : OOB_OFF);
+      m[u] = ((w >> 16) == P.epoch) ? (w & 0xFFFFu) : 0u;  // an idle lane reads 0: no epoch
+    }
+    const int64_t s1 = s0 + stride;
+    const bool more = s1 < S.nseg;  // uniform
+    pat_issue<U, EAGER>(S, pol, more ? s1 : s0, more, l4, l8, nxt);
+    if constexpr (!EAGER) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        cur.meta[u] = bld64(make_rsrc(S.t_meta + cur.seg[u].y, (uint64_t)cur.n[u] * 8u), m[u] != 0u ? l8 : OOB_OFF);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (s0 + u < S.nseg) pull_finish<VK>(P, cur.seg[u], cur.cb[u], m[u], cur.meta[u], m[u] != 0u, sx, spart, s_mark, lane);
+    if (!more) break;
+    cur = nxt;
+    s0 = s1;
   }
-  uint32_t cb[U], m[U];
-  uint64_t meta[U];
-  bool act[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const uint32_t t = seg[u].y + (uint32_t)lane;
-    act[u] = s0 + u < P.nseg && t < seg[u].z;
-    const uint32_t tc = act[u] ? t : seg[u].y;
-    cb[u] = P.t_cb[tc];
-    meta[u] = eager ? P.t_meta[tc] : 0ull;
-  }
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const uint32_t w = P.xmask[cb[u]];
-    m[u] = (act[u] & ((w >> 16) == P.epoch)) ? (w & 0xFFFFu) : 0u;
-    act[u] = m[u] != 0u;
-  }
-  if (!eager) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) meta[u] = P.t_meta[act[u] ? seg[u].y + (uint32_t)lane : seg[u].y];
-  }
-  uint32_t pw0[U], pw1[U];
-  if (SR == DBS_OR_AND) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) coo_preload(P.payload, meta[u], act[u], pw0[u], pw1[u]);
-  }
-#pragma unroll
-  for (int u = 0; u < U; ++u)
-    if (s0 + u < P.nseg)
-      pull_finish<VK, SR>(P, seg[u], cb[u], m[u], meta[u], act[u], SR == DBS_OR_AND ? pw0[u] : 0u,
-                          SR == DBS_OR_AND ? pw1[u] : 0u, sx, spart, lane);
+}
+
+template <int VK, int U>
+DBS_DEV void plus_pull(const SpmvParams &P, int64_t gw, int64_t nw, bool eager, float *sx, float *spart,
+                       uint32_t *s_mark, int lane) {
+  const PatSrc S{P.t_cb, P.t_meta, P.segs, P.nseg,
+                 make_rsrc(P.payload, (uint64_t)P.payload_bytes + DBS_PAYLOAD_SLACK)};
+  const brsrc_t xm = make_rsrc(P.xmask, (uint64_t)P.nb * 4);
+  if (eager) plus_pull_wave<VK, U, true>(P, S, xm, gw * U, nw * U, sx, spart, s_mark, lane);
+  else plus_pull_wave<VK, U, false>(P, S, xm, gw * U, nw * U, sx, spart, s_mark, lane);
 }
 
 // OR-AND pull (the Boolean semiring of graph traversal): as pull_group, with
@@ -473,8 +530,8 @@ __global__ __launch_bounds__(KT) void k_spmspv(SpmvParams P) {
         for (int64_t s = gw * U; s < P.nseg; s += nw * U) pull_or_group<VK, U>(P, R, s, eager, lane);
       }
     } else {
-      constexpr int U = PULL_U_PLUS;
-      for (int64_t s = gw * U; s < P.nseg; s += nw * U) pull_group<VK, SR, U>(P, s, eager, s_x[w], s_part[w], lane);
+      if (P.plus_u == PULL_U_PLUS_WIDE) plus_pull<VK, PULL_U_PLUS_WIDE>(P, gw, nw, eager, s_x[w], s_part[w], s_mark[w], lane);
+      else plus_pull<VK, 1>(P, gw, nw, eager, s_x[w], s_part[w], s_mark[w], lane);
     }
   }
 }
@@ -591,7 +648,17 @@ dbs_status dbs_spmspv_impl(dbs_matrix *A, int32_t nnz_x, const int32_t *x_idx, c
   P.local_cutoff = (int32_t)A->opt[DBS_OPT_LOCAL_PUSH_CUTOFF];
   P.y = y;
   // one wave per group of pull segments (PULL_U_OR or PULL_U_PLUS of them), capped at the resident grid
-  const int pu = sr == DBS_PLUS_TIMES ? PULL_U_PLUS : A->vk == VK_PAT ? PULL_U_PAT : PULL_U_OR;
+  // PLUS_TIMES: several segments per wave step only when there are enough
+  // for every resident wave (about 8 per SIMD) to get several steps
+  static const int cus = [] {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      n = 256;
+    return n;
+  }();
+  P.plus_u = A->nseg >= (int64_t)PULL_U_PLUS_WIDE * 32 * cus * 4 ? PULL_U_PLUS_WIDE : 1;
+  const int pu = sr == DBS_PLUS_TIMES ? P.plus_u : A->vk == VK_PAT ? PULL_U_PAT : PULL_U_OR;
   const int64_t pull_waves = (A->nseg + pu - 1) / pu;
   const int64_t waves = pull_waves > A->max_chunks ? pull_waves : A->max_chunks;
   const int vk = A->vk;

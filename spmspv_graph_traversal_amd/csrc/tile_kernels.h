@@ -53,6 +53,17 @@ DBS_DEV uint32_t wave_incl_max(uint32_t v) {
   return v;
 }
 
+// inclusive prefix sum over lanes 0..lane (same DPP steps as wave_incl_max)
+DBS_DEV uint32_t wave_incl_add(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true);  // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return v;
+}
+
 // inclusive prefix sum over the 16 lanes of each quarter (DPP row shifts;
 // lanes shifted in from outside the quarter read 0)
 DBS_DEV uint32_t quarter_incl_scan(uint32_t v) {
