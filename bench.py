@@ -43,7 +43,7 @@ if ROOT not in sys.path:
 METRIC = "SpMSpV effective GB/s (% of HBM peak) vs x density; BFS GTEPS; decode-layer µs"
 HBM_PEAK_GBS = 8000.0
 DENSITIES = [0.0001, 0.001, 0.01, 0.1, 0.5]
-KERNEL_SRC = ["spmspv.hip", "tile_kernels.h", "common.h"]
+KERNEL_SRC = ["spmspv.hip", "pattern_pull.h", "tile_kernels.h", "common.h"]
 
 
 def log(*a):
