@@ -84,10 +84,12 @@ typedef struct {
   int32_t seg_w_csr;      /*   ForceCSR / ForceCSC / CSR (default 2) */
   int32_t seg_w_coo;      /*   COO (default 1) */
   int32_t seg_cap;        /* a segment closes at the tile bringing its weight to >= cap.
-                             Default 64: one 64-lane wave works on a segment, one COO tile
-                             per lane (the pages' 32-lane warps use 16).  Range 1..64 (a
-                             segment holds at most seg_cap tiles, one per lane); other
-                             values give DBS_ERR_INVALID_ARG. */
+                             0 (default): 64 for value matrices, 256 for pattern matrices
+                             (one 64-lane wave works on a segment, one tile per lane for
+                             value matrices, four for pattern matrices; the pages'
+                             32-lane warps use 16).  Explicit range 1..64 (value) or
+                             1..256 (pattern): a segment holds at most seg_cap tiles;
+                             other values give DBS_ERR_INVALID_ARG. */
 } dbs_build_options;
 
 /* Fills `opt` with the defaults above.  Never fails for a non-NULL pointer. */

@@ -91,8 +91,7 @@ dbs_status map_err(hipError_t e) {
 bool valid_options(const dbs_build_options &o) {
   if (o.th0 < 0 || o.th1 < 0 || o.th2_num <= 0 || o.th2_den <= 0) return false;
   if (o.force_format < -1 || o.force_format > DBS_TILE_CSR) return false;
-  if (o.seg_w_dense < 1 || o.seg_w_csr < 1 || o.seg_w_coo < 1 || o.seg_cap < 1) return false;
-  if (o.seg_cap > DBS_WAVE) return false;  // at most one tile per lane in a pull segment
+  if (o.seg_w_dense < 1 || o.seg_w_csr < 1 || o.seg_w_coo < 1 || o.seg_cap < 0) return false;
   return true;
 }
 
@@ -142,7 +141,7 @@ dbs_status dbs_build_options_default(dbs_build_options *o) {
   o->seg_w_dense = 4;
   o->seg_w_csr = 2;
   o->seg_w_coo = 1;
-  o->seg_cap = 64;
+  o->seg_cap = 0;  // by value type
   return DBS_OK;
 }
 
@@ -157,6 +156,11 @@ dbs_status dbs_build(int32_t m, int32_t n, int64_t nnz, const int32_t *row_ptr, 
   if (opt) o = *opt;
   else dbs_build_options_default(&o);
   if (!valid_options(o)) return DBS_ERR_INVALID_ARG;
+  // a pull segment holds at most one tile per lane for value matrices and
+  // PAT_SEG_CAP tiles (four per lane) for pattern matrices
+  const int cap_max = dtype == DBS_PATTERN ? DBS_PAT_SEG_CAP : DBS_WAVE;
+  if (o.seg_cap == 0) o.seg_cap = cap_max;
+  if (o.seg_cap > cap_max) return DBS_ERR_INVALID_ARG;
 
   dbs_matrix *A = new (std::nothrow) dbs_matrix;
   if (!A) return DBS_ERR_OUT_OF_MEMORY;

@@ -182,11 +182,9 @@ struct BfsPol {
   }
 };
 
-constexpr int BFS_U_PAT = 4;  // segments per wave step, pattern pull
-
 template <int VK>
 __global__ __launch_bounds__(KT) void k_bfs_level(BfsParams P) {
-  __shared__ uint32_t s_mark[KT / DBS_WAVE][64];
+  __shared__ uint32_t s_pat[VK == VK_PAT ? KT / DBS_WAVE : 1][PAT_LDS_WORDS];
   const int lane = __lane_id();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / DBS_WAVE);
   const uint32_t nz = P.cur_ctr[0];
@@ -209,7 +207,7 @@ __global__ __launch_bounds__(KT) void k_bfs_level(BfsParams P) {
       const PatSrc S{P.t_cb, P.t_meta, P.segs, P.nseg,
                      make_rsrc(P.payload, (uint64_t)P.payload_bytes + DBS_PAYLOAD_SLACK)};
       const BfsPol pol{&P, R.bm};
-      pattern_pull<BFS_U_PAT>(S, pol, gw * BFS_U_PAT, nw * BFS_U_PAT, eager, lane, s_mark[w]);
+      pattern_pull(S, pol, gw, nw, eager, lane, s_pat[w]);
     } else {
       for (int64_t s = gw * U; s < P.nseg; s += nw * U) bfs_pull_group<VK, U>(P, R, s, eager, lane);
     }
@@ -313,7 +311,7 @@ dbs_status dbs_bfs_impl(dbs_matrix *A, int32_t src, int32_t *levels, hipStream_t
   P.force_path = (int32_t)A->opt[DBS_OPT_PATH];
   P.th3_num = A->opt[DBS_OPT_TH3_NUM];
   P.th3_den = A->opt[DBS_OPT_TH3_DEN];
-  const int pu = A->vk == VK_PAT ? BFS_U_PAT : 8;
+  const int pu = A->vk == VK_PAT ? 1 : 8;
   int64_t waves = (A->nseg + pu - 1) / pu > chunk_cap ? (A->nseg + pu - 1) / pu : chunk_cap;
   int64_t g = (waves + 3) / 4;
   static const unsigned res_f32 = dbs_resident_groups(k_bfs_level<VK_F32>, KT);

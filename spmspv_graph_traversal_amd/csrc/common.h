@@ -98,6 +98,9 @@ __host__ __device__ inline uint32_t tile_payload_bytes(int type, uint32_t nnz, i
 // zeroed bytes allocated after the payload: wide row loads that start inside
 // the last tile stay inside the allocation
 #define DBS_PAYLOAD_SLACK 256u
+// tiles per pull segment at most, pattern matrices (the Boolean pull's wave
+// holds four tiles per lane)
+#define DBS_PAT_SEG_CAP 256
 
 // ---------------------------------------------------------------------------
 // The handle.

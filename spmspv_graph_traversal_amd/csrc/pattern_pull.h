@@ -49,127 +49,215 @@ DBS_DEV void pat_issue(const PatSrc &S, const Pol &pol, int64_t s0, bool live, u
   }
 }
 
-// Pattern matrices (the graph workloads), pull.  Per step a wave takes U
-// segments and issues each load phase for all of them: segment descriptors
-// (scalar loads), column blocks (and, when most vector blocks are active,
-// metadata) through a buffer range cut to the segment, so lanes past its end
-// read 0 without any address arithmetic; the blk_x_mask gather; metadata of
-// the active tiles; then the coordinate words of the active COO tiles that do
-// not fit in their metadata word.  Those tiles' payloads are consecutive in the
-// COO section, so the segment reads them as one run of words spread over the
-// lanes (word j by lane j), each lane finding the tile of its word by a wave
-// max-scan of the tiles' first-word marks.  A segment thus costs two to five
-// vector memory instructions whatever its size mix, and each instruction
-// covers up to 64 tiles or words.  Larger tiles (Dense, ForceCSR, ForceCSC,
-// patched CSR: all keep the 16 row masks for pattern matrices) are rare and
-// take a separate step.
-// One wave's share of the pull, software-pipelined over its steps: the
-// descriptors, column blocks and metadata of step i+1 are in flight while
-// step i waits for its masks and coordinate words.  EAGER (most vector
-// blocks active): metadata comes with the column blocks and the coordinate
-// words of every non-inline COO tile are read with the masks (an inactive
-// tile's words meet a zero mask).  Otherwise metadata and words are read for
-// the active tiles only, after their masks.
-template <int U, bool EAGER, class Pol>
-DBS_DEV void pattern_pull_wave(const PatSrc &S, const Pol &pol, int64_t s0, int64_t stride, int lane,
-                               uint32_t *s_mark) {
-  if (s0 >= S.nseg) return;
-  const uint32_t l4 = (uint32_t)lane * 4u, l8 = (uint32_t)lane * 8u;
-  PatRound<U> cur, nxt;
-  pat_issue<U, EAGER>(S, pol, s0, true, l4, l8, cur);
-  while (true) {
-    uint32_t m[U];
+// Pattern matrices (the graph workloads), pull.  A wave takes one segment of
+// up to 64*K tiles per step (K slices of 64 consecutive tiles, lane i holding
+// tile 64k+i of slice k), software-pipelined: the next segment's descriptor
+// (scalar loads), column blocks and, when most vector blocks are active,
+// metadata are in flight while the current one waits for its masks and
+// words.  Column blocks and metadata come through a buffer range cut to the
+// segment, so lanes past its end read 0 without any address arithmetic.  COO
+// tiles of up to four entries are decoded from their metadata word; the
+// coordinate words of the other COO tiles are consecutive in the COO section,
+// so the segment reads them as one run spread over the lanes (word j by lane
+// j), each lane finding the tile of its word by a wave max-scan of the tiles'
+// first-word marks and an end test.  Larger tiles (Dense, ForceCSR,
+// ForceCSC, patched CSR: all keep the 16 row masks for pattern matrices) are
+// rare and read their masks per lane.  The work per segment that does not
+// grow with its tiles (descriptor, ballots, word setup, wave OR, writeback)
+// is what bounds this pull, hence segments of up to 256 tiles.
+template <int K>
+struct PatSeg {  // stage A: descriptor, column blocks, metadata
+  uint4 seg;
+  uint32_t n, need;
+  uint32_t cb[K];
+  uint64_t meta[K];
+};
+
+template <int K>
+struct PatMasks {  // stage B: masks, and (EAGER) the first chunk of coordinate words
+  uint32_t m[K];
+  uint64_t nb[K];
+  int tf, tl;  // first and last non-inline COO tile whose words are read (uniform; tl < 0: none)
+  uint32_t base, nwords, word;
+};
+
+template <int K, bool EAGER, class Pol>
+DBS_DEV void patk_issue(const PatSrc &S, const Pol &pol, int64_t s, bool live, uint32_t l4, uint32_t l8,
+                        PatSeg<K> &r) {
+  const cu32_t *q = (const cu32_t *)S.segs + 4 * s;
+  r.seg = make_uint4(q[0], q[1], q[2], 0u);
+  r.need = pol.need(r.seg.x & ~SEG_SPLIT);
+  r.n = (live & (s < S.nseg) & (r.need != 0u)) ? r.seg.z - r.seg.y : 0u;
+  const brsrc_t rcb = make_rsrc(S.t_cb + r.seg.y, (uint64_t)r.n * 4u);
+  const brsrc_t rmt = make_rsrc(S.t_meta + r.seg.y, (uint64_t)r.n * 8u);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      m[u] = pol.mask(cur.cb[u], (uint32_t)lane < cur.n[u]);
-    }
-    // coordinate words of the non-inline COO tiles: [base, base + 4 * nwords)
-    uint32_t word[U], base[U], nwords[U];
-    uint64_t nicb[U];
-    auto issue_words = [&]() {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const bool live = EAGER ? ((uint32_t)lane < cur.n[u]) : (m[u] != 0u);
-        const bool nic = live & (meta_type(cur.meta[u]) == DBS_TILE_COO) & !meta_inline(cur.meta[u]);
-        nicb[u] = __ballot(nic);
-        const int first = nicb[u] ? __ffsll((unsigned long long)nicb[u]) - 1 : 0;
-        const int last = nicb[u] ? 63 - __clzll((long long)nicb[u]) : 0;
-        const uint32_t vp = (uint32_t)meta_vp(cur.meta[u]);
-        const uint32_t vend = vp + coo_val_off(meta_nnz(cur.meta[u]));
-        base[u] = (uint32_t)__builtin_amdgcn_readlane((int)vp, first);
-        nwords[u] = nicb[u] ? ((uint32_t)__builtin_amdgcn_readlane((int)vend, last) - base[u]) >> 2 : 0u;
-        word[u] = bld32(S.pay, (uint32_t)lane < nwords[u] ? base[u] + l4 : OOB_OFF);
-      }
-    };
-    const int64_t s1 = s0 + stride;
-    const bool more = s1 < S.nseg;  // uniform
-    if constexpr (EAGER) {
-      issue_words();
-      pat_issue<U, EAGER>(S, pol, more ? s1 : s0, more, l4, l8, nxt);
-    } else {
-      pat_issue<U, EAGER>(S, pol, more ? s1 : s0, more, l4, l8, nxt);
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        cur.meta[u] = bld64(make_rsrc(S.t_meta + cur.seg[u].y, (uint64_t)cur.n[u] * 8u), m[u] != 0u ? l8 : OOB_OFF);
-      issue_words();
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (s0 + u >= S.nseg) break;
-      const uint64_t meta = cur.meta[u];
-      const uint32_t type = meta_type(meta);
-      // COO tiles with at most four entries: the coordinates are in the metadata word
-      uint32_t f = ((m[u] != 0u) & (type == DBS_TILE_COO) & meta_inline(meta)) ? coo_or4((uint32_t)meta, m[u]) : 0u;
-      if (nicb[u] != 0ull) {
-        const bool nic = (nicb[u] >> lane) & 1ull;
-        // words [slot, send) of this lane's tile; the end test leaves out words
-        // of tiles that are not marked
-        const uint32_t slot = ((uint32_t)meta_vp(meta) - base[u]) >> 2;
-        const uint32_t send = slot + (coo_val_off(meta_nnz(meta)) >> 2);
-        uint32_t carry = 0u;
-        for (uint32_t j0 = 0; j0 < nwords[u]; j0 += 64u) {
-          // lanes talk through LDS: each step is fenced at wave scope, or the
-          // compiler may hand a lane back its own earlier store
-          __syncwarp();
-          s_mark[lane] = 0u;
-          __syncwarp();
-          if (nic & (slot >= j0) & (slot < j0 + 64u)) s_mark[slot - j0] = (uint32_t)lane + 1u;
-          __syncwarp();
-          uint32_t own = wave_incl_max(s_mark[lane]);
-          own = own > carry ? own : carry;
-          carry = (uint32_t)__builtin_amdgcn_readlane((int)own, 63);  // owner of the next chunk's first word
-          const uint32_t mw = (uint32_t)__shfl((int)m[u], (int)own - 1);
-          const uint32_t oend = (uint32_t)__shfl((int)send, (int)own - 1);
-          const uint32_t j = j0 + (uint32_t)lane;
-          const uint32_t wd = j0 == 0u ? word[u] : bld32(S.pay, j < nwords[u] ? base[u] + 4u * j : OOB_OFF);
-          f |= ((j < nwords[u]) & (j < oend)) ? coo_or4(wd, mw) : 0u;
-        }
-      }
-      // larger tiles: 16 row masks each
-      const bool big = (m[u] != 0u) & (type != DBS_TILE_COO);
-      if (__ballot(big) != 0ull) {
-        const uint32_t vp = big ? (uint32_t)meta_vp(meta) : OOB_OFF;
-        const auto a = __builtin_amdgcn_raw_buffer_load_b128(S.pay, vp, 0, 0);
-        const auto b = __builtin_amdgcn_raw_buffer_load_b128(S.pay, big ? vp + 16u : OOB_OFF, 0, 0);
-        const uint32_t rm[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-        uint32_t g = 0;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) g |= (((rm[r >> 1] >> (16 * (r & 1))) & m[u]) != 0u) ? (1u << r) : 0u;
-        f |= g;
-      }
-      f = wave_or(f) & cur.need[u];
-      if (f != 0u) pol.found(cur.seg[u].x & ~SEG_SPLIT, f, lane);  // uniform
-    }
-    if (!more) break;
-    cur = nxt;
-    s0 = s1;
+  for (int k = 0; k < K; ++k) {
+    r.cb[k] = __builtin_amdgcn_raw_buffer_load_b32(rcb, l4 + 256u * k, 0, 0);
+    if constexpr (EAGER) r.meta[k] = bld64(rmt, l8 + 512u * k);
+    else r.meta[k] = 0ull;
   }
 }
 
-template <int U, class Pol>
-DBS_DEV void pattern_pull(const PatSrc &S, const Pol &pol, int64_t s0, int64_t stride, bool eager, int lane,
-                          uint32_t *s_mark) {
-  if (eager) pattern_pull_wave<U, true>(S, pol, s0, stride, lane, s_mark);
-  else pattern_pull_wave<U, false>(S, pol, s0, stride, lane, s_mark);
+// lane l's value of slice k (both wave-uniform), read from every slice so
+// that no array is indexed at run time (the compiler would place it in
+// scratch memory)
+template <int K>
+DBS_DEV uint32_t slice_lane(const uint32_t (&v)[K], int k, int l) {
+  uint32_t r = (uint32_t)__builtin_amdgcn_readlane((int)v[0], l);
+#pragma unroll
+  for (int i = 1; i < K; ++i) {
+    const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v[i], l);
+    r = k == i ? c : r;
+  }
+  return r;
 }
 
+// the non-inline COO tiles whose words are read (every such tile when EAGER:
+// an inactive tile's words meet a zero mask; else the active ones), the run
+// of their words, and its first chunk
+template <int K, bool EAGER>
+DBS_DEV void pat_words(const PatSrc &S, const PatSeg<K> &a, PatMasks<K> &b, int lane, uint32_t l4) {
+  uint32_t vp[K], vend[K];
+  b.tf = 1 << 20;
+  b.tl = -1;
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const bool live = EAGER ? (64u * k + (uint32_t)lane < a.n) : (b.m[k] != 0u);
+    b.nb[k] = __ballot(live & (meta_type(a.meta[k]) == DBS_TILE_COO) & !meta_inline(a.meta[k]));
+    vp[k] = (uint32_t)meta_vp(a.meta[k]);
+    vend[k] = vp[k] + coo_val_off(meta_nnz(a.meta[k]));
+    if (b.nb[k] != 0ull) {
+      const int f = 64 * k + __ffsll((unsigned long long)b.nb[k]) - 1, l = 64 * k + 63 - __clzll((long long)b.nb[k]);
+      b.tf = f < b.tf ? f : b.tf;
+      b.tl = l > b.tl ? l : b.tl;
+    }
+  }
+  b.base = 0u;
+  b.nwords = 0u;
+  if (b.tl >= 0) {
+    b.base = slice_lane<K>(vp, b.tf >> 6, b.tf & 63);
+    b.nwords = (slice_lane<K>(vend, b.tl >> 6, b.tl & 63) - b.base) >> 2;
+  }
+  b.word = bld32(S.pay, (uint32_t)lane < b.nwords ? b.base + l4 : OOB_OFF);
+}
+
+// everything of one segment once its loads have arrived
+template <int K, class Pol>
+DBS_DEV void pat_finish(const PatSrc &S, const Pol &pol, const PatSeg<K> &a, const PatMasks<K> &b, int lane,
+                        uint32_t *s_mark, uint32_t *s_tm, uint32_t *s_te) {
+  const uint32_t n = a.n;  // uniform
+  uint32_t f = 0u;
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    if (64u * k >= n) break;  // uniform
+    const uint64_t meta = a.meta[k];
+    // COO tiles with at most four entries: the coordinates are in the metadata word
+    f |= ((b.m[k] != 0u) & (meta_type(meta) == DBS_TILE_COO) & meta_inline(meta)) ? coo_or4((uint32_t)meta, b.m[k])
+                                                                                    : 0u;
+  }
+  if (b.tl >= 0) {
+    // per-tile mask and word end of this segment, for the word owners
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      if (64u * k >= n) break;  // uniform
+      s_tm[64 * k + lane] = b.m[k];
+      s_te[64 * k + lane] = ((uint32_t)meta_vp(a.meta[k]) + coo_val_off(meta_nnz(a.meta[k])) - b.base) >> 2;
+    }
+    uint32_t carry = 0u;
+    for (uint32_t j0 = 0; j0 < b.nwords; j0 += 64u) {
+      // lanes talk through LDS: each step is fenced at wave scope, or the
+      // compiler may hand a lane back its own earlier store
+      __syncwarp();
+      s_mark[lane] = 0u;
+      __syncwarp();
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const uint32_t slot = ((uint32_t)meta_vp(a.meta[k]) - b.base) >> 2;  // first word of this lane's tile
+        const bool nic = (b.nb[k] >> lane) & 1ull;
+        if (nic & (slot >= j0) & (slot < j0 + 64u)) s_mark[slot - j0] = 64u * k + (uint32_t)lane + 1u;
+      }
+      __syncwarp();
+      uint32_t own = wave_incl_max(s_mark[lane]);
+      own = own > carry ? own : carry;
+      carry = (uint32_t)__builtin_amdgcn_readlane((int)own, 63);  // owner of the next chunk's first word
+      const uint32_t t = own ? own - 1u : 0u;
+      const uint32_t mw = s_tm[t], oend = s_te[t];
+      const uint32_t j = j0 + (uint32_t)lane;
+      const uint32_t wd = j0 == 0u ? b.word : bld32(S.pay, j < b.nwords ? b.base + 4u * j : OOB_OFF);
+      f |= ((j < b.nwords) & (j < oend)) ? coo_or4(wd, mw) : 0u;
+    }
+    __syncwarp();
+  }
+  // larger tiles: 16 row masks each
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    if (64u * k >= n) break;  // uniform
+    const bool big = (b.m[k] != 0u) & (meta_type(a.meta[k]) != DBS_TILE_COO);
+    if (__ballot(big) != 0ull) {
+      const uint32_t o = big ? (uint32_t)meta_vp(a.meta[k]) : OOB_OFF;
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(S.pay, o, 0, 0);
+      const auto y = __builtin_amdgcn_raw_buffer_load_b128(S.pay, big ? o + 16u : OOB_OFF, 0, 0);
+      const uint32_t rm[8] = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+      uint32_t g = 0;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) g |= (((rm[r >> 1] >> (16 * (r & 1))) & b.m[k]) != 0u) ? (1u << r) : 0u;
+      f |= g;
+    }
+  }
+  f = wave_or(f) & a.need;
+  if (f != 0u) pol.found(a.seg.x & ~SEG_SPLIT, f, lane);  // uniform
+}
+
+// One wave's share: segments s0, s0 + stride, ...  Three steps are in flight:
+// while segment i is finished, segment i+1 has its masks (and, EAGER, its
+// coordinate words) and segment i+2 its descriptor, column blocks and
+// metadata in flight.  Loads are issued in that order, so a wait for segment
+// i's data never waits for the loads of the later segments.
+template <int K, bool EAGER, class Pol>
+DBS_DEV void pattern_pull_wave(const PatSrc &S, const Pol &pol, int64_t s0, int64_t stride, int lane,
+                               uint32_t *s_mark, uint32_t *s_tm, uint32_t *s_te) {
+  if (s0 >= S.nseg) return;
+  const uint32_t l4 = (uint32_t)lane * 4u, l8 = (uint32_t)lane * 8u;
+  auto masks = [&](const PatSeg<K> &a, PatMasks<K> &b) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) b.m[k] = pol.mask(a.cb[k], 64u * k + (uint32_t)lane < a.n);
+    if constexpr (EAGER) pat_words<K, true>(S, a, b, lane, l4);
+  };
+  PatSeg<K> a0, a1, a2;
+  PatMasks<K> b0, b1;
+  const int64_t s1 = s0 + stride;
+  patk_issue<K, EAGER>(S, pol, s0, true, l4, l8, a0);
+  patk_issue<K, EAGER>(S, pol, s1 < S.nseg ? s1 : s0, s1 < S.nseg, l4, l8, a1);
+  masks(a0, b0);
+  while (true) {
+    if constexpr (!EAGER) {
+      // metadata of segment s0's active tiles, before the later loads
+      const brsrc_t rmt = make_rsrc(S.t_meta + a0.seg.y, (uint64_t)a0.n * 8u);
+#pragma unroll
+      for (int k = 0; k < K; ++k) a0.meta[k] = bld64(rmt, b0.m[k] != 0u ? l8 + 512u * k : OOB_OFF);
+    }
+    const int64_t sa = s0 + 2 * stride;
+    patk_issue<K, EAGER>(S, pol, sa < S.nseg ? sa : s0, sa < S.nseg, l4, l8, a2);
+    masks(a1, b1);
+    if constexpr (!EAGER) pat_words<K, false>(S, a0, b0, lane, l4);
+    pat_finish<K>(S, pol, a0, b0, lane, s_mark, s_tm, s_te);
+    s0 += stride;
+    if (s0 >= S.nseg) break;
+    a0 = a1;
+    a1 = a2;
+    b0 = b1;
+  }
+}
+
+constexpr int PAT_K = DBS_PAT_SEG_CAP / 64;  // slices of 64 tiles per pattern-pull segment
+
+// LDS per wave: marks (64), masks and word ends of a segment's tiles (2 x 64*K)
+constexpr int PAT_LDS_WORDS = 64 + 2 * 64 * PAT_K;
+
+template <class Pol>
+DBS_DEV void pattern_pull(const PatSrc &S, const Pol &pol, int64_t s0, int64_t stride, bool eager, int lane,
+                          uint32_t *s_lds) {
+  uint32_t *s_mark = s_lds, *s_tm = s_lds + 64, *s_te = s_lds + 64 + 64 * PAT_K;
+  if (eager) pattern_pull_wave<PAT_K, true>(S, pol, s0, stride, lane, s_mark, s_tm, s_te);
+  else pattern_pull_wave<PAT_K, false>(S, pol, s0, stride, lane, s_mark, s_tm, s_te);
+}

@@ -225,7 +225,6 @@ DBS_DEV void push_chunk(const SpmvParams &P, uint64_t own, float *sx, float *spa
 // several segments share it.
 constexpr int PULL_U_PLUS_WIDE = 4;  // segments per wave step, PLUS_TIMES pull with many segments
 constexpr int PULL_U_OR = 8;    // segments per wave step, OR_AND pull (value matrices)
-constexpr int PULL_U_PAT = 4;   // segments per wave step, OR_AND pull of pattern matrices
 
 // ---------------------------------------------------------------------------
 // PLUS_TIMES over the COO tiles of one pull segment, entries spread over the
@@ -502,6 +501,7 @@ __global__ __launch_bounds__(KT) void k_spmspv(SpmvParams P) {
   __shared__ float s_x[KT / DBS_WAVE][16];
   __shared__ float s_part[KT / DBS_WAVE][64];
   __shared__ uint32_t s_mark[KT / DBS_WAVE][64];
+  __shared__ uint32_t s_pat[VK == VK_PAT && SR == DBS_OR_AND ? KT / DBS_WAVE : 1][PAT_LDS_WORDS];
   const int lane = __lane_id();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / DBS_WAVE);
   const uint32_t nz = P.ctr[0];
@@ -525,7 +525,7 @@ __global__ __launch_bounds__(KT) void k_spmspv(SpmvParams P) {
       if constexpr (VK == VK_PAT) {
         const PatSrc S{P.t_cb, P.t_meta, P.segs, P.nseg, R.pay};
         const OrPol pol{R.xmask, P.epoch, P.m, (uint8_t *)P.y};
-        pattern_pull<PULL_U_PAT>(S, pol, gw * PULL_U_PAT, nw * PULL_U_PAT, eager, lane, s_mark[w]);
+        pattern_pull(S, pol, gw, nw, eager, lane, s_pat[w]);
       } else {
         for (int64_t s = gw * U; s < P.nseg; s += nw * U) pull_or_group<VK, U>(P, R, s, eager, lane);
       }
@@ -658,7 +658,7 @@ dbs_status dbs_spmspv_impl(dbs_matrix *A, int32_t nnz_x, const int32_t *x_idx, c
     return n;
   }();
   P.plus_u = A->nseg >= (int64_t)PULL_U_PLUS_WIDE * 32 * cus * 4 ? PULL_U_PLUS_WIDE : 1;
-  const int pu = sr == DBS_PLUS_TIMES ? P.plus_u : A->vk == VK_PAT ? PULL_U_PAT : PULL_U_OR;
+  const int pu = sr == DBS_PLUS_TIMES ? P.plus_u : A->vk == VK_PAT ? 1 : PULL_U_OR;
   const int64_t pull_waves = (A->nseg + pu - 1) / pu;
   const int64_t waves = pull_waves > A->max_chunks ? pull_waves : A->max_chunks;
   const int vk = A->vk;

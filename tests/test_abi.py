@@ -76,5 +76,5 @@ def test_default_build_options(lib):
     assert lib.dbs_build_options_default(C.byref(o)) == 0
     # section 3.2.1 thresholds, section 3.3.2 weights; cap 64 for one 64-lane wave
     assert (o.th0, o.th1, o.th2_num, o.th2_den, o.force_format) == (32, 128, 2, 1, -1)
-    assert (o.seg_w_dense, o.seg_w_csr, o.seg_w_coo, o.seg_cap) == (4, 2, 1, 64)
+    assert (o.seg_w_dense, o.seg_w_csr, o.seg_w_coo, o.seg_cap) == (4, 2, 1, 0)
     assert lib.dbs_build_options_default(None) == 1

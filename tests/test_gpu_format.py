@@ -31,7 +31,9 @@ def _arrays(dbs, A):
     }
 
 
-def check_format(dbs, m, n, rp, ci, vbits, dtype, vk, opt=None, th=(32, 128, 2.0), force=-1, cap=64):
+def check_format(dbs, m, n, rp, ci, vbits, dtype, vk, opt=None, th=(32, 128, 2.0), force=-1, cap=None):
+    if cap is None:  # the default segment cap by value type
+        cap = 256 if dtype == dbs.DBS_PATTERN else 64
     A = build(dbs, m, n, rp, ci, vbits, dtype, options=opt)
     ar = _arrays(dbs, A)
     tv = orc.tile_view(m, n, rp, ci, th[0], th[1], th[2])

@@ -239,10 +239,11 @@ def test_argument_errors(dbs):
     assert lib.dbs_set_option(A.handle, 99, 0) == dbs.DBS_ERR_INVALID_ARG
     assert lib.dbs_set_option(A.handle, dbs.DBS_OPT_PATH, 3) == dbs.DBS_ERR_INVALID_ARG
     # a pull segment holds at most one tile per lane
-    for cap in (0, 65):
+    for cap, dt, vals in ((-1, dbs.DBS_F32, v), (65, dbs.DBS_F32, v), (257, dbs.DBS_PATTERN, None)):
         with pytest.raises(dbs.DBSError) as e:
-            build(dbs, 64, 64, rp, ci, v, dbs.DBS_F32, options(dbs, seg_cap=cap))
+            build(dbs, 64, 64, rp, ci, vals, dt, options(dbs, seg_cap=cap))
         assert e.value.status == dbs.DBS_ERR_INVALID_ARG
+    build(dbs, 64, 64, rp, ci, None, dbs.DBS_PATTERN, options(dbs, seg_cap=256))
 
 
 def test_rmat20_or_and_sweep_full_size(dbs):
