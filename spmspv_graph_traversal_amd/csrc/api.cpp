@@ -69,8 +69,8 @@ void free_all(dbs_matrix *A) {
   for (void *b : bufs)
     if (b) (void)hipFree(b);
   if (A->bfs_host) (void)hipHostFree(A->bfs_host);
-  for (int i = 0; i < 6; ++i)
-    if (A->ev[i]) (void)hipEventDestroy(A->ev[i]);
+  for (hipEvent_t e : A->ev)
+    if (e) (void)hipEventDestroy(e);
   if (A->tev_ready)
     for (int i = 0; i < dbs_matrix::kTimingRing; ++i)
       for (int j = 0; j < 3; ++j) (void)hipEventDestroy(A->tev[i][j]);
@@ -197,7 +197,8 @@ dbs_status dbs_build(int32_t m, int32_t n, int64_t nnz, const int32_t *row_ptr, 
     A->st.build_peak_bytes = A->mem_peak;
     st = alloc_call_scratch(A);
   }
-  for (int i = 0; st == DBS_OK && i < 6; ++i) st = map_err(DBS_NOTE(hipEventCreate(&A->ev[i])));
+  for (hipEvent_t &e : A->ev)
+    if (st == DBS_OK) st = map_err(DBS_NOTE(hipEventCreate(&e)));
   if (st == DBS_OK) st = map_err(DBS_NOTE(hipStreamSynchronize(s)));
   if (st != DBS_OK) {
     (void)hipStreamSynchronize(s);

@@ -13,7 +13,11 @@
 //                (one atomic per workgroup), cuts them into push chunks when
 //                the next level pushes, and clears the bitmap two levels back.
 // Three bitmaps rotate: current frontier, next frontier, and one being
-// cleared.  The host reads one counter per level to stop.
+// cleared.  The host launches levels in batches without waiting: each level
+// kernel records its frontier's nonzero-block count, and one read of those
+// counts per batch finds the first empty frontier, where the traversal ends.
+// Levels of a batch past that point see an empty frontier and return at
+// once (no vertex is found, nothing is written but cleared buffers).
 #include "meta.h"
 #include "pattern_pull.h"
 #include "tile_kernels.h"
@@ -38,6 +42,7 @@ struct BfsParams {
   uint32_t *vis;            // visited bitmap
   const uint32_t *cur_ctr;  // [0] nonzero blocks, [1] push chunks
   const uint64_t *cur_chunks;
+  uint32_t *hist;           // nonzero blocks of the current frontier, stored at [level % batch]
   int32_t *levels;
   int32_t level;            // level of the current frontier
   int32_t force_path;
@@ -188,6 +193,8 @@ __global__ __launch_bounds__(KT) void k_bfs_level(BfsParams P) {
   const int lane = __lane_id();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / DBS_WAVE);
   const uint32_t nz = P.cur_ctr[0];
+  if (blockIdx.x == 0 && threadIdx.x == 0) P.hist[P.level % dbs_matrix::kBfsBatch] = nz;
+  if (nz == 0u) return;  // uniform: empty frontier, nothing to find
   const bool push = P.force_path == 1 ||
                     (P.force_path == 0 && (int64_t)nz * P.th3_den < (int64_t)P.nb * P.th3_num);
   const int64_t gw = (int64_t)blockIdx.x * (KT / DBS_WAVE) + w;
@@ -264,11 +271,11 @@ dbs_status dbs_bfs_impl(dbs_matrix *A, int32_t src, int32_t *levels, hipStream_t
     BFS_TRY(dbs_dev_alloc(A, (void **)&A->bfs_vis, (size_t)(nwords + 1) * 4));
     BFS_TRY(dbs_dev_alloc(A, (void **)&A->bfs_list, (size_t)(3 * (int64_t)A->nb + 1) * 4));
     BFS_TRY(dbs_dev_alloc(A, (void **)&A->bfs_chunks, (size_t)(3 * chunk_cap + 1) * 8));
-    BFS_TRY(dbs_dev_alloc(A, (void **)&A->bfs_ctr, 24 * 4));
+    BFS_TRY(dbs_dev_alloc(A, (void **)&A->bfs_ctr, (24 + dbs_matrix::kBfsBatch) * 4));
     BFS_TRY(hipHostMalloc((void **)&A->bfs_host, 64, hipHostMallocDefault));
   }
   const bool timing = A->opt[DBS_OPT_TIMING] != 0;
-  if (timing) BFS_TRY(hipEventRecord(A->ev[3], s));
+  if (timing) BFS_TRY(hipEventRecord(A->ev[0], s));
   hipLaunchKernelGGL(k_bfs_init, dim3(1024), dim3(256), 0, s, levels, A->m, A->bfs_bm, 3 * nwords,
                      A->bfs_vis, nwords, A->bfs_ctr, src);
   hipLaunchKernelGGL(k_bfs_seed, dim3(1), dim3(1), 0, s, A->bfs_bm, A->bfs_vis, src);
@@ -320,46 +327,55 @@ dbs_status dbs_bfs_impl(dbs_matrix *A, int32_t src, int32_t *levels, hipStream_t
   const unsigned cap = A->vk == VK_F32 ? res_f32 : A->vk == VK_BF16 ? res_bf16 : res_pat;
   const unsigned grid = (unsigned)(g < 1 ? 1 : (g > cap ? cap : g));
 
-  int32_t L = 0, push_levels = 0;
+  constexpr int B = dbs_matrix::kBfsBatch;
+  static_assert(B * 4 <= 64, "pinned mirror holds 16 counts");
+  P.hist = A->bfs_ctr + 24;
+  int32_t L = -1, push_levels = 0;
   float kms = 0.0f;
-  while (true) {
-    const int cur = L % 3, nxt = (L + 1) % 3, clr = (L + 2) % 3;
-    P.cur_bm = A->bfs_bm + cur * nwords;
-    P.next_bm = A->bfs_bm + nxt * nwords;
-    P.cur_ctr = A->bfs_ctr + 8 * cur;
-    P.cur_chunks = A->bfs_chunks + cur * chunk_cap;
-    P.level = L;
-    if (timing) BFS_TRY(hipEventRecord(A->ev[4], s));
-    if (A->vk == VK_F32) hipLaunchKernelGGL(k_bfs_level<VK_F32>, dim3(grid), dim3(KT), 0, s, P);
-    else if (A->vk == VK_BF16) hipLaunchKernelGGL(k_bfs_level<VK_BF16>, dim3(grid), dim3(KT), 0, s, P);
-    else hipLaunchKernelGGL(k_bfs_level<VK_PAT>, dim3(grid), dim3(KT), 0, s, P);
-    BFS_TRY(hipGetLastError());
-    if (timing) BFS_TRY(hipEventRecord(A->ev[5], s));
-    hipLaunchKernelGGL(k_bfs_meta, dim3(mgrid), dim3(dbs_meta::MT), 0, s, (const uint32_t *)P.next_bm, A->nb, reg_for(nxt),
-                       A->bfs_bm + clr * nwords, A->bfs_ctr + 8 * clr, nwords);
-    BFS_TRY(hipGetLastError());
-    BFS_TRY(hipMemcpyAsync(A->bfs_host, A->bfs_ctr + 8 * cur, 8, hipMemcpyDeviceToHost, s));
-    BFS_TRY(hipMemcpyAsync(A->bfs_host + 2, A->bfs_ctr + 8 * nxt, 4, hipMemcpyDeviceToHost, s));
-    BFS_TRY(hipStreamSynchronize(s));
-    if (timing) {
-      float ms = 0.0f;
-      BFS_TRY(hipEventElapsedTime(&ms, A->ev[4], A->ev[5]));
-      kms += ms;
+  for (int64_t L0 = 0; L < 0; L0 += B) {
+    if (L0 > (int64_t)A->m + 1) return DBS_ERR_DEVICE;  // cannot happen: every level adds a vertex
+    for (int i = 0; i < B; ++i) {
+      const int64_t l = L0 + i;
+      const int cur = (int)(l % 3), nxt = (int)((l + 1) % 3), clr = (int)((l + 2) % 3);
+      P.cur_bm = A->bfs_bm + cur * nwords;
+      P.next_bm = A->bfs_bm + nxt * nwords;
+      P.cur_ctr = A->bfs_ctr + 8 * cur;
+      P.cur_chunks = A->bfs_chunks + cur * chunk_cap;
+      P.level = (int32_t)l;
+      if (timing) BFS_TRY(hipEventRecord(A->ev[2 + 2 * i], s));
+      if (A->vk == VK_F32) hipLaunchKernelGGL(k_bfs_level<VK_F32>, dim3(grid), dim3(KT), 0, s, P);
+      else if (A->vk == VK_BF16) hipLaunchKernelGGL(k_bfs_level<VK_BF16>, dim3(grid), dim3(KT), 0, s, P);
+      else hipLaunchKernelGGL(k_bfs_level<VK_PAT>, dim3(grid), dim3(KT), 0, s, P);
+      BFS_TRY(hipGetLastError());
+      if (timing) BFS_TRY(hipEventRecord(A->ev[3 + 2 * i], s));
+      hipLaunchKernelGGL(k_bfs_meta, dim3(mgrid), dim3(dbs_meta::MT), 0, s, (const uint32_t *)P.next_bm, A->nb,
+                         reg_for(nxt), A->bfs_bm + clr * nwords, A->bfs_ctr + 8 * clr, nwords);
+      BFS_TRY(hipGetLastError());
     }
-    const uint32_t nz_cur = A->bfs_host[0];
-    const bool was_push = A->opt[DBS_OPT_PATH] == 1 ||
-                          (A->opt[DBS_OPT_PATH] == 0 &&
-                           (int64_t)nz_cur * A->opt[DBS_OPT_TH3_DEN] < (int64_t)A->nb * A->opt[DBS_OPT_TH3_NUM]);
-    push_levels += was_push ? 1 : 0;
-    ++L;
-    if (A->bfs_host[2] == 0u) break;
-    if (L > A->m + 1) return DBS_ERR_DEVICE;  // cannot happen: every level adds a vertex
+    BFS_TRY(hipMemcpyAsync(A->bfs_host, P.hist, B * 4, hipMemcpyDeviceToHost, s));
+    BFS_TRY(hipStreamSynchronize(s));
+    for (int i = 0; i < B; ++i) {
+      const uint32_t nz = A->bfs_host[i];  // nonzero blocks of frontier L0 + i
+      if (nz == 0u) {
+        L = (int32_t)(L0 + i);
+        break;
+      }
+      const bool was_push = A->opt[DBS_OPT_PATH] == 1 ||
+                            (A->opt[DBS_OPT_PATH] == 0 &&
+                             (int64_t)nz * A->opt[DBS_OPT_TH3_DEN] < (int64_t)A->nb * A->opt[DBS_OPT_TH3_NUM]);
+      push_levels += was_push ? 1 : 0;
+      if (timing) {
+        float ms = 0.0f;
+        BFS_TRY(hipEventElapsedTime(&ms, A->ev[2 + 2 * i], A->ev[3 + 2 * i]));
+        kms += ms;
+      }
+    }
   }
   if (timing) {
-    BFS_TRY(hipEventRecord(A->ev[4], s));
-    BFS_TRY(hipEventSynchronize(A->ev[4]));
+    BFS_TRY(hipEventRecord(A->ev[1], s));
+    BFS_TRY(hipEventSynchronize(A->ev[1]));
     float ms = 0.0f;
-    BFS_TRY(hipEventElapsedTime(&ms, A->ev[3], A->ev[4]));
+    BFS_TRY(hipEventElapsedTime(&ms, A->ev[0], A->ev[1]));
     A->st.bfs_ms = ms;
     A->st.bfs_kernel_ms = kms;
   } else {

@@ -140,14 +140,16 @@ struct dbs_matrix {
   uint32_t *bfs_vis;     // visited bitmap
   uint32_t *bfs_list;    // 3 lists of nb vertex blocks
   uint64_t *bfs_chunks;  // 3 chunk lists
-  uint32_t *bfs_ctr;     // 3 x 8 counters
-  uint32_t *bfs_host;    // pinned host mirror of a counter
+  uint32_t *bfs_ctr;     // 3 x 8 counters, then the frontier sizes of one batch of levels
+  uint32_t *bfs_host;    // pinned host mirror of those frontier sizes
 
   // options and statistics
   int64_t opt[8];
   dbs_stats st;
   hipStream_t last_stream;
-  hipEvent_t ev[6];      // BFS timing
+  // BFS: levels launched between two host reads of the frontier sizes
+  static constexpr int kBfsBatch = 4;
+  hipEvent_t ev[2 + 2 * kBfsBatch];  // BFS timing: whole run, then each level kernel of a batch
   // ring of per-call event triples (before meta, after meta, after compute)
   static constexpr int kTimingRing = 64;
   hipEvent_t tev[kTimingRing][3];
