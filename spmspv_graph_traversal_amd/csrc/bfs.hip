@@ -1,14 +1,14 @@
 // DB-BFS (section 4.2 and Algorithm 5 of "DB-SpMSpV: Dual-View Blocked Sparse
 // Matrix-Sparse Vector Multiplication for Dynamic GPU Workloads").
 //
-// The frontier is kept as a bitmap, 16 bits per vertex block, which is
-// directly the blk_x_mask array of the SpMSpV (section 4.1: "the frontier can
-// be represented directly as a set of masks").  Per level:
+// The frontier is kept as a bitmap, 16 bits per vertex block, which serves
+// unchanged as the blk_x_mask array of the SpMSpV (section 4.1 treats the
+// frontier as such a mask set).  Per level:
 //   k_bfs_level  masked Boolean SpMSpV next = A f & ~visited, push or pull
 //                chosen on the device from the frontier's nonzero-block count;
-//                newly found vertices are claimed with an atomic OR on the
-//                next bitmap (the winner writes their level and marks them
-//                visited);
+//                rows found that were unvisited when the level started are
+//                claimed with non-returning atomic ORs on the next and
+//                visited bitmaps, and their level is stored;
 //   k_bfs_meta   counts the nonzero blocks of the next bitmap, lists them
 //                (one atomic per workgroup), cuts them into push chunks when
 //                the next level pushes, and clears the bitmap two levels back.
@@ -56,16 +56,29 @@ DBS_DEV uint32_t rows_valid(int32_t m, uint32_t rb) {
   return left >= 16 ? 0xFFFFu : (left <= 0 ? 0u : ((1u << left) - 1u));
 }
 
-// claim the vertices `f` of row block rb for the next level
-DBS_DEV void discover(const BfsParams &P, uint32_t rb, uint32_t f) {
+// Claim rows `f` of row block rb for the next level.  Every row in f was
+// unvisited when this level started, so its distance is level + 1 whoever
+// claims it: the bitmaps take plain (non-returning) atomic ORs and a row
+// found twice in this level just has the same level stored twice.
+DBS_DEV void claim(const BfsParams &P, uint32_t rb, uint32_t f) {
   const uint32_t sh = (rb & 1u) * 16u;
+  atomicOr(&P.next_bm[rb >> 1], f << sh);
+  atomicOr(&P.vis[rb >> 1], f << sh);
+}
+
+// the same for a wave-uniform f: lane 0 takes the atomics, lanes 0..15
+// store the levels
+DBS_DEV void claim_wave(const BfsParams &P, uint32_t rb, uint32_t f, int lane) {
+  if (lane == 0) claim(P, rb, f);
+  if (lane < 16 && ((f >> lane) & 1u)) P.levels[rb * 16u + (uint32_t)lane] = P.level + 1;
+}
+
+// one lane's rows, not yet checked against the visited bitmap
+DBS_DEV void discover(const BfsParams &P, uint32_t rb, uint32_t f) {
   f &= ~bm_get(P.vis, rb) & rows_valid(P.m, rb);
   if (!f) return;
-  const uint32_t old = atomicOr(&P.next_bm[rb >> 1], f << sh);
-  const uint32_t fresh = f & ~(old >> sh);
-  if (!fresh) return;
-  atomicOr(&P.vis[rb >> 1], fresh << sh);
-  for (uint32_t b = fresh; b; b &= b - 1u) P.levels[rb * 16u + (uint32_t)(__ffs(b) - 1)] = P.level + 1;
+  claim(P, rb, f);
+  for (uint32_t b = f; b; b &= b - 1u) P.levels[rb * 16u + (uint32_t)(__ffs(b) - 1)] = P.level + 1;
 }
 
 template <int VK>
@@ -163,28 +176,26 @@ DBS_DEV void bfs_pull_group(const BfsParams &P, const BfsRes &R, int64_t s0, boo
       const uint32_t tmask = (uint32_t)__shfl((int)m[u], src);
       f |= tile_or<VK>(P.payload + meta_vp(tm), dmask<VK>(P, meta_vp(tm)), meta_type(tm), tmask, lane);
     }
-    if (lane == 0 && (f & need[u])) discover(P, seg[u].x & ~SEG_SPLIT, f & need[u]);
+    if (f & need[u]) claim_wave(P, seg[u].x & ~SEG_SPLIT, f & need[u], lane);  // uniform
   }
 }
 
 // BFS pull on a pattern matrix: rows of a row block not yet visited are
-// wanted (a hint read through the scalar cache: a stale word only costs
-// work, discover() checks again), masks come from the frontier bitmap, found
-// rows are claimed for the next level.
+// wanted, masks come from the frontier bitmap, found rows are claimed for
+// the next level.  The visited word may miss rows claimed earlier in this
+// level (that only costs work), never rows of earlier levels.
 struct BfsPol {
   const BfsParams *P;
-  brsrc_t bm;
-  DBS_DEV uint32_t need(uint32_t rb) const {
-    const cu32_t *v = (const cu32_t *)P->vis;
-    return ~(v[rb >> 1] >> ((rb & 1u) * 16u)) & rows_valid(P->m, rb);
+  brsrc_t bm, vis;
+  DBS_DEV uint32_t need_v(uint32_t rb, bool in) const {
+    const uint32_t w = bld32(vis, in ? (rb >> 1) * 4u : OOB_OFF);
+    return ~(w >> ((rb & 1u) * 16u)) & rows_valid(P->m, rb);
   }
   DBS_DEV uint32_t mask(uint32_t cb, bool in) const {
     const uint32_t w = bld32(bm, in ? (cb >> 1) * 4u : OOB_OFF);
     return (w >> ((cb & 1u) * 16u)) & 0xFFFFu;
   }
-  DBS_DEV void found(uint32_t rb, uint32_t f, int lane) const {
-    if (lane == 0) discover(*P, rb, f);
-  }
+  DBS_DEV void found(uint32_t rb, uint32_t f, int lane) const { claim_wave(*P, rb, f, lane); }
 };
 
 template <int VK>
@@ -213,7 +224,7 @@ __global__ __launch_bounds__(KT) void k_bfs_level(BfsParams P) {
     if constexpr (VK == VK_PAT) {
       const PatSrc S{P.t_cb, P.t_meta, P.segs, P.nseg,
                      make_rsrc(P.payload, (uint64_t)P.payload_bytes + DBS_PAYLOAD_SLACK)};
-      const BfsPol pol{&P, R.bm};
+      const BfsPol pol{&P, R.bm, make_rsrc(P.vis, (uint64_t)((P.nb + 1) / 2) * 4)};
       pattern_pull(S, pol, gw, nw, eager, lane, s_pat[w]);
     } else {
       for (int64_t s = gw * U; s < P.nseg; s += nw * U) bfs_pull_group<VK, U>(P, R, s, eager, lane);
@@ -236,13 +247,15 @@ __global__ __launch_bounds__(dbs_meta::MT) void k_bfs_meta(const uint32_t *bm, i
   });
 }
 
+// Rows without an entry start out visited: no level can reach them, and a
+// row block whose remaining rows are all such is skipped by the pull.
 __global__ void k_bfs_init(int32_t *levels, int32_t m, uint32_t *bm3, int64_t bm_words3, uint32_t *vis,
-                           int64_t nwords, uint32_t *ctr3, int32_t src) {
+                           const uint32_t *rows_nz, int64_t nwords, uint32_t *ctr3, int32_t src) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t gs = (int64_t)gridDim.x * blockDim.x;
   for (int64_t k = i; k < m; k += gs) levels[k] = k == src ? 0 : -1;
   for (int64_t k = i; k < bm_words3; k += gs) bm3[k] = 0;
-  for (int64_t k = i; k < nwords; k += gs) vis[k] = 0;
+  for (int64_t k = i; k < nwords; k += gs) vis[k] = ~rows_nz[k];
   if (i < 24) ctr3[i] = 0;
 }
 
@@ -250,7 +263,7 @@ __global__ void k_bfs_seed(uint32_t *bm0, uint32_t *vis, int32_t src) {
   const uint32_t b = (uint32_t)src >> 4, bit = 1u << ((uint32_t)src & 15u);
   const uint32_t sh = (b & 1u) * 16u;
   bm0[b >> 1] = bit << sh;
-  vis[b >> 1] = bit << sh;
+  vis[b >> 1] |= bit << sh;
 }
 
 }  // namespace
@@ -277,7 +290,7 @@ dbs_status dbs_bfs_impl(dbs_matrix *A, int32_t src, int32_t *levels, hipStream_t
   const bool timing = A->opt[DBS_OPT_TIMING] != 0;
   if (timing) BFS_TRY(hipEventRecord(A->ev[0], s));
   hipLaunchKernelGGL(k_bfs_init, dim3(1024), dim3(256), 0, s, levels, A->m, A->bfs_bm, 3 * nwords,
-                     A->bfs_vis, nwords, A->bfs_ctr, src);
+                     A->bfs_vis, (const uint32_t *)A->rows_nz, nwords, A->bfs_ctr, src);
   hipLaunchKernelGGL(k_bfs_seed, dim3(1), dim3(1), 0, s, A->bfs_bm, A->bfs_vis, src);
   BFS_TRY(hipGetLastError());
   const unsigned mgrid = dbs_meta::groups_for(A->nb, nwords);

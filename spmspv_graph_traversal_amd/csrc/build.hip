@@ -44,6 +44,19 @@ __global__ __launch_bounds__(BT) void k_validate(int32_t m, int32_t n, int64_t n
   if (f) atomicOr(flag, f);
 }
 
+// Rows that hold an entry, 16 bits per row block (two row blocks a word).
+// BFS starts with the empty rows marked visited: nothing can reach them.
+__global__ __launch_bounds__(BT) void k_rows_nz(int32_t m, int64_t words, const int32_t *row_ptr, uint32_t *out) {
+  const int64_t k = (int64_t)blockIdx.x * BT + threadIdx.x;
+  if (k >= words) return;
+  uint32_t w = 0;
+  for (int i = 0; i < 32; ++i) {
+    const int64_t r = k * 32 + i;
+    if (r < m && row_ptr[r + 1] > row_ptr[r]) w |= 1u << i;
+  }
+  out[k] = w;
+}
+
 // Per-lane row cursor of the merge.
 struct RowCursor {
   int64_t p, e;
@@ -404,6 +417,12 @@ dbs_status dbs_build_impl(dbs_matrix *A, const int32_t *row_ptr, const int32_t *
   BUILD_TRY(hipMemcpyAsync(&hflag, flag, 4, hipMemcpyDeviceToHost, s));
   BUILD_TRY(hipStreamSynchronize(s));
   if (hflag) return DBS_ERR_BAD_CSR;
+
+  // --- rows holding an entry
+  const int64_t rwords = ((int64_t)mb + 1) / 2;
+  BUILD_TRY(dbs_dev_alloc(A, (void **)&A->rows_nz, (size_t)rwords * 4));
+  hipLaunchKernelGGL(k_rows_nz, dim3(nblocks(rwords, BT)), dim3(BT), 0, s, m, rwords, row_ptr, A->rows_nz);
+  BUILD_TRY(hipGetLastError());
 
   // --- pass 1: tiles per row block, block-CSR row pointer
   uint32_t *rb_cnt;

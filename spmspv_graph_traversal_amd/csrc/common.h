@@ -124,6 +124,7 @@ struct dbs_matrix {
   uint64_t dense_mask_off;  // start of the Dense row-mask section in the arena
   uint32_t *segs;       // [4*nseg] pull segments
   int64_t payload_bytes;
+  uint32_t *rows_nz;    // [(mb+1)/2] rows holding an entry, 16 bits per row block
 
   // per-call scratch (device)
   uint32_t *xmask;       // [nb] (epoch << 16) | blk_x_mask

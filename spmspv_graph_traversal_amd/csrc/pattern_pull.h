@@ -51,10 +51,9 @@ DBS_DEV void pat_issue(const PatSrc &S, const Pol &pol, int64_t s0, bool live, u
 
 // Pattern matrices (the graph workloads), pull.  A wave takes one segment of
 // up to 64*K tiles per step (K slices of 64 consecutive tiles, lane i holding
-// tile 64k+i of slice k), software-pipelined: the next segment's descriptor
-// (scalar loads), column blocks and, when most vector blocks are active,
-// metadata are in flight while the current one waits for its masks and
-// words.  Column blocks and metadata come through a buffer range cut to the
+// tile 64k+i of slice k), software-pipelined: the next segment's column
+// blocks and, when most vector blocks are active, metadata are in flight
+// while the current one waits for its masks and words.  Column blocks and metadata come through a buffer range cut to the
 // segment, so lanes past its end read 0 without any address arithmetic.  COO
 // tiles of up to four entries are decoded from their metadata word; the
 // coordinate words of the other COO tiles are consecutive in the COO section,
@@ -66,9 +65,8 @@ DBS_DEV void pat_issue(const PatSrc &S, const Pol &pol, int64_t s0, bool live, u
 // grow with its tiles (descriptor, ballots, word setup, wave OR, writeback)
 // is what bounds this pull, hence segments of up to 256 tiles.
 template <int K>
-struct PatSeg {  // stage A: descriptor, column blocks, metadata
-  uint4 seg;
-  uint32_t n, need;
+struct PatSeg {  // stage A: descriptor, column blocks, metadata (n == 0: no segment)
+  uint32_t rb, t0, n, need;
   uint32_t cb[K];
   uint64_t meta[K];
 };
@@ -81,15 +79,57 @@ struct PatMasks {  // stage B: masks, and (EAGER) the first chunk of coordinate 
   uint32_t base, nwords, word;
 };
 
+// The descriptors of a wave's next 64 segments (lane j: segment next +
+// j*stride) with the rows still wanted in each, and the ballot of those with
+// work.  Read 64 at a time, a descriptor costs no round trip of its own, and
+// segments with nothing to do (all rows found) are skipped without a step.
+struct SegWin {
+  uint32_t rb, t0, t1, need;  // per lane
+  uint64_t live;              // lanes whose segment has tiles and wanted rows
+  int64_t next;               // first segment of the next window
+};
+
+template <class Pol>
+DBS_DEV void win_fill(const PatSrc &S, const Pol &pol, int64_t stride, int lane, SegWin &w) {
+  const int64_t s = w.next + (int64_t)lane * stride;
+  const bool in = s < S.nseg;
+  const uint4 d = ((const uint4 *)S.segs)[in ? s : 0];  // unconditional: no branch around the load
+  w.rb = d.x & ~SEG_SPLIT;
+  w.t0 = d.y;
+  w.t1 = d.z;
+  w.need = pol.need_v(w.rb, in);
+  w.live = __ballot(in & (w.need != 0u) & (d.z > d.y));
+  w.next += 64 * stride;
+}
+
+// next segment with work, false once the wave's share is done (uniform)
+template <class Pol>
+DBS_DEV bool win_next(const PatSrc &S, const Pol &pol, int64_t stride, int lane, SegWin &w, uint32_t &rb,
+                      uint32_t &t0, uint32_t &t1, uint32_t &need) {
+  while (w.live == 0ull) {
+    if (w.next >= S.nseg) return false;
+    win_fill(S, pol, stride, lane, w);
+  }
+  const int j = __ffsll((unsigned long long)w.live) - 1;
+  w.live &= w.live - 1ull;
+  rb = (uint32_t)__builtin_amdgcn_readlane((int)w.rb, j);
+  t0 = (uint32_t)__builtin_amdgcn_readlane((int)w.t0, j);
+  t1 = (uint32_t)__builtin_amdgcn_readlane((int)w.t1, j);
+  need = (uint32_t)__builtin_amdgcn_readlane((int)w.need, j);
+  return true;
+}
+
 template <int K, bool EAGER, class Pol>
-DBS_DEV void patk_issue(const PatSrc &S, const Pol &pol, int64_t s, bool live, uint32_t l4, uint32_t l8,
-                        PatSeg<K> &r) {
-  const cu32_t *q = (const cu32_t *)S.segs + 4 * s;
-  r.seg = make_uint4(q[0], q[1], q[2], 0u);
-  r.need = pol.need(r.seg.x & ~SEG_SPLIT);
-  r.n = (live & (s < S.nseg) & (r.need != 0u)) ? r.seg.z - r.seg.y : 0u;
-  const brsrc_t rcb = make_rsrc(S.t_cb + r.seg.y, (uint64_t)r.n * 4u);
-  const brsrc_t rmt = make_rsrc(S.t_meta + r.seg.y, (uint64_t)r.n * 8u);
+DBS_DEV void patk_issue(const PatSrc &S, const Pol &pol, int64_t stride, int lane, SegWin &w, uint32_t l4,
+                        uint32_t l8, PatSeg<K> &r) {
+  uint32_t rb = 0, t0 = 0, t1 = 0, need = 0;
+  const bool any = win_next(S, pol, stride, lane, w, rb, t0, t1, need);
+  r.rb = rb;
+  r.t0 = t0;
+  r.need = need;
+  r.n = any ? t1 - t0 : 0u;
+  const brsrc_t rcb = make_rsrc(S.t_cb + t0, (uint64_t)r.n * 4u);
+  const brsrc_t rmt = make_rsrc(S.t_meta + t0, (uint64_t)r.n * 8u);
 #pragma unroll
   for (int k = 0; k < K; ++k) {
     r.cb[k] = __builtin_amdgcn_raw_buffer_load_b32(rcb, l4 + 256u * k, 0, 0);
@@ -205,14 +245,15 @@ DBS_DEV void pat_finish(const PatSrc &S, const Pol &pol, const PatSeg<K> &a, con
     }
   }
   f = wave_or(f) & a.need;
-  if (f != 0u) pol.found(a.seg.x & ~SEG_SPLIT, f, lane);  // uniform
+  if (f != 0u) pol.found(a.rb, f, lane);  // uniform
 }
 
-// One wave's share: segments s0, s0 + stride, ...  Three steps are in flight:
-// while segment i is finished, segment i+1 has its masks (and, EAGER, its
-// coordinate words) and segment i+2 its descriptor, column blocks and
-// metadata in flight.  Loads are issued in that order, so a wait for segment
-// i's data never waits for the loads of the later segments.
+// One wave's share: segments s0, s0 + stride, ... that have work.  Three
+// steps are in flight: while segment i is finished, segment i+1 has its
+// masks (and, EAGER, its coordinate words) and segment i+2 its column blocks
+// and metadata in flight.  Loads are issued in that order, so a wait for
+// segment i's data never waits for the loads of the later segments (a new
+// window of descriptors, once per 64 segments, does wait).
 template <int K, bool EAGER, class Pol>
 DBS_DEV void pattern_pull_wave(const PatSrc &S, const Pol &pol, int64_t s0, int64_t stride, int lane,
                                uint32_t *s_mark, uint32_t *s_tm, uint32_t *s_te) {
@@ -223,26 +264,25 @@ DBS_DEV void pattern_pull_wave(const PatSrc &S, const Pol &pol, int64_t s0, int6
     for (int k = 0; k < K; ++k) b.m[k] = pol.mask(a.cb[k], 64u * k + (uint32_t)lane < a.n);
     if constexpr (EAGER) pat_words<K, true>(S, a, b, lane, l4);
   };
+  SegWin w;
+  w.next = s0;
+  w.live = 0ull;
   PatSeg<K> a0, a1, a2;
   PatMasks<K> b0, b1;
-  const int64_t s1 = s0 + stride;
-  patk_issue<K, EAGER>(S, pol, s0, true, l4, l8, a0);
-  patk_issue<K, EAGER>(S, pol, s1 < S.nseg ? s1 : s0, s1 < S.nseg, l4, l8, a1);
+  patk_issue<K, EAGER>(S, pol, stride, lane, w, l4, l8, a0);
+  patk_issue<K, EAGER>(S, pol, stride, lane, w, l4, l8, a1);
   masks(a0, b0);
-  while (true) {
+  while (a0.n != 0u) {
     if constexpr (!EAGER) {
-      // metadata of segment s0's active tiles, before the later loads
-      const brsrc_t rmt = make_rsrc(S.t_meta + a0.seg.y, (uint64_t)a0.n * 8u);
+      // metadata of segment i's active tiles, before the later loads
+      const brsrc_t rmt = make_rsrc(S.t_meta + a0.t0, (uint64_t)a0.n * 8u);
 #pragma unroll
       for (int k = 0; k < K; ++k) a0.meta[k] = bld64(rmt, b0.m[k] != 0u ? l8 + 512u * k : OOB_OFF);
     }
-    const int64_t sa = s0 + 2 * stride;
-    patk_issue<K, EAGER>(S, pol, sa < S.nseg ? sa : s0, sa < S.nseg, l4, l8, a2);
+    patk_issue<K, EAGER>(S, pol, stride, lane, w, l4, l8, a2);
     masks(a1, b1);
     if constexpr (!EAGER) pat_words<K, false>(S, a0, b0, lane, l4);
     pat_finish<K>(S, pol, a0, b0, lane, s_mark, s_tm, s_te);
-    s0 += stride;
-    if (s0 >= S.nseg) break;
     a0 = a1;
     a1 = a2;
     b0 = b1;

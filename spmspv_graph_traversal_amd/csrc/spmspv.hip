@@ -431,7 +431,7 @@ struct OrPol {
   uint32_t epoch;
   int32_t m;
   uint8_t *y;
-  DBS_DEV uint32_t need(uint32_t) const { return 0xFFFFu; }
+  DBS_DEV uint32_t need_v(uint32_t, bool) const { return 0xFFFFu; }
   DBS_DEV uint32_t mask(uint32_t cb, bool in) const {
     const uint32_t w = bld32(xmask, in ? cb * 4u : OOB_OFF);
     return ((w >> 16) == epoch) ? (w & 0xFFFFu) : 0u;  // an idle lane reads 0: no epoch
