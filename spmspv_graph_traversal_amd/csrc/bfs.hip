@@ -8,7 +8,11 @@
 //                chosen on the device from the frontier's nonzero-block count;
 //                rows found that were unvisited when the level started are
 //                claimed with non-returning atomic ORs on the next and
-//                visited bitmaps, and their level is stored;
+//                visited bitmaps, and their level is stored.  On a pattern
+//                matrix a pull level is two launches, the first segment of
+//                each row block and then the others, so that a long row
+//                block whose rows are all found by its first segment is not
+//                read further (the bottom-up early exit, per row block);
 //   k_bfs_meta   counts the nonzero blocks of the next bitmap, lists them
 //                (one atomic per workgroup), cuts them into push chunks when
 //                the next level pushes, and clears the bitmap two levels back.
@@ -35,7 +39,9 @@ struct BfsParams {
   const uint8_t *payload;
   uint64_t dense_mask_off;
   const uint32_t *segs;
-  int64_t nseg, T, payload_bytes;
+  const uint32_t *psegs;    // pattern matrices: Boolean-pull segments, the nseg0 of the first launch ahead
+  const uint32_t *rb_ptr;
+  int64_t nseg, npseg, nseg0, T, payload_bytes;
   int32_t m, nb;
   const uint32_t *cur_bm;   // frontier of this level
   uint32_t *next_bm;        // frontier of the next level (cleared)
@@ -45,6 +51,7 @@ struct BfsParams {
   uint32_t *hist;           // nonzero blocks of the current frontier, stored at [level % batch]
   int32_t *levels;
   int32_t level;            // level of the current frontier
+  int32_t phase;            // 0: push, or the first segment of each row block; 1: the other segments
   int32_t force_path;
   int64_t th3_num, th3_den;
 };
@@ -204,10 +211,12 @@ __global__ __launch_bounds__(KT) void k_bfs_level(BfsParams P) {
   const int lane = __lane_id();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / DBS_WAVE);
   const uint32_t nz = P.cur_ctr[0];
-  if (blockIdx.x == 0 && threadIdx.x == 0) P.hist[P.level % dbs_matrix::kBfsBatch] = nz;
+  if (P.phase == 0 && blockIdx.x == 0 && threadIdx.x == 0) P.hist[P.level % dbs_matrix::kBfsBatch] = nz;
   if (nz == 0u) return;  // uniform: empty frontier, nothing to find
   const bool push = P.force_path == 1 ||
                     (P.force_path == 0 && (int64_t)nz * P.th3_den < (int64_t)P.nb * P.th3_num);
+  // the second launch only pulls the remaining segments of a pattern matrix
+  if (P.phase != 0 && (push || VK != VK_PAT)) return;  // uniform
   const int64_t gw = (int64_t)blockIdx.x * (KT / DBS_WAVE) + w;
   const int64_t nw = (int64_t)gridDim.x * (KT / DBS_WAVE);
   if (push) {
@@ -222,8 +231,10 @@ __global__ __launch_bounds__(KT) void k_bfs_level(BfsParams P) {
     R.pay = make_rsrc(P.payload, (uint64_t)P.payload_bytes);
     R.bm = make_rsrc(P.cur_bm, (uint64_t)((P.nb + 1) / 2) * 4);
     if constexpr (VK == VK_PAT) {
-      const PatSrc S{P.t_cb, P.t_meta, P.segs, P.nseg,
-                     make_rsrc(P.payload, (uint64_t)P.payload_bytes + DBS_PAYLOAD_SLACK)};
+      const uint32_t *sg = P.phase == 0 ? P.psegs : P.psegs + 4 * P.nseg0;
+      const PatSrc S{P.t_cb, P.t_meta, sg, P.phase == 0 ? P.nseg0 : P.npseg - P.nseg0,
+                     make_rsrc(P.payload, (uint64_t)P.payload_bytes + DBS_PAYLOAD_SLACK),
+                     make_rsrc(P.rb_ptr, (uint64_t)(P.m + 15) / 16 * 4 + 4)};
       const BfsPol pol{&P, R.bm, make_rsrc(P.vis, (uint64_t)((P.nb + 1) / 2) * 4)};
       pattern_pull(S, pol, gw, nw, eager, lane, s_pat[w]);
     } else {
@@ -321,7 +332,11 @@ dbs_status dbs_bfs_impl(dbs_matrix *A, int32_t src, int32_t *levels, hipStream_t
   P.payload = A->payload;
   P.dense_mask_off = A->dense_mask_off;
   P.segs = A->segs;
+  P.psegs = A->psegs;
+  P.rb_ptr = A->rb_ptr;
   P.nseg = A->nseg;
+  P.npseg = A->npseg;
+  P.nseg0 = A->nseg0;
   P.T = A->T;
   P.payload_bytes = A->payload_bytes;
   P.m = A->m;
@@ -332,7 +347,8 @@ dbs_status dbs_bfs_impl(dbs_matrix *A, int32_t src, int32_t *levels, hipStream_t
   P.th3_num = A->opt[DBS_OPT_TH3_NUM];
   P.th3_den = A->opt[DBS_OPT_TH3_DEN];
   const int pu = A->vk == VK_PAT ? 1 : 8;
-  int64_t waves = (A->nseg + pu - 1) / pu > chunk_cap ? (A->nseg + pu - 1) / pu : chunk_cap;
+  const int64_t ns = A->vk == VK_PAT ? A->npseg : A->nseg;
+  int64_t waves = (ns + pu - 1) / pu > chunk_cap ? (ns + pu - 1) / pu : chunk_cap;
   int64_t g = (waves + 3) / 4;
   static const unsigned res_f32 = dbs_resident_groups(k_bfs_level<VK_F32>, KT);
   static const unsigned res_bf16 = dbs_resident_groups(k_bfs_level<VK_BF16>, KT);
@@ -356,9 +372,21 @@ dbs_status dbs_bfs_impl(dbs_matrix *A, int32_t src, int32_t *levels, hipStream_t
       P.cur_chunks = A->bfs_chunks + cur * chunk_cap;
       P.level = (int32_t)l;
       if (timing) BFS_TRY(hipEventRecord(A->ev[2 + 2 * i], s));
-      if (A->vk == VK_F32) hipLaunchKernelGGL(k_bfs_level<VK_F32>, dim3(grid), dim3(KT), 0, s, P);
-      else if (A->vk == VK_BF16) hipLaunchKernelGGL(k_bfs_level<VK_BF16>, dim3(grid), dim3(KT), 0, s, P);
-      else hipLaunchKernelGGL(k_bfs_level<VK_PAT>, dim3(grid), dim3(KT), 0, s, P);
+      if (A->vk == VK_F32) {
+        P.phase = 0;
+        hipLaunchKernelGGL(k_bfs_level<VK_F32>, dim3(grid), dim3(KT), 0, s, P);
+      } else if (A->vk == VK_BF16) {
+        P.phase = 0;
+        hipLaunchKernelGGL(k_bfs_level<VK_BF16>, dim3(grid), dim3(KT), 0, s, P);
+      } else {
+        // a pull level in two launches: the first segment of every row block,
+        // then the rest, which skips row blocks with nothing left to find
+        P.phase = 0;
+        hipLaunchKernelGGL(k_bfs_level<VK_PAT>, dim3(grid), dim3(KT), 0, s, P);
+        BFS_TRY(hipGetLastError());
+        P.phase = 1;
+        hipLaunchKernelGGL(k_bfs_level<VK_PAT>, dim3(grid), dim3(KT), 0, s, P);
+      }
       BFS_TRY(hipGetLastError());
       if (timing) BFS_TRY(hipEventRecord(A->ev[3 + 2 * i], s));
       hipLaunchKernelGGL(k_bfs_meta, dim3(mgrid), dim3(dbs_meta::MT), 0, s, (const uint32_t *)P.next_bm, A->nb,

@@ -11,6 +11,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <vector>
+
 #include "common.h"
 
 namespace {
@@ -359,6 +361,68 @@ __global__ void k_type_stats(const uint32_t *t_nt, int64_t T, unsigned long long
 
 inline unsigned nblocks(int64_t n, int b) { return (unsigned)((n + b - 1) / b); }
 
+// Segments of the Boolean pull (pattern matrices), in the order it runs
+// them: first, one segment per run of consecutive short row blocks (a
+// single segment each above; at most PAT_MAX_RB row blocks and seg_cap tiles
+// per run) and the first segment of every long row block; then the other
+// segments of the long row blocks.  A BFS pull level runs the two parts as
+// two launches: most rows of a long row block are found by its first
+// segment, and the second launch skips the row blocks with nothing left to
+// find.  Packing short row blocks keeps a wave's 256 lanes busy, and the
+// pull's cost per segment is what bounds it.  Built on the host: one
+// sequential pass over the row blocks.
+hipError_t build_pull_order(dbs_matrix *A, const uint32_t *seg_cnt, hipStream_t s) {
+  const int32_t mb = A->mb;
+  const int64_t nseg = A->nseg;
+  std::vector<uint32_t> cnt(mb), rbp(mb + 1), sg(4 * (size_t)nseg);
+  hipError_t e = hipMemcpyAsync(cnt.data(), seg_cnt, (size_t)mb * 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(rbp.data(), A->rb_ptr, (size_t)(mb + 1) * 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess && nseg > 0) e = hipMemcpyAsync(sg.data(), A->segs, (size_t)nseg * 16, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return e;
+  const uint32_t cap = (uint32_t)A->bopt.seg_cap;
+  std::vector<uint32_t> first, rest;
+  first.reserve(4 * (size_t)mb);
+  rest.reserve(4 * (size_t)nseg);
+  auto put = [](std::vector<uint32_t> &v, uint32_t rb, uint32_t t0, uint32_t t1, uint32_t nrb) {
+    v.push_back(rb);
+    v.push_back(t0);
+    v.push_back(t1);
+    v.push_back(nrb);
+  };
+  int64_t run = -1;  // first row block of the open run of short row blocks
+  auto close_run = [&](int32_t end_rb) {  // the run covers row blocks [run, end_rb]
+    if (run >= 0) put(first, (uint32_t)run, rbp[run], rbp[end_rb + 1], (uint32_t)(end_rb - run + 1));
+    run = -1;
+  };
+  int32_t last_short = -1;
+  uint64_t o = 0;  // first segment of the row block in sg
+  for (int32_t rb = 0; rb < mb; ++rb) {
+    const uint32_t c = cnt[rb];
+    if (c == 1u) {
+      if (run >= 0 && (rbp[rb + 1] - rbp[run] > cap || rb - run + 1 > DBS_PAT_MAX_RB)) close_run(last_short);
+      if (run < 0) run = rb;
+      last_short = rb;
+    } else if (c > 1u) {
+      close_run(last_short);
+      for (uint32_t j = 0; j < c; ++j) {
+        const uint32_t *d = &sg[4 * (o + j)];
+        put(j == 0 ? first : rest, d[0] & ~SEG_SPLIT, d[1], d[2], 1u);
+      }
+    }
+    o += c;
+  }
+  close_run(last_short);
+  A->nseg0 = (int64_t)first.size() / 4;
+  A->npseg = A->nseg0 + (int64_t)rest.size() / 4;
+  first.insert(first.end(), rest.begin(), rest.end());
+  first.resize(first.size() + 4 * 16, 0u);  // 16 zeroed descriptors of padding
+  e = dbs_dev_alloc(A, (void **)&A->psegs, first.size() * 4);
+  if (e == hipSuccess) e = hipMemcpyAsync(A->psegs, first.data(), first.size() * 4, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  return e;
+}
+
 int bits_for(uint32_t maxval) {
   int b = 0;
   while (b < 32 && (maxval >> b) != 0) ++b;
@@ -529,6 +593,7 @@ dbs_status dbs_build_impl(dbs_matrix *A, const int32_t *row_ptr, const int32_t *
   hipLaunchKernelGGL(k_segments, dim3(nblocks(mb, BT)), dim3(BT), 0, s, mb, (const uint32_t *)A->rb_ptr,
                      (const uint32_t *)t_nt, A->bopt, seg_cnt, (const uint32_t *)seg_off, A->segs, 1);
   BUILD_TRY(hipGetLastError());
+  if (vk == VK_PAT) BUILD_TRY(build_pull_order(A, seg_cnt, s));
 
   // --- statistics per format
   unsigned long long *st;

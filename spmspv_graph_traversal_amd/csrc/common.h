@@ -101,6 +101,8 @@ __host__ __device__ inline uint32_t tile_payload_bytes(int type, uint32_t nnz, i
 // tiles per pull segment at most, pattern matrices (the Boolean pull's wave
 // holds four tiles per lane)
 #define DBS_PAT_SEG_CAP 256
+// row blocks per Boolean-pull segment at most (runs of short row blocks)
+#define DBS_PAT_MAX_RB 16
 
 // ---------------------------------------------------------------------------
 // The handle.
@@ -109,6 +111,7 @@ struct dbs_matrix {
   int device;
   int32_t m, n, mb, nb;
   int64_t nnz, T, nseg;
+  int64_t npseg, nseg0;  // pattern matrices: Boolean-pull segments, and those of the first launch
   dbs_dtype dtype;
   int vk;
   dbs_build_options bopt;
@@ -123,6 +126,8 @@ struct dbs_matrix {
   uint8_t *payload;     // arena
   uint64_t dense_mask_off;  // start of the Dense row-mask section in the arena
   uint32_t *segs;       // [4*nseg] pull segments
+  uint32_t *psegs;      // [4*npseg] pattern matrices: Boolean-pull segments (first row block, first
+                        // tile, end tile, row blocks), first-launch ones ahead
   int64_t payload_bytes;
   uint32_t *rows_nz;    // [(mb+1)/2] rows holding an entry, 16 bits per row block
 

@@ -16,6 +16,7 @@ struct PatSrc {
   const uint32_t *segs;  // padded with 16 zeroed descriptors
   int64_t nseg;
   brsrc_t pay;  // payload and its zeroed slack
+  brsrc_t rbp;  // block-CSR row pointer (the row blocks of a segment that holds several)
 };
 
 template <int U>
@@ -66,7 +67,8 @@ DBS_DEV void pat_issue(const PatSrc &S, const Pol &pol, int64_t s0, bool live, u
 // is what bounds this pull, hence segments of up to 256 tiles.
 template <int K>
 struct PatSeg {  // stage A: descriptor, column blocks, metadata (n == 0: no segment)
-  uint32_t rb, t0, n, need;
+  uint32_t rb, t0, n, nrb;  // first row block, first tile, tiles, row blocks (uniform)
+  uint32_t needl, bnd;      // lane j < nrb: rows wanted in row block rb + j, and its first tile
   uint32_t cb[K];
   uint64_t meta[K];
 };
@@ -80,13 +82,17 @@ struct PatMasks {  // stage B: masks, and (EAGER) the first chunk of coordinate 
 };
 
 // The descriptors of a wave's next 64 segments (lane j: segment next +
-// j*stride) with the rows still wanted in each, and the ballot of those with
-// work.  Read 64 at a time, a descriptor costs no round trip of its own, and
-// segments with nothing to do (all rows found) are skipped without a step.
+// j*stride) and the ballot of those with wanted rows.  Read 64 at a time, a
+// descriptor costs no round trip of its own, and segments with nothing to do
+// (all rows found) are skipped without a step.  A descriptor is (first row
+// block, first tile, end tile, row blocks): several consecutive short row
+// blocks may share one segment (at most PAT_MAX_RB).
+constexpr int PAT_MAX_RB = DBS_PAT_MAX_RB;
+
 struct SegWin {
-  uint32_t rb, t0, t1, need;  // per lane
-  uint64_t live;              // lanes whose segment has tiles and wanted rows
-  int64_t next;               // first segment of the next window
+  uint32_t rb, t0, t1, nrb;  // per lane
+  uint64_t live;             // lanes whose segment has tiles and wanted rows
+  int64_t next;              // first segment of the next window
 };
 
 template <class Pol>
@@ -97,15 +103,21 @@ DBS_DEV void win_fill(const PatSrc &S, const Pol &pol, int64_t stride, int lane,
   w.rb = d.x & ~SEG_SPLIT;
   w.t0 = d.y;
   w.t1 = d.z;
-  w.need = pol.need_v(w.rb, in);
-  w.live = __ballot(in & (w.need != 0u) & (d.z > d.y));
+  w.nrb = d.w > 1u ? d.w : 1u;
+  uint32_t need = 0u;
+#pragma unroll
+  for (int j = 0; j < PAT_MAX_RB; ++j) {
+    const bool jin = (uint32_t)j < w.nrb;
+    need |= pol.need_v(w.rb + j, in & jin) & (0u - (uint32_t)jin);
+  }
+  w.live = __ballot(in & (need != 0u) & (d.z > d.y));
   w.next += 64 * stride;
 }
 
 // next segment with work, false once the wave's share is done (uniform)
 template <class Pol>
 DBS_DEV bool win_next(const PatSrc &S, const Pol &pol, int64_t stride, int lane, SegWin &w, uint32_t &rb,
-                      uint32_t &t0, uint32_t &t1, uint32_t &need) {
+                      uint32_t &t0, uint32_t &t1, uint32_t &nrb) {
   while (w.live == 0ull) {
     if (w.next >= S.nseg) return false;
     win_fill(S, pol, stride, lane, w);
@@ -115,18 +127,18 @@ DBS_DEV bool win_next(const PatSrc &S, const Pol &pol, int64_t stride, int lane,
   rb = (uint32_t)__builtin_amdgcn_readlane((int)w.rb, j);
   t0 = (uint32_t)__builtin_amdgcn_readlane((int)w.t0, j);
   t1 = (uint32_t)__builtin_amdgcn_readlane((int)w.t1, j);
-  need = (uint32_t)__builtin_amdgcn_readlane((int)w.need, j);
+  nrb = (uint32_t)__builtin_amdgcn_readlane((int)w.nrb, j);
   return true;
 }
 
 template <int K, bool EAGER, class Pol>
 DBS_DEV void patk_issue(const PatSrc &S, const Pol &pol, int64_t stride, int lane, SegWin &w, uint32_t l4,
                         uint32_t l8, PatSeg<K> &r) {
-  uint32_t rb = 0, t0 = 0, t1 = 0, need = 0;
-  const bool any = win_next(S, pol, stride, lane, w, rb, t0, t1, need);
+  uint32_t rb = 0, t0 = 0, t1 = 0, nrb = 1;
+  const bool any = win_next(S, pol, stride, lane, w, rb, t0, t1, nrb);
   r.rb = rb;
   r.t0 = t0;
-  r.need = need;
+  r.nrb = nrb;
   r.n = any ? t1 - t0 : 0u;
   const brsrc_t rcb = make_rsrc(S.t_cb + t0, (uint64_t)r.n * 4u);
   const brsrc_t rmt = make_rsrc(S.t_meta + t0, (uint64_t)r.n * 8u);
@@ -136,6 +148,9 @@ DBS_DEV void patk_issue(const PatSrc &S, const Pol &pol, int64_t stride, int lan
     if constexpr (EAGER) r.meta[k] = bld64(rmt, l8 + 512u * k);
     else r.meta[k] = 0ull;
   }
+  const bool mine = any & ((uint32_t)lane < nrb);
+  r.needl = pol.need_v(rb + (uint32_t)lane, mine);
+  r.bnd = bld32(S.rbp, (mine & (lane > 0)) ? (rb + (uint32_t)lane) * 4u : OOB_OFF);
 }
 
 // lane l's value of slice k (both wave-uniform), read from every slice so
@@ -181,27 +196,50 @@ DBS_DEV void pat_words(const PatSrc &S, const PatSeg<K> &a, PatMasks<K> &b, int 
   b.word = bld32(S.pay, (uint32_t)lane < b.nwords ? b.base + l4 : OOB_OFF);
 }
 
-// everything of one segment once its loads have arrived
-template <int K, class Pol>
+// everything of one segment once its loads have arrived.  MULTI: the
+// segment holds several row blocks; each found row goes to its row block
+// through an LDS OR (s_f, one word per row block), the row block of a tile
+// being the number of row-block starts up to it.
+template <int K, bool MULTI, class Pol>
 DBS_DEV void pat_finish(const PatSrc &S, const Pol &pol, const PatSeg<K> &a, const PatMasks<K> &b, int lane,
-                        uint32_t *s_mark, uint32_t *s_tm, uint32_t *s_te) {
+                        uint32_t *s_mark, uint32_t *s_tm, uint32_t *s_te, uint32_t *s_f) {
   const uint32_t n = a.n;  // uniform
   uint32_t f = 0u;
+  uint32_t ri[K];  // MULTI: row block (0 .. nrb-1) of this lane's tile in each slice
+#pragma unroll
+  for (int k = 0; k < K; ++k) ri[k] = 0u;
+  if constexpr (MULTI) {
+    if (lane < PAT_MAX_RB) s_f[lane] = 0u;
+    for (uint32_t j = 1; j < a.nrb; ++j) {  // uniform
+      const uint32_t st = (uint32_t)__builtin_amdgcn_readlane((int)a.bnd, (int)j) - a.t0;
+#pragma unroll
+      for (int k = 0; k < K; ++k) ri[k] += (64u * k + (uint32_t)lane >= st) ? 1u : 0u;
+    }
+    __syncwarp();
+  }
+  auto add = [&](int k, uint32_t x) {
+    if constexpr (MULTI) {
+      if (x) atomicOr(&s_f[ri[k]], x);
+    } else {
+      f |= x;
+    }
+  };
 #pragma unroll
   for (int k = 0; k < K; ++k) {
     if (64u * k >= n) break;  // uniform
     const uint64_t meta = a.meta[k];
     // COO tiles with at most four entries: the coordinates are in the metadata word
-    f |= ((b.m[k] != 0u) & (meta_type(meta) == DBS_TILE_COO) & meta_inline(meta)) ? coo_or4((uint32_t)meta, b.m[k])
-                                                                                    : 0u;
+    add(k, ((b.m[k] != 0u) & (meta_type(meta) == DBS_TILE_COO) & meta_inline(meta)) ? coo_or4((uint32_t)meta, b.m[k])
+                                                                                      : 0u);
   }
   if (b.tl >= 0) {
-    // per-tile mask and word end of this segment, for the word owners
+    // per-tile mask, word end (and, MULTI, row block) of this segment, for the word owners
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       if (64u * k >= n) break;  // uniform
       s_tm[64 * k + lane] = b.m[k];
-      s_te[64 * k + lane] = ((uint32_t)meta_vp(a.meta[k]) + coo_val_off(meta_nnz(a.meta[k])) - b.base) >> 2;
+      s_te[64 * k + lane] =
+          (((uint32_t)meta_vp(a.meta[k]) + coo_val_off(meta_nnz(a.meta[k])) - b.base) >> 2) | (ri[k] << 24);
     }
     uint32_t carry = 0u;
     for (uint32_t j0 = 0; j0 < b.nwords; j0 += 64u) {
@@ -221,10 +259,16 @@ DBS_DEV void pat_finish(const PatSrc &S, const Pol &pol, const PatSeg<K> &a, con
       own = own > carry ? own : carry;
       carry = (uint32_t)__builtin_amdgcn_readlane((int)own, 63);  // owner of the next chunk's first word
       const uint32_t t = own ? own - 1u : 0u;
-      const uint32_t mw = s_tm[t], oend = s_te[t];
+      const uint32_t mw = s_tm[t], te = s_te[t];
+      const uint32_t oend = te & 0xFFFFFFu;
       const uint32_t j = j0 + (uint32_t)lane;
       const uint32_t wd = j0 == 0u ? b.word : bld32(S.pay, j < b.nwords ? b.base + 4u * j : OOB_OFF);
-      f |= ((j < b.nwords) & (j < oend)) ? coo_or4(wd, mw) : 0u;
+      const uint32_t x = ((j < b.nwords) & (j < oend)) ? coo_or4(wd, mw) : 0u;
+      if constexpr (MULTI) {
+        if (x) atomicOr(&s_f[te >> 24], x);
+      } else {
+        f |= x;
+      }
     }
     __syncwarp();
   }
@@ -241,11 +285,21 @@ DBS_DEV void pat_finish(const PatSrc &S, const Pol &pol, const PatSeg<K> &a, con
       uint32_t g = 0;
 #pragma unroll
       for (int r = 0; r < 16; ++r) g |= (((rm[r >> 1] >> (16 * (r & 1))) & b.m[k]) != 0u) ? (1u << r) : 0u;
-      f |= g;
+      add(k, g);
     }
   }
-  f = wave_or(f) & a.need;
-  if (f != 0u) pol.found(a.rb, f, lane);  // uniform
+  if constexpr (MULTI) {
+    __syncwarp();
+    const uint32_t fl = ((uint32_t)lane < a.nrb) ? s_f[lane] & a.needl : 0u;
+    __syncwarp();
+    for (uint64_t any = __ballot(fl != 0u); any; any &= any - 1ull) {  // uniform
+      const int r = __ffsll((unsigned long long)any) - 1;
+      pol.found(a.rb + (uint32_t)r, (uint32_t)__builtin_amdgcn_readlane((int)fl, r), lane);
+    }
+  } else {
+    f = wave_or(f) & (uint32_t)__builtin_amdgcn_readlane((int)a.needl, 0);
+    if (f != 0u) pol.found(a.rb, f, lane);  // uniform
+  }
 }
 
 // One wave's share: segments s0, s0 + stride, ... that have work.  Three
@@ -256,7 +310,7 @@ DBS_DEV void pat_finish(const PatSrc &S, const Pol &pol, const PatSeg<K> &a, con
 // window of descriptors, once per 64 segments, does wait).
 template <int K, bool EAGER, class Pol>
 DBS_DEV void pattern_pull_wave(const PatSrc &S, const Pol &pol, int64_t s0, int64_t stride, int lane,
-                               uint32_t *s_mark, uint32_t *s_tm, uint32_t *s_te) {
+                               uint32_t *s_mark, uint32_t *s_tm, uint32_t *s_te, uint32_t *s_f) {
   if (s0 >= S.nseg) return;
   const uint32_t l4 = (uint32_t)lane * 4u, l8 = (uint32_t)lane * 8u;
   auto masks = [&](const PatSeg<K> &a, PatMasks<K> &b) {
@@ -282,7 +336,8 @@ DBS_DEV void pattern_pull_wave(const PatSrc &S, const Pol &pol, int64_t s0, int6
     patk_issue<K, EAGER>(S, pol, stride, lane, w, l4, l8, a2);
     masks(a1, b1);
     if constexpr (!EAGER) pat_words<K, false>(S, a0, b0, lane, l4);
-    pat_finish<K>(S, pol, a0, b0, lane, s_mark, s_tm, s_te);
+    if (a0.nrb > 1u) pat_finish<K, true>(S, pol, a0, b0, lane, s_mark, s_tm, s_te, s_f);  // uniform
+    else pat_finish<K, false>(S, pol, a0, b0, lane, s_mark, s_tm, s_te, s_f);
     a0 = a1;
     a1 = a2;
     b0 = b1;
@@ -291,13 +346,14 @@ DBS_DEV void pattern_pull_wave(const PatSrc &S, const Pol &pol, int64_t s0, int6
 
 constexpr int PAT_K = DBS_PAT_SEG_CAP / 64;  // slices of 64 tiles per pattern-pull segment
 
-// LDS per wave: marks (64), masks and word ends of a segment's tiles (2 x 64*K)
-constexpr int PAT_LDS_WORDS = 64 + 2 * 64 * PAT_K;
+// LDS per wave: marks (64), masks and word ends of a segment's tiles (2 x
+// 64*K), found rows per row block
+constexpr int PAT_LDS_WORDS = 64 + 2 * 64 * PAT_K + PAT_MAX_RB;
 
 template <class Pol>
 DBS_DEV void pattern_pull(const PatSrc &S, const Pol &pol, int64_t s0, int64_t stride, bool eager, int lane,
                           uint32_t *s_lds) {
-  uint32_t *s_mark = s_lds, *s_tm = s_lds + 64, *s_te = s_lds + 64 + 64 * PAT_K;
-  if (eager) pattern_pull_wave<PAT_K, true>(S, pol, s0, stride, lane, s_mark, s_tm, s_te);
-  else pattern_pull_wave<PAT_K, false>(S, pol, s0, stride, lane, s_mark, s_tm, s_te);
+  uint32_t *s_mark = s_lds, *s_tm = s_lds + 64, *s_te = s_lds + 64 + 64 * PAT_K, *s_f = s_te + 64 * PAT_K;
+  if (eager) pattern_pull_wave<PAT_K, true>(S, pol, s0, stride, lane, s_mark, s_tm, s_te, s_f);
+  else pattern_pull_wave<PAT_K, false>(S, pol, s0, stride, lane, s_mark, s_tm, s_te, s_f);
 }

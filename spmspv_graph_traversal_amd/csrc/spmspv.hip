@@ -119,7 +119,8 @@ struct SpmvParams {
   const uint32_t *csc2csr;
   const uint8_t *payload;
   uint64_t dense_mask_off;
-  const uint32_t *segs;
+  const uint32_t *segs;     // pull segments (pattern matrices: the Boolean pull's)
+  const uint32_t *rb_ptr;
   int64_t nseg, T, payload_bytes;
   int32_t m, nb;
   const uint32_t *xmask;
@@ -397,7 +398,7 @@ template <int VK, int U>
 DBS_DEV void plus_pull(const SpmvParams &P, int64_t gw, int64_t nw, bool eager, float *sx, float *spart,
                        uint32_t *s_mark, int lane) {
   const PatSrc S{P.t_cb, P.t_meta, P.segs, P.nseg,
-                 make_rsrc(P.payload, (uint64_t)P.payload_bytes + DBS_PAYLOAD_SLACK)};
+                 make_rsrc(P.payload, (uint64_t)P.payload_bytes + DBS_PAYLOAD_SLACK), make_rsrc(P.rb_ptr, 0)};
   const brsrc_t xm = make_rsrc(P.xmask, (uint64_t)P.nb * 4);
   if (eager) plus_pull_wave<VK, U, true>(P, S, xm, gw * U, nw * U, sx, spart, s_mark, lane);
   else plus_pull_wave<VK, U, false>(P, S, xm, gw * U, nw * U, sx, spart, s_mark, lane);
@@ -523,7 +524,7 @@ __global__ __launch_bounds__(KT) void k_spmspv(SpmvParams P) {
       R.pay = make_rsrc(P.payload, (uint64_t)P.payload_bytes + DBS_PAYLOAD_SLACK);
       R.xmask = make_rsrc(P.xmask, (uint64_t)P.nb * 4);
       if constexpr (VK == VK_PAT) {
-        const PatSrc S{P.t_cb, P.t_meta, P.segs, P.nseg, R.pay};
+        const PatSrc S{P.t_cb, P.t_meta, P.segs, P.nseg, R.pay, make_rsrc(P.rb_ptr, (uint64_t)(P.m + 15) / 16 * 4 + 4)};
         const OrPol pol{R.xmask, P.epoch, P.m, (uint8_t *)P.y};
         pattern_pull(S, pol, gw, nw, eager, lane, s_pat[w]);
       } else {
@@ -632,8 +633,9 @@ dbs_status dbs_spmspv_impl(dbs_matrix *A, int32_t nnz_x, const int32_t *x_idx, c
   P.csc2csr = A->csc2csr;
   P.payload = A->payload;
   P.dense_mask_off = A->dense_mask_off;
-  P.segs = A->segs;
-  P.nseg = A->nseg;
+  P.segs = A->vk == VK_PAT ? A->psegs : A->segs;
+  P.nseg = A->vk == VK_PAT ? A->npseg : A->nseg;
+  P.rb_ptr = A->rb_ptr;
   P.m = A->m;
   P.nb = A->nb;
   P.xmask = A->xmask;
@@ -659,7 +661,7 @@ dbs_status dbs_spmspv_impl(dbs_matrix *A, int32_t nnz_x, const int32_t *x_idx, c
   }();
   P.plus_u = A->nseg >= (int64_t)PULL_U_PLUS_WIDE * 32 * cus * 4 ? PULL_U_PLUS_WIDE : 1;
   const int pu = sr == DBS_PLUS_TIMES ? P.plus_u : A->vk == VK_PAT ? 1 : PULL_U_OR;
-  const int64_t pull_waves = (A->nseg + pu - 1) / pu;
+  const int64_t pull_waves = (P.nseg + pu - 1) / pu;
   const int64_t waves = pull_waves > A->max_chunks ? pull_waves : A->max_chunks;
   const int vk = A->vk;
   if (sr == DBS_OR_AND) {

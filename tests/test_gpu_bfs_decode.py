@@ -70,6 +70,32 @@ def test_bfs_directed_follows_y_equals_Ax(dbs):
             np.testing.assert_array_equal(gpu_bfs(dbs, A, n, src), orc.bfs(n, cp, ri, src))
 
 
+def test_bfs_directed_pattern_long_rows(dbs):
+    # a directed pattern matrix whose row blocks span many pull segments (a
+    # pull level reads each row block's first segment in one launch and the
+    # rest in another), with rows that hold no entry and columns that do
+    rng = rng_for("test", 811)
+    n = 8192
+    deg = np.where(rng.random(n) < 0.02, rng.integers(1000, 4000, n), rng.integers(0, 6, n))
+    deg[rng.random(n) < 0.2] = 0
+    rows = []
+    for r in range(n):
+        rows.append(np.unique(rng.integers(0, n, deg[r])))
+    rp = np.zeros(n + 1, np.int64)
+    rp[1:] = np.cumsum([len(x) for x in rows])
+    ci = np.concatenate(rows).astype(np.int32)
+    rp = rp.astype(np.int32)
+    cp, ri, _ = orc.csr_to_csc(n, n, rp, ci)
+    A = build(dbs, n, n, rp, ci, None, dbs.DBS_PATTERN)
+    st = dbs.dbs_get_stats(A)
+    assert st["segments"] > n // 16  # some row blocks are split
+    for src in (0, 1, 4097, n - 1):
+        ref = orc.bfs(n, cp, ri, src)
+        for path in (0, 1, 2):
+            dbs.dbs_set_option(A, dbs.DBS_OPT_PATH, path)
+            np.testing.assert_array_equal(gpu_bfs(dbs, A, n, src), ref, err_msg=f"src {src} path {path}")
+
+
 def test_bfs_mixed_formats_value_matrix(dbs):
     a = mixed_tile_dense(6, mb=8, nb=8, ragged=(0, 0))
     a = ((a != 0) | (a.T != 0)).astype(np.float32)
