@@ -41,6 +41,7 @@ struct BfsParams {
   const uint32_t *segs;
   const uint32_t *psegs;    // pattern matrices: Boolean-pull segments, the nseg0 of the first launch ahead
   const uint32_t *rb_ptr;
+  const uint8_t *wown;      // pattern matrices: owner tile of each payload word
   int64_t nseg, npseg, nseg0, T, payload_bytes;
   int32_t m, nb;
   const uint32_t *cur_bm;   // frontier of this level
@@ -202,7 +203,17 @@ struct BfsPol {
     const uint32_t w = bld32(bm, in ? (cb >> 1) * 4u : OOB_OFF);
     return (w >> ((cb & 1u) * 16u)) & 0xFFFFu;
   }
-  DBS_DEV void found(uint32_t rb, uint32_t f, int lane) const { claim_wave(*P, rb, f, lane); }
+  // rows found in n row blocks (LDS): lane j claims row block j, then the
+  // levels are stored four row blocks per pass, a lane per row
+  DBS_DEV void flush(const uint32_t *frb, const uint32_t *ff, int n, int lane) const {
+    if (lane < n) claim(*P, frb[lane], ff[lane]);
+    for (int e0 = 0; e0 < n; e0 += 4) {
+      const int e = e0 + (lane >> 4), r = lane & 15;
+      const bool in = e < n;
+      const uint32_t rb = frb[in ? e : 0], f = in ? ff[e] : 0u;
+      if ((f >> r) & 1u) P->levels[rb * 16u + (uint32_t)r] = P->level + 1;
+    }
+  }
 };
 
 template <int VK>
@@ -234,7 +245,8 @@ __global__ __launch_bounds__(KT) void k_bfs_level(BfsParams P) {
       const uint32_t *sg = P.phase == 0 ? P.psegs : P.psegs + 4 * P.nseg0;
       const PatSrc S{P.t_cb, P.t_meta, sg, P.phase == 0 ? P.nseg0 : P.npseg - P.nseg0,
                      make_rsrc(P.payload, (uint64_t)P.payload_bytes + DBS_PAYLOAD_SLACK),
-                     make_rsrc(P.rb_ptr, (uint64_t)(P.m + 15) / 16 * 4 + 4)};
+                     make_rsrc(P.rb_ptr, (uint64_t)(P.m + 15) / 16 * 4 + 4),
+                     make_rsrc(P.wown, (uint64_t)(P.payload_bytes + DBS_PAYLOAD_SLACK) / 4)};
       const BfsPol pol{&P, R.bm, make_rsrc(P.vis, (uint64_t)((P.nb + 1) / 2) * 4)};
       pattern_pull(S, pol, gw, nw, eager, lane, s_pat[w]);
     } else {
@@ -334,6 +346,7 @@ dbs_status dbs_bfs_impl(dbs_matrix *A, int32_t src, int32_t *levels, hipStream_t
   P.segs = A->segs;
   P.psegs = A->psegs;
   P.rb_ptr = A->rb_ptr;
+  P.wown = A->wown;
   P.nseg = A->nseg;
   P.npseg = A->npseg;
   P.nseg0 = A->nseg0;

@@ -361,6 +361,22 @@ __global__ void k_type_stats(const uint32_t *t_nt, int64_t T, unsigned long long
 
 inline unsigned nblocks(int64_t n, int b) { return (unsigned)((n + b - 1) / b); }
 
+// Owner of every coordinate word of a pattern COO tile held in the payload:
+// the tile's index in its Boolean-pull segment (< 256).  The pull spreads a
+// segment's words over the lanes; with the owner stored, a lane finds the
+// mask of its word's tile with one LDS read.  One thread per segment.
+__global__ void k_word_owner(const uint32_t *psegs, int64_t npseg, const uint64_t *t_meta, uint8_t *wown) {
+  const int64_t sg = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (sg >= npseg) return;
+  const uint32_t t0 = psegs[4 * sg + 1], t1 = psegs[4 * sg + 2];
+  for (uint32_t t = t0; t < t1; ++t) {
+    const uint64_t meta = t_meta[t];
+    if (meta_type(meta) != DBS_TILE_COO || meta_inline(meta)) continue;
+    const uint64_t w0 = meta_vp(meta) / 4, nw = (meta_nnz(meta) + 3u) / 4u;
+    for (uint64_t w = 0; w < nw; ++w) wown[w0 + w] = (uint8_t)(t - t0);
+  }
+}
+
 // Segments of the Boolean pull (pattern matrices), in the order it runs
 // them: first, one segment per run of consecutive short row blocks (a
 // single segment each above; at most PAT_MAX_RB row blocks and seg_cap tiles
@@ -593,7 +609,17 @@ dbs_status dbs_build_impl(dbs_matrix *A, const int32_t *row_ptr, const int32_t *
   hipLaunchKernelGGL(k_segments, dim3(nblocks(mb, BT)), dim3(BT), 0, s, mb, (const uint32_t *)A->rb_ptr,
                      (const uint32_t *)t_nt, A->bopt, seg_cnt, (const uint32_t *)seg_off, A->segs, 1);
   BUILD_TRY(hipGetLastError());
-  if (vk == VK_PAT) BUILD_TRY(build_pull_order(A, seg_cnt, s));
+  if (vk == VK_PAT) {
+    BUILD_TRY(build_pull_order(A, seg_cnt, s));
+    const size_t ow = (size_t)(A->payload_bytes + DBS_PAYLOAD_SLACK) / 4;
+    BUILD_TRY(dbs_dev_alloc(A, (void **)&A->wown, ow));
+    BUILD_TRY(hipMemsetAsync(A->wown, 0, ow, s));
+    if (A->npseg > 0) {
+      hipLaunchKernelGGL(k_word_owner, dim3(nblocks(A->npseg, BT)), dim3(BT), 0, s, (const uint32_t *)A->psegs,
+                         A->npseg, (const uint64_t *)A->t_meta, A->wown);
+      BUILD_TRY(hipGetLastError());
+    }
+  }
 
   // --- statistics per format
   unsigned long long *st;

@@ -126,6 +126,8 @@ struct dbs_matrix {
   uint8_t *payload;     // arena
   uint64_t dense_mask_off;  // start of the Dense row-mask section in the arena
   uint32_t *segs;       // [4*nseg] pull segments
+  uint8_t *wown;        // pattern matrices: per 4-byte payload word of a COO tile, that tile's index
+                        // in its Boolean-pull segment
   uint32_t *psegs;      // [4*npseg] pattern matrices: Boolean-pull segments (first row block, first
                         // tile, end tile, row blocks), first-launch ones ahead
   int64_t payload_bytes;

@@ -2,7 +2,11 @@
 // Blocked Sparse Matrix-Sparse Vector Multiplication for Dynamic GPU
 // Workloads"), shared by the OR-AND SpMSpV and the BFS level step.  The
 // caller's policy says which rows of a row block are still wanted, gives the
-// blk_x_mask of a column block and takes the found rows of each segment.
+// blk_x_mask of a column block and writes out the found rows.  Found rows
+// are collected in LDS (row block, rows) and written out 48 to 64 row blocks
+// at a time: this GPU counts stores and loads on one counter, and a store in
+// flight makes the next wait for a load wait for every load in flight, so a
+// store per segment would undo the pipelining.
 #pragma once
 
 #include "tile_kernels.h"
@@ -17,6 +21,7 @@ struct PatSrc {
   int64_t nseg;
   brsrc_t pay;  // payload and its zeroed slack
   brsrc_t rbp;  // block-CSR row pointer (the row blocks of a segment that holds several)
+  brsrc_t own;  // per payload word of a COO tile: the tile's index in its segment
 };
 
 template <int U>
@@ -59,8 +64,8 @@ DBS_DEV void pat_issue(const PatSrc &S, const Pol &pol, int64_t s0, bool live, u
 // tiles of up to four entries are decoded from their metadata word; the
 // coordinate words of the other COO tiles are consecutive in the COO section,
 // so the segment reads them as one run spread over the lanes (word j by lane
-// j), each lane finding the tile of its word by a wave max-scan of the tiles'
-// first-word marks and an end test.  Larger tiles (Dense, ForceCSR,
+// j) together with each word's owner tile (a byte per word, recorded at
+// build), whose mask the lane reads from LDS.  Larger tiles (Dense, ForceCSR,
 // ForceCSC, patched CSR: all keep the 16 row masks for pattern matrices) are
 // rare and read their masks per lane.  The work per segment that does not
 // grow with its tiles (descriptor, ballots, word setup, wave OR, writeback)
@@ -74,11 +79,18 @@ struct PatSeg {  // stage A: descriptor, column blocks, metadata (n == 0: no seg
 };
 
 template <int K>
-struct PatMasks {  // stage B: masks, and (EAGER) the first chunk of coordinate words
+struct PatMasks {  // stage B: masks, and (EAGER) the first chunk of coordinate words and their owners
   uint32_t m[K];
-  uint64_t nb[K];
   int tf, tl;  // first and last non-inline COO tile whose words are read (uniform; tl < 0: none)
-  uint32_t base, nwords, word;
+  uint32_t base, nwords, word, own;
+};
+
+// Found rows of a wave not yet written: entry i is row block rb[i], rows f[i]
+// (LDS), n entries (uniform).
+constexpr int PAT_FOUND_CAP = 64;
+struct FoundBuf {
+  uint32_t *rb, *f;
+  int n;
 };
 
 // The descriptors of a wave's next 64 segments (lane j: segment next +
@@ -169,7 +181,7 @@ DBS_DEV uint32_t slice_lane(const uint32_t (&v)[K], int k, int l) {
 
 // the non-inline COO tiles whose words are read (every such tile when EAGER:
 // an inactive tile's words meet a zero mask; else the active ones), the run
-// of their words, and its first chunk
+// of their words, and its first chunk with the words' owner tiles
 template <int K, bool EAGER>
 DBS_DEV void pat_words(const PatSrc &S, const PatSeg<K> &a, PatMasks<K> &b, int lane, uint32_t l4) {
   uint32_t vp[K], vend[K];
@@ -178,11 +190,11 @@ DBS_DEV void pat_words(const PatSrc &S, const PatSeg<K> &a, PatMasks<K> &b, int 
 #pragma unroll
   for (int k = 0; k < K; ++k) {
     const bool live = EAGER ? (64u * k + (uint32_t)lane < a.n) : (b.m[k] != 0u);
-    b.nb[k] = __ballot(live & (meta_type(a.meta[k]) == DBS_TILE_COO) & !meta_inline(a.meta[k]));
+    const uint64_t nb = __ballot(live & (meta_type(a.meta[k]) == DBS_TILE_COO) & !meta_inline(a.meta[k]));
     vp[k] = (uint32_t)meta_vp(a.meta[k]);
     vend[k] = vp[k] + coo_val_off(meta_nnz(a.meta[k]));
-    if (b.nb[k] != 0ull) {
-      const int f = 64 * k + __ffsll((unsigned long long)b.nb[k]) - 1, l = 64 * k + 63 - __clzll((long long)b.nb[k]);
+    if (nb != 0ull) {
+      const int f = 64 * k + __ffsll((unsigned long long)nb) - 1, l = 64 * k + 63 - __clzll((long long)nb);
       b.tf = f < b.tf ? f : b.tf;
       b.tl = l > b.tl ? l : b.tl;
     }
@@ -193,7 +205,9 @@ DBS_DEV void pat_words(const PatSrc &S, const PatSeg<K> &a, PatMasks<K> &b, int 
     b.base = slice_lane<K>(vp, b.tf >> 6, b.tf & 63);
     b.nwords = (slice_lane<K>(vend, b.tl >> 6, b.tl & 63) - b.base) >> 2;
   }
-  b.word = bld32(S.pay, (uint32_t)lane < b.nwords ? b.base + l4 : OOB_OFF);
+  const bool in = (uint32_t)lane < b.nwords;
+  b.word = bld32(S.pay, in ? b.base + l4 : OOB_OFF);
+  b.own = __builtin_amdgcn_raw_buffer_load_b8(S.own, in ? (b.base >> 2) + (uint32_t)lane : OOB_OFF, 0, 0);
 }
 
 // everything of one segment once its loads have arrived.  MULTI: the
@@ -202,7 +216,7 @@ DBS_DEV void pat_words(const PatSrc &S, const PatSeg<K> &a, PatMasks<K> &b, int 
 // being the number of row-block starts up to it.
 template <int K, bool MULTI, class Pol>
 DBS_DEV void pat_finish(const PatSrc &S, const Pol &pol, const PatSeg<K> &a, const PatMasks<K> &b, int lane,
-                        uint32_t *s_mark, uint32_t *s_tm, uint32_t *s_te, uint32_t *s_f) {
+                        uint32_t *s_tm, uint32_t *s_f, FoundBuf &fb) {
   const uint32_t n = a.n;  // uniform
   uint32_t f = 0u;
   uint32_t ri[K];  // MULTI: row block (0 .. nrb-1) of this lane's tile in each slice
@@ -233,39 +247,23 @@ DBS_DEV void pat_finish(const PatSrc &S, const Pol &pol, const PatSeg<K> &a, con
                                                                                       : 0u);
   }
   if (b.tl >= 0) {
-    // per-tile mask, word end (and, MULTI, row block) of this segment, for the word owners
+    // per-tile mask (and, MULTI, row block << 16), read by the lanes holding the tile's words
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       if (64u * k >= n) break;  // uniform
-      s_tm[64 * k + lane] = b.m[k];
-      s_te[64 * k + lane] =
-          (((uint32_t)meta_vp(a.meta[k]) + coo_val_off(meta_nnz(a.meta[k])) - b.base) >> 2) | (ri[k] << 24);
+      s_tm[64 * k + lane] = b.m[k] | (ri[k] << 16);
     }
-    uint32_t carry = 0u;
+    __syncwarp();
     for (uint32_t j0 = 0; j0 < b.nwords; j0 += 64u) {
-      // lanes talk through LDS: each step is fenced at wave scope, or the
-      // compiler may hand a lane back its own earlier store
-      __syncwarp();
-      s_mark[lane] = 0u;
-      __syncwarp();
-#pragma unroll
-      for (int k = 0; k < K; ++k) {
-        const uint32_t slot = ((uint32_t)meta_vp(a.meta[k]) - b.base) >> 2;  // first word of this lane's tile
-        const bool nic = (b.nb[k] >> lane) & 1ull;
-        if (nic & (slot >= j0) & (slot < j0 + 64u)) s_mark[slot - j0] = 64u * k + (uint32_t)lane + 1u;
-      }
-      __syncwarp();
-      uint32_t own = wave_incl_max(s_mark[lane]);
-      own = own > carry ? own : carry;
-      carry = (uint32_t)__builtin_amdgcn_readlane((int)own, 63);  // owner of the next chunk's first word
-      const uint32_t t = own ? own - 1u : 0u;
-      const uint32_t mw = s_tm[t], te = s_te[t];
-      const uint32_t oend = te & 0xFFFFFFu;
       const uint32_t j = j0 + (uint32_t)lane;
-      const uint32_t wd = j0 == 0u ? b.word : bld32(S.pay, j < b.nwords ? b.base + 4u * j : OOB_OFF);
-      const uint32_t x = ((j < b.nwords) & (j < oend)) ? coo_or4(wd, mw) : 0u;
+      const bool in = j < b.nwords;
+      const uint32_t wd = j0 == 0u ? b.word : bld32(S.pay, in ? b.base + 4u * j : OOB_OFF);
+      const uint32_t ow =
+          j0 == 0u ? b.own : __builtin_amdgcn_raw_buffer_load_b8(S.own, in ? (b.base >> 2) + j : OOB_OFF, 0, 0);
+      const uint32_t tm = s_tm[ow & 255u];
+      const uint32_t x = in ? coo_or4(wd, tm & 0xFFFFu) : 0u;
       if constexpr (MULTI) {
-        if (x) atomicOr(&s_f[te >> 24], x);
+        if (x) atomicOr(&s_f[tm >> 16], x);
       } else {
         f |= x;
       }
@@ -291,14 +289,35 @@ DBS_DEV void pat_finish(const PatSrc &S, const Pol &pol, const PatSeg<K> &a, con
   if constexpr (MULTI) {
     __syncwarp();
     const uint32_t fl = ((uint32_t)lane < a.nrb) ? s_f[lane] & a.needl : 0u;
-    __syncwarp();
-    for (uint64_t any = __ballot(fl != 0u); any; any &= any - 1ull) {  // uniform
-      const int r = __ffsll((unsigned long long)any) - 1;
-      pol.found(a.rb + (uint32_t)r, (uint32_t)__builtin_amdgcn_readlane((int)fl, r), lane);
+    const uint64_t any = __ballot(fl != 0u);
+    if (fl != 0u) {
+      const int pos = fb.n + __popcll(any & ((1ull << lane) - 1ull));
+      fb.rb[pos] = a.rb + (uint32_t)lane;
+      fb.f[pos] = fl;
     }
+    fb.n += __popcll(any);
+    __syncwarp();
   } else {
     f = wave_or(f) & (uint32_t)__builtin_amdgcn_readlane((int)a.needl, 0);
-    if (f != 0u) pol.found(a.rb, f, lane);  // uniform
+    if (f != 0u) {  // uniform
+      if (lane == 0) {
+        fb.rb[fb.n] = a.rb;
+        fb.f[fb.n] = f;
+      }
+      fb.n += 1;
+    }
+  }
+}
+
+// write out the collected found rows (the policy's flush) once the buffer
+// may not take another segment's row blocks
+template <class Pol>
+DBS_DEV void pat_flush(const Pol &pol, FoundBuf &fb, int lane, bool all) {
+  if (fb.n > (all ? 0 : PAT_FOUND_CAP - PAT_MAX_RB)) {  // uniform
+    __syncwarp();
+    pol.flush(fb.rb, fb.f, fb.n, lane);
+    __syncwarp();
+    fb.n = 0;
   }
 }
 
@@ -310,7 +329,7 @@ DBS_DEV void pat_finish(const PatSrc &S, const Pol &pol, const PatSeg<K> &a, con
 // window of descriptors, once per 64 segments, does wait).
 template <int K, bool EAGER, class Pol>
 DBS_DEV void pattern_pull_wave(const PatSrc &S, const Pol &pol, int64_t s0, int64_t stride, int lane,
-                               uint32_t *s_mark, uint32_t *s_tm, uint32_t *s_te, uint32_t *s_f) {
+                               uint32_t *s_tm, uint32_t *s_f, FoundBuf &fb) {
   if (s0 >= S.nseg) return;
   const uint32_t l4 = (uint32_t)lane * 4u, l8 = (uint32_t)lane * 8u;
   auto masks = [&](const PatSeg<K> &a, PatMasks<K> &b) {
@@ -336,8 +355,9 @@ DBS_DEV void pattern_pull_wave(const PatSrc &S, const Pol &pol, int64_t s0, int6
     patk_issue<K, EAGER>(S, pol, stride, lane, w, l4, l8, a2);
     masks(a1, b1);
     if constexpr (!EAGER) pat_words<K, false>(S, a0, b0, lane, l4);
-    if (a0.nrb > 1u) pat_finish<K, true>(S, pol, a0, b0, lane, s_mark, s_tm, s_te, s_f);  // uniform
-    else pat_finish<K, false>(S, pol, a0, b0, lane, s_mark, s_tm, s_te, s_f);
+    if (a0.nrb > 1u) pat_finish<K, true>(S, pol, a0, b0, lane, s_tm, s_f, fb);  // uniform
+    else pat_finish<K, false>(S, pol, a0, b0, lane, s_tm, s_f, fb);
+    pat_flush(pol, fb, lane, false);
     a0 = a1;
     a1 = a2;
     b0 = b1;
@@ -346,14 +366,16 @@ DBS_DEV void pattern_pull_wave(const PatSrc &S, const Pol &pol, int64_t s0, int6
 
 constexpr int PAT_K = DBS_PAT_SEG_CAP / 64;  // slices of 64 tiles per pattern-pull segment
 
-// LDS per wave: marks (64), masks and word ends of a segment's tiles (2 x
-// 64*K), found rows per row block
-constexpr int PAT_LDS_WORDS = 64 + 2 * 64 * PAT_K + PAT_MAX_RB;
+// LDS per wave: masks of a segment's tiles (64*K), found rows per row block,
+// the found-row buffer (2 x PAT_FOUND_CAP)
+constexpr int PAT_LDS_WORDS = 64 * PAT_K + PAT_MAX_RB + 2 * PAT_FOUND_CAP;
 
 template <class Pol>
 DBS_DEV void pattern_pull(const PatSrc &S, const Pol &pol, int64_t s0, int64_t stride, bool eager, int lane,
                           uint32_t *s_lds) {
-  uint32_t *s_mark = s_lds, *s_tm = s_lds + 64, *s_te = s_lds + 64 + 64 * PAT_K, *s_f = s_te + 64 * PAT_K;
-  if (eager) pattern_pull_wave<PAT_K, true>(S, pol, s0, stride, lane, s_mark, s_tm, s_te, s_f);
-  else pattern_pull_wave<PAT_K, false>(S, pol, s0, stride, lane, s_mark, s_tm, s_te, s_f);
+  uint32_t *s_tm = s_lds, *s_f = s_lds + 64 * PAT_K;
+  FoundBuf fb{s_f + PAT_MAX_RB, s_f + PAT_MAX_RB + PAT_FOUND_CAP, 0};
+  if (eager) pattern_pull_wave<PAT_K, true>(S, pol, s0, stride, lane, s_tm, s_f, fb);
+  else pattern_pull_wave<PAT_K, false>(S, pol, s0, stride, lane, s_tm, s_f, fb);
+  pat_flush(pol, fb, lane, true);
 }

@@ -121,6 +121,7 @@ struct SpmvParams {
   uint64_t dense_mask_off;
   const uint32_t *segs;     // pull segments (pattern matrices: the Boolean pull's)
   const uint32_t *rb_ptr;
+  const uint8_t *wown;     // pattern matrices: owner tile of each payload word
   int64_t nseg, T, payload_bytes;
   int32_t m, nb;
   const uint32_t *xmask;
@@ -398,7 +399,8 @@ template <int VK, int U>
 DBS_DEV void plus_pull(const SpmvParams &P, int64_t gw, int64_t nw, bool eager, float *sx, float *spart,
                        uint32_t *s_mark, int lane) {
   const PatSrc S{P.t_cb, P.t_meta, P.segs, P.nseg,
-                 make_rsrc(P.payload, (uint64_t)P.payload_bytes + DBS_PAYLOAD_SLACK), make_rsrc(P.rb_ptr, 0)};
+                 make_rsrc(P.payload, (uint64_t)P.payload_bytes + DBS_PAYLOAD_SLACK), make_rsrc(P.rb_ptr, 0),
+                 make_rsrc(nullptr, 0)};
   const brsrc_t xm = make_rsrc(P.xmask, (uint64_t)P.nb * 4);
   if (eager) plus_pull_wave<VK, U, true>(P, S, xm, gw * U, nw * U, sx, spart, s_mark, lane);
   else plus_pull_wave<VK, U, false>(P, S, xm, gw * U, nw * U, sx, spart, s_mark, lane);
@@ -437,9 +439,15 @@ struct OrPol {
     const uint32_t w = bld32(xmask, in ? cb * 4u : OOB_OFF);
     return ((w >> 16) == epoch) ? (w & 0xFFFFu) : 0u;  // an idle lane reads 0: no epoch
   }
-  DBS_DEV void found(uint32_t rb, uint32_t f, int lane) const {
-    const int64_t row = (int64_t)rb * 16 + lane;
-    if ((lane < 16) & ((f >> lane) & 1u) & (row < m)) y[row] = 1;
+  // found rows of n row blocks (LDS): four row blocks per pass, a lane per row
+  DBS_DEV void flush(const uint32_t *frb, const uint32_t *ff, int n, int lane) const {
+    for (int e0 = 0; e0 < n; e0 += 4) {
+      const int e = e0 + (lane >> 4), r = lane & 15;
+      const bool in = e < n;
+      const uint32_t rb = frb[in ? e : 0], f = in ? ff[e] : 0u;
+      const int64_t row = (int64_t)rb * 16 + r;
+      if (((f >> r) & 1u) & (row < m)) y[row] = 1;
+    }
   }
 };
 
@@ -524,7 +532,8 @@ __global__ __launch_bounds__(KT) void k_spmspv(SpmvParams P) {
       R.pay = make_rsrc(P.payload, (uint64_t)P.payload_bytes + DBS_PAYLOAD_SLACK);
       R.xmask = make_rsrc(P.xmask, (uint64_t)P.nb * 4);
       if constexpr (VK == VK_PAT) {
-        const PatSrc S{P.t_cb, P.t_meta, P.segs, P.nseg, R.pay, make_rsrc(P.rb_ptr, (uint64_t)(P.m + 15) / 16 * 4 + 4)};
+        const PatSrc S{P.t_cb, P.t_meta, P.segs, P.nseg, R.pay, make_rsrc(P.rb_ptr, (uint64_t)(P.m + 15) / 16 * 4 + 4),
+                       make_rsrc(P.wown, (uint64_t)(P.payload_bytes + DBS_PAYLOAD_SLACK) / 4)};
         const OrPol pol{R.xmask, P.epoch, P.m, (uint8_t *)P.y};
         pattern_pull(S, pol, gw, nw, eager, lane, s_pat[w]);
       } else {
@@ -636,6 +645,7 @@ dbs_status dbs_spmspv_impl(dbs_matrix *A, int32_t nnz_x, const int32_t *x_idx, c
   P.segs = A->vk == VK_PAT ? A->psegs : A->segs;
   P.nseg = A->vk == VK_PAT ? A->npseg : A->nseg;
   P.rb_ptr = A->rb_ptr;
+  P.wown = A->wown;
   P.m = A->m;
   P.nb = A->nb;
   P.xmask = A->xmask;

@@ -246,6 +246,34 @@ def test_argument_errors(dbs):
     build(dbs, 64, 64, rp, ci, None, dbs.DBS_PATTERN, options(dbs, seg_cap=256))
 
 
+def clustered_pattern_csr(n, seed):
+    """Rows whose entries fall in a few 16-column windows: most tiles hold 5-30
+    entries (their coordinates are payload words), short and long row blocks mixed."""
+    rng = rng_for("test", 760, seed)
+    rows = []
+    for r in range(n):
+        k = int(rng.integers(0, 5)) if r % 97 else int(rng.integers(40, 200))
+        wins = rng.integers(0, n // 16, k)
+        cols = (wins[:, None] * 16 + rng.integers(0, 16, (k, 12))).ravel()
+        rows.append(np.unique(cols))
+    rp = np.zeros(n + 1, np.int64)
+    rp[1:] = np.cumsum([len(x) for x in rows])
+    return rp.astype(np.int32), np.concatenate(rows).astype(np.int32)
+
+
+@pytest.mark.parametrize("cap", [256, 100, 17])
+def test_or_and_pattern_coordinate_words(dbs, cap):
+    n = 12000  # ragged last block
+    rp, ci = clustered_pattern_csr(n, cap)
+    A = build(dbs, n, n, rp, ci, None, dbs.DBS_PATTERN, options(dbs, seg_cap=cap))
+    for k, density in enumerate([0.001, 0.02, 0.3]):
+        xi, _ = sparse_x(n, density, rng_for("test", 761, cap, k), with_values=False)
+        yr = orc.or_and_pull(n, n, rp, ci, xi)
+        for path in PATHS:
+            dbs.dbs_set_option(A, dbs.DBS_OPT_PATH, path)
+            np.testing.assert_array_equal(run_or(dbs, A, n, xi), yr, err_msg=f"density {density} path {path}")
+
+
 def test_rmat20_or_and_sweep_full_size(dbs):
     """R-MAT scale 20 (edge factor 16, symmetrized), OR-AND, the density sweep."""
     rp, ci = rmat_csr(20, 16, rng_for("rmat20"))
