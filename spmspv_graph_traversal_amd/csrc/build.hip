@@ -11,6 +11,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "common.h"
@@ -361,6 +362,22 @@ __global__ void k_type_stats(const uint32_t *t_nt, int64_t T, unsigned long long
 
 inline unsigned nblocks(int64_t n, int b) { return (unsigned)((n + b - 1) / b); }
 
+// Work of a Boolean-pull segment, for ordering: its tiles, plus two per
+// coordinate word and eight per tile read as row masks.  One thread per
+// segment.
+__global__ void k_seg_cost(const uint32_t *psegs, int64_t npseg, const uint64_t *t_meta, uint32_t *cost) {
+  const int64_t sg = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (sg >= npseg) return;
+  const uint32_t t0 = psegs[4 * sg + 1], t1 = psegs[4 * sg + 2];
+  uint32_t c = 0;
+  for (uint32_t t = t0; t < t1; ++t) {
+    const uint64_t meta = t_meta[t];
+    const uint32_t type = meta_type(meta);
+    c += 1u + (type != DBS_TILE_COO ? 8u : meta_inline(meta) ? 0u : 2u * ((meta_nnz(meta) + 3u) / 4u));
+  }
+  cost[sg] = c;
+}
+
 // Owner of every coordinate word of a pattern COO tile held in the payload:
 // the tile's index in its Boolean-pull segment (< 256).  The pull spreads a
 // segment's words over the lanes; with the owner stored, a lane finds the
@@ -435,6 +452,37 @@ hipError_t build_pull_order(dbs_matrix *A, const uint32_t *seg_cnt, hipStream_t 
   first.resize(first.size() + 4 * 16, 0u);  // 16 zeroed descriptors of padding
   e = dbs_dev_alloc(A, (void **)&A->psegs, first.size() * 4);
   if (e == hipSuccess) e = hipMemcpyAsync(A->psegs, first.data(), first.size() * 4, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  return e;
+}
+
+// Each launch's segments sorted by decreasing work: a wave takes every
+// (number of waves)-th segment, so every wave gets one segment of each
+// size class and the waves finish together (in list order, the waves that
+// drew the long row blocks' segments ran up to a third longer than the
+// median).  Row-block order does not matter to the pull.
+template <class Tmp>
+hipError_t order_by_cost(dbs_matrix *A, Tmp &tmp, hipStream_t s) {
+  const int64_t np = A->npseg;
+  uint32_t *dcost;
+  hipError_t e = tmp.get((void **)&dcost, (size_t)np * 4);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_seg_cost, dim3(nblocks(np, 256)), dim3(256), 0, s, (const uint32_t *)A->psegs, np,
+                     (const uint64_t *)A->t_meta, dcost);
+  e = hipGetLastError();
+  std::vector<uint32_t> cost(np), sg(4 * (size_t)np);
+  if (e == hipSuccess) e = hipMemcpyAsync(cost.data(), dcost, (size_t)np * 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(sg.data(), A->psegs, (size_t)np * 16, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return e;
+  std::vector<uint32_t> idx(np), out(4 * (size_t)np);
+  for (int64_t i = 0; i < np; ++i) idx[i] = (uint32_t)i;
+  auto by_cost = [&](uint32_t a, uint32_t b) { return cost[a] > cost[b]; };
+  std::stable_sort(idx.begin(), idx.begin() + A->nseg0, by_cost);
+  std::stable_sort(idx.begin() + A->nseg0, idx.end(), by_cost);
+  for (int64_t i = 0; i < np; ++i)
+    for (int j = 0; j < 4; ++j) out[4 * i + j] = sg[4 * (size_t)idx[i] + j];
+  e = hipMemcpyAsync(A->psegs, out.data(), (size_t)np * 16, hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   return e;
 }
@@ -618,6 +666,7 @@ dbs_status dbs_build_impl(dbs_matrix *A, const int32_t *row_ptr, const int32_t *
       hipLaunchKernelGGL(k_word_owner, dim3(nblocks(A->npseg, BT)), dim3(BT), 0, s, (const uint32_t *)A->psegs,
                          A->npseg, (const uint64_t *)A->t_meta, A->wown);
       BUILD_TRY(hipGetLastError());
+      BUILD_TRY(order_by_cost(A, tmp, s));
     }
   }
 

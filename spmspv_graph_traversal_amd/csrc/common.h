@@ -73,6 +73,8 @@ __host__ __device__ inline bool coo_is_inline(int vk, uint32_t nnz) { return vk 
 __host__ __device__ inline uint64_t meta_vp(uint64_t m) { return m & ((1ull << 40) - 1); }
 __host__ __device__ inline uint32_t meta_nnz(uint64_t m) { return (uint32_t)((m >> 40) & 0xFF) + 1; }
 __host__ __device__ inline uint32_t meta_type(uint64_t m) { return (uint32_t)((m >> 48) & 0x7); }
+// format | inline << 3, from the upper half of a metadata word
+__host__ __device__ inline uint32_t meta_kind(uint32_t hi) { return (hi >> 16) & 0xFu; }
 
 // section of a tile in the arena: 0 Dense, 1 mask-based, 2 COO
 __host__ __device__ inline int tile_section(int type, int vk) {

@@ -184,15 +184,15 @@ DBS_DEV uint32_t slice_lane(const uint32_t (&v)[K], int k, int l) {
 // of their words, and its first chunk with the words' owner tiles
 template <int K, bool EAGER>
 DBS_DEV void pat_words(const PatSrc &S, const PatSeg<K> &a, PatMasks<K> &b, int lane, uint32_t l4) {
-  uint32_t vp[K], vend[K];
+  uint32_t lo[K], hi[K];  // halves of the metadata words
   b.tf = 1 << 20;
   b.tl = -1;
 #pragma unroll
   for (int k = 0; k < K; ++k) {
+    lo[k] = (uint32_t)a.meta[k];
+    hi[k] = (uint32_t)(a.meta[k] >> 32);
     const bool live = EAGER ? (64u * k + (uint32_t)lane < a.n) : (b.m[k] != 0u);
-    const uint64_t nb = __ballot(live & (meta_type(a.meta[k]) == DBS_TILE_COO) & !meta_inline(a.meta[k]));
-    vp[k] = (uint32_t)meta_vp(a.meta[k]);
-    vend[k] = vp[k] + coo_val_off(meta_nnz(a.meta[k]));
+    const uint64_t nb = __ballot(live & (meta_kind(hi[k]) == DBS_TILE_COO));  // COO, not inline
     if (nb != 0ull) {
       const int f = 64 * k + __ffsll((unsigned long long)nb) - 1, l = 64 * k + 63 - __clzll((long long)nb);
       b.tf = f < b.tf ? f : b.tf;
@@ -202,8 +202,11 @@ DBS_DEV void pat_words(const PatSrc &S, const PatSeg<K> &a, PatMasks<K> &b, int 
   b.base = 0u;
   b.nwords = 0u;
   if (b.tl >= 0) {
-    b.base = slice_lane<K>(vp, b.tf >> 6, b.tf & 63);
-    b.nwords = (slice_lane<K>(vend, b.tl >> 6, b.tl & 63) - b.base) >> 2;
+    // the run starts at the first tile's words and ends after the last one's
+    b.base = slice_lane<K>(lo, b.tf >> 6, b.tf & 63);
+    const uint32_t lvp = slice_lane<K>(lo, b.tl >> 6, b.tl & 63);
+    const uint32_t lhi = slice_lane<K>(hi, b.tl >> 6, b.tl & 63);
+    b.nwords = (lvp + coo_val_off(((lhi >> 8) & 0xFFu) + 1u) - b.base) >> 2;
   }
   const bool in = (uint32_t)lane < b.nwords;
   b.word = bld32(S.pay, in ? b.base + l4 : OOB_OFF);
@@ -242,9 +245,9 @@ DBS_DEV void pat_finish(const PatSrc &S, const Pol &pol, const PatSeg<K> &a, con
   for (int k = 0; k < K; ++k) {
     if (64u * k >= n) break;  // uniform
     const uint64_t meta = a.meta[k];
-    // COO tiles with at most four entries: the coordinates are in the metadata word
-    add(k, ((b.m[k] != 0u) & (meta_type(meta) == DBS_TILE_COO) & meta_inline(meta)) ? coo_or4((uint32_t)meta, b.m[k])
-                                                                                      : 0u);
+    // COO tiles with at most four entries: the coordinates are in the metadata
+    // word (a zero mask decodes to nothing)
+    add(k, meta_kind((uint32_t)(meta >> 32)) == (DBS_TILE_COO | 8u) ? coo_or4((uint32_t)meta, b.m[k]) : 0u);
   }
   if (b.tl >= 0) {
     // per-tile mask (and, MULTI, row block << 16), read by the lanes holding the tile's words
