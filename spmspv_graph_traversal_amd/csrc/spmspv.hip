@@ -386,9 +386,12 @@ DBS_DEV void plus_pull_wave(const SpmvParams &P, const PatSrc &S, const brsrc_t 
       for (int u = 0; u < U; ++u)
         cur.meta[u] = bld64(make_rsrc(S.t_meta + cur.seg[u].y, (uint64_t)cur.n[u] * 8u), m[u] != 0u ? l8 : OOB_OFF);
     }
+    // a segment with no active tile has nothing to add (y was cleared by the
+    // metadata kernel)
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      if (s0 + u < S.nseg) pull_finish<VK>(P, cur.seg[u], cur.cb[u], m[u], cur.meta[u], m[u] != 0u, sx, spart, s_mark, lane);
+      if ((s0 + u < S.nseg) && __ballot(m[u] != 0u) != 0ull)  // uniform
+        pull_finish<VK>(P, cur.seg[u], cur.cb[u], m[u], cur.meta[u], m[u] != 0u, sx, spart, s_mark, lane);
     if (!more) break;
     cur = nxt;
     s0 = s1;
@@ -506,7 +509,10 @@ DBS_DEV void pull_or_group(const SpmvParams &P, const PullRes &R, int64_t s0, bo
 }
 
 template <int VK, int SR>
-__global__ __launch_bounds__(KT) void k_spmspv(SpmvParams P) {
+// the bf16 PLUS_TIMES pull (decode layers) runs five waves per SIMD in 96
+// VGPRs (12 bytes spilled) and is faster so (7% on the decode layers); the
+// others keep their own register counts
+__global__ __launch_bounds__(KT, (VK == VK_BF16 && SR == DBS_PLUS_TIMES) ? 5 : 1) void k_spmspv(SpmvParams P) {
   __shared__ float s_x[KT / DBS_WAVE][16];
   __shared__ float s_part[KT / DBS_WAVE][64];
   __shared__ uint32_t s_mark[KT / DBS_WAVE][64];
