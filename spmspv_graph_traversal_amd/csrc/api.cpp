@@ -38,9 +38,9 @@ namespace {
 // fold the timing slot `i` into the sums (waits for its last event)
 hipError_t fold_slot(dbs_matrix *A, int i) {
   float a = 0.0f, b = 0.0f;
-  hipError_t e = hipEventSynchronize(A->tev[i][2]);
+  hipError_t e = hipEventSynchronize(A->tev[i][3]);
   if (e == hipSuccess) e = hipEventElapsedTime(&a, A->tev[i][0], A->tev[i][1]);
-  if (e == hipSuccess) e = hipEventElapsedTime(&b, A->tev[i][1], A->tev[i][2]);
+  if (e == hipSuccess) e = hipEventElapsedTime(&b, A->tev[i][2], A->tev[i][3]);
   if (e != hipSuccess) return e;
   A->st.timed_calls += 1;
   A->st.sum_meta_ms += a;
@@ -73,7 +73,7 @@ void free_all(dbs_matrix *A) {
     if (e) (void)hipEventDestroy(e);
   if (A->tev_ready)
     for (int i = 0; i < dbs_matrix::kTimingRing; ++i)
-      for (int j = 0; j < 3; ++j) (void)hipEventDestroy(A->tev[i][j]);
+      for (int j = 0; j < 4; ++j) (void)hipEventDestroy(A->tev[i][j]);
 }
 
 dbs_status map_err(hipError_t e) {
@@ -114,7 +114,7 @@ hipEvent_t *dbs_timing_slot(dbs_matrix *A) {
   const int R = dbs_matrix::kTimingRing;
   if (!A->tev_ready) {
     for (int i = 0; i < R; ++i)
-      for (int j = 0; j < 3; ++j)
+      for (int j = 0; j < 4; ++j)
         if (DBS_NOTE(hipEventCreate(&A->tev[i][j])) != hipSuccess) return nullptr;
     A->tev_ready = 1;
   }

@@ -160,9 +160,10 @@ struct dbs_matrix {
   // BFS: levels launched between two host reads of the frontier sizes
   static constexpr int kBfsBatch = 4;
   hipEvent_t ev[2 + 2 * kBfsBatch];  // BFS timing: whole run, then each level kernel of a batch
-  // ring of per-call event triples (before meta, after meta, after compute)
+  // ring of per-call event quadruples: start and end of the metadata kernel,
+  // start and end of the SpMSpV kernel, taken by the dispatches themselves
   static constexpr int kTimingRing = 64;
-  hipEvent_t tev[kTimingRing][3];
+  hipEvent_t tev[kTimingRing][4];
   int tev_head, tev_used, tev_ready;
   int64_t mem_now, mem_peak;
 };

@@ -12,6 +12,8 @@
 //               either the push chunks or the static pull segments, one wave
 //               per chunk / segment, grid-stride.
 #include "meta.h"
+#include <hip/hip_ext.h>
+
 #include "pattern_pull.h"
 #include "tile_kernels.h"
 
@@ -558,10 +560,16 @@ inline unsigned grid_for(int64_t waves, unsigned cap) {
   return (unsigned)(g < cap ? g : cap);
 }
 
+// launch; with timing events, the dispatch itself records its start and end
+template <typename K, typename... Args>
+void launch_k(K kernel, dim3 grid, dim3 block, hipStream_t s, hipEvent_t e0, hipEvent_t e1, Args... args) {
+  hipExtLaunchKernelGGL(kernel, grid, block, 0, s, e0, e1, 0, args...);
+}
+
 template <int VK, int SR>
-void launch_spmspv(const SpmvParams &P, int64_t waves, hipStream_t s) {
+void launch_spmspv(const SpmvParams &P, int64_t waves, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   static const unsigned resident = dbs_resident_groups(k_spmspv<VK, SR>, KT);
-  hipLaunchKernelGGL((k_spmspv<VK, SR>), dim3(grid_for(waves, resident)), dim3(KT), 0, s, P);
+  launch_k(k_spmspv<VK, SR>, dim3(grid_for(waves, resident)), dim3(KT), s, e0, e1, P);
 }
 
 }  // namespace
@@ -619,24 +627,24 @@ dbs_status dbs_spmspv_impl(dbs_matrix *A, int32_t nnz_x, const int32_t *x_idx, c
   if (timing) {
     tev = dbs_timing_slot(A);
     if (!tev) return DBS_ERR_DEVICE;
-    SPMV_TRY(hipEventRecord(tev[0], s));
   }
+  hipEvent_t m0 = tev ? tev[0] : nullptr, m1 = tev ? tev[1] : nullptr;
+  hipEvent_t c0 = tev ? tev[2] : nullptr, c1 = tev ? tev[3] : nullptr;
   if (dense) {
     void *xd = sr == DBS_PLUS_TIMES ? A->xd : nullptr;
-    if (xk == VK_BF16) hipLaunchKernelGGL(k_xmeta_dense<VK_BF16>, dim3(mgrid), dim3(dbs_meta::MT), 0, s, o, x_dense, xd);
-    else hipLaunchKernelGGL(k_xmeta_dense<VK_F32>, dim3(mgrid), dim3(dbs_meta::MT), 0, s, o, x_dense, xd);
+    if (xk == VK_BF16) launch_k(k_xmeta_dense<VK_BF16>, dim3(mgrid), dim3(dbs_meta::MT), s, m0, m1, o, x_dense, xd);
+    else launch_k(k_xmeta_dense<VK_F32>, dim3(mgrid), dim3(dbs_meta::MT), s, m0, m1, o, x_dense, xd);
   } else {
     const int check = (int)A->opt[DBS_OPT_CHECK];
     const void *xv = sr == DBS_PLUS_TIMES ? x_val : nullptr;
     if (xk == VK_F32)
-      hipLaunchKernelGGL(k_xmeta_sparse<VK_F32>, dim3(mgrid), dim3(dbs_meta::MT), 0, s, o, nnz_x, x_idx, xv, A->xd, check);
+      launch_k(k_xmeta_sparse<VK_F32>, dim3(mgrid), dim3(dbs_meta::MT), s, m0, m1, o, nnz_x, x_idx, xv, A->xd, check);
     else if (xk == VK_BF16)
-      hipLaunchKernelGGL(k_xmeta_sparse<VK_BF16>, dim3(mgrid), dim3(dbs_meta::MT), 0, s, o, nnz_x, x_idx, xv, A->xd, check);
+      launch_k(k_xmeta_sparse<VK_BF16>, dim3(mgrid), dim3(dbs_meta::MT), s, m0, m1, o, nnz_x, x_idx, xv, A->xd, check);
     else
-      hipLaunchKernelGGL(k_xmeta_sparse<VK_PAT>, dim3(mgrid), dim3(dbs_meta::MT), 0, s, o, nnz_x, x_idx, xv, A->xd, check);
+      launch_k(k_xmeta_sparse<VK_PAT>, dim3(mgrid), dim3(dbs_meta::MT), s, m0, m1, o, nnz_x, x_idx, xv, A->xd, check);
   }
   SPMV_TRY(hipGetLastError());
-  if (timing) SPMV_TRY(hipEventRecord(tev[1], s));
 
   SpmvParams P;
   P.T = A->T;
@@ -681,15 +689,14 @@ dbs_status dbs_spmspv_impl(dbs_matrix *A, int32_t nnz_x, const int32_t *x_idx, c
   const int64_t waves = pull_waves > A->max_chunks ? pull_waves : A->max_chunks;
   const int vk = A->vk;
   if (sr == DBS_OR_AND) {
-    if (vk == VK_F32) launch_spmspv<VK_F32, DBS_OR_AND>(P, waves, s);
-    else if (vk == VK_BF16) launch_spmspv<VK_BF16, DBS_OR_AND>(P, waves, s);
-    else launch_spmspv<VK_PAT, DBS_OR_AND>(P, waves, s);
+    if (vk == VK_F32) launch_spmspv<VK_F32, DBS_OR_AND>(P, waves, s, c0, c1);
+    else if (vk == VK_BF16) launch_spmspv<VK_BF16, DBS_OR_AND>(P, waves, s, c0, c1);
+    else launch_spmspv<VK_PAT, DBS_OR_AND>(P, waves, s, c0, c1);
   } else {
-    if (vk == VK_F32) launch_spmspv<VK_F32, DBS_PLUS_TIMES>(P, waves, s);
-    else launch_spmspv<VK_BF16, DBS_PLUS_TIMES>(P, waves, s);
+    if (vk == VK_F32) launch_spmspv<VK_F32, DBS_PLUS_TIMES>(P, waves, s, c0, c1);
+    else launch_spmspv<VK_BF16, DBS_PLUS_TIMES>(P, waves, s, c0, c1);
   }
   SPMV_TRY(hipGetLastError());
-  if (timing) SPMV_TRY(hipEventRecord(tev[2], s));
   A->cbuf ^= 1;
   A->last_stream = s;
   A->st.last_path = -2;  // resolved from the device counters by dbs_get_stats
