@@ -304,6 +304,82 @@ DBS_DEV void coo_entries_plus(const brsrc_t pay, const brsrc_t xr, bool coo, uin
   __syncwarp();
 }
 
+// The COO entries of the U segments of a wave step together: round i takes
+// chunk i (entries 64i .. 64i+63 of the segment's run) of every segment that
+// has one, and issues all their coordinate and value loads, then all their
+// x loads, before any is used, so a step waits about twice per round for
+// memory whatever U.  Products go to s_y[16 u + row]; the row totals are
+// left there.
+template <int VK, int U>
+DBS_DEV void coo_entries_plus_u(const brsrc_t pay, const brsrc_t xr, const bool (&coo)[U], const uint64_t (&meta)[U],
+                                const uint32_t (&m)[U], const uint32_t (&cb)[U], uint32_t *s_mark, float *s_y,
+                                int lane) {
+  constexpr uint32_t VS = VK == VK_F32 ? 4u : 2u;
+  uint32_t cnt[U], start[U], total[U], carry[U];
+  uint32_t rounds = 0;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    cnt[u] = coo[u] ? meta_nnz(meta[u]) : 0u;
+    start[u] = wave_incl_add(cnt[u]) - cnt[u];
+    total[u] = (uint32_t)__builtin_amdgcn_readlane((int)(start[u] + cnt[u]), 63);
+    carry[u] = 0u;
+    const uint32_t r = (total[u] + 63u) >> 6;
+    rounds = r > rounds ? r : rounds;
+  }
+  if (lane < 16 * U) s_y[lane] = 0.0f;
+  __syncwarp();
+  for (uint32_t i = 0; i < rounds; ++i) {
+    const uint32_t j0 = 64u * i;
+    int own[U];
+    // owner tile of each entry of the round's chunks (lanes talk through
+    // LDS, each step fenced at wave scope)
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      own[u] = 0;
+      if (j0 >= total[u]) continue;  // uniform
+      __syncwarp();
+      s_mark[lane] = 0u;
+      __syncwarp();
+      if ((cnt[u] != 0u) & (start[u] >= j0) & (start[u] < j0 + 64u)) s_mark[start[u] - j0] = (uint32_t)lane + 1u;
+      __syncwarp();
+      uint32_t o = wave_incl_max(s_mark[lane]);
+      o = o > carry[u] ? o : carry[u];
+      carry[u] = (uint32_t)__builtin_amdgcn_readlane((int)o, 63);
+      own[u] = (int)o - 1;
+    }
+    uint32_t rc[U], ocb[U], om[U];
+    float a[U], x[U];
+    bool live[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t j = j0 + (uint32_t)lane;
+      live[u] = j < total[u];
+      const uint32_t ovp = (uint32_t)__shfl((int)(uint32_t)meta_vp(meta[u]), own[u]);
+      const uint32_t ost = (uint32_t)__shfl((int)start[u], own[u]);
+      const uint32_t ocnt = (uint32_t)__shfl((int)cnt[u], own[u]);
+      ocb[u] = (uint32_t)__shfl((int)cb[u], own[u]);
+      om[u] = (uint32_t)__shfl((int)m[u], own[u]);
+      const uint32_t e = j - ost;
+      rc[u] = __builtin_amdgcn_raw_buffer_load_b8(pay, live[u] ? ovp + e : OOB_OFF, 0, 0);
+      const uint32_t aoff = live[u] ? ovp + coo_val_off(ocnt) + e * VS : OOB_OFF;
+      if (VK == VK_F32) a[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(pay, aoff, 0, 0));
+      else a[u] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(pay, aoff, 0, 0) << 16);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t c = rc[u] & 15u;
+      live[u] = live[u] & ((om[u] >> c) & 1u);
+      const uint32_t xoff = live[u] ? (ocb[u] * 16u + c) * VS : OOB_OFF;
+      if (VK == VK_F32) x[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(xr, xoff, 0, 0));
+      else x[u] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(xr, xoff, 0, 0) << 16);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (live[u]) atomicAdd(&s_y[16 * u + (rc[u] >> 4)], a[u] * x[u]);
+  }
+  __syncwarp();
+}
+
 // ---------------------------------------------------------------------------
 // Finish one PLUS_TIMES pull segment whose tiles are loaded: COO entries over
 // the lanes, Dense and CSR-family tiles four at a time (row per lane),
@@ -311,9 +387,9 @@ DBS_DEV void coo_entries_plus(const brsrc_t pay, const brsrc_t xr, bool coo, uin
 // block: a plain store when it is one segment, an atomic add when several
 // segments share it.
 // ---------------------------------------------------------------------------
-template <int VK>
+template <int VK, bool COO_DONE = false>
 DBS_DEV void pull_finish(const SpmvParams &P, uint4 seg, uint32_t cb, uint32_t m, uint64_t meta, bool act,
-                         float *sx, float *spart, uint32_t *s_mark, int lane) {
+                         float *sx, float *spart, uint32_t *s_mark, int lane, float coo_sum = 0.0f) {
   constexpr uint64_t VS = VK == VK_F32 ? 4 : 2;
   const uint32_t rb = seg.x & ~SEG_SPLIT;
   const bool split = (seg.x & SEG_SPLIT) != 0u;
@@ -321,9 +397,9 @@ DBS_DEV void pull_finish(const SpmvParams &P, uint4 seg, uint32_t cb, uint32_t m
   const int64_t row0 = (int64_t)rb * 16;
   const brsrc_t pay = make_rsrc(P.payload, (uint64_t)P.payload_bytes + DBS_PAYLOAD_SLACK);
   const brsrc_t xr = make_rsrc(P.xd, (uint64_t)P.nb * 16 * VS);
-  float rowsum = 0.0f;
+  float rowsum = coo_sum;  // COO_DONE: the segment's COO entries were summed already
   const bool coo = act & (type == DBS_TILE_COO);
-  if (__ballot(coo) != 0ull) {
+  if (!COO_DONE && __ballot(coo) != 0ull) {
     float *s_y = spart;
     if (lane < 16) s_y[lane] = 0.0f;
     coo_entries_plus<VK>(pay, xr, coo, meta, m, cb, s_mark, s_y, lane);
@@ -388,12 +464,31 @@ DBS_DEV void plus_pull_wave(const SpmvParams &P, const PatSrc &S, const brsrc_t 
       for (int u = 0; u < U; ++u)
         cur.meta[u] = bld64(make_rsrc(S.t_meta + cur.seg[u].y, (uint64_t)cur.n[u] * 8u), m[u] != 0u ? l8 : OOB_OFF);
     }
-    // a segment with no active tile has nothing to add (y was cleared by the
-    // metadata kernel)
+    // the COO entries of all U segments first (their loads batched), then
+    // each segment's other tiles and writeback; a segment with no active
+    // tile has nothing to add (y was cleared by the metadata kernel)
+    bool coo[U];
+    uint64_t any_coo = 0ull;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      coo[u] = (m[u] != 0u) & (meta_type(cur.meta[u]) == DBS_TILE_COO);
+      any_coo |= __ballot(coo[u]);
+    }
+    float coo_sum[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) coo_sum[u] = 0.0f;
+    if (any_coo != 0ull) {  // uniform
+      coo_entries_plus_u<VK, U>(S.pay, make_rsrc(P.xd, (uint64_t)P.nb * 16 * (VK == VK_F32 ? 4 : 2)), coo, cur.meta,
+                                m, cur.cb, s_mark, spart, lane);
+#pragma unroll
+      for (int u = 0; u < U; ++u) coo_sum[u] = spart[16 * u + (lane & 15)];
+      __syncwarp();
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u)
       if ((s0 + u < S.nseg) && __ballot(m[u] != 0u) != 0ull)  // uniform
-        pull_finish<VK>(P, cur.seg[u], cur.cb[u], m[u], cur.meta[u], m[u] != 0u, sx, spart, s_mark, lane);
+        pull_finish<VK, true>(P, cur.seg[u], cur.cb[u], m[u], cur.meta[u], m[u] != 0u, sx, spart, s_mark, lane,
+                              coo_sum[u]);
     if (!more) break;
     cur = nxt;
     s0 = s1;
