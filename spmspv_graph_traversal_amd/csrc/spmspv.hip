@@ -432,8 +432,10 @@ DBS_DEV void pull_finish(const SpmvParams &P, uint4 seg, uint32_t cb, uint32_t m
 
 // ---------------------------------------------------------------------------
 // PLUS_TIMES pull: static segments of one row block each (section 3.3.2),
-// U per wave step, software-pipelined like the Boolean pull: descriptors,
-// column blocks and metadata of step i+1 are in flight while step i works.
+// U per wave step, software-pipelined in three stages like the Boolean
+// pull: while step i works, step i+1 has its mask gathers and step i+2 its
+// descriptors, column blocks and (eager) metadata in flight; step i's lazy
+// metadata is issued first in the step.
 // U = 1 when there are too few segments to give every resident wave several
 // (the decode layers), PULL_U_PLUS_WIDE otherwise.
 // ---------------------------------------------------------------------------
@@ -447,23 +449,30 @@ DBS_DEV void plus_pull_wave(const SpmvParams &P, const PatSrc &S, const brsrc_t 
   if (s0 >= S.nseg) return;
   const uint32_t l4 = (uint32_t)lane * 4u, l8 = (uint32_t)lane * 8u;
   const AllRows pol;
-  PatRound<U> cur, nxt;
-  pat_issue<U, EAGER>(S, pol, s0, true, l4, l8, cur);
-  while (true) {
-    uint32_t m[U];
+  const brsrc_t xr = make_rsrc(P.xd, (uint64_t)P.nb * 16 * (VK == VK_F32 ? 4 : 2));
+  auto masks = [&](const PatRound<U> &g, uint32_t (&m)[U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const uint32_t w = bld32(xm, (uint32_t)lane < cur.n[u] ? cur.cb[u] * 4u : OOB_OFF);
+      const uint32_t w = bld32(xm, (uint32_t)lane < g.n[u] ? g.cb[u] * 4u : OOB_OFF);
       m[u] = ((w >> 16) == P.epoch) ? (w & 0xFFFFu) : 0u;  // an idle lane reads 0: no epoch
     }
-    const int64_t s1 = s0 + stride;
-    const bool more = s1 < S.nseg;  // uniform
-    pat_issue<U, EAGER>(S, pol, more ? s1 : s0, more, l4, l8, nxt);
+  };
+  PatRound<U> g0, g1, g2;
+  uint32_t m0[U], m1[U];
+  const int64_t s1 = s0 + stride;
+  pat_issue<U, EAGER>(S, pol, s0, true, l4, l8, g0);
+  pat_issue<U, EAGER>(S, pol, s1 < S.nseg ? s1 : s0, s1 < S.nseg, l4, l8, g1);
+  masks(g0, m0);
+  while (true) {
     if constexpr (!EAGER) {
+      // metadata of this step's active tiles, before the later loads
 #pragma unroll
       for (int u = 0; u < U; ++u)
-        cur.meta[u] = bld64(make_rsrc(S.t_meta + cur.seg[u].y, (uint64_t)cur.n[u] * 8u), m[u] != 0u ? l8 : OOB_OFF);
+        g0.meta[u] = bld64(make_rsrc(S.t_meta + g0.seg[u].y, (uint64_t)g0.n[u] * 8u), m0[u] != 0u ? l8 : OOB_OFF);
     }
+    const int64_t s2 = s0 + 2 * stride;
+    pat_issue<U, EAGER>(S, pol, s2 < S.nseg ? s2 : s0, s2 < S.nseg, l4, l8, g2);
+    masks(g1, m1);
     // the COO entries of all U segments first (their loads batched), then
     // each segment's other tiles and writeback; a segment with no active
     // tile has nothing to add (y was cleared by the metadata kernel)
@@ -471,27 +480,29 @@ DBS_DEV void plus_pull_wave(const SpmvParams &P, const PatSrc &S, const brsrc_t 
     uint64_t any_coo = 0ull;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      coo[u] = (m[u] != 0u) & (meta_type(cur.meta[u]) == DBS_TILE_COO);
+      coo[u] = (m0[u] != 0u) & (meta_type(g0.meta[u]) == DBS_TILE_COO);
       any_coo |= __ballot(coo[u]);
     }
     float coo_sum[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) coo_sum[u] = 0.0f;
     if (any_coo != 0ull) {  // uniform
-      coo_entries_plus_u<VK, U>(S.pay, make_rsrc(P.xd, (uint64_t)P.nb * 16 * (VK == VK_F32 ? 4 : 2)), coo, cur.meta,
-                                m, cur.cb, s_mark, spart, lane);
+      coo_entries_plus_u<VK, U>(S.pay, xr, coo, g0.meta, m0, g0.cb, s_mark, spart, lane);
 #pragma unroll
       for (int u = 0; u < U; ++u) coo_sum[u] = spart[16 * u + (lane & 15)];
       __syncwarp();
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      if ((s0 + u < S.nseg) && __ballot(m[u] != 0u) != 0ull)  // uniform
-        pull_finish<VK, true>(P, cur.seg[u], cur.cb[u], m[u], cur.meta[u], m[u] != 0u, sx, spart, s_mark, lane,
+      if ((s0 + u < S.nseg) && __ballot(m0[u] != 0u) != 0ull)  // uniform
+        pull_finish<VK, true>(P, g0.seg[u], g0.cb[u], m0[u], g0.meta[u], m0[u] != 0u, sx, spart, s_mark, lane,
                               coo_sum[u]);
-    if (!more) break;
-    cur = nxt;
-    s0 = s1;
+    s0 += stride;
+    if (s0 >= S.nseg) break;
+    g0 = g1;
+    g1 = g2;
+#pragma unroll
+    for (int u = 0; u < U; ++u) m0[u] = m1[u];
   }
 }
 
