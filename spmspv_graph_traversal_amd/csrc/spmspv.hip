@@ -667,9 +667,11 @@ inline unsigned grid_for(int64_t waves, unsigned cap) {
 }
 
 // launch; with timing events, the dispatch itself records its start and end
+// (the extended launch costs the host more, so only then)
 template <typename K, typename... Args>
 void launch_k(K kernel, dim3 grid, dim3 block, hipStream_t s, hipEvent_t e0, hipEvent_t e1, Args... args) {
-  hipExtLaunchKernelGGL(kernel, grid, block, 0, s, e0, e1, 0, args...);
+  if (e0) hipExtLaunchKernelGGL(kernel, grid, block, 0, s, e0, e1, 0, args...);
+  else hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
 }
 
 template <int VK, int SR>
