@@ -270,23 +270,29 @@ __global__ __launch_bounds__(dbs_meta::MT) void k_bfs_meta(const uint32_t *bm, i
   });
 }
 
-// Rows without an entry start out visited: no level can reach them, and a
-// row block whose remaining rows are all such is skipped by the pull.
+// Start of a BFS in one launch: levels (0 at the source, -1 elsewhere), the
+// three frontier bitmaps cleared but for the source's bit, the visited
+// bitmap (rows without an entry start out visited: no level can reach them,
+// and a row block whose remaining rows are all such is skipped by the pull),
+// and the first frontier's metadata: one nonzero block, listed, and, when
+// level 0 pushes, the push chunks of its column block.
 __global__ void k_bfs_init(int32_t *levels, int32_t m, uint32_t *bm3, int64_t bm_words3, uint32_t *vis,
-                           const uint32_t *rows_nz, int64_t nwords, uint32_t *ctr3, int32_t src) {
+                           const uint32_t *rows_nz, int64_t nwords, uint32_t *ctr3, int32_t src,
+                           const uint32_t *cb_ptr, uint32_t *list0, uint64_t *chunks0, int64_t chunk_cap, int push0) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t gs = (int64_t)gridDim.x * blockDim.x;
+  const uint32_t b = (uint32_t)src >> 4;
+  const int64_t ws = b >> 1;
+  const uint32_t bits = (1u << ((uint32_t)src & 15u)) << ((b & 1u) * 16u);
   for (int64_t k = i; k < m; k += gs) levels[k] = k == src ? 0 : -1;
-  for (int64_t k = i; k < bm_words3; k += gs) bm3[k] = 0;
-  for (int64_t k = i; k < nwords; k += gs) vis[k] = ~rows_nz[k];
-  if (i < 24) ctr3[i] = 0;
-}
-
-__global__ void k_bfs_seed(uint32_t *bm0, uint32_t *vis, int32_t src) {
-  const uint32_t b = (uint32_t)src >> 4, bit = 1u << ((uint32_t)src & 15u);
-  const uint32_t sh = (b & 1u) * 16u;
-  bm0[b >> 1] = bit << sh;
-  vis[b >> 1] |= bit << sh;
+  for (int64_t k = i; k < bm_words3; k += gs) bm3[k] = k == ws ? bits : 0u;
+  for (int64_t k = i; k < nwords; k += gs) vis[k] = ~rows_nz[k] | (k == ws ? bits : 0u);
+  const uint32_t t = cb_ptr[b + 1] - cb_ptr[b];
+  int64_t nch = push0 ? (int64_t)((t + 63u) >> 6) : 0;
+  nch = nch < chunk_cap ? nch : chunk_cap;
+  for (int64_t k = i; k < nch; k += gs) chunks0[k] = (uint64_t)b | ((uint64_t)k << 32);
+  if (i < 24) ctr3[i] = i == 0 ? 1u : i == 1 ? (uint32_t)nch : 0u;
+  if (i == 0) list0[0] = b;
 }
 
 }  // namespace
@@ -312,9 +318,11 @@ dbs_status dbs_bfs_impl(dbs_matrix *A, int32_t src, int32_t *levels, hipStream_t
   }
   const bool timing = A->opt[DBS_OPT_TIMING] != 0;
   if (timing) BFS_TRY(hipEventRecord(A->ev[0], s));
-  hipLaunchKernelGGL(k_bfs_init, dim3(1024), dim3(256), 0, s, levels, A->m, A->bfs_bm, 3 * nwords,
-                     A->bfs_vis, (const uint32_t *)A->rows_nz, nwords, A->bfs_ctr, src);
-  hipLaunchKernelGGL(k_bfs_seed, dim3(1), dim3(1), 0, s, A->bfs_bm, A->bfs_vis, src);
+  const int64_t fp = A->opt[DBS_OPT_PATH];
+  const int push0 = fp == 1 || (fp == 0 && A->opt[DBS_OPT_TH3_DEN] < (int64_t)A->nb * A->opt[DBS_OPT_TH3_NUM]);
+  hipLaunchKernelGGL(k_bfs_init, dim3(1024), dim3(256), 0, s, levels, A->m, A->bfs_bm, 3 * nwords, A->bfs_vis,
+                     (const uint32_t *)A->rows_nz, nwords, A->bfs_ctr, src, (const uint32_t *)A->cb_ptr, A->bfs_list,
+                     A->bfs_chunks, chunk_cap, push0);
   BFS_TRY(hipGetLastError());
   const unsigned mgrid = dbs_meta::groups_for(A->nb, nwords);
   auto reg_for = [&](int buf) {
@@ -331,9 +339,6 @@ dbs_status dbs_bfs_impl(dbs_matrix *A, int32_t src, int32_t *levels, hipStream_t
     r.th3_den = A->opt[DBS_OPT_TH3_DEN];
     return r;
   };
-  hipLaunchKernelGGL(k_bfs_meta, dim3(mgrid), dim3(dbs_meta::MT), 0, s, (const uint32_t *)A->bfs_bm, A->nb, reg_for(0),
-                     (uint32_t *)nullptr, (uint32_t *)nullptr, (int64_t)0);
-  BFS_TRY(hipGetLastError());
 
   BfsParams P;
   P.t_cb = A->t_cb;
