@@ -136,6 +136,7 @@ struct SpmvParams {
   int64_t th3_num, th3_den;
   int32_t local_cutoff;
   int32_t plus_u;  // segments per wave step of the PLUS_TIMES pull (1 or PULL_U_PLUS_WIDE)
+  int32_t plus_parts;  // U = 1: waves sharing one segment (1, 2 or 4), each taking a lane range
   void *y;
 };
 
@@ -228,6 +229,7 @@ DBS_DEV void push_chunk(const SpmvParams &P, uint64_t own, float *sx, float *spa
 // once: a plain store when the row block is one segment, an atomic add when
 // several segments share it.
 constexpr int PULL_U_PLUS_WIDE = 4;  // segments per wave step, PLUS_TIMES pull with many segments
+constexpr int PLUS_MAX_PARTS = 4;    // waves sharing one PLUS_TIMES pull segment at most
 constexpr int PULL_U_OR = 8;    // segments per wave step, OR_AND pull (value matrices)
 
 // ---------------------------------------------------------------------------
@@ -387,7 +389,7 @@ DBS_DEV void coo_entries_plus_u(const brsrc_t pay, const brsrc_t xr, const bool 
 // block: a plain store when it is one segment, an atomic add when several
 // segments share it.
 // ---------------------------------------------------------------------------
-template <int VK, bool COO_DONE = false>
+template <int VK, bool COO_DONE = false, bool DENSE_PATH = true>
 DBS_DEV void pull_finish(const SpmvParams &P, uint4 seg, uint32_t cb, uint32_t m, uint64_t meta, bool act,
                          float *sx, float *spart, uint32_t *s_mark, int lane, float coo_sum = 0.0f) {
   constexpr uint64_t VS = VK == VK_F32 ? 4 : 2;
@@ -407,11 +409,18 @@ DBS_DEV void pull_finish(const SpmvParams &P, uint4 seg, uint32_t cb, uint32_t m
     __syncwarp();
   }
   // patched CSR tiles with few active columns take the column variant
-  // (section 3.3.3); the other row-major tiles go four at a time through
-  // the row-per-lane path; ForceCSC tiles one at a time
+  // (section 3.3.3); Dense tiles go four at a time through the row-broadcast
+  // path, the other row-major tiles four at a time through the row-per-lane
+  // path; ForceCSC tiles one at a time
   const uint64_t colv = __ballot(act & (type == DBS_TILE_CSR) & (__popc(m) < P.local_cutoff));
-  const uint64_t rowt = __ballot(act & (type != DBS_TILE_COO) & (type != DBS_TILE_FORCE_CSC)) & ~colv;
-  if (rowt) rowsum += quarter_merge(rows_plus<VK>(pay, xr, rowt, meta, m, cb, lane));
+  const uint64_t dent = DENSE_PATH ? __ballot(act & (type == DBS_TILE_DENSE)) : 0ull;
+  const uint64_t rowt = __ballot(act & (type != DBS_TILE_COO) & (type != DBS_TILE_FORCE_CSC)) & ~colv & ~dent;
+  if (dent | rowt) {  // uniform
+    float part = 0.0f;
+    if (dent) part = dense_plus<VK>(pay, xr, dent, meta, m, cb, lane);
+    if (rowt) part += rows_plus<VK>(pay, xr, rowt, meta, m, cb, lane);
+    rowsum += quarter_merge(part);
+  }
   uint64_t todo = __ballot(act & (type == DBS_TILE_FORCE_CSC)) | colv;
   while (todo) {
     const int src = __ffsll((unsigned long long)todo) - 1;
@@ -424,9 +433,13 @@ DBS_DEV void pull_finish(const SpmvParams &P, uint4 seg, uint32_t cb, uint32_t m
                             P.local_cutoff, lane);
     __syncwarp();
   }
-  if (lane < 16 && row0 + lane < P.m) {
-    if (!split) ((float *)P.y)[row0 + lane] = rowsum;
-    else if (rowsum != 0.0f) unsafeAtomicAdd((float *)P.y + row0 + lane, rowsum);
+  // y through a descriptor of the row block's entries (built in scalar
+  // registers; rows past m fall outside it, so their lanes store nothing)
+  const int64_t nrow = P.m - row0 < 16 ? P.m - row0 : 16;
+  const brsrc_t yr = make_rsrc((float *)P.y + row0, (uint64_t)nrow * 4);
+  if (lane < 16) {
+    if (!split) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(rowsum), yr, (uint32_t)lane * 4u, 0, 0);
+    else if (rowsum != 0.0f) __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(rowsum, yr, lane * 4, 0, 0);
   }
 }
 
@@ -445,8 +458,17 @@ struct AllRows {
 
 template <int VK, int U, bool EAGER>
 DBS_DEV void plus_pull_wave(const SpmvParams &P, const PatSrc &S, const brsrc_t xm, int64_t s0, int64_t stride,
-                            float *sx, float *spart, uint32_t *s_mark, int lane) {
-  if (s0 >= S.nseg) return;
+                            int parts, float *sx, float *spart, uint32_t *s_mark, int lane) {
+  // work items: segments (U of them per step), or with parts > 1 (U = 1)
+  // lane ranges of a segment, item = segment * parts + part
+  const int64_t nitems = S.nseg * parts;
+  if (s0 >= nitems) return;
+  auto seg_of = [&](int64_t it) { return parts == 1 ? it : it / parts; };
+  auto lanes_of = [&](int64_t it) {  // lanes (tiles) of the item's part
+    if (parts == 1) return ~0ull;
+    const int w = 64 / parts;
+    return ((1ull << w) - 1ull) << (w * (int)(it % parts));
+  };
   const uint32_t l4 = (uint32_t)lane * 4u, l8 = (uint32_t)lane * 8u;
   const AllRows pol;
   const brsrc_t xr = make_rsrc(P.xd, (uint64_t)P.nb * 16 * (VK == VK_F32 ? 4 : 2));
@@ -460,8 +482,8 @@ DBS_DEV void plus_pull_wave(const SpmvParams &P, const PatSrc &S, const brsrc_t 
   PatRound<U> g0, g1, g2;
   uint32_t m0[U], m1[U];
   const int64_t s1 = s0 + stride;
-  pat_issue<U, EAGER>(S, pol, s0, true, l4, l8, g0);
-  pat_issue<U, EAGER>(S, pol, s1 < S.nseg ? s1 : s0, s1 < S.nseg, l4, l8, g1);
+  pat_issue<U, EAGER>(S, pol, seg_of(s0), true, l4, l8, g0);
+  pat_issue<U, EAGER>(S, pol, seg_of(s1 < nitems ? s1 : s0), s1 < nitems, l4, l8, g1);
   masks(g0, m0);
   while (true) {
     if constexpr (!EAGER) {
@@ -471,8 +493,13 @@ DBS_DEV void plus_pull_wave(const SpmvParams &P, const PatSrc &S, const brsrc_t 
         g0.meta[u] = bld64(make_rsrc(S.t_meta + g0.seg[u].y, (uint64_t)g0.n[u] * 8u), m0[u] != 0u ? l8 : OOB_OFF);
     }
     const int64_t s2 = s0 + 2 * stride;
-    pat_issue<U, EAGER>(S, pol, s2 < S.nseg ? s2 : s0, s2 < S.nseg, l4, l8, g2);
+    pat_issue<U, EAGER>(S, pol, seg_of(s2 < nitems ? s2 : s0), s2 < nitems, l4, l8, g2);
     masks(g1, m1);
+    // this item's tiles; a segment shared by several waves adds its rows atomically
+    const bool mine = (lanes_of(s0) >> lane) & 1ull;
+    uint32_t ma[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) ma[u] = mine ? m0[u] : 0u;
     // the COO entries of all U segments first (their loads batched), then
     // each segment's other tiles and writeback; a segment with no active
     // tile has nothing to add (y was cleared by the metadata kernel)
@@ -480,25 +507,28 @@ DBS_DEV void plus_pull_wave(const SpmvParams &P, const PatSrc &S, const brsrc_t 
     uint64_t any_coo = 0ull;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      coo[u] = (m0[u] != 0u) & (meta_type(g0.meta[u]) == DBS_TILE_COO);
+      coo[u] = (ma[u] != 0u) & (meta_type(g0.meta[u]) == DBS_TILE_COO);
       any_coo |= __ballot(coo[u]);
     }
     float coo_sum[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) coo_sum[u] = 0.0f;
     if (any_coo != 0ull) {  // uniform
-      coo_entries_plus_u<VK, U>(S.pay, xr, coo, g0.meta, m0, g0.cb, s_mark, spart, lane);
+      coo_entries_plus_u<VK, U>(S.pay, xr, coo, g0.meta, ma, g0.cb, s_mark, spart, lane);
 #pragma unroll
       for (int u = 0; u < U; ++u) coo_sum[u] = spart[16 * u + (lane & 15)];
       __syncwarp();
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      if ((s0 + u < S.nseg) && __ballot(m0[u] != 0u) != 0ull)  // uniform
-        pull_finish<VK, true>(P, g0.seg[u], g0.cb[u], m0[u], g0.meta[u], m0[u] != 0u, sx, spart, s_mark, lane,
-                              coo_sum[u]);
+    for (int u = 0; u < U; ++u) {
+      uint4 sg = g0.seg[u];
+      if (parts > 1) sg.x |= SEG_SPLIT;
+      if ((s0 + u < nitems) && __ballot(ma[u] != 0u) != 0ull)  // uniform
+        pull_finish<VK, true, U == 1>(P, sg, g0.cb[u], ma[u], g0.meta[u], ma[u] != 0u, sx, spart, s_mark, lane,
+                                      coo_sum[u]);
+    }
     s0 += stride;
-    if (s0 >= S.nseg) break;
+    if (s0 >= nitems) break;
     g0 = g1;
     g1 = g2;
 #pragma unroll
@@ -513,8 +543,9 @@ DBS_DEV void plus_pull(const SpmvParams &P, int64_t gw, int64_t nw, bool eager, 
                  make_rsrc(P.payload, (uint64_t)P.payload_bytes + DBS_PAYLOAD_SLACK), make_rsrc(P.rb_ptr, 0),
                  make_rsrc(nullptr, 0)};
   const brsrc_t xm = make_rsrc(P.xmask, (uint64_t)P.nb * 4);
-  if (eager) plus_pull_wave<VK, U, true>(P, S, xm, gw * U, nw * U, sx, spart, s_mark, lane);
-  else plus_pull_wave<VK, U, false>(P, S, xm, gw * U, nw * U, sx, spart, s_mark, lane);
+  const int parts = U == 1 ? P.plus_parts : 1;
+  if (eager) plus_pull_wave<VK, U, true>(P, S, xm, gw * U, nw * U, parts, sx, spart, s_mark, lane);
+  else plus_pull_wave<VK, U, false>(P, S, xm, gw * U, nw * U, parts, sx, spart, s_mark, lane);
 }
 
 // OR-AND pull (the Boolean semiring of graph traversal): as pull_group, with
@@ -616,11 +647,14 @@ DBS_DEV void pull_or_group(const SpmvParams &P, const PullRes &R, int64_t s0, bo
   }
 }
 
-template <int VK, int SR>
-// the bf16 PLUS_TIMES pull (decode layers) runs five waves per SIMD in 96
-// VGPRs (12 bytes spilled) and is faster so (7% on the decode layers); the
-// others keep their own register counts
-__global__ __launch_bounds__(KT, (VK == VK_BF16 && SR == DBS_PLUS_TIMES) ? 5 : 1) void k_spmspv(SpmvParams P) {
+// PU: segments per wave step of the PLUS_TIMES pull (1 or PULL_U_PLUS_WIDE;
+// 1 for OR_AND), a kernel each so that each has its own register count.
+// The bf16 PLUS_TIMES pull with PU = 1 (the decode layers) runs five waves
+// per SIMD (at most 96 VGPRs), the wide PLUS_TIMES pull four (at most 128);
+// the others keep their own register counts.
+template <int VK, int SR, int PU>
+__global__ __launch_bounds__(KT, (VK == VK_BF16 && SR == DBS_PLUS_TIMES && PU == 1) ? 5 : PU > 1 ? 4 : 1) void k_spmspv(
+    SpmvParams P) {
   __shared__ float s_x[KT / DBS_WAVE][16];
   __shared__ float s_part[KT / DBS_WAVE][64];
   __shared__ uint32_t s_mark[KT / DBS_WAVE][64];
@@ -654,8 +688,7 @@ __global__ __launch_bounds__(KT, (VK == VK_BF16 && SR == DBS_PLUS_TIMES) ? 5 : 1
         for (int64_t s = gw * U; s < P.nseg; s += nw * U) pull_or_group<VK, U>(P, R, s, eager, lane);
       }
     } else {
-      if (P.plus_u == PULL_U_PLUS_WIDE) plus_pull<VK, PULL_U_PLUS_WIDE>(P, gw, nw, eager, s_x[w], s_part[w], s_mark[w], lane);
-      else plus_pull<VK, 1>(P, gw, nw, eager, s_x[w], s_part[w], s_mark[w], lane);
+      plus_pull<VK, PU>(P, gw, nw, eager, s_x[w], s_part[w], s_mark[w], lane);
     }
   }
 }
@@ -674,10 +707,19 @@ void launch_k(K kernel, dim3 grid, dim3 block, hipStream_t s, hipEvent_t e0, hip
   else hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
 }
 
-template <int VK, int SR>
-void launch_spmspv(const SpmvParams &P, int64_t waves, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  static const unsigned resident = dbs_resident_groups(k_spmspv<VK, SR>, KT);
-  launch_k(k_spmspv<VK, SR>, dim3(grid_for(waves, resident)), dim3(KT), s, e0, e1, P);
+template <int VK, int SR, int PU = 1>
+void launch_spmspv(SpmvParams P, int64_t waves, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  static const unsigned resident = dbs_resident_groups(k_spmspv<VK, SR, PU>, KT);
+  P.plus_parts = 1;
+  if (SR == DBS_PLUS_TIMES && PU == 1 && P.nseg > 0) {
+    // fewer segments than resident waves: waves share segments by lane
+    // range, so that every resident wave has work
+    const int64_t rw = (int64_t)resident * (KT / DBS_WAVE);
+    const int64_t parts = (rw + P.nseg - 1) / P.nseg;
+    P.plus_parts = parts >= PLUS_MAX_PARTS ? PLUS_MAX_PARTS : parts >= 2 ? 2 : 1;
+    if (P.nseg * P.plus_parts > waves) waves = P.nseg * P.plus_parts;
+  }
+  launch_k(k_spmspv<VK, SR, PU>, dim3(grid_for(waves, resident)), dim3(KT), s, e0, e1, P);
 }
 
 }  // namespace
@@ -801,8 +843,14 @@ dbs_status dbs_spmspv_impl(dbs_matrix *A, int32_t nnz_x, const int32_t *x_idx, c
     else if (vk == VK_BF16) launch_spmspv<VK_BF16, DBS_OR_AND>(P, waves, s, c0, c1);
     else launch_spmspv<VK_PAT, DBS_OR_AND>(P, waves, s, c0, c1);
   } else {
-    if (vk == VK_F32) launch_spmspv<VK_F32, DBS_PLUS_TIMES>(P, waves, s, c0, c1);
-    else launch_spmspv<VK_BF16, DBS_PLUS_TIMES>(P, waves, s, c0, c1);
+    const bool wide = P.plus_u == PULL_U_PLUS_WIDE;
+    if (vk == VK_F32) {
+      if (wide) launch_spmspv<VK_F32, DBS_PLUS_TIMES, PULL_U_PLUS_WIDE>(P, waves, s, c0, c1);
+      else launch_spmspv<VK_F32, DBS_PLUS_TIMES, 1>(P, waves, s, c0, c1);
+    } else {
+      if (wide) launch_spmspv<VK_BF16, DBS_PLUS_TIMES, PULL_U_PLUS_WIDE>(P, waves, s, c0, c1);
+      else launch_spmspv<VK_BF16, DBS_PLUS_TIMES, 1>(P, waves, s, c0, c1);
+    }
   }
   SPMV_TRY(hipGetLastError());
   A->cbuf ^= 1;

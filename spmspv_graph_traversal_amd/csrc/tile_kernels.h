@@ -444,82 +444,285 @@ DBS_DEV uint32_t lane_coo_or(const uint8_t *payload, uint64_t meta, uint32_t m, 
 // the last value; `xr` covers the block-padded x.  Returns lane (q, r)'s
 // partial for row r, to be summed over the quarters.
 // ---------------------------------------------------------------------------
+// One step's four tiles: this lane's tile (lane of the segment, wave-uniform
+// per quarter), its metadata, and the row mask and x entry in flight.
+struct RowsStep {
+  uint32_t mk, c, vp, tyn;  // active columns, column block, payload offset, type | nnz << 8
+  uint32_t rmk;             // row mask (Dense: loaded as 0, all 16 later)
+  uint32_t xw;              // raw x entry of column r
+  bool valid;
+};
+
+// first stage: take the next four tiles of `todo` and issue their row-mask
+// and x loads (used only by later stages, so they stay in flight)
 template <int VK>
-DBS_DEV float rows_plus(brsrc_t pay, brsrc_t xr, uint64_t todo, uint64_t meta, uint32_t m, uint32_t cb, int lane) {
+DBS_DEV RowsStep rows_issue(brsrc_t pay, brsrc_t xr, uint64_t &todo, uint64_t meta, uint32_t m, uint32_t cb,
+                            uint32_t q, uint32_t r) {
+  int l[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    l[k] = todo ? __ffsll((unsigned long long)todo) - 1 : -1;
+    todo &= todo - 1;
+  }
+  const int src = q == 0 ? l[0] : q == 1 ? l[1] : q == 2 ? l[2] : l[3];
+  RowsStep t;
+  t.valid = src >= 0;
+  const int sl = t.valid ? src : 0;
+  const uint64_t mt = (uint64_t)(uint32_t)__shfl((int)(uint32_t)meta, sl) |
+                      ((uint64_t)(uint32_t)__shfl((int)(uint32_t)(meta >> 32), sl) << 32);
+  // every lane takes part in each shuffle (a lane outside EXEC reads as 0
+  // to the others), the mask is applied afterwards
+  const uint32_t mall = (uint32_t)__shfl((int)m, sl);
+  t.mk = t.valid ? mall : 0u;
+  t.c = (uint32_t)__shfl((int)cb, sl);
+  t.vp = (uint32_t)meta_vp(mt);
+  const uint32_t ty = meta_type(mt);
+  t.tyn = ty | (meta_nnz(mt) << 8);
+  const bool dn = ty == DBS_TILE_DENSE;
+  t.rmk = __builtin_amdgcn_raw_buffer_load_b16(pay, (t.valid & !dn) ? t.vp + 2u * r : OOB_OFF, 0, 0);
+  if (VK == VK_F32) t.xw = __builtin_amdgcn_raw_buffer_load_b32(xr, t.valid ? (t.c * 16u + r) * 4u : OOB_OFF, 0, 0);
+  else t.xw = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(xr, t.valid ? (t.c * 16u + r) * 2u : OOB_OFF, 0, 0);
+  return t;
+}
+
+// values of this lane's row, raw: 16 dwords (fp32) or 9 dwords holding the
+// row's bf16 values from a dword boundary
+template <int VK>
+struct RowVals {
+  uint32_t w[VK == VK_F32 ? 16 : 9];
+};
+
+// second stage: the row mask is in; derive the row's value offset (the
+// quarter's prefix sum of row counts) and issue the value loads
+template <int VK>
+DBS_DEV RowVals<VK> rows_values(brsrc_t pay, RowsStep &t, uint32_t r) {
   constexpr uint32_t VS = VK == VK_F32 ? 4u : 2u;
+  const uint32_t ty = t.tyn & 0xFFu;
+  const bool dn = ty == DBS_TILE_DENSE;
+  t.rmk = (t.valid & dn) ? 0xFFFFu : t.rmk;
+  const uint32_t cnt = (uint32_t)__popc(t.rmk);
+  const uint32_t rp = quarter_incl_scan(cnt) - cnt;
+  const uint32_t vbase = ty == DBS_TILE_CSR ? csr_val_off(t.tyn >> 8) : (uint32_t)PL_FORCE_VAL;
+  const uint32_t voff = dn ? t.vp + r * 16u * VS : t.vp + vbase + rp * VS;
+  const uint32_t lo = cnt ? (voff & ~3u) : OOB_OFF;
+  t.vp = voff;  // from here on: the row's value offset (its parity picks the bf16 half)
+  RowVals<VK> v;
+  if (VK == VK_F32) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const auto w = __builtin_amdgcn_raw_buffer_load_b128(pay, cnt ? lo + 16u * j : OOB_OFF, 0, 0);
+      v.w[4 * j] = w[0];
+      v.w[4 * j + 1] = w[1];
+      v.w[4 * j + 2] = w[2];
+      v.w[4 * j + 3] = w[3];
+    }
+  } else {
+    const auto wa = __builtin_amdgcn_raw_buffer_load_b128(pay, lo, 0, 0);
+    const auto wb = __builtin_amdgcn_raw_buffer_load_b128(pay, cnt ? lo + 16u : OOB_OFF, 0, 0);
+    v.w[0] = wa[0];
+    v.w[1] = wa[1];
+    v.w[2] = wa[2];
+    v.w[3] = wa[3];
+    v.w[4] = wb[0];
+    v.w[5] = wb[1];
+    v.w[6] = wb[2];
+    v.w[7] = wb[3];
+    v.w[8] = __builtin_amdgcn_raw_buffer_load_b32(pay, cnt ? lo + 32u : OOB_OFF, 0, 0);
+  }
+  return v;
+}
+
+// last stage: products over the row's stored columns, in order; the x value
+// of a column comes from the lane of the quarter that holds it.  Entries go
+// four at a time with fixed register indices (their gathers batched); a
+// lane's entries past its row's count add nothing.
+template <int VK, int K0>
+DBS_DEV void rows_chunk(const RowVals<VK> &vw, uint32_t sh, float xt, uint32_t qb, uint32_t cnt, uint32_t &rest,
+                        float &part) {
+  float v[4];
+  if (VK == VK_F32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(vw.w[K0 + i]);
+  } else {
+    // the row's entries K0..K0+3 from a dword boundary (sh = 16: the row
+    // starts in the upper half of a dword)
+    const uint32_t u0 = __builtin_amdgcn_alignbit(vw.w[K0 / 2 + 1], vw.w[K0 / 2], sh);
+    const uint32_t u1 = __builtin_amdgcn_alignbit(vw.w[K0 / 2 + 2], vw.w[K0 / 2 + 1], sh);
+    v[0] = __uint_as_float(u0 << 16);
+    v[1] = __uint_as_float(u0 & 0xFFFF0000u);
+    v[2] = __uint_as_float(u1 << 16);
+    v[3] = __uint_as_float(u1 & 0xFFFF0000u);
+  }
+  uint32_t a[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[i] = (qb | ((uint32_t)(__ffs(rest) - 1) & 15u)) << 2;
+    rest &= rest - 1u;
+  }
+  float xv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) xv[i] = __int_as_float(__builtin_amdgcn_ds_bpermute((int)a[i], __float_as_int(xt)));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float pv = part + v[i] * xv[i];
+    part = (K0 + i < (int)cnt) ? pv : part;
+  }
+}
+
+template <int VK>
+DBS_DEV float rows_products(const RowsStep &t, const RowVals<VK> &vw, uint32_t q, uint32_t r, float part) {
+  float xt = VK == VK_F32 ? __uint_as_float(t.xw) : __uint_as_float(t.xw << 16);
+  xt = ((t.mk >> r) & 1u) ? xt : 0.0f;
+  const uint32_t cnt = (uint32_t)__popc(t.rmk);
+  const uint32_t kmax = wave_max(cnt);
+  const uint32_t sh = (t.vp & 2u) ? 16u : 0u;
+  const uint32_t qb = q << 4;
+  uint32_t rest = t.rmk;
+  if (kmax > 0u) rows_chunk<VK, 0>(vw, sh, xt, qb, cnt, rest, part);  // uniform
+  if (kmax > 4u) rows_chunk<VK, 4>(vw, sh, xt, qb, cnt, rest, part);
+  if (kmax > 8u) rows_chunk<VK, 8>(vw, sh, xt, qb, cnt, rest, part);
+  if (kmax > 12u) rows_chunk<VK, 12>(vw, sh, xt, qb, cnt, rest, part);
+  return part;
+}
+
+// ---------------------------------------------------------------------------
+// PLUS_TIMES over Dense tiles, four per step like rows_plus: lane (q, r)
+// reads row r of its quarter's tile (16 values, zeros where the tile holds
+// none) and takes column k's x from lane (q, k) by a row broadcast (DPP
+// row_newbcast); bf16 values go in pairs through the bf16 dot product, x
+// pairs held by lanes (q, 0..7).  No row mask and no prefix sum: a step is
+// one round of loads.
+// ---------------------------------------------------------------------------
+template <int VK>
+struct DenseStep {
+  uint32_t mk;   // active columns of the lane's tile (0: no tile)
+  uint32_t xw;   // bf16: x pair of columns 2(r&7), 2(r&7)+1; fp32: x of column r
+  uint32_t w[VK == VK_F32 ? 16 : 8];
+};
+
+template <int VK>
+DBS_DEV DenseStep<VK> dense_issue(brsrc_t pay, brsrc_t xr, uint64_t &todo, uint64_t meta, uint32_t m, uint32_t cb,
+                                  uint32_t q, uint32_t r) {
+  int l[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    l[k] = todo ? __ffsll((unsigned long long)todo) - 1 : -1;
+    todo &= todo - 1;
+  }
+  const int src = q == 0 ? l[0] : q == 1 ? l[1] : q == 2 ? l[2] : l[3];
+  const bool valid = src >= 0;
+  const int sl = valid ? src : 0;
+  const uint64_t mt = (uint64_t)(uint32_t)__shfl((int)(uint32_t)meta, sl) |
+                      ((uint64_t)(uint32_t)__shfl((int)(uint32_t)(meta >> 32), sl) << 32);
+  const uint32_t mall = (uint32_t)__shfl((int)m, sl);
+  const uint32_t c = (uint32_t)__shfl((int)cb, sl);
+  DenseStep<VK> t;
+  t.mk = valid ? mall : 0u;
+  const uint32_t vp = (uint32_t)meta_vp(mt);
+  if (VK == VK_F32) {
+    t.xw = __builtin_amdgcn_raw_buffer_load_b32(xr, valid ? (c * 16u + r) * 4u : OOB_OFF, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const auto w = __builtin_amdgcn_raw_buffer_load_b128(pay, valid ? vp + r * 64u + 16u * j : OOB_OFF, 0, 0);
+      t.w[4 * j] = w[0];
+      t.w[4 * j + 1] = w[1];
+      t.w[4 * j + 2] = w[2];
+      t.w[4 * j + 3] = w[3];
+    }
+  } else {
+    t.xw = __builtin_amdgcn_raw_buffer_load_b32(xr, valid ? (c * 16u + 2u * (r & 7u)) * 2u : OOB_OFF, 0, 0);
+    const auto wa = __builtin_amdgcn_raw_buffer_load_b128(pay, valid ? vp + r * 32u : OOB_OFF, 0, 0);
+    const auto wb = __builtin_amdgcn_raw_buffer_load_b128(pay, valid ? vp + r * 32u + 16u : OOB_OFF, 0, 0);
+    t.w[0] = wa[0];
+    t.w[1] = wa[1];
+    t.w[2] = wa[2];
+    t.w[3] = wa[3];
+    t.w[4] = wb[0];
+    t.w[5] = wb[1];
+    t.w[6] = wb[2];
+    t.w[7] = wb[3];
+  }
+  return t;
+}
+
+// lane (q, K)'s value to every lane of quarter q
+template <int K>
+DBS_DEV uint32_t quarter_bcast(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x150 + K, 0xF, 0xF, true);
+}
+
+typedef __bf16 dbs_bf16x2 __attribute__((ext_vector_type(2)));
+
+template <int VK, int K = 0>
+DBS_DEV float dense_dot(const uint32_t (&w)[VK == VK_F32 ? 16 : 8], uint32_t xm, float part) {
+  if constexpr (K < (VK == VK_F32 ? 16 : 8)) {
+    const uint32_t xb = quarter_bcast<K>(xm);
+    if constexpr (VK == VK_F32) {
+      part = fmaf(__uint_as_float(w[K]), __uint_as_float(xb), part);
+    } else {
+      part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(dbs_bf16x2, w[K]), __builtin_bit_cast(dbs_bf16x2, xb),
+                                             part, false);
+    }
+    return dense_dot<VK, K + 1>(w, xm, part);
+  } else {
+    return part;
+  }
+}
+
+template <int VK>
+DBS_DEV float dense_products(const DenseStep<VK> &t, uint32_t r, float part) {
+  uint32_t xm;
+  if (VK == VK_F32) {
+    xm = ((t.mk >> r) & 1u) ? t.xw : 0u;
+  } else {
+    const uint32_t m2 = t.mk >> (2u * (r & 7u));
+    xm = t.xw & (((m2 & 1u) ? 0x0000FFFFu : 0u) | ((m2 & 2u) ? 0xFFFF0000u : 0u));
+  }
+  return dense_dot<VK>(t.w, xm, part);
+}
+
+template <int VK>
+DBS_DEV float dense_plus(brsrc_t pay, brsrc_t xr, uint64_t todo, uint64_t meta, uint32_t m, uint32_t cb, int lane) {
   const uint32_t q = (uint32_t)lane >> 4, r = (uint32_t)lane & 15u;
   float part = 0.0f;
-  while (todo) {
-    // lanes holding the next four tiles (wave-uniform), then the one of this quarter
-    int l[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      l[k] = todo ? __ffsll((unsigned long long)todo) - 1 : -1;
-      todo &= todo - 1;
-    }
-    const int src = q == 0 ? l[0] : q == 1 ? l[1] : q == 2 ? l[2] : l[3];
-    const bool valid = src >= 0;
-    const int sl = valid ? src : 0;
-    const uint64_t mt = (uint64_t)(uint32_t)__shfl((int)(uint32_t)meta, sl) |
-                        ((uint64_t)(uint32_t)__shfl((int)(uint32_t)(meta >> 32), sl) << 32);
-    // every lane takes part in each shuffle (a lane outside EXEC reads as 0
-    // to the others), the mask is applied afterwards
-    const uint32_t mall = (uint32_t)__shfl((int)m, sl);
-    const uint32_t mk = valid ? mall : 0u;
-    const uint32_t c = (uint32_t)__shfl((int)cb, sl);
-    const uint32_t ty = meta_type(mt), vp = (uint32_t)meta_vp(mt);
-    const bool dn = ty == DBS_TILE_DENSE;
-    // phase 1: row mask and x
-    uint32_t rmk = __builtin_amdgcn_raw_buffer_load_b16(pay, (valid & !dn) ? vp + 2u * r : OOB_OFF, 0, 0);
-    rmk = (valid & dn) ? 0xFFFFu : rmk;
-    float xt;
-    if (VK == VK_F32) {
-      xt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(xr, valid ? (c * 16u + r) * 4u : OOB_OFF, 0, 0));
-    } else {
-      xt = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(xr, valid ? (c * 16u + r) * 2u : OOB_OFF, 0, 0)
-                           << 16);
-    }
-    xt = ((mk >> r) & 1u) ? xt : 0.0f;
-    // phase 2: the row's values
-    const uint32_t cnt = (uint32_t)__popc(rmk);
-    const uint32_t rp = quarter_incl_scan(cnt) - cnt;
-    const uint32_t vbase = ty == DBS_TILE_CSR ? csr_val_off(meta_nnz(mt)) : (uint32_t)PL_FORCE_VAL;
-    const uint32_t voff = dn ? vp + r * 16u * VS : vp + vbase + rp * VS;
-    const uint32_t lo = cnt ? (voff & ~3u) : OOB_OFF;
-    float v[16];
-    if (VK == VK_F32) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const auto w = __builtin_amdgcn_raw_buffer_load_b128(pay, cnt ? lo + 16u * j : OOB_OFF, 0, 0);
-        v[4 * j] = __uint_as_float(w[0]);
-        v[4 * j + 1] = __uint_as_float(w[1]);
-        v[4 * j + 2] = __uint_as_float(w[2]);
-        v[4 * j + 3] = __uint_as_float(w[3]);
-      }
-    } else {
-      const auto wa = __builtin_amdgcn_raw_buffer_load_b128(pay, lo, 0, 0);
-      const auto wb = __builtin_amdgcn_raw_buffer_load_b128(pay, cnt ? lo + 16u : OOB_OFF, 0, 0);
-      const uint32_t wc = __builtin_amdgcn_raw_buffer_load_b32(pay, cnt ? lo + 32u : OOB_OFF, 0, 0);
-      const uint32_t w[9] = {wa[0], wa[1], wa[2], wa[3], wb[0], wb[1], wb[2], wb[3], wc};
-      const bool odd = (voff & 2u) != 0u;  // the row starts in the upper half of a dword
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t u = odd ? __builtin_amdgcn_alignbit(w[j + 1], w[j], 16) : w[j];
-        v[2 * j] = __uint_as_float(u << 16);
-        v[2 * j + 1] = __uint_as_float(u & 0xFFFF0000u);
-      }
-    }
-    // products over the row's stored columns, in order
-    const uint32_t kmax = wave_max(cnt);
-    uint32_t rest = rmk;
-#pragma unroll
-    for (uint32_t k = 0; k < 16; ++k) {
-      if (k >= kmax) break;  // uniform
-      const uint32_t col = (uint32_t)(__ffs(rest) - 1) & 15u;
-      rest &= rest - 1u;
-      const float xv = __shfl(xt, (int)((q << 4) | col));
-      if (k < cnt) part += v[k] * xv;
-    }
+  // step b's loads are in flight while step a's products run (a and b
+  // alternate; the next step is issued even when no tile remains, so that
+  // the wait for a step does not wait for the one after it)
+  DenseStep<VK> a = dense_issue<VK>(pay, xr, todo, meta, m, cb, q, r);
+  while (true) {
+    const bool more_b = todo != 0ull;  // uniform
+    const DenseStep<VK> b = dense_issue<VK>(pay, xr, todo, meta, m, cb, q, r);
+    part = dense_products<VK>(a, r, part);
+    if (!more_b) break;
+    const bool more_a = todo != 0ull;
+    a = dense_issue<VK>(pay, xr, todo, meta, m, cb, q, r);
+    part = dense_products<VK>(b, r, part);
+    if (!more_a) break;
+  }
+  return part;
+}
+
+template <int VK>
+DBS_DEV float rows_plus(brsrc_t pay, brsrc_t xr, uint64_t todo, uint64_t meta, uint32_t m, uint32_t cb, int lane) {
+  const uint32_t q = (uint32_t)lane >> 4, r = (uint32_t)lane & 15u;
+  float part = 0.0f;
+  // two steps in flight: while step a's values load and its products run,
+  // step b's row masks and x entries are on their way (a and b alternate,
+  // so that no in-flight register is copied).  The next step is issued
+  // whether or not tiles remain (then with every lane out of range), so
+  // that the waits for a step's values do not also wait for it.
+  RowsStep a = rows_issue<VK>(pay, xr, todo, meta, m, cb, q, r);
+  while (true) {
+    const RowVals<VK> va = rows_values<VK>(pay, a, r);
+    const bool more_b = todo != 0ull;  // uniform
+    RowsStep b = rows_issue<VK>(pay, xr, todo, meta, m, cb, q, r);
+    part = rows_products<VK>(a, va, q, r, part);
+    if (!more_b) break;
+    const RowVals<VK> vb = rows_values<VK>(pay, b, r);
+    const bool more_a = todo != 0ull;
+    a = rows_issue<VK>(pay, xr, todo, meta, m, cb, q, r);
+    part = rows_products<VK>(b, vb, q, r, part);
+    if (!more_a) break;
   }
   return part;
 }
