@@ -218,6 +218,25 @@ int orc_spmspv_dense_x(int32_t m, int32_t n, const int32_t *row_ptr, const int32
   return 0;
 }
 
+/*
+ * Activation sparsification by magnitude thresholding (the decoding
+ * evaluation of section 5.4: activation sparsity from magnitude-based
+ * thresholding, after the training-free activation-sparsity reference):
+ * x'_j = x_j when |x_j| > t, else +0.  The comparison is exact (|x_j| and t
+ * are both exactly representable in double); a NaN entry compares false and
+ * becomes 0.  x and out are of the same value kind (float32 or bf16 bits).
+ */
+int orc_threshold_activation(int32_t n, const void *x, int xkind, float t, void *out) {
+  if (xkind != ORC_F32 && xkind != ORC_BF16) return 1;
+  for (int32_t j = 0; j < n; ++j) {
+    const double a = fabs(orc_load(x, xkind, j));
+    const int keep = a > (double)t;
+    if (xkind == ORC_F32) ((float *)out)[j] = keep ? ((const float *)x)[j] : 0.0f;
+    else ((uint16_t *)out)[j] = keep ? ((const uint16_t *)x)[j] : (uint16_t)0;
+  }
+  return 0;
+}
+
 /* ------------------------------------------------------------------------
  * Vector-block metadata (section 3.2.2, section 4.1): blk_x_mask[b] has bit k
  * set iff element 16b+k is active; N_nzblk counts the blocks with a nonzero

@@ -52,6 +52,7 @@ def _load():
             "orc_masked_or_and": (C.c_int, [i32, i32, vp, vp, i32, vp, vp, vp]),
             "orc_bfs": (C.c_int, [i32, vp, vp, i32, vp]),
             "orc_spmspv_dense_x": (C.c_int, [i32, i32, vp, vp, vp, C.c_int, vp, C.c_int, vp, vp]),
+            "orc_threshold_activation": (C.c_int, [i32, vp, C.c_int, C.c_float, vp]),
             "orc_xmeta": (C.c_int, [i32, i32, vp, vp, vp]),
             "orc_xmeta_dense": (C.c_int, [i32, vp, C.c_int, vp, vp]),
             "orc_select_push": (C.c_int, [i32, i32, dbl]),
@@ -170,6 +171,18 @@ def spmspv_dense_x(m, n, row_ptr, col_idx, val, kind, x, xkind):
     _check(lib.orc_spmspv_dense_x(m, n, _p(row_ptr), _p(col_idx), _p(v), kind, _p(xx), xkind,
                                   _p(y), _p(s)), "spmspv_dense_x")
     return y, s
+
+
+def threshold_activation(x, xkind, t):
+    """x' with x'_j = x_j if |x_j| > t else 0 (magnitude thresholding of a
+    dense activation, the decoding evaluation's activation sparsity); x of
+    the value kind xkind (float32 array, or uint16 bf16 bits); t a float32."""
+    lib = _load()
+    xx = np.ascontiguousarray(x, dtype=np.float32 if xkind == F32 else np.uint16)
+    out = np.empty_like(xx)
+    _check(lib.orc_threshold_activation(xx.shape[0], _p(xx), xkind, float(np.float32(t)), _p(out)),
+           "threshold_activation")
+    return out
 
 
 # ------------------------------------------------------------------ metadata

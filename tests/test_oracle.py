@@ -191,6 +191,40 @@ def test_dense_x_matches_dense_product_and_signed_zero_inactive():
     assert cnt == int(np.count_nonzero(masks))
 
 
+def test_threshold_activation_worked_example():
+    # magnitude thresholding worked by hand at t = 0.5: kept iff |x| > t
+    # (0.5 itself and -0.0 drop, -0.6 and just-above -0.5 stay, NaN drops)
+    x = np.array([0.4, -0.6, 0.5, 2.0, -0.0, np.nan, -0.5000001, 0.0], np.float32)
+    out = orc.threshold_activation(x, orc.F32, 0.5)
+    exp = np.array([0.0, -0.6, 0.0, 2.0, 0.0, 0.0, -0.5000001, 0.0], np.float32)
+    assert np.array_equal(out.view(np.uint32), exp.view(np.uint32))  # dropped entries are +0
+    # bf16: 0x3ED0 = 0.40625, 0xBF1A = -0.6015625, 0x3F00 = 0.5, 0x4000 = 2.0, 0x8000 = -0.0
+    xb = np.array([0x3ED0, 0xBF1A, 0x3F00, 0x4000, 0x8000], np.uint16)
+    assert orc.threshold_activation(xb, orc.BF16, 0.5).tolist() == [0, 0xBF1A, 0, 0x4000, 0]
+    # the comparison is against the float32 threshold, exactly: t = 0.40625 drops 0.40625
+    assert orc.threshold_activation(xb, orc.BF16, 0.40625).tolist() == [0, 0xBF1A, 0x3F00, 0x4000, 0]
+
+
+def test_threshold_activation_special_cases_and_decode():
+    rng = rng_for("test", 31)
+    x = rng.normal(0.0, 1.0, 300).astype(np.float32)
+    x[::17] = 0.0
+    # t = 0 keeps exactly the nonzeros (the plain dense decode rule)
+    assert np.array_equal(orc.threshold_activation(x, orc.F32, 0.0), np.where(x != 0, x, 0).astype(np.float32))
+    # t at or above max |x| keeps nothing; counts fall as t grows
+    assert not orc.threshold_activation(x, orc.F32, float(np.abs(x).max())).any()
+    counts = [np.count_nonzero(orc.threshold_activation(x, orc.F32, t)) for t in (0.0, 0.3, 1.0, 2.0)]
+    assert counts == sorted(counts, reverse=True) and counts[0] > counts[-1]
+    # decode with the sparsified activation: the dense product over the kept entries
+    a = _rand_sparse_dense(rng, 40, 300, 0.5)
+    rp, ci, v = csr_from_dense(a)
+    xs = orc.threshold_activation(x, orc.F32, 1.0)
+    keep = np.abs(x.astype(np.float64)) > 1.0
+    y, _ = orc.spmspv_dense_x(40, 300, rp, ci, v, orc.F32, xs, orc.F32)
+    np.testing.assert_allclose(y, a.astype(np.float64)[:, keep] @ x.astype(np.float64)[keep], rtol=1e-12,
+                               atol=1e-13)
+
+
 def test_xmeta_bit_order_figure5_caption():
     # Figure 5 caption: a mask value of 10 = 0b1010 marks local positions 1 and 3
     masks, cnt = orc.xmeta(32, np.array([1, 3], np.int32))
