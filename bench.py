@@ -376,8 +376,47 @@ def bench_decode(dbs, torch, args):
                             "GBps_rotating": round((mb + cb) / (cold_us * 1e-6) / 1e9, 1),
                             "tiles_by_format": st["tiles_by_format"]})
                 log(f"[bench] decode {rows}x{cols} s={sp} z={z}: warm {warm_us:.2f} us, rotating {cold_us:.2f} us")
+            if sp == 0.5:
+                out.append(bench_decode_threshold(dbs, torch, args, copies[0], fmt, rows, cols, y))
             del copies
     return out
+
+
+def bench_decode_threshold(dbs, torch, args, A, fmt, rows, cols, y):
+    """Fused activation sparsification: a dense bf16 activation without zeros,
+    thresholded by magnitude inside the metadata kernel so that ~10% of it
+    stays active (the activation density of the decoding evaluation)."""
+    from synth import decode_activation, rng_for
+
+    x = decode_activation(cols, 0.0, rng_for("decode", rows, 99))
+    xf = np.abs((x.astype(np.uint32) << 16).view(np.float32))
+    t = float(np.float32(np.quantile(xf, 0.9)))
+    kept = np.nonzero(xf > t)[0]
+    xd = torch.from_numpy(x.view(np.int16)).to(y.device)
+    mb, cb = fmt.call_bytes(np.unique(kept // 16), 0, 4 * rows, False)
+    mb += 2 * cols
+    for _ in range(args.warmup):
+        dbs.dbs_spmspv_dense_threshold(A, xd, t, dbs.DBS_PLUS_TIMES, y)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(args.steps):
+        dbs.dbs_spmspv_dense_threshold(A, xd, t, dbs.DBS_PLUS_TIMES, y)
+    ev1.record()
+    torch.cuda.synchronize()
+    warm_us = ev0.elapsed_time(ev1) / args.steps * 1e3
+    dbs.dbs_set_option(A, dbs.DBS_OPT_TIMING, 1)
+    for _ in range(args.steps):
+        dbs.dbs_spmspv_dense_threshold(A, xd, t, dbs.DBS_PLUS_TIMES, y)
+    s2 = dbs.dbs_get_stats(A)
+    dbs.dbs_set_option(A, dbs.DBS_OPT_TIMING, 0)
+    log(f"[bench] decode {rows}x{cols} s=0.5 fused threshold (10% kept): warm {warm_us:.2f} us")
+    return {"shape": [rows, cols], "weight_sparsity": 0.5, "activation": "dense, |x| > t keeps 10%",
+            "threshold": t, "kept": int(kept.shape[0]), "path": "push" if s2["last_path"] == 0 else "pull",
+            "xb_ratio": round(s2["last_n_nzblk"] / fmt.nb, 4), "us_warm": round(warm_us, 2),
+            "compute_kernel_us_warm": round(s2["sum_compute_ms"] / s2["timed_calls"] * 1e3, 2),
+            "meta_kernel_us_warm": round(s2["sum_meta_ms"] / s2["timed_calls"] * 1e3, 2),
+            "bytes": int(mb + cb), "GBps_warm": round((mb + cb) / (warm_us * 1e-6) / 1e9, 1)}
 
 
 ZIPF_DENSITIES = [1e-5, 1e-4, 1e-3, 1e-2, 5e-2, 0.2]

@@ -150,6 +150,22 @@ dbs_status dbs_spmspv_dense(dbs_handle A, const void *x, dbs_semiring sr, void *
                             void *stream);
 
 /*
+ * dbs_spmspv_dense_threshold — decode with the activation sparsified in the
+ * metadata kernel: y = A x' with x'_j = x_j when |x_j| > threshold, else 0
+ * (magnitude thresholding, the activation sparsity of the decoding
+ * evaluation, section 5.4).  The masks (section 4.1) come from x' and the
+ * multiply reads x' only; x itself is not written.  threshold = 0 gives
+ * dbs_spmspv_dense, except that a NaN entry of x is dropped here (every
+ * comparison with NaN is false).
+ *
+ *   x          as for dbs_spmspv_dense
+ *   threshold  finite and >= 0, else DBS_ERR_INVALID_ARG
+ *   y          as for dbs_spmspv
+ */
+dbs_status dbs_spmspv_dense_threshold(dbs_handle A, const void *x, float threshold, dbs_semiring sr,
+                                      void *y, void *stream);
+
+/*
  * dbs_bfs — single-source BFS levels (section 4.2, Algorithm 5).  Each level
  * is one masked OR_AND SpMSpV y = A f with the frontier f as the sparse
  * vector; push or pull is chosen per level from the frontier's nonzero-block

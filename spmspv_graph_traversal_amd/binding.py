@@ -59,7 +59,8 @@ class dbs_stats(C.Structure):
     ]
 
 
-EXPORTED = ["dbs_build_options_default", "dbs_build", "dbs_spmspv", "dbs_spmspv_dense", "dbs_bfs",
+EXPORTED = ["dbs_build_options_default", "dbs_build", "dbs_spmspv", "dbs_spmspv_dense",
+            "dbs_spmspv_dense_threshold", "dbs_bfs",
             "dbs_set_option", "dbs_get_option", "dbs_get_stats", "dbs_copy_array", "dbs_free",
             "dbs_status_string"]
 
@@ -82,6 +83,7 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
                       C.POINTER(vp)],
         "dbs_spmspv": [vp, i32, vp, vp, C.c_int, vp, vp],
         "dbs_spmspv_dense": [vp, vp, C.c_int, vp, vp],
+        "dbs_spmspv_dense_threshold": [vp, vp, C.c_float, C.c_int, vp, vp],
         "dbs_bfs": [vp, i32, vp, vp],
         "dbs_set_option": [vp, i32, i64],
         "dbs_get_option": [vp, i32, C.POINTER(i64)],
@@ -208,6 +210,16 @@ def dbs_spmspv_dense(A: Matrix, x, semiring, y, stream=None) -> None:
     _need(y, "y", (torch.float32,) if semiring == DBS_PLUS_TIMES else (torch.uint8,), A.m)
     _check(_lib.dbs_spmspv_dense(A.handle, _ptr(x), int(semiring), _ptr(y), _stream(stream)),
            "dbs_spmspv_dense")
+
+
+def dbs_spmspv_dense_threshold(A: Matrix, x, threshold: float, semiring, y, stream=None) -> None:
+    import torch
+
+    xd = _value_dtypes(A.dtype) if A.dtype != DBS_PATTERN else (torch.float32,)
+    _need(x, "x", xd, A.n)
+    _need(y, "y", (torch.float32,) if semiring == DBS_PLUS_TIMES else (torch.uint8,), A.m)
+    _check(_lib.dbs_spmspv_dense_threshold(A.handle, _ptr(x), float(threshold), int(semiring), _ptr(y),
+                                           _stream(stream)), "dbs_spmspv_dense_threshold")
 
 
 def dbs_bfs(A: Matrix, src: int, levels, stream=None) -> None:

@@ -1,6 +1,7 @@
 // C-ABI entry points of the library (declared in include/dbs.h): argument
 // validation, handle lifetime, options, statistics and array export.  All
 // compute is in the HIP kernels of build.hip, spmspv.hip and bfs.hip.
+#include <float.h>
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
@@ -241,6 +242,15 @@ dbs_status dbs_spmspv_dense(dbs_handle A, const void *x, dbs_semiring sr, void *
   dbs_status st = check_semiring(A, sr);
   if (st != DBS_OK) return st;
   return dbs_spmspv_impl(A, 0, nullptr, nullptr, x, sr, y, (hipStream_t)stream);
+}
+
+dbs_status dbs_spmspv_dense_threshold(dbs_handle A, const void *x, float threshold, dbs_semiring sr, void *y,
+                                      void *stream) {
+  if (!A || !x || !y) return DBS_ERR_INVALID_ARG;
+  if (!(threshold >= 0.0f) || threshold > FLT_MAX) return DBS_ERR_INVALID_ARG;  // NaN, negative, inf
+  dbs_status st = check_semiring(A, sr);
+  if (st != DBS_OK) return st;
+  return dbs_spmspv_impl(A, 0, nullptr, nullptr, x, sr, y, (hipStream_t)stream, threshold);
 }
 
 dbs_status dbs_bfs(dbs_handle A, int32_t src, int32_t *levels, void *stream) {

@@ -186,9 +186,10 @@ size_t dbs_radix_tmp_bytes(int64_t n);
 
 dbs_status dbs_build_impl(dbs_matrix *A, const int32_t *row_ptr, const int32_t *col_idx,
                           const void *val, hipStream_t s);
+// thr < 0: a dense x's entries are active iff nonzero; thr >= 0: iff |x_j| > thr
 dbs_status dbs_spmspv_impl(dbs_matrix *A, int32_t nnz_x, const int32_t *x_idx,
                            const void *x_val, const void *x_dense, dbs_semiring sr, void *y,
-                           hipStream_t s);
+                           hipStream_t s, float thr = -1.0f);
 dbs_status dbs_bfs_impl(dbs_matrix *A, int32_t src, int32_t *levels, hipStream_t s);
 // next free event triple of the timing ring (folds the oldest into the sums
 // when the ring is full); nullptr on a HIP error

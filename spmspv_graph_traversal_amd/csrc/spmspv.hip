@@ -81,8 +81,10 @@ __global__ __launch_bounds__(dbs_meta::MT) void k_xmeta_sparse(MetaOut o, int32_
 
 // Dense x (decode, section 4.1): one ballot per wave gives the nonzero
 // pattern of 64 consecutive entries, i.e. the masks of four vector blocks.
+// thr >= 0: the activation is sparsified on the way (an entry is active iff
+// |x_j| > thr, and the staged x holds 0 for the others).
 template <int VK>
-__global__ __launch_bounds__(dbs_meta::MT) void k_xmeta_dense(MetaOut o, const void *x, void *xd) {
+__global__ __launch_bounds__(dbs_meta::MT) void k_xmeta_dense(MetaOut o, const void *x, void *xd, float thr) {
   if (blockIdx.x == 0 && threadIdx.x < 8) o.ctr_next[threadIdx.x] = 0;
   clear_y(o);
   const int lane = __lane_id();
@@ -90,8 +92,8 @@ __global__ __launch_bounds__(dbs_meta::MT) void k_xmeta_dense(MetaOut o, const v
   dbs_meta::register_blocks(o.reg, npad, [&](int64_t j, int pass, bool &leader, uint32_t &b) {
     bool nz = false;
     if (j < o.n) {
-      if (VK == VK_BF16) nz = (((const uint16_t *)x)[j] & 0x7FFFu) != 0u;
-      else nz = (__float_as_uint(((const float *)x)[j]) & 0x7FFFFFFFu) != 0u;
+      const uint32_t bits = VK == VK_BF16 ? (uint32_t)((const uint16_t *)x)[j] << 16 : __float_as_uint(((const float *)x)[j]);
+      nz = thr < 0.0f ? (bits & 0x7FFFFFFFu) != 0u : fabsf(__uint_as_float(bits)) > thr;
     }
     const uint64_t bal = __ballot(nz);
     const uint32_t mk = (uint32_t)(bal >> (lane & 48)) & 0xFFFFu;
@@ -102,8 +104,8 @@ __global__ __launch_bounds__(dbs_meta::MT) void k_xmeta_dense(MetaOut o, const v
     // PLUS_TIMES: copy x into the block-padded staging vector (zero tail),
     // so the multiply reads whole column quarters of every vector block
     if (pass == 0 && xd && j < npad) {
-      if (VK == VK_BF16) ((uint16_t *)xd)[j] = j < o.n ? ((const uint16_t *)x)[j] : (uint16_t)0;
-      else ((float *)xd)[j] = j < o.n ? ((const float *)x)[j] : 0.0f;
+      if (VK == VK_BF16) ((uint16_t *)xd)[j] = nz ? ((const uint16_t *)x)[j] : (uint16_t)0;
+      else ((float *)xd)[j] = nz ? ((const float *)x)[j] : 0.0f;
     }
   });
 }
@@ -730,7 +732,7 @@ void launch_spmspv(SpmvParams P, int64_t waves, hipStream_t s, hipEvent_t e0, hi
   } while (0)
 
 dbs_status dbs_spmspv_impl(dbs_matrix *A, int32_t nnz_x, const int32_t *x_idx, const void *x_val,
-                           const void *x_dense, dbs_semiring sr, void *y, hipStream_t s) {
+                           const void *x_dense, dbs_semiring sr, void *y, hipStream_t s, float thr) {
   const bool timing = A->opt[DBS_OPT_TIMING] != 0;
   // epoch tag of this call's masks; a full clear every 65535 calls
   A->epoch++;
@@ -782,8 +784,9 @@ dbs_status dbs_spmspv_impl(dbs_matrix *A, int32_t nnz_x, const int32_t *x_idx, c
   hipEvent_t c0 = tev ? tev[2] : nullptr, c1 = tev ? tev[3] : nullptr;
   if (dense) {
     void *xd = sr == DBS_PLUS_TIMES ? A->xd : nullptr;
-    if (xk == VK_BF16) launch_k(k_xmeta_dense<VK_BF16>, dim3(mgrid), dim3(dbs_meta::MT), s, m0, m1, o, x_dense, xd);
-    else launch_k(k_xmeta_dense<VK_F32>, dim3(mgrid), dim3(dbs_meta::MT), s, m0, m1, o, x_dense, xd);
+    if (xk == VK_BF16)
+      launch_k(k_xmeta_dense<VK_BF16>, dim3(mgrid), dim3(dbs_meta::MT), s, m0, m1, o, x_dense, xd, thr);
+    else launch_k(k_xmeta_dense<VK_F32>, dim3(mgrid), dim3(dbs_meta::MT), s, m0, m1, o, x_dense, xd, thr);
   } else {
     const int check = (int)A->opt[DBS_OPT_CHECK];
     const void *xv = sr == DBS_PLUS_TIMES ? x_val : nullptr;

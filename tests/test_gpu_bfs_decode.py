@@ -154,3 +154,75 @@ def test_dense_x_signed_zero_and_f32(dbs):
     assert ok.all()
     masks, _ = orc.xmeta_dense(n, x, orc.F32)
     np.testing.assert_array_equal(dbs.dbs_copy_array(A, dbs.DBS_ARR_XMASK), masks)
+
+
+def run_dense_threshold(dbs, A, m, x_t, t):
+    import torch
+
+    y = torch.full((m,), float("nan"), dtype=torch.float32, device="cuda")
+    dbs.dbs_spmspv_dense_threshold(A, x_t, t, dbs.DBS_PLUS_TIMES, y)
+    return y.cpu().numpy()
+
+
+@pytest.mark.parametrize("shape", [(11008, 4096), (4096, 11008)])
+def test_decode_fused_threshold_full_size(dbs, shape):
+    """Decode with the activation sparsified by magnitude in the metadata kernel:
+    a dense bf16 activation without zeros, thresholds keeping ~10% and ~50% of
+    it, against the oracle's thresholding followed by its dense-x product."""
+    rows, cols = shape
+    rp, ci, bits = decode_weight_csr(rows, cols, 0.5, rng_for("decode", rows, 5))
+    A = build(dbs, rows, cols, rp, ci, bits, dbs.DBS_BF16)
+    x = decode_activation(cols, 0.0, rng_for("decode", rows, 99))
+    xf = np.abs(orc_bf16(x))
+    x_t = up(x.view(np.int16))
+    for keep in (0.1, 0.5):
+        t = float(np.float32(np.quantile(xf, 1.0 - keep)))
+        xs = orc.threshold_activation(x, orc.BF16, t)
+        yr, s = orc.spmspv_dense_x(rows, cols, rp, ci, bits, orc.BF16, xs, orc.BF16)
+        for path in (0, 1, 2):
+            dbs.dbs_set_option(A, dbs.DBS_OPT_PATH, path)
+            ok, err = orc.within_tolerance(run_dense_threshold(dbs, A, rows, x_t, t), yr, s)
+            assert ok.all(), f"keep {keep} path {path}: max err {err.max():.3g}"
+        masks, nz = orc.xmeta_dense(cols, xs, orc.BF16)
+        assert dbs.dbs_get_stats(A)["last_n_nzblk"] == nz
+        np.testing.assert_array_equal(dbs.dbs_copy_array(A, dbs.DBS_ARR_XMASK), masks)
+    # x itself is not written
+    np.testing.assert_array_equal(x_t.cpu().numpy().view(np.uint16), x)
+
+
+def orc_bf16(bits):
+    return (np.asarray(bits, np.uint32) << 16).view(np.float32)
+
+
+def test_threshold_edge_cases(dbs):
+    import torch
+
+    a = mixed_tile_dense(9)
+    m, n = a.shape
+    rp, ci, v = csr_of(a)
+    A = build(dbs, m, n, rp, ci, v, dbs.DBS_F32)
+    x = rng_for("test", 830).normal(0, 1, n).astype(np.float32)
+    x[::4] = 0.0
+    x[1::9] = -0.0
+    x[5] = np.nan
+    x_t = up(x)
+    # t = 0: the plain dense rule except the NaN entry, which is dropped
+    xs = orc.threshold_activation(x, orc.F32, 0.0)
+    yr, s = orc.spmspv_dense_x(m, n, rp, ci, v, orc.F32, xs, orc.F32)
+    ok, err = orc.within_tolerance(run_dense_threshold(dbs, A, m, x_t, 0.0), yr, s)
+    assert ok.all(), f"max err {err.max():.3g}"
+    # a threshold above every |x|: nothing active, y all zero
+    y = run_dense_threshold(dbs, A, m, x_t, 1e30)
+    assert np.array_equal(y, np.zeros(m, np.float32))
+    assert dbs.dbs_get_stats(A)["last_n_nzblk"] == 0
+    # thresholds that are not finite and non-negative are rejected on the host
+    yt = torch.empty(m, dtype=torch.float32, device="cuda")
+    for bad in (-1.0, float("nan"), float("inf")):
+        with pytest.raises(dbs.DBSError):
+            dbs.dbs_spmspv_dense_threshold(A, x_t, bad, dbs.DBS_PLUS_TIMES, yt)
+    # the plain dense call after a thresholded one sees its own x again
+    xz = np.where(np.isnan(x), 0.0, x).astype(np.float32)
+    dbs.dbs_spmspv_dense(A, up(xz), dbs.DBS_PLUS_TIMES, yt)
+    yr, s = orc.spmspv_dense_x(m, n, rp, ci, v, orc.F32, xz, orc.F32)
+    ok, _ = orc.within_tolerance(yt.cpu().numpy(), yr, s)
+    assert ok.all()
