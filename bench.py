@@ -14,10 +14,15 @@ second pass over the same calls with DBS_OPT_TIMING on, where each kernel
 dispatch records its own start and end (those events cost the host and the
 device a few µs per call, so they are kept out of the throughput passes).
 
-Also reported (nested under "extra"): per-density numbers, BFS on R-MAT
-scale 22 from 64 seeded sources of the largest component (GTEPS), and the
-single-token decode layers 11008x4096 / 4096x11008 (µs per call, warm and
-with rotating copies to defeat the on-package cache).
+Also reported (nested under "extra"): per-density numbers; the selector
+ablation (the kernel with push and with pull forced at every density, and the
+x-block ratio where they cross); BFS on R-MAT scale 22 from 64 seeded sources
+of the largest component (GTEPS) with an Auto / Push / Pull ablation on 8 of
+them; the single-token decode layers 11008x4096 / 4096x11008 (µs per call,
+warm and with rotating copies to defeat the on-package cache), also with the
+activation sparsified by magnitude inside the metadata kernel (10% kept); the
+format size against CSR and CSR + CSC; the Zipf/band stress matrix.
+`--ablations` adds the tile-format ablation (COO-only / CSR-only / adaptive).
 
 Byte model (bytes a kernel must move for the path it takes; per call):
   pull     16*segments + 4*T (column block of every tile) + 4*N_blk (masks)
@@ -135,6 +140,28 @@ def load_traffic(workload):
 
 
 # ---------------------------------------------------------------- workloads
+def format_size(st, m, n, vsize):
+    """Bytes of the blocked dual view against CSR and against CSR + CSC
+    (int32 pointers and indices, values of vsize bytes)."""
+    nnz = st["nnz"]
+    csr = 4 * (m + 1) + 4 * nnz + vsize * nnz
+    both = csr + 4 * (n + 1) + 4 * nnz + vsize * nnz
+    return {"format_bytes": st["format_bytes"], "csr_bytes": csr, "csr_csc_bytes": both,
+            "vs_csr": round(st["format_bytes"] / csr, 3), "vs_csr_csc": round(st["format_bytes"] / both, 3)}
+
+
+def crossover(rows):
+    """x-block ratio where the forced-push and forced-pull kernel times cross,
+    interpolated linearly between the two measured densities around it."""
+    for a, b in zip(rows, rows[1:]):
+        da = a["push_kernel_us"] - a["pull_kernel_us"]
+        db = b["push_kernel_us"] - b["pull_kernel_us"]
+        if da < 0 <= db:
+            f = -da / (db - da)
+            return round(a["xb_ratio"] + f * (b["xb_ratio"] - a["xb_ratio"]), 4)
+    return None
+
+
 def bench_rmat20(dbs, torch, args):
     from synth import rmat_csr, rng_for, sparse_x
 
@@ -221,23 +248,28 @@ def bench_rmat20(dbs, torch, args):
             "compute_kernel_GBps": round(x["comp_bytes"] / (kms * 1e-3) / 1e9, 1),
             "compute_kernel_frac_of_hbm": round(x["comp_bytes"] / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         })
-    # forced push at the low densities (ablation of the global selector)
+    # ablation of the global selector: the kernel with push and with pull
+    # forced at every density, and the x-block ratio where the two cross
     forced = []
-    dbs.dbs_set_option(A, dbs.DBS_OPT_PATH, 1)
-    for x in ([] if args.headline_only else xs[:3]):
-        dbs.dbs_set_option(A, dbs.DBS_OPT_TIMING, 1)
-        for _ in range(args.steps):
-            dbs.dbs_spmspv(A, x["x"], None, dbs.DBS_OR_AND, y)
-        s2 = dbs.dbs_get_stats(A)
-        forced.append({"density": x["density"], "path": "push (forced)",
-                       "compute_kernel_us": round(s2["sum_compute_ms"] / s2["timed_calls"] * 1e3, 2)})
+    for x in ([] if args.headline_only else xs):
+        row = {"density": x["density"]}
+        for path, name in ((1, "push"), (2, "pull")):
+            dbs.dbs_set_option(A, dbs.DBS_OPT_PATH, path)
+            dbs.dbs_set_option(A, dbs.DBS_OPT_TIMING, 1)
+            for _ in range(args.steps):
+                dbs.dbs_spmspv(A, x["x"], None, dbs.DBS_OR_AND, y)
+            s2 = dbs.dbs_get_stats(A)
+            row[f"{name}_kernel_us"] = round(s2["sum_compute_ms"] / s2["timed_calls"] * 1e3, 2)
+            row["xb_ratio"] = round(s2["last_n_nzblk"] / fmt.nb, 5)
+        forced.append(row)
     dbs.dbs_set_option(A, dbs.DBS_OPT_PATH, 0)
     dbs.dbs_set_option(A, dbs.DBS_OPT_TIMING, 0)
     res = {
         "ms_per_step": ms_per_step, "value": value, "step_bytes": step_bytes,
         "kernel_avg_us": kernel_ms * 1e3, "achieved": achieved, "comp_bytes_per_launch": comp_bytes / len(xs),
-        "per_density": per, "forced_push": forced, "build_s": build_s,
+        "per_density": per, "forced_paths": forced, "xb_crossover": crossover(forced), "build_s": build_s,
         "format": {"tiles": st["tiles"], "segments": st["segments"], "format_MB": round(st["format_bytes"] / 1e6, 1),
+                   "size": format_size(st, n, n, 0),
                    "tiles_by_format": st["tiles_by_format"]},
         "graph": (rp, ci, n), "xs": xs,
     }
@@ -305,6 +337,22 @@ def bench_bfs22(dbs, torch, args):
         dbs.dbs_bfs(A, int(s), lv)
         ktimes.append(dbs.dbs_get_stats(A)["bfs_kernel_ms"])
     dbs.dbs_set_option(A, dbs.DBS_OPT_TIMING, 0)
+    # DB-BFS with the path forced at every level (the first 8 sources)
+    ablation = {}
+    k = min(8, len(srcs))
+    for path, name in ((0, "auto"), (1, "push"), (2, "pull")):
+        dbs.dbs_set_option(A, dbs.DBS_OPT_PATH, path)
+        tt = []
+        for s in srcs[:k]:
+            ev0.record()
+            dbs.dbs_bfs(A, int(s), lv)
+            ev1.record()
+            torch.cuda.synchronize()
+            tt.append(ev0.elapsed_time(ev1))
+        g = edges / (np.array(tt) * 1e-3) / 1e9
+        ablation[name] = {"gteps_harmonic_mean": round(float(len(g) / np.sum(1.0 / g)), 2),
+                          "ms_median": round(float(np.median(tt)), 3)}
+    dbs.dbs_set_option(A, dbs.DBS_OPT_PATH, 0)
     times = np.array(times)
     gteps = edges / (times * 1e-3) / 1e9
     return {"workload": "R-MAT scale 22, edge factor 16, symmetrized; 64 sources in the largest component",
@@ -315,7 +363,8 @@ def bench_bfs22(dbs, torch, args):
             "level_kernels_ms_median": round(float(np.median(ktimes)), 3),
             "levels_median": int(np.median(levels)), "push_levels_median": int(np.median(pushl)),
             "first_source_matches_oracle": ok, "oracle_bfs_s_first_source": round(cpu_bfs_s, 2),
-            "oracle_gteps_first_source": round(edges / cpu_bfs_s / 1e9, 4), "build_s": round(build_s, 2)}
+            "oracle_gteps_first_source": round(edges / cpu_bfs_s / 1e9, 4), "build_s": round(build_s, 2),
+            "path_ablation_first_8_sources": ablation}
 
 
 def bench_decode(dbs, torch, args):
@@ -374,7 +423,7 @@ def bench_decode(dbs, torch, args):
                             "bytes": int(mb + cb),
                             "GBps_warm": round((mb + cb) / (warm_us * 1e-6) / 1e9, 1),
                             "GBps_rotating": round((mb + cb) / (cold_us * 1e-6) / 1e9, 1),
-                            "tiles_by_format": st["tiles_by_format"]})
+                            "tiles_by_format": st["tiles_by_format"], "size": format_size(st, rows, cols, 2)})
                 log(f"[bench] decode {rows}x{cols} s={sp} z={z}: warm {warm_us:.2f} us, rotating {cold_us:.2f} us")
             if sp == 0.5:
                 out.append(bench_decode_threshold(dbs, torch, args, copies[0], fmt, rows, cols, y))
@@ -417,6 +466,69 @@ def bench_decode_threshold(dbs, torch, args, A, fmt, rows, cols, y):
             "compute_kernel_us_warm": round(s2["sum_compute_ms"] / s2["timed_calls"] * 1e3, 2),
             "meta_kernel_us_warm": round(s2["sum_meta_ms"] / s2["timed_calls"] * 1e3, 2),
             "bytes": int(mb + cb), "GBps_warm": round((mb + cb) / (warm_us * 1e-6) / 1e9, 1)}
+
+
+FORMATS = {"adaptive": -1, "COO-only": 0, "CSR-only": 4}
+
+
+def bench_format_ablation(dbs, torch, args):
+    """Tile-format ablation: every tile stored as COO, as patched CSR, or by the
+    adaptive rule, on the R-MAT 20 sweep (kernel µs per density) and on the
+    11008x4096 decode layer at 50% weight sparsity (kernel µs per activation)."""
+    from synth import decode_activation, decode_weight_csr, rmat_csr, rng_for, sparse_x
+
+    dev = torch.device("cuda:0")
+    out = {"rmat20_or_and": {}, "decode_11008x4096_s0.5": {}}
+    rp, ci = rmat_csr(20, 16, rng_for("rmat20"))
+    n = 1 << 20
+    rp_d, ci_d = torch.from_numpy(rp).to(dev), torch.from_numpy(ci).to(dev)
+    xs = [torch.from_numpy(sparse_x(n, d, rng_for("rmat20", 1, k), with_values=False)[0]).to(dev)
+          for k, d in enumerate(DENSITIES)]
+    y = torch.empty(n, dtype=torch.uint8, device=dev)
+    for name, f in FORMATS.items():
+        o = dbs.default_build_options()
+        o.force_format = f
+        A = dbs.dbs_build(n, n, rp_d, ci_d, None, dbs.DBS_PATTERN, options=o)
+        st = dbs.dbs_get_stats(A)
+        row = {"format_MB": round(st["format_bytes"] / 1e6, 1)}
+        for d, x in zip(DENSITIES, xs):
+            for _ in range(2):
+                dbs.dbs_spmspv(A, x, None, dbs.DBS_OR_AND, y)
+            dbs.dbs_set_option(A, dbs.DBS_OPT_TIMING, 1)
+            for _ in range(args.steps):
+                dbs.dbs_spmspv(A, x, None, dbs.DBS_OR_AND, y)
+            s2 = dbs.dbs_get_stats(A)
+            dbs.dbs_set_option(A, dbs.DBS_OPT_TIMING, 0)
+            row[str(d)] = round(s2["sum_compute_ms"] / s2["timed_calls"] * 1e3, 2)
+        out["rmat20_or_and"][name] = row
+        dbs.dbs_free(A)
+        log(f"[bench] format ablation rmat20 {name}: {row}")
+    rows, cols = 11008, 4096
+    rp, ci, bits = decode_weight_csr(rows, cols, 0.5, rng_for("decode", rows, 5))
+    rp_d, ci_d = torch.from_numpy(rp).to(dev), torch.from_numpy(ci).to(dev)
+    v_d = torch.from_numpy(bits.view(np.int16)).to(dev)
+    y = torch.empty(rows, dtype=torch.float32, device=dev)
+    acts = {z: torch.from_numpy(decode_activation(cols, z, rng_for("decode", rows, 5, int(z * 10))).view(np.int16)).to(dev)
+            for z in (0.1, 0.5, 0.9)}
+    for name, f in FORMATS.items():
+        o = dbs.default_build_options()
+        o.force_format = f
+        A = dbs.dbs_build(rows, cols, rp_d, ci_d, v_d, dbs.DBS_BF16, options=o)
+        st = dbs.dbs_get_stats(A)
+        row = {"format_MB": round(st["format_bytes"] / 1e6, 2)}
+        for z, xd in acts.items():
+            for _ in range(2):
+                dbs.dbs_spmspv_dense(A, xd, dbs.DBS_PLUS_TIMES, y)
+            dbs.dbs_set_option(A, dbs.DBS_OPT_TIMING, 1)
+            for _ in range(args.steps):
+                dbs.dbs_spmspv_dense(A, xd, dbs.DBS_PLUS_TIMES, y)
+            s2 = dbs.dbs_get_stats(A)
+            dbs.dbs_set_option(A, dbs.DBS_OPT_TIMING, 0)
+            row[f"zeros {z}"] = round(s2["sum_compute_ms"] / s2["timed_calls"] * 1e3, 2)
+        out["decode_11008x4096_s0.5"][name] = row
+        dbs.dbs_free(A)
+        log(f"[bench] format ablation decode {name}: {row}")
+    return out
 
 
 ZIPF_DENSITIES = [1e-5, 1e-4, 1e-3, 1e-2, 5e-2, 0.2]
@@ -494,6 +606,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-zipf", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--ablations", action="store_true",
+                    help="also the tile-format ablation (COO-only / CSR-only / adaptive builds; slow)")
     ap.add_argument("--headline-only", action="store_true",
                     help="only the timed sweep (for profiling: every SpMSpV launch is one of the timed mix)")
     ap.add_argument("--bfs-sources", type=int, default=64)
@@ -524,7 +638,8 @@ def main():
     torch.cuda.set_device(0)
     res = bench_rmat20(dbs, torch, args)
     log(f"[bench] rmat20 sweep: {res['ms_per_step']:.3f} ms/step, {res['value']:.1f} GB/s")
-    extra = {"rmat20_per_density": res["per_density"], "rmat20_forced_push": res["forced_push"],
+    extra = {"rmat20_per_density": res["per_density"], "rmat20_forced_paths": res["forced_paths"],
+             "rmat20_xb_crossover": res["xb_crossover"],
              "rmat20_format": res["format"], "rmat20_build_s": round(res["build_s"], 2)}
     cpu = None
     if args.headline_only:
@@ -540,6 +655,8 @@ def main():
         extra["decode"] = bench_decode(dbs, torch, args)
     if not args.no_zipf:
         extra["zipf_band"] = bench_zipf(dbs, torch, args)
+    if args.ablations:
+        extra["format_ablation"] = bench_format_ablation(dbs, torch, args)
     traffic = load_traffic("rmat20_sweep")
     line = {
         "metric": METRIC,
