@@ -608,6 +608,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--ablations", action="store_true",
                     help="also the tile-format ablation (COO-only / CSR-only / adaptive builds; slow)")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only the decode layers (for profiling the decode kernel); prints their JSON")
     ap.add_argument("--headline-only", action="store_true",
                     help="only the timed sweep (for profiling: every SpMSpV launch is one of the timed mix)")
     ap.add_argument("--bfs-sources", type=int, default=64)
@@ -636,6 +638,9 @@ def main():
     import spmspv_graph_traversal_amd as dbs
 
     torch.cuda.set_device(0)
+    if args.decode_only:
+        print(json.dumps({"decode": bench_decode(dbs, torch, args)}), flush=True)
+        return
     res = bench_rmat20(dbs, torch, args)
     log(f"[bench] rmat20 sweep: {res['ms_per_step']:.3f} ms/step, {res['value']:.1f} GB/s")
     extra = {"rmat20_per_density": res["per_density"], "rmat20_forced_paths": res["forced_paths"],
