@@ -119,11 +119,17 @@ def _ptr(t):
     return None if t is None else C.c_void_p(t.data_ptr())
 
 
-def _stream(stream):
+def _stream(stream, device=None):
+    """Raw HIP stream handle: the given stream, else the current stream of
+    `device` (the call's output tensor's device), read without building a
+    Stream object where torch offers that."""
     import torch
 
     if stream is None:
-        stream = torch.cuda.current_stream()
+        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        if raw is not None and device is not None:
+            return C.c_void_p(raw(device.index if device.index is not None else torch.cuda.current_device()))
+        stream = torch.cuda.current_stream(device)
     return C.c_void_p(stream.cuda_stream)
 
 
@@ -198,7 +204,7 @@ def dbs_spmspv(A: Matrix, x_idx, x_val, semiring, y, stream=None) -> None:
         _need(y, "y", (torch.uint8,), A.m)
     st = _lib.dbs_spmspv(A.handle, int(x_idx.numel()), _ptr(x_idx),
                          _ptr(x_val) if semiring == DBS_PLUS_TIMES else None, int(semiring), _ptr(y),
-                         _stream(stream))
+                         _stream(stream, y.device))
     _check(st, "dbs_spmspv")
 
 
@@ -208,7 +214,7 @@ def dbs_spmspv_dense(A: Matrix, x, semiring, y, stream=None) -> None:
     xd = _value_dtypes(A.dtype) if A.dtype != DBS_PATTERN else (torch.float32,)
     _need(x, "x", xd, A.n)
     _need(y, "y", (torch.float32,) if semiring == DBS_PLUS_TIMES else (torch.uint8,), A.m)
-    _check(_lib.dbs_spmspv_dense(A.handle, _ptr(x), int(semiring), _ptr(y), _stream(stream)),
+    _check(_lib.dbs_spmspv_dense(A.handle, _ptr(x), int(semiring), _ptr(y), _stream(stream, y.device)),
            "dbs_spmspv_dense")
 
 
@@ -219,14 +225,14 @@ def dbs_spmspv_dense_threshold(A: Matrix, x, threshold: float, semiring, y, stre
     _need(x, "x", xd, A.n)
     _need(y, "y", (torch.float32,) if semiring == DBS_PLUS_TIMES else (torch.uint8,), A.m)
     _check(_lib.dbs_spmspv_dense_threshold(A.handle, _ptr(x), float(threshold), int(semiring), _ptr(y),
-                                           _stream(stream)), "dbs_spmspv_dense_threshold")
+                                           _stream(stream, y.device)), "dbs_spmspv_dense_threshold")
 
 
 def dbs_bfs(A: Matrix, src: int, levels, stream=None) -> None:
     import torch
 
     _need(levels, "levels", (torch.int32,), A.m)
-    _check(_lib.dbs_bfs(A.handle, int(src), _ptr(levels), _stream(stream)), "dbs_bfs")
+    _check(_lib.dbs_bfs(A.handle, int(src), _ptr(levels), _stream(stream, levels.device)), "dbs_bfs")
 
 
 def dbs_set_option(A: Matrix, option: int, value: int) -> None:

@@ -7,7 +7,8 @@
 // Same-address device atomics serialize on this GPU (about 11 ns each, one
 // after the other), so a workgroup first counts its blocks over all its
 // rounds, reserves its range of the list with ONE atomic, then runs its
-// rounds again and writes the entries.  The value that atomic returns plus
+// rounds again and writes the entries (a workgroup with a single round, the
+// usual case, does it all in one pass).  The value that atomic returns plus
 // the workgroup's own count is a lower bound of N_nzblk: once it rules the
 // push path out (section 3.2 selector), the workgroup skips the chunks, so at
 // the densities that pull the chunk list costs next to nothing.  When the
@@ -65,6 +66,48 @@ DBS_DEV void register_blocks(const Reg &o, int64_t nitems, Item item) {
   __shared__ uint32_t s_base, s_cbase;
   const int tid = threadIdx.x;
   const int64_t rounds = (nitems + MT - 1) / MT;
+  // the list entries and push chunks of one round, given the round's scan
+  // (e, t) and the list position run of its first entry
+  auto emit = [&](bool leader, uint32_t b, uint32_t e, uint32_t t, uint32_t run, bool chunks) {
+    if (leader && (int64_t)run + e < o.list_cap) o.list[run + e] = b;
+    if (!chunks) return;  // uniform
+    const uint32_t nch = leader ? (o.cb_ptr[b + 1] - o.cb_ptr[b] + 63u) >> 6 : 0u;
+    uint32_t ec, tc;
+    wg_scan(nch, ec, tc);
+    if (tc == 0u) return;  // uniform
+    if (tid == 0) s_cbase = atomicAdd(&o.ctr[1], tc);
+    s_pref[tid] = ec + nch;
+    s_ex[tid] = ec;
+    s_blk[tid] = b;
+    __syncthreads();
+    const uint32_t cbase = s_cbase;
+    for (uint32_t j = (uint32_t)tid; j < tc; j += MT) {
+      int lo = 0, hi = MT - 1;  // first thread whose inclusive prefix exceeds j
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (s_pref[mid] > j) hi = mid;
+        else lo = mid + 1;
+      }
+      const int64_t pos = (int64_t)cbase + j;
+      if (pos < o.chunk_cap) o.chunks[pos] = (uint64_t)s_blk[lo] | ((uint64_t)(j - s_ex[lo]) << 32);
+    }
+    __syncthreads();
+  };
+  if (blockIdx.x < rounds && blockIdx.x + (int64_t)gridDim.x >= rounds) {
+    // one round for this workgroup: count, reserve and write in one pass
+    bool leader = false;
+    uint32_t b = 0;
+    item((int64_t)blockIdx.x * MT + tid, 0, leader, b);
+    uint32_t e, t;
+    wg_scan(leader ? 1u : 0u, e, t);
+    if (t == 0u) return;  // uniform
+    if (tid == 0) s_base = atomicAdd(&o.ctr[0], t);
+    __syncthreads();
+    const uint32_t run = s_base;
+    // N_nzblk >= run + t: once that already rules push out, no chunks
+    emit(leader, b, e, t, run, o.force_path == 1 || (o.force_path == 0 && takes_push(o, run + t)));
+    return;
+  }
   uint32_t tot = 0;
   for (int r = blockIdx.x; r < rounds; r += gridDim.x) {  // pass 0: count
     bool leader = false;
@@ -86,30 +129,8 @@ DBS_DEV void register_blocks(const Reg &o, int64_t nitems, Item item) {
     item((int64_t)r * MT + tid, 1, leader, b);
     uint32_t e, t;
     wg_scan(leader ? 1u : 0u, e, t);
-    if (leader && (int64_t)run + e < o.list_cap) o.list[run + e] = b;
+    emit(leader, b, e, t, run, chunks);
     run += t;
-    if (!chunks) continue;  // uniform
-    const uint32_t nch = leader ? (o.cb_ptr[b + 1] - o.cb_ptr[b] + 63u) >> 6 : 0u;
-    uint32_t ec, tc;
-    wg_scan(nch, ec, tc);
-    if (tc == 0u) continue;  // uniform
-    if (tid == 0) s_cbase = atomicAdd(&o.ctr[1], tc);
-    s_pref[tid] = ec + nch;
-    s_ex[tid] = ec;
-    s_blk[tid] = b;
-    __syncthreads();
-    const uint32_t cbase = s_cbase;
-    for (uint32_t j = (uint32_t)tid; j < tc; j += MT) {
-      int lo = 0, hi = MT - 1;  // first thread whose inclusive prefix exceeds j
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (s_pref[mid] > j) hi = mid;
-        else lo = mid + 1;
-      }
-      const int64_t pos = (int64_t)cbase + j;
-      if (pos < o.chunk_cap) o.chunks[pos] = (uint64_t)s_blk[lo] | ((uint64_t)(j - s_ex[lo]) << 32);
-    }
-    __syncthreads();
   }
 }
 
