@@ -209,7 +209,8 @@ typedef struct {
   /* last dbs_spmspv / dbs_spmspv_dense call (reading them synchronizes its stream) */
   int32_t last_path;               /* 0 push, 1 pull, -1 no call yet */
   int32_t last_n_nzblk;            /* nonzero vector blocks */
-  int64_t last_push_chunks;        /* 64-tile work chunks listed for push */
+  int64_t last_push_chunks;        /* 64-tile work chunks listed ahead for push (0 when the
+                                      pushing kernel takes them from the block list itself) */
   float last_meta_ms;              /* metadata kernel time (DBS_OPT_TIMING), else -1 */
   float last_compute_ms;           /* SpMSpV kernel time (DBS_OPT_TIMING), else -1 */
   /* sums over the SpMSpV calls made since DBS_OPT_TIMING was last set to 1 (HIP

@@ -14,8 +14,12 @@
 //                block whose rows are all found by its first segment is not
 //                read further (the bottom-up early exit, per row block);
 //   k_bfs_meta   counts the nonzero blocks of the next bitmap, lists them
-//                (one atomic per workgroup), cuts them into push chunks when
-//                the next level pushes, and clears the bitmap two levels back.
+//                (one atomic per workgroup) and clears the bitmap two levels
+//                back.  A pushing level takes its work chunks from that list
+//                (each workgroup enumerates them); only when a push could
+//                involve more blocks than that enumeration holds does the
+//                metadata kernel cut the chunks ahead, while push is still
+//                possible.
 // Three bitmaps rotate: current frontier, next frontier, and one being
 // cleared.  The host launches levels in batches without waiting: each level
 // kernel records its frontier's nonzero-block count, and one read of those
@@ -49,6 +53,8 @@ struct BfsParams {
   uint32_t *vis;            // visited bitmap
   const uint32_t *cur_ctr;  // [0] nonzero blocks, [1] push chunks
   const uint64_t *cur_chunks;
+  const uint32_t *cur_list; // nonzero blocks of the frontier
+  int32_t list_push;        // push chunks come from cur_list (none were built)
   uint32_t *hist;           // nonzero blocks of the current frontier, stored at [level % batch]
   int32_t *levels;
   int32_t level;            // level of the current frontier
@@ -219,6 +225,7 @@ struct BfsPol {
 template <int VK>
 __global__ __launch_bounds__(KT) void k_bfs_level(BfsParams P) {
   __shared__ uint32_t s_pat[VK == VK_PAT ? KT / DBS_WAVE : 1][PAT_LDS_WORDS];
+  __shared__ uint32_t s_cum[dbs_meta::PUSH_LIST_MAX];
   const int lane = __lane_id();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / DBS_WAVE);
   const uint32_t nz = P.cur_ctr[0];
@@ -231,8 +238,11 @@ __global__ __launch_bounds__(KT) void k_bfs_level(BfsParams P) {
   const int64_t gw = (int64_t)blockIdx.x * (KT / DBS_WAVE) + w;
   const int64_t nw = (int64_t)gridDim.x * (KT / DBS_WAVE);
   if (push) {
-    const int64_t nch = P.cur_ctr[1];
-    for (int64_t c = gw; c < nch; c += nw) bfs_push_chunk<VK>(P, P.cur_chunks[c], lane);
+    const int64_t nch =
+        P.list_push ? (int64_t)dbs_meta::listed_chunks<KT>(P.cur_list, nz, P.cb_ptr, s_cum) : (int64_t)P.cur_ctr[1];
+    for (int64_t c = gw; c < nch; c += nw)
+      bfs_push_chunk<VK>(P, P.list_push ? dbs_meta::listed_chunk(P.cur_list, nz, s_cum, (uint32_t)c) : P.cur_chunks[c],
+                         lane);
   } else {
     constexpr int U = 8;
     const bool eager = (int64_t)nz * 4 > (int64_t)P.nb;
@@ -275,7 +285,7 @@ __global__ __launch_bounds__(dbs_meta::MT) void k_bfs_meta(const uint32_t *bm, i
 // bitmap (rows without an entry start out visited: no level can reach them,
 // and a row block whose remaining rows are all such is skipped by the pull),
 // and the first frontier's metadata: one nonzero block, listed, and, when
-// level 0 pushes, the push chunks of its column block.
+// level 0 pushes from chunks built ahead, the push chunks of its column block.
 __global__ void k_bfs_init(int32_t *levels, int32_t m, uint32_t *bm3, int64_t bm_words3, uint32_t *vis,
                            const uint32_t *rows_nz, int64_t nwords, uint32_t *ctr3, int32_t src,
                            const uint32_t *cb_ptr, uint32_t *list0, uint64_t *chunks0, int64_t chunk_cap, int push0) {
@@ -319,7 +329,10 @@ dbs_status dbs_bfs_impl(dbs_matrix *A, int32_t src, int32_t *levels, hipStream_t
   const bool timing = A->opt[DBS_OPT_TIMING] != 0;
   if (timing) BFS_TRY(hipEventRecord(A->ev[0], s));
   const int64_t fp = A->opt[DBS_OPT_PATH];
-  const int push0 = fp == 1 || (fp == 0 && A->opt[DBS_OPT_TH3_DEN] < (int64_t)A->nb * A->opt[DBS_OPT_TH3_NUM]);
+  const bool list_push =
+      dbs_meta::push_from_list(A->nb, fp, A->opt[DBS_OPT_TH3_NUM], A->opt[DBS_OPT_TH3_DEN]);
+  const int push0 =
+      !list_push && (fp == 1 || (fp == 0 && A->opt[DBS_OPT_TH3_DEN] < (int64_t)A->nb * A->opt[DBS_OPT_TH3_NUM]));
   hipLaunchKernelGGL(k_bfs_init, dim3(1024), dim3(256), 0, s, levels, A->m, A->bfs_bm, 3 * nwords, A->bfs_vis,
                      (const uint32_t *)A->rows_nz, nwords, A->bfs_ctr, src, (const uint32_t *)A->cb_ptr, A->bfs_list,
                      A->bfs_chunks, chunk_cap, push0);
@@ -337,6 +350,7 @@ dbs_status dbs_bfs_impl(dbs_matrix *A, int32_t src, int32_t *levels, hipStream_t
     r.force_path = (int32_t)A->opt[DBS_OPT_PATH];
     r.th3_num = A->opt[DBS_OPT_TH3_NUM];
     r.th3_den = A->opt[DBS_OPT_TH3_DEN];
+    r.build_chunks = list_push ? 0 : 1;
     return r;
   };
 
@@ -364,6 +378,7 @@ dbs_status dbs_bfs_impl(dbs_matrix *A, int32_t src, int32_t *levels, hipStream_t
   P.force_path = (int32_t)A->opt[DBS_OPT_PATH];
   P.th3_num = A->opt[DBS_OPT_TH3_NUM];
   P.th3_den = A->opt[DBS_OPT_TH3_DEN];
+  P.list_push = list_push ? 1 : 0;
   const int pu = A->vk == VK_PAT ? 1 : 8;
   const int64_t ns = A->vk == VK_PAT ? A->npseg : A->nseg;
   int64_t waves = (ns + pu - 1) / pu > chunk_cap ? (ns + pu - 1) / pu : chunk_cap;
@@ -388,6 +403,7 @@ dbs_status dbs_bfs_impl(dbs_matrix *A, int32_t src, int32_t *levels, hipStream_t
       P.next_bm = A->bfs_bm + nxt * nwords;
       P.cur_ctr = A->bfs_ctr + 8 * cur;
       P.cur_chunks = A->bfs_chunks + cur * chunk_cap;
+      P.cur_list = A->bfs_list + (int64_t)cur * A->nb;
       P.level = (int32_t)l;
       if (timing) BFS_TRY(hipEventRecord(A->ev[2 + 2 * i], s));
       if (A->vk == VK_F32) {

@@ -32,6 +32,7 @@ struct Reg {
   // selector: push iff force_path == 1, or force_path == 0 and N_nzblk * th3_den < nb * th3_num
   int32_t nb, force_path;
   int64_t th3_num, th3_den;
+  int32_t build_chunks;  // 0: the pushing kernel enumerates the chunks from the list itself
 };
 
 DBS_DEV bool takes_push(const Reg &o, uint32_t nz) {
@@ -105,7 +106,8 @@ DBS_DEV void register_blocks(const Reg &o, int64_t nitems, Item item) {
     __syncthreads();
     const uint32_t run = s_base;
     // N_nzblk >= run + t: once that already rules push out, no chunks
-    emit(leader, b, e, t, run, o.force_path == 1 || (o.force_path == 0 && takes_push(o, run + t)));
+    emit(leader, b, e, t, run,
+         o.build_chunks != 0 && (o.force_path == 1 || (o.force_path == 0 && takes_push(o, run + t))));
     return;
   }
   uint32_t tot = 0;
@@ -122,7 +124,8 @@ DBS_DEV void register_blocks(const Reg &o, int64_t nitems, Item item) {
   __syncthreads();
   uint32_t run = s_base;
   // N_nzblk >= run + tot: once that already rules push out, no chunks
-  const bool chunks = o.force_path == 1 || (o.force_path == 0 && takes_push(o, run + tot));
+  const bool chunks =
+      o.build_chunks != 0 && (o.force_path == 1 || (o.force_path == 0 && takes_push(o, run + tot)));
   for (int r = blockIdx.x; r < rounds; r += gridDim.x) {  // pass 1: write
     bool leader = false;
     uint32_t b = 0;
@@ -132,6 +135,69 @@ DBS_DEV void register_blocks(const Reg &o, int64_t nitems, Item item) {
     emit(leader, b, e, t, run, chunks);
     run += t;
   }
+}
+
+// Push work taken straight from the compacted list: each workgroup lists the
+// chunks (64 tiles of one column block, section 3.3.2) of the n listed blocks
+// on its own, as inclusive prefix sums of their chunk counts in LDS (s_cum,
+// at most PUSH_LIST_MAX entries; returns the number of chunks), and finds
+// chunk c of the grid-stride loop by binary search (listed_chunk).  So no
+// chunk list is built ahead of a call that may not push.  Every thread of the
+// workgroup calls listed_chunks.
+constexpr int PUSH_LIST_MAX = 6144;
+
+template <int KTH>
+DBS_DEV uint32_t listed_chunks(const uint32_t *list, uint32_t n, const uint32_t *cb_ptr, uint32_t *s_cum) {
+  __shared__ uint32_t s_wtot[KTH / DBS_WAVE];
+  const uint32_t tid = threadIdx.x;
+  for (uint32_t i = tid; i < n; i += KTH) {
+    const uint32_t b = list[i];
+    s_cum[i] = (cb_ptr[b + 1] - cb_ptr[b] + 63u) >> 6;
+  }
+  __syncthreads();
+  // thread t scans its run of entries, then the runs are offset by the
+  // workgroup's exclusive scan of their sums
+  const uint32_t per = (n + KTH - 1) / KTH, i0 = tid * per;
+  const uint32_t i1 = i0 + per < n ? i0 + per : n;
+  uint32_t loc = 0;
+  for (uint32_t i = i0; i < i1; ++i) {
+    loc += s_cum[i];
+    s_cum[i] = loc;
+  }
+  const uint32_t inc = group_incl_scan_u32<64>(loc);
+  const int w = (int)(tid / DBS_WAVE);
+  if ((tid & (DBS_WAVE - 1)) == DBS_WAVE - 1) s_wtot[w] = inc;
+  __syncthreads();
+  uint32_t off = inc - loc;
+  for (int k = 0; k < w; ++k) off += s_wtot[k];
+  for (uint32_t i = i0; i < i1; ++i) s_cum[i] += off;
+  __syncthreads();
+  return n ? s_cum[n - 1] : 0u;
+}
+
+// chunk c (< the count listed_chunks returned) as (block, chunk of the block << 32)
+DBS_DEV uint64_t listed_chunk(const uint32_t *list, uint32_t n, const uint32_t *s_cum, uint32_t c) {
+  uint32_t lo = 0, hi = n - 1;  // first entry whose inclusive sum exceeds c
+  while (lo < hi) {
+    const uint32_t mid = (lo + hi) >> 1;
+    if (s_cum[mid] > c) hi = mid;
+    else lo = mid + 1;
+  }
+  const uint32_t j = c - (lo ? s_cum[lo - 1] : 0u);
+  return (uint64_t)list[lo] | ((uint64_t)j << 32);
+}
+
+// Host side: whether every call whose selector can pick push has at most
+// PUSH_LIST_MAX nonzero blocks (then the pushing kernel enumerates its chunks
+// from the list and the metadata kernel builds none).
+inline bool push_from_list(int64_t nb, int64_t force_path, int64_t th3_num, int64_t th3_den) {
+  if (force_path == 2) return true;  // never pushes
+  if (force_path == 1) return nb <= PUSH_LIST_MAX;
+  // push iff N * den < nb * num, so N <= (nb * num - 1) / den
+  const __int128 lim = (__int128)nb * th3_num;
+  if (lim <= 0) return true;
+  if (th3_den <= 0) return false;
+  return (lim - 1) / th3_den <= PUSH_LIST_MAX;
 }
 
 inline unsigned groups_for(int64_t nitems, int64_t other_work) {

@@ -6,11 +6,13 @@
 // One call = two launches on the caller's stream:
 //   k_xmeta_*   builds blk_x_mask (tagged with a per-call epoch so it never
 //               needs clearing), stages x, counts the nonzero vector blocks
-//               with one atomic per workgroup, lists them, reserves push
-//               work chunks (64 tiles of one column block each) and clears y;
+//               with one atomic per workgroup, lists them and clears y;
 //   k_spmspv    reads N_nzblk, picks push or pull on the device, and walks
-//               either the push chunks or the static pull segments, one wave
-//               per chunk / segment, grid-stride.
+//               either the push work chunks (64 tiles of one column block
+//               each, enumerated from the list by every workgroup) or the
+//               static pull segments, one wave per chunk / segment,
+//               grid-stride.  (When a push could involve more blocks than
+//               that enumeration holds, k_xmeta_* cuts the chunks ahead.)
 #include "meta.h"
 #include <hip/hip_ext.h>
 
@@ -139,6 +141,8 @@ struct SpmvParams {
   int32_t local_cutoff;
   int32_t plus_u;  // segments per wave step of the PLUS_TIMES pull (1 or PULL_U_PLUS_WIDE)
   int32_t plus_parts;  // U = 1: waves sharing one segment (1, 2 or 4), each taking a lane range
+  const uint32_t *xlist;  // this call's nonzero vector blocks (N_nzblk of them)
+  int32_t list_push;      // push chunks come from xlist (none were built)
   void *y;
 };
 
@@ -660,6 +664,7 @@ __global__ __launch_bounds__(KT, (VK == VK_BF16 && SR == DBS_PLUS_TIMES && PU ==
   __shared__ float s_x[KT / DBS_WAVE][16];
   __shared__ float s_part[KT / DBS_WAVE][64];
   __shared__ uint32_t s_mark[KT / DBS_WAVE][64];
+  __shared__ uint32_t s_cum[SR == DBS_OR_AND ? dbs_meta::PUSH_LIST_MAX : 1];
   __shared__ uint32_t s_pat[VK == VK_PAT && SR == DBS_OR_AND ? KT / DBS_WAVE : 1][PAT_LDS_WORDS];
   const int lane = __lane_id();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / DBS_WAVE);
@@ -669,8 +674,18 @@ __global__ __launch_bounds__(KT, (VK == VK_BF16 && SR == DBS_PLUS_TIMES && PU ==
   const int64_t gw = (int64_t)blockIdx.x * (KT / DBS_WAVE) + w;
   const int64_t nw = (int64_t)gridDim.x * (KT / DBS_WAVE);
   if (push) {
-    const int64_t nch = (int64_t)P.ctr[1] < P.max_chunks ? (int64_t)P.ctr[1] : P.max_chunks;
-    for (int64_t c = gw; c < nch; c += nw) push_chunk<VK, SR>(P, P.chunks[c], s_x[w], s_part[w], lane);
+    // OR_AND: the work chunks come from the block list (enumerated here);
+    // PLUS_TIMES (whose pull kernels have no registers to spare) and OR_AND
+    // calls that may push more blocks than the enumeration holds: from the
+    // chunk list built ahead
+    if (SR == DBS_OR_AND && P.list_push) {  // uniform
+      const uint32_t nch = dbs_meta::listed_chunks<KT>(P.xlist, nz, P.cb_ptr, s_cum);
+      for (int64_t c = gw; c < nch; c += nw)
+        push_chunk<VK, SR>(P, dbs_meta::listed_chunk(P.xlist, nz, s_cum, (uint32_t)c), s_x[w], s_part[w], lane);
+    } else {
+      const int64_t nch = (int64_t)P.ctr[1] < P.max_chunks ? (int64_t)P.ctr[1] : P.max_chunks;
+      for (int64_t c = gw; c < nch; c += nw) push_chunk<VK, SR>(P, P.chunks[c], s_x[w], s_part[w], lane);
+    }
   } else {
     // metadata of every tile is loaded up front once most vector blocks are active
     const bool eager = (int64_t)nz * 4 > (int64_t)P.nb;
@@ -755,6 +770,10 @@ dbs_status dbs_spmspv_impl(dbs_matrix *A, int32_t nnz_x, const int32_t *x_idx, c
   o.reg.force_path = (int32_t)A->opt[DBS_OPT_PATH];
   o.reg.th3_num = A->opt[DBS_OPT_TH3_NUM];
   o.reg.th3_den = A->opt[DBS_OPT_TH3_DEN];
+  const bool list_push =
+      sr == DBS_OR_AND &&
+      dbs_meta::push_from_list(A->nb, A->opt[DBS_OPT_PATH], A->opt[DBS_OPT_TH3_NUM], A->opt[DBS_OPT_TH3_DEN]);
+  o.reg.build_chunks = list_push ? 0 : 1;
   o.ctr_next = A->ctr + 8 * (1 - A->cbuf);
   o.n = A->n;
   o.nb = A->nb;
@@ -820,6 +839,8 @@ dbs_status dbs_spmspv_impl(dbs_matrix *A, int32_t nnz_x, const int32_t *x_idx, c
   P.xd = A->xd;  // PLUS_TIMES only: the staged x (OR_AND reads the masks alone)
   P.chunks = A->chunks;
   P.max_chunks = A->max_chunks;
+  P.xlist = A->act_list;
+  P.list_push = list_push ? 1 : 0;
   P.ctr = o.reg.ctr;
   P.force_path = (int32_t)A->opt[DBS_OPT_PATH];
   P.th3_num = A->opt[DBS_OPT_TH3_NUM];
