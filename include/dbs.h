@@ -244,7 +244,8 @@ enum {
   DBS_ARR_PAYLOAD = 6,     /* uint8[]        tile payload arena */
   DBS_ARR_SEGMENTS = 7,    /* uint32[4*S]    {row block | split<<31, t0, t1, 0} */
   DBS_ARR_XMASK = 8,       /* uint16[nb]     blk_x_mask of the last call */
-  DBS_ARR_ACTIVE = 9       /* uint32[N_nzblk] nonzero vector blocks of the last call (any order) */
+  DBS_ARR_ACTIVE = 9,      /* uint32[N_nzblk] nonzero vector blocks of the last call (any order) */
+  DBS_ARR_CSC_CM = 10      /* uint16[T]      columns of each tile that hold entries, CSC order */
 };
 dbs_status dbs_copy_array(dbs_handle A, int32_t which, void *dst, int64_t capacity,
                           int64_t *bytes_out);

@@ -64,7 +64,7 @@ hipError_t fold_all(dbs_matrix *A) {
 }
 
 void free_all(dbs_matrix *A) {
-  void *bufs[] = {A->rb_ptr, A->t_cb,     A->t_meta,   A->cb_ptr,     A->csc_rb,  A->csc2csr,
+  void *bufs[] = {A->rb_ptr, A->t_cb,     A->t_meta,   A->cb_ptr,     A->csc_rb,  A->csc2csr, A->csc_cm,
                   A->payload, A->segs,    A->psegs,    A->wown,    A->rows_nz,  A->xmask,    A->xd,         A->act_list, A->chunks,
                   A->ctr,    A->bfs_bm,   A->bfs_vis,  A->bfs_list,   A->bfs_chunks, A->bfs_ctr};
   for (void *b : bufs)
@@ -331,6 +331,7 @@ dbs_status dbs_copy_array(dbs_handle A, int32_t which, void *dst, int64_t capaci
     case DBS_ARR_CB_PTR: src = A->cb_ptr; bytes = (int64_t)(A->nb + 1) * 4; break;
     case DBS_ARR_CSC_RB: src = A->csc_rb; bytes = A->T * 4; break;
     case DBS_ARR_CSC2CSR: src = A->csc2csr; bytes = A->T * 4; break;
+    case DBS_ARR_CSC_CM: src = A->csc_cm; bytes = A->T * 2; break;
     case DBS_ARR_PAYLOAD: src = A->payload; bytes = A->payload_bytes; break;
     case DBS_ARR_SEGMENTS: src = A->segs; bytes = A->nseg * 16; break;
     case DBS_ARR_XMASK: src = A->xmask; bytes = (int64_t)A->nb * 2; break;

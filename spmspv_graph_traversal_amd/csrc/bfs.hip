@@ -40,6 +40,7 @@ struct BfsParams {
   const uint32_t *cb_ptr;
   const uint32_t *csc_rb;
   const uint32_t *csc2csr;
+  const uint16_t *csc_cm;   // columns of each tile with entries, CSC order
   const uint8_t *payload;
   uint64_t dense_mask_off;
   const uint32_t *segs;
@@ -105,8 +106,10 @@ template <int VK>
 DBS_DEV void bfs_push_chunk(const BfsParams &P, uint64_t own, int lane) {
   const uint32_t b = (uint32_t)own, j = (uint32_t)(own >> 32);
   const uint32_t m = bm_get(P.cur_bm, b);
-  const uint32_t k = P.cb_ptr[b] + j * 64u + (uint32_t)lane;
-  const bool act = k < P.cb_ptr[b + 1];
+  const uint32_t k0 = P.cb_ptr[b] + j * 64u, k = k0 + (uint32_t)lane;
+  // a tile without an entry in a frontier column finds nothing: its
+  // metadata is not read
+  const bool act = k < P.cb_ptr[b + 1] && (P.csc_cm[k < P.cb_ptr[b + 1] ? k : k0] & m) != 0u;
   uint32_t rb = 0;
   uint64_t meta = 0;
   if (act) {
@@ -360,6 +363,7 @@ dbs_status dbs_bfs_impl(dbs_matrix *A, int32_t src, int32_t *levels, hipStream_t
   P.cb_ptr = A->cb_ptr;
   P.csc_rb = A->csc_rb;
   P.csc2csr = A->csc2csr;
+  P.csc_cm = A->csc_cm;
   P.payload = A->payload;
   P.dense_mask_off = A->dense_mask_off;
   P.segs = A->segs;

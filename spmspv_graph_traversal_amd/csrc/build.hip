@@ -198,7 +198,7 @@ __global__ __launch_bounds__(BT) void k_tile_fill(int32_t m, int32_t mb, const i
                                                   const int32_t *col_idx, const void *val,
                                                   const uint32_t *rb_ptr, const uint64_t *t_meta,
                                                   uint64_t *t_meta_w, uint8_t *payload,
-                                                  uint64_t dense_mask_off) {
+                                                  uint64_t dense_mask_off, uint16_t *t_cm) {
   constexpr int VS = VK == VK_F32 ? 4 : VK == VK_BF16 ? 2 : 0;
   const int r = threadIdx.x & 15;
   const int32_t rb = (int32_t)blockIdx.x * RB_PER_BLOCK + (int32_t)(threadIdx.x >> 4);
@@ -209,6 +209,8 @@ __global__ __launch_bounds__(BT) void k_tile_fill(int32_t m, int32_t mb, const i
     if (cb == 0xFFFFFFFFu) break;
     const int64_t p0 = c.p;
     const uint32_t rm = cursor_take(c, col_idx, cb);
+    const uint32_t tcm = group_or_u32<16>(rm);  // the tile's columns with entries
+    if (r == 0) t_cm[t] = (uint16_t)tcm;
     const uint32_t cnt = (uint32_t)__popc(rm);
     const uint32_t rp = group_incl_scan_u32<16>(cnt) - cnt;  // row start inside the tile
     const uint32_t cm = transpose_masks16(rm, r);            // lane r: column r
@@ -300,6 +302,11 @@ __global__ void k_gather_rb(const uint32_t *csc2csr, const uint32_t *t_rb, int64
                             uint32_t *csc_rb) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < T) csc_rb[i] = t_rb[csc2csr[i]];
+}
+
+__global__ void k_gather_cm(const uint32_t *csc2csr, const uint16_t *t_cm, int64_t T, uint16_t *csc_cm) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < T) csc_cm[i] = t_cm[csc2csr[i]];
 }
 
 DBS_DEV uint32_t seg_weight(uint32_t type, const dbs_build_options &o) {
@@ -599,22 +606,28 @@ dbs_status dbs_build_impl(dbs_matrix *A, const int32_t *row_ptr, const int32_t *
     BUILD_TRY(hipGetLastError());
   }
 
-  // --- pass 3: payloads
+  // --- pass 3: payloads, and each tile's column set (CSR order)
+  uint16_t *t_cm;
+  BUILD_TRY(tmp.get((void **)&t_cm, (size_t)T * 2 + 2));
   if (vk == VK_F32)
     hipLaunchKernelGGL(k_tile_fill<VK_F32>, dim3(gblocks), dim3(BT), 0, s, m, mb, row_ptr, col_idx, val,
-                       (const uint32_t *)A->rb_ptr, (const uint64_t *)A->t_meta, A->t_meta, A->payload, A->dense_mask_off);
+                       (const uint32_t *)A->rb_ptr, (const uint64_t *)A->t_meta, A->t_meta, A->payload, A->dense_mask_off,
+                       t_cm);
   else if (vk == VK_BF16)
     hipLaunchKernelGGL(k_tile_fill<VK_BF16>, dim3(gblocks), dim3(BT), 0, s, m, mb, row_ptr, col_idx, val,
-                       (const uint32_t *)A->rb_ptr, (const uint64_t *)A->t_meta, A->t_meta, A->payload, A->dense_mask_off);
+                       (const uint32_t *)A->rb_ptr, (const uint64_t *)A->t_meta, A->t_meta, A->payload, A->dense_mask_off,
+                       t_cm);
   else
     hipLaunchKernelGGL(k_tile_fill<VK_PAT>, dim3(gblocks), dim3(BT), 0, s, m, mb, row_ptr, col_idx, val,
-                       (const uint32_t *)A->rb_ptr, (const uint64_t *)A->t_meta, A->t_meta, A->payload, A->dense_mask_off);
+                       (const uint32_t *)A->rb_ptr, (const uint64_t *)A->t_meta, A->t_meta, A->payload, A->dense_mask_off,
+                       t_cm);
   BUILD_TRY(hipGetLastError());
 
   // --- block-level CSC view: stable sort of the tiles by column block
   BUILD_TRY(dbs_dev_alloc(A, (void **)&A->cb_ptr, (size_t)(nb + 1) * 4));
   BUILD_TRY(dbs_dev_alloc(A, (void **)&A->csc_rb, (size_t)T * 4 + 4));
   BUILD_TRY(dbs_dev_alloc(A, (void **)&A->csc2csr, (size_t)T * 4 + 4));
+  BUILD_TRY(dbs_dev_alloc(A, (void **)&A->csc_cm, (size_t)T * 2 + 2));
   uint32_t *keys, *keys_tmp, *vals_tmp, *cb_cnt;
   void *rtmp;
   BUILD_TRY(tmp.get((void **)&keys, (size_t)T * 4 + 4));
@@ -634,6 +647,9 @@ dbs_status dbs_build_impl(dbs_matrix *A, const int32_t *row_ptr, const int32_t *
                                    rtmp, s));
     hipLaunchKernelGGL(k_gather_rb, dim3(nblocks(T, BT)), dim3(BT), 0, s, (const uint32_t *)A->csc2csr,
                        (const uint32_t *)t_rb, T, A->csc_rb);
+    BUILD_TRY(hipGetLastError());
+    hipLaunchKernelGGL(k_gather_cm, dim3(nblocks(T, BT)), dim3(BT), 0, s, (const uint32_t *)A->csc2csr,
+                       (const uint16_t *)t_cm, T, A->csc_cm);
     BUILD_TRY(hipGetLastError());
   }
   BUILD_TRY(dbs_scan_u32(cb_cnt, A->cb_ptr, nb, stmpn, s));

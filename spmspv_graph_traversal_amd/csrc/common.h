@@ -125,6 +125,8 @@ struct dbs_matrix {
   uint32_t *cb_ptr;     // [nb+1] block-CSC column pointer
   uint32_t *csc_rb;     // [T]    block-CSC row block
   uint32_t *csc2csr;    // [T]    primary tile id of each CSC position
+  uint16_t *csc_cm;     // [T]    columns of the tile that hold entries, CSC order (lets push skip
+                        //        tiles without an active column before reading their metadata)
   uint8_t *payload;     // arena
   uint64_t dense_mask_off;  // start of the Dense row-mask section in the arena
   uint32_t *segs;       // [4*nseg] pull segments

@@ -123,6 +123,7 @@ struct SpmvParams {
   const uint32_t *cb_ptr;
   const uint32_t *csc_rb;
   const uint32_t *csc2csr;
+  const uint16_t *csc_cm;   // columns of each tile with entries, CSC order
   const uint8_t *payload;
   uint64_t dense_mask_off;
   const uint32_t *segs;     // pull segments (pattern matrices: the Boolean pull's)
@@ -170,7 +171,9 @@ DBS_DEV void push_chunk(const SpmvParams &P, uint64_t own, float *sx, float *spa
   const uint32_t m = P.xmask[b] & 0xFFFFu;
   const uint32_t k0 = P.cb_ptr[b] + j * 64u, kend = P.cb_ptr[b + 1];
   const uint32_t k = k0 + (uint32_t)lane;
-  const bool act = k < kend;
+  // a tile without an entry in an active column adds nothing: its metadata
+  // is not read
+  const bool act = k < kend && (P.csc_cm[k < kend ? k : k0] & m) != 0u;
   uint32_t rb = 0;
   uint64_t meta = 0;
   if (act) {
@@ -826,6 +829,7 @@ dbs_status dbs_spmspv_impl(dbs_matrix *A, int32_t nnz_x, const int32_t *x_idx, c
   P.cb_ptr = A->cb_ptr;
   P.csc_rb = A->csc_rb;
   P.csc2csr = A->csc2csr;
+  P.csc_cm = A->csc_cm;
   P.payload = A->payload;
   P.dense_mask_off = A->dense_mask_off;
   P.segs = A->vk == VK_PAT ? A->psegs : A->segs;

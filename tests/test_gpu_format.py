@@ -28,6 +28,7 @@ def _arrays(dbs, A):
         "csc2csr": dbs.dbs_copy_array(A, dbs.DBS_ARR_CSC2CSR),
         "payload": dbs.dbs_copy_array(A, dbs.DBS_ARR_PAYLOAD),
         "segs": dbs.dbs_copy_array(A, dbs.DBS_ARR_SEGMENTS).reshape(-1, 4),
+        "csc_cm": dbs.dbs_copy_array(A, dbs.DBS_ARR_CSC_CM),
     }
 
 
@@ -42,6 +43,10 @@ def check_format(dbs, m, n, rp, ci, vbits, dtype, vk, opt=None, th=(32, 128, 2.0
     np.testing.assert_array_equal(ar["cb_ptr"], tv["cb_ptr"])
     np.testing.assert_array_equal(ar["csc_rb"], tv["csc_rb"])
     np.testing.assert_array_equal(ar["csc2csr"], tv["csc2csr"])
+    # column set of every tile (a bit per column with entries), CSC order
+    has = tv["t_colmask"].reshape(-1, 16) != 0
+    cset = (has * (1 << np.arange(16))).sum(axis=1).astype(np.uint16)
+    np.testing.assert_array_equal(ar["csc_cm"], cset[tv["csc2csr"]])
     st = dbs.dbs_get_stats(A)
     exp_types = tv["t_type"] if force < 0 else np.full(tv["T"], force)
     n_dense = int(np.count_nonzero(exp_types == orc.DENSE))
