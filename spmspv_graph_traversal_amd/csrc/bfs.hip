@@ -225,8 +225,10 @@ struct BfsPol {
   }
 };
 
+// pattern matrices: five waves per SIMD (at most 96 VGPRs), as the Boolean
+// SpMSpV pull
 template <int VK>
-__global__ __launch_bounds__(KT) void k_bfs_level(BfsParams P) {
+__global__ __launch_bounds__(KT, VK == VK_PAT ? 5 : 1) void k_bfs_level(BfsParams P) {
   __shared__ uint32_t s_pat[VK == VK_PAT ? KT / DBS_WAVE : 1][PAT_LDS_WORDS];
   __shared__ uint32_t s_cum[dbs_meta::PUSH_LIST_MAX];
   const int lane = __lane_id();

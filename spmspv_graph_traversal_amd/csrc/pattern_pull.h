@@ -284,8 +284,12 @@ DBS_DEV void pat_finish(const PatSrc &S, const Pol &pol, const PatSeg<K> &a, con
       const auto y = __builtin_amdgcn_raw_buffer_load_b128(S.pay, big ? o + 16u : OOB_OFF, 0, 0);
       const uint32_t rm[8] = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
       uint32_t g = 0;
+      // row r found iff its 16-bit row mask meets the active columns; the
+      // 0/1 bit comes from a carry ((x + 0xFFFF) >> 16), so no per-row
+      // constant is held in a register
 #pragma unroll
-      for (int r = 0; r < 16; ++r) g |= (((rm[r >> 1] >> (16 * (r & 1))) & b.m[k]) != 0u) ? (1u << r) : 0u;
+      for (int r = 0; r < 16; ++r)
+        g |= ((((rm[r >> 1] >> (16 * (r & 1))) & b.m[k]) + 0xFFFFu) >> 16) << r;
       add(k, g);
     }
   }
@@ -294,7 +298,9 @@ DBS_DEV void pat_finish(const PatSrc &S, const Pol &pol, const PatSeg<K> &a, con
     const uint32_t fl = ((uint32_t)lane < a.nrb) ? s_f[lane] & a.needl : 0u;
     const uint64_t any = __ballot(fl != 0u);
     if (fl != 0u) {
-      const int pos = fb.n + __popcll(any & ((1ull << lane) - 1ull));
+      // entries of the lanes below this one (mbcnt: no 64-bit lane mask kept)
+      const int pos = fb.n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(any >> 32),
+                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)any, 0u));
       fb.rb[pos] = a.rb + (uint32_t)lane;
       fb.f[pos] = fl;
     }

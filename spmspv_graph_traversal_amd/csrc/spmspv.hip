@@ -658,11 +658,16 @@ DBS_DEV void pull_or_group(const SpmvParams &P, const PullRes &R, int64_t s0, bo
 
 // PU: segments per wave step of the PLUS_TIMES pull (1 or PULL_U_PLUS_WIDE;
 // 1 for OR_AND), a kernel each so that each has its own register count.
-// The bf16 PLUS_TIMES pull with PU = 1 (the decode layers) runs five waves
-// per SIMD (at most 96 VGPRs), the wide PLUS_TIMES pull four (at most 128);
-// the others keep their own register counts.
+// The bf16 PLUS_TIMES pull with PU = 1 (the decode layers) and the Boolean
+// pull of pattern matrices run five waves per SIMD (at most 96 VGPRs), the
+// wide PLUS_TIMES pull four (at most 128); the others keep their own
+// register counts.
 template <int VK, int SR, int PU>
-__global__ __launch_bounds__(KT, (VK == VK_BF16 && SR == DBS_PLUS_TIMES && PU == 1) ? 5 : PU > 1 ? 4 : 1) void k_spmspv(
+__global__ __launch_bounds__(KT, ((VK == VK_BF16 && SR == DBS_PLUS_TIMES && PU == 1) ||
+                                  (VK == VK_PAT && SR == DBS_OR_AND))
+                                     ? 5
+                                 : PU > 1 ? 4
+                                          : 1) void k_spmspv(
     SpmvParams P) {
   __shared__ float s_x[KT / DBS_WAVE][16];
   __shared__ float s_part[KT / DBS_WAVE][64];
