@@ -39,6 +39,7 @@ coordinates are in the 8-byte metadata word).
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -427,7 +428,11 @@ def bench_decode(dbs, torch, args):
                 log(f"[bench] decode {rows}x{cols} s={sp} z={z}: warm {warm_us:.2f} us, rotating {cold_us:.2f} us")
             if sp == 0.5:
                 out.append(bench_decode_threshold(dbs, torch, args, copies[0], fmt, rows, cols, y))
+            # free this layer's copies here, not inside the next layer's timed calls
+            A = c = None
             del copies
+            gc.collect()
+            torch.cuda.synchronize()
     return out
 
 
