@@ -43,6 +43,28 @@ def test_bfs_rmat_all_paths(dbs, scale):
         assert st["bfs_levels"] == ref.max() + 1  # levels 0..max, the last one finds nothing
 
 
+def test_bfs_push_work_sources(dbs):
+    """Push levels take their work chunks either from the frontier's block list
+    (every call that could push has at most 6144 nonzero blocks) or from chunks
+    the metadata kernel builds ahead (more possible): R-MAT 17 (8192 vertex
+    blocks) with push forced, and with th3 raised to 10% and to 90%."""
+    scale = 17
+    rp, ci = rmat_csr(scale, 16, rng_for("test", 805, scale))
+    n = 1 << scale
+    A = build(dbs, n, n, rp, ci, None, dbs.DBS_PATTERN)
+    lcc = largest_component_vertices(rp, ci, n)
+    src = int(rng_for("test", 806).choice(lcc))
+    ref = orc.bfs(n, rp, ci, src)
+    # forced push (any count possible): chunks built ahead; 10%: at most 819
+    # blocks, from the list; 90%: up to 7372, chunks built ahead
+    for path, num in ((1, 1), (0, 10), (0, 90)):
+        dbs.dbs_set_option(A, dbs.DBS_OPT_PATH, path)
+        dbs.dbs_set_option(A, dbs.DBS_OPT_TH3_NUM, num)
+        np.testing.assert_array_equal(gpu_bfs(dbs, A, n, src), ref, err_msg=f"path {path} th3 {num}%")
+    dbs.dbs_set_option(A, dbs.DBS_OPT_PATH, 0)
+    dbs.dbs_set_option(A, dbs.DBS_OPT_TH3_NUM, 1)
+
+
 def test_bfs_isolated_source_and_ragged(dbs):
     # 50 vertices (ragged last block), a path 0-1-...-9, vertex 20 isolated
     n = 50
