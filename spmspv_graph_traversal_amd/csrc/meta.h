@@ -1,8 +1,10 @@
 // Registration of the nonzero vector blocks (section 4.1 of "DB-SpMSpV:
 // Dual-View Blocked Sparse Matrix-Sparse Vector Multiplication for Dynamic
-// GPU Workloads"): N_nzblk, the compacted list of nonzero blocks and, when
-// the selector will take the push path, its work chunks (64 tiles of one
-// column block each, section 3.3.2).
+// GPU Workloads"): N_nzblk and the compacted list of nonzero blocks.  The
+// push path's work chunks (64 tiles of one column block each, section 3.3.2)
+// are enumerated from that list by the pushing kernel itself
+// (listed_chunks) whenever a push can involve at most PUSH_LIST_MAX blocks;
+// otherwise (Reg::build_chunks) they are cut here, as follows.
 //
 // Same-address device atomics serialize on this GPU (about 11 ns each, one
 // after the other), so a workgroup first counts its blocks over all its

@@ -459,7 +459,9 @@ DBS_DEV void pull_finish(const SpmvParams &P, uint4 seg, uint32_t cb, uint32_t m
 // descriptors, column blocks and (eager) metadata in flight; step i's lazy
 // metadata is issued first in the step.
 // U = 1 when there are too few segments to give every resident wave several
-// (the decode layers), PULL_U_PLUS_WIDE otherwise.
+// (the decode layers), PULL_U_PLUS_WIDE otherwise.  With U = 1 and fewer
+// segments than resident waves, two or four waves share a segment, each
+// taking a range of its lanes (tiles) and adding its rows atomically.
 // ---------------------------------------------------------------------------
 struct AllRows {
   DBS_DEV uint32_t need(uint32_t) const { return 0xFFFFu; }
