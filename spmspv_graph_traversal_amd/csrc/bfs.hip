@@ -243,11 +243,11 @@ __global__ __launch_bounds__(KT, VK == VK_PAT ? 5 : 1) void k_bfs_level(BfsParam
   const int64_t gw = (int64_t)blockIdx.x * (KT / DBS_WAVE) + w;
   const int64_t nw = (int64_t)gridDim.x * (KT / DBS_WAVE);
   if (push) {
+    dbs_meta::Listed L;
     const int64_t nch =
-        P.list_push ? (int64_t)dbs_meta::listed_chunks<KT>(P.cur_list, nz, P.cb_ptr, s_cum) : (int64_t)P.cur_ctr[1];
+        P.list_push ? (int64_t)dbs_meta::listed_chunks<KT>(L, P.cur_list, nz, P.cb_ptr, s_cum) : (int64_t)P.cur_ctr[1];
     for (int64_t c = gw; c < nch; c += nw)
-      bfs_push_chunk<VK>(P, P.list_push ? dbs_meta::listed_chunk(P.cur_list, nz, s_cum, (uint32_t)c) : P.cur_chunks[c],
-                         lane);
+      bfs_push_chunk<VK>(P, P.list_push ? dbs_meta::listed_chunk(L, (uint32_t)c) : P.cur_chunks[c], lane);
   } else {
     constexpr int U = 8;
     const bool eager = (int64_t)nz * 4 > (int64_t)P.nb;

@@ -141,16 +141,36 @@ DBS_DEV void register_blocks(const Reg &o, int64_t nitems, Item item) {
 
 // Push work taken straight from the compacted list: each workgroup lists the
 // chunks (64 tiles of one column block, section 3.3.2) of the n listed blocks
-// on its own, as inclusive prefix sums of their chunk counts in LDS (s_cum,
-// at most PUSH_LIST_MAX entries; returns the number of chunks), and finds
-// chunk c of the grid-stride loop by binary search (listed_chunk).  So no
-// chunk list is built ahead of a call that may not push.  Every thread of the
-// workgroup calls listed_chunks.
+// on its own, as inclusive prefix sums of their chunk counts (returning the
+// number of chunks), and finds chunk c of the grid-stride loop by a search
+// (listed_chunk).  So no chunk list is built ahead of a call that may not
+// push.  Up to 64 blocks each wave keeps the sums in registers (lane i:
+// block i); more go to LDS (s_cum, at most PUSH_LIST_MAX entries), and then
+// every thread of the workgroup calls listed_chunks.
 constexpr int PUSH_LIST_MAX = 6144;
 
+struct Listed {
+  const uint32_t *list, *s_cum;
+  uint32_t n;
+  uint32_t cum, blk;  // n <= 64: this lane's block and inclusive chunk sum
+};
+
 template <int KTH>
-DBS_DEV uint32_t listed_chunks(const uint32_t *list, uint32_t n, const uint32_t *cb_ptr, uint32_t *s_cum) {
+DBS_DEV uint32_t listed_chunks(Listed &L, const uint32_t *list, uint32_t n, const uint32_t *cb_ptr,
+                               uint32_t *s_cum) {
   __shared__ uint32_t s_wtot[KTH / DBS_WAVE];
+  L.list = list;
+  L.s_cum = s_cum;
+  L.n = n;
+  if (n <= (uint32_t)DBS_WAVE) {  // uniform
+    const uint32_t lane = (uint32_t)__lane_id();
+    const bool in = lane < n;
+    const uint32_t b = list[in ? lane : 0u];
+    const uint32_t cnt = in ? (cb_ptr[b + 1] - cb_ptr[b] + 63u) >> 6 : 0u;
+    L.blk = b;
+    L.cum = group_incl_scan_u32<64>(cnt);
+    return (uint32_t)__builtin_amdgcn_readlane((int)L.cum, DBS_WAVE - 1);
+  }
   const uint32_t tid = threadIdx.x;
   for (uint32_t i = tid; i < n; i += KTH) {
     const uint32_t b = list[i];
@@ -174,19 +194,27 @@ DBS_DEV uint32_t listed_chunks(const uint32_t *list, uint32_t n, const uint32_t 
   for (int k = 0; k < w; ++k) off += s_wtot[k];
   for (uint32_t i = i0; i < i1; ++i) s_cum[i] += off;
   __syncthreads();
-  return n ? s_cum[n - 1] : 0u;
+  return s_cum[n - 1];
 }
 
-// chunk c (< the count listed_chunks returned) as (block, chunk of the block << 32)
-DBS_DEV uint64_t listed_chunk(const uint32_t *list, uint32_t n, const uint32_t *s_cum, uint32_t c) {
-  uint32_t lo = 0, hi = n - 1;  // first entry whose inclusive sum exceeds c
+// chunk c (wave-uniform, below the count listed_chunks returned) as (block,
+// chunk of the block << 32); called by every lane of the wave
+DBS_DEV uint64_t listed_chunk(const Listed &L, uint32_t c) {
+  uint32_t lo, before;
+  if (L.n <= (uint32_t)DBS_WAVE) {  // uniform: the first lane whose inclusive sum exceeds c
+    lo = (uint32_t)(__ffsll((unsigned long long)__ballot(L.cum > c)) - 1);
+    before = lo ? (uint32_t)__builtin_amdgcn_readlane((int)L.cum, (int)lo - 1) : 0u;
+    return (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)L.blk, (int)lo) | ((uint64_t)(c - before) << 32);
+  }
+  lo = 0;
+  uint32_t hi = L.n - 1;  // first entry whose inclusive sum exceeds c
   while (lo < hi) {
     const uint32_t mid = (lo + hi) >> 1;
-    if (s_cum[mid] > c) hi = mid;
+    if (L.s_cum[mid] > c) hi = mid;
     else lo = mid + 1;
   }
-  const uint32_t j = c - (lo ? s_cum[lo - 1] : 0u);
-  return (uint64_t)list[lo] | ((uint64_t)j << 32);
+  before = lo ? L.s_cum[lo - 1] : 0u;
+  return (uint64_t)L.list[lo] | ((uint64_t)(c - before) << 32);
 }
 
 // Host side: whether every call whose selector can pick push has at most

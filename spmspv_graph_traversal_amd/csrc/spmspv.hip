@@ -689,9 +689,10 @@ __global__ __launch_bounds__(KT, ((VK == VK_BF16 && SR == DBS_PLUS_TIMES && PU =
     // calls that may push more blocks than the enumeration holds: from the
     // chunk list built ahead
     if (SR == DBS_OR_AND && P.list_push) {  // uniform
-      const uint32_t nch = dbs_meta::listed_chunks<KT>(P.xlist, nz, P.cb_ptr, s_cum);
+      dbs_meta::Listed L;
+      const uint32_t nch = dbs_meta::listed_chunks<KT>(L, P.xlist, nz, P.cb_ptr, s_cum);
       for (int64_t c = gw; c < nch; c += nw)
-        push_chunk<VK, SR>(P, dbs_meta::listed_chunk(P.xlist, nz, s_cum, (uint32_t)c), s_x[w], s_part[w], lane);
+        push_chunk<VK, SR>(P, dbs_meta::listed_chunk(L, (uint32_t)c), s_x[w], s_part[w], lane);
     } else {
       const int64_t nch = (int64_t)P.ctr[1] < P.max_chunks ? (int64_t)P.ctr[1] : P.max_chunks;
       for (int64_t c = gw; c < nch; c += nw) push_chunk<VK, SR>(P, P.chunks[c], s_x[w], s_part[w], lane);
