@@ -272,8 +272,13 @@ __global__ __launch_bounds__(KT, VK == VK_PAT ? 5 : 1) void k_bfs_level(BfsParam
 
 // Frontier metadata: nonzero blocks of `bm`, their list and push chunks;
 // clears `clr_bm` / `clr_ctr` (the buffers two levels back) when given.
+// After the traversal has ended (the level's own frontier, counted in
+// in_ctr, was empty) there is nothing to do: the next frontier is empty, its
+// counters are zero, and the next BFS clears every bitmap at its start.
 __global__ __launch_bounds__(dbs_meta::MT) void k_bfs_meta(const uint32_t *bm, int32_t nb, dbs_meta::Reg reg,
-                                                 uint32_t *clr_bm, uint32_t *clr_ctr, int64_t nwords) {
+                                                 uint32_t *clr_bm, uint32_t *clr_ctr, int64_t nwords,
+                                                 const uint32_t *in_ctr) {
+  if (in_ctr[0] == 0u) return;  // uniform
   const int64_t gs = (int64_t)gridDim.x * dbs_meta::MT;
   if (clr_bm) {
     for (int64_t k = (int64_t)blockIdx.x * dbs_meta::MT + threadIdx.x; k < nwords; k += gs) clr_bm[k] = 0;
@@ -430,7 +435,8 @@ dbs_status dbs_bfs_impl(dbs_matrix *A, int32_t src, int32_t *levels, hipStream_t
       BFS_TRY(hipGetLastError());
       if (timing) BFS_TRY(hipEventRecord(A->ev[3 + 2 * i], s));
       hipLaunchKernelGGL(k_bfs_meta, dim3(mgrid), dim3(dbs_meta::MT), 0, s, (const uint32_t *)P.next_bm, A->nb,
-                         reg_for(nxt), A->bfs_bm + clr * nwords, A->bfs_ctr + 8 * clr, nwords);
+                         reg_for(nxt), A->bfs_bm + clr * nwords, A->bfs_ctr + 8 * clr, nwords,
+                         (const uint32_t *)P.cur_ctr);
       BFS_TRY(hipGetLastError());
     }
     BFS_TRY(hipMemcpyAsync(A->bfs_host, P.hist, B * 4, hipMemcpyDeviceToHost, s));

@@ -160,7 +160,7 @@ struct dbs_matrix {
   dbs_stats st;
   hipStream_t last_stream;
   // BFS: levels launched between two host reads of the frontier sizes
-  static constexpr int kBfsBatch = 4;
+  static constexpr int kBfsBatch = 8;
   hipEvent_t ev[2 + 2 * kBfsBatch];  // BFS timing: whole run, then each level kernel of a batch
   // ring of per-call event quadruples: start and end of the metadata kernel,
   // start and end of the SpMSpV kernel, taken by the dispatches themselves
