@@ -248,3 +248,20 @@ def test_threshold_edge_cases(dbs):
     yr, s = orc.spmspv_dense_x(m, n, rp, ci, v, orc.F32, xz, orc.F32)
     ok, _ = orc.within_tolerance(yt.cpu().numpy(), yr, s)
     assert ok.all()
+
+
+def test_bfs_rmat22_full_size(dbs):
+    """R-MAT scale 22 (edge factor 16, symmetrized), the BFS workload at full
+    size: levels of every vertex, bit-exact against the oracle's queue BFS,
+    for two of the sources the benchmark times (and every path for one)."""
+    rp, ci = rmat_csr(22, 16, rng_for("rmat22"))
+    n = 1 << 22
+    lcc = largest_component_vertices(rp, ci, n)
+    srcs = rng_for("rmat22", 1).choice(lcc, 64, replace=False)[:2]
+    A = build(dbs, n, n, rp, ci, None, dbs.DBS_PATTERN)
+    for k, src in enumerate(srcs):
+        ref = orc.bfs(n, rp, ci, int(src))
+        for path in ((0, 1, 2) if k == 0 else (0,)):
+            dbs.dbs_set_option(A, dbs.DBS_OPT_PATH, path)
+            np.testing.assert_array_equal(gpu_bfs(dbs, A, n, int(src)), ref, err_msg=f"src {src} path {path}")
+    dbs.dbs_set_option(A, dbs.DBS_OPT_PATH, 0)
