@@ -78,3 +78,16 @@ def test_default_build_options(lib):
     assert (o.th0, o.th1, o.th2_num, o.th2_den, o.force_format) == (32, 128, 2, 1, -1)
     assert (o.seg_w_dense, o.seg_w_csr, o.seg_w_coo, o.seg_cap) == (4, 2, 1, 0)
     assert lib.dbs_build_options_default(None) == 1
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # one GPU only: a request for more exits with a message and status 2,
+    # before anything touches a device
+    import subprocess
+    import sys
+
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2", "--steps", "1"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stdout + r.stderr
+    assert r.stdout.strip() == "" or not r.stdout.lstrip().startswith("{")
