@@ -356,7 +356,7 @@ def bench_bfs22(dbs, torch, args):
     dbs.dbs_set_option(A, dbs.DBS_OPT_PATH, 0)
     times = np.array(times)
     gteps = edges / (times * 1e-3) / 1e9
-    return {"workload": "R-MAT scale 22, edge factor 16, symmetrized; 64 sources in the largest component",
+    return {"workload": "R-MAT scale 22, edge factor 16, symmetrized; " + f"{len(srcs)} sources in the largest component",
             "vertices_in_component": int(lcc.shape[0]), "undirected_edges_in_component": edges,
             "gteps_harmonic_mean": round(float(len(gteps) / np.sum(1.0 / gteps)), 2),
             "gteps_median": round(float(np.median(gteps)), 2),
@@ -615,6 +615,10 @@ def main():
                     help="also the tile-format ablation (COO-only / CSR-only / adaptive builds; slow)")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the decode layers (for profiling the decode kernel); prints their JSON")
+    ap.add_argument("--bfs-only", action="store_true",
+                    help="only the R-MAT 22 BFS (for profiling the level kernels); prints its JSON")
+    ap.add_argument("--zipf-only", action="store_true",
+                    help="only the Zipf/band stress matrix (for profiling its pull); prints its JSON")
     ap.add_argument("--headline-only", action="store_true",
                     help="only the timed sweep (for profiling: every SpMSpV launch is one of the timed mix)")
     ap.add_argument("--bfs-sources", type=int, default=64)
@@ -645,6 +649,12 @@ def main():
     torch.cuda.set_device(0)
     if args.decode_only:
         print(json.dumps({"decode": bench_decode(dbs, torch, args)}), flush=True)
+        return
+    if args.bfs_only:
+        print(json.dumps({"bfs_rmat22": bench_bfs22(dbs, torch, args)}), flush=True)
+        return
+    if args.zipf_only:
+        print(json.dumps({"zipf_band": bench_zipf(dbs, torch, args)}), flush=True)
         return
     res = bench_rmat20(dbs, torch, args)
     log(f"[bench] rmat20 sweep: {res['ms_per_step']:.3f} ms/step, {res['value']:.1f} GB/s")
