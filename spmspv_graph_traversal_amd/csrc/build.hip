@@ -24,9 +24,16 @@ constexpr int RB_PER_BLOCK = BT / 16;  // row blocks per block (4 per wave)
 // flags of the CSR validation
 enum { BAD_FIRST = 1, BAD_LAST = 2, BAD_PTR = 4, BAD_COL = 8, BAD_ORDER = 16 };
 
+// Rows with more entries than this are checked by a whole workgroup
+// (k_validate_long): a thread walking a row of a million entries alone would
+// set the time of the whole check.
+constexpr int64_t VAL_LONG = 1024;
+
+// flag[0]: the flags; flag[1]: number of long rows listed in long_rows
+// (room for nnz / (VAL_LONG + 1) + 1 of them)
 __global__ __launch_bounds__(BT) void k_validate(int32_t m, int32_t n, int64_t nnz,
                                                  const int32_t *row_ptr, const int32_t *col_idx,
-                                                 uint32_t *flag) {
+                                                 uint32_t *flag, uint32_t *long_rows) {
   const int64_t i = (int64_t)blockIdx.x * BT + threadIdx.x;
   if (i >= m) return;
   const int64_t a = row_ptr[i], b = row_ptr[i + 1];
@@ -37,6 +44,15 @@ __global__ __launch_bounds__(BT) void k_validate(int32_t m, int32_t n, int64_t n
     atomicOr(flag, f | BAD_PTR);
     return;
   }
+  if (b - a > VAL_LONG) {
+    // rows of valid pointers do not overlap, so at most nnz / (VAL_LONG + 1)
+    // of them are this long; with overlapping pointers BAD_LAST or BAD_PTR
+    // is set somewhere, and the list stops at its room
+    const uint32_t p = atomicAdd(flag + 1, 1u);
+    if ((int64_t)p <= nnz / (VAL_LONG + 1)) long_rows[p] = (uint32_t)i;
+    if (f) atomicOr(flag, f);
+    return;
+  }
   int64_t prev = -1;
   for (int64_t k = a; k < b; ++k) {
     const int64_t c = col_idx[k];
@@ -45,6 +61,26 @@ __global__ __launch_bounds__(BT) void k_validate(int32_t m, int32_t n, int64_t n
     prev = c;
   }
   if (f) atomicOr(flag, f);
+}
+
+// the listed long rows, a workgroup per row: every entry is compared with the
+// one before it in the same row
+__global__ __launch_bounds__(BT) void k_validate_long(int32_t n, int64_t nnz, const int32_t *row_ptr,
+                                                      const int32_t *col_idx, uint32_t *flag,
+                                                      const uint32_t *long_rows) {
+  const uint32_t room = (uint32_t)(nnz / (VAL_LONG + 1) + 1);
+  const uint32_t cnt = flag[1] < room ? flag[1] : room;
+  for (uint32_t j = blockIdx.x; j < cnt; j += gridDim.x) {
+    const int64_t r = long_rows[j];
+    const int64_t a = row_ptr[r], b = row_ptr[r + 1];  // checked by k_validate: 0 <= a <= b <= nnz
+    uint32_t f = 0;
+    for (int64_t k = a + threadIdx.x; k < b; k += BT) {
+      const int64_t c = col_idx[k];
+      if (c < 0 || c >= n) f |= BAD_COL;
+      if (k > a && c <= (int64_t)col_idx[k - 1]) f |= BAD_ORDER;
+    }
+    if (f) atomicOr(flag, f);
+  }
 }
 
 // Rows that hold an entry, 16 bits per row block (two row blocks a word).
@@ -542,11 +578,15 @@ dbs_status dbs_build_impl(dbs_matrix *A, const int32_t *row_ptr, const int32_t *
   const int vk = A->vk;
 
   // --- validate the CSR on the device
-  uint32_t *flag;
-  BUILD_TRY(tmp.get((void **)&flag, 4));
-  BUILD_TRY(hipMemsetAsync(flag, 0, 4, s));
+  uint32_t *flag, *long_rows;
+  BUILD_TRY(tmp.get((void **)&flag, 8));
+  BUILD_TRY(tmp.get((void **)&long_rows, (size_t)(nnz / (VAL_LONG + 1) + 1) * 4));
+  BUILD_TRY(hipMemsetAsync(flag, 0, 8, s));
   hipLaunchKernelGGL(k_validate, dim3(nblocks(m, BT)), dim3(BT), 0, s, m, A->n, nnz, row_ptr,
-                     col_idx, flag);
+                     col_idx, flag, long_rows);
+  BUILD_TRY(hipGetLastError());
+  hipLaunchKernelGGL(k_validate_long, dim3(1024), dim3(BT), 0, s, A->n, nnz, row_ptr, col_idx, flag,
+                     (const uint32_t *)long_rows);
   BUILD_TRY(hipGetLastError());
   uint32_t hflag = 0;
   BUILD_TRY(hipMemcpyAsync(&hflag, flag, 4, hipMemcpyDeviceToHost, s));

@@ -161,3 +161,31 @@ def test_bad_csr_is_rejected(dbs):
         with pytest.raises(dbs.DBSError) as e:
             build(dbs, 2, 4, rp, np.array(bad, np.int32), np.ones(3, np.float32), dbs.DBS_F32)
         assert e.value.status == dbs.DBS_ERR_BAD_CSR
+
+
+def test_bad_csr_in_long_rows_is_rejected(dbs):
+    # rows longer than 1024 entries are checked by a workgroup each: a fault
+    # anywhere in such a row (first entry, a chunk boundary of the workgroup's
+    # threads, the last entry) is still found, and a valid long row passes
+    n = 8192
+    long = np.arange(0, n, 2, dtype=np.int32)  # 4096 sorted columns
+    short = np.array([1, 5], np.int32)
+    rp = np.array([0, 2, 2 + long.size, 4 + long.size], np.int32)
+
+    def ci_with(fix):
+        mid = long.copy()
+        fix(mid)
+        return np.concatenate([short, mid, short])
+
+    A = build(dbs, 3, n, rp, ci_with(lambda c: None), None, dbs.DBS_PATTERN)
+    assert dbs.dbs_get_stats(A)["tiles"] > 0
+    cases = {
+        "first entry out of range": lambda c: c.__setitem__(0, -3),
+        "duplicate at a 256-entry boundary": lambda c: c.__setitem__(256, c[255]),
+        "descending in the middle": lambda c: c.__setitem__(2000, c[1999] - 1),
+        "last entry out of range": lambda c: c.__setitem__(-1, n),
+    }
+    for name, fix in cases.items():
+        with pytest.raises(dbs.DBSError) as e:
+            build(dbs, 3, n, rp, ci_with(fix), None, dbs.DBS_PATTERN)
+        assert e.value.status == dbs.DBS_ERR_BAD_CSR, name
