@@ -45,9 +45,10 @@ __global__ __launch_bounds__(BT) void k_validate(int32_t m, int32_t n, int64_t n
     return;
   }
   if (b - a > VAL_LONG) {
-    // rows of valid pointers do not overlap, so at most nnz / (VAL_LONG + 1)
-    // of them are this long; with overlapping pointers BAD_LAST or BAD_PTR
-    // is set somewhere, and the list stops at its room
+    // when every row passes the pointer check the pointers never decrease,
+    // the rows do not overlap and at most nnz / (VAL_LONG + 1) of them are
+    // this long; otherwise BAD_PTR is set for some row and the list stops at
+    // its room
     const uint32_t p = atomicAdd(flag + 1, 1u);
     if ((int64_t)p <= nnz / (VAL_LONG + 1)) long_rows[p] = (uint32_t)i;
     if (f) atomicOr(flag, f);
