@@ -351,6 +351,11 @@ DBS_DEV uint32_t seg_weight(uint32_t type, const dbs_build_options &o) {
                                 : type == DBS_TILE_COO ? (uint32_t)o.seg_w_coo : (uint32_t)o.seg_w_csr;
 }
 
+// Row blocks of more tiles than this are segmented by a workgroup each
+// (k_segments_long): one thread walking a hub row block's tiles alone would
+// set the time of the whole pass.
+constexpr uint32_t SEG_LONG = 512;
+
 // Pull load balance (section 3.3.2): greedy weighted segments inside each row
 // block.  mode 0 counts, mode 1 writes.
 __global__ void k_segments(int32_t mb, const uint32_t *rb_ptr, const uint32_t *t_nt,
@@ -359,6 +364,7 @@ __global__ void k_segments(int32_t mb, const uint32_t *rb_ptr, const uint32_t *t
   const int32_t rb = (int32_t)(blockIdx.x * blockDim.x + threadIdx.x);
   if (rb >= mb) return;
   const uint32_t t0 = rb_ptr[rb], t1 = rb_ptr[rb + 1];
+  if (t1 - t0 > SEG_LONG) return;  // k_segments_long
   uint32_t nseg = 0, acc = 0, start = t0;
   uint32_t out = mode ? seg_off[rb] : 0;
   const uint32_t split = (mode && seg_cnt[rb] > 1) ? SEG_SPLIT : 0u;
@@ -388,6 +394,77 @@ __global__ void k_segments(int32_t mb, const uint32_t *rb_ptr, const uint32_t *t
     ++nseg;
   }
   if (!mode) seg_cnt[rb] = nseg;
+}
+
+// The same rule for the row blocks of more than SEG_LONG tiles, a workgroup
+// per row block, 256 tiles at a time: an inclusive prefix of the chunk's
+// weights, then each close is the first tile after the previous one whose
+// running weight reaches the cap (one ballot per close).
+__global__ __launch_bounds__(BT) void k_segments_long(int32_t mb, const uint32_t *rb_ptr, const uint32_t *t_nt,
+                                                      dbs_build_options o, uint32_t *seg_cnt,
+                                                      const uint32_t *seg_off, uint32_t *segs, int mode) {
+  __shared__ uint32_t s_pre[BT];
+  __shared__ uint32_t s_min[BT / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const uint32_t cap = (uint32_t)o.seg_cap;
+  for (int32_t rb = (int32_t)blockIdx.x; rb < mb; rb += (int32_t)gridDim.x) {
+    const uint32_t t0 = rb_ptr[rb], t1 = rb_ptr[rb + 1];
+    if (t1 - t0 <= SEG_LONG) continue;  // uniform
+    const uint32_t out = mode ? seg_off[rb] : 0u;
+    const uint32_t split = (mode && seg_cnt[rb] > 1) ? SEG_SPLIT : 0u;
+    uint32_t nseg = 0, start = t0, acc = 0;  // uniform: running weight since the last close
+    for (uint32_t c0 = t0; c0 < t1; c0 += BT) {
+      const uint32_t t = c0 + (uint32_t)tid;
+      const bool in = t < t1;
+      __syncthreads();  // the previous chunk's reads of s_pre are done
+      s_pre[tid] = in ? seg_weight(t_nt[t] >> 16, o) : 0u;
+      __syncthreads();
+      for (int d = 1; d < BT; d <<= 1) {
+        const uint32_t add = tid >= d ? s_pre[tid - d] : 0u;
+        __syncthreads();
+        s_pre[tid] += add;
+        __syncthreads();
+      }
+      const uint32_t pre = s_pre[tid];
+      uint32_t off = 0;  // prefix at the last close inside this chunk
+      int jlast = -1;    // that close's position in the chunk
+      while (true) {     // uniform
+        const bool hit = in && tid > jlast && acc + (pre - off) >= cap;
+        const uint64_t b = __ballot(hit);
+        if (lane == 0) s_min[wv] = b ? (uint32_t)(wv * 64 + __ffsll((unsigned long long)b) - 1) : (uint32_t)BT;
+        __syncthreads();
+        uint32_t j = s_min[0];
+#pragma unroll
+        for (int k = 1; k < BT / 64; ++k) j = s_min[k] < j ? s_min[k] : j;
+        __syncthreads();
+        if (j >= (uint32_t)BT) break;
+        if (mode && tid == 0) {
+          uint32_t *sg = segs + 4 * (uint64_t)(out + nseg);
+          sg[0] = (uint32_t)rb | split;
+          sg[1] = start;
+          sg[2] = c0 + j + 1;
+          sg[3] = 0;
+        }
+        ++nseg;
+        start = c0 + j + 1;
+        off = s_pre[j];
+        acc = 0;
+        jlast = (int)j;
+      }
+      acc += s_pre[BT - 1] - off;
+    }
+    if (start < t1) {
+      if (mode && tid == 0) {
+        uint32_t *sg = segs + 4 * (uint64_t)(out + nseg);
+        sg[0] = (uint32_t)rb | split;
+        sg[1] = start;
+        sg[2] = t1;
+        sg[3] = 0;
+      }
+      ++nseg;
+    }
+    if (!mode && tid == 0) seg_cnt[rb] = nseg;
+  }
 }
 
 __global__ void k_type_stats(const uint32_t *t_nt, int64_t T, unsigned long long *st) {
@@ -703,6 +780,10 @@ dbs_status dbs_build_impl(dbs_matrix *A, const int32_t *row_ptr, const int32_t *
                      (const uint32_t *)t_nt, A->bopt, seg_cnt, (const uint32_t *)nullptr,
                      (uint32_t *)nullptr, 0);
   BUILD_TRY(hipGetLastError());
+  const unsigned lgrid = mb < 2048 ? (unsigned)mb : 2048u;
+  hipLaunchKernelGGL(k_segments_long, dim3(lgrid), dim3(BT), 0, s, mb, (const uint32_t *)A->rb_ptr,
+                     (const uint32_t *)t_nt, A->bopt, seg_cnt, (const uint32_t *)nullptr, (uint32_t *)nullptr, 0);
+  BUILD_TRY(hipGetLastError());
   BUILD_TRY(dbs_scan_u32(seg_cnt, seg_off, mb, stmp, s));
   uint32_t hS = 0;
   BUILD_TRY(hipMemcpyAsync(&hS, seg_off + mb, 4, hipMemcpyDeviceToHost, s));
@@ -712,6 +793,9 @@ dbs_status dbs_build_impl(dbs_matrix *A, const int32_t *row_ptr, const int32_t *
   BUILD_TRY(dbs_dev_alloc(A, (void **)&A->segs, ((size_t)hS + 16) * 16));
   BUILD_TRY(hipMemsetAsync(A->segs + 4 * (size_t)hS, 0, 16 * 16, s));
   hipLaunchKernelGGL(k_segments, dim3(nblocks(mb, BT)), dim3(BT), 0, s, mb, (const uint32_t *)A->rb_ptr,
+                     (const uint32_t *)t_nt, A->bopt, seg_cnt, (const uint32_t *)seg_off, A->segs, 1);
+  BUILD_TRY(hipGetLastError());
+  hipLaunchKernelGGL(k_segments_long, dim3(lgrid), dim3(BT), 0, s, mb, (const uint32_t *)A->rb_ptr,
                      (const uint32_t *)t_nt, A->bopt, seg_cnt, (const uint32_t *)seg_off, A->segs, 1);
   BUILD_TRY(hipGetLastError());
   if (vk == VK_PAT) {

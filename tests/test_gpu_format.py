@@ -189,3 +189,24 @@ def test_bad_csr_in_long_rows_is_rejected(dbs):
         with pytest.raises(dbs.DBSError) as e:
             build(dbs, 3, n, rp, ci_with(fix), None, dbs.DBS_PATTERN)
         assert e.value.status == dbs.DBS_ERR_BAD_CSR, name
+
+
+@pytest.mark.parametrize("cap", [None, 7, 1])
+def test_long_row_blocks_segments(dbs, cap):
+    # row blocks of more than 512 tiles are segmented by a workgroup each; the
+    # segments must still follow the oracle's rule exactly, with the weights of
+    # mixed formats (Dense and CSR-like tiles among COO ones) inside a long row
+    # block and segments closing across its 256-tile chunks
+    rng = rng_for("test", 610)
+    m, n = 40, 16 * 1300
+    a = np.zeros((m, n), np.float32)
+    a[:16] = (rng.random((16, n)) < 0.02) * rng.uniform(-1, 1, (16, n))
+    a[:16, :64] = rng.uniform(0.5, 1, (16, 64))        # Dense tiles
+    a[:16, 800:816][:, :3] = rng.uniform(0.5, 1, (16, 3))  # a column-heavy tile
+    a[16:32, ::37] = 1.0                                 # a second long row block, one column per tile
+    a[35, 5] = 2.0                                       # a short one
+    rp, ci, v = csr_of(a)
+    opt = None if cap is None else options(dbs, seg_cap=cap)
+    _, tv = check_format(dbs, m, n, rp, ci, v, dbs.DBS_F32, 0, opt=opt, cap=cap)
+    assert np.diff(tv["rb_ptr"]).max() > 1024
+    check_format(dbs, m, n, rp, ci, None, dbs.DBS_PATTERN, 2, opt=opt, cap=cap)
