@@ -176,7 +176,11 @@ dbs_status dbs_spmspv_dense_threshold(dbs_handle A, const void *x, float thresho
  *   src      source vertex, 0 <= src < m
  *   levels   device int32[m]: hop distance from src, -1 if unreachable
  *
- * Synchronizes the stream once per level to read the frontier size.
+ * SYNCHRONOUS on `stream`: the levels are launched in batches of eight and
+ * the host reads the frontier sizes of a batch once (one stream
+ * synchronization per eight levels); the levels of the last batch that come
+ * after the first empty frontier return at once.  Uses device scratch that
+ * the handle allocates on the first call (bitmaps, block lists, counters).
  */
 dbs_status dbs_bfs(dbs_handle A, int32_t src, int32_t *levels, void *stream);
 
@@ -190,7 +194,17 @@ enum {
                                     the row microkernel, the faster one on this GPU) */
   DBS_OPT_TIMING = 4,            /* 1: time the kernels of each call with HIP events (setting
                                     it, to 0 or 1, also clears the sums in dbs_stats) */
-  DBS_OPT_CHECK = 5              /* 1: validate x_idx ordering on the device */
+  DBS_OPT_CHECK = 5,             /* 1: validate x_idx ordering on the device */
+  DBS_OPT_PULL_WIDTH = 6,        /* PLUS_TIMES pull of a value matrix, segments per wave
+                                    step: 0 auto (default: four when every resident wave
+                                    gets several steps, else one), 1 or 4 forced */
+  DBS_OPT_PULL_SHARE = 7         /* PLUS_TIMES pull with one segment per step: waves that
+                                    share a segment, each taking a range of its tiles:
+                                    0 auto (default: enough to give every resident wave
+                                    work, at most 4), 1, 2 or 4 forced.  Ignored with four
+                                    segments per step.  Both options change only the work
+                                    split (and the fp32 summation order), not the result's
+                                    bound; they exist to test and measure every variant */
 };
 dbs_status dbs_set_option(dbs_handle A, int32_t option, int64_t value);
 dbs_status dbs_get_option(dbs_handle A, int32_t option, int64_t *value);
@@ -221,7 +235,8 @@ typedef struct {
   /* last dbs_bfs call */
   int32_t bfs_levels;              /* levels run (including the empty last one) */
   int32_t bfs_push_levels;         /* of which push */
-  int64_t bfs_reached;             /* vertices with a level >= 0 */
+  int64_t bfs_reached;             /* vertices with a level >= 0 (counted from the handle's
+                                      visited bitmap when dbs_get_stats is called) */
   float bfs_ms;                    /* whole BFS (DBS_OPT_TIMING), else -1 */
   float bfs_kernel_ms;             /* sum of the level kernels (DBS_OPT_TIMING), else -1 */
 } dbs_stats;

@@ -26,6 +26,7 @@ DBS_TILE_COO, DBS_TILE_DENSE, DBS_TILE_FORCE_CSR, DBS_TILE_FORCE_CSC, DBS_TILE_C
 # options
 DBS_OPT_PATH, DBS_OPT_TH3_NUM, DBS_OPT_TH3_DEN = 0, 1, 2
 DBS_OPT_LOCAL_PUSH_CUTOFF, DBS_OPT_TIMING, DBS_OPT_CHECK = 3, 4, 5
+DBS_OPT_PULL_WIDTH, DBS_OPT_PULL_SHARE = 6, 7
 # exported arrays
 (DBS_ARR_RB_PTR, DBS_ARR_T_CB, DBS_ARR_T_META, DBS_ARR_CB_PTR, DBS_ARR_CSC_RB, DBS_ARR_CSC2CSR,
  DBS_ARR_PAYLOAD, DBS_ARR_SEGMENTS, DBS_ARR_XMASK, DBS_ARR_ACTIVE, DBS_ARR_CSC_CM) = range(11)

@@ -9,6 +9,7 @@
 #include <new>
 
 #include "common.h"
+#include "meta.h"
 
 hipError_t dbs_note(hipError_t e, const char *file, int line) {
   static const int verbose = getenv("DBS_VERBOSE") != nullptr;
@@ -185,6 +186,8 @@ dbs_status dbs_build(int32_t m, int32_t n, int64_t nnz, const int32_t *row_ptr, 
   A->opt[DBS_OPT_LOCAL_PUSH_CUTOFF] = 0;
   A->opt[DBS_OPT_TIMING] = 0;
   A->opt[DBS_OPT_CHECK] = 0;
+  A->opt[DBS_OPT_PULL_WIDTH] = 0;
+  A->opt[DBS_OPT_PULL_SHARE] = 0;
   A->st.last_path = -1;
   A->st.last_meta_ms = -1.0f;
   A->st.last_compute_ms = -1.0f;
@@ -283,6 +286,12 @@ dbs_status dbs_set_option(dbs_handle A, int32_t option, int64_t value) {
     case DBS_OPT_CHECK:
       if (value != 0 && value != 1) return DBS_ERR_INVALID_ARG;
       break;
+    case DBS_OPT_PULL_WIDTH:
+      if (value != 0 && value != 1 && value != 4) return DBS_ERR_INVALID_ARG;
+      break;
+    case DBS_OPT_PULL_SHARE:
+      if (value != 0 && value != 1 && value != 2 && value != 4) return DBS_ERR_INVALID_ARG;
+      break;
     default:
       return DBS_ERR_INVALID_ARG;
   }
@@ -291,7 +300,7 @@ dbs_status dbs_set_option(dbs_handle A, int32_t option, int64_t value) {
 }
 
 dbs_status dbs_get_option(dbs_handle A, int32_t option, int64_t *value) {
-  if (!A || !value || option < 0 || option > DBS_OPT_CHECK) return DBS_ERR_INVALID_ARG;
+  if (!A || !value || option < 0 || option > DBS_OPT_PULL_SHARE) return DBS_ERR_INVALID_ARG;
   *value = A->opt[option];
   return DBS_OK;
 }
@@ -305,17 +314,19 @@ dbs_status dbs_get_stats(dbs_handle A, dbs_stats *out) {
     uint32_t h[8];
     API_TRY(hipMemcpyAsync(h, c, sizeof h, hipMemcpyDeviceToHost, A->last_stream));
     API_TRY(hipStreamSynchronize(A->last_stream));
-    A->st.last_n_nzblk = (int32_t)h[0];
+    const uint32_t nz = dbs_meta::nzblk_clamped(h[0], A->nb);
+    A->st.last_n_nzblk = (int32_t)nz;
     A->st.last_push_chunks = h[1];
-    const int64_t fp = A->opt[DBS_OPT_PATH];
-    const bool push = fp == 1 || (fp == 0 && (int64_t)h[0] * A->opt[DBS_OPT_TH3_DEN] <
-                                                 (int64_t)A->nb * A->opt[DBS_OPT_TH3_NUM]);
+    const bool push = dbs_meta::selector_push(nz, A->nb, (int32_t)A->opt[DBS_OPT_PATH], A->opt[DBS_OPT_TH3_NUM],
+                                              A->opt[DBS_OPT_TH3_DEN]);
     A->st.last_path = push ? 0 : 1;
     if (h[2]) ret = DBS_ERR_BAD_VECTOR;
   } else {
     API_TRY(hipStreamSynchronize(A->last_stream));
   }
   API_TRY(fold_all(A));
+  const dbs_status sr = dbs_bfs_count_reached(A);
+  if (sr != DBS_OK) return sr;
   *out = A->st;
   return ret;
 }

@@ -25,7 +25,7 @@
 // kernel records its frontier's nonzero-block count, and one read of those
 // counts per batch finds the first empty frontier, where the traversal ends.
 // Levels of a batch past that point see an empty frontier and return at
-// once (no vertex is found, nothing is written but cleared buffers).
+// once (no vertex is found, nothing is written but cleared counters).
 #include "meta.h"
 #include "pattern_pull.h"
 #include "tile_kernels.h"
@@ -233,11 +233,12 @@ __global__ __launch_bounds__(KT, VK == VK_PAT ? 5 : 1) void k_bfs_level(BfsParam
   __shared__ uint32_t s_cum[dbs_meta::PUSH_LIST_MAX];
   const int lane = __lane_id();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / DBS_WAVE);
-  const uint32_t nz = P.cur_ctr[0];
+  // the frontier's blocks are registered once each (one per nonzero bitmap
+  // word half), so the count is at most nb; clamped all the same
+  const uint32_t nz = dbs_meta::nzblk_clamped(P.cur_ctr[0], P.nb);
   if (P.phase == 0 && blockIdx.x == 0 && threadIdx.x == 0) P.hist[P.level % dbs_matrix::kBfsBatch] = nz;
   if (nz == 0u) return;  // uniform: empty frontier, nothing to find
-  const bool push = P.force_path == 1 ||
-                    (P.force_path == 0 && (int64_t)nz * P.th3_den < (int64_t)P.nb * P.th3_num);
+  const bool push = dbs_meta::selector_push(nz, P.nb, P.force_path, P.th3_num, P.th3_den);
   // the second launch only pulls the remaining segments of a pattern matrix
   if (P.phase != 0 && (push || VK != VK_PAT)) return;  // uniform
   const int64_t gw = (int64_t)blockIdx.x * (KT / DBS_WAVE) + w;
@@ -273,12 +274,17 @@ __global__ __launch_bounds__(KT, VK == VK_PAT ? 5 : 1) void k_bfs_level(BfsParam
 // Frontier metadata: nonzero blocks of `bm`, their list and push chunks;
 // clears `clr_bm` / `clr_ctr` (the buffers two levels back) when given.
 // After the traversal has ended (the level's own frontier, counted in
-// in_ctr, was empty) there is nothing to do: the next frontier is empty, its
-// counters are zero, and the next BFS clears every bitmap at its start.
+// in_ctr, was empty) only the counters two levels back are cleared: the next
+// frontier is empty and its counters are zero already, and with those
+// cleared too every later level of the batch sees an empty frontier and
+// returns at once (the bitmaps are cleared by the next BFS's start).
 __global__ __launch_bounds__(dbs_meta::MT) void k_bfs_meta(const uint32_t *bm, int32_t nb, dbs_meta::Reg reg,
                                                  uint32_t *clr_bm, uint32_t *clr_ctr, int64_t nwords,
                                                  const uint32_t *in_ctr) {
-  if (in_ctr[0] == 0u) return;  // uniform
+  if (in_ctr[0] == 0u) {  // uniform
+    if (clr_ctr && blockIdx.x == 0 && threadIdx.x < 8) clr_ctr[threadIdx.x] = 0;
+    return;
+  }
   const int64_t gs = (int64_t)gridDim.x * dbs_meta::MT;
   if (clr_bm) {
     for (int64_t k = (int64_t)blockIdx.x * dbs_meta::MT + threadIdx.x; k < nwords; k += gs) clr_bm[k] = 0;
@@ -315,6 +321,27 @@ __global__ void k_bfs_init(int32_t *levels, int32_t m, uint32_t *bm3, int64_t bm
   if (i == 0) list0[0] = b;
 }
 
+// Vertices reached by the last BFS: the visited bitmap holds every row
+// without an entry (set at the start: such a row cannot be reached) and the
+// reached rows, so the reached rows are the visited rows that hold an entry,
+// plus the source when its row holds none.  One workgroup sum, one atomic
+// per workgroup.
+__global__ __launch_bounds__(256) void k_bfs_reached(const uint32_t *vis, const uint32_t *rows_nz, int64_t nwords,
+                                                     uint32_t *out) {
+  __shared__ uint32_t s_w[256 / DBS_WAVE];
+  uint32_t c = 0;
+  for (int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x; k < nwords; k += (int64_t)gridDim.x * 256)
+    c += (uint32_t)__popc(vis[k] & rows_nz[k]);
+  c = group_sum_u32<64>(c);
+  if (__lane_id() == 0) s_w[threadIdx.x / DBS_WAVE] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t t = 0;
+    for (int i = 0; i < 256 / DBS_WAVE; ++i) t += s_w[i];
+    if (t) atomicAdd(out, t);
+  }
+}
+
 }  // namespace
 
 #define BFS_TRY(expr)                                                                            \
@@ -333,7 +360,7 @@ dbs_status dbs_bfs_impl(dbs_matrix *A, int32_t src, int32_t *levels, hipStream_t
     BFS_TRY(dbs_dev_alloc(A, (void **)&A->bfs_vis, (size_t)(nwords + 1) * 4));
     BFS_TRY(dbs_dev_alloc(A, (void **)&A->bfs_list, (size_t)(3 * (int64_t)A->nb + 1) * 4));
     BFS_TRY(dbs_dev_alloc(A, (void **)&A->bfs_chunks, (size_t)(3 * chunk_cap + 1) * 8));
-    BFS_TRY(dbs_dev_alloc(A, (void **)&A->bfs_ctr, (24 + dbs_matrix::kBfsBatch) * 4));
+    BFS_TRY(dbs_dev_alloc(A, (void **)&A->bfs_ctr, (24 + dbs_matrix::kBfsBatch + 1) * 4));
     BFS_TRY(hipHostMalloc((void **)&A->bfs_host, 64, hipHostMallocDefault));
   }
   const bool timing = A->opt[DBS_OPT_TIMING] != 0;
@@ -447,9 +474,8 @@ dbs_status dbs_bfs_impl(dbs_matrix *A, int32_t src, int32_t *levels, hipStream_t
         L = (int32_t)(L0 + i);
         break;
       }
-      const bool was_push = A->opt[DBS_OPT_PATH] == 1 ||
-                            (A->opt[DBS_OPT_PATH] == 0 &&
-                             (int64_t)nz * A->opt[DBS_OPT_TH3_DEN] < (int64_t)A->nb * A->opt[DBS_OPT_TH3_NUM]);
+      const bool was_push = dbs_meta::selector_push(nz, A->nb, (int32_t)A->opt[DBS_OPT_PATH],
+                                                    A->opt[DBS_OPT_TH3_NUM], A->opt[DBS_OPT_TH3_DEN]);
       push_levels += was_push ? 1 : 0;
       if (timing) {
         float ms = 0.0f;
@@ -471,7 +497,28 @@ dbs_status dbs_bfs_impl(dbs_matrix *A, int32_t src, int32_t *levels, hipStream_t
   }
   A->st.bfs_levels = L;
   A->st.bfs_push_levels = push_levels;
-  A->st.bfs_reached = -1;
+  A->st.bfs_reached = -1;  // counted from the visited bitmap when the statistics are read
+  A->bfs_src = src;
   A->last_stream = s;
+  return DBS_OK;
+}
+
+dbs_status dbs_bfs_count_reached(dbs_matrix *A) {
+  if (!A->bfs_vis || A->st.bfs_levels <= 0 || A->st.bfs_reached >= 0) return DBS_OK;
+  const int64_t nwords = ((int64_t)A->nb + 1) / 2;
+  hipStream_t s = A->last_stream;
+  // the counter: the slot after the batch's frontier sizes
+  uint32_t *cnt = A->bfs_ctr + 24 + dbs_matrix::kBfsBatch;
+  BFS_TRY(hipMemsetAsync(cnt, 0, 4, s));
+  const int64_t g = (nwords + 255) / 256;
+  hipLaunchKernelGGL(k_bfs_reached, dim3((unsigned)(g < 1024 ? (g < 1 ? 1 : g) : 1024)), dim3(256), 0, s,
+                     (const uint32_t *)A->bfs_vis, (const uint32_t *)A->rows_nz, nwords, cnt);
+  BFS_TRY(hipGetLastError());
+  uint32_t h = 0, src_word = 0;
+  BFS_TRY(hipMemcpyAsync(&h, cnt, 4, hipMemcpyDeviceToHost, s));
+  BFS_TRY(hipMemcpyAsync(&src_word, A->rows_nz + ((uint32_t)A->bfs_src >> 5), 4, hipMemcpyDeviceToHost, s));
+  BFS_TRY(hipStreamSynchronize(s));
+  const bool src_has_entry = (src_word >> ((uint32_t)A->bfs_src & 31u)) & 1u;
+  A->st.bfs_reached = (int64_t)h + (src_has_entry ? 0 : 1);
   return DBS_OK;
 }

@@ -37,8 +37,28 @@ struct Reg {
   int32_t build_chunks;  // 0: the pushing kernel enumerates the chunks from the list itself
 };
 
+// The selector of section 3.3.1 on an integer count: push iff the path is
+// forced to push, or it is automatic and N_nzblk / N_blk < th3 = num / den.
+__host__ __device__ inline bool selector_push(uint32_t nz, int32_t nb, int32_t force_path, int64_t th3_num,
+                                              int64_t th3_den) {
+  return force_path == 1 || (force_path == 0 && (int64_t)nz * th3_den < (int64_t)nb * th3_num);
+}
+
+// N_nzblk as every consumer of the count uses it.  The registration counts
+// one list entry per leader (an x entry whose predecessor lies in another
+// vector block).  A strictly increasing x_idx has exactly one leader per
+// nonzero block, so the count is at most nb; an x_idx that is not strictly
+// increasing may have several leaders per block (up to 16 nb counted), and
+// the list holds only nb entries.  Every position below the clamped count
+// has been written with a valid block (workgroups reserve contiguous ranges
+// from 0 and write each position below the list's capacity), so reading the
+// list up to the clamped count stays in bounds whatever x_idx holds.
+__host__ __device__ inline uint32_t nzblk_clamped(uint32_t raw, int32_t nb) {
+  return raw < (uint32_t)nb ? raw : (uint32_t)nb;
+}
+
 DBS_DEV bool takes_push(const Reg &o, uint32_t nz) {
-  return o.force_path == 1 || (o.force_path == 0 && (int64_t)nz * o.th3_den < (int64_t)o.nb * o.th3_num);
+  return selector_push(nzblk_clamped(nz, o.nb), o.nb, o.force_path, o.th3_num, o.th3_den);
 }
 
 // exclusive workgroup scan; total in t
@@ -159,6 +179,10 @@ template <int KTH>
 DBS_DEV uint32_t listed_chunks(Listed &L, const uint32_t *list, uint32_t n, const uint32_t *cb_ptr,
                                uint32_t *s_cum) {
   __shared__ uint32_t s_wtot[KTH / DBS_WAVE];
+  // a pushing call that enumerates from the list has n <= PUSH_LIST_MAX
+  // (push_from_list and the clamped count guarantee it); the clamp keeps
+  // s_cum in bounds even if a caller broke that
+  n = n < (uint32_t)PUSH_LIST_MAX ? n : (uint32_t)PUSH_LIST_MAX;
   L.list = list;
   L.s_cum = s_cum;
   L.n = n;

@@ -678,9 +678,8 @@ __global__ __launch_bounds__(KT, ((VK == VK_BF16 && SR == DBS_PLUS_TIMES && PU =
   __shared__ uint32_t s_pat[VK == VK_PAT && SR == DBS_OR_AND ? KT / DBS_WAVE : 1][PAT_LDS_WORDS];
   const int lane = __lane_id();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / DBS_WAVE);
-  const uint32_t nz = P.ctr[0];
-  const bool push = P.force_path == 1 ||
-                    (P.force_path == 0 && (int64_t)nz * P.th3_den < (int64_t)P.nb * P.th3_num);
+  const uint32_t nz = dbs_meta::nzblk_clamped(P.ctr[0], P.nb);
+  const bool push = dbs_meta::selector_push(nz, P.nb, P.force_path, P.th3_num, P.th3_den);
   const int64_t gw = (int64_t)blockIdx.x * (KT / DBS_WAVE) + w;
   const int64_t nw = (int64_t)gridDim.x * (KT / DBS_WAVE);
   if (push) {
@@ -736,15 +735,15 @@ void launch_k(K kernel, dim3 grid, dim3 block, hipStream_t s, hipEvent_t e0, hip
 }
 
 template <int VK, int SR, int PU = 1>
-void launch_spmspv(SpmvParams P, int64_t waves, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+void launch_spmspv(SpmvParams P, int64_t waves, int share, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   static const unsigned resident = dbs_resident_groups(k_spmspv<VK, SR, PU>, KT);
   P.plus_parts = 1;
   if (SR == DBS_PLUS_TIMES && PU == 1 && P.nseg > 0) {
     // fewer segments than resident waves: waves share segments by lane
-    // range, so that every resident wave has work
+    // range, so that every resident wave has work (or as forced)
     const int64_t rw = (int64_t)resident * (KT / DBS_WAVE);
     const int64_t parts = (rw + P.nseg - 1) / P.nseg;
-    P.plus_parts = parts >= PLUS_MAX_PARTS ? PLUS_MAX_PARTS : parts >= 2 ? 2 : 1;
+    P.plus_parts = share ? share : parts >= PLUS_MAX_PARTS ? PLUS_MAX_PARTS : parts >= 2 ? 2 : 1;
     if (P.nseg * P.plus_parts > waves) waves = P.nseg * P.plus_parts;
   }
   launch_k(k_spmspv<VK, SR, PU>, dim3(grid_for(waves, resident)), dim3(KT), s, e0, e1, P);
@@ -869,23 +868,27 @@ dbs_status dbs_spmspv_impl(dbs_matrix *A, int32_t nnz_x, const int32_t *x_idx, c
       n = 256;
     return n;
   }();
-  P.plus_u = A->nseg >= (int64_t)PULL_U_PLUS_WIDE * 32 * cus * 4 ? PULL_U_PLUS_WIDE : 1;
+  const int64_t fw = A->opt[DBS_OPT_PULL_WIDTH];
+  P.plus_u = fw == 1 ? 1
+             : fw == 4 ? PULL_U_PLUS_WIDE
+                       : (A->nseg >= (int64_t)PULL_U_PLUS_WIDE * 32 * cus * 4 ? PULL_U_PLUS_WIDE : 1);
+  const int share = (int)A->opt[DBS_OPT_PULL_SHARE];
   const int pu = sr == DBS_PLUS_TIMES ? P.plus_u : A->vk == VK_PAT ? 1 : PULL_U_OR;
   const int64_t pull_waves = (P.nseg + pu - 1) / pu;
   const int64_t waves = pull_waves > A->max_chunks ? pull_waves : A->max_chunks;
   const int vk = A->vk;
   if (sr == DBS_OR_AND) {
-    if (vk == VK_F32) launch_spmspv<VK_F32, DBS_OR_AND>(P, waves, s, c0, c1);
-    else if (vk == VK_BF16) launch_spmspv<VK_BF16, DBS_OR_AND>(P, waves, s, c0, c1);
-    else launch_spmspv<VK_PAT, DBS_OR_AND>(P, waves, s, c0, c1);
+    if (vk == VK_F32) launch_spmspv<VK_F32, DBS_OR_AND>(P, waves, 0, s, c0, c1);
+    else if (vk == VK_BF16) launch_spmspv<VK_BF16, DBS_OR_AND>(P, waves, 0, s, c0, c1);
+    else launch_spmspv<VK_PAT, DBS_OR_AND>(P, waves, 0, s, c0, c1);
   } else {
     const bool wide = P.plus_u == PULL_U_PLUS_WIDE;
     if (vk == VK_F32) {
-      if (wide) launch_spmspv<VK_F32, DBS_PLUS_TIMES, PULL_U_PLUS_WIDE>(P, waves, s, c0, c1);
-      else launch_spmspv<VK_F32, DBS_PLUS_TIMES, 1>(P, waves, s, c0, c1);
+      if (wide) launch_spmspv<VK_F32, DBS_PLUS_TIMES, PULL_U_PLUS_WIDE>(P, waves, share, s, c0, c1);
+      else launch_spmspv<VK_F32, DBS_PLUS_TIMES, 1>(P, waves, share, s, c0, c1);
     } else {
-      if (wide) launch_spmspv<VK_BF16, DBS_PLUS_TIMES, PULL_U_PLUS_WIDE>(P, waves, s, c0, c1);
-      else launch_spmspv<VK_BF16, DBS_PLUS_TIMES, 1>(P, waves, s, c0, c1);
+      if (wide) launch_spmspv<VK_BF16, DBS_PLUS_TIMES, PULL_U_PLUS_WIDE>(P, waves, share, s, c0, c1);
+      else launch_spmspv<VK_BF16, DBS_PLUS_TIMES, 1>(P, waves, share, s, c0, c1);
     }
   }
   SPMV_TRY(hipGetLastError());

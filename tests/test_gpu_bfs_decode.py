@@ -41,6 +41,7 @@ def test_bfs_rmat_all_paths(dbs, scale):
             np.testing.assert_array_equal(gpu_bfs(dbs, A, n, src), ref, err_msg=f"src {src} path {path}")
         st = dbs.dbs_get_stats(A)
         assert st["bfs_levels"] == ref.max() + 1  # levels 0..max, the last one finds nothing
+        assert st["bfs_reached"] == np.count_nonzero(ref >= 0)
 
 
 def test_bfs_push_work_sources(dbs):
@@ -76,7 +77,13 @@ def test_bfs_isolated_source_and_ragged(dbs):
     for dt, vv in (("pattern", None), ("f32", v)):
         A = build(dbs, n, n, rp, ci, vv, dbs.DBS_PATTERN if vv is None else dbs.DBS_F32)
         for src in (0, 5, 20, 49):
-            np.testing.assert_array_equal(gpu_bfs(dbs, A, n, src), orc.bfs(n, rp, ci, src), err_msg=f"{dt} {src}")
+            ref = orc.bfs(n, rp, ci, src)
+            np.testing.assert_array_equal(gpu_bfs(dbs, A, n, src), ref, err_msg=f"{dt} {src}")
+            # reached vertices, counted from the visited bitmap (an isolated
+            # source, whose row holds no entry, counts itself)
+            st = dbs.dbs_get_stats(A)
+            assert st["bfs_reached"] == np.count_nonzero(ref >= 0), f"{dt} {src}"
+            assert st["bfs_levels"] == ref.max() + 1
 
 
 def test_bfs_directed_follows_y_equals_Ax(dbs):

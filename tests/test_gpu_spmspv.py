@@ -291,3 +291,39 @@ def test_rmat20_or_and_sweep_full_size(dbs):
         if density <= 0.01:
             dbs.dbs_set_option(A, dbs.DBS_OPT_PATH, 1)
             np.testing.assert_array_equal(run_or(dbs, A, n, xi), yr, err_msg=f"push {density}")
+
+
+@pytest.mark.parametrize("kind", ["alternating", "permuted"])
+def test_unsorted_x_is_memory_safe(dbs, kind):
+    """An x_idx that is not strictly increasing registers a block once per
+    leader (an entry whose predecessor is in another block): up to 16 nb
+    entries for nb list slots.  Every consumer clamps the count to nb, and a
+    push that enumerates its chunks from the list stays within the LDS prefix
+    array.  With nb = 6144 a forced push enumerates from the list and the raw
+    count reaches 16 nb = 98,304.  y is unspecified for such input: the calls
+    must return, report at most nb blocks and export at most nb of them, and
+    the next (sorted) call must be exact."""
+    n, m = 6144 * 16, 3000
+    rp, ci, v = uniform_csr(m, n, 6, rng_for("test", 780))
+    A = build(dbs, m, n, rp, ci, v, dbs.DBS_F32)
+    P = build(dbs, m, n, rp, ci, None, dbs.DBS_PATTERN)
+    if kind == "alternating":
+        bad = np.tile(np.array([0, 16], np.int32), n // 2)
+    else:
+        bad = rng_for("test", 781).permutation(n).astype(np.int32)
+    bv = np.ones(bad.shape[0], np.float32)
+    good, gv = sparse_x(n, 0.0005, rng_for("test", 782))
+    yr, s = orc.spmspv_pull(m, n, rp, ci, v, orc.F32, good, gv, orc.F32)
+    yb = orc.or_and_pull(m, n, rp, ci, good)
+    for path in PATHS:
+        for H in (A, P):
+            dbs.dbs_set_option(H, dbs.DBS_OPT_PATH, path)
+        run_plus(dbs, A, m, bad, bv)
+        st = dbs.dbs_get_stats(A)
+        assert 0 <= st["last_n_nzblk"] <= n // 16
+        assert dbs.dbs_copy_array(A, dbs.DBS_ARR_ACTIVE).shape[0] <= n // 16
+        run_or(dbs, P, m, bad)
+        st = dbs.dbs_get_stats(P)
+        assert 0 <= st["last_n_nzblk"] <= n // 16
+        assert_close(run_plus(dbs, A, m, good, gv), yr, s, f"sorted call after unsorted, path {path}")
+        np.testing.assert_array_equal(run_or(dbs, P, m, good), yb, err_msg=f"path {path}")

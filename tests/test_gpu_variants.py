@@ -1,0 +1,144 @@
+"""Every kernel variant and every forced tile format against the CPU oracle.
+
+* The PLUS_TIMES pull of a value matrix runs one or four segments per wave
+  step, and with one segment per step two or four waves may share a segment;
+  DBS_OPT_PULL_WIDTH / DBS_OPT_PULL_SHARE force each variant, so each
+  instantiation of the pull kernel (f32 and bf16) meets the oracle on tiles of
+  every format, including the Dense tiles the four-segment variant routes
+  through the row-per-lane path.
+* force_format stores every tile in one format (the format ablation of the
+  DB-SpMSpV paper, Figure 10); SpMSpV (both semirings, every path) and BFS run
+  on each such build.
+
+fp32: |y - y_ref| <= 1e-5 * sum|a*x| + 1e-6 per entry; OR-AND and BFS levels:
+exact.
+"""
+import numpy as np
+import pytest
+
+import oracle as orc
+from gpu_helpers import bf16_csr_of, build, csr_of, mixed_tile_dense, options, up
+from synth import f32_to_bf16_bits, rng_for, sparse_x
+
+pytestmark = pytest.mark.gpu
+
+PATHS = [0, 1, 2]  # auto, push, pull
+
+
+@pytest.fixture(scope="module")
+def dbs():
+    import spmspv_graph_traversal_amd as d
+
+    return d
+
+
+def run_plus(dbs, A, m, xi, xv, bf16=False):
+    import torch
+
+    y = torch.full((m,), float("nan"), dtype=torch.float32, device="cuda")
+    xv_t = up(np.asarray(xv, np.uint16).view(np.int16)) if bf16 else up(np.asarray(xv, np.float32))
+    dbs.dbs_spmspv(A, up(np.asarray(xi, np.int32)), xv_t, dbs.DBS_PLUS_TIMES, y)
+    return y.cpu().numpy()
+
+
+def run_or(dbs, A, m, xi):
+    import torch
+
+    y = torch.full((m,), 7, dtype=torch.uint8, device="cuda")
+    dbs.dbs_spmspv(A, up(np.asarray(xi, np.int32)), None, dbs.DBS_OR_AND, y)
+    return y.cpu().numpy()
+
+
+def run_bfs(dbs, A, n, src):
+    import torch
+
+    lv = torch.full((n,), -7, dtype=torch.int32, device="cuda")
+    dbs.dbs_bfs(A, src, lv)
+    return lv.cpu().numpy()
+
+
+def assert_close(y, yr, s, what=""):
+    ok, err = orc.within_tolerance(y, yr, s)
+    assert ok.all(), f"{what}: {np.count_nonzero(~ok)} entries out of tolerance, max err {err.max():.3g}"
+
+
+WIDTH_SHARE = [(1, 1), (1, 2), (1, 4), (4, 0)]
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+@pytest.mark.parametrize("cap", [64, 13])
+def test_plus_times_pull_variants_mixed_formats(dbs, seed, cap):
+    """Tiles of every format, long row blocks (split into several segments)
+    and a ragged edge, through every pull variant, f32 and bf16."""
+    a = mixed_tile_dense(seed, mb=4, nb=40)
+    m, n = a.shape
+    opt = options(dbs, seg_cap=cap)
+    rp, ci, v = csr_of(a)
+    _, _, bits = bf16_csr_of(a)
+    A = build(dbs, m, n, rp, ci, v, dbs.DBS_F32, opt)
+    B = build(dbs, m, n, rp, ci, bits, dbs.DBS_BF16, opt)
+    st = dbs.dbs_get_stats(A)
+    assert st["tiles_by_format"][dbs.DBS_TILE_DENSE] > 0 and st["tiles_by_format"][dbs.DBS_TILE_CSR] > 0
+    for density in (0.01, 0.2, 1.0):
+        xi, xv = sparse_x(n, density, rng_for("test", 900, seed, cap, int(density * 100)))
+        xb = f32_to_bf16_bits(xv)
+        yr, s = orc.spmspv_pull(m, n, rp, ci, v, orc.F32, xi, xv, orc.F32)
+        yb, sb = orc.spmspv_pull(m, n, rp, ci, bits, orc.BF16, xi, xb, orc.BF16)
+        for width, share in WIDTH_SHARE:
+            for H in (A, B):
+                dbs.dbs_set_option(H, dbs.DBS_OPT_PATH, 2)
+                dbs.dbs_set_option(H, dbs.DBS_OPT_PULL_WIDTH, width)
+                dbs.dbs_set_option(H, dbs.DBS_OPT_PULL_SHARE, share)
+            what = f"density {density} width {width} share {share}"
+            assert_close(run_plus(dbs, A, m, xi, xv), yr, s, "f32 " + what)
+            assert_close(run_plus(dbs, B, m, xi, xb, bf16=True), yb, sb, "bf16 " + what)
+
+
+def test_pull_variant_options_are_validated(dbs):
+    a = mixed_tile_dense(0)
+    rp, ci, v = csr_of(a)
+    A = build(dbs, a.shape[0], a.shape[1], rp, ci, v, dbs.DBS_F32)
+    for opt, bad in ((dbs.DBS_OPT_PULL_WIDTH, 2), (dbs.DBS_OPT_PULL_WIDTH, -1), (dbs.DBS_OPT_PULL_SHARE, 3),
+                     (dbs.DBS_OPT_PULL_SHARE, 8)):
+        with pytest.raises(dbs.DBSError):
+            dbs.dbs_set_option(A, opt, bad)
+    dbs.dbs_set_option(A, dbs.DBS_OPT_PULL_WIDTH, 4)
+    assert dbs.dbs_get_option(A, dbs.DBS_OPT_PULL_WIDTH) == 4
+
+
+@pytest.mark.parametrize("force", [0, 1, 2, 3, 4])
+def test_forced_format_spmspv_and_bfs(dbs, force):
+    """Every tile stored in one format, value (f32, bf16) and pattern builds:
+    PLUS_TIMES and OR-AND on every path, and BFS levels on every path."""
+    a = mixed_tile_dense(force, mb=6, nb=6, ragged=(9, 9))
+    a = np.where((a != 0) | (a.T != 0), np.where(a != 0, a, 0.25), 0).astype(np.float32)  # symmetric pattern
+    n = a.shape[0]
+    opt = options(dbs, force_format=force)
+    rp, ci, v = csr_of(a)
+    _, _, bits = bf16_csr_of(a)
+    A = build(dbs, n, n, rp, ci, v, dbs.DBS_F32, opt)
+    B = build(dbs, n, n, rp, ci, bits, dbs.DBS_BF16, opt)
+    P = build(dbs, n, n, rp, ci, None, dbs.DBS_PATTERN, opt)
+    for H in (A, B, P):
+        st = dbs.dbs_get_stats(H)
+        assert st["tiles_by_format"][force] == st["tiles"]
+    for k, density in enumerate((0.005, 0.1, 0.7)):
+        xi, xv = sparse_x(n, density, rng_for("test", 910, force, k))
+        xb = f32_to_bf16_bits(xv)
+        yr, s = orc.spmspv_pull(n, n, rp, ci, v, orc.F32, xi, xv, orc.F32)
+        yb, sb = orc.spmspv_pull(n, n, rp, ci, bits, orc.BF16, xi, xb, orc.BF16)
+        yo = orc.or_and_pull(n, n, rp, ci, xi)
+        for path in PATHS:
+            for H in (A, B, P):
+                dbs.dbs_set_option(H, dbs.DBS_OPT_PATH, path)
+            what = f"force {force} density {density} path {path}"
+            assert_close(run_plus(dbs, A, n, xi, xv), yr, s, "f32 " + what)
+            assert_close(run_plus(dbs, B, n, xi, xb, bf16=True), yb, sb, "bf16 " + what)
+            for H in (A, B, P):
+                np.testing.assert_array_equal(run_or(dbs, H, n, xi), yo, err_msg="or-and " + what)
+    for src in (0, 40, n - 1):
+        ref = orc.bfs(n, rp, ci, src)
+        for path in PATHS:
+            for H in (A, B, P):
+                dbs.dbs_set_option(H, dbs.DBS_OPT_PATH, path)
+                np.testing.assert_array_equal(run_bfs(dbs, H, n, src), ref, err_msg=f"bfs src {src} path {path}")
