@@ -50,7 +50,9 @@ typedef enum {
   DBS_ERR_OUT_OF_MEMORY = 3, /* a device allocation failed; nothing is leaked */
   DBS_ERR_DEVICE = 4,        /* a HIP runtime call failed */
   DBS_ERR_UNSUPPORTED = 5,   /* valid request this library does not implement */
-  DBS_ERR_BAD_VECTOR = 6     /* check mode found x_idx not strictly increasing */
+  DBS_ERR_BAD_VECTOR = 6,    /* check mode found x_idx not strictly increasing */
+  DBS_ERR_TOO_LARGE = 7      /* the problem needs more than the fixed scratch of an
+                                allocation-free call (DBS_NOALLOC_SCRATCH_BYTES) */
 } dbs_status;
 
 /* value type of the matrix (and of x for DBS_PLUS_TIMES) */
@@ -183,6 +185,34 @@ dbs_status dbs_spmspv_dense_threshold(dbs_handle A, const void *x, float thresho
  * the handle allocates on the first call (bitmaps, block lists, counters).
  */
 dbs_status dbs_bfs(dbs_handle A, int32_t src, int32_t *levels, void *stream);
+
+/*
+ * dbs_bfs_noalloc — dbs_bfs for callers that cannot allocate memory (code
+ * that must not call hipMalloc, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, same levels, same kernels; the run's device
+ * scratch comes from a fixed array of DBS_NOALLOC_SCRATCH_BYTES that each
+ * device holds for the life of the process (set up on the first call on a
+ * device), and the frontier sizes go to a host buffer on the call's stack.
+ * The call makes no allocation of its own (no hipMalloc, hipHostMalloc,
+ * hipFree).
+ *
+ *   Scratch needed: the 256-B-aligned sum of 4 (3 ceil(nb/2) + 1) (frontier
+ *   bitmaps), 4 (ceil(nb/2) + 1) (visited), 4 (3 nb + 1) (block lists) and
+ *   4 (25 + 8) (counters) bytes, about 20 nb bytes (nb = ceil(n/16)): up to
+ *   about 26 million vertices.  When a push level could need chunk lists cut
+ *   ahead (a forced push with nb > 6144, or th3 above 6144 / nb), 8 (3
+ *   (T/64 + nb + 1) + 1) bytes more.  A larger problem returns
+ *   DBS_ERR_TOO_LARGE before any work.
+ *
+ *   The array is shared by every call on the device and keeps the last
+ *   call's contents (each call clears what it needs at its start): calls that
+ *   overlap in time on one device race.  The current device must be the
+ *   handle's (else DBS_ERR_INVALID_ARG).  dbs_stats.bfs_reached is not
+ *   counted for this call (it stays -1): the visited bitmap it would be
+ *   counted from lives in the shared array.
+ */
+#define DBS_NOALLOC_SCRATCH_BYTES (32u << 20)
+dbs_status dbs_bfs_noalloc(dbs_handle A, int32_t src, int32_t *levels, void *stream);
 
 /* Per-handle run-time options (dbs_set_option / dbs_get_option). */
 enum {

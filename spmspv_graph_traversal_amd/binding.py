@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(_HERE, "libdbs.so")
 
 # status codes (dbs_status)
 DBS_OK, DBS_ERR_INVALID_ARG, DBS_ERR_BAD_CSR, DBS_ERR_OUT_OF_MEMORY = 0, 1, 2, 3
-DBS_ERR_DEVICE, DBS_ERR_UNSUPPORTED, DBS_ERR_BAD_VECTOR = 4, 5, 6
+DBS_ERR_DEVICE, DBS_ERR_UNSUPPORTED, DBS_ERR_BAD_VECTOR, DBS_ERR_TOO_LARGE = 4, 5, 6, 7
+DBS_NOALLOC_SCRATCH_BYTES = 32 << 20
 # dtypes, semirings, tile formats
 DBS_F32, DBS_BF16, DBS_PATTERN = 0, 1, 2
 DBS_PLUS_TIMES, DBS_OR_AND = 0, 1
@@ -61,7 +62,7 @@ class dbs_stats(C.Structure):
 
 
 EXPORTED = ["dbs_build_options_default", "dbs_build", "dbs_spmspv", "dbs_spmspv_dense",
-            "dbs_spmspv_dense_threshold", "dbs_bfs",
+            "dbs_spmspv_dense_threshold", "dbs_bfs", "dbs_bfs_noalloc",
             "dbs_set_option", "dbs_get_option", "dbs_get_stats", "dbs_copy_array", "dbs_free",
             "dbs_status_string"]
 
@@ -86,6 +87,7 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
         "dbs_spmspv_dense": [vp, vp, C.c_int, vp, vp],
         "dbs_spmspv_dense_threshold": [vp, vp, C.c_float, C.c_int, vp, vp],
         "dbs_bfs": [vp, i32, vp, vp],
+        "dbs_bfs_noalloc": [vp, i32, vp, vp],
         "dbs_set_option": [vp, i32, i64],
         "dbs_get_option": [vp, i32, C.POINTER(i64)],
         "dbs_get_stats": [vp, C.POINTER(dbs_stats)],
@@ -234,6 +236,16 @@ def dbs_bfs(A: Matrix, src: int, levels, stream=None) -> None:
 
     _need(levels, "levels", (torch.int32,), A.m)
     _check(_lib.dbs_bfs(A.handle, int(src), _ptr(levels), _stream(stream, levels.device)), "dbs_bfs")
+
+
+def dbs_bfs_noalloc(A: Matrix, src: int, levels, stream=None) -> None:
+    """dbs_bfs without allocation: the run's scratch is the library's fixed
+    per-device array (DBS_NOALLOC_SCRATCH_BYTES); DBS_ERR_TOO_LARGE above it."""
+    import torch
+
+    _need(levels, "levels", (torch.int32,), A.m)
+    _check(_lib.dbs_bfs_noalloc(A.handle, int(src), _ptr(levels), _stream(stream, levels.device)),
+           "dbs_bfs_noalloc")
 
 
 def dbs_set_option(A: Matrix, option: int, value: int) -> None:

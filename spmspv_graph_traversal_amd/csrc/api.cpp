@@ -261,6 +261,11 @@ dbs_status dbs_bfs(dbs_handle A, int32_t src, int32_t *levels, void *stream) {
   return dbs_bfs_impl(A, src, levels, (hipStream_t)stream);
 }
 
+dbs_status dbs_bfs_noalloc(dbs_handle A, int32_t src, int32_t *levels, void *stream) {
+  if (!A || !levels || A->m != A->n || src < 0 || src >= A->m) return DBS_ERR_INVALID_ARG;
+  return dbs_bfs_noalloc_impl(A, src, levels, (hipStream_t)stream);
+}
+
 dbs_status dbs_set_option(dbs_handle A, int32_t option, int64_t value) {
   if (!A) return DBS_ERR_INVALID_ARG;
   switch (option) {
@@ -395,6 +400,7 @@ const char *dbs_status_string(dbs_status s) {
     case DBS_ERR_DEVICE: return "HIP runtime error";
     case DBS_ERR_UNSUPPORTED: return "unsupported";
     case DBS_ERR_BAD_VECTOR: return "x_idx not strictly increasing";
+    case DBS_ERR_TOO_LARGE: return "problem larger than the fixed scratch of an allocation-free call";
   }
   return "unknown status";
 }

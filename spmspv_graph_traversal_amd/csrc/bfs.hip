@@ -26,6 +26,8 @@
 // counts per batch finds the first empty frontier, where the traversal ends.
 // Levels of a batch past that point see an empty frontier and return at
 // once (no vertex is found, nothing is written but cleared counters).
+#include <mutex>
+
 #include "meta.h"
 #include "pattern_pull.h"
 #include "tile_kernels.h"
@@ -352,6 +354,29 @@ __global__ __launch_bounds__(256) void k_bfs_reached(const uint32_t *vis, const 
                                                                        : DBS_ERR_DEVICE;        \
   } while (0)
 
+namespace {
+
+// Device scratch of one BFS run: three rotating frontier bitmaps, the
+// visited bitmap, three block lists, three chunk lists (only when a push may
+// need chunks cut ahead), 3 x 8 counters then the frontier sizes of one batch
+// of levels and a spare counter, and a host buffer that receives the sizes.
+struct BfsScratch {
+  uint32_t *bm, *vis, *list;
+  uint64_t *chunks;
+  uint32_t *ctr;
+  uint32_t *host;  // 64 B of host memory (pinned for dbs_bfs)
+};
+
+// whether push chunks come from the frontier's block list (then no chunk
+// list is needed)
+bool bfs_list_push(const dbs_matrix *A) {
+  return dbs_meta::push_from_list(A->nb, A->opt[DBS_OPT_PATH], A->opt[DBS_OPT_TH3_NUM], A->opt[DBS_OPT_TH3_DEN]);
+}
+
+dbs_status bfs_run(dbs_matrix *A, const BfsScratch &S, int32_t src, int32_t *levels, hipStream_t s);
+
+}  // namespace
+
 dbs_status dbs_bfs_impl(dbs_matrix *A, int32_t src, int32_t *levels, hipStream_t s) {
   const int64_t nwords = ((int64_t)A->nb + 1) / 2;
   const int64_t chunk_cap = A->max_chunks;
@@ -363,23 +388,33 @@ dbs_status dbs_bfs_impl(dbs_matrix *A, int32_t src, int32_t *levels, hipStream_t
     BFS_TRY(dbs_dev_alloc(A, (void **)&A->bfs_ctr, (24 + dbs_matrix::kBfsBatch + 1) * 4));
     BFS_TRY(hipHostMalloc((void **)&A->bfs_host, 64, hipHostMallocDefault));
   }
+  const BfsScratch S{A->bfs_bm, A->bfs_vis, A->bfs_list, A->bfs_chunks, A->bfs_ctr, A->bfs_host};
+  const dbs_status st = bfs_run(A, S, src, levels, s);
+  A->bfs_counted = st == DBS_OK ? 1 : 0;  // its visited bitmap stays in the handle
+  return st;
+}
+
+namespace {
+
+dbs_status bfs_run(dbs_matrix *A, const BfsScratch &S, int32_t src, int32_t *levels, hipStream_t s) {
+  const int64_t nwords = ((int64_t)A->nb + 1) / 2;
+  const int64_t chunk_cap = A->max_chunks;
   const bool timing = A->opt[DBS_OPT_TIMING] != 0;
   if (timing) BFS_TRY(hipEventRecord(A->ev[0], s));
   const int64_t fp = A->opt[DBS_OPT_PATH];
-  const bool list_push =
-      dbs_meta::push_from_list(A->nb, fp, A->opt[DBS_OPT_TH3_NUM], A->opt[DBS_OPT_TH3_DEN]);
+  const bool list_push = bfs_list_push(A);
   const int push0 =
       !list_push && (fp == 1 || (fp == 0 && A->opt[DBS_OPT_TH3_DEN] < (int64_t)A->nb * A->opt[DBS_OPT_TH3_NUM]));
-  hipLaunchKernelGGL(k_bfs_init, dim3(1024), dim3(256), 0, s, levels, A->m, A->bfs_bm, 3 * nwords, A->bfs_vis,
-                     (const uint32_t *)A->rows_nz, nwords, A->bfs_ctr, src, (const uint32_t *)A->cb_ptr, A->bfs_list,
-                     A->bfs_chunks, chunk_cap, push0);
+  hipLaunchKernelGGL(k_bfs_init, dim3(1024), dim3(256), 0, s, levels, A->m, S.bm, 3 * nwords, S.vis,
+                     (const uint32_t *)A->rows_nz, nwords, S.ctr, src, (const uint32_t *)A->cb_ptr, S.list,
+                     S.chunks, chunk_cap, push0);
   BFS_TRY(hipGetLastError());
   const unsigned mgrid = dbs_meta::groups_for(A->nb, nwords);
   auto reg_for = [&](int buf) {
     dbs_meta::Reg r;
-    r.ctr = A->bfs_ctr + 8 * buf;
-    r.list = A->bfs_list + (int64_t)buf * A->nb;
-    r.chunks = A->bfs_chunks + buf * chunk_cap;
+    r.ctr = S.ctr + 8 * buf;
+    r.list = S.list + (int64_t)buf * A->nb;
+    r.chunks = S.chunks ? S.chunks + buf * chunk_cap : nullptr;  // none: chunks come from the list
     r.list_cap = A->nb;
     r.chunk_cap = chunk_cap;
     r.cb_ptr = A->cb_ptr;
@@ -411,7 +446,7 @@ dbs_status dbs_bfs_impl(dbs_matrix *A, int32_t src, int32_t *levels, hipStream_t
   P.payload_bytes = A->payload_bytes;
   P.m = A->m;
   P.nb = A->nb;
-  P.vis = A->bfs_vis;
+  P.vis = S.vis;
   P.levels = levels;
   P.force_path = (int32_t)A->opt[DBS_OPT_PATH];
   P.th3_num = A->opt[DBS_OPT_TH3_NUM];
@@ -429,7 +464,7 @@ dbs_status dbs_bfs_impl(dbs_matrix *A, int32_t src, int32_t *levels, hipStream_t
 
   constexpr int B = dbs_matrix::kBfsBatch;
   static_assert(B * 4 <= 64, "pinned mirror holds 16 counts");
-  P.hist = A->bfs_ctr + 24;
+  P.hist = S.ctr + 24;
   int32_t L = -1, push_levels = 0;
   float kms = 0.0f;
   for (int64_t L0 = 0; L < 0; L0 += B) {
@@ -437,11 +472,11 @@ dbs_status dbs_bfs_impl(dbs_matrix *A, int32_t src, int32_t *levels, hipStream_t
     for (int i = 0; i < B; ++i) {
       const int64_t l = L0 + i;
       const int cur = (int)(l % 3), nxt = (int)((l + 1) % 3), clr = (int)((l + 2) % 3);
-      P.cur_bm = A->bfs_bm + cur * nwords;
-      P.next_bm = A->bfs_bm + nxt * nwords;
-      P.cur_ctr = A->bfs_ctr + 8 * cur;
-      P.cur_chunks = A->bfs_chunks + cur * chunk_cap;
-      P.cur_list = A->bfs_list + (int64_t)cur * A->nb;
+      P.cur_bm = S.bm + cur * nwords;
+      P.next_bm = S.bm + nxt * nwords;
+      P.cur_ctr = S.ctr + 8 * cur;
+      P.cur_chunks = S.chunks ? S.chunks + cur * chunk_cap : nullptr;
+      P.cur_list = S.list + (int64_t)cur * A->nb;
       P.level = (int32_t)l;
       if (timing) BFS_TRY(hipEventRecord(A->ev[2 + 2 * i], s));
       if (A->vk == VK_F32) {
@@ -462,14 +497,14 @@ dbs_status dbs_bfs_impl(dbs_matrix *A, int32_t src, int32_t *levels, hipStream_t
       BFS_TRY(hipGetLastError());
       if (timing) BFS_TRY(hipEventRecord(A->ev[3 + 2 * i], s));
       hipLaunchKernelGGL(k_bfs_meta, dim3(mgrid), dim3(dbs_meta::MT), 0, s, (const uint32_t *)P.next_bm, A->nb,
-                         reg_for(nxt), A->bfs_bm + clr * nwords, A->bfs_ctr + 8 * clr, nwords,
+                         reg_for(nxt), S.bm + clr * nwords, S.ctr + 8 * clr, nwords,
                          (const uint32_t *)P.cur_ctr);
       BFS_TRY(hipGetLastError());
     }
-    BFS_TRY(hipMemcpyAsync(A->bfs_host, P.hist, B * 4, hipMemcpyDeviceToHost, s));
+    BFS_TRY(hipMemcpyAsync(S.host, P.hist, B * 4, hipMemcpyDeviceToHost, s));
     BFS_TRY(hipStreamSynchronize(s));
     for (int i = 0; i < B; ++i) {
-      const uint32_t nz = A->bfs_host[i];  // nonzero blocks of frontier L0 + i
+      const uint32_t nz = S.host[i];  // nonzero blocks of frontier L0 + i
       if (nz == 0u) {
         L = (int32_t)(L0 + i);
         break;
@@ -503,8 +538,10 @@ dbs_status dbs_bfs_impl(dbs_matrix *A, int32_t src, int32_t *levels, hipStream_t
   return DBS_OK;
 }
 
+}  // namespace
+
 dbs_status dbs_bfs_count_reached(dbs_matrix *A) {
-  if (!A->bfs_vis || A->st.bfs_levels <= 0 || A->st.bfs_reached >= 0) return DBS_OK;
+  if (!A->bfs_counted || !A->bfs_vis || A->st.bfs_levels <= 0 || A->st.bfs_reached >= 0) return DBS_OK;
   const int64_t nwords = ((int64_t)A->nb + 1) / 2;
   hipStream_t s = A->last_stream;
   // the counter: the slot after the batch's frontier sizes
@@ -521,4 +558,73 @@ dbs_status dbs_bfs_count_reached(dbs_matrix *A) {
   const bool src_has_entry = (src_word >> ((uint32_t)A->bfs_src & 31u)) & 1u;
   A->st.bfs_reached = (int64_t)h + (src_has_entry ? 0 : 1);
   return DBS_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free BFS (dbs_bfs_noalloc): the same steps as dbs_bfs, with the
+// scratch of the run carved from a fixed device array instead of memory the
+// handle allocates.  Each device holds its own copy of the array until the
+// process ends; its address is looked up once per device, with that device
+// current, and kept.  Kernels receive that address, never the array's name
+// (which in host code does not name device memory).  Every call on a device
+// shares the array: calls that overlap in time on one device race.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[DBS_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// address of this device's array (looked up on the first call on the device)
+hipError_t noalloc_scratch(int dev, uint8_t **out) {
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = (uint8_t *)g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+// Carve the run's scratch out of `base` (256-B aligned pieces); returns the
+// bytes needed, so that a null base only measures.
+size_t carve(const dbs_matrix *A, bool list_push, uint8_t *base, BfsScratch &S) {
+  const int64_t nwords = ((int64_t)A->nb + 1) / 2;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    uint8_t *p = base ? base + off : nullptr;
+    off += (bytes + 255) & ~(size_t)255;
+    return p;
+  };
+  S.bm = (uint32_t *)take((size_t)(3 * nwords + 1) * 4);
+  S.vis = (uint32_t *)take((size_t)(nwords + 1) * 4);
+  S.list = (uint32_t *)take((size_t)(3 * (int64_t)A->nb + 1) * 4);
+  S.ctr = (uint32_t *)take((size_t)(24 + dbs_matrix::kBfsBatch + 1) * 4);
+  S.chunks = list_push ? nullptr : (uint64_t *)take((size_t)(3 * A->max_chunks + 1) * 8);
+  return off;
+}
+
+}  // namespace
+
+dbs_status dbs_bfs_noalloc_impl(dbs_matrix *A, int32_t src, int32_t *levels, hipStream_t s) {
+  int dev = -1;
+  BFS_TRY(hipGetDevice(&dev));
+  if (dev != A->device) return DBS_ERR_INVALID_ARG;
+  const bool list_push = bfs_list_push(A);
+  BfsScratch S{};
+  if (carve(A, list_push, nullptr, S) > (size_t)DBS_NOALLOC_SCRATCH_BYTES) return DBS_ERR_TOO_LARGE;
+  uint8_t *base = nullptr;
+  BFS_TRY(noalloc_scratch(dev, &base));
+  carve(A, list_push, base, S);
+  uint32_t host[16];  // the batch's frontier sizes (the run synchronizes before reading them)
+  S.host = host;
+  const dbs_status st = bfs_run(A, S, src, levels, s);
+  A->bfs_counted = 0;  // the visited bitmap lives in the shared array: not counted later
+  return st;
 }

@@ -155,6 +155,7 @@ struct dbs_matrix {
   uint32_t *bfs_ctr;     // 3 x 8 counters, then the frontier sizes of one batch of levels
   uint32_t *bfs_host;    // pinned host mirror of those frontier sizes
   int32_t bfs_src;       // source of the last BFS
+  int32_t bfs_counted;   // the last BFS left its visited bitmap in bfs_vis (bfs_reached can be counted)
 
   // options and statistics
   int64_t opt[8];
@@ -194,6 +195,8 @@ dbs_status dbs_spmspv_impl(dbs_matrix *A, int32_t nnz_x, const int32_t *x_idx,
                            const void *x_val, const void *x_dense, dbs_semiring sr, void *y,
                            hipStream_t s, float thr = -1.0f);
 dbs_status dbs_bfs_impl(dbs_matrix *A, int32_t src, int32_t *levels, hipStream_t s);
+// the same on the fixed device array, allocating nothing
+dbs_status dbs_bfs_noalloc_impl(dbs_matrix *A, int32_t src, int32_t *levels, hipStream_t s);
 // fills st.bfs_reached for the last BFS (counts its visited bitmap; synchronous)
 dbs_status dbs_bfs_count_reached(dbs_matrix *A);
 // next free event triple of the timing ring (folds the oldest into the sums
