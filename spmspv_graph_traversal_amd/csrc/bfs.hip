@@ -152,7 +152,7 @@ DBS_DEV void bfs_pull_group(const BfsParams &P, const BfsRes &R, int64_t s0, boo
   // skipped without reading its tiles
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const uint32_t rb = seg[u].x & ~SEG_SPLIT;
+    const uint32_t rb = seg[u].x & SEG_RB_MASK;
     need[u] = s0 + u < P.nseg ? (~bm_get(P.vis, rb) & rows_valid(P.m, rb)) : 0u;
   }
   uint32_t cb[U], m[U], pw0[U], pw1[U];
@@ -195,7 +195,7 @@ DBS_DEV void bfs_pull_group(const BfsParams &P, const BfsRes &R, int64_t s0, boo
       const uint32_t tmask = (uint32_t)__shfl((int)m[u], src);
       f |= tile_or<VK>(P.payload + meta_vp(tm), dmask<VK>(P, meta_vp(tm)), meta_type(tm), tmask, lane);
     }
-    if (f & need[u]) claim_wave(P, seg[u].x & ~SEG_SPLIT, f & need[u], lane);  // uniform
+    if (f & need[u]) claim_wave(P, seg[u].x & SEG_RB_MASK, f & need[u], lane);  // uniform
   }
 }
 

@@ -467,6 +467,68 @@ __global__ __launch_bounds__(BT) void k_segments_long(int32_t mb, const uint32_t
   }
 }
 
+// Partial slots (value matrices): per row block, the slots its segments
+// need (its segment count when above SEG_SLOT_MIN, else 0) and whether it
+// is listed for the finalize.
+__global__ void k_slot_counts(int32_t mb, const uint32_t *seg_cnt, uint32_t *nslot, uint32_t *isfin) {
+  const int32_t rb = (int32_t)(blockIdx.x * blockDim.x + threadIdx.x);
+  if (rb >= mb) return;
+  const uint32_t c = seg_cnt[rb];
+  nslot[rb] = c > SEG_SLOT_MIN ? c : 0u;
+  isfin[rb] = c > SEG_SLOT_MIN ? 1u : 0u;
+}
+
+// Class bits and slot of every segment of such a row block (segment j of
+// row block rb takes slot slot_off[rb] + j), and the finalize list entry
+// {row block, first slot, segments, class} of each; the largest class goes
+// to *maxcls (one atomic per wave).
+__global__ void k_slots(int64_t nseg, uint32_t *segs, const uint32_t *seg_cnt, const uint32_t *seg_off,
+                        const uint32_t *slot_off, const uint32_t *fin_off, uint32_t *fin, uint32_t *maxcls) {
+  const int64_t sg = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  uint32_t cls = 0;
+  if (sg < nseg) {
+    const uint32_t rb = segs[4 * sg] & SEG_RB_MASK;
+    const uint32_t c = seg_cnt[rb];
+    cls = seg_class(c);
+    if (cls) {
+      const uint32_t j = (uint32_t)sg - seg_off[rb];
+      segs[4 * sg] |= cls << SEG_CLS_SHIFT;
+      segs[4 * sg + 3] = slot_off[rb] + j + 1u;
+      if (j == 0) {
+        uint32_t *f = fin + 4 * (uint64_t)fin_off[rb];
+        f[0] = rb;
+        f[1] = slot_off[rb];
+        f[2] = c;
+        f[3] = cls;
+      }
+    }
+  }
+  cls = group_max_u32<64>(cls);
+  if ((threadIdx.x & 63) == 0 && cls) atomicMax(maxcls, cls);
+}
+
+// Marks (SEG_DRAIN) the pull segments of a value matrix in which some row
+// holds more than SEG_DRAIN_ROW entries of COO tiles: the wide PLUS_TIMES
+// pull then empties its LDS row sums after every round of those segments.
+// One thread per segment, counting its COO tiles' coordinate bytes per row.
+__global__ void k_seg_drain(int64_t nseg, uint32_t *segs, const uint64_t *t_meta, const uint8_t *payload) {
+  const int64_t sg = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (sg >= nseg) return;
+  const uint32_t t0 = segs[4 * sg + 1], t1 = segs[4 * sg + 2];
+  uint32_t cnt[16];
+  for (int r = 0; r < 16; ++r) cnt[r] = 0;
+  for (uint32_t t = t0; t < t1; ++t) {
+    const uint64_t mt = t_meta[t];
+    if (meta_type(mt) != DBS_TILE_COO) continue;
+    const uint8_t *c = payload + meta_vp(mt);
+    const uint32_t nz = meta_nnz(mt);
+    for (uint32_t e = 0; e < nz; ++e) cnt[c[e] >> 4] += 1;
+  }
+  uint32_t mx = 0;
+  for (int r = 0; r < 16; ++r) mx = cnt[r] > mx ? cnt[r] : mx;
+  if (mx > SEG_DRAIN_ROW) segs[4 * sg] |= SEG_DRAIN;
+}
+
 __global__ void k_type_stats(const uint32_t *t_nt, int64_t T, unsigned long long *st) {
   __shared__ unsigned long long s[10];
   if (threadIdx.x < 10) s[threadIdx.x] = 0;
@@ -798,6 +860,68 @@ dbs_status dbs_build_impl(dbs_matrix *A, const int32_t *row_ptr, const int32_t *
   hipLaunchKernelGGL(k_segments_long, dim3(lgrid), dim3(BT), 0, s, mb, (const uint32_t *)A->rb_ptr,
                      (const uint32_t *)t_nt, A->bopt, seg_cnt, (const uint32_t *)seg_off, A->segs, 1);
   BUILD_TRY(hipGetLastError());
+  if (vk != VK_PAT && hS > 0) {
+    hipLaunchKernelGGL(k_seg_drain, dim3(nblocks(hS, BT)), dim3(BT), 0, s, (int64_t)hS, A->segs,
+                       (const uint64_t *)A->t_meta, (const uint8_t *)A->payload);
+    BUILD_TRY(hipGetLastError());
+    // partial slots of the row blocks with more than SEG_SLOT_MIN segments
+    uint32_t *nslot, *slot_off, *isfin, *fin_off, *maxcls;
+    BUILD_TRY(tmp.get((void **)&nslot, (size_t)mb * 4));
+    BUILD_TRY(tmp.get((void **)&slot_off, (size_t)(mb + 1) * 4));
+    BUILD_TRY(tmp.get((void **)&isfin, (size_t)mb * 4));
+    BUILD_TRY(tmp.get((void **)&fin_off, (size_t)(mb + 1) * 4 + 4));
+    maxcls = fin_off + mb + 1;
+    BUILD_TRY(hipMemsetAsync(maxcls, 0, 4, s));
+    hipLaunchKernelGGL(k_slot_counts, dim3(nblocks(mb, BT)), dim3(BT), 0, s, mb, (const uint32_t *)seg_cnt, nslot,
+                       isfin);
+    BUILD_TRY(hipGetLastError());
+    BUILD_TRY(dbs_scan_u32(nslot, slot_off, mb, stmp, s));
+    BUILD_TRY(dbs_scan_u32(isfin, fin_off, mb, stmp, s));
+    uint32_t hn[2] = {0, 0};
+    BUILD_TRY(hipMemcpyAsync(&hn[0], slot_off + mb, 4, hipMemcpyDeviceToHost, s));
+    BUILD_TRY(hipMemcpyAsync(&hn[1], fin_off + mb, 4, hipMemcpyDeviceToHost, s));
+    BUILD_TRY(hipStreamSynchronize(s));
+    A->nslots = hn[0];
+    A->nfin = hn[1];
+    // the pull addresses the slots with 32-bit byte offsets
+    if ((uint64_t)A->nslots * DBS_MAX_SHARE * SLOT_WORDS * 4 >= 0xFFFFFFF0ull) return DBS_ERR_UNSUPPORTED;
+    if (A->nfin > 0) {
+      BUILD_TRY(dbs_dev_alloc(A, (void **)&A->fin, (size_t)A->nfin * 16));
+      const size_t pbytes = (size_t)A->nslots * DBS_MAX_SHARE * SLOT_WORDS * 4;
+      BUILD_TRY(dbs_dev_alloc(A, (void **)&A->partial, pbytes));
+      BUILD_TRY(hipMemsetAsync(A->partial, 0, pbytes, s));  // no slot holds a valid epoch
+      hipLaunchKernelGGL(k_slots, dim3(nblocks(hS, BT)), dim3(BT), 0, s, (int64_t)hS, A->segs,
+                         (const uint32_t *)seg_cnt, (const uint32_t *)seg_off, (const uint32_t *)slot_off,
+                         (const uint32_t *)fin_off, A->fin, maxcls);
+      BUILD_TRY(hipGetLastError());
+      uint32_t hm = 0;
+      BUILD_TRY(hipMemcpyAsync(&hm, maxcls, 4, hipMemcpyDeviceToHost, s));
+      // the finalize takes the list in order: longest row blocks first, so
+      // that they do not start last
+      std::vector<uint32_t> fl(4 * (size_t)A->nfin), fo(4 * (size_t)A->nfin);
+      BUILD_TRY(hipMemcpyAsync(fl.data(), A->fin, (size_t)A->nfin * 16, hipMemcpyDeviceToHost, s));
+      BUILD_TRY(hipStreamSynchronize(s));
+      std::vector<uint32_t> ix((size_t)A->nfin);
+      for (size_t i = 0; i < ix.size(); ++i) ix[i] = (uint32_t)i;
+      std::stable_sort(ix.begin(), ix.end(), [&](uint32_t a, uint32_t b) { return fl[4 * (size_t)a + 2] > fl[4 * (size_t)b + 2]; });
+      for (size_t i = 0; i < ix.size(); ++i)
+        for (int j = 0; j < 4; ++j) fo[4 * i + j] = fl[4 * (size_t)ix[i] + j];
+      BUILD_TRY(hipMemcpyAsync(A->fin, fo.data(), (size_t)A->nfin * 16, hipMemcpyHostToDevice, s));
+      BUILD_TRY(hipStreamSynchronize(s));
+      // sorted by segment count, the entries of class >= c come first
+      for (int c = 0; c < 4; ++c) {
+        int64_t k = 0;
+        while (k < A->nfin && fo[4 * (size_t)k + 3] >= (uint32_t)c) ++k;
+        A->fin_cls[c] = k;
+      }
+      for (int p = 0; p < 3; ++p) {
+        int64_t k = 0;
+        while (k < A->nfin && (uint64_t)fo[4 * (size_t)k + 2] * (1u << p) > 256u) ++k;
+        A->fin_big[p] = k;
+      }
+      (void)hm;
+    }
+  }
   if (vk == VK_PAT) {
     BUILD_TRY(build_pull_order(A, seg_cnt, s));
     const size_t ow = (size_t)(A->payload_bytes + DBS_PAYLOAD_SLACK) / 4;

@@ -95,8 +95,37 @@ __host__ __device__ inline uint32_t tile_payload_bytes(int type, uint32_t nnz, i
   return align_up(PL_FORCE_VAL + nnz * vs, 16);  // ForceCSR / ForceCSC
 }
 
-// Pull segment descriptor: {row block | split << 31, first tile, end tile, 0}.
+// Pull segment descriptor: {row block | class << 28 | split << 31, first
+// tile, end tile, partial slot + 1 (0: none)}.  Split: the row block has
+// several segments.  Value matrices only: the row blocks of more than
+// SEG_SLOT_MIN segments carry a size class (1: at most 32 segments, 2: at
+// most 64, 3: more) and give each segment a partial slot, so that a call can
+// write those segments' row sums to slots and add them with a fixed-order
+// pairwise finalize instead of same-address atomics.  The class decides per
+// call, from the number of waves that share a segment, which row blocks do:
+// every other row block receives at most SEG_MAX_ADDS atomic adds per
+// y entry (its segments x sharing waves).
 #define SEG_SPLIT 0x80000000u
+// the segment has a row with more than SEG_DRAIN_ROW entries in its COO tiles
+#define SEG_DRAIN 0x40000000u
+#define SEG_DRAIN_ROW 32
+#define SEG_RB_MASK 0x0FFFFFFFu
+#define SEG_CLS_SHIFT 28
+#define SEG_SLOT_MIN 16
+#define SEG_MAX_ADDS 64
+// waves that share one PLUS_TIMES pull segment at most
+#define DBS_MAX_SHARE 4
+// a partial slot: the 16 row sums, then the epoch of the call that wrote
+// them (a slot of another call counts as zero, so a segment with nothing to
+// add writes nothing)
+#define SLOT_WORDS 17
+__host__ __device__ inline uint32_t seg_class(uint32_t nsegs) {
+  return nsegs <= SEG_SLOT_MIN ? 0u : nsegs <= 32 ? 1u : nsegs <= 64 ? 2u : 3u;
+}
+// the smallest class whose row blocks take partial slots when `share` waves
+// share a segment (1, 2 or 4): those of class below it have at most
+// SEG_MAX_ADDS / share segments
+__host__ __device__ inline uint32_t seg_slot_class(int share) { return share >= 4 ? 1u : share == 2 ? 2u : 3u; }
 // zeroed bytes allocated after the payload: wide row loads that start inside
 // the last tile stay inside the allocation
 #define DBS_PAYLOAD_SLACK 256u
@@ -136,6 +165,12 @@ struct dbs_matrix {
                         // tile, end tile, row blocks), first-launch ones ahead
   int64_t payload_bytes;
   uint32_t *rows_nz;    // [(mb+1)/2] rows holding an entry, 16 bits per row block
+  // value matrices: row blocks of more than SEG_SLOT_MIN pull segments
+  uint32_t *fin;        // [4*nfin] {row block, first slot, segments, class}
+  int64_t nfin, nslots;
+  int64_t fin_cls[4];   // entries of the list (sorted by segment count) of class >= c
+  int64_t fin_big[3];   // leading entries of more than 256 slots with 1, 2 and 4 sharing waves
+  float *partial;       // [nslots * DBS_MAX_SHARE * SLOT_WORDS] segment row sums of such row blocks
 
   // per-call scratch (device)
   uint32_t *xmask;       // [nb] (epoch << 16) | blk_x_mask

@@ -43,10 +43,10 @@ DBS_DEV void pat_issue(const PatSrc &S, const Pol &pol, int64_t s0, bool live, u
                        PatRound<U> &r) {
   const cu32_t *q = (const cu32_t *)S.segs + 4 * s0;
 #pragma unroll
-  for (int u = 0; u < U; ++u) r.seg[u] = make_uint4(q[4 * u], q[4 * u + 1], q[4 * u + 2], 0u);
+  for (int u = 0; u < U; ++u) r.seg[u] = make_uint4(q[4 * u], q[4 * u + 1], q[4 * u + 2], q[4 * u + 3]);
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    r.need[u] = pol.need(r.seg[u].x & ~SEG_SPLIT);
+    r.need[u] = pol.need(r.seg[u].x & SEG_RB_MASK);
     r.n[u] = (live & (s0 + u < S.nseg) & (r.need[u] != 0u)) ? r.seg[u].z - r.seg[u].y : 0u;
     const brsrc_t rcb = make_rsrc(S.t_cb + r.seg[u].y, (uint64_t)r.n[u] * 4u);
     r.cb[u] = __builtin_amdgcn_raw_buffer_load_b32(rcb, l4, 0, 0);

@@ -142,6 +142,9 @@ struct SpmvParams {
   int32_t local_cutoff;
   int32_t plus_u;  // segments per wave step of the PLUS_TIMES pull (1 or PULL_U_PLUS_WIDE)
   int32_t plus_parts;  // U = 1: waves sharing one segment (1, 2 or 4), each taking a lane range
+  int32_t slot_cls;    // segments of row blocks of at least this class write partial slots
+  float *partial;      // the partial slots (finalized by k_plus_finalize), < 4 GiB
+  uint32_t partial_bytes;
   const uint32_t *xlist;  // this call's nonzero vector blocks (N_nzblk of them)
   int32_t list_push;      // push chunks come from xlist (none were built)
   void *y;
@@ -238,93 +241,46 @@ DBS_DEV void push_chunk(const SpmvParams &P, uint64_t own, float *sx, float *spa
 // once: a plain store when the row block is one segment, an atomic add when
 // several segments share it.
 constexpr int PULL_U_PLUS_WIDE = 4;  // segments per wave step, PLUS_TIMES pull with many segments
-constexpr int PLUS_MAX_PARTS = 4;    // waves sharing one PLUS_TIMES pull segment at most
+constexpr int PLUS_MAX_PARTS = DBS_MAX_SHARE;  // waves sharing one PLUS_TIMES pull segment at most
 constexpr int PULL_U_OR = 8;    // segments per wave step, OR_AND pull (value matrices)
 
 // ---------------------------------------------------------------------------
-// PLUS_TIMES over the COO tiles of one pull segment, entries spread over the
-// lanes: the COO tiles' payloads (coordinates, then values) follow one
-// another in tile order, so entry j of the segment is entry j - start_t of
-// the tile t whose first entry start_t (a wave prefix sum of the tiles' entry
-// counts) is the last one at or below j, found by a wave max-scan of the
-// tiles' marks.  Lane j reads its entry's coordinate, value and x value and
-// adds the product to its row in LDS (s_y, 16 floats of this wave).  Each
-// vector memory instruction thus covers 64 entries, whatever the tiles'
-// sizes, instead of one tile per lane looping over the largest tile's
-// entries.  The row totals are left in s_y.
+// PLUS_TIMES over the COO tiles of the U pull segments of a wave step,
+// entries spread over the lanes: the COO tiles' payloads (coordinates, then
+// values) follow one another in tile order, so entry j of a segment is entry
+// j - start_t of the tile t whose first entry start_t (a wave prefix sum of
+// the tiles' entry counts) is the last one at or below j, found by a wave
+// max-scan of the tiles' marks.  Each vector memory instruction thus covers
+// 64 entries, whatever the tiles' sizes.  Round i takes chunk i (entries
+// 64i .. 64i+63 of the segment's run) of every segment that has one, and
+// issues all their coordinate and value loads, then all their x loads,
+// before any is used, so a step waits about twice per round for memory
+// whatever U.
+//
+// The row sums (hierarchical writeback, section 3.3.3):
+//   U == 1: lane l adds its product to its own slot s_acc[row * 64 + l] (16
+//           rows x 64 lanes per wave; the LDS bank is the lane, so the adds
+//           never conflict and no two lanes share an address); at the end
+//           lane (q, r) adds the 16 slots of row r of quarter q's lanes (in
+//           a bank-conflict-free order) and the quarters are merged; the
+//           slots are cleared on the way;
+//   U > 1:  the products go to 16 LDS row sums per segment (lanes of one
+//           row add to one address; the hardware adds them one after the
+//           other).  A row's chain of adds is then its number of COO entries
+//           in the segment: the builder marks (SEG_DRAIN) the segments where
+//           a row has more than SEG_DRAIN_ROW of them, and in those the
+//           round's row sums are moved to a register after every round (at
+//           most 64 adds per round).  Per lane-private slots or a drain of
+//           every segment cost the COO-heavy pulls 10-40% more time.
+// Every lane returns the total of row (lane & 15) of segment u in
+// coo_sum[u]; a product passes through at most rounds + 17 additions
+// (U = 1), SEG_DRAIN_ROW (U > 1, unmarked) or 64 + rounds (marked).
 // ---------------------------------------------------------------------------
-template <int VK>
-DBS_DEV void coo_entries_plus(const brsrc_t pay, const brsrc_t xr, bool coo, uint64_t meta, uint32_t m, uint32_t cb,
-                              uint32_t *s_mark, float *s_y, int lane) {
-  constexpr uint32_t VS = VK == VK_F32 ? 4u : 2u;
-  constexpr int B = 4;  // chunks of 64 entries whose loads are issued together
-  const uint32_t cnt = coo ? meta_nnz(meta) : 0u;
-  const uint32_t start = wave_incl_add(cnt) - cnt;
-  const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)(start + cnt), 63);
-  const uint32_t vp = (uint32_t)meta_vp(meta);
-  uint32_t carry = 0u;
-  for (uint32_t j00 = 0; j00 < total; j00 += 64u * B) {
-    // owner tile of each entry of the B chunks (lanes talk through LDS, each
-    // step fenced at wave scope)
-    int own[B];
-#pragma unroll
-    for (int b = 0; b < B; ++b) {
-      const uint32_t j0 = j00 + 64u * b;
-      own[b] = 0;
-      if (j0 >= total) continue;  // uniform
-      __syncwarp();
-      s_mark[lane] = 0u;
-      __syncwarp();
-      if ((cnt != 0u) & (start >= j0) & (start < j0 + 64u)) s_mark[start - j0] = (uint32_t)lane + 1u;
-      __syncwarp();
-      uint32_t o = wave_incl_max(s_mark[lane]);
-      o = o > carry ? o : carry;
-      carry = (uint32_t)__builtin_amdgcn_readlane((int)o, 63);
-      own[b] = (int)o - 1;
-    }
-    // coordinates and values, then x values, of all B chunks
-    uint32_t rc[B], ocb[B], om[B];
-    float a[B], x[B];
-    bool live[B];
-#pragma unroll
-    for (int b = 0; b < B; ++b) {
-      const uint32_t j = j00 + 64u * b + (uint32_t)lane;
-      live[b] = j < total;
-      const uint32_t ovp = (uint32_t)__shfl((int)vp, own[b]), ost = (uint32_t)__shfl((int)start, own[b]);
-      const uint32_t ocnt = (uint32_t)__shfl((int)cnt, own[b]);
-      ocb[b] = (uint32_t)__shfl((int)cb, own[b]);
-      om[b] = (uint32_t)__shfl((int)m, own[b]);
-      const uint32_t e = j - ost;
-      rc[b] = __builtin_amdgcn_raw_buffer_load_b8(pay, live[b] ? ovp + e : OOB_OFF, 0, 0);
-      const uint32_t aoff = live[b] ? ovp + coo_val_off(ocnt) + e * VS : OOB_OFF;
-      if (VK == VK_F32) a[b] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(pay, aoff, 0, 0));
-      else a[b] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(pay, aoff, 0, 0) << 16);
-    }
-#pragma unroll
-    for (int b = 0; b < B; ++b) {
-      const uint32_t c = rc[b] & 15u;
-      live[b] = live[b] & ((om[b] >> c) & 1u);
-      const uint32_t xoff = live[b] ? (ocb[b] * 16u + c) * VS : OOB_OFF;
-      if (VK == VK_F32) x[b] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(xr, xoff, 0, 0));
-      else x[b] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(xr, xoff, 0, 0) << 16);
-    }
-#pragma unroll
-    for (int b = 0; b < B; ++b)
-      if (live[b]) atomicAdd(&s_y[rc[b] >> 4], a[b] * x[b]);
-  }
-  __syncwarp();
-}
-
-// The COO entries of the U segments of a wave step together: round i takes
-// chunk i (entries 64i .. 64i+63 of the segment's run) of every segment that
-// has one, and issues all their coordinate and value loads, then all their
-// x loads, before any is used, so a step waits about twice per round for
-// memory whatever U.  Products go to s_y[16 u + row]; the row totals are
-// left there.
 template <int VK, int U>
 DBS_DEV void coo_entries_plus_u(const brsrc_t pay, const brsrc_t xr, const bool (&coo)[U], const uint64_t (&meta)[U],
-                                const uint32_t (&m)[U], const uint32_t (&cb)[U], uint32_t *s_mark, float *s_y,
-                                int lane) {
+                                const uint32_t (&m)[U], const uint32_t (&cb)[U], uint32_t drain,
+                                uint32_t *s_mark, float *s_acc, float (&coo_sum)[U], int lane) {
+  // drain: bit u set for a marked segment u (uniform)
   constexpr uint32_t VS = VK == VK_F32 ? 4u : 2u;
   uint32_t cnt[U], start[U], total[U], carry[U];
   uint32_t rounds = 0;
@@ -334,11 +290,10 @@ DBS_DEV void coo_entries_plus_u(const brsrc_t pay, const brsrc_t xr, const bool 
     start[u] = wave_incl_add(cnt[u]) - cnt[u];
     total[u] = (uint32_t)__builtin_amdgcn_readlane((int)(start[u] + cnt[u]), 63);
     carry[u] = 0u;
+    coo_sum[u] = 0.0f;
     const uint32_t r = (total[u] + 63u) >> 6;
     rounds = r > rounds ? r : rounds;
   }
-  if (lane < 16 * U) s_y[lane] = 0.0f;
-  __syncwarp();
   for (uint32_t i = 0; i < rounds; ++i) {
     const uint32_t j0 = 64u * i;
     int own[U];
@@ -384,39 +339,74 @@ DBS_DEV void coo_entries_plus_u(const brsrc_t pay, const brsrc_t xr, const bool 
       if (VK == VK_F32) x[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(xr, xoff, 0, 0));
       else x[u] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(xr, xoff, 0, 0) << 16);
     }
+    if constexpr (U == 1) {
+      // lane-private slot: the address differs for every lane
+      if (live[0]) atomicAdd(&s_acc[(rc[0] >> 4) * 64u + (uint32_t)lane], a[0] * x[0]);
+    } else {
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (live[u]) atomicAdd(&s_y[16 * u + (rc[u] >> 4)], a[u] * x[u]);
+      for (int u = 0; u < U; ++u)
+        if (live[u]) atomicAdd(&s_acc[16 * u + (rc[u] >> 4)], a[u] * x[u]);
+      if (drain != 0u) {  // uniform
+        // a step with a segment where a row holds more than SEG_DRAIN_ROW COO
+        // entries: the round's row sums of every segment go to a register at
+        // once, so that no LDS address takes more than 64 adds in a row
+        __syncwarp();
+#pragma unroll
+        for (int u = 0; u < U; ++u) coo_sum[u] += s_acc[16 * u + (lane & 15)];
+        __syncwarp();
+        if (lane < 16 * U) s_acc[lane] = 0.0f;
+      }
+    }
   }
-  __syncwarp();
+  if constexpr (U > 1) {
+    __syncwarp();
+#pragma unroll
+    for (int u = 0; u < U; ++u) coo_sum[u] += s_acc[16 * u + (lane & 15)];
+    __syncwarp();
+    if (lane < 16 * U) s_acc[lane] = 0.0f;
+    __syncwarp();
+  }
+  if constexpr (U == 1) {
+    if (rounds != 0u) {  // uniform
+      // lane (q, r) sums row r's slots of quarter q's lanes, starting at a
+      // lane that differs with r, so that the 64 reads of each step fall in
+      // 64 different banks; then the quarters are added (17 additions)
+      __syncwarp();
+      const uint32_t q = (uint32_t)lane >> 4, r = (uint32_t)lane & 15u;
+      float t = 0.0f;
+#pragma unroll 2
+      for (uint32_t k = 0; k < 16; ++k) {
+        const uint32_t idx = r * 64u + 16u * q + ((k + r) & 15u);
+        t += s_acc[idx];
+        s_acc[idx] = 0.0f;
+      }
+      coo_sum[0] = quarter_merge(t);
+      __syncwarp();
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
-// Finish one PLUS_TIMES pull segment whose tiles are loaded: COO entries over
-// the lanes, Dense and CSR-family tiles four at a time (row per lane),
-// ForceCSC and few-column patched CSR tiles one at a time; then write the row
-// block: a plain store when it is one segment, an atomic add when several
-// segments share it.
+// Finish one PLUS_TIMES pull segment whose COO entries are summed
+// (coo_sum) and whose other tiles are loaded: Dense and CSR-family tiles four
+// at a time (row per lane), ForceCSC and few-column patched CSR tiles one at
+// a time; then write the row block (section 3.3.3): a plain store when it is
+// one segment, the segment's partial slot when its row block is summed by
+// the finalize, else an atomic add.  Every product passes through at most
+// 16 (within a tile row) + 16 (tiles per lane) + 2 (quarter merge), or the
+// COO bound above, or 6 + 64 (one-at-a-time tiles) additions, plus 2 to join
+// the three sums.
 // ---------------------------------------------------------------------------
-template <int VK, bool COO_DONE = false, bool DENSE_PATH = true>
-DBS_DEV void pull_finish(const SpmvParams &P, uint4 seg, uint32_t cb, uint32_t m, uint64_t meta, bool act,
-                         float *sx, float *spart, uint32_t *s_mark, int lane, float coo_sum = 0.0f) {
+template <int VK, bool DENSE_PATH = true>
+DBS_DEV void pull_finish(const SpmvParams &P, uint4 seg, uint32_t part, uint32_t cb, uint32_t m, uint64_t meta,
+                         bool act, float *sx, float *spart, int lane, float coo_sum) {
   constexpr uint64_t VS = VK == VK_F32 ? 4 : 2;
-  const uint32_t rb = seg.x & ~SEG_SPLIT;
+  const uint32_t rb = seg.x & SEG_RB_MASK;
   const bool split = (seg.x & SEG_SPLIT) != 0u;
   const uint32_t type = meta_type(meta);
   const int64_t row0 = (int64_t)rb * 16;
   const brsrc_t pay = make_rsrc(P.payload, (uint64_t)P.payload_bytes + DBS_PAYLOAD_SLACK);
   const brsrc_t xr = make_rsrc(P.xd, (uint64_t)P.nb * 16 * VS);
-  float rowsum = coo_sum;  // COO_DONE: the segment's COO entries were summed already
-  const bool coo = act & (type == DBS_TILE_COO);
-  if (!COO_DONE && __ballot(coo) != 0ull) {
-    float *s_y = spart;
-    if (lane < 16) s_y[lane] = 0.0f;
-    coo_entries_plus<VK>(pay, xr, coo, meta, m, cb, s_mark, s_y, lane);
-    rowsum = s_y[lane & 15];
-    __syncwarp();
-  }
   // patched CSR tiles with few active columns take the column variant
   // (section 3.3.3); Dense tiles go four at a time through the row-broadcast
   // path, the other row-major tiles four at a time through the row-per-lane
@@ -424,12 +414,14 @@ DBS_DEV void pull_finish(const SpmvParams &P, uint4 seg, uint32_t cb, uint32_t m
   const uint64_t colv = __ballot(act & (type == DBS_TILE_CSR) & (__popc(m) < P.local_cutoff));
   const uint64_t dent = DENSE_PATH ? __ballot(act & (type == DBS_TILE_DENSE)) : 0ull;
   const uint64_t rowt = __ballot(act & (type != DBS_TILE_COO) & (type != DBS_TILE_FORCE_CSC)) & ~colv & ~dent;
+  float rsum = 0.0f;
   if (dent | rowt) {  // uniform
-    float part = 0.0f;
-    if (dent) part = dense_plus<VK>(pay, xr, dent, meta, m, cb, lane);
-    if (rowt) part += rows_plus<VK>(pay, xr, rowt, meta, m, cb, lane);
-    rowsum += quarter_merge(part);
+    float part_r = 0.0f;
+    if (dent) part_r = dense_plus<VK>(pay, xr, dent, meta, m, cb, lane);
+    if (rowt) part_r += rows_plus<VK>(pay, xr, rowt, meta, m, cb, lane);
+    rsum = quarter_merge(part_r);
   }
+  float tsum = 0.0f;
   uint64_t todo = __ballot(act & (type == DBS_TILE_FORCE_CSC)) | colv;
   while (todo) {
     const int src = __ffsll((unsigned long long)todo) - 1;
@@ -438,9 +430,24 @@ DBS_DEV void pull_finish(const SpmvParams &P, uint4 seg, uint32_t cb, uint32_t m
     const uint32_t tmask = (uint32_t)__shfl((int)m, src);
     const uint32_t tcb = (uint32_t)__shfl((int)cb, src);
     stage_x<VK>(sx, P.xd, tcb, tmask, lane);
-    rowsum += tile_plus<VK>(P.payload + meta_vp(tm), meta_type(tm), meta_nnz(tm), tmask, sx, spart,
-                            P.local_cutoff, lane);
+    tsum += tile_plus<VK>(P.payload + meta_vp(tm), meta_type(tm), meta_nnz(tm), tmask, sx, spart, P.local_cutoff,
+                          lane);
     __syncwarp();
+  }
+  const float rowsum = coo_sum + (rsum + tsum);
+  const uint32_t cls = (seg.x >> SEG_CLS_SHIFT) & 3u;
+  if (seg.w != 0u && cls >= (uint32_t)P.slot_cls) {  // uniform
+    // the row block is summed by the finalize: this segment's (and part's)
+    // slot, row sums in lanes 0..15 and this call's epoch in lane 16.  Row
+    // sums that are all zero are not written (a store in flight makes the
+    // next wait for a load wait for every load in flight): a slot without
+    // this call's epoch counts as zero.
+    if (__ballot((lane < 16) & (rowsum != 0.0f)) != 0ull) {
+      const uint32_t off = (((seg.w - 1u) * (uint32_t)P.plus_parts + part) * SLOT_WORDS + (uint32_t)lane) * 4u;
+      const uint32_t v = lane < 16 ? __float_as_uint(rowsum) : P.epoch;
+      if (lane < SLOT_WORDS) __builtin_amdgcn_raw_buffer_store_b32(v, make_rsrc(P.partial, P.partial_bytes), off, 0, 0);
+    }
+    return;
   }
   // y through a descriptor of the row block's entries (built in scalar
   // registers; rows past m fall outside it, so their lanes store nothing)
@@ -469,7 +476,7 @@ struct AllRows {
 
 template <int VK, int U, bool EAGER>
 DBS_DEV void plus_pull_wave(const SpmvParams &P, const PatSrc &S, const brsrc_t xm, int64_t s0, int64_t stride,
-                            int parts, float *sx, float *spart, uint32_t *s_mark, int lane) {
+                            int parts, float *sx, float *spart, uint32_t *s_mark, float *s_acc, int lane) {
   // work items: segments (U of them per step), or with parts > 1 (U = 1)
   // lane ranges of a segment, item = segment * parts + part
   const int64_t nitems = S.nseg * parts;
@@ -525,18 +532,21 @@ DBS_DEV void plus_pull_wave(const SpmvParams &P, const PatSrc &S, const brsrc_t 
 #pragma unroll
     for (int u = 0; u < U; ++u) coo_sum[u] = 0.0f;
     if (any_coo != 0ull) {  // uniform
-      coo_entries_plus_u<VK, U>(S.pay, xr, coo, g0.meta, ma, g0.cb, s_mark, spart, lane);
+      uint32_t drain = 0u;
 #pragma unroll
-      for (int u = 0; u < U; ++u) coo_sum[u] = spart[16 * u + (lane & 15)];
-      __syncwarp();
+      for (int u = 0; u < U; ++u) drain |= ((g0.seg[u].x >> 30) & 1u) << u;  // SEG_DRAIN
+      coo_entries_plus_u<VK, U>(S.pay, xr, coo, g0.meta, ma, g0.cb, drain, s_mark, s_acc, coo_sum, lane);
     }
+    const uint32_t part = (uint32_t)s0 & (uint32_t)(parts - 1);  // parts is 1, 2 or 4
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       uint4 sg = g0.seg[u];
       if (parts > 1) sg.x |= SEG_SPLIT;
+      // a segment with no active tile has nothing to add (y was cleared by
+      // the metadata kernel; a slot it does not write counts as zero)
       if ((s0 + u < nitems) && __ballot(ma[u] != 0u) != 0ull)  // uniform
-        pull_finish<VK, true, U == 1>(P, sg, g0.cb[u], ma[u], g0.meta[u], ma[u] != 0u, sx, spart, s_mark, lane,
-                                      coo_sum[u]);
+        pull_finish<VK, U == 1>(P, sg, part, g0.cb[u], ma[u], g0.meta[u], ma[u] != 0u, sx, spart, lane,
+                                coo_sum[u]);
     }
     s0 += stride;
     if (s0 >= nitems) break;
@@ -549,14 +559,22 @@ DBS_DEV void plus_pull_wave(const SpmvParams &P, const PatSrc &S, const brsrc_t 
 
 template <int VK, int U>
 DBS_DEV void plus_pull(const SpmvParams &P, int64_t gw, int64_t nw, bool eager, float *sx, float *spart,
-                       uint32_t *s_mark, int lane) {
+                       uint32_t *s_mark, float *s_acc, int lane) {
   const PatSrc S{P.t_cb, P.t_meta, P.segs, P.nseg,
                  make_rsrc(P.payload, (uint64_t)P.payload_bytes + DBS_PAYLOAD_SLACK), make_rsrc(P.rb_ptr, 0),
                  make_rsrc(nullptr, 0)};
   const brsrc_t xm = make_rsrc(P.xmask, (uint64_t)P.nb * 4);
   const int parts = U == 1 ? P.plus_parts : 1;
-  if (eager) plus_pull_wave<VK, U, true>(P, S, xm, gw * U, nw * U, parts, sx, spart, s_mark, lane);
-  else plus_pull_wave<VK, U, false>(P, S, xm, gw * U, nw * U, parts, sx, spart, s_mark, lane);
+  // the COO slots start (and are left) at zero
+  if constexpr (U == 1) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) s_acc[k * 64 + lane] = 0.0f;
+  } else {
+    if (lane < 16 * U) s_acc[lane] = 0.0f;
+  }
+  __syncwarp();
+  if (eager) plus_pull_wave<VK, U, true>(P, S, xm, gw * U, nw * U, parts, sx, spart, s_mark, s_acc, lane);
+  else plus_pull_wave<VK, U, false>(P, S, xm, gw * U, nw * U, parts, sx, spart, s_mark, s_acc, lane);
 }
 
 // OR-AND pull (the Boolean semiring of graph traversal): as pull_group, with
@@ -570,7 +588,7 @@ struct PullRes {
 
 // write the found rows of one segment's row block (lanes 0..15)
 DBS_DEV void pull_or_store(const SpmvParams &P, uint4 seg, uint32_t f, int lane) {
-  const uint32_t rb = seg.x & ~SEG_SPLIT;
+  const uint32_t rb = seg.x & SEG_RB_MASK;
   const int64_t row = (int64_t)rb * 16 + lane;
   if (lane < 16 && row < P.m) {
     const uint8_t bit = (uint8_t)((f >> lane) & 1u);
@@ -676,6 +694,9 @@ __global__ __launch_bounds__(KT, ((VK == VK_BF16 && SR == DBS_PLUS_TIMES && PU =
   __shared__ uint32_t s_mark[KT / DBS_WAVE][64];
   __shared__ uint32_t s_cum[SR == DBS_OR_AND ? dbs_meta::PUSH_LIST_MAX : 1];
   __shared__ uint32_t s_pat[VK == VK_PAT && SR == DBS_OR_AND ? KT / DBS_WAVE : 1][PAT_LDS_WORDS];
+  // PLUS_TIMES pull: COO row sums, lane-private (16 rows x 64 lanes per wave)
+  // with one segment per step, 16 per segment of a step otherwise
+  __shared__ float s_acc[SR == DBS_PLUS_TIMES ? KT / DBS_WAVE : 1][SR == DBS_PLUS_TIMES ? (PU == 1 ? 1024 : 16 * PU) : 1];
   const int lane = __lane_id();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / DBS_WAVE);
   const uint32_t nz = dbs_meta::nzblk_clamped(P.ctr[0], P.nb);
@@ -715,9 +736,144 @@ __global__ __launch_bounds__(KT, ((VK == VK_BF16 && SR == DBS_PLUS_TIMES && PU =
         for (int64_t s = gw * U; s < P.nseg; s += nw * U) pull_or_group<VK, U>(P, R, s, eager, lane);
       }
     } else {
-      plus_pull<VK, PU>(P, gw, nw, eager, s_x[w], s_part[w], s_mark[w], lane);
+      plus_pull<VK, PU>(P, gw, nw, eager, s_x[w], s_part[w], s_mark[w], s_acc[w], lane);
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Finalize of the row blocks whose pull segments wrote partial slots this
+// call (long row blocks split over many segments, section 3.3.2; the last
+// level of the hierarchical writeback, section 3.3.3): y of each of their
+// rows is the sum of K = segments x sharing waves row sums, in one fixed
+// order, so the result does not depend on the order the waves ran in.  The
+// list runs from the longest row block down (only its first entries take
+// slots at a given sharing).  The first nbig entries (more than 256 slots)
+// get a workgroup of 1024 threads each, the others a wave each (16 per
+// workgroup).  Thread (g, r) of a row block's G groups of 16 takes the
+// blocks of 16 consecutive slots b = g, g + G, ..., sums each block pairwise
+// for row r (four levels) and keeps the block sums in a binary counter
+// (level k holds the sum of 2^k consecutive blocks, earlier blocks on the
+// left); the G group sums of a row are then added pairwise (through LDS for
+// G = 64, by lane exchanges for G = 4).  A slot's value passes through at
+// most 4 + 2 ceil(log2(blocks per group)) + 1 + log2(G) additions here.  A
+// slot that does not carry this call's epoch was not written by this call
+// (its segment had nothing to add) and counts as zero.
+// ---------------------------------------------------------------------------
+constexpr int FIN_LV = 24;  // counter levels: up to 2^24 blocks per group
+
+// one block of 16 slots for row r: the values and, from lane j of the
+// 16-lane group, slot j's epoch tag
+struct FinBlock {
+  float v[16];
+  uint32_t tag;
+};
+
+DBS_DEV FinBlock fin_load(const float *partial, uint64_t base, uint32_t K, uint32_t b, int r) {
+  FinBlock f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const uint32_t k = b * 16u + (uint32_t)j;
+    f.v[j] = partial[(base + (k < K ? k : 0u)) * SLOT_WORDS + (uint32_t)r];
+  }
+  const uint32_t kr = b * 16u + (uint32_t)r;
+  f.tag = kr < K ? __float_as_uint(partial[(base + kr) * SLOT_WORDS + 16u]) : 0u;
+  return f;
+}
+
+template <int J = 0>
+DBS_DEV void fin_mask(FinBlock &f, uint32_t epoch) {
+  if constexpr (J < 16) {
+    const uint32_t t = quarter_bcast<J>(f.tag);  // slot J's tag, from lane J of the group
+    f.v[J] = t == epoch ? f.v[J] : 0.0f;
+    fin_mask<J + 1>(f, epoch);
+  }
+}
+
+// group g's sum of row r over blocks g, g + G, ... (every lane of the wave
+// takes part: the tag broadcast works on whole rows of 16 lanes)
+DBS_DEV float fin_group(const float *partial, uint64_t base, uint32_t K, uint32_t g, uint32_t G, int r,
+                        uint32_t epoch) {
+  const uint32_t nblk = (K + 15u) >> 4;
+  float st[FIN_LV];
+#pragma unroll
+  for (int lv = 0; lv < FIN_LV; ++lv) st[lv] = 0.0f;
+  uint32_t cnt = 0;
+  uint32_t b = g;
+  FinBlock cur = fin_load(partial, base, K, b < nblk ? b : 0u, r);
+  const uint32_t iters = (nblk + G - 1u) / G;  // the same for every group of the row block
+  for (uint32_t it = 0; it < iters; ++it) {    // the next block's loads in flight
+    const uint32_t bn = b + G;
+    const FinBlock nxt = fin_load(partial, base, K, bn < nblk ? bn : 0u, r);
+    fin_mask(cur, epoch);
+#pragma unroll
+    for (int w = 1; w < 16; w <<= 1)
+#pragma unroll
+      for (int j = 0; j < 16; j += 2 * w) cur.v[j] = cur.v[j] + cur.v[j + w];
+    if (b < nblk) {
+      // binary counter: merge the levels below the first free one
+      float bs = cur.v[0];
+      const uint32_t t = (uint32_t)__builtin_ctz(~cnt);
+#pragma unroll
+      for (int lv = 0; lv < FIN_LV; ++lv)
+        if ((uint32_t)lv < t) bs = st[lv] + bs;
+#pragma unroll
+      for (int lv = 0; lv < FIN_LV; ++lv)
+        if ((uint32_t)lv == t) st[lv] = bs;
+      ++cnt;
+    }
+    cur = nxt;
+    b = bn;
+  }
+  // fold the counter, the most recent (lowest) level first
+  float tot = 0.0f;
+  bool have = false;
+#pragma unroll
+  for (int lv = 0; lv < FIN_LV; ++lv) {
+    if ((cnt >> lv) & 1u) {
+      tot = have ? st[lv] + tot : st[lv];
+      have = true;
+    }
+  }
+  return tot;
+}
+
+__global__ __launch_bounds__(1024) void k_plus_finalize(const uint32_t *fin, int64_t nfin, int64_t nbig,
+                                                       const float *partial, int32_t parts, uint32_t epoch,
+                                                       const uint32_t *ctr, int32_t nb, int32_t force_path,
+                                                       int64_t th3_num, int64_t th3_den, float *y, int32_t m) {
+  __shared__ float s_g[64][16];  // [thread group][row]
+  const uint32_t nz = dbs_meta::nzblk_clamped(ctr[0], nb);
+  if (dbs_meta::selector_push(nz, nb, force_path, th3_num, th3_den)) return;  // uniform: pushed, no slots
+  const int tid = (int)threadIdx.x, r = tid & 15;
+  if ((int64_t)blockIdx.x < nbig) {
+    // a long row block: 64 groups of 16 threads
+    const int64_t e = blockIdx.x;
+    const uint32_t rb = fin[4 * e], slot0 = fin[4 * e + 1], nsegs = fin[4 * e + 2];
+    const int g = tid >> 4;
+    const float tot = fin_group(partial, (uint64_t)slot0 * (uint32_t)parts, nsegs * (uint32_t)parts, (uint32_t)g,
+                                64u, r, epoch);
+    s_g[g][r] = tot;
+    __syncthreads();
+#pragma unroll
+    for (int w = 1; w < 64; w <<= 1) {
+      if ((g & (2 * w - 1)) == 0) s_g[g][r] = s_g[g][r] + s_g[g + w][r];
+      __syncthreads();
+    }
+    const int64_t row = (int64_t)rb * 16 + r;
+    if (g == 0 && row < m) y[row] = s_g[0][r];
+    return;
+  }
+  // the others: a wave each, 4 groups of 16 lanes
+  const int64_t e = nbig + ((int64_t)blockIdx.x - nbig) * 16 + (tid >> 6);
+  if (e >= nfin) return;  // uniform per wave
+  const uint32_t rb = fin[4 * e], slot0 = fin[4 * e + 1], nsegs = fin[4 * e + 2];
+  const int lane = tid & 63;
+  const float tot = fin_group(partial, (uint64_t)slot0 * (uint32_t)parts, nsegs * (uint32_t)parts,
+                              (uint32_t)(lane >> 4), 4u, r, epoch);
+  const float sum = quarter_merge(tot);  // (g0 + g1) + (g2 + g3)
+  const int64_t row = (int64_t)rb * 16 + r;
+  if (lane < 16 && row < m) y[row] = sum;
 }
 
 inline unsigned grid_for(int64_t waves, unsigned cap) {
@@ -730,12 +886,14 @@ inline unsigned grid_for(int64_t waves, unsigned cap) {
 // (the extended launch costs the host more, so only then)
 template <typename K, typename... Args>
 void launch_k(K kernel, dim3 grid, dim3 block, hipStream_t s, hipEvent_t e0, hipEvent_t e1, Args... args) {
-  if (e0) hipExtLaunchKernelGGL(kernel, grid, block, 0, s, e0, e1, 0, args...);
+  if (e0 || e1) hipExtLaunchKernelGGL(kernel, grid, block, 0, s, e0, e1, 0, args...);
   else hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
 }
 
+// returns the number of waves that share a segment (1 unless PLUS_TIMES
+// with one segment per step)
 template <int VK, int SR, int PU = 1>
-void launch_spmspv(SpmvParams P, int64_t waves, int share, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+int launch_spmspv(SpmvParams P, int64_t waves, int share, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   static const unsigned resident = dbs_resident_groups(k_spmspv<VK, SR, PU>, KT);
   P.plus_parts = 1;
   if (SR == DBS_PLUS_TIMES && PU == 1 && P.nseg > 0) {
@@ -746,7 +904,9 @@ void launch_spmspv(SpmvParams P, int64_t waves, int share, hipStream_t s, hipEve
     P.plus_parts = share ? share : parts >= PLUS_MAX_PARTS ? PLUS_MAX_PARTS : parts >= 2 ? 2 : 1;
     if (P.nseg * P.plus_parts > waves) waves = P.nseg * P.plus_parts;
   }
+  P.slot_cls = (int32_t)seg_slot_class(P.plus_parts);
   launch_k(k_spmspv<VK, SR, PU>, dim3(grid_for(waves, resident)), dim3(KT), s, e0, e1, P);
+  return P.plus_parts;
 }
 
 }  // namespace
@@ -765,6 +925,12 @@ dbs_status dbs_spmspv_impl(dbs_matrix *A, int32_t nnz_x, const int32_t *x_idx, c
     hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)((A->nb + 255) / 256)), dim3(256), 0, s, A->xmask,
                        (int64_t)A->nb, 0u);
     SPMV_TRY(hipGetLastError());
+    if (A->partial) {  // the partial slots' epoch tags too
+      const int64_t words = A->nslots * DBS_MAX_SHARE * SLOT_WORDS;
+      hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, s, (uint32_t *)A->partial,
+                         words, 0u);
+      SPMV_TRY(hipGetLastError());
+    }
     A->epoch = 1;
   }
   MetaOut o;
@@ -848,6 +1014,9 @@ dbs_status dbs_spmspv_impl(dbs_matrix *A, int32_t nnz_x, const int32_t *x_idx, c
   P.xmask = A->xmask;
   P.epoch = A->epoch;
   P.xd = A->xd;  // PLUS_TIMES only: the staged x (OR_AND reads the masks alone)
+  P.partial = A->partial;
+  P.partial_bytes = (uint32_t)(A->nslots * DBS_MAX_SHARE * SLOT_WORDS * 4);
+  P.slot_cls = 4;  // set per launch
   P.chunks = A->chunks;
   P.max_chunks = A->max_chunks;
   P.xlist = A->act_list;
@@ -883,12 +1052,51 @@ dbs_status dbs_spmspv_impl(dbs_matrix *A, int32_t nnz_x, const int32_t *x_idx, c
     else launch_spmspv<VK_PAT, DBS_OR_AND>(P, waves, 0, s, c0, c1);
   } else {
     const bool wide = P.plus_u == PULL_U_PLUS_WIDE;
+    // the parts (waves sharing a segment) are fixed before the launch: the
+    // same rule as launch_spmspv's, so that the finalize is known here
+    int parts = 1;
+    if (!wide && P.nseg > 0) {
+      parts = share;
+      if (!parts) {
+        static const unsigned res1_f = dbs_resident_groups(k_spmspv<VK_F32, DBS_PLUS_TIMES, 1>, KT);
+        static const unsigned res1_b = dbs_resident_groups(k_spmspv<VK_BF16, DBS_PLUS_TIMES, 1>, KT);
+        const int64_t rw = (int64_t)(vk == VK_F32 ? res1_f : res1_b) * (KT / DBS_WAVE);
+        const int64_t pp = (rw + P.nseg - 1) / P.nseg;
+        parts = pp >= PLUS_MAX_PARTS ? PLUS_MAX_PARTS : pp >= 2 ? 2 : 1;
+      }
+    }
+    // a sparse x has N_nzblk <= nnz_x (whatever its order), so a call that
+    // must push is known here: it needs no finalize launch
+    const int64_t fp = A->opt[DBS_OPT_PATH];
+    const bool must_push =
+        fp == 1 || (!dense && fp == 0 && (int64_t)nnz_x * A->opt[DBS_OPT_TH3_DEN] <
+                                             (int64_t)A->nb * A->opt[DBS_OPT_TH3_NUM]);
+    // the list is sorted by segment count: its first fin_cls[c] entries are
+    // those of class c or above, the ones that took slots
+    const int64_t nfin_used = A->nfin > 0 ? A->fin_cls[seg_slot_class(parts)] : 0;
+    const bool fin = nfin_used > 0 && !must_push;
+    // with a finalize, the call's compute time runs from the pull's start to
+    // the finalize's end
+    hipEvent_t pe1 = fin ? nullptr : c1;
+    int used = 0;
     if (vk == VK_F32) {
-      if (wide) launch_spmspv<VK_F32, DBS_PLUS_TIMES, PULL_U_PLUS_WIDE>(P, waves, share, s, c0, c1);
-      else launch_spmspv<VK_F32, DBS_PLUS_TIMES, 1>(P, waves, share, s, c0, c1);
+      if (wide) used = launch_spmspv<VK_F32, DBS_PLUS_TIMES, PULL_U_PLUS_WIDE>(P, waves, parts, s, c0, pe1);
+      else used = launch_spmspv<VK_F32, DBS_PLUS_TIMES, 1>(P, waves, parts, s, c0, pe1);
     } else {
-      if (wide) launch_spmspv<VK_BF16, DBS_PLUS_TIMES, PULL_U_PLUS_WIDE>(P, waves, share, s, c0, c1);
-      else launch_spmspv<VK_BF16, DBS_PLUS_TIMES, 1>(P, waves, share, s, c0, c1);
+      if (wide) used = launch_spmspv<VK_BF16, DBS_PLUS_TIMES, PULL_U_PLUS_WIDE>(P, waves, parts, s, c0, pe1);
+      else used = launch_spmspv<VK_BF16, DBS_PLUS_TIMES, 1>(P, waves, parts, s, c0, pe1);
+    }
+    SPMV_TRY(hipGetLastError());
+    if (used != parts) return DBS_ERR_DEVICE;  // cannot happen: both follow the same rule
+    if (fin) {
+      // entries of more than 256 slots get a workgroup each, the others a wave
+      const int64_t nbig = A->fin_big[parts == 4 ? 2 : parts == 2 ? 1 : 0] < nfin_used
+                               ? A->fin_big[parts == 4 ? 2 : parts == 2 ? 1 : 0]
+                               : nfin_used;
+      const int64_t g = nbig + (nfin_used - nbig + 15) / 16;
+      launch_k(k_plus_finalize, dim3((unsigned)g), dim3(1024), s, nullptr, c1, (const uint32_t *)A->fin, nfin_used,
+               nbig, (const float *)A->partial, (int32_t)parts, A->epoch, (const uint32_t *)o.reg.ctr, A->nb,
+               (int32_t)A->opt[DBS_OPT_PATH], A->opt[DBS_OPT_TH3_NUM], A->opt[DBS_OPT_TH3_DEN], (float *)y, A->m);
     }
   }
   SPMV_TRY(hipGetLastError());

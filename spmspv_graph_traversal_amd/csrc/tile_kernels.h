@@ -270,47 +270,6 @@ DBS_DEV uint32_t tile_or(const uint8_t *base, const uint8_t *dense_mask, uint32_
 // ---------------------------------------------------------------------------
 // COO (section 3.3.3: scan the packed coordinates), one tile per lane.
 // ---------------------------------------------------------------------------
-// PLUS_TIMES, accumulated into the lane's 16 row registers.  Coordinates and
-// values are read 8 entries at a time with independent loads (the COO
-// payload is 4-B aligned), then the x values of those entries, so a tile
-// costs two memory round trips per 8 entries instead of one per entry.
-template <int VK>
-DBS_DEV void coo_plus(const uint8_t *base, uint32_t nnz, uint32_t m, const void *xd, int64_t xbase,
-                      float (&acc)[16]) {
-  constexpr int VS = VK == VK_F32 ? 4 : 2;
-  const uint8_t *vals = base + coo_val_off(nnz);
-  const uint32_t lastw = (nnz - 1) >> 2;
-  for (uint32_t e0 = 0; e0 < nnz; e0 += 8) {
-    // clamped indices everywhere: no branch around a load
-    const uint32_t w0 = ((const uint32_t *)base)[e0 >> 2];
-    const uint32_t w1 = ((const uint32_t *)base)[((e0 >> 2) + 1) < lastw ? (e0 >> 2) + 1 : lastw];
-    float a[8], xv[8];
-    uint32_t rc[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      rc[k] = ((k < 4 ? w0 : w1) >> (8 * (k & 3))) & 0xFFu;
-      const uint32_t e = e0 + k < nnz ? e0 + k : nnz - 1;
-      a[k] = load_a<VK>(vals + e * VS);
-    }
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const uint32_t c = rc[k] & 15u;
-      const bool on = e0 + k < nnz && ((m >> c) & 1u);
-      const float v = load_x<VK>(xd, xbase + (on ? c : 0u));
-      xv[k] = on ? v : 0.0f;
-    }
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const uint32_t c = rc[k] & 15u, rr = rc[k] >> 4;
-      if (e0 + k < nnz && ((m >> c) & 1u)) {
-        const float t = a[k] * xv[k];
-#pragma unroll
-        for (int q = 0; q < 16; ++q) acc[q] += (rr == (uint32_t)q) ? t : 0.0f;
-      }
-    }
-  }
-}
-
 // OR-AND of a COO tile from its (4-B aligned) coordinate bytes, 32 entries
 // per round of independent loads
 DBS_DEV uint32_t coo_or(const uint8_t *base, uint32_t nnz, uint32_t m) {
@@ -333,30 +292,6 @@ DBS_DEV uint32_t coo_or(const uint8_t *base, uint32_t nnz, uint32_t m) {
   return f;
 }
 
-// OR-AND of a COO tile whose first 8 coordinate bytes were loaded ahead
-// (pw0, pw1); entries beyond the eighth are read here.
-DBS_DEV uint32_t coo_or_pre(const uint8_t *payload, uint64_t meta, uint32_t m, uint32_t pw0, uint32_t pw1) {
-  const uint32_t nnz = meta_nnz(meta);
-  if (meta_inline(meta)) pw0 = (uint32_t)meta;
-  uint32_t f = 0;
-#pragma unroll
-  for (uint32_t e = 0; e < 8; ++e) {
-    const uint32_t rc = ((e < 4 ? pw0 : pw1) >> (8 * (e & 3))) & 0xFFu;
-    if (e < nnz && ((m >> (rc & 15u)) & 1u)) f |= 1u << (rc >> 4);
-  }
-  if (nnz > 8) f |= coo_or(payload + meta_vp(meta) + 8, nnz - 8, m);
-  return f;
-}
-
-// first two payload words of a COO tile that is not inline (else of the
-// arena start, a valid dummy), loaded without a branch
-DBS_DEV void coo_preload(const uint8_t *payload, uint64_t meta, bool act, uint32_t &pw0, uint32_t &pw1) {
-  const bool pre = act & (meta_type(meta) == DBS_TILE_COO) & !meta_inline(meta);
-  const uint32_t *w = (const uint32_t *)(payload + (pre ? meta_vp(meta) : 0));
-  pw0 = w[0];
-  pw1 = w[1];
-}
-
 // OR-AND of a COO tile given its metadata word (coordinates inline or in the payload)
 DBS_DEV uint32_t coo_or_meta(const uint8_t *payload, uint64_t meta, uint32_t m) {
   const uint32_t nnz = meta_nnz(meta);
@@ -371,37 +306,6 @@ DBS_DEV uint32_t coo_or_meta(const uint8_t *payload, uint64_t meta, uint32_t m) 
     return f;
   }
   return coo_or(payload + meta_vp(meta), nnz, m);
-}
-
-// Sum of the 16 per-lane row registers over the wave; row k's total ends in
-// lane k (lanes 0..15).  Recursive halving: each of the first four exchange
-// rounds keeps half of the rows, then two rounds finish the sum.
-DBS_DEV float wave_rows_reduce(float (&acc)[16], int lane) {
-  float v8[8], v4[4], v2[2];
-  const bool h5 = lane & 32, h4 = lane & 16, h3 = lane & 8, h2 = lane & 4;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float keep = h5 ? acc[8 + i] : acc[i];
-    const float send = h5 ? acc[i] : acc[8 + i];
-    v8[i] = keep + __shfl_xor(send, 32);
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float keep = h4 ? v8[4 + i] : v8[i];
-    const float send = h4 ? v8[i] : v8[4 + i];
-    v4[i] = keep + __shfl_xor(send, 16);
-  }
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const float keep = h3 ? v4[2 + i] : v4[i];
-    const float send = h3 ? v4[i] : v4[2 + i];
-    v2[i] = keep + __shfl_xor(send, 8);
-  }
-  float v = (h2 ? v2[1] : v2[0]) + __shfl_xor(h2 ? v2[0] : v2[1], 4);
-  v += __shfl_xor(v, 2);
-  v += __shfl_xor(v, 1);
-  // lanes 4k..4k+3 hold row k
-  return __shfl(v, (lane & 15) * 4);
 }
 
 // ---------------------------------------------------------------------------
@@ -578,11 +482,13 @@ DBS_DEV float rows_products(const RowsStep &t, const RowVals<VK> &vw, uint32_t q
   const uint32_t sh = (t.vp & 2u) ? 16u : 0u;
   const uint32_t qb = q << 4;
   uint32_t rest = t.rmk;
-  if (kmax > 0u) rows_chunk<VK, 0>(vw, sh, xt, qb, cnt, rest, part);  // uniform
-  if (kmax > 4u) rows_chunk<VK, 4>(vw, sh, xt, qb, cnt, rest, part);
-  if (kmax > 8u) rows_chunk<VK, 8>(vw, sh, xt, qb, cnt, rest, part);
-  if (kmax > 12u) rows_chunk<VK, 12>(vw, sh, xt, qb, cnt, rest, part);
-  return part;
+  // the tile row's dot product on its own (at most 16 products), then one add
+  float tp = 0.0f;
+  if (kmax > 0u) rows_chunk<VK, 0>(vw, sh, xt, qb, cnt, rest, tp);  // uniform
+  if (kmax > 4u) rows_chunk<VK, 4>(vw, sh, xt, qb, cnt, rest, tp);
+  if (kmax > 8u) rows_chunk<VK, 8>(vw, sh, xt, qb, cnt, rest, tp);
+  if (kmax > 12u) rows_chunk<VK, 12>(vw, sh, xt, qb, cnt, rest, tp);
+  return part + tp;
 }
 
 // ---------------------------------------------------------------------------
@@ -678,7 +584,8 @@ DBS_DEV float dense_products(const DenseStep<VK> &t, uint32_t r, float part) {
     const uint32_t m2 = t.mk >> (2u * (r & 7u));
     xm = t.xw & (((m2 & 1u) ? 0x0000FFFFu : 0u) | ((m2 & 2u) ? 0xFFFF0000u : 0u));
   }
-  return dense_dot<VK>(t.w, xm, part);
+  // the tile row's dot product on its own (at most 16 products), then one add
+  return part + dense_dot<VK>(t.w, xm, 0.0f);
 }
 
 template <int VK>

@@ -64,11 +64,39 @@ def check_format(dbs, m, n, rp, ci, vbits, dtype, vk, opt=None, th=(32, 128, 2.0
     # pull segments follow the weighted rule of the oracle
     srb, s0, s1 = orc.segments(tv["rb_ptr"], exp_types, cap=cap)
     segs = ar["segs"]
-    np.testing.assert_array_equal(segs[:, 0] & 0x7FFFFFFF, srb)
+    np.testing.assert_array_equal(segs[:, 0] & 0x0FFFFFFF, srb)
     np.testing.assert_array_equal(segs[:, 1], s0)
     np.testing.assert_array_equal(segs[:, 2], s1)
     per_rb = np.bincount(srb, minlength=(m + 15) // 16)
     np.testing.assert_array_equal(segs[:, 0] >> 31, (per_rb[srb] > 1).astype(np.uint32))
+    # value matrices: the row blocks of more than 16 segments carry a size
+    # class (1: <= 32 segments, 2: <= 64, 3: more) and one partial slot per
+    # segment, numbered in segment order over those row blocks
+    c = per_rb[srb]
+    if vk != 2:
+        cls = np.where(c <= 16, 0, np.where(c <= 32, 1, np.where(c <= 64, 2, 3)))
+        long_seg = c > 16
+        slot = np.zeros(srb.shape[0], np.uint32)
+        slot[long_seg] = np.arange(1, int(long_seg.sum()) + 1, dtype=np.uint32)
+    else:
+        cls = np.zeros(srb.shape[0], np.int64)
+        slot = np.zeros(srb.shape[0], np.uint32)
+    np.testing.assert_array_equal((segs[:, 0] >> 28) & 3, cls.astype(np.uint32))
+    # value matrices: segments where a row has more than 32 entries in COO
+    # tiles are marked (bit 30)
+    if vk != 2:
+        # tile of every CSR entry (tiles in block-CSR order), its segment
+        key_t = tv["t_rb"].astype(np.int64) * (n // 16 + 1) + tv["t_cb"]
+        key_e = (ref_rows // 16).astype(np.int64) * (n // 16 + 1) + ci // 16
+        tile_e = np.searchsorted(key_t, key_e)
+        tile_seg = np.repeat(np.arange(srb.shape[0]), s1 - s0)
+        coo_e = exp_types[tile_e] == 0
+        k2 = tile_seg[tile_e[coo_e]] * 16 + ref_rows[coo_e] % 16
+        coo_rows = np.bincount(k2, minlength=16 * srb.shape[0]).reshape(-1, 16)
+        np.testing.assert_array_equal((segs[:, 0] >> 30) & 1, (coo_rows.max(axis=1) > 32).astype(np.uint32))
+    else:
+        assert not ((segs[:, 0] >> 30) & 1).any()
+    np.testing.assert_array_equal(segs[:, 3], slot)
     for f in range(5):
         assert st["tiles_by_format"][f] == int(np.count_nonzero(exp_types == f))
         assert st["nnz_by_format"][f] == int(tv["t_nnz"][exp_types == f].sum())
@@ -210,3 +238,26 @@ def test_long_row_blocks_segments(dbs, cap):
     _, tv = check_format(dbs, m, n, rp, ci, v, dbs.DBS_F32, 0, opt=opt, cap=cap)
     assert np.diff(tv["rb_ptr"]).max() > 1024
     check_format(dbs, m, n, rp, ci, None, dbs.DBS_PATTERN, 2, opt=opt, cap=cap)
+
+
+def hub_row_dense(seed, n=8192):
+    """64 x n: row 5 holds an entry in every column (16 per tile), the others
+    a few random ones, so every tile stays COO (fewer than 32 entries) while
+    row 5 has 64 x 16 entries per full pull segment."""
+    rng = rng_for("test", 630, seed)
+    a = np.zeros((64, n), np.float32)
+    a[5, :] = rng.uniform(-1, 1, n).astype(np.float32)
+    for r in range(64):
+        if r != 5:
+            cols = rng.choice(n, 40, replace=False)
+            a[r, cols] = rng.uniform(-1, 1, 40).astype(np.float32)
+    a[a == 0.0] = 0.0
+    return a
+
+
+def test_drain_marks_hub_rows(dbs):
+    a = hub_row_dense(0)
+    rp, ci, v = csr_of(a)
+    A, tv = check_format(dbs, a.shape[0], a.shape[1], rp, ci, v, dbs.DBS_F32, 0)
+    segs = dbs.dbs_copy_array(A, dbs.DBS_ARR_SEGMENTS).reshape(-1, 4)
+    assert ((segs[:, 0] >> 30) & 1).any() and not ((segs[:, 0] >> 30) & 1).all()

@@ -142,3 +142,65 @@ def test_forced_format_spmspv_and_bfs(dbs, force):
             for H in (A, B, P):
                 dbs.dbs_set_option(H, dbs.DBS_OPT_PATH, path)
                 np.testing.assert_array_equal(run_bfs(dbs, H, n, src), ref, err_msg=f"bfs src {src} path {path}")
+
+
+@pytest.mark.parametrize("cap", [3, 5, 9])
+def test_plus_times_partial_slots_and_finalize(dbs, cap):
+    """Row blocks of 150 tiles of mixed formats split into many pull segments
+    (with cap 3 50 to 75 per row block, class 3; cap 5 50, class 2; cap 9 25,
+    class 1): their row sums go to partial slots, summed by the finalize,
+    whenever segments x sharing waves exceeds 64.  Consecutive
+    calls activate different column ranges, so segments that wrote a slot in
+    one call have nothing to add in the next: their slots must count as zero
+    (they carry the writing call's epoch).  f32 and bf16, every pull width
+    and sharing, the finalize's result against the oracle."""
+    a = mixed_tile_dense(2, mb=3, nb=150, ragged=(5, 3))
+    m, n = a.shape
+    opt = options(dbs, seg_cap=cap)
+    rp, ci, v = csr_of(a)
+    _, _, bits = bf16_csr_of(a)
+    A = build(dbs, m, n, rp, ci, v, dbs.DBS_F32, opt)
+    B = build(dbs, m, n, rp, ci, bits, dbs.DBS_BF16, opt)
+    segs = dbs.dbs_copy_array(A, dbs.DBS_ARR_SEGMENTS).reshape(-1, 4)
+    per_rb = np.bincount(segs[:, 0] & 0x0FFFFFFF)
+    assert per_rb.max() > (64 if cap == 3 else 16)
+    rng = rng_for("test", 920, cap)
+    calls = []
+    for k in range(4):
+        lo, hi = [(0, n), (0, n // 3), (n // 2, n), (n // 4, n // 4 + 40)][k]
+        xi = np.sort(rng.choice(np.arange(lo, hi), size=max(1, (hi - lo) // 5), replace=False)).astype(np.int32)
+        xv = rng.uniform(-1, 1, xi.shape[0]).astype(np.float32)
+        calls.append((xi, xv))
+    for width, share in WIDTH_SHARE:
+        for H in (A, B):
+            dbs.dbs_set_option(H, dbs.DBS_OPT_PATH, 2)
+            dbs.dbs_set_option(H, dbs.DBS_OPT_PULL_WIDTH, width)
+            dbs.dbs_set_option(H, dbs.DBS_OPT_PULL_SHARE, share)
+        for k, (xi, xv) in enumerate(calls):
+            xb = f32_to_bf16_bits(xv)
+            yr, s = orc.spmspv_pull(m, n, rp, ci, v, orc.F32, xi, xv, orc.F32)
+            yb, sb = orc.spmspv_pull(m, n, rp, ci, bits, orc.BF16, xi, xb, orc.BF16)
+            what = f"call {k} width {width} share {share}"
+            assert_close(run_plus(dbs, A, m, xi, xv), yr, s, "f32 " + what)
+            assert_close(run_plus(dbs, B, m, xi, xb, bf16=True), yb, sb, "bf16 " + what)
+
+
+def test_plus_times_hub_row_drained_segments(dbs):
+    """A row with an entry in every column, in COO tiles: its pull segments
+    hold up to 1024 of its entries (marked segments, whose LDS row sums are
+    emptied after every round in the wide pull).  Every pull variant against
+    the oracle, sparse and full x."""
+    from test_gpu_format import hub_row_dense
+
+    a = hub_row_dense(1)
+    m, n = a.shape
+    rp, ci, v = csr_of(a)
+    A = build(dbs, m, n, rp, ci, v, dbs.DBS_F32)
+    for k, density in enumerate((0.05, 1.0)):
+        xi, xv = sparse_x(n, density, rng_for("test", 930, k))
+        yr, s = orc.spmspv_pull(m, n, rp, ci, v, orc.F32, xi, xv, orc.F32)
+        for width, share in WIDTH_SHARE:
+            dbs.dbs_set_option(A, dbs.DBS_OPT_PATH, 2)
+            dbs.dbs_set_option(A, dbs.DBS_OPT_PULL_WIDTH, width)
+            dbs.dbs_set_option(A, dbs.DBS_OPT_PULL_SHARE, share)
+            assert_close(run_plus(dbs, A, m, xi, xv), yr, s, f"density {density} width {width} share {share}")
