@@ -21,8 +21,12 @@ of the largest component (GTEPS) with an Auto / Push / Pull ablation on 8 of
 them; the single-token decode layers 11008x4096 / 4096x11008 (µs per call,
 warm and with rotating copies to defeat the on-package cache), also with the
 activation sparsified by magnitude inside the metadata kernel (10% kept); the
-format size against CSR and CSR + CSC; the Zipf/band stress matrix.
-`--ablations` adds the tile-format ablation (COO-only / CSR-only / adaptive).
+format size against CSR and CSR + CSC; the Tiny configuration (4096^2, fp32,
+x 1%); the Zipf/band stress matrix; GFLOP/s of the plus-times workloads in the
+SpMV-equivalent count 2 nnz(A) and the useful count 2 nnz(A[:, J]); and the
+tile-format ablation (COO-only / CSR-only / adaptive; `--no-ablations` skips
+it).  The CPU baseline is the oracle's Boolean pull on one host thread, with
+the same loop on every host core beside it.
 
 Byte model (bytes a kernel must move for the path it takes; per call):
   pull     16*segments + 4*T (column block of every tile) + 4*N_blk (masks)
@@ -163,6 +167,64 @@ def crossover(rows):
     return None
 
 
+def gflops(nnz_all, nnz_active, seconds):
+    """GFLOP/s of a call in the two counts: the SpMV-equivalent 2 nnz(A) (the
+    DB-SpMSpV paper's evaluation count) and the useful 2 nnz(A[:, J]) (entries
+    in the active columns)."""
+    return {"GFLOPs_spmv_equiv": round(2.0 * nnz_all / seconds / 1e9, 2),
+            "GFLOPs_useful": round(2.0 * nnz_active / seconds / 1e9, 2)}
+
+
+def bench_tiny(dbs, torch, args):
+    """Tiny: 4096 x 4096, 16 distinct uniform columns per row, fp32 U[-1,1];
+    x with 1% entries (41) at uniform positions; plus-times.  A latency-bound
+    configuration (about 1 MB per call)."""
+    from synth import rng_for, sparse_x, uniform_csr
+
+    n = 4096
+    rp, ci, v = uniform_csr(n, n, 16, rng_for("tiny"))
+    xi, xv = sparse_x(n, 0.01, rng_for("tiny", 1))
+    dev = torch.device("cuda:0")
+    A = dbs.dbs_build(n, n, torch.from_numpy(rp).to(dev), torch.from_numpy(ci).to(dev), torch.from_numpy(v).to(dev),
+                      dbs.DBS_F32)
+    st = dbs.dbs_get_stats(A)
+    fmt = Format(dbs, A, 0)
+    act = np.unique(xi // 16)
+    push = 100 * act.shape[0] < fmt.nb
+    mb, cb = fmt.call_bytes(act, xi.shape[0], 4 * n, push, vsize=4)
+    useful = int(np.bincount(ci, minlength=n)[xi].sum())
+    xi_d, xv_d = torch.from_numpy(xi).to(dev), torch.from_numpy(xv).to(dev)
+    y = torch.empty(n, dtype=torch.float32, device=dev)
+    for _ in range(args.warmup):
+        dbs.dbs_spmspv(A, xi_d, xv_d, dbs.DBS_PLUS_TIMES, y)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(args.steps):
+        dbs.dbs_spmspv(A, xi_d, xv_d, dbs.DBS_PLUS_TIMES, y)
+    ev1.record()
+    torch.cuda.synchronize()
+    call_ms = ev0.elapsed_time(ev1) / args.steps
+    dbs.dbs_set_option(A, dbs.DBS_OPT_TIMING, 1)
+    for _ in range(args.steps):
+        dbs.dbs_spmspv(A, xi_d, xv_d, dbs.DBS_PLUS_TIMES, y)
+    s2 = dbs.dbs_get_stats(A)
+    dbs.dbs_set_option(A, dbs.DBS_OPT_TIMING, 0)
+    kms = s2["sum_compute_ms"] / s2["timed_calls"]
+    out = {"workload": "tiny: 4096x4096, 16 uniform nnz/row, fp32; x 1% (41 entries); plus-times",
+           "nnz": int(rp[-1]), "nnz_active_columns": useful, "tiles": st["tiles"],
+           "tiles_by_format": st["tiles_by_format"], "build_peak_bytes": st["build_peak_bytes"],
+           "path": "push" if s2["last_path"] == 0 else "pull", "xb_ratio": round(s2["last_n_nzblk"] / fmt.nb, 4),
+           "call_us": round(call_ms * 1e3, 2), "compute_kernel_us": round(kms * 1e3, 2),
+           "meta_kernel_us": round(s2["sum_meta_ms"] / s2["timed_calls"] * 1e3, 2),
+           "bytes": int(mb + cb), "compute_kernel_GBps": round(cb / (kms * 1e-3) / 1e9, 1),
+           "compute_kernel_frac_of_hbm": round(cb / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "kernel": gflops(int(rp[-1]), useful, kms * 1e-3), "call": gflops(int(rp[-1]), useful, call_ms * 1e-3)}
+    log(f"[bench] tiny: {out}")
+    dbs.dbs_free(A)
+    return out
+
+
 def bench_rmat20(dbs, torch, args):
     from synth import rmat_csr, rng_for, sparse_x
 
@@ -270,30 +332,59 @@ def bench_rmat20(dbs, torch, args):
         "kernel_avg_us": kernel_ms * 1e3, "achieved": achieved, "comp_bytes_per_launch": comp_bytes / len(xs),
         "per_density": per, "forced_paths": forced, "xb_crossover": crossover(forced), "build_s": build_s,
         "format": {"tiles": st["tiles"], "segments": st["segments"], "format_MB": round(st["format_bytes"] / 1e6, 1),
-                   "size": format_size(st, n, n, 0),
+                   "size": format_size(st, n, n, 0), "build_peak_bytes": st["build_peak_bytes"],
                    "tiles_by_format": st["tiles_by_format"]},
         "graph": (rp, ci, n), "xs": xs,
     }
     return res
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline_rmat20(res, seconds):
+    """The oracle on the host: its Boolean pull over the same sweep, first on
+    one thread (the oracle as it stands), then the same loop over every host
+    core (OpenMP), each for about `seconds` (at most 50 steps)."""
     import oracle as orc
+    import oracle.oracle as orc_mod
 
     rp, ci, n = res["graph"]
-    t0 = time.time()
-    steps = 0
-    while True:
-        for x in res["xs"]:
-            orc.or_and_pull(n, n, rp, ci, x["xi"])
-        steps += 1
-        el = time.time() - t0
-        if el >= seconds or steps >= 50:
-            break
-    per_step = el / steps
-    return {"value": round(res["step_bytes"] / per_step / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "ms_per_step": round(per_step * 1e3, 1),
-            "sample": f"{steps} full sweep steps (5 OR-AND calls each, CSR pull) on one host thread"}
+
+    def timed(fn):
+        t0 = time.time()
+        steps = 0
+        while True:
+            for x in res["xs"]:
+                fn(x["xi"])
+            steps += 1
+            el = time.time() - t0
+            if el >= seconds or steps >= 50:
+                return el / steps, steps
+
+    one, steps1 = timed(lambda xi: orc.or_and_pull(n, n, rp, ci, xi))
+    threads = [1]
+
+    def omp(xi):
+        _, t = orc_mod.or_and_pull_all_cores(n, n, rp, ci, xi)
+        threads[0] = t
+
+    allc, steps_all = timed(omp)
+    return {"value": round(res["step_bytes"] / one / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "ms_per_step": round(one * 1e3, 1),
+            "sample": f"{steps1} full sweep steps (5 OR-AND calls each, CSR pull) on one host thread",
+            "all_cores": {"value": round(res["step_bytes"] / allc / 1e9, 3), "unit": "GB/s", "cores": threads[0],
+                          "ms_per_step": round(allc * 1e3, 1),
+                          "sample": f"{steps_all} sweep steps, the same loop with its rows over OpenMP threads"},
+            "nproc": os.cpu_count(), "cpu_model": cpu_model()}
 
 
 def bench_bfs22(dbs, torch, args):
@@ -322,6 +413,8 @@ def bench_bfs22(dbs, torch, args):
     cpu_bfs_s = time.time() - t0
     dbs.dbs_bfs(A, int(srcs[0]), lv)
     ok = bool(np.array_equal(lv.cpu().numpy(), ref))
+    reached = dbs.dbs_get_stats(A)["bfs_reached"]
+    ok = ok and reached == int(np.count_nonzero(ref >= 0))
     times, ktimes, levels, pushl = [], [], [], []
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     for s in srcs:  # BFS time without the library's timing events
@@ -356,6 +449,25 @@ def bench_bfs22(dbs, torch, args):
     dbs.dbs_set_option(A, dbs.DBS_OPT_PATH, 0)
     times = np.array(times)
     gteps = edges / (times * 1e-3) / 1e9
+    # bytes of the first source's BFS in the SpMSpV byte model: every level
+    # a masked OR-AND SpMSpV of its frontier (push or pull by the th3 rule),
+    # writing the next frontier's bitmap (n/8 B) and 4 B per found vertex,
+    # plus the frontier metadata (bitmap scan and block list).  The pull
+    # levels' early exit (row blocks with nothing left to find are skipped)
+    # reads less than this, so the model bounds the work of each level from
+    # above.
+    fmt = Format(dbs, A, 2)
+    model_bytes = 0
+    for L in range(int(ref.max()) + 1):
+        fr = np.nonzero(ref == L)[0]
+        act = np.unique(fr // 16)
+        nxt = int(np.count_nonzero(ref == L + 1))
+        push = 100 * act.shape[0] < fmt.nb
+        _, cb = fmt.call_bytes(act, fr.shape[0], n // 8 + 4 * nxt, push)
+        model_bytes += cb + n // 8 + 8 * act.shape[0]
+    del fmt
+    gc.collect()
+    st = dbs.dbs_get_stats(A)
     return {"workload": "R-MAT scale 22, edge factor 16, symmetrized; " + f"{len(srcs)} sources in the largest component",
             "vertices_in_component": int(lcc.shape[0]), "undirected_edges_in_component": edges,
             "gteps_harmonic_mean": round(float(len(gteps) / np.sum(1.0 / gteps)), 2),
@@ -364,6 +476,12 @@ def bench_bfs22(dbs, torch, args):
             "level_kernels_ms_median": round(float(np.median(ktimes)), 3),
             "levels_median": int(np.median(levels)), "push_levels_median": int(np.median(pushl)),
             "first_source_matches_oracle": ok, "oracle_bfs_s_first_source": round(cpu_bfs_s, 2),
+            "first_source_model_bytes": int(model_bytes),
+            "first_source_GBps": round(model_bytes / (times[0] * 1e-3) / 1e9, 1),
+            "first_source_frac_of_hbm": round(model_bytes / (times[0] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "first_source_level_kernels_frac_of_hbm": round(model_bytes / (ktimes[0] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "first_source_reached": int(reached),
+            "build_peak_bytes": st["build_peak_bytes"],
             "oracle_gteps_first_source": round(edges / cpu_bfs_s / 1e9, 4), "build_s": round(build_s, 2),
             "path_ablation_first_8_sources": ablation}
 
@@ -380,6 +498,7 @@ def bench_decode(dbs, torch, args):
             rp_d, ci_d = torch.from_numpy(rp).to(dev), torch.from_numpy(ci).to(dev)
             v_d = torch.from_numpy(bits.view(np.int16)).to(dev)
             copies = [dbs.dbs_build(rows, cols, rp_d, ci_d, v_d, dbs.DBS_BF16) for _ in range(args.decode_copies)]
+            colcount = np.bincount(ci, minlength=cols)
             fmt = Format(dbs, copies[0], 1)
             st = dbs.dbs_get_stats(copies[0])
             y = torch.empty(rows, dtype=torch.float32, device=dev)
@@ -416,7 +535,12 @@ def bench_decode(dbs, torch, args):
                 ev1.record()
                 torch.cuda.synchronize()
                 cold_us = ev0.elapsed_time(ev1) / reps * 1e3
+                useful = int(colcount[np.nonzero(x)[0]].sum())
                 out.append({"shape": [rows, cols], "weight_sparsity": sp, "activation_zeros": z,
+                            "nnz": int(rp[-1]), "nnz_active_columns": useful,
+                            "kernel_warm": gflops(int(rp[-1]), useful, kus * 1e-6),
+                            "call_warm": gflops(int(rp[-1]), useful, warm_us * 1e-6),
+                            "build_peak_bytes": st["build_peak_bytes"],
                             "path": "push" if s2["last_path"] == 0 else "pull",
                             "xb_ratio": round(s2["last_n_nzblk"] / fmt.nb, 4),
                             "us_warm": round(warm_us, 2), "compute_kernel_us_warm": round(kus, 2),
@@ -477,10 +601,13 @@ FORMATS = {"adaptive": -1, "COO-only": 0, "CSR-only": 4}
 
 
 def bench_format_ablation(dbs, torch, args):
-    """Tile-format ablation: every tile stored as COO, as patched CSR, or by the
-    adaptive rule, on the R-MAT 20 sweep (kernel µs per density) and on the
-    11008x4096 decode layer at 50% weight sparsity (kernel µs per activation)."""
+    """Tile-format ablation (the DB-SpMSpV paper's Figure 10): every tile stored
+    as COO, as patched CSR, or by the adaptive rule, on the R-MAT 20 sweep
+    (kernel µs per density) and on the 11008x4096 decode layer at 50% weight
+    sparsity (kernel µs per activation); at most 5 timed calls per point."""
     from synth import decode_activation, decode_weight_csr, rmat_csr, rng_for, sparse_x
+
+    steps = min(args.steps, 5)
 
     dev = torch.device("cuda:0")
     out = {"rmat20_or_and": {}, "decode_11008x4096_s0.5": {}}
@@ -500,7 +627,7 @@ def bench_format_ablation(dbs, torch, args):
             for _ in range(2):
                 dbs.dbs_spmspv(A, x, None, dbs.DBS_OR_AND, y)
             dbs.dbs_set_option(A, dbs.DBS_OPT_TIMING, 1)
-            for _ in range(args.steps):
+            for _ in range(steps):
                 dbs.dbs_spmspv(A, x, None, dbs.DBS_OR_AND, y)
             s2 = dbs.dbs_get_stats(A)
             dbs.dbs_set_option(A, dbs.DBS_OPT_TIMING, 0)
@@ -525,7 +652,7 @@ def bench_format_ablation(dbs, torch, args):
             for _ in range(2):
                 dbs.dbs_spmspv_dense(A, xd, dbs.DBS_PLUS_TIMES, y)
             dbs.dbs_set_option(A, dbs.DBS_OPT_TIMING, 1)
-            for _ in range(args.steps):
+            for _ in range(steps):
                 dbs.dbs_spmspv_dense(A, xd, dbs.DBS_PLUS_TIMES, y)
             s2 = dbs.dbs_get_stats(A)
             dbs.dbs_set_option(A, dbs.DBS_OPT_TIMING, 0)
@@ -556,6 +683,7 @@ def bench_zipf(dbs, torch, args):
                       torch.from_numpy(v).to(dev), dbs.DBS_F32)
     torch.cuda.synchronize()
     build_s = time.time() - t0
+    colcount = np.bincount(ci, minlength=n)
     del rp, ci, v
     st = dbs.dbs_get_stats(A)
     fmt = Format(dbs, A, 0)
@@ -583,8 +711,11 @@ def bench_zipf(dbs, torch, args):
         s2 = dbs.dbs_get_stats(A)
         dbs.dbs_set_option(A, dbs.DBS_OPT_TIMING, 0)
         kms = s2["sum_compute_ms"] / s2["timed_calls"]
+        useful = int(colcount[xi].sum())
         per.append({
             "density": d, "nnz_x": int(xi.shape[0]), "xb_ratio": round(s2["last_n_nzblk"] / fmt.nb, 5),
+            "nnz_active_columns": useful, "kernel": gflops(int(lens.sum()), useful, kms * 1e-3),
+            "call": gflops(int(lens.sum()), useful, call_ms * 1e-3),
             "path": "push" if s2["last_path"] == 0 else "pull", "call_us": round(call_ms * 1e3, 2),
             "compute_kernel_us": round(kms * 1e3, 2),
             "meta_kernel_us": round(s2["sum_meta_ms"] / s2["timed_calls"] * 1e3, 2),
@@ -599,7 +730,8 @@ def bench_zipf(dbs, torch, args):
             "nnz": int(lens.sum()), "max_row": int(lens.max()),
             "row_length_log2_histogram": hist.tolist(), "generate_s": round(gen_s, 1), "build_s": round(build_s, 2),
             "tiles": st["tiles"], "tiles_by_format": st["tiles_by_format"], "segments": st["segments"],
-            "format_MB": round(st["format_bytes"] / 1e6, 1), "per_density": per}
+            "format_MB": round(st["format_bytes"] / 1e6, 1), "build_peak_bytes": st["build_peak_bytes"],
+            "per_density": per}
 
 
 def main():
@@ -611,8 +743,9 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-zipf", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--ablations", action="store_true",
-                    help="also the tile-format ablation (COO-only / CSR-only / adaptive builds; slow)")
+    ap.add_argument("--no-ablations", action="store_true",
+                    help="skip the tile-format ablation (COO-only / CSR-only / adaptive builds)")
+    ap.add_argument("--no-tiny", action="store_true")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the decode layers (for profiling the decode kernel); prints their JSON")
     ap.add_argument("--bfs-only", action="store_true",
@@ -663,7 +796,7 @@ def main():
              "rmat20_format": res["format"], "rmat20_build_s": round(res["build_s"], 2)}
     cpu = None
     if args.headline_only:
-        args.no_cpu = args.no_bfs = args.no_decode = args.no_zipf = True
+        args.no_cpu = args.no_bfs = args.no_decode = args.no_zipf = args.no_ablations = args.no_tiny = True
     if not args.no_cpu:
         cpu = cpu_baseline_rmat20(res, args.cpu_seconds)
         log(f"[bench] cpu baseline: {cpu}")
@@ -673,9 +806,11 @@ def main():
         log(f"[bench] bfs: {extra['bfs_rmat22']}")
     if not args.no_decode:
         extra["decode"] = bench_decode(dbs, torch, args)
+    if not args.no_tiny:
+        extra["tiny"] = bench_tiny(dbs, torch, args)
     if not args.no_zipf:
         extra["zipf_band"] = bench_zipf(dbs, torch, args)
-    if args.ablations:
+    if not args.no_ablations:
         extra["format_ablation"] = bench_format_ablation(dbs, torch, args)
     traffic = load_traffic("rmat20_sweep")
     line = {

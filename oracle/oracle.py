@@ -15,6 +15,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+_SRC_OMP = os.path.join(_HERE, "oracle_omp.c")
+_LIB_OMP = os.path.join(_HERE, "liboracle_omp.so")
 
 F32, BF16, PATTERN = 0, 1, 2
 COO, DENSE, FORCE_CSR, FORCE_CSC, CSR = 0, 1, 2, 3, 4
@@ -25,15 +27,38 @@ TH0, TH1, TH2, TH3 = 32, 128, 2.0, 0.01
 W_DENSE, W_CSR, W_COO, SEG_CAP = 4, 2, 1, 16
 
 _lib = None
+_lib_omp = None
 
 
 def build_oracle(force: bool = True) -> str:
-    """Compile oracle.c with gcc (plain -O2, no OpenMP)."""
+    """Compile oracle.c with gcc (plain -O2, no OpenMP), and oracle_omp.c (the
+    all-core copy of the Boolean pull loop used only as a CPU baseline)."""
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp"
         subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB)
+    if force or not os.path.exists(_LIB_OMP):
+        tmp = _LIB_OMP + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared", "-o", tmp, _SRC_OMP])
+        os.replace(tmp, _LIB_OMP)
     return _LIB
+
+
+def or_and_pull_all_cores(m, n, row_ptr, col_idx, x_idx):
+    """orc_or_and_pull on every host core (OpenMP over rows); returns (y, threads)."""
+    global _lib_omp
+    if _lib_omp is None:
+        if not os.path.exists(_LIB_OMP):
+            build_oracle(force=True)
+        _lib_omp = C.CDLL(_LIB_OMP)
+        _lib_omp.orc_or_and_pull_omp.argtypes = [C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_int32,
+                                                 C.c_void_p, C.c_void_p]
+        _lib_omp.orc_or_and_pull_omp.restype = C.c_int
+        _lib_omp.orc_omp_threads.restype = C.c_int
+    rp, ci, xi = _i32(row_ptr), _i32(col_idx), _i32(x_idx)
+    y = np.empty(m, np.uint8)
+    _check(_lib_omp.orc_or_and_pull_omp(m, n, _p(rp), _p(ci), xi.shape[0], _p(xi), _p(y)), "or_and_pull_omp")
+    return y, int(_lib_omp.orc_omp_threads())
 
 
 def _load():

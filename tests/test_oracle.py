@@ -373,3 +373,18 @@ def test_segments_cover_every_tile_once():
         assert rb_ptr[rb] <= a < b <= rb_ptr[rb + 1]
         cover[a:b] += 1
     assert np.all(cover == 1)
+
+
+def test_all_core_or_and_pull_equals_the_oracle():
+    """The all-core CPU baseline (the oracle's Boolean pull loop with its rows
+    split over OpenMP threads) gives the oracle's y exactly."""
+    import oracle.oracle as o
+    from synth import rmat_csr, sparse_x
+
+    rp, ci = rmat_csr(13, 16, rng_for("test", 990))
+    n = 1 << 13
+    for k, d in enumerate((0.0, 0.001, 0.05, 1.0)):
+        xi, _ = sparse_x(n, d, rng_for("test", 991, k), with_values=False)
+        y, threads = o.or_and_pull_all_cores(n, n, rp, ci, xi)
+        assert threads >= 1
+        np.testing.assert_array_equal(y, orc.or_and_pull(n, n, rp, ci, xi))
