@@ -282,15 +282,20 @@ dbs_status dbs_get_stats(dbs_handle A, dbs_stats *out);
 enum {
   DBS_ARR_RB_PTR = 0,      /* uint32[mb+1]   global_block_csr_row_ptr */
   DBS_ARR_T_CB = 1,        /* uint32[T]      global_block_csr_col_idx */
-  DBS_ARR_T_META = 2,      /* uint64[T]      payload offset | (nnz-1)<<40 | format<<48 */
+  DBS_ARR_T_META = 2,      /* uint64[T]      payload offset | (nnz-1)<<40 | format<<48
+                                             | inline<<51 | pattern: row block in its
+                                             Boolean-pull segment<<52 */
   DBS_ARR_CB_PTR = 3,      /* uint32[nb+1]   global_block_csc_col_ptr */
   DBS_ARR_CSC_RB = 4,      /* uint32[T]      global_block_csc_row_idx */
   DBS_ARR_CSC2CSR = 5,     /* uint32[T]      global_block_csc2csr */
   DBS_ARR_PAYLOAD = 6,     /* uint8[]        tile payload arena */
-  DBS_ARR_SEGMENTS = 7,    /* uint32[4*S]    {row block | split<<31, t0, t1, 0} */
+  DBS_ARR_SEGMENTS = 7,    /* uint32[4*S]    {row block | split<<31 | drain<<30 | slot
+                                             class<<28, t0, t1, partial slot + 1 or 0} */
   DBS_ARR_XMASK = 8,       /* uint16[nb]     blk_x_mask of the last call */
   DBS_ARR_ACTIVE = 9,      /* uint32[N_nzblk] nonzero vector blocks of the last call (any order) */
-  DBS_ARR_CSC_CM = 10      /* uint16[T]      columns of each tile that hold entries, CSC order */
+  DBS_ARR_CSC_CM = 10,     /* uint16[T]      columns of each tile that hold entries, CSC order */
+  DBS_ARR_PAT_SEGS = 11    /* uint32[4*S']   pattern matrices: Boolean-pull segments {first row
+                                             block, t0, t1, row blocks}, in launch order */
 };
 dbs_status dbs_copy_array(dbs_handle A, int32_t which, void *dst, int64_t capacity,
                           int64_t *bytes_out);

@@ -66,7 +66,8 @@ hipError_t fold_all(dbs_matrix *A) {
 
 void free_all(dbs_matrix *A) {
   void *bufs[] = {A->rb_ptr, A->t_cb,     A->t_meta,   A->cb_ptr,     A->csc_rb,  A->csc2csr, A->csc_cm,
-                  A->payload, A->segs,    A->psegs,    A->wown,    A->rows_nz,  A->xmask,    A->xd,         A->act_list, A->chunks,
+                  A->payload, A->segs,    A->psegs,    A->wown,    A->rows_nz,  A->xmask,    A->xbits,      A->xd,
+                  A->act_list, A->chunks,
                   A->ctr,    A->bfs_bm,   A->bfs_vis,  A->bfs_list,   A->bfs_chunks, A->bfs_ctr,
                   A->fin,    A->partial};
   for (void *b : bufs)
@@ -102,6 +103,11 @@ dbs_status alloc_call_scratch(dbs_matrix *A) {
   const int vs = A->vk == VK_F32 ? 4 : 2;  // a dense f32 x on a pattern matrix needs no staging
   API_TRY(dbs_dev_alloc(A, (void **)&A->xmask, (size_t)A->nb * 4));
   API_TRY(hipMemset(A->xmask, 0, (size_t)A->nb * 4));
+  A->nbw = (A->nb + 31) / 32;
+  if (A->vk == VK_PAT) {
+    API_TRY(dbs_dev_alloc(A, (void **)&A->xbits, (size_t)A->nbw * 8 + 4));
+    API_TRY(hipMemset(A->xbits, 0, (size_t)A->nbw * 8 + 4));
+  }
   API_TRY(dbs_dev_alloc(A, &A->xd, (size_t)A->nb * 16 * vs));
   API_TRY(dbs_dev_alloc(A, (void **)&A->act_list, (size_t)A->nb * 4));
   A->max_chunks = A->T / 64 + A->nb + 1;
@@ -351,6 +357,7 @@ dbs_status dbs_copy_array(dbs_handle A, int32_t which, void *dst, int64_t capaci
     case DBS_ARR_CSC_CM: src = A->csc_cm; bytes = A->T * 2; break;
     case DBS_ARR_PAYLOAD: src = A->payload; bytes = A->payload_bytes; break;
     case DBS_ARR_SEGMENTS: src = A->segs; bytes = A->nseg * 16; break;
+    case DBS_ARR_PAT_SEGS: src = A->psegs; bytes = A->psegs ? A->npseg * 16 : 0; break;
     case DBS_ARR_XMASK: src = A->xmask; bytes = (int64_t)A->nb * 2; break;
     case DBS_ARR_ACTIVE: {
       dbs_stats tmp;

@@ -263,7 +263,6 @@ __global__ __launch_bounds__(KT, VK == VK_PAT ? 5 : 1) void k_bfs_level(BfsParam
       const uint32_t *sg = P.phase == 0 ? P.psegs : P.psegs + 4 * P.nseg0;
       const PatSrc S{P.t_cb, P.t_meta, sg, P.phase == 0 ? P.nseg0 : P.npseg - P.nseg0,
                      make_rsrc(P.payload, (uint64_t)P.payload_bytes + DBS_PAYLOAD_SLACK),
-                     make_rsrc(P.rb_ptr, (uint64_t)(P.m + 15) / 16 * 4 + 4),
                      make_rsrc(P.wown, (uint64_t)(P.payload_bytes + DBS_PAYLOAD_SLACK) / 4)};
       const BfsPol pol{&P, R.bm, make_rsrc(P.vis, (uint64_t)((P.nb + 1) / 2) * 4)};
       pattern_pull(S, pol, gw, nw, eager, lane, s_pat[w]);

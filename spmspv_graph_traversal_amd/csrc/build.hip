@@ -564,13 +564,23 @@ __global__ void k_seg_cost(const uint32_t *psegs, int64_t npseg, const uint64_t 
 // Owner of every coordinate word of a pattern COO tile held in the payload:
 // the tile's index in its Boolean-pull segment (< 256).  The pull spreads a
 // segment's words over the lanes; with the owner stored, a lane finds the
-// mask of its word's tile with one LDS read.  One thread per segment.
-__global__ void k_word_owner(const uint32_t *psegs, int64_t npseg, const uint64_t *t_meta, uint8_t *wown) {
+// mask of its word's tile with one LDS read.  Also the tile's row block
+// within its segment (0 .. PAT_MAX_RB-1), in bits 52..55 of its metadata
+// word: a segment that packs several row blocks sends each found row to its
+// row block by it.  One thread per segment.
+__global__ void k_word_owner(const uint32_t *psegs, int64_t npseg, const uint32_t *rb_ptr, uint64_t *t_meta,
+                             uint8_t *wown) {
   const int64_t sg = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (sg >= npseg) return;
-  const uint32_t t0 = psegs[4 * sg + 1], t1 = psegs[4 * sg + 2];
+  const uint32_t rb = psegs[4 * sg], t0 = psegs[4 * sg + 1], t1 = psegs[4 * sg + 2], nrb = psegs[4 * sg + 3];
+  uint32_t ri = 0, next = nrb > 1u ? rb_ptr[rb + 1] : t1;  // first tile of row block rb + ri + 1
   for (uint32_t t = t0; t < t1; ++t) {
-    const uint64_t meta = t_meta[t];
+    while (t >= next && ri + 1u < nrb) {
+      ++ri;
+      next = ri + 1u < nrb ? rb_ptr[rb + ri + 1u] : t1;
+    }
+    const uint64_t meta = (t_meta[t] & ~META_SEG_RB) | ((uint64_t)ri << META_SEG_RB_SHIFT);
+    t_meta[t] = meta;
     if (meta_type(meta) != DBS_TILE_COO || meta_inline(meta)) continue;
     const uint64_t w0 = meta_vp(meta) / 4, nw = (meta_nnz(meta) + 3u) / 4u;
     for (uint64_t w = 0; w < nw; ++w) wown[w0 + w] = (uint8_t)(t - t0);
@@ -929,7 +939,7 @@ dbs_status dbs_build_impl(dbs_matrix *A, const int32_t *row_ptr, const int32_t *
     BUILD_TRY(hipMemsetAsync(A->wown, 0, ow, s));
     if (A->npseg > 0) {
       hipLaunchKernelGGL(k_word_owner, dim3(nblocks(A->npseg, BT)), dim3(BT), 0, s, (const uint32_t *)A->psegs,
-                         A->npseg, (const uint64_t *)A->t_meta, A->wown);
+                         A->npseg, (const uint32_t *)A->rb_ptr, (uint64_t *)A->t_meta, A->wown);
       BUILD_TRY(hipGetLastError());
       BUILD_TRY(order_by_cost(A, tmp, s));
     }

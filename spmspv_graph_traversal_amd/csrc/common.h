@@ -59,12 +59,16 @@ __host__ __device__ inline uint32_t align_up(uint32_t x, uint32_t a) { return (x
 __host__ __device__ inline uint32_t coo_val_off(uint32_t nnz) { return align_up(nnz, 4); }
 __host__ __device__ inline uint32_t csr_val_off(uint32_t nnz) { return PL_CSR_RC + align_up(nnz, 16); }
 
-// Tile metadata word: payload offset (40 bits) | (nnz-1) << 40 | format << 48.
+// Tile metadata word: payload offset (40 bits) | (nnz-1) << 40 | format << 48
+// (| row block in its Boolean-pull segment << 52, pattern matrices).
 // COO tiles of a pattern matrix with at most COO_INLINE entries keep their
 // coordinate bytes in bits 0..31 instead of an offset (bit 51 set) and have
 // no payload: the metadata load brings the whole tile.
 #define COO_INLINE 4
 #define META_INLINE (1ull << 51)
+// pattern matrices: the tile's row block within its Boolean-pull segment
+#define META_SEG_RB_SHIFT 52
+#define META_SEG_RB (15ull << META_SEG_RB_SHIFT)
 __host__ __device__ inline uint64_t meta_pack(uint64_t vp, uint32_t nnz, uint32_t type) {
   return vp | ((uint64_t)(nnz - 1) << 40) | ((uint64_t)type << 48);
 }
@@ -134,6 +138,7 @@ __host__ __device__ inline uint32_t seg_slot_class(int share) { return share >= 
 #define DBS_PAT_SEG_CAP 256
 // row blocks per Boolean-pull segment at most (runs of short row blocks)
 #define DBS_PAT_MAX_RB 16
+static_assert(DBS_PAT_MAX_RB <= 16, "a tile's row block within its segment takes four metadata bits");
 
 // ---------------------------------------------------------------------------
 // The handle.
@@ -174,6 +179,8 @@ struct dbs_matrix {
 
   // per-call scratch (device)
   uint32_t *xmask;       // [nb] (epoch << 16) | blk_x_mask
+  uint32_t *xbits;       // pattern matrices: [2][nbw] a bit per nonzero vector block, by epoch parity
+  int32_t nbw;           // (nb + 31) / 32
   void *xd;              // [n] staged x values (only active positions are meaningful)
   uint32_t *act_list;    // [nb] compacted nonzero vector blocks
   uint64_t *chunks;      // [max_chunks] push work: column block | chunk index << 32

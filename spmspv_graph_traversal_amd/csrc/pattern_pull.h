@@ -20,7 +20,6 @@ struct PatSrc {
   const uint32_t *segs;  // padded with 16 zeroed descriptors
   int64_t nseg;
   brsrc_t pay;  // payload and its zeroed slack
-  brsrc_t rbp;  // block-CSR row pointer (the row blocks of a segment that holds several)
   brsrc_t own;  // per payload word of a COO tile: the tile's index in its segment
 };
 
@@ -73,7 +72,7 @@ DBS_DEV void pat_issue(const PatSrc &S, const Pol &pol, int64_t s0, bool live, u
 template <int K>
 struct PatSeg {  // stage A: descriptor, column blocks, metadata (n == 0: no segment)
   uint32_t rb, t0, n, nrb;  // first row block, first tile, tiles, row blocks (uniform)
-  uint32_t needl, bnd;      // lane j < nrb: rows wanted in row block rb + j, and its first tile
+  uint32_t needl;           // lane j < nrb: rows wanted in row block rb + j
   uint32_t cb[K];
   uint64_t meta[K];
 };
@@ -162,7 +161,6 @@ DBS_DEV void patk_issue(const PatSrc &S, const Pol &pol, int64_t stride, int lan
   }
   const bool mine = any & ((uint32_t)lane < nrb);
   r.needl = pol.need_v(rb + (uint32_t)lane, mine);
-  r.bnd = bld32(S.rbp, (mine & (lane > 0)) ? (rb + (uint32_t)lane) * 4u : OOB_OFF);
 }
 
 // lane l's value of slice k (both wave-uniform), read from every slice so
@@ -216,22 +214,20 @@ DBS_DEV void pat_words(const PatSrc &S, const PatSeg<K> &a, PatMasks<K> &b, int 
 // everything of one segment once its loads have arrived.  MULTI: the
 // segment holds several row blocks; each found row goes to its row block
 // through an LDS OR (s_f, one word per row block), the row block of a tile
-// being the number of row-block starts up to it.
-template <int K, bool MULTI, class Pol>
+// within the segment being recorded in its metadata word at build (a tile
+// whose metadata was not read is inactive and finds nothing).  SKIP: slices
+// without an active tile skip the inline-COO decode (worth its test when few
+// vector blocks are active).
+template <int K, bool MULTI, bool SKIP, class Pol>
 DBS_DEV void pat_finish(const PatSrc &S, const Pol &pol, const PatSeg<K> &a, const PatMasks<K> &b, int lane,
                         uint32_t *s_tm, uint32_t *s_f, FoundBuf &fb) {
   const uint32_t n = a.n;  // uniform
   uint32_t f = 0u;
   uint32_t ri[K];  // MULTI: row block (0 .. nrb-1) of this lane's tile in each slice
 #pragma unroll
-  for (int k = 0; k < K; ++k) ri[k] = 0u;
+  for (int k = 0; k < K; ++k) ri[k] = MULTI ? (uint32_t)(a.meta[k] >> META_SEG_RB_SHIFT) & 15u : 0u;
   if constexpr (MULTI) {
     if (lane < PAT_MAX_RB) s_f[lane] = 0u;
-    for (uint32_t j = 1; j < a.nrb; ++j) {  // uniform
-      const uint32_t st = (uint32_t)__builtin_amdgcn_readlane((int)a.bnd, (int)j) - a.t0;
-#pragma unroll
-      for (int k = 0; k < K; ++k) ri[k] += (64u * k + (uint32_t)lane >= st) ? 1u : 0u;
-    }
     __syncwarp();
   }
   auto add = [&](int k, uint32_t x) {
@@ -244,6 +240,7 @@ DBS_DEV void pat_finish(const PatSrc &S, const Pol &pol, const PatSeg<K> &a, con
 #pragma unroll
   for (int k = 0; k < K; ++k) {
     if (64u * k >= n) break;  // uniform
+    if (SKIP && __ballot(b.m[k] != 0u) == 0ull) continue;  // uniform
     const uint64_t meta = a.meta[k];
     // COO tiles with at most four entries: the coordinates are in the metadata
     // word (a zero mask decodes to nothing)
@@ -330,12 +327,24 @@ DBS_DEV void pat_flush(const Pol &pol, FoundBuf &fb, int lane, bool all) {
   }
 }
 
+template <int K, bool SKIP, class Pol>
+DBS_DEV void pat_finish_any(const PatSrc &S, const Pol &pol, const PatSeg<K> &a, const PatMasks<K> &b, int lane,
+                            uint32_t *s_tm, uint32_t *s_f, FoundBuf &fb) {
+  if (a.nrb > 1u) pat_finish<K, true, SKIP>(S, pol, a, b, lane, s_tm, s_f, fb);  // uniform
+  else pat_finish<K, false, SKIP>(S, pol, a, b, lane, s_tm, s_f, fb);
+  pat_flush(pol, fb, lane, false);
+}
+
 // One wave's share: segments s0, s0 + stride, ... that have work.  Three
 // steps are in flight: while segment i is finished, segment i+1 has its
 // masks (and, EAGER, its coordinate words) and segment i+2 its column blocks
 // and metadata in flight.  Loads are issued in that order, so a wait for
 // segment i's data never waits for the loads of the later segments (a new
-// window of descriptors, once per 64 segments, does wait).
+// window of descriptors, once per 64 segments, does wait).  Without EAGER,
+// segment i's metadata (of its active tiles) and then its coordinate words
+// are read in its own step; a deeper pipeline that reads them one and two
+// steps ahead ran slower (more registers and moves per step, and this pull
+// is bound by the vector-memory instructions it issues, not by waits).
 template <int K, bool EAGER, class Pol>
 DBS_DEV void pattern_pull_wave(const PatSrc &S, const Pol &pol, int64_t s0, int64_t stride, int lane,
                                uint32_t *s_tm, uint32_t *s_f, FoundBuf &fb) {
@@ -364,8 +373,8 @@ DBS_DEV void pattern_pull_wave(const PatSrc &S, const Pol &pol, int64_t s0, int6
     patk_issue<K, EAGER>(S, pol, stride, lane, w, l4, l8, a2);
     masks(a1, b1);
     if constexpr (!EAGER) pat_words<K, false>(S, a0, b0, lane, l4);
-    if (a0.nrb > 1u) pat_finish<K, true>(S, pol, a0, b0, lane, s_tm, s_f, fb);  // uniform
-    else pat_finish<K, false>(S, pol, a0, b0, lane, s_tm, s_f, fb);
+    if (a0.nrb > 1u) pat_finish<K, true, !EAGER>(S, pol, a0, b0, lane, s_tm, s_f, fb);  // uniform
+    else pat_finish<K, false, !EAGER>(S, pol, a0, b0, lane, s_tm, s_f, fb);
     pat_flush(pol, fb, lane, false);
     a0 = a1;
     a1 = a2;
@@ -379,12 +388,14 @@ constexpr int PAT_K = DBS_PAT_SEG_CAP / 64;  // slices of 64 tiles per pattern-p
 // the found-row buffer (2 x PAT_FOUND_CAP)
 constexpr int PAT_LDS_WORDS = 64 * PAT_K + PAT_MAX_RB + 2 * PAT_FOUND_CAP;
 
-template <class Pol>
+// LAZY_ONLY: the policy is only used with the metadata of the active tiles
+// (no instantiation for `eager`)
+template <bool LAZY_ONLY = false, class Pol>
 DBS_DEV void pattern_pull(const PatSrc &S, const Pol &pol, int64_t s0, int64_t stride, bool eager, int lane,
                           uint32_t *s_lds) {
   uint32_t *s_tm = s_lds, *s_f = s_lds + 64 * PAT_K;
   FoundBuf fb{s_f + PAT_MAX_RB, s_f + PAT_MAX_RB + PAT_FOUND_CAP, 0};
-  if (eager) pattern_pull_wave<PAT_K, true>(S, pol, s0, stride, lane, s_tm, s_f, fb);
+  if (!LAZY_ONLY && eager) pattern_pull_wave<PAT_K, !LAZY_ONLY>(S, pol, s0, stride, lane, s_tm, s_f, fb);
   else pattern_pull_wave<PAT_K, false>(S, pol, s0, stride, lane, s_tm, s_f, fb);
   pat_flush(pol, fb, lane, true);
 }

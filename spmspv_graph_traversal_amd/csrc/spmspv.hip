@@ -26,6 +26,10 @@ constexpr int KT = 256;  // threads per workgroup (4 waves)
 struct MetaOut {
   uint32_t *xmask;
   uint32_t epoch;
+  // pattern matrices: this call's active-block bits (set here) and the next
+  // call's (cleared here), nbw words each; null otherwise
+  uint32_t *bits_set, *bits_clear;
+  int32_t nbw;
   dbs_meta::Reg reg;    // this call's counters ([0] N_nzblk, [1] push chunks, [2] error flags, [3] done) and lists
   uint32_t *ctr_next;   // next call's counters, cleared here
   int32_t n, nb;
@@ -40,6 +44,76 @@ DBS_DEV void clear_y(const MetaOut &o) {
   uint4 *body = (uint4 *)(o.y + o.y_head);
   for (int64_t k = gt; k < o.y_body; k += gs) body[k] = make_uint4(0, 0, 0, 0);
   if (gt < o.y_tail) o.y[o.y_head + 16 * o.y_body + gt] = 0;
+  // the next call's active-block bits start from zero (this call's array was
+  // cleared by the previous call, both in stream order)
+  if (o.bits_clear)
+    for (int64_t k = gt; k < o.nbw; k += gs) o.bits_clear[k] = 0u;
+}
+
+// The bits of the blocks that lanes with `on` register (a dense x), called
+// by the whole wave.  Bits of one word are first ORed across the lanes that
+// hold it (segmented by runs of equal words), and the first lane of each run
+// sets them with one non-returning atomic.
+DBS_DEV void set_block_bits(const MetaOut &o, bool on, uint32_t b) {
+  if (!o.bits_set) return;  // uniform
+  const int lane = __lane_id();
+  const uint32_t wi = on ? b >> 5 : 0xFFFFFFFFu;
+  uint32_t bits = on ? 1u << (b & 31u) : 0u;
+#pragma unroll
+  for (int d = 1; d < DBS_WAVE; d <<= 1) {
+    const uint32_t ow = (uint32_t)__shfl_down((int)wi, d), ob = (uint32_t)__shfl_down((int)bits, d);
+    if (lane + d < DBS_WAVE && ow == wi) bits |= ob;
+  }
+  const uint32_t pw = (uint32_t)__shfl_up((int)wi, 1);
+  if (on && (lane == 0 || pw != wi)) atomicOr(&o.bits_set[wi], bits);
+}
+
+// The active-block bits of a sparse x, one round (1024 entries) of a
+// workgroup at a time.  The round's leaders set their blocks' bits in an LDS
+// window of words starting at the word of the round's first entry; the
+// window's words are then written out, the words strictly between the
+// round's first and last entries' words with plain stores (a sorted x_idx
+// has no other entries there) and the others with non-returning atomics.
+// Device-scope atomics on one cache line are served one after another, so
+// one atomic per block (up to 1024 per line) cost more than the rest of the
+// metadata kernel at high densities.  Blocks outside the window (an x_idx
+// that is not sorted) take an atomic each.
+constexpr uint32_t BITS_WIN = 1024;
+DBS_DEV void block_bits_sparse(const MetaOut &o, int32_t nnz_x, const int32_t *x_idx) {
+  __shared__ uint32_t s_w[BITS_WIN];
+  __shared__ uint32_t s_lo, s_hi;
+  if (!o.bits_set || nnz_x <= 0) return;  // uniform
+  const int tid = (int)threadIdx.x;
+  const int64_t rounds = ((int64_t)nnz_x + dbs_meta::MT - 1) / dbs_meta::MT;
+  for (int64_t r = blockIdx.x; r < rounds; r += gridDim.x) {  // uniform
+    const int64_t i0 = r * dbs_meta::MT, i1 = i0 + dbs_meta::MT < nnz_x ? i0 + dbs_meta::MT : nnz_x;
+    if (tid == 0) {
+      const int32_t f = x_idx[i0], l = x_idx[i1 - 1];
+      s_lo = (f >= 0 && f < o.n) ? (uint32_t)f >> 9 : 0u;
+      s_hi = (l >= 0 && l < o.n) ? (uint32_t)l >> 9 : 0u;
+    }
+    for (uint32_t k = (uint32_t)tid; k < BITS_WIN; k += dbs_meta::MT) s_w[k] = 0u;
+    __syncthreads();
+    const uint32_t lo = s_lo, hi = s_hi;
+    const int64_t i = i0 + tid;
+    if (i < i1) {
+      const int32_t idx = x_idx[i], prev = i > 0 ? x_idx[i - 1] : -1;
+      if (idx >= 0 && idx < o.n && (i == 0 || (prev >> 4) != (idx >> 4))) {
+        const uint32_t b = (uint32_t)idx >> 4, w = b >> 5, bit = 1u << (b & 31u);
+        if (w - lo < BITS_WIN) atomicOr(&s_w[w - lo], bit);  // LDS
+        else atomicOr(&o.bits_set[w], bit);
+      }
+    }
+    __syncthreads();
+    for (uint32_t k = (uint32_t)tid; k < BITS_WIN; k += dbs_meta::MT) {
+      const uint32_t v = s_w[k], w = lo + k;
+      if (v != 0u && w < (uint32_t)o.nbw) {
+        if (k > 0u && w < hi) o.bits_set[w] = v;
+        else atomicOr(&o.bits_set[w], v);
+      }
+    }
+    __syncthreads();
+  }
 }
 
 // Sparse x: sorted x_idx.  The first entry of each vector block (the leader)
@@ -79,6 +153,7 @@ __global__ __launch_bounds__(dbs_meta::MT) void k_xmeta_sparse(MetaOut o, int32_
       o.xmask[b] = (o.epoch << 16) | mk;
     }
   });
+  block_bits_sparse(o, nnz_x, x_idx);
 }
 
 // Dense x (decode, section 4.1): one ballot per wave gives the nonzero
@@ -103,6 +178,7 @@ __global__ __launch_bounds__(dbs_meta::MT) void k_xmeta_dense(MetaOut o, const v
     b = (uint32_t)(j >> 4);
     leader = head && mk != 0u;
     if (pass == 0 && head) o.xmask[b] = (o.epoch << 16) | mk;
+    if (pass == 0) set_block_bits(o, head && mk != 0u, b);
     // PLUS_TIMES: copy x into the block-padded staging vector (zero tail),
     // so the multiply reads whole column quarters of every vector block
     if (pass == 0 && xd && j < npad) {
@@ -145,6 +221,8 @@ struct SpmvParams {
   int32_t slot_cls;    // segments of row blocks of at least this class write partial slots
   float *partial;      // the partial slots (finalized by k_plus_finalize), < 4 GiB
   uint32_t partial_bytes;
+  const uint32_t *xbits;  // pattern matrices with nbw <= PUSH_LIST_MAX: this call's active-block bits
+  int32_t nbw;
   const uint32_t *xlist;  // this call's nonzero vector blocks (N_nzblk of them)
   int32_t list_push;      // push chunks come from xlist (none were built)
   void *y;
@@ -561,8 +639,7 @@ template <int VK, int U>
 DBS_DEV void plus_pull(const SpmvParams &P, int64_t gw, int64_t nw, bool eager, float *sx, float *spart,
                        uint32_t *s_mark, float *s_acc, int lane) {
   const PatSrc S{P.t_cb, P.t_meta, P.segs, P.nseg,
-                 make_rsrc(P.payload, (uint64_t)P.payload_bytes + DBS_PAYLOAD_SLACK), make_rsrc(P.rb_ptr, 0),
-                 make_rsrc(nullptr, 0)};
+                 make_rsrc(P.payload, (uint64_t)P.payload_bytes + DBS_PAYLOAD_SLACK), make_rsrc(nullptr, 0)};
   const brsrc_t xm = make_rsrc(P.xmask, (uint64_t)P.nb * 4);
   const int parts = U == 1 ? P.plus_parts : 1;
   // the COO slots start (and are left) at zero
@@ -599,14 +676,20 @@ DBS_DEV void pull_or_store(const SpmvParams &P, uint4 seg, uint32_t f, int lane)
 
 // OR-AND SpMSpV on a pattern matrix: every row is wanted, masks are this
 // call's epoch-tagged blk_x_mask words, found rows are set in y (cleared by
-// the metadata kernel, so only ones are written).
+// the metadata kernel, so only ones are written).  FILTER: the call's
+// active-block bits are in LDS, and only the tiles whose column block is
+// active read its mask word from memory.  Those reads (a cache line per lane)
+// are the costliest part of the pull when few blocks are active.
+template <bool FILTER>
 struct OrPol {
   brsrc_t xmask;
   uint32_t epoch;
   int32_t m;
   uint8_t *y;
+  const uint32_t *bits;  // FILTER: LDS, a bit per column block
   DBS_DEV uint32_t need_v(uint32_t, bool) const { return 0xFFFFu; }
   DBS_DEV uint32_t mask(uint32_t cb, bool in) const {
+    if constexpr (FILTER) in = in && ((bits[cb >> 5] >> (cb & 31u)) & 1u);  // idle lanes hold cb 0
     const uint32_t w = bld32(xmask, in ? cb * 4u : OOB_OFF);
     return ((w >> 16) == epoch) ? (w & 0xFFFFu) : 0u;  // an idle lane reads 0: no epoch
   }
@@ -728,10 +811,18 @@ __global__ __launch_bounds__(KT, ((VK == VK_BF16 && SR == DBS_PLUS_TIMES && PU =
       R.pay = make_rsrc(P.payload, (uint64_t)P.payload_bytes + DBS_PAYLOAD_SLACK);
       R.xmask = make_rsrc(P.xmask, (uint64_t)P.nb * 4);
       if constexpr (VK == VK_PAT) {
-        const PatSrc S{P.t_cb, P.t_meta, P.segs, P.nseg, R.pay, make_rsrc(P.rb_ptr, (uint64_t)(P.m + 15) / 16 * 4 + 4),
+        const PatSrc S{P.t_cb, P.t_meta, P.segs, P.nseg, R.pay,
                        make_rsrc(P.wown, (uint64_t)(P.payload_bytes + DBS_PAYLOAD_SLACK) / 4)};
-        const OrPol pol{R.xmask, P.epoch, P.m, (uint8_t *)P.y};
-        pattern_pull(S, pol, gw, nw, eager, lane, s_pat[w]);
+        if (!eager && P.xbits) {  // uniform
+          // the active-block bits in the push enumeration's LDS
+          for (int i = (int)threadIdx.x; i < P.nbw; i += KT) s_cum[i] = P.xbits[i];
+          __syncthreads();
+          const OrPol<true> pol{R.xmask, P.epoch, P.m, (uint8_t *)P.y, s_cum};
+          pattern_pull<true>(S, pol, gw, nw, false, lane, s_pat[w]);
+        } else {
+          const OrPol<false> pol{R.xmask, P.epoch, P.m, (uint8_t *)P.y, nullptr};
+          pattern_pull(S, pol, gw, nw, eager, lane, s_pat[w]);
+        }
       } else {
         for (int64_t s = gw * U; s < P.nseg; s += nw * U) pull_or_group<VK, U>(P, R, s, eager, lane);
       }
@@ -936,6 +1027,9 @@ dbs_status dbs_spmspv_impl(dbs_matrix *A, int32_t nnz_x, const int32_t *x_idx, c
   MetaOut o;
   o.xmask = A->xmask;
   o.epoch = A->epoch;
+  o.nbw = A->nbw;
+  o.bits_set = A->xbits ? A->xbits + (size_t)(A->epoch & 1u) * A->nbw : nullptr;
+  o.bits_clear = A->xbits ? A->xbits + (size_t)((A->epoch + 1u) & 1u) * A->nbw : nullptr;
   o.reg.ctr = A->ctr + 8 * A->cbuf;
   o.reg.list = A->act_list;
   o.reg.chunks = A->chunks;
@@ -1013,6 +1107,9 @@ dbs_status dbs_spmspv_impl(dbs_matrix *A, int32_t nnz_x, const int32_t *x_idx, c
   P.nb = A->nb;
   P.xmask = A->xmask;
   P.epoch = A->epoch;
+  // the Boolean pull stages the active-block bits in LDS when they fit
+  P.xbits = (A->xbits && sr == DBS_OR_AND && A->nbw <= dbs_meta::PUSH_LIST_MAX) ? o.bits_set : nullptr;
+  P.nbw = A->nbw;
   P.xd = A->xd;  // PLUS_TIMES only: the staged x (OR_AND reads the masks alone)
   P.partial = A->partial;
   P.partial_bytes = (uint32_t)(A->nslots * DBS_MAX_SHARE * SLOT_WORDS * 4);

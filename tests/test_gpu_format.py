@@ -32,6 +32,33 @@ def _arrays(dbs, A):
     }
 
 
+def check_pattern_segments(dbs, A, ar, tv, cap):
+    """Boolean-pull segments of a pattern matrix: every tile in exactly one;
+    a segment holds whole row blocks when it holds several (at most 16, at
+    most `cap` tiles) and part of one otherwise; each tile's metadata carries
+    its row block within its segment in bits 52..55."""
+    ps = dbs.dbs_copy_array(A, dbs.DBS_ARR_PAT_SEGS).reshape(-1, 4).astype(np.int64)
+    T = int(tv["T"])
+    if T == 0:
+        assert ps.shape[0] == 0
+        return
+    rbp = tv["rb_ptr"].astype(np.int64)
+    rb0, t0, t1, nrb = ps[:, 0], ps[:, 1], ps[:, 2], ps[:, 3]
+    assert np.all(t1 > t0) and np.all((nrb >= 1) & (nrb <= 16))
+    multi = nrb > 1
+    np.testing.assert_array_equal(t0[multi], rbp[rb0[multi]])
+    np.testing.assert_array_equal(t1[multi], rbp[rb0[multi] + nrb[multi]])
+    assert np.all(t1[multi] - t0[multi] <= cap)
+    lens = t1 - t0
+    seg_of = np.repeat(np.arange(ps.shape[0]), lens)
+    tiles = np.arange(int(lens.sum())) - np.repeat(np.cumsum(lens) - lens, lens) + np.repeat(t0, lens)
+    np.testing.assert_array_equal(np.bincount(tiles, minlength=T), np.ones(T, np.int64))
+    ri = tv["t_rb"].astype(np.int64)[tiles] - rb0[seg_of]
+    assert np.all((ri >= 0) & (ri < nrb[seg_of]))
+    bits = ((ar["t_meta"] >> np.uint64(52)) & np.uint64(15)).astype(np.int64)
+    np.testing.assert_array_equal(bits[tiles], ri)
+
+
 def check_format(dbs, m, n, rp, ci, vbits, dtype, vk, opt=None, th=(32, 128, 2.0), force=-1, cap=None):
     if cap is None:  # the default segment cap by value type
         cap = 256 if dtype == dbs.DBS_PATTERN else 64
@@ -97,6 +124,8 @@ def check_format(dbs, m, n, rp, ci, vbits, dtype, vk, opt=None, th=(32, 128, 2.0
     else:
         assert not ((segs[:, 0] >> 30) & 1).any()
     np.testing.assert_array_equal(segs[:, 3], slot)
+    if vk == 2:
+        check_pattern_segments(dbs, A, ar, tv, cap)
     for f in range(5):
         assert st["tiles_by_format"][f] == int(np.count_nonzero(exp_types == f))
         assert st["nnz_by_format"][f] == int(tv["t_nnz"][exp_types == f].sum())

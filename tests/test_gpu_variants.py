@@ -18,7 +18,7 @@ import pytest
 
 import oracle as orc
 from gpu_helpers import bf16_csr_of, build, csr_of, mixed_tile_dense, options, up
-from synth import f32_to_bf16_bits, rng_for, sparse_x
+from synth import f32_to_bf16_bits, rmat_csr, rng_for, sparse_x, uniform_csr
 
 pytestmark = pytest.mark.gpu
 
@@ -104,6 +104,45 @@ def test_pull_variant_options_are_validated(dbs):
             dbs.dbs_set_option(A, opt, bad)
     dbs.dbs_set_option(A, dbs.DBS_OPT_PULL_WIDTH, 4)
     assert dbs.dbs_get_option(A, dbs.DBS_OPT_PULL_WIDTH) == 4
+
+
+# (rows, columns, entries per row): column-block counts 1, 5, 63, 4099,
+# 65537, 196608 (the most whose active-block bits the Boolean pull stages in
+# LDS) and 196609 (one more: every tile reads its mask word)
+OR_SHAPES = [(40, 9, 3), (77, 80, 6), (300, 1000, 9), (700, 65584, 12), (500, (1 << 20) + 16, 20),
+             (300, 196608 * 16, 12), (300, 196609 * 16, 12)]
+
+
+@pytest.mark.parametrize("shape", OR_SHAPES, ids=lambda s: f"{s[0]}x{s[1]}")
+def test_or_and_shapes(dbs, shape):
+    """OR-AND on pattern matrices of uniform rows: equal to the oracle on
+    every path, at densities that push, pull with the metadata of the active
+    tiles only and pull with every tile's metadata, over consecutive calls."""
+    m, n, per = shape
+    rp, ci, _ = uniform_csr(m, n, per, rng_for("test", 920, m, n))
+    P = build(dbs, m, n, rp, ci, None, dbs.DBS_PATTERN)
+    for k, density in enumerate((0.0005, 0.02, 0.3, 0.9)):
+        xi, _ = sparse_x(n, density, rng_for("test", 921, n, k), with_values=False)
+        if xi.size == 0:
+            xi = np.array([n // 2], np.int32)
+        yo = orc.or_and_pull(m, n, rp, ci, xi)
+        for path in PATHS:
+            dbs.dbs_set_option(P, dbs.DBS_OPT_PATH, path)
+            np.testing.assert_array_equal(run_or(dbs, P, m, xi), yo, err_msg=f"density {density} path {path}")
+
+
+def test_or_and_rmat_sweep(dbs):
+    """R-MAT pattern (packed multi-row-block segments, long row blocks split
+    over segments): every path equals the oracle over a density sweep."""
+    rp, ci = rmat_csr(13, 16, rng_for("test", 922))[:2]
+    n = rp.shape[0] - 1
+    P = build(dbs, n, n, rp, ci, None, dbs.DBS_PATTERN)
+    for k, density in enumerate((0.0001, 0.001, 0.01, 0.1, 0.5)):
+        xi, _ = sparse_x(n, density, rng_for("test", 923, k), with_values=False)
+        yo = orc.or_and_pull(n, n, rp, ci, xi)
+        for path in PATHS:
+            dbs.dbs_set_option(P, dbs.DBS_OPT_PATH, path)
+            np.testing.assert_array_equal(run_or(dbs, P, n, xi), yo, err_msg=f"density {density} path {path}")
 
 
 @pytest.mark.parametrize("force", [0, 1, 2, 3, 4])
