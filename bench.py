@@ -673,7 +673,7 @@ def bench_zipf(dbs, torch, args):
 
     n = 1 << 23
     t0 = time.time()
-    rp, ci, v = zipf_band_csr(n, rng_for("zipf"))
+    rp, ci, v = zipf_band_csr(n, rng_for("zipf"), band_frac=args.zipf_band_frac)
     gen_s = time.time() - t0
     lens = np.diff(rp.astype(np.int64))
     log(f"[bench] zipf generated: nnz={ci.shape[0]} max_row={int(lens.max())} in {gen_s:.1f}s")
@@ -726,7 +726,9 @@ def bench_zipf(dbs, torch, args):
         log(f"[bench] zipf d={d}: {per[-1]}")
     dbs.dbs_set_option(A, dbs.DBS_OPT_TIMING, 0)
     hist = np.bincount(np.floor(np.log2(np.maximum(lens, 1))).astype(np.int64))
-    return {"workload": "zipf(1.8) row lengths capped at 2^20, 90% band + 10% uniform, 8388608^2, fp32",
+    bf = args.zipf_band_frac
+    return {"workload": f"zipf(1.8) row lengths capped at 2^20, {100 * bf:g}% band + {100 * (1 - bf):g}% uniform, "
+                        "8388608^2, fp32",
             "nnz": int(lens.sum()), "max_row": int(lens.max()),
             "row_length_log2_histogram": hist.tolist(), "generate_s": round(gen_s, 1), "build_s": round(build_s, 2),
             "tiles": st["tiles"], "tiles_by_format": st["tiles_by_format"], "segments": st["segments"],
@@ -754,6 +756,9 @@ def main():
                     help="only the Zipf/band stress matrix (for profiling its pull); prints its JSON")
     ap.add_argument("--headline-only", action="store_true",
                     help="only the timed sweep (for profiling: every SpMSpV launch is one of the timed mix)")
+    ap.add_argument("--zipf-band-frac", type=float, default=0.9,
+                    help="share of each Zipf row's columns in its band (the rest uniform over all columns); "
+                         "other values only to attribute the pull's memory traffic to the two parts")
     ap.add_argument("--bfs-sources", type=int, default=64)
     ap.add_argument("--decode-copies", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)

@@ -680,6 +680,50 @@ hipError_t order_by_cost(dbs_matrix *A, Tmp &tmp, hipStream_t s) {
   return e;
 }
 
+// First column block of each segment (for ordering).  One thread per segment.
+__global__ void k_seg_first_cb(const uint32_t *segs, int64_t nseg, const uint32_t *t_cb, uint32_t *key) {
+  const int64_t sg = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (sg >= nseg) return;
+  key[sg] = t_cb[segs[4 * sg + 1]];
+}
+
+// Order of the PLUS_TIMES pull's segments: the segments of the row blocks
+// split into more than 64 segments (class 3) first, sorted by their first
+// column block, then the others in row-block order.  The pull's waves take
+// consecutive segments together, so the segments in flight of the long row
+// blocks cover one window of columns: the x lines of that window are read
+// into L2 once and used by every long row block whose band covers it,
+// instead of once per row block.  (A long row block's segments already
+// write their sums to slots or with atomics, in any order.)
+template <class Tmp>
+hipError_t order_long_by_column(dbs_matrix *A, Tmp &tmp, hipStream_t s) {
+  const int64_t ns = A->nseg;
+  uint32_t *dkey;
+  hipError_t e = tmp.get((void **)&dkey, (size_t)ns * 4);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_seg_first_cb, dim3(nblocks(ns, 256)), dim3(256), 0, s, (const uint32_t *)A->segs, ns,
+                     (const uint32_t *)A->t_cb, dkey);
+  e = hipGetLastError();
+  std::vector<uint32_t> key(ns), sg(4 * (size_t)ns), out(4 * (size_t)ns);
+  if (e == hipSuccess) e = hipMemcpyAsync(key.data(), dkey, (size_t)ns * 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(sg.data(), A->segs, (size_t)ns * 16, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return e;
+  std::vector<uint32_t> idx;
+  idx.reserve(ns);
+  for (int64_t i = 0; i < ns; ++i)
+    if (((sg[4 * (size_t)i] >> SEG_CLS_SHIFT) & 3u) == 3u) idx.push_back((uint32_t)i);
+  if (idx.empty()) return hipSuccess;
+  std::stable_sort(idx.begin(), idx.end(), [&](uint32_t a, uint32_t b) { return key[a] < key[b]; });
+  for (int64_t i = 0; i < ns; ++i)
+    if (((sg[4 * (size_t)i] >> SEG_CLS_SHIFT) & 3u) != 3u) idx.push_back((uint32_t)i);
+  for (int64_t i = 0; i < ns; ++i)
+    for (int j = 0; j < 4; ++j) out[4 * i + j] = sg[4 * (size_t)idx[i] + j];
+  e = hipMemcpyAsync(A->segs, out.data(), (size_t)ns * 16, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  return e;
+}
+
 int bits_for(uint32_t maxval) {
   int b = 0;
   while (b < 32 && (maxval >> b) != 0) ++b;
@@ -930,6 +974,7 @@ dbs_status dbs_build_impl(dbs_matrix *A, const int32_t *row_ptr, const int32_t *
         A->fin_big[p] = k;
       }
       (void)hm;
+      BUILD_TRY(order_long_by_column(A, tmp, s));
     }
   }
   if (vk == VK_PAT) {

@@ -91,11 +91,7 @@ def check_format(dbs, m, n, rp, ci, vbits, dtype, vk, opt=None, th=(32, 128, 2.0
     # pull segments follow the weighted rule of the oracle
     srb, s0, s1 = orc.segments(tv["rb_ptr"], exp_types, cap=cap)
     segs = ar["segs"]
-    np.testing.assert_array_equal(segs[:, 0] & 0x0FFFFFFF, srb)
-    np.testing.assert_array_equal(segs[:, 1], s0)
-    np.testing.assert_array_equal(segs[:, 2], s1)
     per_rb = np.bincount(srb, minlength=(m + 15) // 16)
-    np.testing.assert_array_equal(segs[:, 0] >> 31, (per_rb[srb] > 1).astype(np.uint32))
     # value matrices: the row blocks of more than 16 segments carry a size
     # class (1: <= 32 segments, 2: <= 64, 3: more) and one partial slot per
     # segment, numbered in segment order over those row blocks
@@ -105,10 +101,20 @@ def check_format(dbs, m, n, rp, ci, vbits, dtype, vk, opt=None, th=(32, 128, 2.0
         long_seg = c > 16
         slot = np.zeros(srb.shape[0], np.uint32)
         slot[long_seg] = np.arange(1, int(long_seg.sum()) + 1, dtype=np.uint32)
+        # stored order: the class-3 segments first, by their first column
+        # block (ties in segment order), then the others in segment order
+        c3 = np.nonzero(cls == 3)[0]
+        c3 = c3[np.argsort(tv["t_cb"][s0[c3]], kind="stable")]
+        order = np.concatenate([c3, np.nonzero(cls != 3)[0]])
     else:
         cls = np.zeros(srb.shape[0], np.int64)
         slot = np.zeros(srb.shape[0], np.uint32)
-    np.testing.assert_array_equal((segs[:, 0] >> 28) & 3, cls.astype(np.uint32))
+        order = np.arange(srb.shape[0])
+    np.testing.assert_array_equal(segs[:, 0] & 0x0FFFFFFF, srb[order])
+    np.testing.assert_array_equal(segs[:, 1], s0[order])
+    np.testing.assert_array_equal(segs[:, 2], s1[order])
+    np.testing.assert_array_equal(segs[:, 0] >> 31, (per_rb[srb] > 1).astype(np.uint32)[order])
+    np.testing.assert_array_equal((segs[:, 0] >> 28) & 3, cls.astype(np.uint32)[order])
     # value matrices: segments where a row has more than 32 entries in COO
     # tiles are marked (bit 30)
     if vk != 2:
@@ -120,10 +126,10 @@ def check_format(dbs, m, n, rp, ci, vbits, dtype, vk, opt=None, th=(32, 128, 2.0
         coo_e = exp_types[tile_e] == 0
         k2 = tile_seg[tile_e[coo_e]] * 16 + ref_rows[coo_e] % 16
         coo_rows = np.bincount(k2, minlength=16 * srb.shape[0]).reshape(-1, 16)
-        np.testing.assert_array_equal((segs[:, 0] >> 30) & 1, (coo_rows.max(axis=1) > 32).astype(np.uint32))
+        np.testing.assert_array_equal((segs[:, 0] >> 30) & 1, (coo_rows.max(axis=1) > 32).astype(np.uint32)[order])
     else:
         assert not ((segs[:, 0] >> 30) & 1).any()
-    np.testing.assert_array_equal(segs[:, 3], slot)
+    np.testing.assert_array_equal(segs[:, 3], slot[order])
     if vk == 2:
         check_pattern_segments(dbs, A, ar, tv, cap)
     for f in range(5):
