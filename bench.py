@@ -339,6 +339,26 @@ def bench_rmat20(dbs, torch, args):
     return res
 
 
+def measure_copy_gbps(torch, gib=1, reps=10):
+    """A plain device-to-device copy of `gib` GiB (torch's copy kernel), timed
+    with HIP events: read + write bytes per second, the streaming bandwidth
+    this box reaches, beside the published 8 TB/s."""
+    a = torch.ones(gib << 28, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    gbps = 2 * a.numel() * 4 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+    torch.cuda.empty_cache()
+    return round(gbps, 1)
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -818,6 +838,8 @@ def main():
     if not args.no_ablations:
         extra["format_ablation"] = bench_format_ablation(dbs, torch, args)
     traffic = load_traffic("rmat20_sweep")
+    copy_gbps = measure_copy_gbps(torch)
+    log(f"[bench] device copy: {copy_gbps} GB/s (read + write)")
     line = {
         "metric": METRIC,
         "value": round(res["value"], 2),
@@ -837,7 +859,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(res["achieved"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(res["achieved"] / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "k_spmspv<pattern, or-and>", "kernel_avg_us": round(res["kernel_avg_us"], 2),
-                     "algorithmic_bytes_per_launch": int(res["comp_bytes_per_launch"])},
+                     "algorithmic_bytes_per_launch": int(res["comp_bytes_per_launch"]),
+                     "measured_copy_GBps": copy_gbps,
+                     "frac_of_measured_copy": round(res["achieved"] / copy_gbps, 4)},
         "cpu_baseline": cpu,
         "extra": extra,
     }

@@ -118,28 +118,34 @@ def _check(st: int, where: str) -> None:
         raise DBSError(st, where)
 
 
+# torch (imported by load_library before the library) and its raw current
+# stream getter, looked up once: the per-call wrappers run at a few us
+import torch as _torch  # noqa: E402
+
+_RAW_STREAM = getattr(_torch._C, "_cuda_getCurrentRawStream", None)
+_Tensor = _torch.Tensor
+_I32, _F32, _U8 = (_torch.int32,), (_torch.float32,), (_torch.uint8,)
+
+
 def _ptr(t):
-    return None if t is None else C.c_void_p(t.data_ptr())
+    # the argtypes are c_void_p: a plain int (or None) converts on the call
+    return None if t is None else t.data_ptr()
 
 
 def _stream(stream, device=None):
     """Raw HIP stream handle: the given stream, else the current stream of
     `device` (the call's output tensor's device), read without building a
     Stream object where torch offers that."""
-    import torch
-
     if stream is None:
-        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
-        if raw is not None and device is not None:
-            return C.c_void_p(raw(device.index if device.index is not None else torch.cuda.current_device()))
-        stream = torch.cuda.current_stream(device)
-    return C.c_void_p(stream.cuda_stream)
+        if _RAW_STREAM is not None and device is not None:
+            idx = device.index
+            return _RAW_STREAM(idx if idx is not None else _torch.cuda.current_device())
+        stream = _torch.cuda.current_stream(device)
+    return stream.cuda_stream
 
 
 def _need(t, name, dtypes, numel=None):
-    import torch
-
-    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+    if not isinstance(t, _Tensor) or not t.is_cuda:
         raise TypeError(f"{name} must be a CUDA tensor")
     if t.dtype not in dtypes:
         raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
@@ -149,13 +155,14 @@ def _need(t, name, dtypes, numel=None):
         raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
 
 
-def _value_dtypes(dtype):
-    import torch
+_BF16_DTYPES = (_torch.bfloat16, _torch.int16, _torch.uint16)
 
+
+def _value_dtypes(dtype):
     if dtype == DBS_F32:
-        return (torch.float32,)
+        return _F32
     if dtype == DBS_BF16:
-        return (torch.bfloat16, torch.int16, torch.uint16)
+        return _BF16_DTYPES
     return ()
 
 
@@ -197,18 +204,18 @@ def dbs_build(m, n, row_ptr, col_idx, val, dtype, options=None, stream=None) -> 
 
 
 def dbs_spmspv(A: Matrix, x_idx, x_val, semiring, y, stream=None) -> None:
-    import torch
-
-    _need(x_idx, "x_idx", (torch.int32,))
+    _need(x_idx, "x_idx", _I32)
     if semiring == DBS_PLUS_TIMES:
         _need(x_val, "x_val", _value_dtypes(A.dtype), x_idx.numel())
-        _need(y, "y", (torch.float32,), A.m)
+        _need(y, "y", _F32, A.m)
+        xv = x_val.data_ptr()
     else:
-        _need(y, "y", (torch.uint8,), A.m)
-    st = _lib.dbs_spmspv(A.handle, int(x_idx.numel()), _ptr(x_idx),
-                         _ptr(x_val) if semiring == DBS_PLUS_TIMES else None, int(semiring), _ptr(y),
+        _need(y, "y", _U8, A.m)
+        xv = None
+    st = _lib.dbs_spmspv(A.handle, x_idx.numel(), x_idx.data_ptr(), xv, int(semiring), y.data_ptr(),
                          _stream(stream, y.device))
-    _check(st, "dbs_spmspv")
+    if st != DBS_OK:
+        raise DBSError(st, "dbs_spmspv")
 
 
 def dbs_spmspv_dense(A: Matrix, x, semiring, y, stream=None) -> None:
