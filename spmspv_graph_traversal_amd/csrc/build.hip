@@ -102,12 +102,40 @@ struct RowCursor {
   int64_t p, e;
 };
 
-DBS_DEV RowCursor row_cursor(int32_t m, int32_t mb, const int32_t *row_ptr, int32_t rb, int r) {
+// Merge items: a row block whose rows hold more than LONG_RB_NNZ entries is
+// merged in pieces of CHUNK_CB column blocks, one 16-lane group each (the
+// merge walks a row block's tiles one after another, so a hub row block's
+// walk set the build time); the others are one item each.  Item i covers
+// row block item_rb[i], column blocks [item_lo[i], item_hi[i]), and its tiles
+// start at item_off[i] in block-CSR order.
+constexpr int64_t LONG_RB_NNZ = 4096;
+constexpr uint32_t CHUNK_CB = 64;
+
+struct Items {
+  const uint32_t *rb, *lo, *hi;
+  int64_t n;
+};
+
+// first position in [p, e) whose column is >= col (entries sorted)
+DBS_DEV int64_t lower_col(const int32_t *col_idx, int64_t p, int64_t e, int64_t col) {
+  while (p < e) {
+    const int64_t mid = p + ((e - p) >> 1);
+    if ((int64_t)col_idx[mid] < col) p = mid + 1;
+    else e = mid;
+  }
+  return p;
+}
+
+// lane r's cursor over its row's entries in the item's column-block range
+DBS_DEV RowCursor item_cursor(int32_t m, const int32_t *row_ptr, const int32_t *col_idx, uint32_t rb,
+                              uint32_t lo, uint32_t hi, int r) {
   RowCursor c{0, 0};
   const int64_t row = (int64_t)rb * DBS_TILE + r;
-  if (rb < mb && row < m) {
+  if (row < m) {
     c.p = row_ptr[row];
     c.e = row_ptr[row + 1];
+    if (lo != 0u) c.p = lower_col(col_idx, c.p, c.e, (int64_t)lo * DBS_TILE);
+    if (hi != 0xFFFFFFFFu) c.e = lower_col(col_idx, c.p, c.e, (int64_t)hi * DBS_TILE);
   }
   return c;
 }
@@ -156,12 +184,65 @@ DBS_DEV uint32_t classify_tile(uint32_t nnz, uint32_t maxr, uint32_t maxc,
   return DBS_TILE_CSR;
 }
 
-// pass 1: tiles per row block
-__global__ __launch_bounds__(BT) void k_tile_count(int32_t m, int32_t mb, const int32_t *row_ptr,
-                                                   const int32_t *col_idx, uint32_t *rb_cnt) {
+// Items: the number of merge items of each row block and the first column
+// block's chunk of a long one.  One thread per row block.
+__global__ void k_rb_items(int32_t m, int32_t mb, const int32_t *row_ptr, const int32_t *col_idx, uint32_t *nitem,
+                           uint32_t *chunk0) {
+  const int64_t rb = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (rb >= mb) return;
+  const int64_t r0 = rb * DBS_TILE, r1 = r0 + DBS_TILE < m ? r0 + DBS_TILE : m;
+  uint32_t n = 1, c0 = 0;
+  if ((int64_t)row_ptr[r1] - row_ptr[r0] > LONG_RB_NNZ) {
+    uint32_t lo = 0xFFFFFFFFu, hi = 0;
+    for (int64_t row = r0; row < r1; ++row) {
+      const int64_t a = row_ptr[row], b = row_ptr[row + 1];
+      if (a < b) {
+        const uint32_t f = (uint32_t)col_idx[a] >> 4, l = (uint32_t)col_idx[b - 1] >> 4;
+        lo = f < lo ? f : lo;
+        hi = l > hi ? l : hi;
+      }
+    }
+    c0 = lo / CHUNK_CB;
+    n = hi / CHUNK_CB - c0 + 1;
+  }
+  nitem[rb] = n;
+  chunk0[rb] = c0;
+}
+
+// the items themselves: (row block, column-block range); one thread per row block
+__global__ void k_fill_items(int32_t mb, const uint32_t *nitem, const uint32_t *item_start, const uint32_t *chunk0,
+                             uint32_t *item_rb, uint32_t *item_lo, uint32_t *item_hi) {
+  const int64_t rb = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (rb >= mb) return;
+  const uint32_t n = nitem[rb], s0 = item_start[rb];
+  if (n == 1u) {
+    item_rb[s0] = (uint32_t)rb;
+    item_lo[s0] = 0u;
+    item_hi[s0] = 0xFFFFFFFFu;
+    return;
+  }
+  for (uint32_t j = 0; j < n; ++j) {
+    item_rb[s0 + j] = (uint32_t)rb;
+    item_lo[s0 + j] = (chunk0[rb] + j) * CHUNK_CB;
+    item_hi[s0 + j] = (chunk0[rb] + j + 1) * CHUNK_CB;
+  }
+}
+
+// block-CSR row pointer: the first tile of each row block's first item
+__global__ void k_rb_ptr_from_items(int32_t mb, const uint32_t *item_start, const uint32_t *item_off, int64_t ni,
+                                    uint32_t *rb_ptr) {
+  const int64_t rb = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (rb > mb) return;
+  rb_ptr[rb] = rb < mb ? item_off[item_start[rb]] : item_off[ni];
+}
+
+// pass 1: tiles per item
+__global__ __launch_bounds__(BT) void k_tile_count(int32_t m, const int32_t *row_ptr, const int32_t *col_idx,
+                                                   Items it, uint32_t *item_cnt) {
   const int r = threadIdx.x & 15;
-  const int32_t rb = (int32_t)blockIdx.x * RB_PER_BLOCK + (int32_t)(threadIdx.x >> 4);
-  RowCursor c = row_cursor(m, mb, row_ptr, rb, r);
+  const int64_t i = (int64_t)blockIdx.x * RB_PER_BLOCK + (int64_t)(threadIdx.x >> 4);
+  RowCursor c{0, 0};
+  if (i < it.n) c = item_cursor(m, row_ptr, col_idx, it.rb[i], it.lo[i], it.hi[i], r);
   uint32_t cnt = 0;
   while (true) {
     const uint32_t cb = group_min_u32<16>(cursor_cb(c, col_idx));
@@ -169,19 +250,24 @@ __global__ __launch_bounds__(BT) void k_tile_count(int32_t m, int32_t mb, const 
     ++cnt;
     (void)cursor_take(c, col_idx, cb);
   }
-  if (r == 0 && rb < mb) rb_cnt[rb] = cnt;
+  if (r == 0 && i < it.n) item_cnt[i] = cnt;
 }
 
 // pass 2: per tile column block, row block, nnz, format and payload size
-__global__ __launch_bounds__(BT) void k_tile_classify(int32_t m, int32_t mb, const int32_t *row_ptr,
-                                                      const int32_t *col_idx, const uint32_t *rb_ptr,
+__global__ __launch_bounds__(BT) void k_tile_classify(int32_t m, const int32_t *row_ptr, const int32_t *col_idx,
+                                                      Items it, const uint32_t *item_off,
                                                       dbs_build_options o, int vk, int64_t T,
                                                       uint32_t *t_cb, uint32_t *t_rb, uint32_t *t_nt,
                                                       uint64_t *sizes) {
   const int r = threadIdx.x & 15;
-  const int32_t rb = (int32_t)blockIdx.x * RB_PER_BLOCK + (int32_t)(threadIdx.x >> 4);
-  RowCursor c = row_cursor(m, mb, row_ptr, rb, r);
-  int64_t t = rb < mb ? (int64_t)rb_ptr[rb] : 0;
+  const int64_t i = (int64_t)blockIdx.x * RB_PER_BLOCK + (int64_t)(threadIdx.x >> 4);
+  RowCursor c{0, 0};
+  uint32_t rb = 0;
+  if (i < it.n) {
+    rb = it.rb[i];
+    c = item_cursor(m, row_ptr, col_idx, rb, it.lo[i], it.hi[i], r);
+  }
+  int64_t t = i < it.n ? (int64_t)item_off[i] : 0;
   while (true) {
     const uint32_t cb = group_min_u32<16>(cursor_cb(c, col_idx));
     if (cb == 0xFFFFFFFFu) break;
@@ -231,16 +317,16 @@ DBS_DEV void store_zero(uint8_t *dst) {
 
 // pass 3: write every tile's payload in its format
 template <int VK>
-__global__ __launch_bounds__(BT) void k_tile_fill(int32_t m, int32_t mb, const int32_t *row_ptr,
-                                                  const int32_t *col_idx, const void *val,
-                                                  const uint32_t *rb_ptr, const uint64_t *t_meta,
-                                                  uint64_t *t_meta_w, uint8_t *payload,
+__global__ __launch_bounds__(BT) void k_tile_fill(int32_t m, const int32_t *row_ptr, const int32_t *col_idx,
+                                                  const void *val, Items it, const uint32_t *item_off,
+                                                  const uint64_t *t_meta, uint64_t *t_meta_w, uint8_t *payload,
                                                   uint64_t dense_mask_off, uint16_t *t_cm) {
   constexpr int VS = VK == VK_F32 ? 4 : VK == VK_BF16 ? 2 : 0;
   const int r = threadIdx.x & 15;
-  const int32_t rb = (int32_t)blockIdx.x * RB_PER_BLOCK + (int32_t)(threadIdx.x >> 4);
-  RowCursor c = row_cursor(m, mb, row_ptr, rb, r);
-  int64_t t = rb < mb ? (int64_t)rb_ptr[rb] : 0;
+  const int64_t i = (int64_t)blockIdx.x * RB_PER_BLOCK + (int64_t)(threadIdx.x >> 4);
+  RowCursor c{0, 0};
+  if (i < it.n) c = item_cursor(m, row_ptr, col_idx, it.rb[i], it.lo[i], it.hi[i], r);
+  int64_t t = i < it.n ? (int64_t)item_off[i] : 0;
   while (true) {
     const uint32_t cb = group_min_u32<16>(cursor_cb(c, col_idx));
     if (cb == 0xFFFFFFFFu) break;
@@ -793,16 +879,42 @@ dbs_status dbs_build_impl(dbs_matrix *A, const int32_t *row_ptr, const int32_t *
   hipLaunchKernelGGL(k_rows_nz, dim3(nblocks(rwords, BT)), dim3(BT), 0, s, m, rwords, row_ptr, A->rows_nz);
   BUILD_TRY(hipGetLastError());
 
-  // --- pass 1: tiles per row block, block-CSR row pointer
-  uint32_t *rb_cnt;
-  BUILD_TRY(tmp.get((void **)&rb_cnt, (size_t)mb * 4));
-  BUILD_TRY(dbs_dev_alloc(A, (void **)&A->rb_ptr, (size_t)(mb + 1) * 4));
+  // --- merge items: one per row block, long row blocks in column-block pieces
+  uint32_t *nitem, *chunk0, *item_start;
+  BUILD_TRY(tmp.get((void **)&nitem, (size_t)mb * 4));
+  BUILD_TRY(tmp.get((void **)&chunk0, (size_t)mb * 4));
+  BUILD_TRY(tmp.get((void **)&item_start, (size_t)(mb + 1) * 4));
   void *stmp;
   BUILD_TRY(tmp.get(&stmp, dbs_scan_tmp_bytes((int64_t)mb + 1)));
-  const unsigned gblocks = nblocks(mb, RB_PER_BLOCK);
-  hipLaunchKernelGGL(k_tile_count, dim3(gblocks), dim3(BT), 0, s, m, mb, row_ptr, col_idx, rb_cnt);
+  hipLaunchKernelGGL(k_rb_items, dim3(nblocks(mb, BT)), dim3(BT), 0, s, m, mb, row_ptr, col_idx, nitem, chunk0);
   BUILD_TRY(hipGetLastError());
-  BUILD_TRY(dbs_scan_u32(rb_cnt, A->rb_ptr, mb, stmp, s));
+  BUILD_TRY(dbs_scan_u32(nitem, item_start, mb, stmp, s));
+  uint32_t hNI = 0;
+  BUILD_TRY(hipMemcpyAsync(&hNI, item_start + mb, 4, hipMemcpyDeviceToHost, s));
+  BUILD_TRY(hipStreamSynchronize(s));
+  const int64_t NI = hNI;
+  uint32_t *item_rb, *item_lo, *item_hi, *item_cnt, *item_off;
+  BUILD_TRY(tmp.get((void **)&item_rb, (size_t)NI * 4 + 4));
+  BUILD_TRY(tmp.get((void **)&item_lo, (size_t)NI * 4 + 4));
+  BUILD_TRY(tmp.get((void **)&item_hi, (size_t)NI * 4 + 4));
+  BUILD_TRY(tmp.get((void **)&item_cnt, (size_t)NI * 4 + 4));
+  BUILD_TRY(tmp.get((void **)&item_off, (size_t)(NI + 1) * 4));
+  void *stmpi;
+  BUILD_TRY(tmp.get(&stmpi, dbs_scan_tmp_bytes(NI + 1)));
+  hipLaunchKernelGGL(k_fill_items, dim3(nblocks(mb, BT)), dim3(BT), 0, s, mb, (const uint32_t *)nitem,
+                     (const uint32_t *)item_start, (const uint32_t *)chunk0, item_rb, item_lo, item_hi);
+  BUILD_TRY(hipGetLastError());
+  const Items items{item_rb, item_lo, item_hi, NI};
+  const unsigned gblocks = nblocks(NI, RB_PER_BLOCK);
+
+  // --- pass 1: tiles per item, block-CSR row pointer
+  BUILD_TRY(dbs_dev_alloc(A, (void **)&A->rb_ptr, (size_t)(mb + 1) * 4));
+  hipLaunchKernelGGL(k_tile_count, dim3(gblocks), dim3(BT), 0, s, m, row_ptr, col_idx, items, item_cnt);
+  BUILD_TRY(hipGetLastError());
+  BUILD_TRY(dbs_scan_u32(item_cnt, item_off, NI, stmpi, s));
+  hipLaunchKernelGGL(k_rb_ptr_from_items, dim3(nblocks((int64_t)mb + 1, BT)), dim3(BT), 0, s, mb,
+                     (const uint32_t *)item_start, (const uint32_t *)item_off, NI, A->rb_ptr);
+  BUILD_TRY(hipGetLastError());
   uint32_t hT = 0;
   BUILD_TRY(hipMemcpyAsync(&hT, A->rb_ptr + mb, 4, hipMemcpyDeviceToHost, s));
   BUILD_TRY(hipStreamSynchronize(s));
@@ -820,8 +932,8 @@ dbs_status dbs_build_impl(dbs_matrix *A, const int32_t *row_ptr, const int32_t *
   BUILD_TRY(tmp.get((void **)&offs, (size_t)(3 * T + 1) * 8));
   void *stmp3;
   BUILD_TRY(tmp.get(&stmp3, dbs_scan_tmp_bytes(3 * T + 1)));
-  hipLaunchKernelGGL(k_tile_classify, dim3(gblocks), dim3(BT), 0, s, m, mb, row_ptr, col_idx,
-                     (const uint32_t *)A->rb_ptr, A->bopt, vk, T, A->t_cb, t_rb, t_nt, sizes);
+  hipLaunchKernelGGL(k_tile_classify, dim3(gblocks), dim3(BT), 0, s, m, row_ptr, col_idx, items,
+                     (const uint32_t *)item_off, A->bopt, vk, T, A->t_cb, t_rb, t_nt, sizes);
   BUILD_TRY(hipGetLastError());
   BUILD_TRY(dbs_scan_u64(sizes, offs, 3 * T, stmp3, s));
   uint64_t total = 0, dense_bytes = 0;
@@ -844,17 +956,17 @@ dbs_status dbs_build_impl(dbs_matrix *A, const int32_t *row_ptr, const int32_t *
   uint16_t *t_cm;
   BUILD_TRY(tmp.get((void **)&t_cm, (size_t)T * 2 + 2));
   if (vk == VK_F32)
-    hipLaunchKernelGGL(k_tile_fill<VK_F32>, dim3(gblocks), dim3(BT), 0, s, m, mb, row_ptr, col_idx, val,
-                       (const uint32_t *)A->rb_ptr, (const uint64_t *)A->t_meta, A->t_meta, A->payload, A->dense_mask_off,
-                       t_cm);
+    hipLaunchKernelGGL(k_tile_fill<VK_F32>, dim3(gblocks), dim3(BT), 0, s, m, row_ptr, col_idx, val, items,
+                       (const uint32_t *)item_off, (const uint64_t *)A->t_meta, A->t_meta, A->payload,
+                       A->dense_mask_off, t_cm);
   else if (vk == VK_BF16)
-    hipLaunchKernelGGL(k_tile_fill<VK_BF16>, dim3(gblocks), dim3(BT), 0, s, m, mb, row_ptr, col_idx, val,
-                       (const uint32_t *)A->rb_ptr, (const uint64_t *)A->t_meta, A->t_meta, A->payload, A->dense_mask_off,
-                       t_cm);
+    hipLaunchKernelGGL(k_tile_fill<VK_BF16>, dim3(gblocks), dim3(BT), 0, s, m, row_ptr, col_idx, val, items,
+                       (const uint32_t *)item_off, (const uint64_t *)A->t_meta, A->t_meta, A->payload,
+                       A->dense_mask_off, t_cm);
   else
-    hipLaunchKernelGGL(k_tile_fill<VK_PAT>, dim3(gblocks), dim3(BT), 0, s, m, mb, row_ptr, col_idx, val,
-                       (const uint32_t *)A->rb_ptr, (const uint64_t *)A->t_meta, A->t_meta, A->payload, A->dense_mask_off,
-                       t_cm);
+    hipLaunchKernelGGL(k_tile_fill<VK_PAT>, dim3(gblocks), dim3(BT), 0, s, m, row_ptr, col_idx, val, items,
+                       (const uint32_t *)item_off, (const uint64_t *)A->t_meta, A->t_meta, A->payload,
+                       A->dense_mask_off, t_cm);
   BUILD_TRY(hipGetLastError());
 
   // --- block-level CSC view: stable sort of the tiles by column block

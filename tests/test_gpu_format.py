@@ -275,6 +275,33 @@ def test_long_row_blocks_segments(dbs, cap):
     check_format(dbs, m, n, rp, ci, None, dbs.DBS_PATTERN, 2, opt=opt, cap=cap)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "pattern"])
+def test_long_row_blocks_merged_in_pieces(dbs, dtype):
+    # row blocks with more than 4096 entries are merged in pieces of 64 column
+    # blocks: entries on both sides of piece boundaries, a piece with no
+    # entries, a hub row spanning most columns next to short rows, dense
+    # tiles inside a long row block, and a row block just at the threshold
+    rng = rng_for("test", 640, 0 if dtype == "f32" else 1)
+    n = 16 * 64 * 40 + 7  # 40 pieces and a ragged last column block
+    m = 70
+    a = np.zeros((m, n), np.float32)
+    a[3, :] = (rng.random(n) < 0.3) * rng.uniform(-1, 1, n)          # hub row
+    for c in (1023, 1024, 1025, 2047, 2048, 16 * 64 * 7, 16 * 64 * 7 - 1, n - 1):
+        a[9, c] = 1.5                                                  # piece boundaries
+    a[0:16, 16 * 64 * 20: 16 * 64 * 20 + 48] = rng.uniform(0.5, 1, (16, 48))  # dense tiles
+    a[:, 16 * 64 * 30: 16 * 64 * 32] = 0.0                           # two empty pieces
+    a[16, : 4097] = 1.0                                                # row block 1: 4097 entries
+    a[32, : 4096] = 1.0                                                # row block 2: 4096 entries
+    a[50:66, ::97] = 2.0                                               # a long row block of short rows
+    rp, ci, v = csr_of(a)
+    nnz_rb = np.add.reduceat(np.diff(rp), np.arange(0, m, 16))
+    assert nnz_rb[0] > 4096 and nnz_rb[1] > 4096 and nnz_rb[2] == 4096
+    if dtype == "f32":
+        check_format(dbs, m, n, rp, ci, v, dbs.DBS_F32, 0)
+    else:
+        check_format(dbs, m, n, rp, ci, None, dbs.DBS_PATTERN, 2)
+
+
 def hub_row_dense(seed, n=8192):
     """64 x n: row 5 holds an entry in every column (16 per tile), the others
     a few random ones, so every tile stays COO (fewer than 32 entries) while
