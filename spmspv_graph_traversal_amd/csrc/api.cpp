@@ -68,7 +68,7 @@ void free_all(dbs_matrix *A) {
   void *bufs[] = {A->rb_ptr, A->t_cb,     A->t_meta,   A->cb_ptr,     A->csc_rb,  A->csc2csr, A->csc_cm,
                   A->payload, A->segs,    A->psegs,    A->wown,    A->rows_nz,  A->xmask,    A->xbits,      A->xd,
                   A->act_list, A->chunks,
-                  A->ctr,    A->bfs_bm,   A->bfs_vis,  A->bfs_list,   A->bfs_chunks, A->bfs_ctr,
+                  A->ctr,    A->bfs_bm,   A->bfs_vis,  A->bfs_fbits, A->bfs_list,   A->bfs_chunks, A->bfs_ctr,
                   A->fin,    A->partial};
   for (void *b : bufs)
     if (b) (void)hipFree(b);

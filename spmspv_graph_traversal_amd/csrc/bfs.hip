@@ -52,6 +52,8 @@ struct BfsParams {
   int64_t nseg, npseg, nseg0, T, payload_bytes;
   int32_t m, nb;
   const uint32_t *cur_bm;   // frontier of this level
+  const uint32_t *cur_fbits;  // a bit per frontier bitmap word (two blocks) that is nonzero, fw words
+  int32_t fw;
   uint32_t *next_bm;        // frontier of the next level (cleared)
   uint32_t *vis;            // visited bitmap
   const uint32_t *cur_ctr;  // [0] nonzero blocks, [1] push chunks
@@ -203,14 +205,20 @@ DBS_DEV void bfs_pull_group(const BfsParams &P, const BfsRes &R, int64_t s0, boo
 // wanted, masks come from the frontier bitmap, found rows are claimed for
 // the next level.  The visited word may miss rows claimed earlier in this
 // level (that only costs work), never rows of earlier levels.
+// FILTER: the frontier's word bits are in LDS, and only the tiles whose
+// column block lies in a nonzero bitmap word read that word from memory
+// (the reads of the others would find a zero mask).
+template <bool FILTER>
 struct BfsPol {
   const BfsParams *P;
   brsrc_t bm, vis;
+  const uint32_t *bits;  // FILTER: LDS
   DBS_DEV uint32_t need_v(uint32_t rb, bool in) const {
     const uint32_t w = bld32(vis, in ? (rb >> 1) * 4u : OOB_OFF);
     return ~(w >> ((rb & 1u) * 16u)) & rows_valid(P->m, rb);
   }
   DBS_DEV uint32_t mask(uint32_t cb, bool in) const {
+    if constexpr (FILTER) in = in && ((bits[cb >> 6] >> ((cb >> 1) & 31u)) & 1u);  // idle lanes hold cb 0
     const uint32_t w = bld32(bm, in ? (cb >> 1) * 4u : OOB_OFF);
     return (w >> ((cb & 1u) * 16u)) & 0xFFFFu;
   }
@@ -264,15 +272,36 @@ __global__ __launch_bounds__(KT, VK == VK_PAT ? 5 : 1) void k_bfs_level(BfsParam
       const PatSrc S{P.t_cb, P.t_meta, sg, P.phase == 0 ? P.nseg0 : P.npseg - P.nseg0,
                      make_rsrc(P.payload, (uint64_t)P.payload_bytes + DBS_PAYLOAD_SLACK),
                      make_rsrc(P.wown, (uint64_t)(P.payload_bytes + DBS_PAYLOAD_SLACK) / 4)};
-      const BfsPol pol{&P, R.bm, make_rsrc(P.vis, (uint64_t)((P.nb + 1) / 2) * 4)};
-      pattern_pull(S, pol, gw, nw, eager, lane, s_pat[w]);
+      const brsrc_t rv = make_rsrc(P.vis, (uint64_t)((P.nb + 1) / 2) * 4);
+      if (!eager && P.fw <= dbs_meta::PUSH_LIST_MAX) {  // uniform
+        // the frontier's word bits in the push enumeration's LDS
+        for (int i = (int)threadIdx.x; i < P.fw; i += KT) s_cum[i] = P.cur_fbits[i];
+        __syncthreads();
+        const BfsPol<true> pol{&P, R.bm, rv, s_cum};
+        pattern_pull<true>(S, pol, gw, nw, false, lane, s_pat[w]);
+      } else {
+        const BfsPol<false> pol{&P, R.bm, rv, nullptr};
+        pattern_pull(S, pol, gw, nw, eager, lane, s_pat[w]);
+      }
     } else {
       for (int64_t s = gw * U; s < P.nseg; s += nw * U) bfs_pull_group<VK, U>(P, R, s, eager, lane);
     }
   }
 }
 
-// Frontier metadata: nonzero blocks of `bm`, their list and push chunks;
+// bit k of the result: block bit 2k or 2k+1 of v (the blocks of one bitmap word)
+DBS_DEV uint32_t word_bits(uint64_t v) {
+  v = (v | (v >> 1)) & 0x5555555555555555ull;
+  v = (v | (v >> 1)) & 0x3333333333333333ull;
+  v = (v | (v >> 2)) & 0x0F0F0F0F0F0F0F0Full;
+  v = (v | (v >> 4)) & 0x00FF00FF00FF00FFull;
+  v = (v | (v >> 8)) & 0x0000FFFF0000FFFFull;
+  v = (v | (v >> 16)) & 0x00000000FFFFFFFFull;
+  return (uint32_t)v;
+}
+
+// Frontier metadata: nonzero blocks of `bm`, their list and push chunks, and
+// a bit per nonzero bitmap word (fbits);
 // clears `clr_bm` / `clr_ctr` (the buffers two levels back) when given.
 // After the traversal has ended (the level's own frontier, counted in
 // in_ctr, was empty) only the counters two levels back are cleared: the next
@@ -281,7 +310,7 @@ __global__ __launch_bounds__(KT, VK == VK_PAT ? 5 : 1) void k_bfs_level(BfsParam
 // returns at once (the bitmaps are cleared by the next BFS's start).
 __global__ __launch_bounds__(dbs_meta::MT) void k_bfs_meta(const uint32_t *bm, int32_t nb, dbs_meta::Reg reg,
                                                  uint32_t *clr_bm, uint32_t *clr_ctr, int64_t nwords,
-                                                 const uint32_t *in_ctr) {
+                                                 const uint32_t *in_ctr, uint32_t *fbits) {
   if (in_ctr[0] == 0u) {  // uniform
     if (clr_ctr && blockIdx.x == 0 && threadIdx.x < 8) clr_ctr[threadIdx.x] = 0;
     return;
@@ -291,9 +320,13 @@ __global__ __launch_bounds__(dbs_meta::MT) void k_bfs_meta(const uint32_t *bm, i
     for (int64_t k = (int64_t)blockIdx.x * dbs_meta::MT + threadIdx.x; k < nwords; k += gs) clr_bm[k] = 0;
     if (blockIdx.x == 0 && threadIdx.x < 8) clr_ctr[threadIdx.x] = 0;
   }
-  dbs_meta::register_blocks(reg, nb, [&](int64_t b, int, bool &leader, uint32_t &bo) {
+  dbs_meta::register_blocks(reg, nb, [&](int64_t b, int pass, bool &leader, uint32_t &bo) {
     leader = b < nb && bm_get(bm, (uint32_t)b) != 0u;
     bo = (uint32_t)b;
+    // the bitmap's word bits: a wave holds 64 consecutive blocks (32 words)
+    // from a multiple of 64, one bit word
+    const uint64_t bal = __ballot(leader);
+    if (pass == 0 && __lane_id() == 0 && b < nb) fbits[b >> 6] = word_bits(bal);
   });
 }
 
@@ -305,7 +338,8 @@ __global__ __launch_bounds__(dbs_meta::MT) void k_bfs_meta(const uint32_t *bm, i
 // level 0 pushes from chunks built ahead, the push chunks of its column block.
 __global__ void k_bfs_init(int32_t *levels, int32_t m, uint32_t *bm3, int64_t bm_words3, uint32_t *vis,
                            const uint32_t *rows_nz, int64_t nwords, uint32_t *ctr3, int32_t src,
-                           const uint32_t *cb_ptr, uint32_t *list0, uint64_t *chunks0, int64_t chunk_cap, int push0) {
+                           const uint32_t *cb_ptr, uint32_t *list0, uint64_t *chunks0, int64_t chunk_cap, int push0,
+                           uint32_t *fbits0, int32_t fw) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t gs = (int64_t)gridDim.x * blockDim.x;
   const uint32_t b = (uint32_t)src >> 4;
@@ -314,6 +348,7 @@ __global__ void k_bfs_init(int32_t *levels, int32_t m, uint32_t *bm3, int64_t bm
   for (int64_t k = i; k < m; k += gs) levels[k] = k == src ? 0 : -1;
   for (int64_t k = i; k < bm_words3; k += gs) bm3[k] = k == ws ? bits : 0u;
   for (int64_t k = i; k < nwords; k += gs) vis[k] = ~rows_nz[k] | (k == ws ? bits : 0u);
+  for (int64_t k = i; k < fw; k += gs) fbits0[k] = k == (int64_t)(b >> 6) ? 1u << ((b >> 1) & 31u) : 0u;
   const uint32_t t = cb_ptr[b + 1] - cb_ptr[b];
   int64_t nch = push0 ? (int64_t)((t + 63u) >> 6) : 0;
   nch = nch < chunk_cap ? nch : chunk_cap;
@@ -361,6 +396,7 @@ namespace {
 // of levels and a spare counter, and a host buffer that receives the sizes.
 struct BfsScratch {
   uint32_t *bm, *vis, *list;
+  uint32_t *fbits;  // 3 x fw words: the bits of each frontier bitmap's nonzero words
   uint64_t *chunks;
   uint32_t *ctr;
   uint32_t *host;  // 64 B of host memory (pinned for dbs_bfs)
@@ -382,12 +418,13 @@ dbs_status dbs_bfs_impl(dbs_matrix *A, int32_t src, int32_t *levels, hipStream_t
   if (!A->bfs_bm) {
     BFS_TRY(dbs_dev_alloc(A, (void **)&A->bfs_bm, (size_t)(3 * nwords + 1) * 4));
     BFS_TRY(dbs_dev_alloc(A, (void **)&A->bfs_vis, (size_t)(nwords + 1) * 4));
+    BFS_TRY(dbs_dev_alloc(A, (void **)&A->bfs_fbits, (size_t)(3 * (((int64_t)A->nb + 63) / 64) + 1) * 4));
     BFS_TRY(dbs_dev_alloc(A, (void **)&A->bfs_list, (size_t)(3 * (int64_t)A->nb + 1) * 4));
     BFS_TRY(dbs_dev_alloc(A, (void **)&A->bfs_chunks, (size_t)(3 * chunk_cap + 1) * 8));
     BFS_TRY(dbs_dev_alloc(A, (void **)&A->bfs_ctr, (24 + dbs_matrix::kBfsBatch + 1) * 4));
     BFS_TRY(hipHostMalloc((void **)&A->bfs_host, 64, hipHostMallocDefault));
   }
-  const BfsScratch S{A->bfs_bm, A->bfs_vis, A->bfs_list, A->bfs_chunks, A->bfs_ctr, A->bfs_host};
+  const BfsScratch S{A->bfs_bm, A->bfs_vis, A->bfs_list, A->bfs_fbits, A->bfs_chunks, A->bfs_ctr, A->bfs_host};
   const dbs_status st = bfs_run(A, S, src, levels, s);
   A->bfs_counted = st == DBS_OK ? 1 : 0;  // its visited bitmap stays in the handle
   return st;
@@ -404,9 +441,10 @@ dbs_status bfs_run(dbs_matrix *A, const BfsScratch &S, int32_t src, int32_t *lev
   const bool list_push = bfs_list_push(A);
   const int push0 =
       !list_push && (fp == 1 || (fp == 0 && A->opt[DBS_OPT_TH3_DEN] < (int64_t)A->nb * A->opt[DBS_OPT_TH3_NUM]));
+  const int32_t fw = (int32_t)(((int64_t)A->nb + 63) / 64);
   hipLaunchKernelGGL(k_bfs_init, dim3(1024), dim3(256), 0, s, levels, A->m, S.bm, 3 * nwords, S.vis,
                      (const uint32_t *)A->rows_nz, nwords, S.ctr, src, (const uint32_t *)A->cb_ptr, S.list,
-                     S.chunks, chunk_cap, push0);
+                     S.chunks, chunk_cap, push0, S.fbits, fw);
   BFS_TRY(hipGetLastError());
   const unsigned mgrid = dbs_meta::groups_for(A->nb, nwords);
   auto reg_for = [&](int buf) {
@@ -451,6 +489,7 @@ dbs_status bfs_run(dbs_matrix *A, const BfsScratch &S, int32_t src, int32_t *lev
   P.th3_num = A->opt[DBS_OPT_TH3_NUM];
   P.th3_den = A->opt[DBS_OPT_TH3_DEN];
   P.list_push = list_push ? 1 : 0;
+  P.fw = fw;
   const int pu = A->vk == VK_PAT ? 1 : 8;
   const int64_t ns = A->vk == VK_PAT ? A->npseg : A->nseg;
   int64_t waves = (ns + pu - 1) / pu > chunk_cap ? (ns + pu - 1) / pu : chunk_cap;
@@ -476,6 +515,7 @@ dbs_status bfs_run(dbs_matrix *A, const BfsScratch &S, int32_t src, int32_t *lev
       P.cur_ctr = S.ctr + 8 * cur;
       P.cur_chunks = S.chunks ? S.chunks + cur * chunk_cap : nullptr;
       P.cur_list = S.list + (int64_t)cur * A->nb;
+      P.cur_fbits = S.fbits + (int64_t)cur * fw;
       P.level = (int32_t)l;
       if (timing) BFS_TRY(hipEventRecord(A->ev[2 + 2 * i], s));
       if (A->vk == VK_F32) {
@@ -497,7 +537,7 @@ dbs_status bfs_run(dbs_matrix *A, const BfsScratch &S, int32_t src, int32_t *lev
       if (timing) BFS_TRY(hipEventRecord(A->ev[3 + 2 * i], s));
       hipLaunchKernelGGL(k_bfs_meta, dim3(mgrid), dim3(dbs_meta::MT), 0, s, (const uint32_t *)P.next_bm, A->nb,
                          reg_for(nxt), S.bm + clr * nwords, S.ctr + 8 * clr, nwords,
-                         (const uint32_t *)P.cur_ctr);
+                         (const uint32_t *)P.cur_ctr, S.fbits + (int64_t)nxt * fw);
       BFS_TRY(hipGetLastError());
     }
     BFS_TRY(hipMemcpyAsync(S.host, P.hist, B * 4, hipMemcpyDeviceToHost, s));
@@ -604,6 +644,7 @@ size_t carve(const dbs_matrix *A, bool list_push, uint8_t *base, BfsScratch &S) 
   S.bm = (uint32_t *)take((size_t)(3 * nwords + 1) * 4);
   S.vis = (uint32_t *)take((size_t)(nwords + 1) * 4);
   S.list = (uint32_t *)take((size_t)(3 * (int64_t)A->nb + 1) * 4);
+  S.fbits = (uint32_t *)take((size_t)(3 * (((int64_t)A->nb + 63) / 64) + 1) * 4);
   S.ctr = (uint32_t *)take((size_t)(24 + dbs_matrix::kBfsBatch + 1) * 4);
   S.chunks = list_push ? nullptr : (uint64_t *)take((size_t)(3 * A->max_chunks + 1) * 8);
   return off;

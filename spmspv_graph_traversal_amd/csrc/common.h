@@ -192,6 +192,7 @@ struct dbs_matrix {
   // BFS scratch (allocated on first use)
   uint32_t *bfs_bm;      // 3 frontier bitmaps of nb/2 words (16 bits per vertex block)
   uint32_t *bfs_vis;     // visited bitmap
+  uint32_t *bfs_fbits;   // 3 x ceil(nb/64) words: a bit per nonzero word of each frontier bitmap
   uint32_t *bfs_list;    // 3 lists of nb vertex blocks
   uint64_t *bfs_chunks;  // 3 chunk lists
   uint32_t *bfs_ctr;     // 3 x 8 counters, then the frontier sizes of one batch of levels
