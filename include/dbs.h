@@ -290,7 +290,9 @@ enum {
   DBS_ARR_CSC2CSR = 5,     /* uint32[T]      global_block_csc2csr */
   DBS_ARR_PAYLOAD = 6,     /* uint8[]        tile payload arena */
   DBS_ARR_SEGMENTS = 7,    /* uint32[4*S]    {row block | split<<31 | drain<<30 | slot
-                                             class<<28, t0, t1, partial slot + 1 or 0} */
+                                             class<<28, t0, t1, partial slot + 1 or 0}:
+                                             value matrices: the segments of class 3 first, by
+                                             first column block, then the others by row block */
   DBS_ARR_XMASK = 8,       /* uint16[nb]     blk_x_mask of the last call */
   DBS_ARR_ACTIVE = 9,      /* uint32[N_nzblk] nonzero vector blocks of the last call (any order) */
   DBS_ARR_CSC_CM = 10,     /* uint16[T]      columns of each tile that hold entries, CSC order */
