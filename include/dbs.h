@@ -296,8 +296,12 @@ enum {
   DBS_ARR_XMASK = 8,       /* uint16[nb]     blk_x_mask of the last call */
   DBS_ARR_ACTIVE = 9,      /* uint32[N_nzblk] nonzero vector blocks of the last call (any order) */
   DBS_ARR_CSC_CM = 10,     /* uint16[T]      columns of each tile that hold entries, CSC order */
-  DBS_ARR_PAT_SEGS = 11    /* uint32[4*S']   pattern matrices: Boolean-pull segments {first row
+  DBS_ARR_PAT_SEGS = 11,   /* uint32[4*S']   pattern matrices: Boolean-pull segments {first row
                                              block, t0, t1, row blocks}, in launch order */
+  DBS_ARR_T_CBX = 12       /* uint32[T]      pattern matrices of at most 2^19 column blocks
+                                             (else empty): column block | row block in its
+                                             Boolean-pull segment<<19 | one entry<<23 | that
+                                             entry's (row<<4 | column)<<24 */
 };
 dbs_status dbs_copy_array(dbs_handle A, int32_t which, void *dst, int64_t capacity,
                           int64_t *bytes_out);

@@ -38,6 +38,7 @@ constexpr int KT = 256;
 
 struct BfsParams {
   const uint32_t *t_cb;
+  const uint32_t *t_cbx;  // pattern matrices with nb <= CBX_MAX_NB, else null
   const uint64_t *t_meta;
   const uint32_t *cb_ptr;
   const uint32_t *csc_rb;
@@ -269,9 +270,15 @@ __global__ __launch_bounds__(KT, VK == VK_PAT ? 5 : 1) void k_bfs_level(BfsParam
     R.bm = make_rsrc(P.cur_bm, (uint64_t)((P.nb + 1) / 2) * 4);
     if constexpr (VK == VK_PAT) {
       const uint32_t *sg = P.phase == 0 ? P.psegs : P.psegs + 4 * P.nseg0;
-      const PatSrc S{P.t_cb, P.t_meta, sg, P.phase == 0 ? P.nseg0 : P.npseg - P.nseg0,
+      const PatSrc S{P.t_cb,
+                     P.t_meta,
+                     sg,
+                     P.phase == 0 ? P.nseg0 : P.npseg - P.nseg0,
                      make_rsrc(P.payload, (uint64_t)P.payload_bytes + DBS_PAYLOAD_SLACK),
-                     make_rsrc(P.wown, (uint64_t)(P.payload_bytes + DBS_PAYLOAD_SLACK) / 4)};
+                     make_rsrc(P.wown, (uint64_t)(P.payload_bytes + DBS_PAYLOAD_SLACK) / 4),
+                     P.t_cbx ? P.t_cbx : P.t_cb,
+                     P.t_cbx ? (uint32_t)(CBX_MAX_NB - 1) : ~0u,
+                     P.t_cbx ? CBX_SINGLE : 0u};
       const brsrc_t rv = make_rsrc(P.vis, (uint64_t)((P.nb + 1) / 2) * 4);
       if (!eager && P.fw <= dbs_meta::PUSH_LIST_MAX) {  // uniform
         // the frontier's word bits in the push enumeration's LDS
@@ -465,6 +472,7 @@ dbs_status bfs_run(dbs_matrix *A, const BfsScratch &S, int32_t src, int32_t *lev
 
   BfsParams P;
   P.t_cb = A->t_cb;
+  P.t_cbx = A->t_cbx;
   P.t_meta = A->t_meta;
   P.cb_ptr = A->cb_ptr;
   P.csc_rb = A->csc_rb;

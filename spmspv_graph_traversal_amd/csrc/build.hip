@@ -673,6 +673,20 @@ __global__ void k_word_owner(const uint32_t *psegs, int64_t npseg, const uint32_
   }
 }
 
+// Column-block words of the Boolean pull (pattern matrices with at most
+// CBX_MAX_NB column blocks): column block, row block within the segment (set
+// in the metadata word by k_word_owner), and the coordinates of a tile of one
+// entry (inline: its first coordinate byte).  One thread per tile.
+__global__ void k_cbx(const uint32_t *t_cb, const uint64_t *t_meta, int64_t T, uint32_t *t_cbx) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T) return;
+  const uint64_t meta = t_meta[t];
+  const bool single = meta_type(meta) == DBS_TILE_COO && meta_nnz(meta) == 1u && meta_inline(meta);
+  uint32_t w = t_cb[t] | ((uint32_t)((meta >> META_SEG_RB_SHIFT) & 15u) << CBX_RI_SHIFT);
+  if (single) w |= CBX_SINGLE | (((uint32_t)meta & 0xFFu) << CBX_RC_SHIFT);
+  t_cbx[t] = w;
+}
+
 // Segments of the Boolean pull (pattern matrices), in the order it runs
 // them: first, one segment per run of consecutive short row blocks (a
 // single segment each above; at most PAT_MAX_RB row blocks and seg_cap tiles
@@ -1099,6 +1113,12 @@ dbs_status dbs_build_impl(dbs_matrix *A, const int32_t *row_ptr, const int32_t *
                          A->npseg, (const uint32_t *)A->rb_ptr, (uint64_t *)A->t_meta, A->wown);
       BUILD_TRY(hipGetLastError());
       BUILD_TRY(order_by_cost(A, tmp, s));
+    }
+    if (A->nb <= CBX_MAX_NB && T > 0) {
+      BUILD_TRY(dbs_dev_alloc(A, (void **)&A->t_cbx, (size_t)T * 4));
+      hipLaunchKernelGGL(k_cbx, dim3(nblocks(T, BT)), dim3(BT), 0, s, (const uint32_t *)A->t_cb,
+                         (const uint64_t *)A->t_meta, T, A->t_cbx);
+      BUILD_TRY(hipGetLastError());
     }
   }
 

@@ -21,6 +21,12 @@ struct PatSrc {
   int64_t nseg;
   brsrc_t pay;  // payload and its zeroed slack
   brsrc_t own;  // per payload word of a COO tile: the tile's index in its segment
+  // the column-block words the Boolean pull reads: with CBX_SINGLE set, a
+  // tile of one entry carries it in its word (else the plain column blocks,
+  // and no tile is marked)
+  const uint32_t *t_cbx = nullptr;
+  uint32_t cbm = ~0u;  // column block of a word
+  uint32_t sbit = 0u;  // CBX_SINGLE, or 0
 };
 
 template <int U>
@@ -73,7 +79,7 @@ template <int K>
 struct PatSeg {  // stage A: descriptor, column blocks, metadata (n == 0: no segment)
   uint32_t rb, t0, n, nrb;  // first row block, first tile, tiles, row blocks (uniform)
   uint32_t needl;           // lane j < nrb: rows wanted in row block rb + j
-  uint32_t cb[K];
+  uint32_t cb[K];  // column-block words
   uint64_t meta[K];
 };
 
@@ -151,7 +157,7 @@ DBS_DEV void patk_issue(const PatSrc &S, const Pol &pol, int64_t stride, int lan
   r.t0 = t0;
   r.nrb = nrb;
   r.n = any ? t1 - t0 : 0u;
-  const brsrc_t rcb = make_rsrc(S.t_cb + t0, (uint64_t)r.n * 4u);
+  const brsrc_t rcb = make_rsrc(S.t_cbx + t0, (uint64_t)r.n * 4u);
   const brsrc_t rmt = make_rsrc(S.t_meta + t0, (uint64_t)r.n * 8u);
 #pragma unroll
   for (int k = 0; k < K; ++k) {
@@ -352,7 +358,7 @@ DBS_DEV void pattern_pull_wave(const PatSrc &S, const Pol &pol, int64_t s0, int6
   const uint32_t l4 = (uint32_t)lane * 4u, l8 = (uint32_t)lane * 8u;
   auto masks = [&](const PatSeg<K> &a, PatMasks<K> &b) {
 #pragma unroll
-    for (int k = 0; k < K; ++k) b.m[k] = pol.mask(a.cb[k], 64u * k + (uint32_t)lane < a.n);
+    for (int k = 0; k < K; ++k) b.m[k] = pol.mask(a.cb[k] & S.cbm, 64u * k + (uint32_t)lane < a.n);
     if constexpr (EAGER) pat_words<K, true>(S, a, b, lane, l4);
   };
   SegWin w;
@@ -382,11 +388,193 @@ DBS_DEV void pattern_pull_wave(const PatSrc &S, const Pol &pol, int64_t s0, int6
   }
 }
 
+// ---------------------------------------------------------------------------
+// Very sparse x (a few percent of the vector blocks active, active-block
+// bits in LDS).  A segment then holds a handful of active tiles, and the
+// per-segment finish above (ballots, decode and writeback of every slice)
+// is mostly idle work.  Here a wave only tests each tile's column block
+// against the active-block bits and queues the active tiles (tile, column
+// block, the segment's first row block) in an LDS ring; every 64 queued
+// tiles are finished together, one tile per lane: its mask word and
+// metadata, then its coordinates (inline, its coordinate words, or the 16
+// row masks of a larger tile), and the found rows go straight to the
+// policy (a row block of a tile is its segment's first plus the offset in
+// bits 52..55 of its metadata word).  Column blocks of the next two
+// segments are in flight while one is tested.
+// ---------------------------------------------------------------------------
+constexpr uint32_t PAT_Q = 128;  // ring entries: 64 queued at most before a batch, plus one slice
+
+template <int K>
+struct ScanSeg {
+  uint32_t rb, t0, n;  // first row block, first tile, tiles (uniform; n == 0: no segment)
+  uint32_t cb[K];      // column-block words
+};
+
+template <int K, class Pol>
+DBS_DEV void scan_issue(const PatSrc &S, const Pol &pol, int64_t stride, int lane, SegWin &w, uint32_t l4,
+                        ScanSeg<K> &r) {
+  uint32_t rb = 0, t0 = 0, t1 = 0, nrb = 1;
+  const bool any = win_next(S, pol, stride, lane, w, rb, t0, t1, nrb);
+  r.rb = rb;
+  r.t0 = t0;
+  r.n = any ? t1 - t0 : 0u;
+  const brsrc_t rcb = make_rsrc(S.t_cbx + t0, (uint64_t)r.n * 4u);
+#pragma unroll
+  for (int k = 0; k < K; ++k) r.cb[k] = __builtin_amdgcn_raw_buffer_load_b32(rcb, l4 + 256u * k, 0, 0);
+}
+
+// A batch of queued tiles (n <= 64, lane j holding the j-th): its mask
+// words and the metadata of its tiles of more than one entry are loaded when
+// it leaves the ring, and it is finished when the next batch leaves (or at
+// the end), so its loads are in flight while the wave scans on.
+struct SpBatch {
+  uint32_t n;  // tiles (uniform; 0: none)
+  uint32_t rb0, cbx, w;
+  uint64_t meta;
+};
+
+template <class Pol>
+DBS_DEV void sp_issue(const PatSrc &S, const Pol &pol, const uint32_t *q, uint32_t head, uint32_t n, int lane,
+                      SpBatch &b) {
+  const bool in = (uint32_t)lane < n;
+  const uint32_t i = (head + (uint32_t)lane) & (PAT_Q - 1u);
+  const uint32_t t = q[i];
+  b.n = n;
+  b.cbx = q[PAT_Q + i];
+  b.rb0 = q[2 * PAT_Q + i];
+  b.w = pol.mask_raw(b.cbx & S.cbm, in);
+  // idle lanes and tiles of one entry repeat lane 0's tile (no extra line)
+  b.meta = S.t_meta[(in & ((b.cbx & S.sbit) == 0u)) ? t : q[head & (PAT_Q - 1u)]];
+}
+
+// found rows of a batch's tiles: a tile of one entry from its column-block
+// word; inline COO tiles from the metadata word; the coordinate words of the
+// other COO tiles are read 16 entries per 16-byte load (the words past a
+// tile's end are not decoded), the 16 row masks of the larger tiles in two
+// loads.  The rows found go to the wave's found-row buffer.
+template <class Pol>
+DBS_DEV void sp_finish(const PatSrc &S, const Pol &pol, const SpBatch &b, int lane, FoundBuf &fb, int cap) {
+  const bool in = (uint32_t)lane < b.n;
+  const uint32_t m = in ? pol.mask_of(b.w, b.cbx & S.cbm) : 0u;
+  const bool single = (b.cbx & S.sbit) != 0u;
+  const uint32_t lo = (uint32_t)b.meta, hi = (uint32_t)(b.meta >> 32);
+  const uint32_t kind = meta_kind(hi);
+  const bool live = (m != 0u) & !single;
+  const uint32_t rc = b.cbx >> CBX_RC_SHIFT;
+  uint32_t f = single ? ((m >> (rc & 15u)) & 1u) << (rc >> 4) : 0u;
+  f |= (live & (kind == (DBS_TILE_COO | 8u))) ? coo_or4(lo, m) : 0u;
+  const uint32_t nw = (live & (kind == DBS_TILE_COO)) ? ((hi >> 8) & 0xFFu) / 4u + 1u : 0u;
+  const bool big = live & (meta_type(b.meta) != DBS_TILE_COO);
+  const uint32_t nq = wave_max((nw + 3u) >> 2);  // uniform
+  for (uint32_t j0 = 0; j0 < nq; j0 += 4u) {
+    uint32_t wd[4][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t jq = j0 + (uint32_t)u;
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(S.pay, 4u * jq < nw ? lo + 16u * jq : OOB_OFF, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) wd[u][e] = v[e];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f |= (4u * (j0 + (uint32_t)u) + (uint32_t)e < nw) ? coo_or4(wd[u][e], m) : 0u;
+  }
+  if (__ballot(big) != 0ull) {  // uniform
+    const uint32_t o = big ? lo : OOB_OFF;
+    const auto x = __builtin_amdgcn_raw_buffer_load_b128(S.pay, o, 0, 0);
+    const auto y = __builtin_amdgcn_raw_buffer_load_b128(S.pay, big ? o + 16u : OOB_OFF, 0, 0);
+    const uint32_t rm[8] = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+    uint32_t g = 0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) g |= ((((rm[r >> 1] >> (16 * (r & 1))) & m) + 0xFFFFu) >> 16) << r;
+    f |= big ? g : 0u;
+  }
+  const uint64_t any = __ballot(f != 0u);
+  if (f != 0u) {
+    const int pos = fb.n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(any >> 32),
+                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)any, 0u));
+    const uint32_t ri = single ? (b.cbx >> CBX_RI_SHIFT) & 15u : (hi >> (META_SEG_RB_SHIFT - 32)) & 15u;
+    fb.rb[pos] = b.rb0 + ri;
+    fb.f[pos] = f;
+  }
+  fb.n += __popcll(any);
+  if (fb.n > cap - 64) {  // uniform: no room for another batch
+    __syncwarp();
+    pol.flush(fb.rb, fb.f, fb.n, lane);
+    __syncwarp();
+    fb.n = 0;
+  }
+}
+
+// LDS per wave of the very sparse pull: the ring (tile, column block, row
+// block), and apart from it the found-row buffer (2 x SP_FOUND_CAP words)
+constexpr int SP_FOUND_CAP = 128;
+constexpr int SP_LDS_WORDS = 3 * (int)PAT_Q;
+
+template <int K, class Pol>
+DBS_DEV void pattern_pull_sparse(const PatSrc &S, const Pol &pol, int64_t s0, int64_t stride, int lane,
+                                 uint32_t *q, uint32_t *found) {
+  if (s0 >= S.nseg) return;
+  const uint32_t l4 = (uint32_t)lane * 4u;
+  FoundBuf fb{found, found + SP_FOUND_CAP, 0};
+  SegWin w;
+  w.next = s0;
+  w.live = 0ull;
+  ScanSeg<K> a0, a1, a2;
+  scan_issue<K>(S, pol, stride, lane, w, l4, a0);
+  scan_issue<K>(S, pol, stride, lane, w, l4, a1);
+  SpBatch pb;
+  pb.n = 0u;
+  uint32_t head = 0u, qn = 0u;  // uniform
+  while (a0.n != 0u) {
+    scan_issue<K>(S, pol, stride, lane, w, l4, a2);
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      if (64u * k >= a0.n) break;  // uniform
+      const bool act = (64u * k + (uint32_t)lane < a0.n) & pol.active(a0.cb[k] & S.cbm);
+      const uint64_t bal = __ballot(act);
+      if (bal != 0ull) {  // uniform
+        const uint32_t pos =
+            (head + qn + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u))) &
+            (PAT_Q - 1u);
+        if (act) {
+          q[pos] = a0.t0 + 64u * k + (uint32_t)lane;
+          q[PAT_Q + pos] = a0.cb[k];
+          q[2 * PAT_Q + pos] = a0.rb;
+        }
+        qn += (uint32_t)__popcll(bal);
+        if (qn >= 64u) {  // uniform
+          __syncwarp();
+          if (pb.n != 0u) sp_finish(S, pol, pb, lane, fb, SP_FOUND_CAP);
+          sp_issue(S, pol, q, head, 64u, lane, pb);
+          __syncwarp();
+          head = (head + 64u) & (PAT_Q - 1u);
+          qn -= 64u;
+        }
+      }
+    }
+    a0 = a1;
+    a1 = a2;
+  }
+  __syncwarp();
+  if (pb.n != 0u) sp_finish(S, pol, pb, lane, fb, SP_FOUND_CAP);
+  if (qn != 0u) {
+    sp_issue(S, pol, q, head, qn, lane, pb);
+    sp_finish(S, pol, pb, lane, fb, SP_FOUND_CAP);
+  }
+  if (fb.n != 0) {
+    __syncwarp();
+    pol.flush(fb.rb, fb.f, fb.n, lane);
+  }
+}
+
 constexpr int PAT_K = DBS_PAT_SEG_CAP / 64;  // slices of 64 tiles per pattern-pull segment
 
 // LDS per wave: masks of a segment's tiles (64*K), found rows per row block,
-// the found-row buffer (2 x PAT_FOUND_CAP)
+// the found-row buffer (2 x PAT_FOUND_CAP); or the very sparse pull's ring
 constexpr int PAT_LDS_WORDS = 64 * PAT_K + PAT_MAX_RB + 2 * PAT_FOUND_CAP;
+static_assert(PAT_LDS_WORDS >= SP_LDS_WORDS, "the very sparse pull's ring takes the same LDS");
 
 // LAZY_ONLY: the policy is only used with the metadata of the active tiles
 // (no instantiation for `eager`)

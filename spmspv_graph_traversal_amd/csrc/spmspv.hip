@@ -195,6 +195,7 @@ __global__ void k_fill_u32(uint32_t *p, int64_t n, uint32_t v) {
 
 struct SpmvParams {
   const uint32_t *t_cb;
+  const uint32_t *t_cbx;  // pattern matrices with nb <= CBX_MAX_NB, else null
   const uint64_t *t_meta;
   const uint32_t *cb_ptr;
   const uint32_t *csc_rb;
@@ -321,6 +322,10 @@ DBS_DEV void push_chunk(const SpmvParams &P, uint64_t own, float *sx, float *spa
 constexpr int PULL_U_PLUS_WIDE = 4;  // segments per wave step, PLUS_TIMES pull with many segments
 constexpr int PLUS_MAX_PARTS = DBS_MAX_SHARE;  // waves sharing one PLUS_TIMES pull segment at most
 constexpr int PULL_U_OR = 8;    // segments per wave step, OR_AND pull (value matrices)
+// Boolean pull with the active-block bits in LDS: up to SP_BITS_MAX words of
+// bits leave room in the same LDS for the very sparse pull's found-row
+// buffers, one per wave
+constexpr int SP_BITS_MAX = dbs_meta::PUSH_LIST_MAX - (KT / DBS_WAVE) * 2 * SP_FOUND_CAP;
 
 // ---------------------------------------------------------------------------
 // PLUS_TIMES over the COO tiles of the U pull segments of a wave step,
@@ -689,8 +694,15 @@ struct OrPol {
   const uint32_t *bits;  // FILTER: LDS, a bit per column block
   DBS_DEV uint32_t need_v(uint32_t, bool) const { return 0xFFFFu; }
   DBS_DEV uint32_t mask(uint32_t cb, bool in) const {
-    if constexpr (FILTER) in = in && ((bits[cb >> 5] >> (cb & 31u)) & 1u);  // idle lanes hold cb 0
-    const uint32_t w = bld32(xmask, in ? cb * 4u : OOB_OFF);
+    if constexpr (FILTER) in = in && active(cb);  // idle lanes hold cb 0
+    return mask_of(mask_raw(cb, in), cb);
+  }
+  // the column block is active this call (its LDS bit)
+  DBS_DEV bool active(uint32_t cb) const { return (bits[cb >> 5] >> (cb & 31u)) & 1u; }
+  // the mask word as loaded, and the mask it gives (split so that the load
+  // can stay in flight)
+  DBS_DEV uint32_t mask_raw(uint32_t cb, bool in) const { return bld32(xmask, in ? cb * 4u : OOB_OFF); }
+  DBS_DEV uint32_t mask_of(uint32_t w, uint32_t) const {
     return ((w >> 16) == epoch) ? (w & 0xFFFFu) : 0u;  // an idle lane reads 0: no epoch
   }
   // found rows of n row blocks (LDS): four row blocks per pass, a lane per row
@@ -811,14 +823,23 @@ __global__ __launch_bounds__(KT, ((VK == VK_BF16 && SR == DBS_PLUS_TIMES && PU =
       R.pay = make_rsrc(P.payload, (uint64_t)P.payload_bytes + DBS_PAYLOAD_SLACK);
       R.xmask = make_rsrc(P.xmask, (uint64_t)P.nb * 4);
       if constexpr (VK == VK_PAT) {
-        const PatSrc S{P.t_cb, P.t_meta, P.segs, P.nseg, R.pay,
-                       make_rsrc(P.wown, (uint64_t)(P.payload_bytes + DBS_PAYLOAD_SLACK) / 4)};
+        const PatSrc S{P.t_cb,
+                       P.t_meta,
+                       P.segs,
+                       P.nseg,
+                       R.pay,
+                       make_rsrc(P.wown, (uint64_t)(P.payload_bytes + DBS_PAYLOAD_SLACK) / 4),
+                       P.t_cbx ? P.t_cbx : P.t_cb,
+                       P.t_cbx ? (uint32_t)(CBX_MAX_NB - 1) : ~0u,
+                       P.t_cbx ? CBX_SINGLE : 0u};
         if (!eager && P.xbits) {  // uniform
           // the active-block bits in the push enumeration's LDS
           for (int i = (int)threadIdx.x; i < P.nbw; i += KT) s_cum[i] = P.xbits[i];
           __syncthreads();
           const OrPol<true> pol{R.xmask, P.epoch, P.m, (uint8_t *)P.y, s_cum};
-          pattern_pull<true>(S, pol, gw, nw, false, lane, s_pat[w]);
+          if (P.nbw <= SP_BITS_MAX)  // uniform: the found-row buffers fit after the bits
+            pattern_pull_sparse<PAT_K>(S, pol, gw, nw, lane, s_pat[w], s_cum + SP_BITS_MAX + w * 2 * SP_FOUND_CAP);
+          else pattern_pull<true>(S, pol, gw, nw, false, lane, s_pat[w]);
         } else {
           const OrPol<false> pol{R.xmask, P.epoch, P.m, (uint8_t *)P.y, nullptr};
           pattern_pull(S, pol, gw, nw, eager, lane, s_pat[w]);
@@ -1092,6 +1113,7 @@ dbs_status dbs_spmspv_impl(dbs_matrix *A, int32_t nnz_x, const int32_t *x_idx, c
   P.T = A->T;
   P.payload_bytes = A->payload_bytes;
   P.t_cb = A->t_cb;
+  P.t_cbx = A->t_cbx;
   P.t_meta = A->t_meta;
   P.cb_ptr = A->cb_ptr;
   P.csc_rb = A->csc_rb;

@@ -41,7 +41,7 @@ def check_pattern_segments(dbs, A, ar, tv, cap):
     T = int(tv["T"])
     if T == 0:
         assert ps.shape[0] == 0
-        return
+        return np.zeros(0, np.int64), np.zeros(0, np.int64)
     rbp = tv["rb_ptr"].astype(np.int64)
     rb0, t0, t1, nrb = ps[:, 0], ps[:, 1], ps[:, 2], ps[:, 3]
     assert np.all(t1 > t0) and np.all((nrb >= 1) & (nrb <= 16))
@@ -57,6 +57,33 @@ def check_pattern_segments(dbs, A, ar, tv, cap):
     assert np.all((ri >= 0) & (ri < nrb[seg_of]))
     bits = ((ar["t_meta"] >> np.uint64(52)) & np.uint64(15)).astype(np.int64)
     np.testing.assert_array_equal(bits[tiles], ri)
+    return tiles, ri
+
+
+def check_cbx(dbs, A, tv, exp_types, tiles, ri, nb):
+    """Column-block words of the Boolean pull: with at most 2^19 column
+    blocks, column block | row block in the segment << 19, and for a COO
+    tile of one entry bit 23 and that entry's (row << 4 | column) << 24;
+    none above 2^19."""
+    cbx = dbs.dbs_copy_array(A, dbs.DBS_ARR_T_CBX)
+    T = int(tv["T"])
+    if nb > 1 << 19 or T == 0:
+        assert cbx.shape[0] == 0
+        return
+    assert cbx.shape[0] == T
+    cbx = cbx.astype(np.int64)
+    np.testing.assert_array_equal(cbx & ((1 << 19) - 1), tv["t_cb"].astype(np.int64))
+    ri_t = np.zeros(T, np.int64)
+    ri_t[tiles] = ri
+    np.testing.assert_array_equal((cbx >> 19) & 15, ri_t)
+    single = (exp_types == orc.COO) & (tv["t_nnz"] == 1)
+    np.testing.assert_array_equal((cbx >> 23) & 1, single.astype(np.int64))
+    # the entry of a one-entry tile from the oracle's per-row column masks
+    rm = tv["t_rowmask"].reshape(-1, 16).astype(np.int64)[single]
+    r = np.argmax(rm != 0, axis=1)
+    c = np.log2(rm[np.arange(rm.shape[0]), r]).astype(np.int64)
+    np.testing.assert_array_equal(cbx[single] >> 24, r * 16 + c)
+    assert not (cbx[~single] >> 24).any()
 
 
 def check_format(dbs, m, n, rp, ci, vbits, dtype, vk, opt=None, th=(32, 128, 2.0), force=-1, cap=None):
@@ -131,7 +158,8 @@ def check_format(dbs, m, n, rp, ci, vbits, dtype, vk, opt=None, th=(32, 128, 2.0
         assert not ((segs[:, 0] >> 30) & 1).any()
     np.testing.assert_array_equal(segs[:, 3], slot[order])
     if vk == 2:
-        check_pattern_segments(dbs, A, ar, tv, cap)
+        tiles, ri = check_pattern_segments(dbs, A, ar, tv, cap)
+        check_cbx(dbs, A, tv, exp_types, tiles, ri, (n + 15) // 16)
     for f in range(5):
         assert st["tiles_by_format"][f] == int(np.count_nonzero(exp_types == f))
         assert st["nnz_by_format"][f] == int(tv["t_nnz"][exp_types == f].sum())
@@ -178,6 +206,22 @@ def test_uniform_tiny_config(dbs):
 def test_rmat_pattern(dbs):
     rp, ci = rmat_csr(11, 16, rng_for("test", 600))
     check_format(dbs, 2048, 2048, rp, ci, None, dbs.DBS_PATTERN, 2)
+
+
+@pytest.mark.parametrize("nb", [1 << 19, (1 << 19) + 1])
+def test_pattern_column_block_words_limit(dbs, nb):
+    """The pull's column-block words exist up to 2^19 column blocks (the
+    last one included) and not beyond; the format is the same either way."""
+    n = 16 * nb
+    g = rng_for("test", 606, nb)
+    m = 40
+    per = g.integers(0, 9, size=m)
+    rows = [np.sort(g.choice(n, size=int(k), replace=False)) for k in per]
+    rows[7] = np.array([0, 5, n - 1])  # the first and the last column block
+    rp = np.zeros(m + 1, np.int32)
+    rp[1:] = np.cumsum([r.shape[0] for r in rows])
+    ci = np.concatenate(rows).astype(np.int32)
+    check_format(dbs, m, n, rp, ci, None, dbs.DBS_PATTERN, 2)
 
 
 def test_decode_weight_bf16(dbs):
