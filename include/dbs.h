@@ -298,10 +298,17 @@ enum {
   DBS_ARR_CSC_CM = 10,     /* uint16[T]      columns of each tile that hold entries, CSC order */
   DBS_ARR_PAT_SEGS = 11,   /* uint32[4*S']   pattern matrices: Boolean-pull segments {first row
                                              block, t0, t1, row blocks}, in launch order */
-  DBS_ARR_T_CBX = 12       /* uint32[T]      pattern matrices of at most 2^19 column blocks
-                                             (else empty): column block | row block in its
-                                             Boolean-pull segment<<19 | one entry<<23 | that
-                                             entry's (row<<4 | column)<<24 */
+  DBS_ARR_T_CBX = 12,      /* uint32[T]      pattern matrices, the Boolean pull's column-block
+                                             words: at most 2^19 column blocks: column block |
+                                             row block in its Boolean-pull segment<<19 | (one
+                                             entry<<23 | that entry's (row<<4 | column)<<24, or
+                                             else the tile's index among its segment's tiles of
+                                             more than one entry<<24); more: column block | that
+                                             row block<<27 */
+  DBS_ARR_META2 = 13,      /* uint64[T']     pattern matrices: the T_META words of the tiles
+                                             without bit 23 in T_CBX, in tile order */
+  DBS_ARR_PAT_M2 = 14      /* uint32[2*S']   per Boolean-pull segment (PAT_SEGS order): its
+                                             first entry in META2, and its entries */
 };
 dbs_status dbs_copy_array(dbs_handle A, int32_t which, void *dst, int64_t capacity,
                           int64_t *bytes_out);

@@ -31,14 +31,14 @@ DBS_OPT_PULL_WIDTH, DBS_OPT_PULL_SHARE = 6, 7
 # exported arrays
 (DBS_ARR_RB_PTR, DBS_ARR_T_CB, DBS_ARR_T_META, DBS_ARR_CB_PTR, DBS_ARR_CSC_RB, DBS_ARR_CSC2CSR,
  DBS_ARR_PAYLOAD, DBS_ARR_SEGMENTS, DBS_ARR_XMASK, DBS_ARR_ACTIVE, DBS_ARR_CSC_CM, DBS_ARR_PAT_SEGS,
- DBS_ARR_T_CBX) = range(13)
+ DBS_ARR_T_CBX, DBS_ARR_META2, DBS_ARR_PAT_M2) = range(15)
 
 _ARR_DTYPES = {
     DBS_ARR_RB_PTR: np.uint32, DBS_ARR_T_CB: np.uint32, DBS_ARR_T_META: np.uint64,
     DBS_ARR_CB_PTR: np.uint32, DBS_ARR_CSC_RB: np.uint32, DBS_ARR_CSC2CSR: np.uint32,
     DBS_ARR_PAYLOAD: np.uint8, DBS_ARR_SEGMENTS: np.uint32, DBS_ARR_XMASK: np.uint16,
     DBS_ARR_ACTIVE: np.uint32, DBS_ARR_CSC_CM: np.uint16, DBS_ARR_PAT_SEGS: np.uint32,
-    DBS_ARR_T_CBX: np.uint32,
+    DBS_ARR_T_CBX: np.uint32, DBS_ARR_META2: np.uint64, DBS_ARR_PAT_M2: np.uint32,
 }
 
 

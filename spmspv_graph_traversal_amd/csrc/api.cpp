@@ -66,7 +66,8 @@ hipError_t fold_all(dbs_matrix *A) {
 
 void free_all(dbs_matrix *A) {
   void *bufs[] = {A->rb_ptr, A->t_cb,     A->t_meta,   A->cb_ptr,     A->csc_rb,  A->csc2csr, A->csc_cm,
-                  A->payload, A->segs,    A->psegs,    A->t_cbx,   A->wown,    A->rows_nz,  A->xmask,    A->xbits,      A->xd,
+                  A->payload, A->segs,    A->psegs,    A->t_cbx,   A->m2seg,   A->wown,
+                  A->meta2 != A->t_meta ? A->meta2 : nullptr,    A->rows_nz,  A->xmask,    A->xbits,      A->xd,
                   A->act_list, A->chunks,
                   A->ctr,    A->bfs_bm,   A->bfs_vis,  A->bfs_fbits, A->bfs_list,   A->bfs_chunks, A->bfs_ctr,
                   A->fin,    A->partial};
@@ -359,6 +360,8 @@ dbs_status dbs_copy_array(dbs_handle A, int32_t which, void *dst, int64_t capaci
     case DBS_ARR_SEGMENTS: src = A->segs; bytes = A->nseg * 16; break;
     case DBS_ARR_PAT_SEGS: src = A->psegs; bytes = A->psegs ? A->npseg * 16 : 0; break;
     case DBS_ARR_T_CBX: src = A->t_cbx; bytes = A->t_cbx ? A->T * 4 : 0; break;
+    case DBS_ARR_META2: src = A->meta2; bytes = A->meta2 ? A->nmeta2 * 8 : 0; break;
+    case DBS_ARR_PAT_M2: src = A->m2seg; bytes = A->m2seg ? A->npseg * 8 : 0; break;
     case DBS_ARR_XMASK: src = A->xmask; bytes = (int64_t)A->nb * 2; break;
     case DBS_ARR_ACTIVE: {
       dbs_stats tmp;

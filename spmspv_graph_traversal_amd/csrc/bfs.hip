@@ -38,7 +38,10 @@ constexpr int KT = 256;
 
 struct BfsParams {
   const uint32_t *t_cb;
-  const uint32_t *t_cbx;  // pattern matrices with nb <= CBX_MAX_NB, else null
+  const uint32_t *t_cbx;   // pattern matrices: the Boolean pull's column-block words
+  const uint64_t *meta2;   // pattern matrices: metadata of the tiles not marked single
+  const uint32_t *m2seg;   // pattern matrices: per pull segment, first entry in meta2 and entries
+  bool cbx_compact;        // nb <= CBX_MAX_NB: the words mark single tiles
   const uint64_t *t_meta;
   const uint32_t *cb_ptr;
   const uint32_t *csc_rb;
@@ -239,7 +242,7 @@ struct BfsPol {
 // pattern matrices: five waves per SIMD (at most 96 VGPRs), as the Boolean
 // SpMSpV pull
 template <int VK>
-__global__ __launch_bounds__(KT, VK == VK_PAT ? 5 : 1) void k_bfs_level(BfsParams P) {
+__global__ __launch_bounds__(KT, VK == VK_PAT ? 4 : 1) void k_bfs_level(BfsParams P) {
   __shared__ uint32_t s_pat[VK == VK_PAT ? KT / DBS_WAVE : 1][PAT_LDS_WORDS];
   __shared__ uint32_t s_cum[dbs_meta::PUSH_LIST_MAX];
   const int lane = __lane_id();
@@ -276,9 +279,12 @@ __global__ __launch_bounds__(KT, VK == VK_PAT ? 5 : 1) void k_bfs_level(BfsParam
                      P.phase == 0 ? P.nseg0 : P.npseg - P.nseg0,
                      make_rsrc(P.payload, (uint64_t)P.payload_bytes + DBS_PAYLOAD_SLACK),
                      make_rsrc(P.wown, (uint64_t)(P.payload_bytes + DBS_PAYLOAD_SLACK) / 4),
-                     P.t_cbx ? P.t_cbx : P.t_cb,
-                     P.t_cbx ? (uint32_t)(CBX_MAX_NB - 1) : ~0u,
-                     P.t_cbx ? CBX_SINGLE : 0u};
+                     P.t_cbx,
+                     P.cbx_compact ? (uint32_t)(CBX_MAX_NB - 1) : (1u << CBX_RI_SHIFT_WIDE) - 1u,
+                     P.cbx_compact ? CBX_SINGLE : 0u,
+                     P.cbx_compact ? (uint32_t)CBX_RI_SHIFT : (uint32_t)CBX_RI_SHIFT_WIDE,
+                     P.meta2,
+                     (const uint2 *)P.m2seg + (P.phase == 0 ? 0 : P.nseg0)};
       const brsrc_t rv = make_rsrc(P.vis, (uint64_t)((P.nb + 1) / 2) * 4);
       if (!eager && P.fw <= dbs_meta::PUSH_LIST_MAX) {  // uniform
         // the frontier's word bits in the push enumeration's LDS
@@ -473,6 +479,9 @@ dbs_status bfs_run(dbs_matrix *A, const BfsScratch &S, int32_t src, int32_t *lev
   BfsParams P;
   P.t_cb = A->t_cb;
   P.t_cbx = A->t_cbx;
+  P.meta2 = A->meta2;
+  P.m2seg = A->m2seg;
+  P.cbx_compact = A->nb <= CBX_MAX_NB;
   P.t_meta = A->t_meta;
   P.cb_ptr = A->cb_ptr;
   P.csc_rb = A->csc_rb;

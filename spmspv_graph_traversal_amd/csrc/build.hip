@@ -647,17 +647,29 @@ __global__ void k_seg_cost(const uint32_t *psegs, int64_t npseg, const uint64_t 
   cost[sg] = c;
 }
 
+// A pattern tile of one entry (held inline): with at most CBX_MAX_NB column
+// blocks, the Boolean pull decodes it from its column-block word alone.
+__host__ __device__ inline bool single_entry_tile(uint64_t meta) {
+  return meta_type(meta) == DBS_TILE_COO && meta_nnz(meta) == 1u && meta_inline(meta);
+}
+
 // Owner of every coordinate word of a pattern COO tile held in the payload:
-// the tile's index in its Boolean-pull segment (< 256).  The pull spreads a
-// segment's words over the lanes; with the owner stored, a lane finds the
-// mask of its word's tile with one LDS read.  Also the tile's row block
-// within its segment (0 .. PAT_MAX_RB-1), in bits 52..55 of its metadata
-// word: a segment that packs several row blocks sends each found row to its
-// row block by it.  One thread per segment.
+// the tile's rank in its Boolean-pull segment (< 256): its index among the
+// segment's tiles not marked single (m2idx: the exclusive count of such tiles
+// before each tile; null: every tile counts).  The pull spreads a segment's
+// words over the lanes; with the owner stored, a lane finds the mask of its
+// word's tile with one LDS read.  Also the tile's row block within its
+// segment (0 .. PAT_MAX_RB-1), in bits 52..55 of its metadata word: a
+// segment that packs several row blocks sends each found row to its row
+// block by it.  And every tile's column-block word for the pull (t_cbx): the
+// column block and that row block, and (m2idx given, at most CBX_MAX_NB
+// column blocks) for a tile of one entry that entry, for the others their
+// rank.  One thread per segment.
 __global__ void k_word_owner(const uint32_t *psegs, int64_t npseg, const uint32_t *rb_ptr, uint64_t *t_meta,
-                             uint8_t *wown) {
+                             uint8_t *wown, const uint32_t *m2idx, const uint32_t *t_cb, uint32_t *t_cbx) {
   const int64_t sg = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (sg >= npseg) return;
+  const bool compact = m2idx != nullptr;
   const uint32_t rb = psegs[4 * sg], t0 = psegs[4 * sg + 1], t1 = psegs[4 * sg + 2], nrb = psegs[4 * sg + 3];
   uint32_t ri = 0, next = nrb > 1u ? rb_ptr[rb + 1] : t1;  // first tile of row block rb + ri + 1
   for (uint32_t t = t0; t < t1; ++t) {
@@ -667,24 +679,40 @@ __global__ void k_word_owner(const uint32_t *psegs, int64_t npseg, const uint32_
     }
     const uint64_t meta = (t_meta[t] & ~META_SEG_RB) | ((uint64_t)ri << META_SEG_RB_SHIFT);
     t_meta[t] = meta;
+    const uint32_t rank = compact ? m2idx[t] - m2idx[t0] : t - t0;
+    // the pull's column-block word
+    uint32_t cw = t_cb[t] | (ri << (compact ? CBX_RI_SHIFT : CBX_RI_SHIFT_WIDE));
+    if (compact)
+      cw |= single_entry_tile(meta) ? CBX_SINGLE | (((uint32_t)meta & 0xFFu) << CBX_RC_SHIFT) : rank << CBX_RC_SHIFT;
+    t_cbx[t] = cw;
     if (meta_type(meta) != DBS_TILE_COO || meta_inline(meta)) continue;
     const uint64_t w0 = meta_vp(meta) / 4, nw = (meta_nnz(meta) + 3u) / 4u;
-    for (uint64_t w = 0; w < nw; ++w) wown[w0 + w] = (uint8_t)(t - t0);
+    for (uint64_t w = 0; w < nw; ++w) wown[w0 + w] = (uint8_t)rank;
   }
 }
 
-// Column-block words of the Boolean pull (pattern matrices with at most
-// CBX_MAX_NB column blocks): column block, row block within the segment (set
-// in the metadata word by k_word_owner), and the coordinates of a tile of one
-// entry (inline: its first coordinate byte).  One thread per tile.
-__global__ void k_cbx(const uint32_t *t_cb, const uint64_t *t_meta, int64_t T, uint32_t *t_cbx) {
+// 1 for a tile whose metadata the Boolean pull reads (not single), else 0
+__global__ void k_ranked_flags(const uint64_t *t_meta, int64_t T, uint32_t *flag) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t < T) flag[t] = single_entry_tile(t_meta[t]) ? 0u : 1u;
+}
+
+// metadata of the tiles not marked single, in tile order.  One thread per tile.
+__global__ void k_meta2(const uint64_t *t_meta, const uint32_t *m2idx, int64_t T, uint64_t *meta2) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= T) return;
-  const uint64_t meta = t_meta[t];
-  const bool single = meta_type(meta) == DBS_TILE_COO && meta_nnz(meta) == 1u && meta_inline(meta);
-  uint32_t w = t_cb[t] | ((uint32_t)((meta >> META_SEG_RB_SHIFT) & 15u) << CBX_RI_SHIFT);
-  if (single) w |= CBX_SINGLE | (((uint32_t)meta & 0xFFu) << CBX_RC_SHIFT);
-  t_cbx[t] = w;
+  if (m2idx[t + 1] != m2idx[t]) meta2[m2idx[t]] = t_meta[t];
+}
+
+// per Boolean-pull segment: its first entry in meta2 and its entries (m2idx
+// null: every tile has one, meta2 being t_meta).  One thread per segment.
+__global__ void k_m2seg(const uint32_t *psegs, int64_t npseg, const uint32_t *m2idx, uint32_t *m2seg) {
+  const int64_t sg = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (sg >= npseg) return;
+  const uint32_t t0 = psegs[4 * sg + 1], t1 = psegs[4 * sg + 2];
+  const uint32_t b = m2idx ? m2idx[t0] : t0, e = m2idx ? m2idx[t1] : t1;
+  m2seg[2 * sg] = b;
+  m2seg[2 * sg + 1] = e - b;
 }
 
 // Segments of the Boolean pull (pattern matrices), in the order it runs
@@ -834,7 +862,7 @@ int bits_for(uint32_t maxval) {
 
 // temporaries of the build, freed on every exit path
 struct BuildTmp {
-  static constexpr int kMax = 32;
+  static constexpr int kMax = 48;
   dbs_matrix *A;
   void *p[kMax] = {nullptr};
   size_t sz[kMax] = {0};
@@ -1108,16 +1136,53 @@ dbs_status dbs_build_impl(dbs_matrix *A, const int32_t *row_ptr, const int32_t *
     const size_t ow = (size_t)(A->payload_bytes + DBS_PAYLOAD_SLACK) / 4;
     BUILD_TRY(dbs_dev_alloc(A, (void **)&A->wown, ow));
     BUILD_TRY(hipMemsetAsync(A->wown, 0, ow, s));
+    // tiles of one entry are marked single (their metadata is not read by
+    // the pull) when the column block leaves room for them in the word
+    const bool compact = A->nb <= CBX_MAX_NB;
+    uint32_t *m2idx = nullptr;
+    A->nmeta2 = T;
+    if (compact) {
+      uint32_t *flag;
+      void *stmpm;
+      BUILD_TRY(tmp.get((void **)&flag, (size_t)T * 4 + 4));
+      BUILD_TRY(tmp.get((void **)&m2idx, (size_t)T * 4 + 4));
+      BUILD_TRY(tmp.get(&stmpm, dbs_scan_tmp_bytes(T + 1)));
+      if (T > 0) {
+        hipLaunchKernelGGL(k_ranked_flags, dim3(nblocks(T, BT)), dim3(BT), 0, s, (const uint64_t *)A->t_meta, T,
+                           flag);
+        BUILD_TRY(hipGetLastError());
+      }
+      BUILD_TRY(dbs_scan_u32(flag, m2idx, T, stmpm, s));
+      uint32_t hn2 = 0;
+      BUILD_TRY(hipMemcpyAsync(&hn2, m2idx + T, 4, hipMemcpyDeviceToHost, s));
+      BUILD_TRY(hipStreamSynchronize(s));
+      A->nmeta2 = hn2;
+    }
+    BUILD_TRY(dbs_dev_alloc(A, (void **)&A->t_cbx, (size_t)T * 4 + 4));
     if (A->npseg > 0) {
       hipLaunchKernelGGL(k_word_owner, dim3(nblocks(A->npseg, BT)), dim3(BT), 0, s, (const uint32_t *)A->psegs,
-                         A->npseg, (const uint32_t *)A->rb_ptr, (uint64_t *)A->t_meta, A->wown);
+                         A->npseg, (const uint32_t *)A->rb_ptr, (uint64_t *)A->t_meta, A->wown,
+                         (const uint32_t *)m2idx, (const uint32_t *)A->t_cb, A->t_cbx);
       BUILD_TRY(hipGetLastError());
       BUILD_TRY(order_by_cost(A, tmp, s));
     }
-    if (A->nb <= CBX_MAX_NB && T > 0) {
-      BUILD_TRY(dbs_dev_alloc(A, (void **)&A->t_cbx, (size_t)T * 4));
-      hipLaunchKernelGGL(k_cbx, dim3(nblocks(T, BT)), dim3(BT), 0, s, (const uint32_t *)A->t_cb,
-                         (const uint64_t *)A->t_meta, T, A->t_cbx);
+    if (compact) {
+      BUILD_TRY(dbs_dev_alloc(A, (void **)&A->meta2, (size_t)(A->nmeta2 + 1) * 8));
+      BUILD_TRY(hipMemsetAsync(A->meta2, 0, (size_t)(A->nmeta2 + 1) * 8, s));
+      if (T > 0) {
+        hipLaunchKernelGGL(k_meta2, dim3(nblocks(T, BT)), dim3(BT), 0, s, (const uint64_t *)A->t_meta,
+                           (const uint32_t *)m2idx, T, A->meta2);
+        BUILD_TRY(hipGetLastError());
+      }
+    } else {
+      A->meta2 = A->t_meta;
+    }
+    const size_t m2b = (size_t)(A->npseg + 16) * 8;
+    BUILD_TRY(dbs_dev_alloc(A, (void **)&A->m2seg, m2b));
+    BUILD_TRY(hipMemsetAsync(A->m2seg, 0, m2b, s));
+    if (A->npseg > 0) {
+      hipLaunchKernelGGL(k_m2seg, dim3(nblocks(A->npseg, BT)), dim3(BT), 0, s, (const uint32_t *)A->psegs,
+                         A->npseg, (const uint32_t *)m2idx, A->m2seg);
       BUILD_TRY(hipGetLastError());
     }
   }

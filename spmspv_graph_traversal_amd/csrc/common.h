@@ -70,17 +70,21 @@ __host__ __device__ inline uint32_t csr_val_off(uint32_t nnz) { return PL_CSR_RC
 #define META_SEG_RB_SHIFT 52
 #define META_SEG_RB (15ull << META_SEG_RB_SHIFT)
 
-// Column-block word of the Boolean pull (pattern matrices with at most
-// CBX_MAX_NB column blocks): the column block in bits 0..18, the tile's row
+// Column-block word of the Boolean pull (pattern matrices).  With at most
+// CBX_MAX_NB column blocks: the column block in bits 0..18, the tile's row
 // block within its Boolean-pull segment in bits 19..22, and for a tile of a
 // single entry bit 23 set and the entry's (row << 4 | column) in bits 24..31,
-// so such a tile is decoded without its metadata word.  Larger matrices use
-// the plain column block instead (no bit 23).
+// so such a tile is decoded without its metadata word; for the other tiles
+// bits 24..31 hold the tile's rank (its index among the segment's tiles not
+// marked single).  Larger matrices: the column block in bits 0..26 and the
+// row block within the segment in bits 27..30 (no tile is marked single; a
+// tile's rank is its index in the segment).
 #define CBX_CB_BITS 19
 #define CBX_MAX_NB (1 << CBX_CB_BITS)
 #define CBX_RI_SHIFT 19
 #define CBX_SINGLE (1u << 23)
 #define CBX_RC_SHIFT 24
+#define CBX_RI_SHIFT_WIDE 27
 __host__ __device__ inline uint64_t meta_pack(uint64_t vp, uint32_t nnz, uint32_t type) {
   return vp | ((uint64_t)(nnz - 1) << 40) | ((uint64_t)type << 48);
 }
@@ -176,8 +180,11 @@ struct dbs_matrix {
   uint8_t *payload;     // arena
   uint64_t dense_mask_off;  // start of the Dense row-mask section in the arena
   uint32_t *segs;       // [4*nseg] pull segments
-  uint32_t *t_cbx;      // [T] pattern matrices with nb <= CBX_MAX_NB: column-block words of the
-                        // Boolean pull (else none: the pull reads t_cb)
+  uint32_t *t_cbx;      // [T] pattern matrices: column-block words of the Boolean pull
+  uint64_t *meta2;      // pattern matrices: metadata of the tiles not marked single in t_cbx,
+                        // tile order (nb > CBX_MAX_NB: t_meta itself, not owned)
+  int64_t nmeta2;       // its entries
+  uint32_t *m2seg;      // [2*npseg] per Boolean-pull segment: first entry in meta2, entries
   uint8_t *wown;        // pattern matrices: per 4-byte payload word of a COO tile, that tile's index
                         // in its Boolean-pull segment
   uint32_t *psegs;      // [4*npseg] pattern matrices: Boolean-pull segments (first row block, first

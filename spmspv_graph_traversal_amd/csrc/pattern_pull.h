@@ -20,13 +20,20 @@ struct PatSrc {
   const uint32_t *segs;  // padded with 16 zeroed descriptors
   int64_t nseg;
   brsrc_t pay;  // payload and its zeroed slack
-  brsrc_t own;  // per payload word of a COO tile: the tile's index in its segment
-  // the column-block words the Boolean pull reads: with CBX_SINGLE set, a
-  // tile of one entry carries it in its word (else the plain column blocks,
-  // and no tile is marked)
+  brsrc_t own;  // per payload word of a COO tile: the tile's rank in its segment (below)
+  // Pattern matrices: the column-block word of every tile (column block, row
+  // block within the segment, and with CBX_SINGLE a tile of one entry with
+  // that entry), and the metadata of the other tiles ("ranked" tiles),
+  // consecutive per segment in tile order: a ranked tile's rank is its index
+  // among its segment's ranked tiles.  Matrices of more than CBX_MAX_NB
+  // column blocks mark no tile single: every tile is ranked, and this
+  // metadata is t_meta itself.
   const uint32_t *t_cbx = nullptr;
-  uint32_t cbm = ~0u;  // column block of a word
-  uint32_t sbit = 0u;  // CBX_SINGLE, or 0
+  uint32_t cbm = ~0u;               // column block of a word
+  uint32_t sbit = 0u;               // CBX_SINGLE, or 0
+  uint32_t rish = CBX_RI_SHIFT_WIDE;  // row block within the segment: (word >> rish) & 15
+  const uint64_t *meta2 = nullptr;
+  const uint2 *m2seg = nullptr;     // per segment: its first ranked tile in meta2, and their count
 };
 
 template <int U>
@@ -76,17 +83,18 @@ DBS_DEV void pat_issue(const PatSrc &S, const Pol &pol, int64_t s0, bool live, u
 // grow with its tiles (descriptor, ballots, word setup, wave OR, writeback)
 // is what bounds this pull, hence segments of up to 256 tiles.
 template <int K>
-struct PatSeg {  // stage A: descriptor, column blocks, metadata (n == 0: no segment)
+struct PatSeg {  // stage A: descriptor, column-block words, EAGER the ranked tiles' metadata (n == 0: no segment)
   uint32_t rb, t0, n, nrb;  // first row block, first tile, tiles, row blocks (uniform)
+  uint32_t m2b, n2;         // first ranked tile in meta2, ranked tiles (uniform)
   uint32_t needl;           // lane j < nrb: rows wanted in row block rb + j
-  uint32_t cb[K];  // column-block words
-  uint64_t meta[K];
+  uint32_t cb[K];           // column-block words, lane i of slice k: tile 64k+i
+  uint64_t meta[K];         // metadata, lane i of slice k: ranked tile 64k+i
 };
 
 template <int K>
 struct PatMasks {  // stage B: masks, and (EAGER) the first chunk of coordinate words and their owners
-  uint32_t m[K];
-  int tf, tl;  // first and last non-inline COO tile whose words are read (uniform; tl < 0: none)
+  uint32_t m[K];  // lane i of slice k: mask of tile 64k+i
+  int tf, tl;     // first and last rank of a COO tile (not inline) whose words are read (uniform; tl < 0: none)
   uint32_t base, nwords, word, own;
 };
 
@@ -107,9 +115,10 @@ struct FoundBuf {
 constexpr int PAT_MAX_RB = DBS_PAT_MAX_RB;
 
 struct SegWin {
-  uint32_t rb, t0, t1, nrb;  // per lane
-  uint64_t live;             // lanes whose segment has tiles and wanted rows
-  int64_t next;              // first segment of the next window
+  uint32_t rb, t0, m2b;  // per lane: first row block, first tile, first entry in meta2
+  uint32_t pk;           // per lane: tiles | row blocks << 9 | entries in meta2 << 14
+  uint64_t live;         // lanes whose segment has tiles and wanted rows
+  int64_t next;          // first segment of the next window
 };
 
 template <class Pol>
@@ -117,56 +126,66 @@ DBS_DEV void win_fill(const PatSrc &S, const Pol &pol, int64_t stride, int lane,
   const int64_t s = w.next + (int64_t)lane * stride;
   const bool in = s < S.nseg;
   const uint4 d = ((const uint4 *)S.segs)[in ? s : 0];  // unconditional: no branch around the load
+  const uint2 e = S.m2seg[in ? s : 0];
+  const uint32_t nrb = d.w > 1u ? d.w : 1u;
   w.rb = d.x & ~SEG_SPLIT;
   w.t0 = d.y;
-  w.t1 = d.z;
-  w.nrb = d.w > 1u ? d.w : 1u;
+  w.m2b = e.x;
+  w.pk = (d.z - d.y) | (nrb << 9) | (e.y << 14);  // at most 256 tiles, 16 row blocks
   uint32_t need = 0u;
 #pragma unroll
   for (int j = 0; j < PAT_MAX_RB; ++j) {
-    const bool jin = (uint32_t)j < w.nrb;
+    const bool jin = (uint32_t)j < nrb;
     need |= pol.need_v(w.rb + j, in & jin) & (0u - (uint32_t)jin);
   }
   w.live = __ballot(in & (need != 0u) & (d.z > d.y));
   w.next += 64 * stride;
 }
 
+struct SegDesc {
+  uint32_t rb, t0, n, nrb, m2b, n2;  // uniform
+};
+
 // next segment with work, false once the wave's share is done (uniform)
 template <class Pol>
-DBS_DEV bool win_next(const PatSrc &S, const Pol &pol, int64_t stride, int lane, SegWin &w, uint32_t &rb,
-                      uint32_t &t0, uint32_t &t1, uint32_t &nrb) {
+DBS_DEV bool win_next(const PatSrc &S, const Pol &pol, int64_t stride, int lane, SegWin &w, SegDesc &d) {
   while (w.live == 0ull) {
     if (w.next >= S.nseg) return false;
     win_fill(S, pol, stride, lane, w);
   }
   const int j = __ffsll((unsigned long long)w.live) - 1;
   w.live &= w.live - 1ull;
-  rb = (uint32_t)__builtin_amdgcn_readlane((int)w.rb, j);
-  t0 = (uint32_t)__builtin_amdgcn_readlane((int)w.t0, j);
-  t1 = (uint32_t)__builtin_amdgcn_readlane((int)w.t1, j);
-  nrb = (uint32_t)__builtin_amdgcn_readlane((int)w.nrb, j);
+  d.rb = (uint32_t)__builtin_amdgcn_readlane((int)w.rb, j);
+  d.t0 = (uint32_t)__builtin_amdgcn_readlane((int)w.t0, j);
+  d.m2b = (uint32_t)__builtin_amdgcn_readlane((int)w.m2b, j);
+  const uint32_t pk = (uint32_t)__builtin_amdgcn_readlane((int)w.pk, j);
+  d.n = pk & 511u;
+  d.nrb = (pk >> 9) & 31u;
+  d.n2 = pk >> 14;
   return true;
 }
 
 template <int K, bool EAGER, class Pol>
 DBS_DEV void patk_issue(const PatSrc &S, const Pol &pol, int64_t stride, int lane, SegWin &w, uint32_t l4,
                         uint32_t l8, PatSeg<K> &r) {
-  uint32_t rb = 0, t0 = 0, t1 = 0, nrb = 1;
-  const bool any = win_next(S, pol, stride, lane, w, rb, t0, t1, nrb);
-  r.rb = rb;
-  r.t0 = t0;
-  r.nrb = nrb;
-  r.n = any ? t1 - t0 : 0u;
-  const brsrc_t rcb = make_rsrc(S.t_cbx + t0, (uint64_t)r.n * 4u);
-  const brsrc_t rmt = make_rsrc(S.t_meta + t0, (uint64_t)r.n * 8u);
+  SegDesc d{0u, 0u, 0u, 1u, 0u, 0u};
+  const bool any = win_next(S, pol, stride, lane, w, d);
+  r.rb = d.rb;
+  r.t0 = d.t0;
+  r.nrb = d.nrb;
+  r.n = any ? d.n : 0u;
+  r.m2b = d.m2b;
+  r.n2 = any ? d.n2 : 0u;
+  const brsrc_t rcb = make_rsrc(S.t_cbx + d.t0, (uint64_t)r.n * 4u);
+  const brsrc_t rmt = make_rsrc(S.meta2 + d.m2b, (uint64_t)r.n2 * 8u);
 #pragma unroll
   for (int k = 0; k < K; ++k) {
     r.cb[k] = __builtin_amdgcn_raw_buffer_load_b32(rcb, l4 + 256u * k, 0, 0);
     if constexpr (EAGER) r.meta[k] = bld64(rmt, l8 + 512u * k);
     else r.meta[k] = 0ull;
   }
-  const bool mine = any & ((uint32_t)lane < nrb);
-  r.needl = pol.need_v(rb + (uint32_t)lane, mine);
+  const bool mine = any & ((uint32_t)lane < d.nrb);
+  r.needl = pol.need_v(d.rb + (uint32_t)lane, mine);
 }
 
 // lane l's value of slice k (both wave-uniform), read from every slice so
@@ -183,19 +202,22 @@ DBS_DEV uint32_t slice_lane(const uint32_t (&v)[K], int k, int l) {
   return r;
 }
 
-// the non-inline COO tiles whose words are read (every such tile when EAGER:
-// an inactive tile's words meet a zero mask; else the active ones), the run
-// of their words, and its first chunk with the words' owner tiles
+// the non-inline COO tiles whose words are read (every such ranked tile when
+// EAGER: an inactive tile's words meet a zero mask; else those with a
+// nonzero mask in s_tm), the run of their words, and its first chunk with
+// the words' owners (ranks)
 template <int K, bool EAGER>
-DBS_DEV void pat_words(const PatSrc &S, const PatSeg<K> &a, PatMasks<K> &b, int lane, uint32_t l4) {
+DBS_DEV void pat_words(const PatSrc &S, const uint64_t (&meta)[K], uint32_t n2, const uint32_t *s_tm,
+                       PatMasks<K> &b, int lane, uint32_t l4) {
   uint32_t lo[K], hi[K];  // halves of the metadata words
   b.tf = 1 << 20;
   b.tl = -1;
 #pragma unroll
   for (int k = 0; k < K; ++k) {
-    lo[k] = (uint32_t)a.meta[k];
-    hi[k] = (uint32_t)(a.meta[k] >> 32);
-    const bool live = EAGER ? (64u * k + (uint32_t)lane < a.n) : (b.m[k] != 0u);
+    lo[k] = (uint32_t)meta[k];
+    hi[k] = (uint32_t)(meta[k] >> 32);
+    const uint32_t r = 64u * k + (uint32_t)lane;
+    const bool live = EAGER ? (r < n2) : ((r < n2) && ((s_tm[r] & 0xFFFFu) != 0u));
     const uint64_t nb = __ballot(live & (meta_kind(hi[k]) == DBS_TILE_COO));  // COO, not inline
     if (nb != 0ull) {
       const int f = 64 * k + __ffsll((unsigned long long)nb) - 1, l = 64 * k + 63 - __clzll((long long)nb);
@@ -217,49 +239,96 @@ DBS_DEV void pat_words(const PatSrc &S, const PatSeg<K> &a, PatMasks<K> &b, int 
   b.own = __builtin_amdgcn_raw_buffer_load_b8(S.own, in ? (b.base >> 2) + (uint32_t)lane : OOB_OFF, 0, 0);
 }
 
-// everything of one segment once its loads have arrived.  MULTI: the
-// segment holds several row blocks; each found row goes to its row block
-// through an LDS OR (s_f, one word per row block), the row block of a tile
-// within the segment being recorded in its metadata word at build (a tile
-// whose metadata was not read is inactive and finds nothing).  SKIP: slices
-// without an active tile skip the inline-COO decode (worth its test when few
-// vector blocks are active).
-template <int K, bool MULTI, bool SKIP, class Pol>
-DBS_DEV void pat_finish(const PatSrc &S, const Pol &pol, const PatSeg<K> &a, const PatMasks<K> &b, int lane,
-                        uint32_t *s_tm, uint32_t *s_f, FoundBuf &fb) {
+// rank of the ranked tile of word w in lane `lane` of slice k: in the word
+// when it can mark single tiles, else the tile's index in the segment
+DBS_DEV uint32_t rank_of(const PatSrc &S, uint32_t w, int k, int lane) {
+  return S.sbit ? w >> CBX_RC_SHIFT : 64u * k + (uint32_t)lane;
+}
+
+// A segment is finished in two parts around the next segments' loads.
+// pat_pre, in tile order: a tile of one entry is decoded from its word; every
+// other tile writes its mask (| its row block within the segment << 16) to
+// s_tm at its rank; without EAGER, the ranked tiles with a nonzero mask then
+// read their metadata.  pat_post, in rank order (lane i of slice k: ranked
+// tile 64k+i): inline COO tiles from the metadata word; the coordinate words
+// of the other COO tiles, spread over the lanes, each finding its tile's mask
+// at s_tm[owner]; the 16 row masks of the larger tiles, per lane.  MULTI: the
+// segment holds several row blocks, and each found row goes to its row block
+// through an LDS OR (s_f, one word per row block).  SKIP: slices without an
+// active tile skip their decode (worth its test when few vector blocks are
+// active).  `f` keeps the found rows of a one-row-block segment in between.
+template <int K, bool MULTI, bool SKIP, bool EAGER, class Pol>
+DBS_DEV void pat_pre(const PatSrc &S, const Pol &pol, PatSeg<K> &a, const PatMasks<K> &b, int lane, uint32_t l8,
+                     uint32_t *s_tm, uint32_t *s_f, uint32_t &f) {
   const uint32_t n = a.n;  // uniform
-  uint32_t f = 0u;
-  uint32_t ri[K];  // MULTI: row block (0 .. nrb-1) of this lane's tile in each slice
-#pragma unroll
-  for (int k = 0; k < K; ++k) ri[k] = MULTI ? (uint32_t)(a.meta[k] >> META_SEG_RB_SHIFT) & 15u : 0u;
+  f = 0u;
   if constexpr (MULTI) {
     if (lane < PAT_MAX_RB) s_f[lane] = 0u;
     __syncwarp();
   }
-  auto add = [&](int k, uint32_t x) {
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    if (64u * k >= n) break;  // uniform
+    const uint32_t w = a.cb[k];
+    const bool in = 64u * k + (uint32_t)lane < n;
+    const bool single = (w & S.sbit) != 0u;  // lanes past the end read 0
+    const uint32_t ri = (w >> S.rish) & 15u;
+    if (in & !single) s_tm[rank_of(S, w, k, lane)] = b.m[k] | (ri << 16);
+    const uint32_t m = b.m[k];
+    const bool hit = single & (m != 0u);
+    if (SKIP && __ballot(hit) == 0ull) continue;  // uniform
+    const uint32_t rc = w >> CBX_RC_SHIFT;
+    const uint32_t x = hit ? ((m >> (rc & 15u)) & 1u) << (rc >> 4) : 0u;
     if constexpr (MULTI) {
-      if (x) atomicOr(&s_f[ri[k]], x);
+      if (x) atomicOr(&s_f[ri], x);
+    } else {
+      f |= x;
+    }
+  }
+  if constexpr (!EAGER) {
+    __syncwarp();
+    // metadata of the ranked tiles with a nonzero mask
+    const brsrc_t rmt = make_rsrc(S.meta2 + a.m2b, (uint64_t)a.n2 * 8u);
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const uint32_t r = 64u * k + (uint32_t)lane;
+      const bool act = (r < a.n2) && ((s_tm[r] & 0xFFFFu) != 0u);
+      a.meta[k] = bld64(rmt, act ? l8 + 512u * k : OOB_OFF);
+    }
+  }
+}
+
+template <int K, bool MULTI, bool SKIP, bool EAGER, class Pol>
+DBS_DEV void pat_post(const PatSrc &S, const Pol &pol, const PatSeg<K> &a, const PatMasks<K> &b0, int lane,
+                      uint32_t l4, uint32_t *s_tm, uint32_t *s_f, FoundBuf &fb, uint32_t f) {
+  const uint32_t n2 = a.n2;  // uniform
+  __syncwarp();
+  // rank order: lane i of slice k reads mask | row block << 16 of ranked tile 64k+i
+  auto tm_of = [&](int k) {
+    const uint32_t r = 64u * k + (uint32_t)lane;
+    return r < n2 ? s_tm[r] : 0u;
+  };
+  PatMasks<K> bl;
+  if constexpr (!EAGER) pat_words<K, false>(S, a.meta, n2, s_tm, bl, lane, l4);
+  const PatMasks<K> &b = EAGER ? b0 : bl;
+  auto add = [&](uint32_t ri, uint32_t x) {
+    if constexpr (MULTI) {
+      if (x) atomicOr(&s_f[ri], x);
     } else {
       f |= x;
     }
   };
 #pragma unroll
   for (int k = 0; k < K; ++k) {
-    if (64u * k >= n) break;  // uniform
-    if (SKIP && __ballot(b.m[k] != 0u) == 0ull) continue;  // uniform
+    if (64u * k >= n2) break;  // uniform
+    const uint32_t tm = tm_of(k), m = tm & 0xFFFFu;
+    if (SKIP && __ballot(m != 0u) == 0ull) continue;  // uniform
     const uint64_t meta = a.meta[k];
     // COO tiles with at most four entries: the coordinates are in the metadata
     // word (a zero mask decodes to nothing)
-    add(k, meta_kind((uint32_t)(meta >> 32)) == (DBS_TILE_COO | 8u) ? coo_or4((uint32_t)meta, b.m[k]) : 0u);
+    add(tm >> 16, meta_kind((uint32_t)(meta >> 32)) == (DBS_TILE_COO | 8u) ? coo_or4((uint32_t)meta, m) : 0u);
   }
   if (b.tl >= 0) {
-    // per-tile mask (and, MULTI, row block << 16), read by the lanes holding the tile's words
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-      if (64u * k >= n) break;  // uniform
-      s_tm[64 * k + lane] = b.m[k] | (ri[k] << 16);
-    }
-    __syncwarp();
     for (uint32_t j0 = 0; j0 < b.nwords; j0 += 64u) {
       const uint32_t j = j0 + (uint32_t)lane;
       const bool in = j < b.nwords;
@@ -274,13 +343,13 @@ DBS_DEV void pat_finish(const PatSrc &S, const Pol &pol, const PatSeg<K> &a, con
         f |= x;
       }
     }
-    __syncwarp();
   }
   // larger tiles: 16 row masks each
 #pragma unroll
   for (int k = 0; k < K; ++k) {
-    if (64u * k >= n) break;  // uniform
-    const bool big = (b.m[k] != 0u) & (meta_type(a.meta[k]) != DBS_TILE_COO);
+    if (64u * k >= n2) break;  // uniform
+    const uint32_t tm = tm_of(k), m = tm & 0xFFFFu;
+    const bool big = (m != 0u) & (meta_type(a.meta[k]) != DBS_TILE_COO);
     if (__ballot(big) != 0ull) {
       const uint32_t o = big ? (uint32_t)meta_vp(a.meta[k]) : OOB_OFF;
       const auto x = __builtin_amdgcn_raw_buffer_load_b128(S.pay, o, 0, 0);
@@ -291,9 +360,8 @@ DBS_DEV void pat_finish(const PatSrc &S, const Pol &pol, const PatSeg<K> &a, con
       // 0/1 bit comes from a carry ((x + 0xFFFF) >> 16), so no per-row
       // constant is held in a register
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        g |= ((((rm[r >> 1] >> (16 * (r & 1))) & b.m[k]) + 0xFFFFu) >> 16) << r;
-      add(k, g);
+      for (int r = 0; r < 16; ++r) g |= ((((rm[r >> 1] >> (16 * (r & 1))) & m) + 0xFFFFu) >> 16) << r;
+      add(tm >> 16, g);
     }
   }
   if constexpr (MULTI) {
@@ -318,6 +386,7 @@ DBS_DEV void pat_finish(const PatSrc &S, const Pol &pol, const PatSeg<K> &a, con
       }
       fb.n += 1;
     }
+    __syncwarp();
   }
 }
 
@@ -333,34 +402,35 @@ DBS_DEV void pat_flush(const Pol &pol, FoundBuf &fb, int lane, bool all) {
   }
 }
 
-template <int K, bool SKIP, class Pol>
-DBS_DEV void pat_finish_any(const PatSrc &S, const Pol &pol, const PatSeg<K> &a, const PatMasks<K> &b, int lane,
-                            uint32_t *s_tm, uint32_t *s_f, FoundBuf &fb) {
-  if (a.nrb > 1u) pat_finish<K, true, SKIP>(S, pol, a, b, lane, s_tm, s_f, fb);  // uniform
-  else pat_finish<K, false, SKIP>(S, pol, a, b, lane, s_tm, s_f, fb);
-  pat_flush(pol, fb, lane, false);
-}
-
 // One wave's share: segments s0, s0 + stride, ... that have work.  Three
 // steps are in flight: while segment i is finished, segment i+1 has its
-// masks (and, EAGER, its coordinate words) and segment i+2 its column blocks
-// and metadata in flight.  Loads are issued in that order, so a wait for
-// segment i's data never waits for the loads of the later segments (a new
-// window of descriptors, once per 64 segments, does wait).  Without EAGER,
-// segment i's metadata (of its active tiles) and then its coordinate words
-// are read in its own step; a deeper pipeline that reads them one and two
-// steps ahead ran slower (more registers and moves per step, and this pull
-// is bound by the vector-memory instructions it issues, not by waits).
+// masks (and, EAGER, its coordinate words) and segment i+2 its column-block
+// words and (EAGER) metadata in flight.  Loads are issued in that order, so a
+// wait for segment i's data never waits for the loads of the later segments
+// (a new window of descriptors, once per 64 segments, does wait).  Without
+// EAGER, segment i's metadata (of its active ranked tiles) is read at the
+// start of its step, before the later segments' loads, and its coordinate
+// words after them; a deeper pipeline that reads them one and two steps ahead
+// ran slower (more registers and moves per step, and this pull is bound by
+// the vector-memory instructions it issues, not by waits).
+template <int K, bool EAGER, bool MULTI, class Pol>
+DBS_DEV void pat_step(const PatSrc &S, const Pol &pol, int64_t stride, int lane, uint32_t l4, uint32_t l8,
+                      SegWin &w, PatSeg<K> &a0, PatSeg<K> &a1, PatSeg<K> &a2, PatMasks<K> &b0, PatMasks<K> &b1,
+                      uint32_t *s_tm, uint32_t *s_f, FoundBuf &fb) {
+  uint32_t f;
+  pat_pre<K, MULTI, !EAGER, EAGER>(S, pol, a0, b0, lane, l8, s_tm, s_f, f);
+  patk_issue<K, EAGER>(S, pol, stride, lane, w, l4, l8, a2);
+#pragma unroll
+  for (int k = 0; k < K; ++k) b1.m[k] = pol.mask(a1.cb[k] & S.cbm, 64u * k + (uint32_t)lane < a1.n);
+  if constexpr (EAGER) pat_words<K, true>(S, a1.meta, a1.n2, s_tm, b1, lane, l4);
+  pat_post<K, MULTI, !EAGER, EAGER>(S, pol, a0, b0, lane, l4, s_tm, s_f, fb, f);
+}
+
 template <int K, bool EAGER, class Pol>
 DBS_DEV void pattern_pull_wave(const PatSrc &S, const Pol &pol, int64_t s0, int64_t stride, int lane,
                                uint32_t *s_tm, uint32_t *s_f, FoundBuf &fb) {
   if (s0 >= S.nseg) return;
   const uint32_t l4 = (uint32_t)lane * 4u, l8 = (uint32_t)lane * 8u;
-  auto masks = [&](const PatSeg<K> &a, PatMasks<K> &b) {
-#pragma unroll
-    for (int k = 0; k < K; ++k) b.m[k] = pol.mask(a.cb[k] & S.cbm, 64u * k + (uint32_t)lane < a.n);
-    if constexpr (EAGER) pat_words<K, true>(S, a, b, lane, l4);
-  };
   SegWin w;
   w.next = s0;
   w.live = 0ull;
@@ -368,19 +438,13 @@ DBS_DEV void pattern_pull_wave(const PatSrc &S, const Pol &pol, int64_t s0, int6
   PatMasks<K> b0, b1;
   patk_issue<K, EAGER>(S, pol, stride, lane, w, l4, l8, a0);
   patk_issue<K, EAGER>(S, pol, stride, lane, w, l4, l8, a1);
-  masks(a0, b0);
-  while (a0.n != 0u) {
-    if constexpr (!EAGER) {
-      // metadata of segment i's active tiles, before the later loads
-      const brsrc_t rmt = make_rsrc(S.t_meta + a0.t0, (uint64_t)a0.n * 8u);
 #pragma unroll
-      for (int k = 0; k < K; ++k) a0.meta[k] = bld64(rmt, b0.m[k] != 0u ? l8 + 512u * k : OOB_OFF);
-    }
-    patk_issue<K, EAGER>(S, pol, stride, lane, w, l4, l8, a2);
-    masks(a1, b1);
-    if constexpr (!EAGER) pat_words<K, false>(S, a0, b0, lane, l4);
-    if (a0.nrb > 1u) pat_finish<K, true, !EAGER>(S, pol, a0, b0, lane, s_tm, s_f, fb);  // uniform
-    else pat_finish<K, false, !EAGER>(S, pol, a0, b0, lane, s_tm, s_f, fb);
+  for (int k = 0; k < K; ++k) b0.m[k] = pol.mask(a0.cb[k] & S.cbm, 64u * k + (uint32_t)lane < a0.n);
+  if constexpr (EAGER) pat_words<K, true>(S, a0.meta, a0.n2, s_tm, b0, lane, l4);
+  while (a0.n != 0u) {
+    if (a0.nrb > 1u)  // uniform
+      pat_step<K, EAGER, true>(S, pol, stride, lane, l4, l8, w, a0, a1, a2, b0, b1, s_tm, s_f, fb);
+    else pat_step<K, EAGER, false>(S, pol, stride, lane, l4, l8, w, a0, a1, a2, b0, b1, s_tm, s_f, fb);
     pat_flush(pol, fb, lane, false);
     a0 = a1;
     a1 = a2;
@@ -393,40 +457,43 @@ DBS_DEV void pattern_pull_wave(const PatSrc &S, const Pol &pol, int64_t s0, int6
 // bits in LDS).  A segment then holds a handful of active tiles, and the
 // per-segment finish above (ballots, decode and writeback of every slice)
 // is mostly idle work.  Here a wave only tests each tile's column block
-// against the active-block bits and queues the active tiles (tile, column
-// block, the segment's first row block) in an LDS ring; every 64 queued
-// tiles are finished together, one tile per lane: its mask word and
-// metadata, then its coordinates (inline, its coordinate words, or the 16
-// row masks of a larger tile), and the found rows go straight to the
-// policy (a row block of a tile is its segment's first plus the offset in
-// bits 52..55 of its metadata word).  Column blocks of the next two
-// segments are in flight while one is tested.
+// against the active-block bits and queues the active tiles in an LDS
+// ring; every 64 queued tiles are finished together, one tile per lane: its
+// mask word and (a ranked tile) its metadata, then its coordinates (a single
+// entry from its word, inline ones from the metadata word, its coordinate
+// words, or the 16 row masks of a larger tile), and the found rows go to the
+// wave's found-row buffer (a tile's row block is its segment's first plus
+// the offset in its word).  The words of the next two segments are in
+// flight while one is tested.
 // ---------------------------------------------------------------------------
 constexpr uint32_t PAT_Q = 128;  // ring entries: 64 queued at most before a batch, plus one slice
 
 template <int K>
 struct ScanSeg {
-  uint32_t rb, t0, n;  // first row block, first tile, tiles (uniform; n == 0: no segment)
-  uint32_t cb[K];      // column-block words
+  uint32_t rb, t0, n, m2b;  // first row block, first tile, tiles, first ranked tile (uniform; n == 0: none)
+  uint32_t cb[K];           // column-block words
 };
 
 template <int K, class Pol>
 DBS_DEV void scan_issue(const PatSrc &S, const Pol &pol, int64_t stride, int lane, SegWin &w, uint32_t l4,
                         ScanSeg<K> &r) {
-  uint32_t rb = 0, t0 = 0, t1 = 0, nrb = 1;
-  const bool any = win_next(S, pol, stride, lane, w, rb, t0, t1, nrb);
-  r.rb = rb;
-  r.t0 = t0;
-  r.n = any ? t1 - t0 : 0u;
-  const brsrc_t rcb = make_rsrc(S.t_cbx + t0, (uint64_t)r.n * 4u);
+  SegDesc d{0u, 0u, 0u, 1u, 0u, 0u};
+  const bool any = win_next(S, pol, stride, lane, w, d);
+  r.rb = d.rb;
+  r.t0 = d.t0;
+  r.n = any ? d.n : 0u;
+  r.m2b = d.m2b;
+  const brsrc_t rcb = make_rsrc(S.t_cbx + d.t0, (uint64_t)r.n * 4u);
 #pragma unroll
   for (int k = 0; k < K; ++k) r.cb[k] = __builtin_amdgcn_raw_buffer_load_b32(rcb, l4 + 256u * k, 0, 0);
 }
 
 // A batch of queued tiles (n <= 64, lane j holding the j-th): its mask
-// words and the metadata of its tiles of more than one entry are loaded when
-// it leaves the ring, and it is finished when the next batch leaves (or at
-// the end), so its loads are in flight while the wave scans on.
+// words and the metadata of its ranked tiles are loaded when it leaves the
+// ring, and it is finished when the next batch leaves (or at the end), so
+// its loads are in flight while the wave scans on.  A queue entry is (the
+// tile's entry in meta2 if it is ranked, its column-block word, its
+// segment's first row block).
 struct SpBatch {
   uint32_t n;  // tiles (uniform; 0: none)
   uint32_t rb0, cbx, w;
@@ -438,13 +505,14 @@ DBS_DEV void sp_issue(const PatSrc &S, const Pol &pol, const uint32_t *q, uint32
                       SpBatch &b) {
   const bool in = (uint32_t)lane < n;
   const uint32_t i = (head + (uint32_t)lane) & (PAT_Q - 1u);
-  const uint32_t t = q[i];
+  const uint32_t e = q[i];
   b.n = n;
   b.cbx = q[PAT_Q + i];
   b.rb0 = q[2 * PAT_Q + i];
   b.w = pol.mask_raw(b.cbx & S.cbm, in);
-  // idle lanes and tiles of one entry repeat lane 0's tile (no extra line)
-  b.meta = S.t_meta[(in & ((b.cbx & S.sbit) == 0u)) ? t : q[head & (PAT_Q - 1u)]];
+  // idle lanes and single tiles repeat lane 0's entry (an entry of meta2, or
+  // its first word, which exists: meta2 is allocated with one word at least)
+  b.meta = S.meta2[(in & ((b.cbx & S.sbit) == 0u)) ? e : q[head & (PAT_Q - 1u)]];
 }
 
 // found rows of a batch's tiles: a tile of one entry from its column-block
@@ -494,8 +562,7 @@ DBS_DEV void sp_finish(const PatSrc &S, const Pol &pol, const SpBatch &b, int la
   if (f != 0u) {
     const int pos = fb.n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(any >> 32),
                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)any, 0u));
-    const uint32_t ri = single ? (b.cbx >> CBX_RI_SHIFT) & 15u : (hi >> (META_SEG_RB_SHIFT - 32)) & 15u;
-    fb.rb[pos] = b.rb0 + ri;
+    fb.rb[pos] = b.rb0 + ((b.cbx >> S.rish) & 15u);
     fb.f[pos] = f;
   }
   fb.n += __popcll(any);
@@ -532,15 +599,17 @@ DBS_DEV void pattern_pull_sparse(const PatSrc &S, const Pol &pol, int64_t s0, in
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       if (64u * k >= a0.n) break;  // uniform
-      const bool act = (64u * k + (uint32_t)lane < a0.n) & pol.active(a0.cb[k] & S.cbm);
+      const bool in = 64u * k + (uint32_t)lane < a0.n;
+      const uint32_t cw = a0.cb[k];
+      const bool act = in & pol.active(cw & S.cbm);
       const uint64_t bal = __ballot(act);
       if (bal != 0ull) {  // uniform
         const uint32_t pos =
             (head + qn + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u))) &
             (PAT_Q - 1u);
         if (act) {
-          q[pos] = a0.t0 + 64u * k + (uint32_t)lane;
-          q[PAT_Q + pos] = a0.cb[k];
+          q[pos] = a0.m2b + rank_of(S, cw, k, lane);  // unused for a single tile
+          q[PAT_Q + pos] = cw;
           q[2 * PAT_Q + pos] = a0.rb;
         }
         qn += (uint32_t)__popcll(bal);

@@ -195,7 +195,10 @@ __global__ void k_fill_u32(uint32_t *p, int64_t n, uint32_t v) {
 
 struct SpmvParams {
   const uint32_t *t_cb;
-  const uint32_t *t_cbx;  // pattern matrices with nb <= CBX_MAX_NB, else null
+  const uint32_t *t_cbx;   // pattern matrices: the Boolean pull's column-block words
+  const uint64_t *meta2;   // pattern matrices: metadata of the tiles not marked single
+  const uint32_t *m2seg;   // pattern matrices: per pull segment, first entry in meta2 and entries
+  bool cbx_compact;        // nb <= CBX_MAX_NB: the words mark single tiles
   const uint64_t *t_meta;
   const uint32_t *cb_ptr;
   const uint32_t *csc_rb;
@@ -829,9 +832,12 @@ __global__ __launch_bounds__(KT, ((VK == VK_BF16 && SR == DBS_PLUS_TIMES && PU =
                        P.nseg,
                        R.pay,
                        make_rsrc(P.wown, (uint64_t)(P.payload_bytes + DBS_PAYLOAD_SLACK) / 4),
-                       P.t_cbx ? P.t_cbx : P.t_cb,
-                       P.t_cbx ? (uint32_t)(CBX_MAX_NB - 1) : ~0u,
-                       P.t_cbx ? CBX_SINGLE : 0u};
+                       P.t_cbx,
+                       P.cbx_compact ? (uint32_t)(CBX_MAX_NB - 1) : (1u << CBX_RI_SHIFT_WIDE) - 1u,
+                       P.cbx_compact ? CBX_SINGLE : 0u,
+                       P.cbx_compact ? (uint32_t)CBX_RI_SHIFT : (uint32_t)CBX_RI_SHIFT_WIDE,
+                       P.meta2,
+                       (const uint2 *)P.m2seg};
         if (!eager && P.xbits) {  // uniform
           // the active-block bits in the push enumeration's LDS
           for (int i = (int)threadIdx.x; i < P.nbw; i += KT) s_cum[i] = P.xbits[i];
@@ -1114,6 +1120,9 @@ dbs_status dbs_spmspv_impl(dbs_matrix *A, int32_t nnz_x, const int32_t *x_idx, c
   P.payload_bytes = A->payload_bytes;
   P.t_cb = A->t_cb;
   P.t_cbx = A->t_cbx;
+  P.meta2 = A->meta2;
+  P.m2seg = A->m2seg;
+  P.cbx_compact = A->nb <= CBX_MAX_NB;
   P.t_meta = A->t_meta;
   P.cb_ptr = A->cb_ptr;
   P.csc_rb = A->csc_rb;

@@ -41,7 +41,7 @@ def check_pattern_segments(dbs, A, ar, tv, cap):
     T = int(tv["T"])
     if T == 0:
         assert ps.shape[0] == 0
-        return np.zeros(0, np.int64), np.zeros(0, np.int64)
+        return np.zeros(0, np.int64), np.zeros(0, np.int64), np.zeros(0, np.int64)
     rbp = tv["rb_ptr"].astype(np.int64)
     rb0, t0, t1, nrb = ps[:, 0], ps[:, 1], ps[:, 2], ps[:, 3]
     assert np.all(t1 > t0) and np.all((nrb >= 1) & (nrb <= 16))
@@ -57,33 +57,49 @@ def check_pattern_segments(dbs, A, ar, tv, cap):
     assert np.all((ri >= 0) & (ri < nrb[seg_of]))
     bits = ((ar["t_meta"] >> np.uint64(52)) & np.uint64(15)).astype(np.int64)
     np.testing.assert_array_equal(bits[tiles], ri)
-    return tiles, ri
+    return tiles, ri, seg_of
 
 
-def check_cbx(dbs, A, tv, exp_types, tiles, ri, nb):
-    """Column-block words of the Boolean pull: with at most 2^19 column
-    blocks, column block | row block in the segment << 19, and for a COO
-    tile of one entry bit 23 and that entry's (row << 4 | column) << 24;
-    none above 2^19."""
-    cbx = dbs.dbs_copy_array(A, dbs.DBS_ARR_T_CBX)
+def check_cbx(dbs, A, ar, tv, exp_types, tiles, ri, seg_of, nb):
+    """Column-block words of the Boolean pull and the metadata it reads.
+    With at most 2^19 column blocks: column block | row block in the segment
+    << 19, and for a COO tile of one entry bit 23 and that entry's (row << 4
+    | column) << 24; more: column block | row block in the segment << 27.
+    META2 holds the metadata words of the tiles without bit 23, in tile
+    order, and PAT_M2 each segment's first entry there and its count."""
+    cbx = dbs.dbs_copy_array(A, dbs.DBS_ARR_T_CBX).astype(np.int64)
     T = int(tv["T"])
-    if nb > 1 << 19 or T == 0:
-        assert cbx.shape[0] == 0
-        return
     assert cbx.shape[0] == T
-    cbx = cbx.astype(np.int64)
-    np.testing.assert_array_equal(cbx & ((1 << 19) - 1), tv["t_cb"].astype(np.int64))
+    compact = nb <= 1 << 19
+    sh = 19 if compact else 27
+    np.testing.assert_array_equal(cbx & ((1 << sh) - 1), tv["t_cb"].astype(np.int64))
     ri_t = np.zeros(T, np.int64)
     ri_t[tiles] = ri
-    np.testing.assert_array_equal((cbx >> 19) & 15, ri_t)
-    single = (exp_types == orc.COO) & (tv["t_nnz"] == 1)
-    np.testing.assert_array_equal((cbx >> 23) & 1, single.astype(np.int64))
-    # the entry of a one-entry tile from the oracle's per-row column masks
-    rm = tv["t_rowmask"].reshape(-1, 16).astype(np.int64)[single]
-    r = np.argmax(rm != 0, axis=1)
-    c = np.log2(rm[np.arange(rm.shape[0]), r]).astype(np.int64)
-    np.testing.assert_array_equal(cbx[single] >> 24, r * 16 + c)
-    assert not (cbx[~single] >> 24).any()
+    np.testing.assert_array_equal((cbx >> sh) & 15, ri_t)
+    single = (exp_types == orc.COO) & (tv["t_nnz"] == 1) & compact
+    if compact:
+        np.testing.assert_array_equal((cbx >> 23) & 1, single.astype(np.int64))
+        # the entry of a one-entry tile from the oracle's per-row column masks
+        rm = tv["t_rowmask"].reshape(-1, 16).astype(np.int64)[single]
+        r = np.argmax(rm != 0, axis=1)
+        c = np.log2(rm[np.arange(rm.shape[0]), r]).astype(np.int64)
+        np.testing.assert_array_equal(cbx[single] >> 24, r * 16 + c)
+    else:
+        assert not (cbx >> 31).any()
+    meta2 = dbs.dbs_copy_array(A, dbs.DBS_ARR_META2)
+    np.testing.assert_array_equal(meta2, ar["t_meta"][~single])
+    ps = dbs.dbs_copy_array(A, dbs.DBS_ARR_PAT_SEGS).reshape(-1, 4).astype(np.int64)
+    m2 = dbs.dbs_copy_array(A, dbs.DBS_ARR_PAT_M2).reshape(-1, 2).astype(np.int64)
+    assert m2.shape[0] == ps.shape[0]
+    before = np.concatenate([[0], np.cumsum(~single)])  # ranked tiles before each tile
+    np.testing.assert_array_equal(m2[:, 0], before[ps[:, 1]])
+    np.testing.assert_array_equal(m2[:, 1], before[ps[:, 2]] - before[ps[:, 1]])
+    if compact:
+        # a ranked tile's index among its segment's ranked tiles
+        seg_t0 = np.zeros(T, np.int64)
+        seg_t0[tiles] = ps[seg_of, 1]
+        rank = before[:-1] - before[seg_t0]
+        np.testing.assert_array_equal(cbx[~single] >> 24, rank[~single])
 
 
 def check_format(dbs, m, n, rp, ci, vbits, dtype, vk, opt=None, th=(32, 128, 2.0), force=-1, cap=None):
@@ -158,8 +174,8 @@ def check_format(dbs, m, n, rp, ci, vbits, dtype, vk, opt=None, th=(32, 128, 2.0
         assert not ((segs[:, 0] >> 30) & 1).any()
     np.testing.assert_array_equal(segs[:, 3], slot[order])
     if vk == 2:
-        tiles, ri = check_pattern_segments(dbs, A, ar, tv, cap)
-        check_cbx(dbs, A, tv, exp_types, tiles, ri, (n + 15) // 16)
+        tiles, ri, seg_of = check_pattern_segments(dbs, A, ar, tv, cap)
+        check_cbx(dbs, A, ar, tv, exp_types, tiles, ri, seg_of, (n + 15) // 16)
     for f in range(5):
         assert st["tiles_by_format"][f] == int(np.count_nonzero(exp_types == f))
         assert st["nnz_by_format"][f] == int(tv["t_nnz"][exp_types == f].sum())
@@ -210,8 +226,9 @@ def test_rmat_pattern(dbs):
 
 @pytest.mark.parametrize("nb", [1 << 19, (1 << 19) + 1])
 def test_pattern_column_block_words_limit(dbs, nb):
-    """The pull's column-block words exist up to 2^19 column blocks (the
-    last one included) and not beyond; the format is the same either way."""
+    """The pull's column-block words mark single tiles up to 2^19 column
+    blocks (the last one included) and not beyond; the format is the same
+    either way."""
     n = 16 * nb
     g = rng_for("test", 606, nb)
     m = 40
