@@ -517,9 +517,9 @@ DBS_DEV void sp_issue(const PatSrc &S, const Pol &pol, const uint32_t *q, uint32
 
 // found rows of a batch's tiles: a tile of one entry from its column-block
 // word; inline COO tiles from the metadata word; the coordinate words of the
-// other COO tiles are read 16 entries per 16-byte load (the words past a
-// tile's end are not decoded), the 16 row masks of the larger tiles in two
-// loads.  The rows found go to the wave's found-row buffer.
+// other COO tiles are read 16 entries per 16-byte load, one load per round
+// (the words past a tile's end are not decoded), the 16 row masks of the
+// larger tiles in two loads.  The rows found go to the wave's found-row buffer.
 template <class Pol>
 DBS_DEV void sp_finish(const PatSrc &S, const Pol &pol, const SpBatch &b, int lane, FoundBuf &fb, int cap) {
   const bool in = (uint32_t)lane < b.n;
@@ -534,19 +534,10 @@ DBS_DEV void sp_finish(const PatSrc &S, const Pol &pol, const SpBatch &b, int la
   const uint32_t nw = (live & (kind == DBS_TILE_COO)) ? ((hi >> 8) & 0xFFu) / 4u + 1u : 0u;
   const bool big = live & (meta_type(b.meta) != DBS_TILE_COO);
   const uint32_t nq = wave_max((nw + 3u) >> 2);  // uniform
-  for (uint32_t j0 = 0; j0 < nq; j0 += 4u) {
-    uint32_t wd[4][4];
+  for (uint32_t jq = 0; jq < nq; ++jq) {  // most tiles have at most 16 entries: one round
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(S.pay, 4u * jq < nw ? lo + 16u * jq : OOB_OFF, 0, 0);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint32_t jq = j0 + (uint32_t)u;
-      const auto v = __builtin_amdgcn_raw_buffer_load_b128(S.pay, 4u * jq < nw ? lo + 16u * jq : OOB_OFF, 0, 0);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) wd[u][e] = v[e];
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) f |= (4u * (j0 + (uint32_t)u) + (uint32_t)e < nw) ? coo_or4(wd[u][e], m) : 0u;
+    for (int e = 0; e < 4; ++e) f |= (4u * jq + (uint32_t)e < nw) ? coo_or4(v[e], m) : 0u;
   }
   if (__ballot(big) != 0ull) {  // uniform
     const uint32_t o = big ? lo : OOB_OFF;
