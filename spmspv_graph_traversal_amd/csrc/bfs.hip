@@ -222,9 +222,18 @@ struct BfsPol {
     return ~(w >> ((rb & 1u) * 16u)) & rows_valid(P->m, rb);
   }
   DBS_DEV uint32_t mask(uint32_t cb, bool in) const {
-    if constexpr (FILTER) in = in && ((bits[cb >> 6] >> ((cb >> 1) & 31u)) & 1u);  // idle lanes hold cb 0
-    const uint32_t w = bld32(bm, in ? (cb >> 1) * 4u : OOB_OFF);
-    return (w >> ((cb & 1u) * 16u)) & 0xFFFFu;
+    if constexpr (FILTER) in = in && active(cb);  // idle lanes hold cb 0
+    return mask_of(mask_raw(cb, in), cb);
+  }
+  // FILTER: the frontier bitmap word of the block is nonzero (LDS bit)
+  DBS_DEV bool active(uint32_t cb) const { return (bits[cb >> 6] >> ((cb >> 1) & 31u)) & 1u; }
+  // the frontier bitmap word as loaded, and the block's mask in it
+  DBS_DEV uint32_t mask_raw(uint32_t cb, bool in) const { return bld32(bm, in ? (cb >> 1) * 4u : OOB_OFF); }
+  DBS_DEV uint32_t mask_of(uint32_t w, uint32_t cb) const { return (w >> ((cb & 1u) * 16u)) & 0xFFFFu; }
+  // rows found by the very sparse pull (n entries, LDS), not yet checked
+  // against the visited bitmap: an entry per lane
+  DBS_DEV void flush_new(const uint32_t *frb, const uint32_t *ff, int n, int lane) const {
+    for (int e = lane; e < n; e += DBS_WAVE) discover(*P, frb[e], ff[e]);
   }
   // rows found in n row blocks (LDS): lane j claims row block j, then the
   // levels are stored four row blocks per pass, a lane per row
@@ -291,7 +300,14 @@ __global__ __launch_bounds__(KT, VK == VK_PAT ? 4 : 1) void k_bfs_level(BfsParam
         for (int i = (int)threadIdx.x; i < P.fw; i += KT) s_cum[i] = P.cur_fbits[i];
         __syncthreads();
         const BfsPol<true> pol{&P, R.bm, rv, s_cum};
-        pattern_pull<true>(S, pol, gw, nw, false, lane, s_pat[w]);
+        constexpr int SP_BITS_MAX = sp_bits_max(KT / DBS_WAVE);
+        // the very sparse pull when under 1/128 of the vertex blocks are in
+        // the frontier (and its found-row buffers fit after the bits): at a
+        // percent or more the frontier's blocks include hub columns that hold
+        // most tiles, and per-segment finishing does better (R-MAT scale 22)
+        if ((int64_t)nz * 128 < (int64_t)P.nb && P.fw <= SP_BITS_MAX)  // uniform
+          pattern_pull_sparse<PAT_K>(S, pol, gw, nw, lane, s_pat[w], s_cum + SP_BITS_MAX + w * 2 * SP_FOUND_CAP);
+        else pattern_pull<true>(S, pol, gw, nw, false, lane, s_pat[w]);
       } else {
         const BfsPol<false> pol{&P, R.bm, rv, nullptr};
         pattern_pull(S, pol, gw, nw, eager, lane, s_pat[w]);

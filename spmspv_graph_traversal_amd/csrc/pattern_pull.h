@@ -559,16 +559,22 @@ DBS_DEV void sp_finish(const PatSrc &S, const Pol &pol, const SpBatch &b, int la
   fb.n += __popcll(any);
   if (fb.n > cap - 64) {  // uniform: no room for another batch
     __syncwarp();
-    pol.flush(fb.rb, fb.f, fb.n, lane);
+    pol.flush_new(fb.rb, fb.f, fb.n, lane);
     __syncwarp();
     fb.n = 0;
   }
 }
 
 // LDS per wave of the very sparse pull: the ring (tile, column block, row
-// block), and apart from it the found-row buffer (2 x SP_FOUND_CAP words)
+// block), and apart from it the found-row buffer (2 x SP_FOUND_CAP words).
+// The found rows are not checked against the rows still wanted: the
+// policy's flush_new does that.
 constexpr int SP_FOUND_CAP = 128;
 constexpr int SP_LDS_WORDS = 3 * (int)PAT_Q;
+// with the active-block bits staged in an LDS array of PUSH_LIST_MAX words
+// for a workgroup of `waves` waves, the bits may take this many words and
+// leave room for the waves' found-row buffers after them
+constexpr int sp_bits_max(int waves) { return dbs_meta::PUSH_LIST_MAX - waves * 2 * SP_FOUND_CAP; }
 
 template <int K, class Pol>
 DBS_DEV void pattern_pull_sparse(const PatSrc &S, const Pol &pol, int64_t s0, int64_t stride, int lane,
@@ -625,7 +631,7 @@ DBS_DEV void pattern_pull_sparse(const PatSrc &S, const Pol &pol, int64_t s0, in
   }
   if (fb.n != 0) {
     __syncwarp();
-    pol.flush(fb.rb, fb.f, fb.n, lane);
+    pol.flush_new(fb.rb, fb.f, fb.n, lane);
   }
 }
 

@@ -325,10 +325,7 @@ DBS_DEV void push_chunk(const SpmvParams &P, uint64_t own, float *sx, float *spa
 constexpr int PULL_U_PLUS_WIDE = 4;  // segments per wave step, PLUS_TIMES pull with many segments
 constexpr int PLUS_MAX_PARTS = DBS_MAX_SHARE;  // waves sharing one PLUS_TIMES pull segment at most
 constexpr int PULL_U_OR = 8;    // segments per wave step, OR_AND pull (value matrices)
-// Boolean pull with the active-block bits in LDS: up to SP_BITS_MAX words of
-// bits leave room in the same LDS for the very sparse pull's found-row
-// buffers, one per wave
-constexpr int SP_BITS_MAX = dbs_meta::PUSH_LIST_MAX - (KT / DBS_WAVE) * 2 * SP_FOUND_CAP;
+constexpr int SP_BITS_MAX = sp_bits_max(KT / DBS_WAVE);  // very sparse pull: bits and buffers in s_cum
 
 // ---------------------------------------------------------------------------
 // PLUS_TIMES over the COO tiles of the U pull segments of a wave step,
@@ -708,7 +705,9 @@ struct OrPol {
   DBS_DEV uint32_t mask_of(uint32_t w, uint32_t) const {
     return ((w >> 16) == epoch) ? (w & 0xFFFFu) : 0u;  // an idle lane reads 0: no epoch
   }
-  // found rows of n row blocks (LDS): four row blocks per pass, a lane per row
+  // found rows of n row blocks (LDS): four row blocks per pass, a lane per
+  // row (every row is wanted: the very sparse pull's rows are the same)
+  DBS_DEV void flush_new(const uint32_t *frb, const uint32_t *ff, int n, int lane) const { flush(frb, ff, n, lane); }
   DBS_DEV void flush(const uint32_t *frb, const uint32_t *ff, int n, int lane) const {
     for (int e0 = 0; e0 < n; e0 += 4) {
       const int e = e0 + (lane >> 4), r = lane & 15;
