@@ -248,7 +248,8 @@ typedef struct {
   int64_t segments;                /* pull segments */
   int64_t payload_bytes;           /* tile payload arena */
   int64_t index_bytes;             /* block-CSR + block-CSC views and tile metadata */
-  int64_t format_bytes;            /* payload + index + segment descriptors */
+  int64_t format_bytes;            /* payload + index + segment descriptors + (pattern
+                                      matrices) the Boolean pull's own arrays */
   int64_t build_peak_bytes;        /* peak device memory held during dbs_build */
   /* last dbs_spmspv / dbs_spmspv_dense call (reading them synchronizes its stream) */
   int32_t last_path;               /* 0 push, 1 pull, -1 no call yet */

@@ -226,8 +226,16 @@ dbs_status dbs_build(int32_t m, int32_t n, int64_t nnz, const int32_t *row_ptr, 
   A->st.tiles = A->T;
   A->st.segments = A->nseg;
   A->st.payload_bytes = A->payload_bytes;
-  A->st.index_bytes = (int64_t)(A->mb + 1) * 4 + A->T * (4 + 8 + 4 + 4) + (int64_t)(A->nb + 1) * 4;
-  A->st.format_bytes = A->st.payload_bytes + A->st.index_bytes + A->nseg * 16;
+  // views: block-CSR (rb_ptr, column blocks, metadata), block-CSC (cb_ptr,
+  // row blocks, primary ids, column sets)
+  A->st.index_bytes = (int64_t)(A->mb + 1) * 4 + A->T * (4 + 8 + 4 + 4 + 2) + (int64_t)(A->nb + 1) * 4;
+  // pattern matrices: the Boolean pull's segments, column-block words,
+  // metadata of the tiles not marked single, per-segment entries and word owners
+  int64_t pull_bytes = 0;
+  if (A->vk == VK_PAT)
+    pull_bytes = A->npseg * (16 + 8) + A->T * 4 + (A->meta2 != A->t_meta ? A->nmeta2 * 8 : 0) +
+                 (A->payload_bytes + DBS_PAYLOAD_SLACK) / 4;
+  A->st.format_bytes = A->st.payload_bytes + A->st.index_bytes + A->nseg * 16 + pull_bytes;
   *out = A;
   return DBS_OK;
 }
