@@ -194,11 +194,11 @@ __global__ void k_fill_u32(uint32_t *p, int64_t n, uint32_t v) {
 }
 
 struct SpmvParams {
-  const uint32_t *t_cb;
   const uint32_t *t_cbx;   // pattern matrices: the Boolean pull's column-block words
   const uint64_t *meta2;   // pattern matrices: metadata of the tiles not marked single
   const uint32_t *m2seg;   // pattern matrices: per pull segment, first entry in meta2 and entries
-  bool cbx_compact;        // nb <= CBX_MAX_NB: the words mark single tiles
+  int32_t cbx_compact;     // nb <= CBX_MAX_NB: the words mark single tiles
+  const uint32_t *t_cb;
   const uint64_t *t_meta;
   const uint32_t *cb_ptr;
   const uint32_t *csc_rb;
