@@ -15,8 +15,8 @@ typedef __attribute__((address_space(4))) const uint32_t cu32_t;  // read-only: 
 
 // the arrays the pull reads
 struct PatSrc {
-  const uint32_t *t_cb;
-  const uint64_t *t_meta;
+  const uint32_t *t_cb;     // value matrices (pat_issue)
+  const uint64_t *t_meta;   // value matrices (pat_issue)
   const uint32_t *segs;  // padded with 16 zeroed descriptors
   int64_t nseg;
   brsrc_t pay;  // payload and its zeroed slack
@@ -69,19 +69,20 @@ DBS_DEV void pat_issue(const PatSrc &S, const Pol &pol, int64_t s0, bool live, u
 
 // Pattern matrices (the graph workloads), pull.  A wave takes one segment of
 // up to 64*K tiles per step (K slices of 64 consecutive tiles, lane i holding
-// tile 64k+i of slice k), software-pipelined: the next segment's column
-// blocks and, when most vector blocks are active, metadata are in flight
-// while the current one waits for its masks and words.  Column blocks and metadata come through a buffer range cut to the
-// segment, so lanes past its end read 0 without any address arithmetic.  COO
-// tiles of up to four entries are decoded from their metadata word; the
-// coordinate words of the other COO tiles are consecutive in the COO section,
-// so the segment reads them as one run spread over the lanes (word j by lane
-// j) together with each word's owner tile (a byte per word, recorded at
-// build), whose mask the lane reads from LDS.  Larger tiles (Dense, ForceCSR,
-// ForceCSC, patched CSR: all keep the 16 row masks for pattern matrices) are
-// rare and read their masks per lane.  The work per segment that does not
-// grow with its tiles (descriptor, ballots, word setup, wave OR, writeback)
-// is what bounds this pull, hence segments of up to 256 tiles.
+// tile 64k+i of slice k), software-pipelined: the next segment's column-block
+// words and, when most vector blocks are active, its ranked tiles' metadata
+// are in flight while the current one waits for its masks and words.  Both
+// come through buffer ranges cut to the segment, so lanes past its end read 0
+// without any address arithmetic.  A tile of one entry is decoded from its
+// word; the ranked tiles are decoded in rank order: COO tiles of up to four
+// entries from their metadata word, the coordinate words of the other COO
+// tiles (consecutive in the COO section) as one run spread over the lanes
+// (word j by lane j) with each word's owner rank (a byte per word, recorded
+// at build), whose mask the lane reads from LDS, and the rare larger tiles
+// (Dense, ForceCSR, ForceCSC, patched CSR: all keep the 16 row masks for
+// pattern matrices) per lane.  The work per segment that does not grow with
+// its tiles (descriptor, ballots, word setup, wave OR, writeback) is a large
+// part of this pull's cost, hence segments of up to 256 tiles.
 template <int K>
 struct PatSeg {  // stage A: descriptor, column-block words, EAGER the ranked tiles' metadata (n == 0: no segment)
   uint32_t rb, t0, n, nrb;  // first row block, first tile, tiles, row blocks (uniform)
