@@ -1054,7 +1054,12 @@ dbs_status dbs_spmspv_impl(dbs_matrix *A, int32_t nnz_x, const int32_t *x_idx, c
   o.xmask = A->xmask;
   o.epoch = A->epoch;
   o.nbw = A->nbw;
-  o.bits_set = A->xbits ? A->xbits + (size_t)(A->epoch & 1u) * A->nbw : nullptr;
+  // the active-block bits serve only pulls that read metadata lazily (under
+  // a quarter of the blocks active); a sorted sparse x of more than 4 N_blk
+  // entries has more active blocks than that, so they are not written (the
+  // array this call would fill stays as the last call cleared it)
+  const bool lazy_possible = x_dense != nullptr || (int64_t)nnz_x <= 4 * (int64_t)A->nb;
+  o.bits_set = A->xbits && lazy_possible ? A->xbits + (size_t)(A->epoch & 1u) * A->nbw : nullptr;
   o.bits_clear = A->xbits ? A->xbits + (size_t)((A->epoch + 1u) & 1u) * A->nbw : nullptr;
   o.reg.ctr = A->ctr + 8 * A->cbuf;
   o.reg.list = A->act_list;
