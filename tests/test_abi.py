@@ -91,3 +91,16 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode == 2
     assert "one GPU only" in r.stdout + r.stderr
     assert r.stdout.strip() == "" or not r.stdout.lstrip().startswith("{")
+
+
+def test_build_helper_imports_without_the_library():
+    """The build helper must import on a tree where libdbs.so is not built yet,
+    without loading the binding (which refuses to load without the library)."""
+    import subprocess
+    import sys
+
+    code = ("import sys; from spmspv_graph_traversal_amd import build_lib; "
+            "assert callable(build_lib.build); "
+            "assert 'spmspv_graph_traversal_amd.binding' not in sys.modules")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
