@@ -117,7 +117,13 @@ DBS_DEV void block_bits_sparse(const MetaOut &o, int32_t nnz_x, const int32_t *x
 }
 
 // Sparse x: sorted x_idx.  The first entry of each vector block (the leader)
-// builds the block's mask from the following entries.
+// writes the block's mask: a strictly increasing x_idx holds a block's
+// entries one after another, so the mask is an OR over the run of lanes of
+// the same block, taken within the wave by a segmented OR (shuffles of
+// doubling distance that combine only lanes of equal block); the run of the
+// wave's last lane may go on for up to 15 entries after the wave, which its
+// leader reads with one load of the wave (lanes 0..14).  Each wave thus
+// issues three loads of x_idx rather than one per following entry.
 template <int VK>
 __global__ __launch_bounds__(dbs_meta::MT) void k_xmeta_sparse(MetaOut o, int32_t nnz_x, const int32_t *x_idx,
                                                      const void *x_val, void *xd, int check) {
@@ -138,20 +144,26 @@ __global__ __launch_bounds__(dbs_meta::MT) void k_xmeta_sparse(MetaOut o, int32_
       if (VK == VK_F32) ((float *)xd)[idx] = ((const float *)x_val)[i];
       else ((uint16_t *)xd)[idx] = ((const uint16_t *)x_val)[i];
     }
+    // (a strictly increasing x_idx holds at most 16 entries per block, so the
+    // check of every pair also rules out a 17th)
     if (check && valid && i > 0 && idx <= prev) atomicOr(&o.reg.ctr[2], 1u);
-    if (leader) {
-      // a strictly increasing x_idx holds at most 16 entries of block b, all
-      // right after the leader: 15 independent look-ahead loads (no chain)
-      uint32_t mk = 1u << (idx & 15);
+    const int lane = __lane_id();
+    const int32_t key = inb ? b : -1;
+    uint32_t mk = inb ? 1u << (idx & 15) : 0u;
 #pragma unroll
-      for (int k = 1; k < 16; ++k) {
-        const int64_t j = i + k < nnz_x ? i + k : i;  // clamped: no branch around the load
-        const int32_t v = x_idx[j];
-        if (i + k < nnz_x && (v >> 4) == b && v < o.n) mk |= 1u << (v & 15);
-      }
-      if (check && i + 16 < nnz_x && (x_idx[i + 16] >> 4) == b) atomicOr(&o.reg.ctr[2], 1u);
-      o.xmask[b] = (o.epoch << 16) | mk;
+    for (int d = 1; d < DBS_WAVE; d <<= 1) {
+      const uint32_t om = (uint32_t)__shfl_down((int)mk, d);
+      const int32_t ok = __shfl_down(key, d);
+      if ((lane + d < DBS_WAVE) & (ok == key)) mk |= om;
     }
+    // the entries after the wave that belong to its last lane's block
+    const int32_t lastk = __builtin_amdgcn_readlane(key, DBS_WAVE - 1);
+    const int64_t it = i + DBS_WAVE;  // lane j < 15: entry j after the wave
+    const bool tin = (lane < 15) & (it < nnz_x);
+    const int32_t tv = x_idx[tin ? it : ic];  // clamped: no branch around the load
+    const uint32_t tb = wave_or((tin & (tv >= 0) & (tv < o.n) & ((tv >> 4) == lastk)) ? 1u << (tv & 15) : 0u);
+    if (key == lastk) mk |= tb;
+    if (leader) o.xmask[b] = (o.epoch << 16) | mk;
   });
   block_bits_sparse(o, nnz_x, x_idx);
 }

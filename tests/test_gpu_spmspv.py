@@ -327,3 +327,31 @@ def test_unsorted_x_is_memory_safe(dbs, kind):
         assert 0 <= st["last_n_nzblk"] <= n // 16
         assert_close(run_plus(dbs, A, m, good, gv), yr, s, f"sorted call after unsorted, path {path}")
         np.testing.assert_array_equal(run_or(dbs, P, m, good), yb, err_msg=f"path {path}")
+
+
+@pytest.mark.parametrize("n,nblocks", [(1 << 16, 3000), (1 << 21, 90000)])
+def test_sparse_masks_runs_across_waves(dbs, n, nblocks):
+    """Block masks of a sparse x whose blocks hold 1 to 16 entries, so that a
+    block's run of entries starts at every lane offset and crosses the 64-entry
+    boundaries of the metadata kernel's waves; the larger case gives every
+    workgroup several rounds.  Masks, N_nzblk and the OR-AND product against
+    the oracle."""
+    rng = rng_for("test", 790, n)
+    blocks = np.sort(rng.choice(n // 16, nblocks, replace=False))
+    parts = []
+    for b in blocks:
+        k = int(rng.integers(1, 17))
+        parts.append(16 * b + np.sort(rng.choice(16, k, replace=False)))
+    xi = np.concatenate(parts).astype(np.int32)
+    rp, ci = rmat_csr(int(np.log2(n)), 2, rng_for("test", 791, n))
+    A = build(dbs, n, n, rp, ci, None, dbs.DBS_PATTERN)
+    dbs.dbs_set_option(A, dbs.DBS_OPT_CHECK, 1)
+    import torch
+
+    y = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dbs.dbs_spmspv(A, up(xi), None, dbs.DBS_OR_AND, y)
+    st = dbs.dbs_get_stats(A)
+    masks, nz = orc.xmeta(n, xi)
+    assert st["last_n_nzblk"] == nz
+    np.testing.assert_array_equal(dbs.dbs_copy_array(A, dbs.DBS_ARR_XMASK), masks)
+    np.testing.assert_array_equal(y.cpu().numpy(), orc.or_and_pull(n, n, rp, ci, xi))
