@@ -112,7 +112,10 @@ dbs_status dbs_build_options_default(dbs_build_options *opt);
  *   out       receives the new handle; untouched on error
  *
  * The CSR arrays may be freed once the call returns.  Returns DBS_ERR_BAD_CSR
- * for an invalid CSR (checked on the device before any other work).
+ * for an invalid CSR (checked on the device before any other work), and
+ * DBS_ERR_UNSUPPORTED for a format the kernels cannot address with their
+ * 32-bit byte offsets: a tile payload of more than 4,294,967,024 bytes (4 GiB -
+ * 272), or more than 536,870,910 tiles.
  */
 dbs_status dbs_build(int32_t m, int32_t n, int64_t nnz, const int32_t *row_ptr,
                      const int32_t *col_idx, const void *val, dbs_dtype dtype,
@@ -131,6 +134,9 @@ dbs_status dbs_build(int32_t m, int32_t n, int64_t nnz, const int32_t *row_ptr,
  *
  * One call launches the vector-metadata kernel and the SpMSpV kernel; the
  * push/pull choice (push iff N_nzblk / N_blk < th3) is taken on the device.
+ * DBS_PLUS_TIMES on a DBS_F32 matrix of more than 1,073,741,808 columns, or a
+ * DBS_BF16 one of more than 2,147,483,632 (x block-padded past 4 GiB - 16
+ * bytes), returns DBS_ERR_UNSUPPORTED; so do the dense calls below.
  * In check mode (DBS_OPT_CHECK) a non-increasing x_idx is flagged on the
  * device and reported by the next dbs_get_stats as DBS_ERR_BAD_VECTOR;
  * without check mode such input gives unspecified (but memory-safe) y.

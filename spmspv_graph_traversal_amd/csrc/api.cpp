@@ -243,6 +243,9 @@ dbs_status dbs_build(int32_t m, int32_t n, int64_t nnz, const int32_t *row_ptr, 
 static dbs_status check_semiring(const dbs_matrix *A, dbs_semiring sr) {
   if (sr != DBS_PLUS_TIMES && sr != DBS_OR_AND) return DBS_ERR_INVALID_ARG;
   if (sr == DBS_PLUS_TIMES && A->dtype == DBS_PATTERN) return DBS_ERR_INVALID_ARG;
+  // PLUS_TIMES stages x block-padded and reads it with 32-bit byte offsets
+  if (sr == DBS_PLUS_TIMES && !dbs_x_fits_offsets((uint64_t)A->nb, A->vk == VK_F32 ? 4u : 2u))
+    return DBS_ERR_UNSUPPORTED;
   return DBS_OK;
 }
 

@@ -985,7 +985,8 @@ dbs_status dbs_build_impl(dbs_matrix *A, const int32_t *row_ptr, const int32_t *
   // Dense row masks after the three value sections (value matrices only)
   A->dense_mask_off = (total + 127) & ~127ull;
   if (vk != VK_PAT) total = A->dense_mask_off + 32ull * (dense_bytes / (256ull * (uint64_t)vk_size(vk)));
-  if (total >= (1ull << 40)) return DBS_ERR_UNSUPPORTED;
+  // (the 40-bit offsets of the metadata word are looser than this)
+  if (!dbs_format_fits_offsets(total, (uint64_t)T)) return DBS_ERR_UNSUPPORTED;
   A->payload_bytes = (int64_t)total;
   BUILD_TRY(dbs_dev_alloc(A, (void **)&A->payload, (size_t)total + DBS_PAYLOAD_SLACK));
   BUILD_TRY(hipMemsetAsync(A->payload + total, 0, DBS_PAYLOAD_SLACK, s));

@@ -149,6 +149,18 @@ __host__ __device__ inline uint32_t seg_slot_class(int share) { return share >= 
 // zeroed bytes allocated after the payload: wide row loads that start inside
 // the last tile stay inside the allocation
 #define DBS_PAYLOAD_SLACK 256u
+// The kernels read the payload, the tile arrays and the staged x through
+// buffer descriptors with 32-bit byte offsets, 0xFFFFFFF0 marking a lane with
+// nothing to load; every real offset must stay below it.
+#define DBS_OFFSET_LIMIT 0xFFFFFFF0ull
+// a built format: payload (with its slack) and per-tile metadata (8 B a tile)
+__host__ __device__ inline bool dbs_format_fits_offsets(uint64_t payload_bytes, uint64_t tiles) {
+  return payload_bytes + DBS_PAYLOAD_SLACK <= DBS_OFFSET_LIMIT && tiles * 8u <= DBS_OFFSET_LIMIT;
+}
+// the block-padded x of a PLUS_TIMES call: 16 values of vs bytes per block
+__host__ __device__ inline bool dbs_x_fits_offsets(uint64_t nb, uint64_t vs) {
+  return nb * 16u * vs <= DBS_OFFSET_LIMIT;
+}
 // tiles per pull segment at most, pattern matrices (the Boolean pull's wave
 // holds four tiles per lane)
 #define DBS_PAT_SEG_CAP 256

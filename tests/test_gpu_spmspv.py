@@ -355,3 +355,43 @@ def test_sparse_masks_runs_across_waves(dbs, n, nblocks):
     assert st["last_n_nzblk"] == nz
     np.testing.assert_array_equal(dbs.dbs_copy_array(A, dbs.DBS_ARR_XMASK), masks)
     np.testing.assert_array_equal(y.cpu().numpy(), orc.or_and_pull(n, n, rp, ci, xi))
+
+
+def test_widest_x_the_offsets_allow(dbs):
+    """x block-padded to the last byte the 32-bit buffer offsets reach: an f32
+    matrix of 1,073,741,808 columns multiplies correctly (entries in the last
+    columns, so the largest offsets are used); one of 2^30 columns is refused
+    for PLUS_TIMES and still takes OR-AND."""
+    import gc
+
+    import torch
+
+    m = 40
+    for n, plus_ok in ((1073741808, True), (1 << 30, False)):
+        cols = np.array([0, 17, n // 2, n - 17, n - 2, n - 1], np.int64)
+        rows = [3, 3, 10, 10, 39, 39]
+        rp = np.zeros(m + 1, np.int32)
+        for r in rows:
+            rp[r + 1:] += 1
+        ci = cols.astype(np.int32)
+        v = rng_for("test", 795).uniform(-1, 1, ci.shape[0]).astype(np.float32)
+        A = build(dbs, m, n, rp, ci, v, dbs.DBS_F32)
+        xi = np.array([17, n // 2, n - 2, n - 1], np.int32)
+        xv = np.array([0.5, -2.0, 1.5, 3.0], np.float32)
+        if plus_ok:
+            for path in PATHS:
+                dbs.dbs_set_option(A, dbs.DBS_OPT_PATH, path)
+                yr, s = orc.spmspv_pull(m, n, rp, ci, v, orc.F32, xi, xv, orc.F32)
+                assert_close(run_plus(dbs, A, m, xi, xv), yr, s, f"n={n} path {path}")
+            dbs.dbs_set_option(A, dbs.DBS_OPT_PATH, 0)
+        else:
+            y = torch.empty(m, dtype=torch.float32, device="cuda")
+            with pytest.raises(dbs.DBSError) as e:
+                dbs.dbs_spmspv(A, up(xi), up(xv), dbs.DBS_PLUS_TIMES, y)
+            assert e.value.status == dbs.DBS_ERR_UNSUPPORTED
+        yb = torch.empty(m, dtype=torch.uint8, device="cuda")
+        dbs.dbs_spmspv(A, up(xi), None, dbs.DBS_OR_AND, yb)
+        np.testing.assert_array_equal(yb.cpu().numpy(), orc.or_and_pull(m, n, rp, ci, xi))
+        del A
+        gc.collect()
+        torch.cuda.synchronize()

@@ -28,3 +28,16 @@ def test_push_list_bounds_host(tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "0 failures" in r.stdout
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC) and shutil.which("hipcc") is None, reason="hipcc not found")
+def test_offset_limits_host(tmp_path):
+    src = os.path.join(HERE, "host_checks", "offset_bounds.cpp")
+    exe = str(tmp_path / "offset_bounds")
+    hipcc = HIPCC if os.path.exists(HIPCC) else shutil.which("hipcc")
+    r = subprocess.run([hipcc, "--offload-host-only", "-x", "hip", "-std=c++17", "-O1", src, "-o", exe],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert " 0 failures" in r.stdout
