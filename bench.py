@@ -683,6 +683,63 @@ def bench_format_ablation(dbs, torch, args):
     return out
 
 
+def bench_decode_th1(dbs, torch, args):
+    """Decode layers with the Dense threshold th1 at the paper's 128 and at 48
+    (activation with 50% zeros): per call warm and with rotating copies, kernel
+    time and format size.  On this GPU a patched-CSR tile costs about ten times
+    the vector instructions of a Dense one, so the layers run faster as Dense
+    tiles although those hold more bytes."""
+    from synth import decode_activation, decode_weight_csr, rng_for
+
+    dev = torch.device("cuda:0")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    steps, ncopy = max(args.steps, 10), 6
+    out = []
+    for rows, cols in [(11008, 4096), (4096, 11008)]:
+        for sp in (0.5, 0.7):
+            rp, ci, bits = decode_weight_csr(rows, cols, sp, rng_for("decode", rows, int(sp * 10)))
+            rp_d, ci_d = torch.from_numpy(rp).to(dev), torch.from_numpy(ci).to(dev)
+            v_d = torch.from_numpy(bits.view(np.int16)).to(dev)
+            x = decode_activation(cols, 0.5, rng_for("decode", rows, int(sp * 10), 5))
+            xd = torch.from_numpy(x.view(np.int16)).to(dev)
+            y = torch.empty(rows, dtype=torch.float32, device=dev)
+            for th1 in (128, 48):
+                o = dbs.default_build_options()
+                o.th1 = th1
+                copies = [dbs.dbs_build(rows, cols, rp_d, ci_d, v_d, dbs.DBS_BF16, options=o) for _ in range(ncopy)]
+                st = dbs.dbs_get_stats(copies[0])
+                for c in copies:
+                    for _ in range(2):
+                        dbs.dbs_spmspv_dense(c, xd, dbs.DBS_PLUS_TIMES, y)
+                torch.cuda.synchronize()
+                ev0.record()
+                for _ in range(steps):
+                    dbs.dbs_spmspv_dense(copies[0], xd, dbs.DBS_PLUS_TIMES, y)
+                ev1.record()
+                torch.cuda.synchronize()
+                warm = ev0.elapsed_time(ev1) / steps * 1e3
+                ev0.record()
+                for r in range(steps):
+                    dbs.dbs_spmspv_dense(copies[r % ncopy], xd, dbs.DBS_PLUS_TIMES, y)
+                ev1.record()
+                torch.cuda.synchronize()
+                cold = ev0.elapsed_time(ev1) / steps * 1e3
+                dbs.dbs_set_option(copies[0], dbs.DBS_OPT_TIMING, 1)
+                for _ in range(steps):
+                    dbs.dbs_spmspv_dense(copies[0], xd, dbs.DBS_PLUS_TIMES, y)
+                s2 = dbs.dbs_get_stats(copies[0])
+                row = {"shape": [rows, cols], "weight_sparsity": sp, "th1": th1,
+                       "tiles_by_format": st["tiles_by_format"], "size": format_size(st, rows, cols, 2),
+                       "us_warm": round(warm, 2), "us_rotating_copies": round(cold, 2),
+                       "compute_kernel_us_warm": round(s2["sum_compute_ms"] / s2["timed_calls"] * 1e3, 2)}
+                out.append(row)
+                log(f"[bench] decode th1 ablation: {row}")
+                del copies
+                gc.collect()
+                torch.cuda.synchronize()
+    return out
+
+
 ZIPF_DENSITIES = [1e-5, 1e-4, 1e-3, 1e-2, 5e-2, 0.2]
 
 
@@ -837,6 +894,7 @@ def main():
         extra["zipf_band"] = bench_zipf(dbs, torch, args)
     if not args.no_ablations:
         extra["format_ablation"] = bench_format_ablation(dbs, torch, args)
+        extra["decode_dense_threshold_ablation"] = bench_decode_th1(dbs, torch, args)
     traffic = load_traffic("rmat20_sweep")
     copy_gbps = measure_copy_gbps(torch)
     log(f"[bench] device copy: {copy_gbps} GB/s (read + write)")
