@@ -108,6 +108,21 @@ class Format:
         self.cb_pay = cum[self.cb_ptr[1:]] - cum[self.cb_ptr[:-1]]
         self.cb_chunks = (self.cb_tiles + 63) // 64
 
+    def pull_bytes_in(self, dbs, A, act_blocks, need_rb, ybytes):
+        """Pull bytes of one call restricted to the tiles of the row blocks in
+        need_rb (a BFS pull level reads no tile of a row block whose rows are
+        all visited); the segment descriptors in proportion to those tiles."""
+        if not hasattr(self, "t_rb"):
+            rb_ptr = dbs.dbs_copy_array(A, dbs.DBS_ARR_RB_PTR).astype(np.int64)
+            self.t_rb = np.repeat(np.arange(rb_ptr.shape[0] - 1), np.diff(rb_ptr))
+        sel = need_rb[self.t_rb]
+        active = np.zeros(self.nb, bool)
+        active[act_blocks] = True
+        at = active[self.t_cb] & sel
+        nsel = int(sel.sum())
+        return (16 * self.nseg * nsel // max(self.T, 1) + 4 * nsel + 4 * self.nb + 8 * int(at.sum())
+                + int(self.pay[at].sum()) + ybytes)
+
     def call_bytes(self, act_blocks, nnz_x, ybytes, push, vsize=0):
         """(metadata bytes, compute bytes) of one call."""
         nact = act_blocks.shape[0]
@@ -472,18 +487,26 @@ def bench_bfs22(dbs, torch, args):
     # bytes of the first source's BFS in the SpMSpV byte model: every level
     # a masked OR-AND SpMSpV of its frontier (push or pull by the th3 rule),
     # writing the next frontier's bitmap (n/8 B) and 4 B per found vertex,
-    # plus the frontier metadata (bitmap scan and block list).  The pull
-    # levels' early exit (row blocks with nothing left to find are skipped)
-    # reads less than this, so the model bounds the work of each level from
-    # above.
+    # plus the frontier metadata (bitmap scan and block list).  A pull level
+    # reads only the row blocks that still hold an unvisited row with an
+    # entry, so its tiles are counted in those row blocks only; within them
+    # it may stop early (a long row block whose rows its first segment
+    # found), so the model still bounds the level's reads from above.
     fmt = Format(dbs, A, 2)
     model_bytes = 0
+    mbk = (n + 15) // 16
     for L in range(int(ref.max()) + 1):
         fr = np.nonzero(ref == L)[0]
         act = np.unique(fr // 16)
         nxt = int(np.count_nonzero(ref == L + 1))
         push = 100 * act.shape[0] < fmt.nb
-        _, cb = fmt.call_bytes(act, fr.shape[0], n // 8 + 4 * nxt, push)
+        if push:
+            _, cb = fmt.call_bytes(act, fr.shape[0], n // 8 + 4 * nxt, push)
+        else:
+            wanted = (deg > 0) & ((ref > L) | (ref < 0))
+            need = np.zeros(16 * mbk, bool)
+            need[:n] = wanted
+            cb = fmt.pull_bytes_in(dbs, A, act, need.reshape(mbk, 16).any(axis=1), n // 8 + 4 * nxt)
         model_bytes += cb + n // 8 + 8 * act.shape[0]
     del fmt
     gc.collect()
