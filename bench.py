@@ -524,7 +524,7 @@ def bench_bfs22(dbs, torch, args):
             "first_source_frac_of_hbm": round(model_bytes / (times[0] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "first_source_level_kernels_frac_of_hbm": round(model_bytes / (ktimes[0] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "first_source_reached": int(reached),
-            "build_peak_bytes": st["build_peak_bytes"],
+            "build_peak_bytes": st["build_peak_bytes"], "size": format_size(st, n, n, 0),
             "oracle_gteps_first_source": round(edges / cpu_bfs_s / 1e9, 4), "build_s": round(build_s, 2),
             "path_ablation_first_8_sources": ablation}
 
@@ -779,8 +779,8 @@ def bench_zipf(dbs, torch, args):
     log(f"[bench] zipf generated: nnz={ci.shape[0]} max_row={int(lens.max())} in {gen_s:.1f}s")
     dev = torch.device("cuda:0")
     t0 = time.time()
-    A = dbs.dbs_build(n, n, torch.from_numpy(rp).to(dev), torch.from_numpy(ci).to(dev),
-                      torch.from_numpy(v).to(dev), dbs.DBS_F32)
+    rp_d, ci_d, v_d = torch.from_numpy(rp).to(dev), torch.from_numpy(ci).to(dev), torch.from_numpy(v).to(dev)
+    A = dbs.dbs_build(n, n, rp_d, ci_d, v_d, dbs.DBS_F32)
     torch.cuda.synchronize()
     build_s = time.time() - t0
     colcount = np.bincount(ci, minlength=n)
@@ -789,7 +789,7 @@ def bench_zipf(dbs, torch, args):
     fmt = Format(dbs, A, 0)
     y = torch.empty(n, dtype=torch.float32, device=dev)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    per = []
+    per, forced = [], []
     for k, d in enumerate(ZIPF_DENSITIES):
         xi, xv = sparse_x_with_dense_blocks(n, d, rng_for("zipf", 1, k))
         act = np.unique(xi // 16)
@@ -824,7 +824,45 @@ def bench_zipf(dbs, torch, args):
             "compute_kernel_frac_of_hbm": round(cb / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         })
         log(f"[bench] zipf d={d}: {per[-1]}")
+        # the selector's ablation: the kernel with push and with pull forced
+        row = {"density": d, "xb_ratio": per[-1]["xb_ratio"]}
+        for path, name in ((1, "push"), (2, "pull")):
+            dbs.dbs_set_option(A, dbs.DBS_OPT_PATH, path)
+            dbs.dbs_set_option(A, dbs.DBS_OPT_TIMING, 1)
+            for _ in range(min(args.steps, 5)):
+                dbs.dbs_spmspv(A, xi_d, xv_d, dbs.DBS_PLUS_TIMES, y)
+            s3 = dbs.dbs_get_stats(A)
+            row[f"{name}_kernel_us"] = round(s3["sum_compute_ms"] / s3["timed_calls"] * 1e3, 2)
+        forced.append(row)
+        dbs.dbs_set_option(A, dbs.DBS_OPT_PATH, 0)
+        dbs.dbs_set_option(A, dbs.DBS_OPT_TIMING, 0)
+        log(f"[bench] zipf forced paths d={d}: {forced[-1]}")
     dbs.dbs_set_option(A, dbs.DBS_OPT_TIMING, 0)
+    # tile-format ablation (the matrix is 99.99% COO tiles under the
+    # adaptive rule, so COO-only is the same build): every tile patched CSR
+    csr_only = None
+    if not args.no_ablations:
+        dbs.dbs_free(A)
+        o = dbs.default_build_options()
+        o.force_format = FORMATS["CSR-only"]
+        B = dbs.dbs_build(n, n, rp_d, ci_d, v_d, dbs.DBS_F32, options=o)
+        sb = dbs.dbs_get_stats(B)
+        csr_only = {"format_MB": round(sb["format_bytes"] / 1e6, 1)}
+        for k, d in enumerate(ZIPF_DENSITIES):
+            if d not in (1e-3, 1e-2, 0.2):
+                continue
+            xi, xv = sparse_x_with_dense_blocks(n, d, rng_for("zipf", 1, k))
+            xi_d, xv_d = torch.from_numpy(xi).to(dev), torch.from_numpy(xv).to(dev)
+            dbs.dbs_spmspv(B, xi_d, xv_d, dbs.DBS_PLUS_TIMES, y)
+            dbs.dbs_set_option(B, dbs.DBS_OPT_TIMING, 1)
+            for _ in range(min(args.steps, 5)):
+                dbs.dbs_spmspv(B, xi_d, xv_d, dbs.DBS_PLUS_TIMES, y)
+            s3 = dbs.dbs_get_stats(B)
+            dbs.dbs_set_option(B, dbs.DBS_OPT_TIMING, 0)
+            csr_only[str(d)] = round(s3["sum_compute_ms"] / s3["timed_calls"] * 1e3, 2)
+        dbs.dbs_free(B)
+        log(f"[bench] zipf CSR-only: {csr_only}")
+    del rp_d, ci_d, v_d
     hist = np.bincount(np.floor(np.log2(np.maximum(lens, 1))).astype(np.int64))
     bf = args.zipf_band_frac
     return {"workload": f"zipf(1.8) row lengths capped at 2^20, {100 * bf:g}% band + {100 * (1 - bf):g}% uniform, "
@@ -832,8 +870,9 @@ def bench_zipf(dbs, torch, args):
             "nnz": int(lens.sum()), "max_row": int(lens.max()),
             "row_length_log2_histogram": hist.tolist(), "generate_s": round(gen_s, 1), "build_s": round(build_s, 2),
             "tiles": st["tiles"], "tiles_by_format": st["tiles_by_format"], "segments": st["segments"],
-            "format_MB": round(st["format_bytes"] / 1e6, 1), "build_peak_bytes": st["build_peak_bytes"],
-            "per_density": per}
+            "format_MB": round(st["format_bytes"] / 1e6, 1), "size": format_size(st, n, n, 4),
+            "build_peak_bytes": st["build_peak_bytes"], "per_density": per,
+            "forced_paths": forced, "xb_crossover": crossover(forced), "format_ablation_csr_only_kernel_us": csr_only}
 
 
 def main():
