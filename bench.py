@@ -14,9 +14,12 @@ second pass over the same calls with DBS_OPT_TIMING on, where each kernel
 dispatch records its own start and end (those events cost the host and the
 device a few µs per call, so they are kept out of the throughput passes).
 
-Also reported (nested under "extra"): per-density numbers; the selector
-ablation (the kernel with push and with pull forced at every density, and the
-x-block ratio where they cross); BFS on R-MAT scale 22 from 64 seeded sources
+Also reported (nested under "extra"): per-density numbers, with B_min (the
+bytes without the pull's full scan of the tiles' column blocks, so that a
+wasteful path choice shows); the selector ablation (the kernel with push and
+with pull forced at every density, and the x-block ratio where they cross);
+the same sweep on the R-MAT 20 graph with its vertices relabelled at random
+(about one entry per tile; `--no-permuted` skips it); BFS on R-MAT scale 22 from 64 seeded sources
 of the largest component (GTEPS) with an Auto / Push / Pull ablation on 8 of
 them; the single-token decode layers 11008x4096 / 4096x11008 (µs per call,
 warm and with rotating copies to defeat the on-package cache), also with the
@@ -26,7 +29,9 @@ x 1%); the Zipf/band stress matrix; GFLOP/s of the plus-times workloads in the
 SpMV-equivalent count 2 nnz(A) and the useful count 2 nnz(A[:, J]); and the
 tile-format ablation (COO-only / CSR-only / adaptive; `--no-ablations` skips
 it).  The CPU baseline is the oracle's Boolean pull on one host thread, with
-the same loop on every host core beside it.
+the same loop on every host core beside it.  Beside the published 8 TB/s, the roofline
+object gives the box's measured bandwidth of a device copy (read + write) and
+of a streaming read (the library's read probe over 1 GiB).
 
 Byte model (bytes a kernel must move for the path it takes; per call):
   pull     16*segments + 4*T (column block of every tile) + 4*N_blk (masks)
@@ -240,8 +245,79 @@ def bench_tiny(dbs, torch, args):
     return out
 
 
+def sweep_inputs(torch, fmt, n, key):
+    """The sweep's x vectors (OR-AND: indices only; density k drawn from
+    rng_for(*key, k)) with the byte model of each call.  `scan_bytes` is
+    the pull's full scan term (segment descriptors, every tile's column-block
+    word, the masks), which B_min leaves out so that a wasteful path choice
+    shows."""
+    from synth import rng_for, sparse_x
+
+    xs = []
+    for k, d in enumerate(DENSITIES):
+        xi, _ = sparse_x(n, d, rng_for(*key, k), with_values=False)
+        act = np.unique(xi // 16)
+        push = 100 * act.shape[0] < fmt.nb
+        mb, cb = fmt.call_bytes(act, xi.shape[0], n, push)
+        scan = 0 if push else 16 * fmt.nseg + 4 * fmt.T + 4 * fmt.nb
+        xs.append(dict(density=d, xi=xi, x=torch.from_numpy(xi).to("cuda"), nact=act.shape[0], push=push,
+                       meta_bytes=mb, comp_bytes=cb, scan_bytes=scan))
+    return xs
+
+
+def sweep_per_density(dbs, torch, args, A, fmt, xs, y):
+    """Per density: call and kernel times, bytes (and B_min), GB/s and the
+    roofline fraction; then the kernel with push and with pull forced."""
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # per-density breakdown (separate loops, same kernels)
+    per = []
+    for x in xs:
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(args.steps):
+            dbs.dbs_spmspv(A, x["x"], None, dbs.DBS_OR_AND, y)
+        ev1.record()
+        torch.cuda.synchronize()
+        call_ms = ev0.elapsed_time(ev1) / args.steps
+        dbs.dbs_set_option(A, dbs.DBS_OPT_TIMING, 1)
+        for _ in range(args.steps):
+            dbs.dbs_spmspv(A, x["x"], None, dbs.DBS_OR_AND, y)
+        s2 = dbs.dbs_get_stats(A)
+        dbs.dbs_set_option(A, dbs.DBS_OPT_TIMING, 0)
+        kms = s2["sum_compute_ms"] / s2["timed_calls"]
+        mms = s2["sum_meta_ms"] / s2["timed_calls"]
+        per.append({
+            "density": x["density"], "nnz_x": int(x["xi"].shape[0]), "n_nzblk": s2["last_n_nzblk"],
+            "xb_ratio": round(s2["last_n_nzblk"] / fmt.nb, 5), "path": "push" if s2["last_path"] == 0 else "pull",
+            "call_us": round(call_ms * 1e3, 2), "compute_kernel_us": round(kms * 1e3, 2),
+            "meta_kernel_us": round(mms * 1e3, 2),
+            "bytes": int(x["meta_bytes"] + x["comp_bytes"]),
+            "bytes_min": int(x["meta_bytes"] + x["comp_bytes"] - x["scan_bytes"]),
+            "call_GBps": round((x["meta_bytes"] + x["comp_bytes"]) / (call_ms * 1e-3) / 1e9, 1),
+            "compute_kernel_GBps": round(x["comp_bytes"] / (kms * 1e-3) / 1e9, 1),
+            "compute_kernel_frac_of_hbm": round(x["comp_bytes"] / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        })
+    # ablation of the global selector: the kernel with push and with pull
+    # forced at every density, and the x-block ratio where the two cross
+    forced = []
+    for x in xs:
+        row = {"density": x["density"]}
+        for path, name in ((1, "push"), (2, "pull")):
+            dbs.dbs_set_option(A, dbs.DBS_OPT_PATH, path)
+            dbs.dbs_set_option(A, dbs.DBS_OPT_TIMING, 1)
+            for _ in range(args.steps):
+                dbs.dbs_spmspv(A, x["x"], None, dbs.DBS_OR_AND, y)
+            s2 = dbs.dbs_get_stats(A)
+            row[f"{name}_kernel_us"] = round(s2["sum_compute_ms"] / s2["timed_calls"] * 1e3, 2)
+            row["xb_ratio"] = round(s2["last_n_nzblk"] / fmt.nb, 5)
+        forced.append(row)
+    dbs.dbs_set_option(A, dbs.DBS_OPT_PATH, 0)
+    dbs.dbs_set_option(A, dbs.DBS_OPT_TIMING, 0)
+    return per, forced
+
+
 def bench_rmat20(dbs, torch, args):
-    from synth import rmat_csr, rng_for, sparse_x
+    from synth import rmat_csr, rng_for
 
     t0 = time.time()
     rp, ci = rmat_csr(20, 16, rng_for("rmat20"))
@@ -256,14 +332,7 @@ def bench_rmat20(dbs, torch, args):
     log(f"[bench] rmat20 built in {build_s:.2f}s: tiles={st['tiles']} segments={st['segments']} "
         f"format={st['format_bytes'] / 1e6:.1f} MB")
     fmt = Format(dbs, A, 2)
-    xs = []
-    for k, d in enumerate(DENSITIES):
-        xi, _ = sparse_x(n, d, rng_for("rmat20", 1, k), with_values=False)
-        act = np.unique(xi // 16)
-        push = 100 * act.shape[0] < fmt.nb
-        mb, cb = fmt.call_bytes(act, xi.shape[0], n, push)
-        xs.append(dict(density=d, xi=xi, x=torch.from_numpy(xi).to(dev), nact=act.shape[0], push=push,
-                       meta_bytes=mb, comp_bytes=cb))
+    xs = sweep_inputs(torch, fmt, n, ("rmat20", 1))
     y = torch.empty(n, dtype=torch.uint8, device=dev)
 
     def step():
@@ -299,49 +368,7 @@ def bench_rmat20(dbs, torch, args):
     kernel_ms = st["sum_compute_ms"] / st["timed_calls"]
     achieved = comp_bytes / len(xs) / (kernel_ms * 1e-3) / 1e9
 
-    # per-density breakdown (separate loops, same kernels)
-    per = []
-    for x in ([] if args.headline_only else xs):
-        torch.cuda.synchronize()
-        ev0.record()
-        for _ in range(args.steps):
-            dbs.dbs_spmspv(A, x["x"], None, dbs.DBS_OR_AND, y)
-        ev1.record()
-        torch.cuda.synchronize()
-        call_ms = ev0.elapsed_time(ev1) / args.steps
-        dbs.dbs_set_option(A, dbs.DBS_OPT_TIMING, 1)
-        for _ in range(args.steps):
-            dbs.dbs_spmspv(A, x["x"], None, dbs.DBS_OR_AND, y)
-        s2 = dbs.dbs_get_stats(A)
-        dbs.dbs_set_option(A, dbs.DBS_OPT_TIMING, 0)
-        kms = s2["sum_compute_ms"] / s2["timed_calls"]
-        mms = s2["sum_meta_ms"] / s2["timed_calls"]
-        per.append({
-            "density": x["density"], "nnz_x": int(x["xi"].shape[0]), "n_nzblk": s2["last_n_nzblk"],
-            "xb_ratio": round(s2["last_n_nzblk"] / fmt.nb, 5), "path": "push" if s2["last_path"] == 0 else "pull",
-            "call_us": round(call_ms * 1e3, 2), "compute_kernel_us": round(kms * 1e3, 2),
-            "meta_kernel_us": round(mms * 1e3, 2),
-            "bytes": int(x["meta_bytes"] + x["comp_bytes"]),
-            "call_GBps": round((x["meta_bytes"] + x["comp_bytes"]) / (call_ms * 1e-3) / 1e9, 1),
-            "compute_kernel_GBps": round(x["comp_bytes"] / (kms * 1e-3) / 1e9, 1),
-            "compute_kernel_frac_of_hbm": round(x["comp_bytes"] / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        })
-    # ablation of the global selector: the kernel with push and with pull
-    # forced at every density, and the x-block ratio where the two cross
-    forced = []
-    for x in ([] if args.headline_only else xs):
-        row = {"density": x["density"]}
-        for path, name in ((1, "push"), (2, "pull")):
-            dbs.dbs_set_option(A, dbs.DBS_OPT_PATH, path)
-            dbs.dbs_set_option(A, dbs.DBS_OPT_TIMING, 1)
-            for _ in range(args.steps):
-                dbs.dbs_spmspv(A, x["x"], None, dbs.DBS_OR_AND, y)
-            s2 = dbs.dbs_get_stats(A)
-            row[f"{name}_kernel_us"] = round(s2["sum_compute_ms"] / s2["timed_calls"] * 1e3, 2)
-            row["xb_ratio"] = round(s2["last_n_nzblk"] / fmt.nb, 5)
-        forced.append(row)
-    dbs.dbs_set_option(A, dbs.DBS_OPT_PATH, 0)
-    dbs.dbs_set_option(A, dbs.DBS_OPT_TIMING, 0)
+    per, forced = ([], []) if args.headline_only else sweep_per_density(dbs, torch, args, A, fmt, xs, y)
     res = {
         "ms_per_step": ms_per_step, "value": value, "step_bytes": step_bytes,
         "kernel_avg_us": kernel_ms * 1e3, "achieved": achieved, "comp_bytes_per_launch": comp_bytes / len(xs),
@@ -352,6 +379,65 @@ def bench_rmat20(dbs, torch, args):
         "graph": (rp, ci, n), "xs": xs,
     }
     return res
+
+
+def bench_rmat20_permuted(dbs, torch, args, rp, ci, n):
+    """The R-MAT 20 graph with its vertices relabelled at random (a secondary
+    stress for the tile format: ~1.0 entries per tile instead of ~1.6), the
+    same OR-AND sweep as the headline, per density and with the paths forced."""
+    from synth import permute_vertices, rng_for
+
+    t0 = time.time()
+    prp, pci = permute_vertices(rp, ci, rng_for("rmat20", 2))
+    log(f"[bench] rmat20 permuted: nnz={int(prp[-1])} in {time.time() - t0:.1f}s")
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    A = dbs.dbs_build(n, n, torch.from_numpy(prp).to(dev), torch.from_numpy(pci).to(dev), None, dbs.DBS_PATTERN)
+    torch.cuda.synchronize()
+    build_s = time.time() - t0
+    st = dbs.dbs_get_stats(A)
+    fmt = Format(dbs, A, 2)
+    xs = sweep_inputs(torch, fmt, n, ("rmat20", 3))
+    y = torch.empty(n, dtype=torch.uint8, device=dev)
+    for _ in range(args.warmup):
+        for x in xs:
+            dbs.dbs_spmspv(A, x["x"], None, dbs.DBS_OR_AND, y)
+    torch.cuda.synchronize()
+    per, forced = sweep_per_density(dbs, torch, args, A, fmt, xs, y)
+    kus = [p["compute_kernel_us"] for p in per]
+    comp = [x["comp_bytes"] for x in xs]
+    out = {
+        "workload": "R-MAT scale 20, edge factor 16, symmetrized, vertices relabelled by a seeded random "
+                    "permutation; OR-AND; the headline's x densities",
+        "nnz": int(prp[-1]), "tiles": st["tiles"], "entries_per_tile": round(int(prp[-1]) / st["tiles"], 3),
+        "segments": st["segments"], "tiles_by_format": st["tiles_by_format"], "build_s": round(build_s, 2),
+        "size": format_size(st, n, n, 0), "build_peak_bytes": st["build_peak_bytes"],
+        "per_density": per, "forced_paths": forced, "xb_crossover": crossover(forced),
+        "sweep_kernel_frac_of_hbm": round(sum(comp) / (sum(kus) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+    }
+    dbs.dbs_free(A)
+    return out
+
+
+def measure_read_gbps(dbs, torch, gib=1, reps=10):
+    """Streaming read bandwidth: the library's read probe (16-byte loads over
+    `gib` GiB, nothing written) timed with HIP events on the stream it runs
+    on."""
+    a = torch.ones(gib << 28, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dbs.dbs_probe_read(a, sink)  # words of 1.0f XOR to 0, never 0xFFFFFFFF
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dbs.dbs_probe_read(a, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 0
+    gbps = a.numel() * 4 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, sink
+    torch.cuda.empty_cache()
+    return round(gbps, 1)
 
 
 def measure_copy_gbps(torch, gib=1, reps=10):
@@ -887,6 +973,8 @@ def main():
     ap.add_argument("--no-ablations", action="store_true",
                     help="skip the tile-format ablation (COO-only / CSR-only / adaptive builds)")
     ap.add_argument("--no-tiny", action="store_true")
+    ap.add_argument("--no-permuted", action="store_true",
+                    help="skip the R-MAT 20 sweep on the randomly relabelled graph")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the decode layers (for profiling the decode kernel); prints their JSON")
     ap.add_argument("--bfs-only", action="store_true",
@@ -941,9 +1029,15 @@ def main():
     cpu = None
     if args.headline_only:
         args.no_cpu = args.no_bfs = args.no_decode = args.no_zipf = args.no_ablations = args.no_tiny = True
+        args.no_permuted = True
     if not args.no_cpu:
         cpu = cpu_baseline_rmat20(res, args.cpu_seconds)
         log(f"[bench] cpu baseline: {cpu}")
+    if not args.no_permuted:
+        rp, ci, n = res["graph"]
+        extra["rmat20_permuted"] = bench_rmat20_permuted(dbs, torch, args, rp, ci, n)
+        log(f"[bench] rmat20 permuted: {extra['rmat20_permuted']}")
+        del rp, ci
     del res["graph"], res["xs"]
     if not args.no_bfs:
         extra["bfs_rmat22"] = bench_bfs22(dbs, torch, args)
@@ -960,6 +1054,8 @@ def main():
     traffic = load_traffic("rmat20_sweep")
     copy_gbps = measure_copy_gbps(torch)
     log(f"[bench] device copy: {copy_gbps} GB/s (read + write)")
+    read_gbps = measure_read_gbps(dbs, torch)
+    log(f"[bench] device read: {read_gbps} GB/s")
     line = {
         "metric": METRIC,
         "value": round(res["value"], 2),
@@ -981,7 +1077,9 @@ def main():
                      "kernel": "k_spmspv<pattern, or-and>", "kernel_avg_us": round(res["kernel_avg_us"], 2),
                      "algorithmic_bytes_per_launch": int(res["comp_bytes_per_launch"]),
                      "measured_copy_GBps": copy_gbps,
-                     "frac_of_measured_copy": round(res["achieved"] / copy_gbps, 4)},
+                     "frac_of_measured_copy": round(res["achieved"] / copy_gbps, 4),
+                     "measured_read_GBps": read_gbps,
+                     "frac_of_measured_read": round(res["achieved"] / read_gbps, 4)},
         "cpu_baseline": cpu,
         "extra": extra,
     }

@@ -327,6 +327,19 @@ dbs_status dbs_free(dbs_handle A);
 /* Static description of a status code. */
 const char *dbs_status_string(dbs_status s);
 
+/*
+ * dbs_probe_read — a measurement helper, not part of the method: reads the
+ * `bytes` bytes at device address `buf` once, with 16-byte vector loads from
+ * a grid of eight 256-thread workgroups per compute unit, and writes nothing
+ * unless the XOR of some thread's words equals `never` (then that value goes
+ * to the device word *sink; pick a value the data cannot produce).  Timing it
+ * on a stream gives the streaming-read bandwidth of the device, the yardstick
+ * beside the published HBM peak for the byte-model roofline of the SpMSpV
+ * kernels.  `buf` 16-byte aligned, `bytes` a positive multiple of 16, `sink`
+ * a device uint32; else DBS_ERR_INVALID_ARG.  Asynchronous on `stream`.
+ */
+dbs_status dbs_probe_read(const void *buf, int64_t bytes, uint32_t *sink, uint32_t never, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

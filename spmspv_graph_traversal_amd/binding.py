@@ -66,7 +66,7 @@ class dbs_stats(C.Structure):
 EXPORTED = ["dbs_build_options_default", "dbs_build", "dbs_spmspv", "dbs_spmspv_dense",
             "dbs_spmspv_dense_threshold", "dbs_bfs", "dbs_bfs_noalloc",
             "dbs_set_option", "dbs_get_option", "dbs_get_stats", "dbs_copy_array", "dbs_free",
-            "dbs_status_string"]
+            "dbs_status_string", "dbs_probe_read"]
 
 
 def load_library(path: str = LIB_PATH) -> C.CDLL:
@@ -95,6 +95,7 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
         "dbs_get_stats": [vp, C.POINTER(dbs_stats)],
         "dbs_copy_array": [vp, i32, vp, i64, C.POINTER(i64)],
         "dbs_free": [vp],
+        "dbs_probe_read": [vp, i64, vp, C.c_uint32, vp],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -288,6 +289,17 @@ def dbs_copy_array(A: Matrix, which: int) -> np.ndarray:
     _check(_lib.dbs_copy_array(A.handle, int(which), out.ctypes.data_as(C.c_void_p), out.nbytes,
                                C.byref(nbytes)), "dbs_copy_array")
     return out
+
+
+def dbs_probe_read(buf, sink, never: int = 0xFFFFFFFF, stream=None) -> None:
+    """Read the CUDA tensor `buf` once through the library's streaming-read
+    probe (a measurement helper); `sink` is a one-element int32 CUDA tensor
+    written only if some thread's XOR of words equals `never`."""
+    if not isinstance(buf, _Tensor) or not buf.is_cuda or not buf.is_contiguous():
+        raise TypeError("buf must be a contiguous CUDA tensor")
+    _need(sink, "sink", _I32, 1)
+    _check(_lib.dbs_probe_read(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(),
+                               int(never) & 0xFFFFFFFF, _stream(stream, buf.device)), "dbs_probe_read")
 
 
 def dbs_free(A: Matrix) -> None:

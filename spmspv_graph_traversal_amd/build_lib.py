@@ -18,7 +18,7 @@ LIB = os.path.join(HERE, "libdbs.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["scan.hip", "build.hip", "spmspv.hip", "bfs.hip", "api.cpp"]
+SOURCES = ["scan.hip", "build.hip", "spmspv.hip", "bfs.hip", "probe.hip", "api.cpp"]
 
 FLAGS = [
     f"--offload-arch={ARCH}",

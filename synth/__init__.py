@@ -8,6 +8,7 @@ from .generators import (  # noqa: F401
     rng_for,
     uniform_csr,
     rmat_csr,
+    permute_vertices,
     largest_component_vertices,
     decode_weight_csr,
     decode_activation,

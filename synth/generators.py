@@ -135,6 +135,21 @@ def rmat_csr(scale: int, edge_factor: int, rng: np.random.Generator,
     return _csr_from_sorted_keys(keys, nv, nv)
 
 
+def permute_vertices(row_ptr: np.ndarray, col_idx: np.ndarray, rng: np.random.Generator):
+    """The same square pattern matrix with its vertices relabelled by a seeded
+    random permutation p (entry (i, j) moves to (p[i], p[j])).  On an R-MAT
+    graph this scatters the hub rows and columns over the whole index range,
+    so its 16x16 tiles hold about one entry each instead of ~1.6.
+    Returns (row_ptr, col_idx) with sorted columns per row."""
+    n = row_ptr.shape[0] - 1
+    perm = rng.permutation(n).astype(np.int64)
+    rows = np.repeat(np.arange(n, dtype=np.int64), np.diff(row_ptr.astype(np.int64)))
+    keys = perm[rows] * n + perm[col_idx.astype(np.int64)]
+    del rows
+    keys.sort()
+    return _csr_from_sorted_keys(keys, n, n)
+
+
 def largest_component_vertices(row_ptr: np.ndarray, col_idx: np.ndarray, n: int) -> np.ndarray:
     """Sorted vertex ids of the largest connected component (symmetric pattern)."""
     import scipy.sparse as sp

@@ -67,6 +67,14 @@ def test_host_side_validation_without_gpu(lib):
     assert lib.dbs_set_option(None, 0, 0) == 1
     lib.dbs_free.argtypes = [vp]
     assert lib.dbs_free(None) == 0
+    # the read probe: null buffer or sink, a size that is not a positive multiple
+    # of 16, a buffer not 16-byte aligned
+    lib.dbs_probe_read.argtypes = [vp, C.c_int64, vp, C.c_uint32, vp]
+    assert lib.dbs_probe_read(None, 64, vp(16), 0, None) == 1
+    assert lib.dbs_probe_read(vp(16), 64, None, 0, None) == 1
+    assert lib.dbs_probe_read(vp(16), 40, vp(16), 0, None) == 1
+    assert lib.dbs_probe_read(vp(16), 0, vp(16), 0, None) == 1
+    assert lib.dbs_probe_read(vp(24), 64, vp(16), 0, None) == 1
 
 
 def test_default_build_options(lib):

@@ -8,7 +8,7 @@ import pytest
 
 import oracle as orc
 from gpu_helpers import bf16_csr_of, build, csr_of, mixed_tile_dense, options, up
-from synth import (bf16_bits_to_f32, f32_to_bf16_bits, rmat_csr, rng_for, sparse_x,
+from synth import (bf16_bits_to_f32, f32_to_bf16_bits, permute_vertices, rmat_csr, rng_for, sparse_x,
                    uniform_csr)
 
 pytestmark = pytest.mark.gpu
@@ -291,6 +291,26 @@ def test_rmat20_or_and_sweep_full_size(dbs):
         if density <= 0.01:
             dbs.dbs_set_option(A, dbs.DBS_OPT_PATH, 1)
             np.testing.assert_array_equal(run_or(dbs, A, n, xi), yr, err_msg=f"push {density}")
+
+
+def test_rmat20_permuted_or_and_sweep_full_size(dbs):
+    """The R-MAT 20 graph with its vertices relabelled at random (about one
+    entry per tile), OR-AND, the density sweep with the inputs the benchmark
+    times; both paths forced at every density against the oracle."""
+    rp, ci = permute_vertices(*rmat_csr(20, 16, rng_for("rmat20")), rng_for("rmat20", 2))
+    n = 1 << 20
+    A = build(dbs, n, n, rp, ci, None, dbs.DBS_PATTERN)
+    st = dbs.dbs_get_stats(A)
+    assert st["tiles"] > 1.4 * 19_000_000  # the relabelled graph's tiles hold ~1 entry each
+    for k, density in enumerate([0.0001, 0.001, 0.01, 0.1, 0.5]):
+        xi, _ = sparse_x(n, density, rng_for("rmat20", 3, k), with_values=False)
+        yr = orc.or_and_pull(n, n, rp, ci, xi)
+        for path in PATHS:
+            dbs.dbs_set_option(A, dbs.DBS_OPT_PATH, path)
+            np.testing.assert_array_equal(run_or(dbs, A, n, xi), yr, err_msg=f"density {density} path {path}")
+        _, nz = orc.xmeta(n, xi)
+        assert dbs.dbs_get_stats(A)["last_n_nzblk"] == nz
+    dbs.dbs_set_option(A, dbs.DBS_OPT_PATH, 0)
 
 
 @pytest.mark.parametrize("kind", ["alternating", "permuted"])
