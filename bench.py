@@ -267,7 +267,10 @@ def sweep_inputs(torch, fmt, n, key):
 
 def sweep_per_density(dbs, torch, args, A, fmt, xs, y):
     """Per density: call and kernel times, bytes (and B_min), GB/s and the
-    roofline fraction; then the kernel with push and with pull forced."""
+    roofline fraction; then the kernel with push and with pull forced.
+    call_us is the mean of back-to-back calls; call_us_each_median / _mean
+    come from 100 calls each bracketed by its own events (which add a little
+    time of their own)."""
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     # per-density breakdown (separate loops, same kernels)
     per = []
@@ -279,6 +282,14 @@ def sweep_per_density(dbs, torch, args, A, fmt, xs, y):
         ev1.record()
         torch.cuda.synchronize()
         call_ms = ev0.elapsed_time(ev1) / args.steps
+        # 100 calls, each between its own pair of events: median and mean
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(100)]
+        for e_a, e_b in pairs:
+            e_a.record()
+            dbs.dbs_spmspv(A, x["x"], None, dbs.DBS_OR_AND, y)
+            e_b.record()
+        torch.cuda.synchronize()
+        each = np.array([e_a.elapsed_time(e_b) for e_a, e_b in pairs]) * 1e3
         dbs.dbs_set_option(A, dbs.DBS_OPT_TIMING, 1)
         for _ in range(args.steps):
             dbs.dbs_spmspv(A, x["x"], None, dbs.DBS_OR_AND, y)
@@ -289,7 +300,8 @@ def sweep_per_density(dbs, torch, args, A, fmt, xs, y):
         per.append({
             "density": x["density"], "nnz_x": int(x["xi"].shape[0]), "n_nzblk": s2["last_n_nzblk"],
             "xb_ratio": round(s2["last_n_nzblk"] / fmt.nb, 5), "path": "push" if s2["last_path"] == 0 else "pull",
-            "call_us": round(call_ms * 1e3, 2), "compute_kernel_us": round(kms * 1e3, 2),
+            "call_us": round(call_ms * 1e3, 2), "call_us_each_median": round(float(np.median(each)), 2),
+            "call_us_each_mean": round(float(each.mean()), 2), "compute_kernel_us": round(kms * 1e3, 2),
             "meta_kernel_us": round(mms * 1e3, 2),
             "bytes": int(x["meta_bytes"] + x["comp_bytes"]),
             "bytes_min": int(x["meta_bytes"] + x["comp_bytes"] - x["scan_bytes"]),
