@@ -993,6 +993,8 @@ def main():
                     help="only the R-MAT 22 BFS (for profiling the level kernels); prints its JSON")
     ap.add_argument("--zipf-only", action="store_true",
                     help="only the Zipf/band stress matrix (for profiling its pull); prints its JSON")
+    ap.add_argument("--permuted-only", action="store_true",
+                    help="only the sweep on the relabelled R-MAT 20 graph (for profiling); prints its JSON")
     ap.add_argument("--headline-only", action="store_true",
                     help="only the timed sweep (for profiling: every SpMSpV launch is one of the timed mix)")
     ap.add_argument("--zipf-band-frac", type=float, default=0.9,
@@ -1032,6 +1034,12 @@ def main():
         return
     if args.zipf_only:
         print(json.dumps({"zipf_band": bench_zipf(dbs, torch, args)}), flush=True)
+        return
+    if args.permuted_only:
+        from synth import rmat_csr, rng_for
+
+        rp, ci = rmat_csr(20, 16, rng_for("rmat20"))
+        print(json.dumps({"rmat20_permuted": bench_rmat20_permuted(dbs, torch, args, rp, ci, 1 << 20)}), flush=True)
         return
     res = bench_rmat20(dbs, torch, args)
     log(f"[bench] rmat20 sweep: {res['ms_per_step']:.3f} ms/step, {res['value']:.1f} GB/s")
